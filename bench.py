@@ -1,0 +1,278 @@
+#!/usr/bin/env python3
+"""Benchmark of the bf16 exponent-Huffman GPU decoder on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic
+weights: every matrix of the workload is decoded from its DFC1 container in
+HBM into bf16 in HBM (one batched kernel launch per step for the default
+workload).  The containers are built on the host beforehand and are already
+resident in device memory when the timed region starts.
+
+Default workload: one Llama-3-8B-shaped transformer block (Wq, Wk, Wv, Wo,
+gate, up, down; 218,103,808 weights), N(0, 0.02^2) bf16 with 0.1% outliers
+at 20 sigma, one codebook per matrix.
+
+Prints one JSON line: decoded bf16 GB/s as ``value``, plus compression ratio,
+bit-exactness, the roofline fraction of the decode kernel (algorithmic HBM
+bytes per launch over its measured duration, against 8 TB/s) and the CPU
+oracle's throughput on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "decoded bf16 GB/s (fraction of HBM roofline) + compression ratio, bit-exact"
+KERNEL = "dfc_decode_kernel"
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for name in ("dfc_decode.hip", "dfc_format.h"):
+        with open(os.path.join(ROOT, "lossless_entropy_coded_dfc_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def workload_matrices(name: str):
+    from lossless_entropy_coded_dfc_amd import synth
+    if name == "llama3-8b-block":
+        return [(n, x) for n, x in synth.llama3_8b_block()]
+    if name == "single-4096":
+        return [("w", synth.single_matrix())]
+    if name.startswith("stress-"):
+        kind = name[len("stress-"):]
+        return [(kind, synth.stress(kind))]
+    raise SystemExit(f"unknown workload {name}")
+
+
+def read_traffic(workload: str, digest: str):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if
+    they were taken on the current kernel source."""
+    path = os.path.join(PROFILES, f"{KERNEL}_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_digest") != digest:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(blobs, budget_s: float):
+    """The oracle's chunk-parallel numpy decoder on a bounded sample: whole
+    matrices in workload order until about ``budget_s`` seconds are spent."""
+    import numpy as np
+    from oracle import blob as oracle_blob
+    done_elems, spent, names = 0, 0.0, []
+    for name, blob, x in blobs:
+        t0 = time.perf_counter()
+        y = oracle_blob.decode_blob(bytes(blob))
+        dt = time.perf_counter() - t0
+        if not np.array_equal(y, x.ravel()):
+            raise SystemExit(f"oracle decode mismatch on {name}")
+        done_elems += x.size
+        spent += dt
+        names.append(name)
+        if spent >= budget_s:
+            break
+    return {
+        "value": round(2.0 * done_elems / spent / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{'+'.join(names)} ({done_elems} weights, {spent:.1f} s, numpy chunk-parallel decoder)",
+    }
+
+
+def copy_probe(nbytes: int, steps: int):
+    """A plain device copy of known size, for scaling HBM counters."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes, "steps": steps}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama3-8b-block")
+    ap.add_argument("--chunk-bytes", type=int, default=16)
+    ap.add_argument("--lut-bits", type=int, default=12)
+    ap.add_argument("--sets", type=int, default=2, help="rotating buffer sets (defeats the 256 MB MALL)")
+    ap.add_argument("--waves", type=int, default=0)
+    ap.add_argument("--bpw", type=int, default=0)
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle CPU decode")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, help="run a plain copy of this many bytes and exit")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the decode shards by matrix with no exchange, and this build "
+              "runs on a single MI355X; --gpus above 1 is not supported.", file=sys.stderr)
+        raise SystemExit(2)
+    if args.copy_probe:
+        copy_probe(args.copy_probe, max(1, args.steps))
+        return
+
+    import numpy as np
+    import torch
+
+    import lossless_entropy_coded_dfc_amd as dfc
+    from oracle import codebook as oracle_cb
+    from oracle import fields as oracle_fields
+
+    dfc.library()
+    dfc.set_launch(args.waves, args.bpw)
+    torch.cuda.init()
+    dev_name = torch.cuda.get_device_name(0)
+
+    log(f"[bench] generating workload {args.workload}")
+    mats = workload_matrices(args.workload)
+    blobs, infos, host = [], [], []
+    n_total = coded = bound = 0.0
+    alg_bytes = 0
+    for name, x in mats:
+        b = dfc.encode(x, chunk_bytes=args.chunk_bytes, lut_bits=args.lut_bits)
+        info = dfc.blob_info(b)
+        blobs.append(b)
+        infos.append(info)
+        host.append((name, b, x))
+        n_total += info.n
+        coded += info.coded_bytes
+        h = oracle_cb.histogram(oracle_fields.split(x)[0])
+        bound += info.n * (8.0 + oracle_cb.entropy_bits(h)) / 8.0
+        # Bytes the kernel must move: every section it reads (stream words,
+        # chunk offsets, block offsets, raw bytes, decode tables) + bf16 out.
+        alg_bytes += (info.words_bytes + info.offsets_bytes + info.blockout_bytes + info.raw_bytes +
+                      info.tables_bytes + 2 * info.n)
+        log(f"[bench] {name}: n={info.n} coded={info.coded_bytes} ratio={2 * info.n / info.coded_bytes:.4f}")
+
+    sets = []
+    for s in range(max(1, args.sets)):
+        devs = [torch.from_numpy(b).cuda() for b in blobs]
+        outs = [torch.empty(int(i.n), dtype=torch.int16, device="cuda") for i in infos]
+        sets.append((devs, outs))
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+
+    def step(k):
+        devs, outs = sets[k % len(sets)]
+        items = list(zip(devs, infos, outs))
+        for j in range(0, len(items), dfc.MAX_BATCH):
+            dfc.decode_batch(items[j: j + dfc.MAX_BATCH], status)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t_all0 = torch.cuda.Event(enable_timing=True)
+    t_all1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_all0.record()
+    for k in range(args.steps):
+        starts[k].record()
+        step(k)
+        ends[k].record()
+    t_all1.record()
+    torch.cuda.synchronize()
+    total_ms = t_all0.elapsed_time(t_all1)
+    per_launch_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    ms_step = total_ms / args.steps
+    med_launch_ms = per_launch_ms[len(per_launch_ms) // 2]
+    mean_launch_ms = sum(per_launch_ms) / len(per_launch_ms)
+
+    # Bit-exactness, outside the timed region, on every buffer set.
+    exact = int(status.item()) == 0
+    for devs, outs in sets:
+        for (name, b, x), out in zip(host, outs):
+            ref = torch.from_numpy(x.ravel().view(np.int16)).cuda()
+            if not torch.equal(out, ref):
+                exact = False
+                log(f"[bench] MISMATCH on {name}")
+    if not exact:
+        raise SystemExit("decode is not bit-exact")
+
+    value = 2.0 * n_total / (ms_step / 1e3) / 1e9
+    achieved = alg_bytes / (mean_launch_ms / 1e3) / 1e9
+    digest = kernel_source_digest()
+    traffic = read_traffic(args.workload, digest)
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload,
+            "matrices": len(mats),
+            "weights": int(n_total),
+            "chunk_bytes": args.chunk_bytes,
+            "lanes_per_block": 64,
+            "lut_bits": args.lut_bits,
+            "launches_per_step": -(-len(mats) // dfc.MAX_BATCH),
+            "buffer_sets": len(sets),
+            "device": dev_name,
+        },
+        "weights_per_s": round(n_total / (ms_step / 1e3), 1),
+        "compression_ratio": round(2.0 * n_total / coded, 5),
+        "coded_over_entropy_bound": round(coded / bound, 5),
+        "bit_exact": exact,
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": int(alg_bytes),
+            "kernel": KERNEL,
+            "launch_ms_mean": round(mean_launch_ms, 5),
+            "launch_ms_median": round(med_launch_ms, 5),
+            "kernel_source_digest": digest,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] timing the CPU oracle (~{args.cpu_budget:.0f} s)")
+        result["cpu_baseline"] = cpu_baseline(host, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,172 @@
+/*
+ * dfc.h - C ABI of libdfc: lossless exponent-Huffman coding of bf16 weights
+ * and its GPU decoder for AMD Instinct MI355X (gfx950).
+ *
+ * Method (DFloat11 blog post, "70% Size, 100% Accuracy: Lossless LLM
+ * Compression for Efficient GPU Inference via Dynamic-Length Float
+ * (DFloat11)"):
+ *   section 02  bf16 weights have a low-entropy distribution; an entropy code
+ *               gives frequent values short codes and rare values long ones,
+ *               and decoding returns the original bits exactly;
+ *   section 03, item 1  decoding uses compact hierarchical lookup tables held
+ *               in on-chip memory;
+ *   section 03, item 2  a two-phase kernel: threads first agree on read and
+ *               write positions through small auxiliary variables, then
+ *               rebuild the weights.
+ *
+ * What is coded: only the 8 exponent bits of every bf16 value, with a
+ * canonical (RFC 1951 section 3.2.2) prefix code of at most 24 bits built by
+ * package-merge from the matrix's own exponent histogram.  Sign and mantissa
+ * stay one raw byte (sign << 7 | mantissa).  The code stream is cut into
+ * fixed-size chunks of C bytes, one per GPU lane; each chunk carries a 5-bit
+ * start offset (bits from the chunk start to its first code) and each block
+ * of T chunks carries a 32-bit output offset (number of codes before it).
+ *
+ * Everything is stateless and re-entrant.  The library never allocates
+ * device memory and never synchronises a stream: the caller owns every
+ * buffer.  Host functions take host pointers; device functions take device
+ * pointers and enqueue work on the given HIP stream (a hipStream_t passed as
+ * void*, NULL = the default stream) and return before it runs.  No C++
+ * exception crosses this interface.
+ */
+#ifndef DFC_H
+#define DFC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DFC_OK = 0,
+    DFC_EINVAL = -1,       /* bad argument (null pointer, bad parameter value, misaligned buffer) */
+    DFC_ESIZE = -2,        /* a buffer is too small, or n does not match the container */
+    DFC_ECORRUPT = -3,     /* the container fails validation (or a decoded block count mismatched) */
+    DFC_EUNSUPPORTED = -4, /* valid container, but this build cannot decode that variant */
+    DFC_EHIP = -5          /* a HIP runtime call failed */
+} dfc_status;
+
+enum { DFC_LAYOUT_FLAT = 0 };
+enum { DFC_MAX_BATCH = 32 };
+
+/* Encoder parameters; dfc_default_params fills the defaults. */
+typedef struct {
+    uint32_t chunk_bytes;     /* C: bytes of code stream per lane: 4, 8, 16 or 32 (default 16) */
+    uint32_t lanes_per_block; /* T: chunks per block: 64 (default; one wavefront), 128 or 256 */
+    uint32_t max_code_len;    /* code length limit, 1..24 (default 24) */
+    uint32_t lut_bits;        /* k: bits indexed by the first-level decode table, 8..12 (default 12) */
+    uint32_t layout;          /* DFC_LAYOUT_FLAT: elements in row-major order */
+    uint32_t threads;         /* host encoder threads; 0 = min(hardware threads, 16) */
+    uint64_t rows, cols;      /* matrix shape recorded in the header; 0,0 = 1 x n */
+} dfc_params;
+
+/* A codebook: code length and canonical code of every exponent value. */
+typedef struct {
+    uint8_t len[256];    /* 0 = unused; otherwise 1..24 */
+    uint32_t code[256];  /* canonical code, right-aligned in len bits */
+    uint32_t n_used;     /* symbols with len > 0 (2 or more for a non-empty histogram) */
+    uint32_t min_len, max_len;
+} dfc_codebook;
+
+/* Validated description of a container (filled by dfc_blob_info). */
+typedef struct {
+    uint64_t n;            /* elements */
+    uint64_t rows, cols;
+    uint64_t blob_bytes;   /* whole container */
+    uint64_t coded_bytes;  /* header + lengths + stream + offsets + block offsets + raw
+                              (excludes derived decode tables and alignment padding) */
+    uint64_t total_bits;   /* code stream length */
+    uint64_t n_chunks, n_blocks;
+    uint64_t off_tables, tables_bytes;
+    uint64_t off_words, words_bytes;
+    uint64_t off_offsets, offsets_bytes;
+    uint64_t off_blockout, blockout_bytes;
+    uint64_t off_raw, raw_bytes;
+    uint32_t chunk_bytes, lanes_per_block, max_code_len, lut_bits, layout;
+    uint32_t n_used, min_len, max_len;
+} dfc_info;
+
+/* One matrix of a batched decode. */
+typedef struct {
+    const void *blob_dev;  /* device copy of the whole container (256-byte aligned) */
+    const dfc_info *info;  /* host description of that container (from dfc_blob_info) */
+    uint16_t *dst_dev;     /* n bf16 outputs (16-byte aligned), row-major */
+    uint64_t n;            /* must equal info->n */
+} dfc_batch_item;
+
+/* Fills *p with the defaults (C = 16, T = 64, limit 24, k = 12, flat). */
+void dfc_default_params(dfc_params *p);
+
+/* 256-bin histogram of the exponent bits (bits 14..7) of n bf16 values.
+ * Host.  src: n uint16 bf16 bit patterns (may be NULL when n == 0).
+ * hist: 256 counts, overwritten.  DFC_EINVAL on a null pointer. */
+dfc_status dfc_histogram(const uint16_t *src, uint64_t n, uint64_t hist[256]);
+
+/* Length-limited optimal code lengths (package-merge) and canonical codes for
+ * an exponent histogram (DFloat11 blog, section 02: short codes for frequent
+ * values).  Host.  Ties between equally good length vectors are broken
+ * deterministically (equal weights: leaves before packages, leaves by
+ * (count, symbol)).  One used symbol gets length 1 plus a phantom symbol
+ * ((s + 1) mod 256) of length 1; an all-zero histogram gives an empty book.
+ * DFC_EINVAL: null pointer or max_code_len outside 1..24; DFC_ESIZE: more
+ * used symbols than 2^max_code_len. */
+dfc_status dfc_build_codebook(const uint64_t hist[256], uint32_t max_code_len, dfc_codebook *out);
+
+/* Upper bound on the container size dfc_encode can produce for n elements.
+ * Host.  DFC_EINVAL on bad parameters. */
+dfc_status dfc_encode_bound(uint64_t n, const dfc_params *p, uint64_t *max_bytes);
+
+/* Encode n bf16 values into a container (DFloat11 blog, section 03 item 2:
+ * the auxiliary per-chunk and per-block position variables are written here).
+ * Host, multithreaded.  src: n bf16 bit patterns, row-major.  p: NULL =
+ * defaults.  cb: NULL = build from src's own histogram with p->max_code_len;
+ * otherwise every exponent present in src must have a code (DFC_EINVAL if
+ * not).  dst: cap bytes, written from offset 0; *written receives the
+ * container size (a multiple of 256).  DFC_ESIZE if cap is too small (use
+ * dfc_encode_bound) or n >= 2^32.  The output is deterministic. */
+dfc_status dfc_encode(const uint16_t *src, uint64_t n, const dfc_params *p,
+                      const dfc_codebook *cb, void *dst, uint64_t cap, uint64_t *written);
+
+/* Validate a host copy of a container and describe it.  Host.  Checks the
+ * header, section placement, code lengths (complete code, limit 24), the
+ * derived decode tables (rebuilt and compared), every chunk offset and every
+ * block offset.  DFC_ECORRUPT on any inconsistency, DFC_EUNSUPPORTED on an
+ * unknown version/layout, DFC_ESIZE if bytes < the declared size. */
+dfc_status dfc_blob_info(const void *blob, uint64_t bytes, dfc_info *out);
+
+/* Decode one container on the GPU (DFloat11 blog, section 03: the two-phase
+ * kernel with lookup tables in on-chip memory).  Device, asynchronous on
+ * stream.  blob_dev: device copy of the container described by info (256-byte
+ * aligned).  dst_dev: n uint16 outputs (16-byte aligned), receives the
+ * original bf16 bit patterns, row-major.  status_dev: NULL, or one device
+ * uint32 that the kernel sets to a nonzero value if a block's decoded count
+ * disagrees with its block offsets (the caller clears it beforehand and reads
+ * it after the stream completes; outputs of such a block are left
+ * unwritten).  Synchronous errors: DFC_EINVAL (null/misaligned pointers),
+ * DFC_ESIZE (n != info->n), DFC_EUNSUPPORTED (lanes_per_block != 64),
+ * DFC_EHIP (launch failure). */
+dfc_status dfc_decode(const void *blob_dev, const dfc_info *info, uint16_t *dst_dev, uint64_t n,
+                      uint32_t *status_dev, void *stream);
+
+/* Decode up to DFC_MAX_BATCH containers with one kernel launch (the
+ * whole-model, matrix-by-matrix decode just before use that the DFloat11
+ * blog's introduction calls online decompression).  Same contract as
+ * dfc_decode for every item; status_dev is shared.  count == 0 is a no-op. */
+dfc_status dfc_decode_batch(const dfc_batch_item *items, uint32_t count, uint32_t *status_dev,
+                            void *stream);
+
+/* Launch tuning knob for benchmarks: wavefronts per workgroup (4, 8 or 16)
+ * and wave-blocks each wavefront decodes (1..64).  0 = automatic.  Returns
+ * DFC_EINVAL for other values.  Process-wide; not thread-safe. */
+dfc_status dfc_set_launch(uint32_t waves_per_group, uint32_t blocks_per_wave);
+
+/* Human-readable name of a status code. */
+const char *dfc_status_str(dfc_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DFC_H */

@@ -1,0 +1,261 @@
+"""Python binding of libdfc: lossless exponent-Huffman compression of bf16
+weights with a gfx950 (MI355X) GPU decoder.
+
+This module only marshals arguments into the C ABI declared in
+``include/dfc.h``: every step of encoding runs in the host library and every
+step of decoding runs in its HIP kernels.  torch supplies device memory
+(``data_ptr()``) and the current HIP stream.  If ``libdfc.so`` has not been
+built, every entry point raises ``DfcLibraryMissing``; there is no fallback.
+
+Importing the package does not load the library; ``synth`` (seeded input
+generators) is usable without it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+__all__ = [
+    "DfcError", "DfcLibraryMissing", "Params", "Codebook", "Info", "BatchItem",
+    "library", "library_path", "default_params", "histogram", "build_codebook",
+    "encode_bound", "encode", "blob_info", "decode", "decode_batch", "set_launch",
+    "status_str", "MAX_BATCH",
+]
+
+MAX_BATCH = 32
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libdfc.so")
+_LIB = None
+
+OK, EINVAL, ESIZE, ECORRUPT, EUNSUPPORTED, EHIP = 0, -1, -2, -3, -4, -5
+
+
+class DfcError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_str(status)} ({status})")
+
+
+class DfcLibraryMissing(ImportError):
+    pass
+
+
+class Params(ctypes.Structure):
+    _fields_ = [("chunk_bytes", ctypes.c_uint32), ("lanes_per_block", ctypes.c_uint32),
+                ("max_code_len", ctypes.c_uint32), ("lut_bits", ctypes.c_uint32),
+                ("layout", ctypes.c_uint32), ("threads", ctypes.c_uint32),
+                ("rows", ctypes.c_uint64), ("cols", ctypes.c_uint64)]
+
+
+class Codebook(ctypes.Structure):
+    _fields_ = [("len", ctypes.c_uint8 * 256), ("code", ctypes.c_uint32 * 256),
+                ("n_used", ctypes.c_uint32), ("min_len", ctypes.c_uint32), ("max_len", ctypes.c_uint32)]
+
+    @property
+    def lengths(self) -> np.ndarray:
+        return np.frombuffer(bytes(self.len), dtype=np.uint8).copy()
+
+    @property
+    def codes(self) -> np.ndarray:
+        return np.array(list(self.code), dtype=np.uint32)
+
+
+class Info(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_uint64) for name in (
+        "n", "rows", "cols", "blob_bytes", "coded_bytes", "total_bits", "n_chunks", "n_blocks",
+        "off_tables", "tables_bytes", "off_words", "words_bytes", "off_offsets", "offsets_bytes",
+        "off_blockout", "blockout_bytes", "off_raw", "raw_bytes")] + \
+        [(name, ctypes.c_uint32) for name in (
+            "chunk_bytes", "lanes_per_block", "max_code_len", "lut_bits", "layout",
+            "n_used", "min_len", "max_len")]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+class BatchItem(ctypes.Structure):
+    _fields_ = [("blob_dev", ctypes.c_void_p), ("info", ctypes.POINTER(Info)),
+                ("dst_dev", ctypes.c_void_p), ("n", ctypes.c_uint64)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def library():
+    """Load libdfc.so (once).  Raises DfcLibraryMissing if it is not built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(_LIB_PATH):
+        raise DfcLibraryMissing(
+            f"{_LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
+            "or `python -m lossless_entropy_coded_dfc_amd.csrc.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    st = ctypes.c_int
+    u64p = ctypes.POINTER(ctypes.c_uint64)
+    lib.dfc_default_params.argtypes = [ctypes.POINTER(Params)]
+    lib.dfc_default_params.restype = None
+    lib.dfc_histogram.argtypes = [ctypes.c_void_p, ctypes.c_uint64, u64p]
+    lib.dfc_histogram.restype = st
+    lib.dfc_build_codebook.argtypes = [u64p, ctypes.c_uint32, ctypes.POINTER(Codebook)]
+    lib.dfc_build_codebook.restype = st
+    lib.dfc_encode_bound.argtypes = [ctypes.c_uint64, ctypes.POINTER(Params), u64p]
+    lib.dfc_encode_bound.restype = st
+    lib.dfc_encode.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.POINTER(Params),
+                               ctypes.POINTER(Codebook), ctypes.c_void_p, ctypes.c_uint64, u64p]
+    lib.dfc_encode.restype = st
+    lib.dfc_blob_info.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.POINTER(Info)]
+    lib.dfc_blob_info.restype = st
+    lib.dfc_decode.argtypes = [ctypes.c_void_p, ctypes.POINTER(Info), ctypes.c_void_p, ctypes.c_uint64,
+                               ctypes.c_void_p, ctypes.c_void_p]
+    lib.dfc_decode.restype = st
+    lib.dfc_decode_batch.argtypes = [ctypes.POINTER(BatchItem), ctypes.c_uint32, ctypes.c_void_p,
+                                     ctypes.c_void_p]
+    lib.dfc_decode_batch.restype = st
+    lib.dfc_set_launch.argtypes = [ctypes.c_uint32, ctypes.c_uint32]
+    lib.dfc_set_launch.restype = st
+    lib.dfc_status_str.argtypes = [ctypes.c_int]
+    lib.dfc_status_str.restype = ctypes.c_char_p
+    _LIB = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    try:
+        return library().dfc_status_str(int(status)).decode()
+    except DfcLibraryMissing:
+        return "libdfc not built"
+
+
+def _check(status: int, where: str):
+    if status != OK:
+        raise DfcError(status, where)
+
+
+def _u16(bits) -> np.ndarray:
+    a = np.asarray(bits)
+    if a.dtype != np.uint16:
+        if a.dtype.itemsize != 2:
+            raise TypeError("expected 16-bit bf16 bit patterns")
+        a = a.view(np.uint16)
+    return np.ascontiguousarray(a).ravel()
+
+
+# ------------------------------------------------------------------ host
+
+def default_params(**overrides) -> Params:
+    p = Params()
+    library().dfc_default_params(ctypes.byref(p))
+    for k, v in overrides.items():
+        setattr(p, k, v)
+    return p
+
+
+def histogram(bits) -> np.ndarray:
+    src = _u16(bits)
+    h = np.zeros(256, dtype=np.uint64)
+    _check(library().dfc_histogram(src.ctypes.data_as(ctypes.c_void_p), src.size,
+                                   h.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64))), "dfc_histogram")
+    return h
+
+
+def build_codebook(hist, max_code_len: int = 24) -> Codebook:
+    h = np.ascontiguousarray(np.asarray(hist, dtype=np.uint64))
+    if h.shape != (256,):
+        raise ValueError("histogram must have 256 bins")
+    cb = Codebook()
+    _check(library().dfc_build_codebook(h.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)), max_code_len,
+                                        ctypes.byref(cb)), "dfc_build_codebook")
+    return cb
+
+
+def encode_bound(n: int, params: Params | None = None) -> int:
+    out = ctypes.c_uint64()
+    _check(library().dfc_encode_bound(n, ctypes.byref(params) if params else None, ctypes.byref(out)),
+           "dfc_encode_bound")
+    return out.value
+
+
+def encode(bits, chunk_bytes: int = 16, lanes: int = 64, max_code_len: int = 24, lut_bits: int = 12,
+           codebook: Codebook | None = None, threads: int = 0, shape=None) -> np.ndarray:
+    """Encode bf16 bit patterns (any shape, row-major) into a DFC1 container
+    (numpy uint8 array)."""
+    arr = np.asarray(bits)
+    src = _u16(arr)
+    if shape is None:
+        shape = arr.shape if arr.ndim == 2 else (1, src.size)
+    p = default_params(chunk_bytes=chunk_bytes, lanes_per_block=lanes, max_code_len=max_code_len,
+                       lut_bits=lut_bits, threads=threads, rows=int(shape[0]), cols=int(shape[1]))
+    if src.size == 0:
+        p.rows, p.cols = 0, 0
+    cap = encode_bound(src.size, p)
+    dst = np.empty(cap, dtype=np.uint8)
+    written = ctypes.c_uint64()
+    _check(library().dfc_encode(src.ctypes.data_as(ctypes.c_void_p), src.size, ctypes.byref(p),
+                                ctypes.byref(codebook) if codebook is not None else None,
+                                dst.ctypes.data_as(ctypes.c_void_p), cap, ctypes.byref(written)),
+           "dfc_encode")
+    return dst[: written.value]
+
+
+def blob_info(blob) -> Info:
+    b = np.ascontiguousarray(np.frombuffer(blob, dtype=np.uint8) if isinstance(blob, (bytes, bytearray))
+                             else np.asarray(blob, dtype=np.uint8))
+    info = Info()
+    _check(library().dfc_blob_info(b.ctypes.data_as(ctypes.c_void_p), b.size, ctypes.byref(info)),
+           "dfc_blob_info")
+    return info
+
+
+# ---------------------------------------------------------------- device
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(int(stream))
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev_ptr(t) -> int:
+    if t is None:
+        return 0
+    if not getattr(t, "is_cuda", False):
+        raise TypeError("expected a device (cuda) tensor")
+    return t.data_ptr()
+
+
+def decode(blob_dev, info: Info, out, status=None, stream=None):
+    """Decode a container held in device memory (torch uint8 tensor) into
+    ``out`` (torch tensor of info.n 16-bit elements).  Asynchronous."""
+    if not out.is_contiguous() or out.element_size() != 2 or out.numel() != info.n:
+        raise ValueError("out must be a contiguous 16-bit tensor with info.n elements")
+    _check(library().dfc_decode(ctypes.c_void_p(_dev_ptr(blob_dev)), ctypes.byref(info),
+                                ctypes.c_void_p(_dev_ptr(out)), info.n,
+                                ctypes.c_void_p(_dev_ptr(status)), _stream(stream)), "dfc_decode")
+    return out
+
+
+def decode_batch(items, status=None, stream=None):
+    """Decode up to MAX_BATCH (blob_dev, info, out) triples with one launch."""
+    items = list(items)
+    if len(items) > MAX_BATCH:
+        raise ValueError(f"at most {MAX_BATCH} items per batch")
+    arr = (BatchItem * max(1, len(items)))()
+    keep = []
+    for k, (blob_dev, info, out) in enumerate(items):
+        if not out.is_contiguous() or out.element_size() != 2 or out.numel() != info.n:
+            raise ValueError("out must be a contiguous 16-bit tensor with info.n elements")
+        keep.append(info)
+        arr[k].blob_dev = _dev_ptr(blob_dev)
+        arr[k].info = ctypes.pointer(info)
+        arr[k].dst_dev = _dev_ptr(out)
+        arr[k].n = info.n
+    _check(library().dfc_decode_batch(arr, len(items), ctypes.c_void_p(_dev_ptr(status)), _stream(stream)),
+           "dfc_decode_batch")
+
+
+def set_launch(waves_per_group: int = 0, blocks_per_wave: int = 0):
+    _check(library().dfc_set_launch(waves_per_group, blocks_per_wave), "dfc_set_launch")

@@ -1,0 +1,56 @@
+"""Build libdfc.so in place (host codec with g++, gfx950 decoder with hipcc).
+
+Usage: python -m lossless_entropy_coded_dfc_amd.csrc.build [-v]
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+PKG = os.path.dirname(HERE)
+ROOT = os.path.dirname(PKG)
+INCLUDE = os.path.join(ROOT, "include")
+OUT = os.path.join(PKG, "libdfc.so")
+ARCH = "gfx950"
+
+# Packed FP32 instructions are kept out of every HIP object.
+HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-Wall", "-Wno-unused-function"]
+CXX_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-pthread", "-Wall", "-Wextra", "-Wno-unused-parameter"]
+
+
+def _hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libdfc)")
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+
+
+def build(verbose: bool = False, out: str = OUT) -> str:
+    """Compile every source and link libdfc.so next to the package."""
+    hipcc = _hipcc()
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    inc = ["-I", INCLUDE, "-I", HERE]
+    host_obj = os.path.join(objdir, "dfc_host.o")
+    dec_obj = os.path.join(objdir, "dfc_decode.o")
+    _run(["g++", *CXX_FLAGS, *inc, "-c", os.path.join(HERE, "dfc_host.cpp"), "-o", host_obj], verbose)
+    _run([hipcc, *HIP_FLAGS, *inc, "-c", os.path.join(HERE, "dfc_decode.hip"), "-o", dec_obj], verbose)
+    tmp = out + ".tmp"
+    _run([hipcc, "-shared", f"--offload-arch={ARCH}", "-fPIC", "-o", tmp, host_obj, dec_obj, "-pthread"], verbose)
+    os.replace(tmp, out)
+    return out
+
+
+if __name__ == "__main__":
+    build(verbose="-v" in sys.argv)

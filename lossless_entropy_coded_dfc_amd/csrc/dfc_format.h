@@ -1,0 +1,92 @@
+// dfc_format.h - byte layout of the DFC1 container shared by the host codec
+// and the device launcher (internal to libdfc).
+//
+// Container: 256-byte header, 256 code lengths, then the sections tables,
+// words, offsets, blockout, raw (and panels, unused by the flat layout),
+// each at the next multiple of 256 bytes, zero padding.  Little-endian.
+#pragma once
+
+#include <cstdint>
+#include <cstring>
+
+namespace dfc {
+
+constexpr uint32_t kMagic = 0x31434644u;  // "DFC1"
+constexpr uint32_t kVersion = 1;
+constexpr uint64_t kHeaderBytes = 512;     // header + code lengths
+constexpr uint32_t kMaxLen = 24;
+constexpr uint32_t kGuardWords = 4;
+constexpr uint32_t kOffsetBits = 5;
+
+// Header field byte offsets.
+namespace hdr {
+constexpr int magic = 0, version = 4, n = 8, total_bits = 16, n_chunks = 24, n_blocks = 32;
+constexpr int chunk_bytes = 40, lanes = 44, max_code_len = 48, lut_bits = 52, layout = 56;
+constexpr int panel_rows = 60, rows = 64, cols = 72, tile_k = 80, reserved = 84;
+constexpr int sections = 88;  // 6 x (u64 offset, u64 bytes): tables, words, offsets, blockout, raw, panels
+constexpr int blob_bytes = 184;
+constexpr int lengths = 256;
+}  // namespace hdr
+
+enum Section { kTables = 0, kWords, kOffsets, kBlockout, kRaw, kPanels, kNumSections };
+
+// Decode-table section layout: lut[2^k] (u64) then limit[32], first[32],
+// base[32] (u32) then order[256] (u8).
+inline uint64_t tables_bytes(uint32_t lut_bits) { return 8ull * (1ull << lut_bits) + 3 * 128 + 256; }
+inline uint64_t tables_limit_off(uint32_t lut_bits) { return 8ull << lut_bits; }
+inline uint64_t tables_first_off(uint32_t lut_bits) { return (8ull << lut_bits) + 128; }
+inline uint64_t tables_base_off(uint32_t lut_bits) { return (8ull << lut_bits) + 256; }
+inline uint64_t tables_order_off(uint32_t lut_bits) { return (8ull << lut_bits) + 384; }
+
+inline uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
+inline uint64_t ceil_div(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
+
+struct Layout {
+    uint64_t n_chunks_used, n_blocks, n_chunks;
+};
+inline Layout layout_sizes(uint64_t total_bits, uint32_t chunk_bytes, uint32_t lanes) {
+    Layout l;
+    l.n_chunks_used = ceil_div(total_bits, 8ull * chunk_bytes);
+    l.n_blocks = ceil_div(l.n_chunks_used, lanes);
+    l.n_chunks = l.n_blocks * lanes;
+    return l;
+}
+
+struct SectionSizes {
+    uint64_t bytes[kNumSections];
+};
+inline SectionSizes section_sizes(uint64_t n, uint64_t n_chunks, uint64_t n_blocks, uint32_t chunk_bytes,
+                                  uint32_t lut_bits) {
+    SectionSizes s;
+    s.bytes[kTables] = tables_bytes(lut_bits);
+    s.bytes[kWords] = 4 * (n_chunks * (chunk_bytes / 4) + kGuardWords);
+    s.bytes[kOffsets] = 4 * (ceil_div(kOffsetBits * (n_chunks + 1), 32) + 1);
+    s.bytes[kBlockout] = 4 * (n_blocks + 1);
+    s.bytes[kRaw] = 16 * ceil_div(n, 16);
+    s.bytes[kPanels] = 0;
+    return s;
+}
+
+// Places the sections after the header; returns the container size.
+inline uint64_t place_sections(const SectionSizes &s, uint64_t off[kNumSections]) {
+    uint64_t pos = kHeaderBytes;
+    for (int i = 0; i < kNumSections; ++i) {
+        pos = align256(pos);
+        off[i] = s.bytes[i] ? pos : 0;
+        pos += s.bytes[i];
+    }
+    return align256(pos);
+}
+
+template <typename T>
+inline T load_le(const uint8_t *p) {
+    T v;
+    std::memcpy(&v, p, sizeof(T));  // little-endian host (x86-64)
+    return v;
+}
+template <typename T>
+inline void store_le(uint8_t *p, T v) {
+    std::memcpy(p, &v, sizeof(T));
+}
+
+}  // namespace dfc

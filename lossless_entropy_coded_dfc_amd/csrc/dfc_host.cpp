@@ -1,0 +1,541 @@
+// dfc_host.cpp - host half of libdfc: exponent histogram, length-limited
+// canonical Huffman codebook, multithreaded encoder and container validation.
+//
+// DFloat11 blog ("70% Size, 100% Accuracy ... (DFloat11)"), section 02:
+// frequent values get short codes and rare values long ones; section 03
+// item 2: decoding threads coordinate through small per-chunk and per-block
+// position variables, which this encoder writes.
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+#include <thread>
+#include <vector>
+
+#include "dfc.h"
+#include "dfc_format.h"
+
+using namespace dfc;
+
+namespace {
+
+unsigned pick_threads(uint32_t requested, uint64_t work) {
+    unsigned hw = std::thread::hardware_concurrency();
+    if (hw == 0) hw = 1;
+    uint64_t t = requested ? requested : std::min(hw, 16u);
+    uint64_t by_work = std::max<uint64_t>(1, work >> 20);  // >= ~1M elements per thread
+    return unsigned(std::max<uint64_t>(1, std::min(t, by_work)));
+}
+
+template <class F>
+void parallel_for(unsigned nt, F &&f) {
+    if (nt <= 1) {
+        f(0u);
+        return;
+    }
+    std::vector<std::thread> pool;
+    pool.reserve(nt - 1);
+    for (unsigned t = 1; t < nt; ++t) pool.emplace_back([&f, t] { f(t); });
+    f(0u);
+    for (auto &th : pool) th.join();
+}
+
+inline uint32_t exponent_of(uint16_t b) { return (b >> 7) & 0xFFu; }
+inline uint8_t raw_of(uint16_t b) { return uint8_t(((b >> 8) & 0x80u) | (b & 0x7Fu)); }
+
+void histogram_mt(const uint16_t *src, uint64_t n, uint64_t hist[256], unsigned nt) {
+    std::vector<uint64_t> local(size_t(nt) * 256, 0);
+    parallel_for(nt, [&](unsigned t) {
+        uint64_t j0 = n * t / nt, j1 = n * (t + 1) / nt;
+        uint64_t *h = &local[size_t(t) * 256];
+        for (uint64_t j = j0; j < j1; ++j) h[exponent_of(src[j])]++;
+    });
+    for (int s = 0; s < 256; ++s) {
+        uint64_t v = 0;
+        for (unsigned t = 0; t < nt; ++t) v += local[size_t(t) * 256 + s];
+        hist[s] = v;
+    }
+}
+
+// Canonical per-length tables (index = length 1..24).
+struct Canon {
+    uint32_t count[kMaxLen + 1], first[kMaxLen + 1], limit[kMaxLen + 1], base[kMaxLen + 1];
+    uint8_t order[256];
+    uint32_t n_used;
+};
+
+void canonical(const uint8_t len[256], Canon &c, uint32_t code[256]) {
+    std::memset(&c, 0, sizeof(c));
+    for (int s = 0; s < 256; ++s)
+        if (len[s]) c.count[len[s]]++;
+    uint32_t seen = 0;
+    for (uint32_t l = 1; l <= kMaxLen; ++l) {
+        c.first[l] = l == 1 ? 0u : (c.first[l - 1] + c.count[l - 1]) << 1;
+        c.limit[l] = (c.first[l] + c.count[l]) << (kMaxLen - l);
+        c.base[l] = seen;
+        seen += c.count[l];
+    }
+    c.n_used = seen;
+    uint32_t next[kMaxLen + 1];
+    std::memcpy(next, c.first, sizeof(next));
+    uint32_t fill[kMaxLen + 1] = {0};
+    for (int s = 0; s < 256; ++s) {
+        uint32_t l = len[s];
+        if (!l) {
+            if (code) code[s] = 0;
+            continue;
+        }
+        if (code) code[s] = next[l]++;
+        c.order[c.base[l] + fill[l]++] = uint8_t(s);  // increasing symbol within a length
+    }
+}
+
+// Package-merge (coin-collector form) with deterministic tie-breaks.
+struct PMItem {
+    uint64_t w;
+    uint32_t kind;   // 0 = leaf, 1 = package
+    uint32_t order;  // leaf rank or package index
+    int32_t a, b;    // children in the previous level (packages)
+    int32_t sym;     // symbol (leaves)
+};
+
+dfc_status package_merge(const uint64_t hist[256], uint32_t limit, uint8_t len[256]) {
+    std::memset(len, 0, 256);
+    std::vector<int> used;
+    for (int s = 0; s < 256; ++s)
+        if (hist[s]) used.push_back(s);
+    const size_t m = used.size();
+    if (m == 0) return DFC_OK;
+    if (m == 1) {
+        len[used[0]] = 1;
+        len[(used[0] + 1) & 255] = 1;
+        return DFC_OK;
+    }
+    if (m > (size_t(1) << limit)) return DFC_ESIZE;
+    std::sort(used.begin(), used.end(), [&](int x, int y) {
+        return hist[x] != hist[y] ? hist[x] < hist[y] : x < y;
+    });
+    std::vector<PMItem> leaves(m);
+    for (size_t r = 0; r < m; ++r) leaves[r] = {hist[used[r]], 0u, uint32_t(r), -1, -1, used[r]};
+    auto less = [](const PMItem &x, const PMItem &y) {
+        if (x.w != y.w) return x.w < y.w;
+        if (x.kind != y.kind) return x.kind < y.kind;
+        return x.order < y.order;
+    };
+    std::vector<std::vector<PMItem>> level(limit);
+    level[0] = leaves;
+    for (uint32_t l = 1; l < limit; ++l) {
+        const auto &prev = level[l - 1];
+        std::vector<PMItem> cur = leaves;
+        for (size_t j = 0; j + 1 < prev.size(); j += 2)
+            cur.push_back({prev[j].w + prev[j + 1].w, 1u, uint32_t(j / 2), int32_t(j), int32_t(j + 1), -1});
+        std::sort(cur.begin(), cur.end(), less);
+        level[l] = std::move(cur);
+    }
+    uint32_t cnt[256] = {0};
+    std::vector<std::pair<int, int>> stack;
+    for (size_t i = 0; i < 2 * m - 2; ++i) stack.push_back({int(limit - 1), int(i)});
+    while (!stack.empty()) {
+        auto [l, i] = stack.back();
+        stack.pop_back();
+        const PMItem &it = level[l][i];
+        if (it.kind == 0) {
+            cnt[it.sym]++;
+        } else {
+            stack.push_back({l - 1, it.a});
+            stack.push_back({l - 1, it.b});
+        }
+    }
+    for (int s = 0; s < 256; ++s) len[s] = uint8_t(cnt[s]);
+    return DFC_OK;
+}
+
+// First-level table entry for a k-bit window (see the container description).
+uint64_t lut_entry(uint32_t window, uint32_t k, const Canon &c) {
+    uint32_t o = 0, ns = 0, nb = 0, mask = 0, syms = 0;
+    while (o < k) {
+        uint32_t found = 0, v = 0;
+        for (uint32_t l = 1; l <= k - o; ++l) {
+            v = (window >> (k - o - l)) & ((1u << l) - 1u);
+            if (v < c.first[l] + c.count[l]) {
+                found = l;
+                break;
+            }
+        }
+        if (!found) break;
+        uint32_t sym = c.order[c.base[found] + v - c.first[found]];
+        mask |= 1u << (o + found - 1);
+        if (ns < 4) {
+            syms |= sym << (8 * ns);
+            ns++;
+            nb += found;
+        }
+        o += found;
+    }
+    return uint64_t(syms) | (uint64_t(ns) << 32) | (uint64_t(nb) << 36) | (uint64_t(mask) << 40) |
+           (uint64_t(o) << 52);
+}
+
+void build_tables(const uint8_t len[256], uint32_t k, uint8_t *out) {
+    Canon c;
+    canonical(len, c, nullptr);
+    for (uint32_t w = 0; w < (1u << k); ++w) store_le<uint64_t>(out + 8ull * w, lut_entry(w, k, c));
+    uint8_t *limit = out + tables_limit_off(k), *first = out + tables_first_off(k), *base = out + tables_base_off(k);
+    std::memset(limit, 0, 3 * 128 + 256);
+    for (uint32_t l = 1; l <= kMaxLen; ++l) {
+        store_le<uint32_t>(limit + 4 * l, c.limit[l]);
+        store_le<uint32_t>(first + 4 * l, c.first[l]);
+        store_le<uint32_t>(base + 4 * l, c.base[l]);
+    }
+    std::memcpy(out + tables_order_off(k), c.order, c.n_used);
+}
+
+bool params_ok(const dfc_params &p) {
+    const uint32_t C = p.chunk_bytes, T = p.lanes_per_block;
+    if (C != 4 && C != 8 && C != 16 && C != 32) return false;
+    if (T != 64 && T != 128 && T != 256) return false;
+    if (p.max_code_len < 1 || p.max_code_len > kMaxLen) return false;
+    if (p.lut_bits < 8 || p.lut_bits > 12) return false;
+    if (p.layout != DFC_LAYOUT_FLAT) return false;
+    return true;
+}
+
+uint64_t kraft(const uint8_t len[256]) {
+    uint64_t k = 0;
+    for (int s = 0; s < 256; ++s)
+        if (len[s]) k += uint64_t(1) << (kMaxLen - len[s]);
+    return k;
+}
+
+}  // namespace
+
+extern "C" {
+
+void dfc_default_params(dfc_params *p) {
+    if (!p) return;
+    std::memset(p, 0, sizeof(*p));
+    p->chunk_bytes = 16;
+    p->lanes_per_block = 64;
+    p->max_code_len = kMaxLen;
+    p->lut_bits = 12;
+    p->layout = DFC_LAYOUT_FLAT;
+}
+
+const char *dfc_status_str(dfc_status s) {
+    switch (s) {
+        case DFC_OK: return "ok";
+        case DFC_EINVAL: return "invalid argument";
+        case DFC_ESIZE: return "size mismatch or buffer too small";
+        case DFC_ECORRUPT: return "corrupt container";
+        case DFC_EUNSUPPORTED: return "unsupported container variant";
+        case DFC_EHIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+dfc_status dfc_histogram(const uint16_t *src, uint64_t n, uint64_t hist[256]) {
+    if (!hist || (!src && n)) return DFC_EINVAL;
+    histogram_mt(src, n, hist, pick_threads(0, n));
+    return DFC_OK;
+}
+
+dfc_status dfc_build_codebook(const uint64_t hist[256], uint32_t max_code_len, dfc_codebook *out) {
+    if (!hist || !out || max_code_len < 1 || max_code_len > kMaxLen) return DFC_EINVAL;
+    dfc_codebook cb;
+    std::memset(&cb, 0, sizeof(cb));
+    dfc_status st = package_merge(hist, max_code_len, cb.len);
+    if (st != DFC_OK) return st;
+    Canon c;
+    canonical(cb.len, c, cb.code);
+    cb.n_used = c.n_used;
+    cb.min_len = cb.max_len = 0;
+    for (int s = 0; s < 256; ++s) {
+        if (!cb.len[s]) continue;
+        if (!cb.min_len || cb.len[s] < cb.min_len) cb.min_len = cb.len[s];
+        cb.max_len = std::max<uint32_t>(cb.max_len, cb.len[s]);
+    }
+    *out = cb;
+    return DFC_OK;
+}
+
+dfc_status dfc_encode_bound(uint64_t n, const dfc_params *pin, uint64_t *max_bytes) {
+    dfc_params p;
+    if (pin) p = *pin; else dfc_default_params(&p);
+    if (!max_bytes || !params_ok(p)) return DFC_EINVAL;
+    const uint64_t bits = n * uint64_t(p.max_code_len);
+    Layout L = layout_sizes(bits, p.chunk_bytes, p.lanes_per_block);
+    SectionSizes s = section_sizes(n, L.n_chunks, L.n_blocks, p.chunk_bytes, p.lut_bits);
+    uint64_t off[kNumSections];
+    *max_bytes = place_sections(s, off);
+    return DFC_OK;
+}
+
+dfc_status dfc_encode(const uint16_t *src, uint64_t n, const dfc_params *pin, const dfc_codebook *cb_in,
+                      void *dst_v, uint64_t cap, uint64_t *written) {
+    dfc_params p;
+    if (pin) p = *pin; else dfc_default_params(&p);
+    if ((!src && n) || !dst_v || !written || !params_ok(p)) return DFC_EINVAL;
+    if (n >= (uint64_t(1) << 32)) return DFC_ESIZE;
+    uint64_t rows = p.rows, cols = p.cols;
+    if (rows == 0 && cols == 0) {
+        rows = 1;
+        cols = n;
+    }
+    if (rows * cols != n) return DFC_EINVAL;
+    uint8_t *dst = static_cast<uint8_t *>(dst_v);
+    const unsigned nt = pick_threads(p.threads, n);
+
+    uint64_t hist[256];
+    histogram_mt(src, n, hist, nt);
+    uint8_t len[256];
+    if (cb_in) {
+        std::memcpy(len, cb_in->len, 256);
+        for (int s = 0; s < 256; ++s) {
+            if (len[s] > p.max_code_len) return DFC_EINVAL;
+            if (hist[s] && !len[s]) return DFC_EINVAL;
+        }
+        uint32_t used = 0;
+        for (int s = 0; s < 256; ++s) used += len[s] != 0;
+        if (n && (used < 2 || kraft(len) != (uint64_t(1) << kMaxLen))) return DFC_EINVAL;
+    } else {
+        dfc_status st = package_merge(hist, p.max_code_len, len);
+        if (st != DFC_OK) return st;
+    }
+    Canon canon;
+    uint32_t code[256];
+    canonical(len, canon, code);
+
+    // Pass 1: bits per thread range.
+    std::vector<uint64_t> range_bits(nt + 1, 0);
+    parallel_for(nt, [&](unsigned t) {
+        uint64_t j0 = n * t / nt, j1 = n * (t + 1) / nt, b = 0;
+        for (uint64_t j = j0; j < j1; ++j) b += len[exponent_of(src[j])];
+        range_bits[t + 1] = b;
+    });
+    for (unsigned t = 0; t < nt; ++t) range_bits[t + 1] += range_bits[t];
+    const uint64_t total_bits = range_bits[nt];
+    const uint32_t C = p.chunk_bytes, T = p.lanes_per_block;
+    Layout L = layout_sizes(total_bits, C, T);
+    SectionSizes sz = section_sizes(n, L.n_chunks, L.n_blocks, C, p.lut_bits);
+    uint64_t off[kNumSections];
+    const uint64_t blob_bytes = place_sections(sz, off);
+    if (cap < blob_bytes) return DFC_ESIZE;
+
+    // Zero the container (padding, guard words and stream words are OR-ed).
+    {
+        const unsigned zt = pick_threads(p.threads, blob_bytes / 4);
+        parallel_for(zt, [&](unsigned t) {
+            uint64_t a = blob_bytes * t / zt, b = blob_bytes * (t + 1) / zt;
+            std::memset(dst + a, 0, b - a);
+        });
+    }
+    store_le<uint32_t>(dst + hdr::magic, kMagic);
+    store_le<uint32_t>(dst + hdr::version, kVersion);
+    store_le<uint64_t>(dst + hdr::n, n);
+    store_le<uint64_t>(dst + hdr::total_bits, total_bits);
+    store_le<uint64_t>(dst + hdr::n_chunks, L.n_chunks);
+    store_le<uint64_t>(dst + hdr::n_blocks, L.n_blocks);
+    store_le<uint32_t>(dst + hdr::chunk_bytes, C);
+    store_le<uint32_t>(dst + hdr::lanes, T);
+    store_le<uint32_t>(dst + hdr::max_code_len, p.max_code_len);
+    store_le<uint32_t>(dst + hdr::lut_bits, p.lut_bits);
+    store_le<uint32_t>(dst + hdr::layout, p.layout);
+    store_le<uint32_t>(dst + hdr::panel_rows, 0);
+    store_le<uint64_t>(dst + hdr::rows, rows);
+    store_le<uint64_t>(dst + hdr::cols, cols);
+    store_le<uint32_t>(dst + hdr::tile_k, 0);
+    for (int i = 0; i < kNumSections; ++i) {
+        store_le<uint64_t>(dst + hdr::sections + 16 * i, off[i]);
+        store_le<uint64_t>(dst + hdr::sections + 16 * i + 8, sz.bytes[i]);
+    }
+    store_le<uint64_t>(dst + hdr::blob_bytes, blob_bytes);
+    std::memcpy(dst + hdr::lengths, len, 256);
+    build_tables(len, p.lut_bits, dst + off[kTables]);
+
+    // Pass 2: pack codes, raw bytes, chunk offsets and block offsets.
+    uint8_t *words = dst + off[kWords];
+    uint8_t *raw = dst + off[kRaw];
+    uint8_t *blockout = dst + off[kBlockout];
+    std::vector<uint8_t> offs(L.n_chunks + 1, 0);
+    std::vector<uint32_t> head(nt, 0);
+    std::vector<uint64_t> head_idx(nt, ~uint64_t(0));
+    const uint64_t chunk_bits = 8ull * C;
+    parallel_for(nt, [&](unsigned t) {
+        const uint64_t j0 = n * t / nt, j1 = n * (t + 1) / nt;
+        uint64_t pos = range_bits[t];
+        uint64_t acc = 0;
+        uint32_t nacc = uint32_t(pos & 31);
+        uint64_t wi = pos >> 5;
+        bool first = true;
+        auto emit = [&](uint64_t w, uint32_t v) {
+            if (first) {
+                head[t] = v;
+                head_idx[t] = w;
+                first = false;
+            } else {
+                store_le<uint32_t>(words + 4 * w, v);
+            }
+        };
+        // Chunk boundaries whose first code start lies in this range.
+        uint64_t lo = j0 == 0 ? 0 : pos - len[exponent_of(src[j0 - 1])] + 1;
+        uint64_t ci = ceil_div(lo, chunk_bits);
+        for (uint64_t j = j0; j < j1; ++j) {
+            const uint16_t b = src[j];
+            const uint32_t e = exponent_of(b);
+            raw[j] = raw_of(b);
+            while (ci * chunk_bits <= pos) {
+                offs[ci] = uint8_t(pos - ci * chunk_bits);
+                if (ci % T == 0) store_le<uint32_t>(blockout + 4 * (ci / T), uint32_t(j));
+                ++ci;
+            }
+            const uint32_t l = len[e];
+            acc = (acc << l) | code[e];
+            nacc += l;
+            pos += l;
+            if (nacc >= 32) {
+                nacc -= 32;
+                emit(wi++, uint32_t(acc >> nacc));
+            }
+        }
+        if (nacc > 0) emit(wi, uint32_t(acc << (32 - nacc)));
+        if (t == nt - 1) {
+            while (ci < L.n_chunks && ci * chunk_bits < total_bits) {
+                offs[ci] = uint8_t(total_bits - ci * chunk_bits);
+                if (ci % T == 0) store_le<uint32_t>(blockout + 4 * (ci / T), uint32_t(n));
+                ++ci;
+            }
+        }
+    });
+    for (unsigned t = 0; t < nt; ++t) {
+        if (head_idx[t] == ~uint64_t(0)) continue;
+        uint8_t *w = words + 4 * head_idx[t];
+        store_le<uint32_t>(w, load_le<uint32_t>(w) | head[t]);
+    }
+    store_le<uint32_t>(blockout + 4 * L.n_blocks, uint32_t(n));
+    // 5-bit offset fields, little-endian bit order.
+    uint8_t *ow = dst + off[kOffsets];
+    for (uint64_t i = 0; i <= L.n_chunks; ++i) {
+        const uint64_t g = kOffsetBits * i;
+        const uint64_t v = uint64_t(offs[i]) << (g & 31);
+        uint8_t *w0 = ow + 4 * (g >> 5);
+        store_le<uint32_t>(w0, load_le<uint32_t>(w0) | uint32_t(v));
+        if (v >> 32) store_le<uint32_t>(w0 + 4, load_le<uint32_t>(w0 + 4) | uint32_t(v >> 32));
+    }
+    *written = blob_bytes;
+    return DFC_OK;
+}
+
+dfc_status dfc_blob_info(const void *blob_v, uint64_t bytes, dfc_info *out) {
+    if (!blob_v || !out) return DFC_EINVAL;
+    const uint8_t *b = static_cast<const uint8_t *>(blob_v);
+    if (bytes < kHeaderBytes) return DFC_ESIZE;
+    if (load_le<uint32_t>(b + hdr::magic) != kMagic) return DFC_ECORRUPT;
+    if (load_le<uint32_t>(b + hdr::version) != kVersion) return DFC_EUNSUPPORTED;
+    dfc_info in;
+    std::memset(&in, 0, sizeof(in));
+    in.n = load_le<uint64_t>(b + hdr::n);
+    in.total_bits = load_le<uint64_t>(b + hdr::total_bits);
+    in.n_chunks = load_le<uint64_t>(b + hdr::n_chunks);
+    in.n_blocks = load_le<uint64_t>(b + hdr::n_blocks);
+    in.chunk_bytes = load_le<uint32_t>(b + hdr::chunk_bytes);
+    in.lanes_per_block = load_le<uint32_t>(b + hdr::lanes);
+    in.max_code_len = load_le<uint32_t>(b + hdr::max_code_len);
+    in.lut_bits = load_le<uint32_t>(b + hdr::lut_bits);
+    in.layout = load_le<uint32_t>(b + hdr::layout);
+    in.rows = load_le<uint64_t>(b + hdr::rows);
+    in.cols = load_le<uint64_t>(b + hdr::cols);
+    in.blob_bytes = load_le<uint64_t>(b + hdr::blob_bytes);
+    if (in.layout != DFC_LAYOUT_FLAT) return DFC_EUNSUPPORTED;
+    dfc_params p;
+    dfc_default_params(&p);
+    p.chunk_bytes = in.chunk_bytes;
+    p.lanes_per_block = in.lanes_per_block;
+    p.max_code_len = in.max_code_len;
+    p.lut_bits = in.lut_bits;
+    if (!params_ok(p)) return DFC_ECORRUPT;
+    if (in.n >= (uint64_t(1) << 32) || in.rows * in.cols != in.n) return DFC_ECORRUPT;
+    if (load_le<uint32_t>(b + hdr::panel_rows) || load_le<uint32_t>(b + hdr::tile_k) ||
+        load_le<uint32_t>(b + hdr::reserved))
+        return DFC_ECORRUPT;
+    for (int i = 192; i < 256; ++i)
+        if (b[i]) return DFC_ECORRUPT;
+
+    // Code lengths: complete code under the limit (or empty for n == 0).
+    const uint8_t *len = b + hdr::lengths;
+    uint32_t used = 0, mn = 0, mx = 0;
+    for (int s = 0; s < 256; ++s) {
+        if (!len[s]) continue;
+        if (len[s] > in.max_code_len) return DFC_ECORRUPT;
+        used++;
+        mn = mn ? std::min<uint32_t>(mn, len[s]) : len[s];
+        mx = std::max<uint32_t>(mx, len[s]);
+    }
+    if (in.n) {
+        if (used < 2 || kraft(len) != (uint64_t(1) << kMaxLen)) return DFC_ECORRUPT;
+        if (in.total_bits < in.n * mn || in.total_bits > in.n * mx) return DFC_ECORRUPT;
+    } else if (in.total_bits) {
+        return DFC_ECORRUPT;
+    }
+    in.n_used = used;
+    in.min_len = mn;
+    in.max_len = mx;
+
+    Layout L = layout_sizes(in.total_bits, in.chunk_bytes, in.lanes_per_block);
+    if (L.n_blocks != in.n_blocks || L.n_chunks != in.n_chunks) return DFC_ECORRUPT;
+    SectionSizes sz = section_sizes(in.n, in.n_chunks, in.n_blocks, in.chunk_bytes, in.lut_bits);
+    uint64_t off[kNumSections];
+    const uint64_t blob_bytes = place_sections(sz, off);
+    if (blob_bytes != in.blob_bytes) return DFC_ECORRUPT;
+    for (int i = 0; i < kNumSections; ++i) {
+        if (load_le<uint64_t>(b + hdr::sections + 16 * i) != off[i]) return DFC_ECORRUPT;
+        if (load_le<uint64_t>(b + hdr::sections + 16 * i + 8) != sz.bytes[i]) return DFC_ECORRUPT;
+    }
+    if (bytes < blob_bytes) return DFC_ESIZE;
+    in.off_tables = off[kTables];
+    in.tables_bytes = sz.bytes[kTables];
+    in.off_words = off[kWords];
+    in.words_bytes = sz.bytes[kWords];
+    in.off_offsets = off[kOffsets];
+    in.offsets_bytes = sz.bytes[kOffsets];
+    in.off_blockout = off[kBlockout];
+    in.blockout_bytes = sz.bytes[kBlockout];
+    in.off_raw = off[kRaw];
+    in.raw_bytes = sz.bytes[kRaw];
+    in.coded_bytes = kHeaderBytes + sz.bytes[kWords] + sz.bytes[kOffsets] + sz.bytes[kBlockout] + sz.bytes[kRaw];
+
+    // Derived tables must match the lengths exactly.
+    {
+        std::vector<uint8_t> t(sz.bytes[kTables], 0);
+        build_tables(len, in.lut_bits, t.data());
+        if (std::memcmp(t.data(), b + off[kTables], t.size()) != 0) return DFC_ECORRUPT;
+    }
+    // Chunk offsets: at most (longest code - 1) for live chunks, 0 elsewhere.
+    {
+        const uint8_t *ow = b + off[kOffsets];
+        const uint64_t chunk_bits = 8ull * in.chunk_bytes;
+        const uint32_t max_off = mx ? mx - 1 : 0;
+        for (uint64_t i = 0; i <= in.n_chunks; ++i) {
+            const uint64_t g = kOffsetBits * i;
+            uint64_t pair = load_le<uint32_t>(ow + 4 * (g >> 5)) |
+                            (uint64_t(load_le<uint32_t>(ow + 4 * (g >> 5) + 4)) << 32);
+            const uint32_t v = uint32_t(pair >> (g & 31)) & 31u;
+            const bool live = i < in.n_chunks && i * chunk_bits < in.total_bits;
+            if (live ? v > max_off : v != 0) return DFC_ECORRUPT;
+        }
+    }
+    // Block offsets: 0 .. n, non-decreasing, each block within LDS staging capacity.
+    {
+        const uint8_t *bo = b + off[kBlockout];
+        if (load_le<uint32_t>(bo) != 0 || load_le<uint32_t>(bo + 4 * in.n_blocks) != in.n) return DFC_ECORRUPT;
+        const uint64_t cap = in.n ? uint64_t(in.lanes_per_block) * ceil_div(8ull * in.chunk_bytes, mn) : 0;
+        uint32_t prev = 0;
+        for (uint64_t k = 1; k <= in.n_blocks; ++k) {
+            uint32_t v = load_le<uint32_t>(bo + 4 * k);
+            if (v < prev || v - prev > cap) return DFC_ECORRUPT;
+            prev = v;
+        }
+    }
+    *out = in;
+    return DFC_OK;
+}
+
+}  // extern "C"

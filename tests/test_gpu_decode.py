@@ -1,0 +1,230 @@
+"""GPU parity of the HIP decoder, called through the C ABI.
+
+Every case compares the kernel's output bit for bit (uint16 views) with the
+original tensor and, at sizes the oracle decodes in seconds, with the
+oracle's own decode of the same container.  Full-size workloads run in the
+launch configuration the benchmark times; there the oracle decodes sampled
+blocks one by one."""
+import sys
+
+import numpy as np
+import pytest
+
+import lossless_entropy_coded_dfc_amd as dfc
+from lossless_entropy_coded_dfc_amd import synth
+from oracle import blob as bl
+from oracle import codebook as cb
+from oracle import fields
+from oracle import stream as st
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    dfc.set_launch(0, 0)
+    yield
+    dfc.set_launch(0, 0)
+
+
+def gpu_decode(blob: np.ndarray, info=None):
+    info = info or dfc.blob_info(blob)
+    dev = torch.from_numpy(np.ascontiguousarray(blob)).cuda()
+    out = torch.empty(int(info.n), dtype=torch.int16, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dfc.decode(dev, info, out, status)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().view(np.uint16), int(status.item())
+
+
+def check(x, C=16, k=12, oracle=True, label=""):
+    say("case", label, x.shape, "C", C, "k", k)
+    blob = dfc.encode(x, chunk_bytes=C, lut_bits=k)
+    got, status = gpu_decode(blob)
+    assert status == 0
+    assert np.array_equal(got, np.asarray(x).ravel()), label
+    if oracle:
+        assert np.array_equal(got, bl.decode_blob(bytes(blob))), label
+    return blob
+
+
+@pytest.mark.parametrize("C", [4, 8, 16, 32])
+def test_single_matrix_small_all_chunks(C):
+    x = synth.gaussian((300, 1000), 0.02, (40, C))   # many blocks, ragged tail
+    for k in (8, 12):
+        check(x, C, k, label=f"gauss300x1000 C{C}")
+
+
+@pytest.mark.parametrize("kind", ["outliers", "uniform", "ladder", "bimodal", "t"])
+def test_distributions_small(kind):
+    shape = (257, 1031)
+    x = {"outliers": lambda: synth.gaussian_with_outliers(shape, 0.02, (41,)),
+         "uniform": lambda: synth.uniform_bits(shape, (42,)),
+         "ladder": lambda: synth.exponent_ladder(shape, (43,)),
+         "bimodal": lambda: synth.bimodal(shape, 0.02, (44,)),
+         "t": lambda: synth.student_t(shape, 3.0, 0.02, (45,))}[kind]()
+    for C in (4, 16, 32):
+        check(x, C, label=kind)
+
+
+def test_edge_sizes():
+    for n in (1, 2, 15, 16, 17, 63, 64, 65, 127, 1000, 4097):
+        for C in (4, 32):
+            check(synth.uniform_bits((n,), (46, n)), C, label=f"n={n}")
+            check(synth.gaussian((n,), 0.02, (47, n)), C, label=f"gauss n={n}")
+
+
+def test_empty_tensor_is_noop():
+    blob = dfc.encode(np.zeros(0, dtype=np.uint16))
+    info = dfc.blob_info(blob)
+    dev = torch.from_numpy(blob).cuda()
+    out = torch.empty(0, dtype=torch.int16, device="cuda")
+    dfc.decode(dev, info, out)
+    torch.cuda.synchronize()
+
+
+def test_constant_and_special_values():
+    check(np.full((100, 100), 0x3F80, dtype=np.uint16), 4, label="constant")
+    specials = np.array([0x7FC1, 0xFF81, 0x7F80, 0xFF80, 0x0000, 0x8000, 0x0001, 0x807F], dtype=np.uint16)
+    x = np.tile(specials, 5000)
+    check(x, 8, label="specials")
+
+
+def test_long_codes_everywhere():
+    """Uniform data under a codebook trained on Gaussian weights: most codes
+    are longer than the first-level table (slow path on every lane)."""
+    g = synth.gaussian((512, 512), 0.02, (48,))
+    h = cb.histogram(fields.split(g)[0]) + 1
+    book = dfc.build_codebook(h, 24)
+    assert book.max_len == 24 or book.max_len > 12
+    x = synth.uniform_bits((200, 999), (49,))
+    for C in (4, 16, 32):
+        blob = dfc.encode(x, chunk_bytes=C, codebook=book)
+        got, status = gpu_decode(blob)
+        assert status == 0 and np.array_equal(got, x.ravel())
+        assert np.array_equal(got, bl.decode_blob(bytes(blob)))
+
+
+def test_oracle_written_container_decodes():
+    x = synth.gaussian_with_outliers((123, 4567), 0.02, (50,))
+    for C in (8, 16):
+        blob = np.frombuffer(bl.write_blob(st.encode(x, C, 64), 12, 123, 4567), dtype=np.uint8)
+        got, status = gpu_decode(blob)
+        assert status == 0 and np.array_equal(got, x.ravel())
+
+
+@pytest.mark.parametrize("waves,bpw", [(4, 1), (8, 1), (8, 3), (16, 2), (4, 16)])
+def test_launch_shapes(waves, bpw):
+    dfc.set_launch(waves, bpw)
+    try:
+        x = synth.gaussian((700, 1024), 0.02, (51,))
+        check(x, 16, oracle=False, label=f"launch {waves}x{bpw}")
+    finally:
+        dfc.set_launch(0, 0)
+
+
+def test_status_flags_count_mismatch():
+    x = synth.gaussian((64, 4096), 0.02, (52,))
+    blob = dfc.encode(x)
+    info = dfc.blob_info(blob)
+    bad = blob.copy()
+    # the host accepts this (same block count) but the decoded count changes
+    import struct
+    bad[16:24] = np.frombuffer(struct.pack("<Q", info.total_bits + 3), dtype=np.uint8)
+    binfo = dfc.blob_info(bad)
+    got, status = gpu_decode(bad, binfo)
+    assert status != 0
+    # a flipped stream bit either changes a count or changes a value
+    flip = blob.copy()
+    flip[info.off_words + 1000] ^= 0x10
+    got, status = gpu_decode(flip, info)
+    assert status != 0 or not np.array_equal(got, x.ravel())
+
+
+def test_invalid_arguments_rejected():
+    x = synth.gaussian((16, 64), 0.02, (53,))
+    blob = dfc.encode(x)
+    info = dfc.blob_info(blob)
+    dev = torch.from_numpy(blob).cuda()
+    out = torch.empty(info.n + 8, dtype=torch.int16, device="cuda")
+    lib = dfc.library()
+    s = lib.dfc_decode(dev.data_ptr(), info, out.data_ptr() + 2, info.n, None, None)   # misaligned dst
+    assert s == dfc.EINVAL
+    s = lib.dfc_decode(dev.data_ptr(), info, out.data_ptr(), info.n + 1, None, None)
+    assert s == dfc.ESIZE
+    b128 = dfc.encode(x, lanes=128)
+    s = lib.dfc_decode(torch.from_numpy(b128).cuda().data_ptr(), dfc.blob_info(b128),
+                                 out.data_ptr(), info.n, None, None)
+    assert s == dfc.EUNSUPPORTED
+
+
+# ---------------------------------------------------------------- full size
+
+def sampled_oracle_check(blob, got, n_samples=6, seed=0):
+    """Decode a few whole blocks with the oracle's chunk decoder and compare
+    the GPU output at those positions."""
+    p = bl.parse_blob(bytes(blob))
+    rng = np.random.default_rng(seed)
+    C = p["chunk_bytes"]
+    picks = sorted(set(rng.integers(0, p["n_blocks"], size=n_samples).tolist()) | {p["n_blocks"] - 1})
+    for b in picks:
+        c0 = 64 * b
+        lo = p["out"][b]
+        hi = p["out"][b + 1]
+        # decode chunks of block b by slicing the stream to that block
+        words = p["words"][c0 * C // 4:]
+        off = p["off"][c0:]
+        e = st.decode_chunked(words, off, p["total_bits"] - 8 * C * c0, C, 64, p["lengths"])
+        assert e.size == hi - lo
+        want = fields.merge(e, p["raw"][lo:hi])
+        assert np.array_equal(got[lo:hi], want), b
+
+
+def test_full_single_matrix_4096():
+    x = synth.single_matrix()
+    for C in (16, 32):
+        say("full 4096x4096 C", C)
+        blob = dfc.encode(x, chunk_bytes=C)
+        got, status = gpu_decode(blob)
+        assert status == 0 and np.array_equal(got, x.ravel())
+        sampled_oracle_check(blob, got)
+
+
+def test_full_llama_block_batched():
+    """The benchmark's workload and launch: one Llama-3-8B block, seven
+    matrices, one batched launch."""
+    mats = list(synth.llama3_8b_block())
+    blobs, infos, devs, outs = [], [], [], []
+    for name, x in mats:
+        say("encode", name, x.shape)
+        b = dfc.encode(x)
+        blobs.append(b)
+        infos.append(dfc.blob_info(b))
+        devs.append(torch.from_numpy(b).cuda())
+        outs.append(torch.empty(x.size, dtype=torch.int16, device="cuda"))
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dfc.decode_batch(list(zip(devs, infos, outs)), status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    for (name, x), out, b in zip(mats, outs, blobs):
+        got = out.cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, x.ravel()), name
+        sampled_oracle_check(b, got, n_samples=3)
+
+
+@pytest.mark.parametrize("kind", list(synth.STRESS_KINDS))
+def test_full_stress_8192x28672(kind):
+    say("stress", kind)
+    x = synth.stress(kind)
+    for C in ((4, 16, 32) if kind == "student_t" else (16,)):
+        blob = dfc.encode(x, chunk_bytes=C)
+        got, status = gpu_decode(blob)
+        assert status == 0 and np.array_equal(got, x.ravel()), (kind, C)
+    sampled_oracle_check(blob, got, n_samples=2)
