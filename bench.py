@@ -123,7 +123,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama3-8b-block")
     ap.add_argument("--chunk-bytes", type=int, default=16)
-    ap.add_argument("--lut-bits", type=int, default=12)
+    ap.add_argument("--lut-bits", type=int, default=11)
     ap.add_argument("--sets", type=int, default=2, help="rotating buffer sets (defeats the 256 MB MALL)")
     ap.add_argument("--waves", type=int, default=0)
     ap.add_argument("--bpw", type=int, default=0)

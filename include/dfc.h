@@ -56,7 +56,8 @@ typedef struct {
     uint32_t chunk_bytes;     /* C: bytes of code stream per lane: 4, 8, 16 or 32 (default 16) */
     uint32_t lanes_per_block; /* T: chunks per block: 64 (default; one wavefront), 128 or 256 */
     uint32_t max_code_len;    /* code length limit, 1..24 (default 24) */
-    uint32_t lut_bits;        /* k: bits indexed by the first-level decode table, 8..12 (default 12) */
+    uint32_t lut_bits;        /* k: bits indexed by the first-level decode table, 8..12 (default 11);
+                                 the container records min(k, 8 * shortest code length) */
     uint32_t layout;          /* DFC_LAYOUT_FLAT: elements in row-major order */
     uint32_t threads;         /* host encoder threads; 0 = min(hardware threads, 16) */
     uint64_t rows, cols;      /* matrix shape recorded in the header; 0,0 = 1 x n */
@@ -86,6 +87,7 @@ typedef struct {
     uint64_t off_raw, raw_bytes;
     uint32_t chunk_bytes, lanes_per_block, max_code_len, lut_bits, layout;
     uint32_t n_used, min_len, max_len;
+    uint32_t max_block_elems;  /* most elements any one block decodes */
 } dfc_info;
 
 /* One matrix of a batched decode. */
@@ -96,7 +98,7 @@ typedef struct {
     uint64_t n;            /* must equal info->n */
 } dfc_batch_item;
 
-/* Fills *p with the defaults (C = 16, T = 64, limit 24, k = 12, flat). */
+/* Fills *p with the defaults (C = 16, T = 64, limit 24, k = 11, flat). */
 void dfc_default_params(dfc_params *p);
 
 /* 256-bin histogram of the exponent bits (bits 14..7) of n bf16 values.

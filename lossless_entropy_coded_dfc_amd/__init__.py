@@ -69,7 +69,7 @@ class Info(ctypes.Structure):
         "off_blockout", "blockout_bytes", "off_raw", "raw_bytes")] + \
         [(name, ctypes.c_uint32) for name in (
             "chunk_bytes", "lanes_per_block", "max_code_len", "lut_bits", "layout",
-            "n_used", "min_len", "max_len")]
+            "n_used", "min_len", "max_len", "max_block_elems")]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -179,7 +179,7 @@ def encode_bound(n: int, params: Params | None = None) -> int:
     return out.value
 
 
-def encode(bits, chunk_bytes: int = 16, lanes: int = 64, max_code_len: int = 24, lut_bits: int = 12,
+def encode(bits, chunk_bytes: int = 16, lanes: int = 64, max_code_len: int = 24, lut_bits: int = 11,
            codebook: Codebook | None = None, threads: int = 0, shape=None) -> np.ndarray:
     """Encode bf16 bit patterns (any shape, row-major) into a DFC1 container
     (numpy uint8 array)."""

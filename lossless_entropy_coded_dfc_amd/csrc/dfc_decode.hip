@@ -2,26 +2,30 @@
 //
 // DFloat11 blog ("70% Size, 100% Accuracy ... (DFloat11)"), section 03:
 //   item 1: compact hierarchical lookup tables in on-chip memory find code
-//           boundaries fast -> the first-level k-bit table and the per-length
-//           canonical tables are copied into LDS by every workgroup;
+//           boundaries fast -> the first-level k-bit tables (step, symbols,
+//           boundary mask) and the per-length canonical tables for longer
+//           codes are copied into LDS once per workgroup;
 //   item 2: a two-phase kernel; in phase one threads agree on read and write
 //           positions through small auxiliary variables, phase two rebuilds
 //           the weights -> per-chunk start offsets and per-block output
 //           offsets come from the container, each lane counts the codes of
 //           its chunk, a wavefront prefix scan turns counts into write
-//           positions, and the exponents are written to LDS and merged with
-//           the raw bytes into bf16 with coalesced 16-byte stores.
+//           positions, the exponents go to LDS and are merged with the raw
+//           bytes into bf16 with coalesced 16-byte stores.
 //
 // Work decomposition: one lane per chunk (C bytes of code stream), one
-// wavefront (64 lanes) per block of 64 chunks, several wavefronts per
-// workgroup sharing one LDS copy of the decode tables.  All decoding is
-// integer work on bit patterns.
+// wavefront (64 lanes) per block of 64 chunks.  Workgroups are persistent:
+// the grid is sized to the resident capacity of the GPU, each workgroup owns
+// a contiguous run of blocks of one matrix, and its wavefronts take those
+// blocks in turn while prefetching the next block's stream words, offsets
+// and raw bytes.  All decoding is integer work on bit patterns.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
 #include <mutex>
+#include <vector>
 
 #include "dfc.h"
 #include "dfc_format.h"
@@ -29,6 +33,13 @@
 namespace {
 
 constexpr int kWave = 64;
+// Accumulator = (codes << 16) + (kBias + shift), shift = bits from the
+// current position to the end of the current 32-bit word pair's first word.
+// kBias keeps the low half from borrowing and is a multiple of 32, so the
+// low 5 bits of the accumulator are the funnel-shift amount.
+constexpr uint32_t kBias = 0x8000u;
+constexpr uint32_t kEscape = dfc::kStepEscape;
+constexpr int kMaxWaves = 16;
 
 struct ItemArgs {
     const uint32_t *words;     // code stream
@@ -40,57 +51,68 @@ struct ItemArgs {
     uint64_t total_bits;
     uint32_t n_blocks;
     uint32_t wg_begin;         // first workgroup of this item in the grid
+    uint32_t blocks_per_wg;
     uint32_t tables_bytes;     // multiple of 16
     uint32_t lut_bits;
+    uint32_t pad;
 };
 
 struct BatchArgs {
     ItemArgs item[DFC_MAX_BATCH];
     uint32_t count;
-    uint32_t blocks_per_wave;
-    uint32_t stage_bytes;  // LDS exponent staging per wavefront
-    uint32_t pad;
+    uint32_t stage_bytes;  // LDS exponent staging per wavefront (multiple of 16)
     uint32_t *status;
 };
 
-// LDS views of the per-length canonical tables (index = code length).
-struct Tabs {
+struct Tables {
+    const uint32_t *step;
+    const uint2 *sym;
+    const uint16_t *mask;
     const uint32_t *limit, *first, *base;
     const uint8_t *order;
+    uint32_t kshift;  // 32 - k
+    uint32_t kb;
 };
 
-// Codes longer than the first-level table: the smallest length l with
+__device__ __forceinline__ uint32_t lo16(uint32_t a) { return a & 0xFFFFu; }
+
+// Codes longer than the first-level window: the smallest length l with
 // window < limit[l] (left-justified 24-bit comparison), then the symbol by
-// canonical rank.
-__device__ __forceinline__ uint32_t long_code(uint32_t w24, int kb, const Tabs &t, uint32_t &sym) {
-    uint32_t l = uint32_t(kb) + 1;
+// canonical rank.  Returns the length; sym receives the rotated exponent.
+__device__ __forceinline__ uint32_t long_code(uint32_t w24, const Tables &t, uint32_t &sym) {
+    uint32_t l = t.kb + 1;
     while (l < 24u && w24 >= t.limit[l]) ++l;
-    sym = t.order[t.base[l] + (w24 >> (24u - l)) - t.first[l]];
+    const uint32_t e = t.order[t.base[l] + (w24 >> (24u - l)) - t.first[l]];
+    sym = ((e >> 1) | (e << 7)) & 0xFFu;
     return l;
 }
 
-// 5-bit chunk start offset i (little-endian bit array of u32 words).
-__device__ __forceinline__ uint32_t off_field(const uint32_t *ow, uint64_t i) {
-    const uint64_t g = 5ull * i;
-    const uint32_t *p = ow + (g >> 5);
-    return __builtin_amdgcn_alignbit(p[1], p[0], uint32_t(g & 31)) & 31u;
-}
-
+// Per-lane view of one chunk: its words plus two lookahead words, the start
+// offset of its first code and the end of its last code (chunk-relative
+// bits), and the block's output range.
 template <int C>
 struct Chunk {
     static constexpr int NW = C / 4;
-    uint32_t w[NW + 1];  // the chunk's words plus one lookahead word
+    uint32_t w[NW + 2];
+    uint32_t o0, o1;  // the two offset-array words holding this chunk's field and the next
+    uint32_t meta;    // lane 0: out[b], lane 1: out[b + 1]
 };
 
 template <int C>
-__device__ __forceinline__ void load_chunk(const uint32_t *words, uint64_t chunk, Chunk<C> &ck) {
-    const uint32_t *p = words + chunk * (C / 4);
+__device__ __forceinline__ void load_chunk(const ItemArgs &a, uint32_t b, uint32_t lane, Chunk<C> &ck) {
+    const uint64_t chunk = uint64_t(b) * kWave + lane;
+    const uint32_t *p = a.words + chunk * (C / 4);
     if constexpr (C == 4) {
         ck.w[0] = p[0];
+        ck.w[1] = p[1];
+        ck.w[2] = p[2];
     } else if constexpr (C == 8) {
         const uint2 v = *reinterpret_cast<const uint2 *>(p);
+        const uint2 u = *reinterpret_cast<const uint2 *>(p + 2);
         ck.w[0] = v.x;
         ck.w[1] = v.y;
+        ck.w[2] = u.x;
+        ck.w[3] = u.y;
     } else {
 #pragma unroll
         for (int q = 0; q < C / 16; ++q) {
@@ -100,165 +122,252 @@ __device__ __forceinline__ void load_chunk(const uint32_t *words, uint64_t chunk
             ck.w[4 * q + 2] = v.z;
             ck.w[4 * q + 3] = v.w;
         }
+        const uint2 u = *reinterpret_cast<const uint2 *>(p + C / 4);
+        ck.w[C / 4] = u.x;
+        ck.w[C / 4 + 1] = u.y;
     }
-    ck.w[C / 4] = p[C / 4];
+    // Only loads here: combining the words right away would make the
+    // compiler wait for every load in flight, prefetches included.
+    const uint32_t *o = a.offw + ((5ull * chunk) >> 5);
+    ck.o0 = o[0];
+    ck.o1 = o[1];
+    ck.meta = a.blockout[b + min(lane, 1u)];
 }
 
-// Phase one: number of codes that start in [start, end) of this chunk (bit
-// positions relative to the chunk's first bit).  The k-loop walks the chunk
-// one 32-bit word at a time so that every window is a funnel shift of two
-// registers: a code starting at pos in (32k, 32k + 32] lies inside words
-// k and k + 1.  Each lookup counts every code that fits in the k-bit window
-// (popcount of the boundary mask); the last lookup may count codes that
-// start at or after `end`, which are subtracted at the end.
-template <int C>
-__device__ __forceinline__ int count_codes(const Chunk<C> &ck, int start, int end, const uint2 *lut, int kb,
-                                           const Tabs &t) {
-    int pos = start, cnt = 0, last_pos = 0;
-    uint32_t last_mask = 0;
-    const uint32_t kshift = 32u - uint32_t(kb);
+// 32 stream bits starting at chunk-relative bit pos, 0 <= pos <= 32 (NW + 1).
+template <int NW>
+__device__ __forceinline__ uint32_t window_at(const uint32_t (&w)[NW + 2], uint32_t pos) {
+    const uint32_t j = (pos + 31) >> 5;  // pos in (32 (j - 1), 32 j]
+    uint32_t hi = 0, lo = w[0];
 #pragma unroll
-    for (int k = -1; k < C / 4; ++k) {
-        const uint32_t hi = k < 0 ? 0u : ck.w[k < 0 ? 0 : k];
-        const uint32_t lo = ck.w[k + 1];
-        const int top = 32 * (k + 1);
-        const int lim = min(end, top + 1);
-        while (pos < lim) {
-            const uint32_t win = __builtin_amdgcn_alignbit(hi, lo, uint32_t(top - pos));
-            const uint32_t eh = lut[win >> kshift].y;
-            const uint32_t mask = (eh >> 8) & 0xFFFu;
-            if (mask == 0u) {
-                uint32_t sym;
-                pos += int(long_code(win >> 8, kb, t, sym));
-                cnt += 1;
-                last_mask = 0;
-            } else {
-                cnt += __popc(mask);
-                last_pos = pos;
-                last_mask = mask;
-                pos += int((eh >> 20) & 0xFu);
-            }
+    for (int q = 1; q <= NW + 1; ++q) {
+        if (j == uint32_t(q)) {
+            hi = w[q - 1];
+            lo = w[q];
         }
     }
-    if (pos > end && last_mask) cnt -= __popc(last_mask >> uint32_t(end - last_pos));
+    return __builtin_amdgcn_alignbit(hi, lo, 32u * j - pos);
+}
+
+// Phase one: number of codes that start in [start, end) (chunk-relative).
+// The k-loop walks the chunk one word at a time so that every window is a
+// funnel shift of two registers: a code starting at pos in (32k, 32k + 32]
+// lies inside words k and k + 1.  Each lookup adds step = (codes << 16) -
+// bits for every whole code inside the k-bit window; the last lookup may
+// count codes that start at or after `end`, which are removed with the
+// boundary mask of the window that starts at `end`.
+template <int C>
+__device__ __forceinline__ uint32_t count_codes(const Chunk<C> &ck, int start, int end, const Tables &t) {
+    constexpr int NW = C / 4;
+    uint32_t acc = kBias - uint32_t(start);
+#pragma unroll
+    for (int k = -1; k < NW; ++k) {
+        const uint32_t hi = k < 0 ? 0u : ck.w[k < 0 ? 0 : k];
+        const uint32_t lo = ck.w[k + 1];
+        // stay while shift >= 0 (pos <= 32 (k + 1)) and pos < end
+        const uint16_t g = uint16_t(kBias + uint32_t(max(0, 32 * (k + 1) - end + 1)));
+        for (;;) {
+            while (uint16_t(acc) >= g) {
+                const uint32_t win = __builtin_amdgcn_alignbit(hi, lo, acc);
+                acc += t.step[win >> t.kshift];
+            }
+            if (lo16(acc) >= kBias - 2048u) break;
+            // escape: the code at pos is longer than the window
+            acc += 0x1000u;
+            uint32_t sym;
+            const uint32_t win = __builtin_amdgcn_alignbit(hi, lo, acc);
+            acc += 0x10000u - long_code(win >> 8, t, sym);
+        }
+        acc += 32u;
+    }
+    uint32_t cnt = acc >> 16;
+    const int pos = 32 * (NW + 1) - int(lo16(acc)) + int(kBias);
+    if (pos > end) {
+        const uint32_t we = window_at<NW>(ck.w, uint32_t(end));
+        cnt -= __popc(uint32_t(t.mask[we >> t.kshift]) & ((1u << (pos - end)) - 1u));
+    }
     return cnt;
 }
 
-// Phase two: decode the chunk again and write its `cnt` exponents to LDS.
-// While four or more codes remain, all four symbol bytes of a lookup are
-// stored: bytes past the lookup's own symbols land on positions this lane
-// writes again in its next lookup.
+__device__ __forceinline__ void store_u64_unaligned(uint8_t *p, uint2 v) {
+    struct __attribute__((packed, aligned(1))) U64 {
+        uint32_t x, y;
+    };
+    reinterpret_cast<U64 *>(p)->x = v.x;
+    reinterpret_cast<U64 *>(p)->y = v.y;
+}
+
+// Writes the first r (1..7) bytes of v to p.
+__device__ __forceinline__ void store_tail(uint8_t *p, uint2 v, uint32_t r) {
+    struct __attribute__((packed, aligned(1))) U32 {
+        uint32_t x;
+    };
+    struct __attribute__((packed, aligned(1))) U16 {
+        uint16_t x;
+    };
+    uint32_t lo = v.x;
+    if (r & 4u) {
+        reinterpret_cast<U32 *>(p)->x = lo;
+        p += 4;
+        lo = v.y;
+    }
+    if (r & 2u) {
+        reinterpret_cast<U16 *>(p)->x = uint16_t(lo);
+        p += 2;
+        lo >>= 16;
+    }
+    if (r & 1u) *p = uint8_t(lo);
+}
+
+// Phase two: decode the chunk again and write its cnt (rotated) exponents to
+// LDS.  While 8 or more codes remain, all 8 symbol bytes of a lookup are
+// stored: the bytes past the lookup's own codes fall on positions this lane
+// overwrites with its next lookup.  The last < 8 codes are written exactly.
 template <int C>
-__device__ __forceinline__ void write_codes(const Chunk<C> &ck, int start, int cnt, uint8_t *out,
-                                            const uint2 *lut, int kb, const Tabs &t) {
-    int pos = start, done = 0;
-    const uint32_t kshift = 32u - uint32_t(kb);
+__device__ __forceinline__ void write_codes(const Chunk<C> &ck, int start, uint32_t cnt, uint8_t *out,
+                                            const Tables &t) {
+    constexpr int NW = C / 4;
+    uint32_t acc = kBias - uint32_t(start);
+    const uint32_t lim = cnt >= 8u ? (cnt - 7u) << 16 : 0u;  // acc < lim <=> done <= cnt - 8
 #pragma unroll
-    for (int k = -1; k < C / 4; ++k) {
+    for (int k = -1; k < NW; ++k) {
         const uint32_t hi = k < 0 ? 0u : ck.w[k < 0 ? 0 : k];
         const uint32_t lo = ck.w[k + 1];
-        const int top = 32 * (k + 1);
-        while (done < cnt && pos <= top) {
-            const uint32_t win = __builtin_amdgcn_alignbit(hi, lo, uint32_t(top - pos));
-            const uint2 e = lut[win >> kshift];
-            const int ns = int(e.y & 0xFu);
-            if (ns == 0) {
-                uint32_t sym;
-                pos += int(long_code(win >> 8, kb, t, sym));
-                out[done] = uint8_t(sym);
-                done += 1;
-            } else if (cnt - done >= 4) {
-                out[done + 0] = uint8_t(e.x);
-                out[done + 1] = uint8_t(e.x >> 8);
-                out[done + 2] = uint8_t(e.x >> 16);
-                out[done + 3] = uint8_t(e.x >> 24);
-                done += ns;
-                pos += int((e.y >> 4) & 0xFu);
-            } else {
-                const int take = min(ns, cnt - done);
-                out[done] = uint8_t(e.x);
-                if (take > 1) out[done + 1] = uint8_t(e.x >> 8);
-                if (take > 2) out[done + 2] = uint8_t(e.x >> 16);
-                done += take;
-                pos += int((e.y >> 4) & 0xFu);
+        for (;;) {
+            while (uint16_t(acc) >= uint16_t(kBias) && acc < lim) {
+                const uint32_t win = __builtin_amdgcn_alignbit(hi, lo, acc);
+                const uint32_t idx = win >> t.kshift;
+                const uint32_t d = t.step[idx];
+                store_u64_unaligned(out + (acc >> 16), t.sym[idx]);
+                acc += d;
             }
+            if (lo16(acc) >= kBias - 2048u) break;
+            acc += 0x1000u;
+            uint32_t sym;
+            const uint32_t win = __builtin_amdgcn_alignbit(hi, lo, acc);
+            const uint32_t l = long_code(win >> 8, t, sym);
+            out[acc >> 16] = uint8_t(sym);
+            acc += 0x10000u - l;
+        }
+        acc += 32u;
+    }
+    uint32_t done = acc >> 16;
+    uint32_t pos = uint32_t(32 * (NW + 1)) - lo16(acc) + kBias;
+    while (done < cnt && pos < uint32_t(32 * (NW + 1))) {
+        const uint32_t win = window_at<NW>(ck.w, pos);
+        const uint32_t idx = win >> t.kshift;
+        const uint32_t d = t.step[idx];
+        if (d == kEscape) {
+            uint32_t sym;
+            pos += long_code(win >> 8, t, sym);
+            out[done] = uint8_t(sym);
+            done += 1;
+        } else {
+            const uint32_t r = min((d >> 16) + 1u, cnt - done);
+            store_tail(out + done, t.sym[idx], r);
+            done += r;
+            pos += 0x10000u - (d & 0xFFFFu);
         }
     }
 }
 
-__device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const int u = __shfl_up(v, d, kWave);
-        if (lane >= d) v += u;
-    }
-    return v;
+// Inclusive prefix sum across the wavefront (DPP row shifts, then row
+// broadcasts 15 and 31).
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
+    x += uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x111, 0xf, 0xf, false));  // row_shr:1
+    x += uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x112, 0xf, 0xf, false));  // row_shr:2
+    x += uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x114, 0xf, 0xf, false));  // row_shr:4
+    x += uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x118, 0xf, 0xf, false));  // row_shr:8
+    x += uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x142, 0xa, 0xf, false));  // row_bcast:15
+    x += uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x143, 0xc, 0xf, false));  // row_bcast:31
+    return x;
 }
 
-// Two bf16 values from the pair x = [raw_a, exp_a, raw_b, exp_b] (bytes, low
-// to high): sign from raw bit 7, exponent, mantissa from raw bits 6..0.
-__device__ __forceinline__ uint32_t bf16_pair(uint32_t x) {
-    return ((x >> 1) & 0x7F807F80u) | (x & 0x007F007Fu) | ((x << 8) & 0x80008000u);
-}
-
+// 16 bf16 values from 16 staged (rotated) exponents and 16 raw bytes.  Per
+// pair of values, x1 = [raw_a, exp_a, raw_b, exp_b] and x2 = [exp_a, raw_a,
+// exp_b, raw_b] (bytes, low first); each output byte keeps bits 6..0 of x1
+// and bit 7 of x2.
 __device__ __forceinline__ void assemble16(const uint4 &E, const uint4 &R, uint32_t o[8]) {
     const uint32_t e[4] = {E.x, E.y, E.z, E.w};
     const uint32_t r[4] = {R.x, R.y, R.z, R.w};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const uint32_t lo = (r[q] & 0xFFu) | ((e[q] & 0xFFu) << 8) | ((r[q] & 0xFF00u) << 8) | ((e[q] & 0xFF00u) << 16);
-        const uint32_t hi = ((r[q] >> 16) & 0xFFu) | ((e[q] >> 8) & 0xFF00u) | ((r[q] >> 8) & 0xFF0000u) |
-                            (e[q] & 0xFF000000u);
-        o[2 * q] = bf16_pair(lo);
-        o[2 * q + 1] = bf16_pair(hi);
+        const uint32_t a1 = __builtin_amdgcn_perm(e[q], r[q], 0x05010400u);
+        const uint32_t a2 = __builtin_amdgcn_perm(e[q], r[q], 0x01050004u);
+        const uint32_t b1 = __builtin_amdgcn_perm(e[q], r[q], 0x07030602u);
+        const uint32_t b2 = __builtin_amdgcn_perm(e[q], r[q], 0x03070206u);
+        o[2 * q] = (a1 & 0x7F7F7F7Fu) | (a2 & 0x80808080u);
+        o[2 * q + 1] = (b1 & 0x7F7F7F7Fu) | (b2 & 0x80808080u);
     }
 }
 
+__device__ __forceinline__ void store_group(const ItemArgs &a, uint32_t g, uint32_t s_out, uint32_t e_out,
+                                            const uint32_t o[8]) {
+    const uint32_t j0 = 16u * g;
+    uint16_t *d = a.dst + j0;
+    if (j0 >= s_out && j0 + 16u <= e_out) {
+        reinterpret_cast<uint4 *>(d)[0] = make_uint4(o[0], o[1], o[2], o[3]);
+        reinterpret_cast<uint4 *>(d)[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    } else {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const uint32_t j = j0 + uint32_t(q);
+            if (j >= s_out && j < e_out) d[q] = uint16_t(o[q >> 1] >> (16 * (q & 1)));
+        }
+    }
+}
+
+// Raw-byte groups prefetched into registers per lane before decoding.
 template <int C>
-__device__ __forceinline__ void decode_block(const ItemArgs &a, uint32_t b, int lane, uint8_t *stage,
-                                             const uint2 *lut, const Tabs &t, uint32_t *status) {
-    const uint64_t chunk = uint64_t(b) * kWave + uint32_t(lane);
-    Chunk<C> ck;
-    load_chunk<C>(a.words, chunk, ck);
-    const int start = int(off_field(a.offw, chunk));
-    const int next_off = int(off_field(a.offw, chunk + 1));
-    const uint32_t s_out = __builtin_amdgcn_readfirstlane(a.blockout[b]);
-    const uint32_t e_out = __builtin_amdgcn_readfirstlane(a.blockout[b + 1]);
+struct Prefetch {
+    static constexpr int N = C >= 32 ? 6 : C / 4;
+};
+
+template <int C>
+__device__ __forceinline__ void decode_block(const ItemArgs &a, uint32_t b, uint32_t lane, const Chunk<C> &ck,
+                                             uint8_t *stage, const Tables &t, uint32_t *status,
+                                             const uint4 (&R)[Prefetch<C>::N], uint32_t s_out,
+                                             uint32_t e_out) {
+    constexpr int PF = Prefetch<C>::N;
+    const uint64_t chunk = uint64_t(b) * kWave + lane;
+    const uint32_t offpair = __builtin_amdgcn_alignbit(ck.o1, ck.o0, uint32_t((5ull * chunk) & 31));
+    const int start = int(offpair & 31u);
+    const int next_off = int((offpair >> 5) & 31u);
     const int64_t rem = int64_t(a.total_bits) - int64_t(chunk * (8ull * C));
     const int end = int(min(int64_t(8 * C + next_off), max(rem, int64_t(-1))));
-    const int kb = int(a.lut_bits);
 
-    const int cnt = start < end ? count_codes<C>(ck, start, end, lut, kb, t) : 0;
-    const int incl = wave_inclusive_scan(cnt, lane);
-    const int total = __shfl(incl, kWave - 1, kWave);
-    if (uint32_t(total) != e_out - s_out) {
+    const uint32_t cnt = start < end ? count_codes<C>(ck, start, end, t) : 0u;
+    const uint32_t incl = wave_inclusive_scan(cnt);
+    const uint32_t total = __builtin_amdgcn_readlane(incl, kWave - 1);
+    // A chunk of 8C bits holds at most 8C code starts; anything else (or a
+    // total that disagrees with the block offsets) means a corrupt stream.
+    if (total != e_out - s_out || __builtin_amdgcn_ballot_w64(cnt > 8u * C) != 0) {
         if (lane == 0 && status) atomicOr(status, 1u);
         return;
     }
     const uint32_t lead = s_out & 15u;
-    if (cnt) write_codes<C>(ck, start, cnt, stage + lead + uint32_t(incl - cnt), lut, kb, t);
+    if (cnt) write_codes<C>(ck, start, cnt, stage + lead + (incl - cnt), t);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
     const uint32_t g0 = s_out >> 4, g1 = (e_out + 15u) >> 4;
-    for (uint32_t g = g0 + uint32_t(lane); g < g1; g += kWave) {
-        const uint4 E = *reinterpret_cast<const uint4 *>(stage + 16u * (g - g0));
-        const uint4 R = *reinterpret_cast<const uint4 *>(a.raw + 16ull * g);
-        uint32_t o[8];
-        assemble16(E, R, o);
-        const uint32_t j0 = 16u * g;
-        uint16_t *d = a.dst + j0;
-        if (j0 >= s_out && j0 + 16u <= e_out) {
-            reinterpret_cast<uint4 *>(d)[0] = make_uint4(o[0], o[1], o[2], o[3]);
-            reinterpret_cast<uint4 *>(d)[1] = make_uint4(o[4], o[5], o[6], o[7]);
-        } else {
 #pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                const uint32_t j = j0 + uint32_t(q);
-                if (j >= s_out && j < e_out) d[q] = uint16_t(o[q >> 1] >> (16 * (q & 1)));
-            }
+    for (int j = 0; j < PF; ++j) {
+        const uint32_t g = g0 + lane + uint32_t(kWave * j);
+        if (g < g1) {
+            const uint4 E = *reinterpret_cast<const uint4 *>(stage + 16u * (g - g0));
+            uint32_t o[8];
+            assemble16(E, R[j], o);
+            store_group(a, g, s_out, e_out, o);
         }
+    }
+    for (uint32_t g = g0 + lane + uint32_t(kWave * PF); g < g1; g += kWave) {
+        const uint4 E = *reinterpret_cast<const uint4 *>(stage + 16u * (g - g0));
+        const uint4 Rg = *reinterpret_cast<const uint4 *>(a.raw + 16ull * g);
+        uint32_t o[8];
+        assemble16(E, Rg, o);
+        store_group(a, g, s_out, e_out, o);
     }
     // The next block reuses this wavefront's staging area.
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -269,6 +378,7 @@ __device__ __forceinline__ void decode_block(const ItemArgs &a, uint32_t b, int 
 template <int C>
 __global__ __launch_bounds__(1024) void dfc_decode_kernel(const BatchArgs args) {
     extern __shared__ __align__(16) uint8_t lds[];
+    constexpr int PF = Prefetch<C>::N;
     const uint32_t wg = blockIdx.x;
     uint32_t it = 0;
     for (uint32_t k = 1; k < args.count; ++k)
@@ -280,24 +390,48 @@ __global__ __launch_bounds__(1024) void dfc_decode_kernel(const BatchArgs args) 
         *reinterpret_cast<uint4 *>(lds + o) = *reinterpret_cast<const uint4 *>(a.tables + o);
     __syncthreads();
 
-    const int kb = int(a.lut_bits);
-    const uint2 *lut = reinterpret_cast<const uint2 *>(lds);
-    Tabs t;
-    t.limit = reinterpret_cast<const uint32_t *>(lds + (8u << kb));
+    Tables t;
+    t.kb = a.lut_bits;
+    t.kshift = 32u - t.kb;
+    t.step = reinterpret_cast<const uint32_t *>(lds);
+    t.sym = reinterpret_cast<const uint2 *>(lds + (4u << t.kb));
+    t.mask = reinterpret_cast<const uint16_t *>(lds + (12u << t.kb));
+    t.limit = reinterpret_cast<const uint32_t *>(lds + (14u << t.kb));
     t.first = t.limit + 32;
     t.base = t.limit + 64;
-    t.order = lds + (8u << kb) + 384;
+    t.order = lds + (14u << t.kb) + 384;
 
     const uint32_t waves = blockDim.x / kWave;
-    const uint32_t wave = threadIdx.x / kWave;
-    const int lane = int(threadIdx.x % kWave);
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const uint32_t lane = threadIdx.x % kWave;
     uint8_t *stage = lds + a.tables_bytes + wave * args.stage_bytes;
-    const uint32_t per_wg = waves * args.blocks_per_wave;
-    const uint32_t first = (wg - a.wg_begin) * per_wg;
-    for (uint32_t r = 0; r < args.blocks_per_wave; ++r) {
-        const uint32_t b = first + r * waves + wave;
-        if (b >= a.n_blocks) break;
-        decode_block<C>(a, b, lane, stage, lut, t, args.status);
+    const uint32_t lo_b = (wg - a.wg_begin) * a.blocks_per_wg;
+    const uint32_t hi_b = min(lo_b + a.blocks_per_wg, a.n_blocks);
+
+    uint32_t b = lo_b + wave;
+    if (b >= hi_b) return;
+    Chunk<C> cur;
+    load_chunk<C>(a, b, lane, cur);
+    for (;;) {
+        const uint32_t s_out = __builtin_amdgcn_readlane(cur.meta, 0);
+        const uint32_t e_out = __builtin_amdgcn_readlane(cur.meta, 1);
+        // raw bytes of this block's first PF groups per lane
+        uint4 R[PF];
+        const uint32_t g0 = s_out >> 4, g1 = (e_out + 15u) >> 4;
+#pragma unroll
+        for (int j = 0; j < PF; ++j) {
+            const uint32_t g = g0 + lane + uint32_t(kWave * j);
+            R[j] = g < g1 ? *reinterpret_cast<const uint4 *>(a.raw + 16ull * g) : make_uint4(0, 0, 0, 0);
+        }
+        // next block's stream words, offsets and output range
+        const uint32_t bn = b + waves;
+        const bool more = bn < hi_b;
+        Chunk<C> nxt;
+        if (more) load_chunk<C>(a, bn, lane, nxt);
+        decode_block<C>(a, b, lane, cur, stage, t, args.status, R, s_out, e_out);
+        if (!more) break;
+        cur = nxt;
+        b = bn;
     }
 }
 
@@ -319,37 +453,90 @@ int device_cu_count() {
     return cus;
 }
 
+constexpr uint32_t kLdsBytes = 160u * 1024u;
+
+// Split `slots` workgroups across items so that the largest per-workgroup
+// block count is as small as possible (each item gets at least one).
+std::vector<uint32_t> share_workgroups(const std::vector<uint64_t> &blocks, uint64_t slots, uint32_t per_wg_min) {
+    const size_t m = blocks.size();
+    std::vector<uint32_t> g(m, 1);
+    uint64_t used = m;
+    auto load = [&](size_t i) { return dfc::ceil_div(blocks[i], g[i]); };
+    while (used < slots) {
+        size_t best = 0;
+        for (size_t i = 1; i < m; ++i)
+            if (load(i) > load(best)) best = i;
+        if (load(best) <= per_wg_min) break;
+        g[best]++;
+        used++;
+    }
+    return g;
+}
+
 template <int C>
 dfc_status launch_group(const dfc_batch_item *items, const uint32_t *idx, uint32_t count, uint32_t *status,
                         hipStream_t stream) {
     BatchArgs args;
     std::memset(&args, 0, sizeof(args));
-    uint32_t min_len = 24, max_tables = 0;
-    uint64_t total_blocks = 0;
+    uint32_t max_tables = 0, max_block = 0;
+    std::vector<uint64_t> blocks;
+    std::vector<uint32_t> live;
     for (uint32_t k = 0; k < count; ++k) {
         const dfc_info &in = *items[idx[k]].info;
-        min_len = std::min(min_len, std::max(1u, in.min_len));
-        max_tables = std::max<uint32_t>(max_tables, uint32_t(in.tables_bytes));
-        total_blocks += in.n_blocks;
-    }
-    const uint32_t stage = uint32_t((16 + kWave * dfc::ceil_div(8ull * C, min_len) + 16 + 15) & ~15ull);
-    const uint32_t tbytes = (max_tables + 15u) & ~15u;
-    uint32_t waves = g_launch.waves ? g_launch.waves : 8;
-    while (waves > 1 && tbytes + waves * stage > 160u * 1024u) waves /= 2;
-    if (tbytes + waves * stage > 160u * 1024u) return DFC_EUNSUPPORTED;
-    uint32_t bpw = g_launch.blocks_per_wave;
-    if (!bpw) {
-        const uint64_t target_wgs = uint64_t(device_cu_count()) * 2;
-        bpw = uint32_t(std::min<uint64_t>(16, std::max<uint64_t>(1, total_blocks / (target_wgs * waves))));
-    }
-    const uint32_t per_wg = waves * bpw;
-    uint32_t wg = 0, used = 0;
-    for (uint32_t k = 0; k < count; ++k) {
-        const dfc_batch_item &bi = items[idx[k]];
-        const dfc_info &in = *bi.info;
         if (in.n_blocks == 0) continue;
+        live.push_back(idx[k]);
+        blocks.push_back(in.n_blocks);
+        max_tables = std::max<uint32_t>(max_tables, uint32_t((in.tables_bytes + 15) & ~15ull));
+        max_block = std::max(max_block, in.max_block_elems);
+    }
+    if (live.empty()) return DFC_OK;
+    // staging: lead (< 16) + elements + one 16-byte group of slack, rounded to 16
+    const uint32_t stage = (max_block + 32u + 15u) & ~15u;
+    // waves per workgroup: the most resident wavefronts per CU under the LDS budget
+    uint32_t waves = g_launch.waves;
+    if (!waves) {
+        uint32_t best = 0;
+        for (uint32_t w = 4; w <= kMaxWaves; ++w) {
+            const uint32_t per = max_tables + w * stage;
+            if (per > kLdsBytes) break;
+            const uint32_t resident = std::min<uint32_t>(kLdsBytes / per, 32 / w) * w;
+            if (resident > best) {
+                best = resident;
+                waves = w;
+            }
+        }
+    }
+    if (!waves) waves = 1;
+    while (waves > 1 && max_tables + waves * stage > kLdsBytes) --waves;
+    const uint32_t lds = max_tables + waves * stage;
+    if (lds > kLdsBytes) return DFC_EUNSUPPORTED;
+    static bool attr_set = false;
+    if (!attr_set) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void *>(&dfc_decode_kernel<C>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, int(kLdsBytes)) != hipSuccess)
+            return DFC_EHIP;
+        attr_set = true;
+    }
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(&dfc_decode_kernel<C>),
+                                                     int(waves * kWave), size_t(lds)) != hipSuccess ||
+        per_cu <= 0)
+        per_cu = int(std::max(1u, kLdsBytes / lds));
+    uint64_t slots = uint64_t(per_cu) * uint64_t(device_cu_count());
+    if (g_launch.blocks_per_wave) {
+        // fixed work per workgroup instead of filling the machine exactly
+        uint64_t total = 0;
+        for (uint64_t nb : blocks) total += dfc::ceil_div(nb, uint64_t(waves) * g_launch.blocks_per_wave);
+        slots = total;
+    }
+    const std::vector<uint32_t> g =
+        share_workgroups(blocks, std::max<uint64_t>(slots, live.size()), waves);
+    uint32_t wg = 0;
+    for (size_t k = 0; k < live.size(); ++k) {
+        const dfc_batch_item &bi = items[live[k]];
+        const dfc_info &in = *bi.info;
         const uint8_t *base = static_cast<const uint8_t *>(bi.blob_dev);
-        ItemArgs &a = args.item[used++];
+        ItemArgs &a = args.item[k];
         a.words = reinterpret_cast<const uint32_t *>(base + in.off_words);
         a.offw = reinterpret_cast<const uint32_t *>(base + in.off_offsets);
         a.blockout = reinterpret_cast<const uint32_t *>(base + in.off_blockout);
@@ -358,24 +545,15 @@ dfc_status launch_group(const dfc_batch_item *items, const uint32_t *idx, uint32
         a.dst = bi.dst_dev;
         a.total_bits = in.total_bits;
         a.n_blocks = uint32_t(in.n_blocks);
+        a.blocks_per_wg = uint32_t(dfc::ceil_div(in.n_blocks, g[k]));
         a.wg_begin = wg;
         a.tables_bytes = uint32_t((in.tables_bytes + 15) & ~15ull);
         a.lut_bits = in.lut_bits;
-        wg += uint32_t(dfc::ceil_div(in.n_blocks, per_wg));
+        wg += uint32_t(dfc::ceil_div(in.n_blocks, a.blocks_per_wg));
     }
-    if (used == 0) return DFC_OK;
-    args.count = used;
-    args.blocks_per_wave = bpw;
+    args.count = uint32_t(live.size());
     args.stage_bytes = stage;
     args.status = status;
-    const uint32_t lds = tbytes + waves * stage;
-    static bool attr_set = false;
-    if (!attr_set) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void *>(&dfc_decode_kernel<C>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
-            return DFC_EHIP;
-        attr_set = true;
-    }
     hipLaunchKernelGGL(dfc_decode_kernel<C>, dim3(wg), dim3(waves * kWave), lds, stream, args);
     return hipGetLastError() == hipSuccess ? DFC_OK : DFC_EHIP;
 }
@@ -392,7 +570,8 @@ dfc_status check_item(const dfc_batch_item &it) {
     if (in.lanes_per_block != 64) return DFC_EUNSUPPORTED;
     const uint32_t C = in.chunk_bytes;
     if (C != 4 && C != 8 && C != 16 && C != 32) return DFC_EINVAL;
-    if (in.lut_bits < 8 || in.lut_bits > 12 || in.min_len < 1) return DFC_EINVAL;
+    if (in.lut_bits < 8 || in.lut_bits > 12 || in.min_len < 1 || in.lut_bits > 8 * in.min_len) return DFC_EINVAL;
+    if (in.max_block_elems > 64u * dfc::ceil_div(8ull * C, in.min_len)) return DFC_EINVAL;
     return DFC_OK;
 }
 
@@ -401,7 +580,7 @@ dfc_status check_item(const dfc_batch_item &it) {
 extern "C" {
 
 dfc_status dfc_set_launch(uint32_t waves_per_group, uint32_t blocks_per_wave) {
-    if (waves_per_group && waves_per_group != 4 && waves_per_group != 8 && waves_per_group != 16) return DFC_EINVAL;
+    if (waves_per_group > kMaxWaves) return DFC_EINVAL;
     if (blocks_per_wave > 64) return DFC_EINVAL;
     g_launch.waves = waves_per_group;
     g_launch.blocks_per_wave = blocks_per_wave;

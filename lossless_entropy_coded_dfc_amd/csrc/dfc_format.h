@@ -30,13 +30,20 @@ constexpr int lengths = 256;
 
 enum Section { kTables = 0, kWords, kOffsets, kBlockout, kRaw, kPanels, kNumSections };
 
-// Decode-table section layout: lut[2^k] (u64) then limit[32], first[32],
-// base[32] (u32) then order[256] (u8).
-inline uint64_t tables_bytes(uint32_t lut_bits) { return 8ull * (1ull << lut_bits) + 3 * 128 + 256; }
-inline uint64_t tables_limit_off(uint32_t lut_bits) { return 8ull << lut_bits; }
-inline uint64_t tables_first_off(uint32_t lut_bits) { return (8ull << lut_bits) + 128; }
-inline uint64_t tables_base_off(uint32_t lut_bits) { return (8ull << lut_bits) + 256; }
-inline uint64_t tables_order_off(uint32_t lut_bits) { return (8ull << lut_bits) + 384; }
+// Decode-table section layout for a k-bit window: step[2^k] (u32),
+// sym[2^k] (u64), mask[2^k] (u16), then limit[32], first[32], base[32]
+// (u32, index = code length) and order[256] (u8).
+constexpr uint32_t kStepEscape = 0xFFFFF000u;
+inline uint64_t tables_bytes(uint32_t k) { return 14ull * (1ull << k) + 3 * 128 + 256; }
+inline uint64_t tables_sym_off(uint32_t k) { return 4ull << k; }
+inline uint64_t tables_mask_off(uint32_t k) { return 12ull << k; }
+inline uint64_t tables_limit_off(uint32_t k) { return 14ull << k; }
+inline uint64_t tables_first_off(uint32_t k) { return (14ull << k) + 128; }
+inline uint64_t tables_base_off(uint32_t k) { return (14ull << k) + 256; }
+inline uint64_t tables_order_off(uint32_t k) { return (14ull << k) + 384; }
+
+// Exponent byte as staged by the decoder: rotated right by one bit.
+inline uint32_t rotate_exponent(uint32_t e) { return ((e >> 1) | ((e & 1u) << 7)) & 0xFFu; }
 
 inline uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 inline uint64_t ceil_div(uint64_t a, uint64_t b) { return (a + b - 1) / b; }

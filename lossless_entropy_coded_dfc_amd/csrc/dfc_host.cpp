@@ -149,9 +149,17 @@ dfc_status package_merge(const uint64_t hist[256], uint32_t limit, uint8_t len[2
     return DFC_OK;
 }
 
-// First-level table entry for a k-bit window (see the container description).
-uint64_t lut_entry(uint32_t window, uint32_t k, const Canon &c) {
-    uint32_t o = 0, ns = 0, nb = 0, mask = 0, syms = 0;
+// First-level table entry for a k-bit window (next k stream bits, first bit
+// most significant): the whole codes that fit, decoded from its first bit.
+struct Entry {
+    uint32_t step;  // (codes << 16) - bits, or kStepEscape
+    uint64_t sym;   // rotated exponent of code j in byte j
+    uint16_t mask;  // bit j: a code ends j + 1 bits in
+};
+
+Entry lut_entry(uint32_t window, uint32_t k, const Canon &c) {
+    uint32_t o = 0, n = 0;
+    Entry e{0, 0, 0};
     while (o < k) {
         uint32_t found = 0, v = 0;
         for (uint32_t l = 1; l <= k - o; ++l) {
@@ -162,23 +170,34 @@ uint64_t lut_entry(uint32_t window, uint32_t k, const Canon &c) {
             }
         }
         if (!found) break;
-        uint32_t sym = c.order[c.base[found] + v - c.first[found]];
-        mask |= 1u << (o + found - 1);
-        if (ns < 4) {
-            syms |= sym << (8 * ns);
-            ns++;
-            nb += found;
-        }
+        const uint32_t sym = c.order[c.base[found] + v - c.first[found]];
+        e.sym |= uint64_t(rotate_exponent(sym)) << (8 * n);  // n < 8: k <= 8 * shortest length
         o += found;
+        e.mask = uint16_t(e.mask | (1u << (o - 1)));
+        ++n;
     }
-    return uint64_t(syms) | (uint64_t(ns) << 32) | (uint64_t(nb) << 36) | (uint64_t(mask) << 40) |
-           (uint64_t(o) << 52);
+    e.step = n ? (n << 16) - o : kStepEscape;
+    return e;
+}
+
+// Window size used for a code: at most 8 * (shortest length), so that no
+// window holds more than 8 whole codes.
+uint32_t effective_lut_bits(const uint8_t len[256], uint32_t requested) {
+    uint32_t mn = 0;
+    for (int s = 0; s < 256; ++s)
+        if (len[s] && (!mn || len[s] < mn)) mn = len[s];
+    return mn ? std::min(requested, 8 * mn) : requested;
 }
 
 void build_tables(const uint8_t len[256], uint32_t k, uint8_t *out) {
     Canon c;
     canonical(len, c, nullptr);
-    for (uint32_t w = 0; w < (1u << k); ++w) store_le<uint64_t>(out + 8ull * w, lut_entry(w, k, c));
+    for (uint32_t w = 0; w < (1u << k); ++w) {
+        const Entry e = lut_entry(w, k, c);
+        store_le<uint32_t>(out + 4ull * w, e.step);
+        store_le<uint64_t>(out + tables_sym_off(k) + 8ull * w, e.sym);
+        store_le<uint16_t>(out + tables_mask_off(k) + 2ull * w, e.mask);
+    }
     uint8_t *limit = out + tables_limit_off(k), *first = out + tables_first_off(k), *base = out + tables_base_off(k);
     std::memset(limit, 0, 3 * 128 + 256);
     for (uint32_t l = 1; l <= kMaxLen; ++l) {
@@ -216,7 +235,7 @@ void dfc_default_params(dfc_params *p) {
     p->chunk_bytes = 16;
     p->lanes_per_block = 64;
     p->max_code_len = kMaxLen;
-    p->lut_bits = 12;
+    p->lut_bits = 11;
     p->layout = DFC_LAYOUT_FLAT;
 }
 
@@ -303,6 +322,7 @@ dfc_status dfc_encode(const uint16_t *src, uint64_t n, const dfc_params *pin, co
     Canon canon;
     uint32_t code[256];
     canonical(len, canon, code);
+    const uint32_t lut_bits = effective_lut_bits(len, p.lut_bits);
 
     // Pass 1: bits per thread range.
     std::vector<uint64_t> range_bits(nt + 1, 0);
@@ -315,7 +335,7 @@ dfc_status dfc_encode(const uint16_t *src, uint64_t n, const dfc_params *pin, co
     const uint64_t total_bits = range_bits[nt];
     const uint32_t C = p.chunk_bytes, T = p.lanes_per_block;
     Layout L = layout_sizes(total_bits, C, T);
-    SectionSizes sz = section_sizes(n, L.n_chunks, L.n_blocks, C, p.lut_bits);
+    SectionSizes sz = section_sizes(n, L.n_chunks, L.n_blocks, C, lut_bits);
     uint64_t off[kNumSections];
     const uint64_t blob_bytes = place_sections(sz, off);
     if (cap < blob_bytes) return DFC_ESIZE;
@@ -337,7 +357,7 @@ dfc_status dfc_encode(const uint16_t *src, uint64_t n, const dfc_params *pin, co
     store_le<uint32_t>(dst + hdr::chunk_bytes, C);
     store_le<uint32_t>(dst + hdr::lanes, T);
     store_le<uint32_t>(dst + hdr::max_code_len, p.max_code_len);
-    store_le<uint32_t>(dst + hdr::lut_bits, p.lut_bits);
+    store_le<uint32_t>(dst + hdr::lut_bits, lut_bits);
     store_le<uint32_t>(dst + hdr::layout, p.layout);
     store_le<uint32_t>(dst + hdr::panel_rows, 0);
     store_le<uint64_t>(dst + hdr::rows, rows);
@@ -349,7 +369,7 @@ dfc_status dfc_encode(const uint16_t *src, uint64_t n, const dfc_params *pin, co
     }
     store_le<uint64_t>(dst + hdr::blob_bytes, blob_bytes);
     std::memcpy(dst + hdr::lengths, len, 256);
-    build_tables(len, p.lut_bits, dst + off[kTables]);
+    build_tables(len, lut_bits, dst + off[kTables]);
 
     // Pass 2: pack codes, raw bytes, chunk offsets and block offsets.
     uint8_t *words = dst + off[kWords];
@@ -478,6 +498,7 @@ dfc_status dfc_blob_info(const void *blob_v, uint64_t bytes, dfc_info *out) {
     in.n_used = used;
     in.min_len = mn;
     in.max_len = mx;
+    if (mn && in.lut_bits > 8 * mn) return DFC_ECORRUPT;
 
     Layout L = layout_sizes(in.total_bits, in.chunk_bytes, in.lanes_per_block);
     if (L.n_blocks != in.n_blocks || L.n_chunks != in.n_chunks) return DFC_ECORRUPT;
@@ -527,12 +548,14 @@ dfc_status dfc_blob_info(const void *blob_v, uint64_t bytes, dfc_info *out) {
         const uint8_t *bo = b + off[kBlockout];
         if (load_le<uint32_t>(bo) != 0 || load_le<uint32_t>(bo + 4 * in.n_blocks) != in.n) return DFC_ECORRUPT;
         const uint64_t cap = in.n ? uint64_t(in.lanes_per_block) * ceil_div(8ull * in.chunk_bytes, mn) : 0;
-        uint32_t prev = 0;
+        uint32_t prev = 0, widest = 0;
         for (uint64_t k = 1; k <= in.n_blocks; ++k) {
             uint32_t v = load_le<uint32_t>(bo + 4 * k);
             if (v < prev || v - prev > cap) return DFC_ECORRUPT;
+            widest = std::max(widest, v - prev);
             prev = v;
         }
+        in.max_block_elems = widest;
     }
     *out = in;
     return DFC_OK;

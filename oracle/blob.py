@@ -29,13 +29,15 @@ each starts at the next multiple of 256 bytes and padding is zero:
 * offsets: 5-bit fields off[0..n_chunks] packed as in ``stream.pack_offsets``
 * blockout: uint32 out[0..n_blocks]
 * raw: the raw bytes (sign << 7 | mantissa), padded to a multiple of 16
-* tables: derived from the code lengths alone (see ``decode_tables``).
+* tables: derived from the code lengths alone (see ``decode_tables``); the
+  header's lut_bits is min(requested, 8 * shortest code length).
 
 The decode tables are the "compact hierarchical lookup tables" of the
 DFloat11 blog (section 03 item 1): a first level indexed by the next k stream
-bits that resolves every code of length <= k, and canonical per-length tables
-that resolve the rare longer codes.  They are stored in the container so that
-a decoder only has to copy them into on-chip memory.
+bits that resolves every whole code inside those k bits at once, and
+canonical per-length tables that resolve the rare codes longer than k bits.
+They are stored in the container so that a decoder only has to copy them
+into on-chip memory.
 """
 from __future__ import annotations
 
@@ -59,26 +61,29 @@ def _align(x: int, a: int = 256) -> int:
 
 # ------------------------------------------------------------ decode tables
 
-def lut_entry(window: int, k: int, tables) -> int:
-    """First-level table entry for a k-bit window (the next k stream bits,
-    first bit most significant).
+ESCAPE = 0xFFFFF000
 
-    Decode codes one after another from the start of the window, as long as a
-    whole code fits inside the k bits.  The entry packs (bit fields of a
-    64-bit integer):
 
-      bits  0..31  the first min(4, count) decoded symbols, one byte each
-      bits 32..35  ns: how many symbols are in bits 0..31
-      bits 36..39  nb: how many bits those ns codes occupy
-      bits 40..51  M: bit j is set when a decoded code ends exactly j+1 bits
-                   into the window (all codes that fit, not only four)
-      bits 52..55  nbm: bits occupied by all the codes that fit
+def rotate_exponent(e: int) -> int:
+    """The byte a decoder stages for exponent e: e rotated right by one bit
+    (bit 0 moves to bit 7).  With the raw byte sign << 7 | mantissa, the two
+    bytes of a bf16 value are then (e' & 0x80 | raw & 0x7F, raw & 0x80 |
+    e' & 0x7F), i.e. a byte-wise merge under a constant mask."""
+    return ((e >> 1) | ((e & 1) << 7)) & 0xFF
 
-    A window whose first code is longer than k bits has entry 0.
-    """
-    syms = []
-    nb = 0
-    mask = 0
+
+def effective_lut_bits(lengths, lut_bits: int) -> int:
+    """Window size actually used: at most 8 * (shortest code length), so that
+    no window holds more than 8 whole codes."""
+    used = [int(l) for l in np.asarray(lengths) if l > 0]
+    return min(lut_bits, 8 * min(used)) if used else lut_bits
+
+
+def window_codes(window: int, k: int, tables):
+    """Codes that fit in a k-bit window (next k stream bits, first bit most
+    significant), decoded one after another from its first bit: a list of
+    (symbol, length)."""
+    out = []
     o = 0
     while o < k:
         found = None
@@ -89,30 +94,53 @@ def lut_entry(window: int, k: int, tables) -> int:
                 break
         if found is None:
             break
-        sym, l = found
-        mask |= 1 << (o + l - 1)
-        if len(syms) < 4:
-            syms.append(sym)
-            nb += l
+        out.append(found)
+        o += found[1]
+    return out
+
+
+def lut_entry(window: int, k: int, tables):
+    """(step, sym, mask) for one k-bit window.
+
+    step: (c << 16) - b as a uint32, where c whole codes of total length b fit
+          in the window; 0xFFFFF000 when the first code is longer than k bits.
+          Adding step to an accumulator (count << 16) + (bias - position)
+          advances both the code count and the bit position.
+    sym:  uint64, byte j = rotate_exponent(symbol j) for j < c, else 0.
+    mask: uint16, bit j set when a code ends exactly j + 1 bits in.
+    """
+    codes = window_codes(window, k, tables)
+    if not codes:
+        return ESCAPE, 0, 0
+    if len(codes) > 8:
+        raise ValueError("more than 8 codes fit in one window")
+    b = sum(l for _, l in codes)
+    step = ((len(codes) << 16) - b) & 0xFFFFFFFF
+    sym = 0
+    mask = 0
+    o = 0
+    for j, (s, l) in enumerate(codes):
+        sym |= rotate_exponent(int(s)) << (8 * j)
         o += l
-    entry = 0
-    for j, s in enumerate(syms):
-        entry |= int(s) << (8 * j)
-    entry |= len(syms) << 32
-    entry |= nb << 36
-    entry |= mask << 40
-    entry |= o << 52
-    return entry
+        mask |= 1 << (o - 1)
+    return step, sym, mask
 
 
 def decode_tables(lengths, lut_bits: int) -> bytes:
-    """The tables section: lut[2^k] (uint64), then limit[32], first[32],
-    base[32] (uint32, index = code length, entries 0 and 25..31 are 0), then
-    the 256-byte list of used symbols ordered by (length, symbol)."""
+    """The tables section for a window of k = lut_bits bits (k must not exceed
+    8 * shortest code length): step[2^k] (uint32), sym[2^k] (uint64),
+    mask[2^k] (uint16), then limit[32], first[32], base[32] (uint32, index =
+    code length; entries 0 and 25..31 are 0) and the 256-byte list of used
+    symbols ordered by (length, symbol)."""
     t = cb.canonical_tables(lengths)
     if not 8 <= lut_bits <= 12:
         raise ValueError("lut_bits must be in 8..12")
-    lut = np.array([lut_entry(w, lut_bits, t) for w in range(1 << lut_bits)], dtype=np.uint64)
+    n = 1 << lut_bits
+    step = np.zeros(n, dtype=np.uint32)
+    sym = np.zeros(n, dtype=np.uint64)
+    mask = np.zeros(n, dtype=np.uint16)
+    for w in range(n):
+        step[w], sym[w], mask[w] = lut_entry(w, lut_bits, t)
     limit = np.zeros(32, dtype=np.uint32)
     first = np.zeros(32, dtype=np.uint32)
     base = np.zeros(32, dtype=np.uint32)
@@ -122,11 +150,12 @@ def decode_tables(lengths, lut_bits: int) -> bytes:
         base[l] = t["base"][l]
     order = np.zeros(256, dtype=np.uint8)
     order[: len(t["order"])] = t["order"]
-    return lut.tobytes() + limit.tobytes() + first.tobytes() + base.tobytes() + order.tobytes()
+    return (step.astype("<u4").tobytes() + sym.astype("<u8").tobytes() + mask.astype("<u2").tobytes() +
+            limit.tobytes() + first.tobytes() + base.tobytes() + order.tobytes())
 
 
 def tables_bytes(lut_bits: int) -> int:
-    return 8 * (1 << lut_bits) + 3 * 128 + 256
+    return 14 * (1 << lut_bits) + 3 * 128 + 256
 
 
 # ----------------------------------------------------------------- container
@@ -143,12 +172,13 @@ def section_sizes(enc, lut_bits: int):
     }
 
 
-def write_blob(enc, lut_bits: int = 12, rows: int | None = None, cols: int | None = None) -> bytes:
+def write_blob(enc, lut_bits: int = 11, rows: int | None = None, cols: int | None = None) -> bytes:
     n = enc["n"]
     if rows is None or cols is None:
         rows, cols = 1, n
     if rows * cols != n:
         raise ValueError("rows * cols != n")
+    lut_bits = effective_lut_bits(enc["lengths"], lut_bits)
     sizes = section_sizes(enc, lut_bits)
     offsets = {}
     pos = HEADER_BYTES

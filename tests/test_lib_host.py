@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     assert dfc.status_str(-3) == "corrupt container"
 
 
-def oracle_blob(x, C, T=64, k=12):
+def oracle_blob(x, C, T=64, k=11):
     shape = x.shape if x.ndim == 2 else (1, x.size)
     if x.size == 0:
         shape = (1, 0)
@@ -100,7 +100,7 @@ def test_external_codebook_and_missing_symbol():
     h = cb.histogram(fields.split(x)[0]) + 1  # smoothed: every exponent has a code
     book = dfc.build_codebook(h, 24)
     b = dfc.encode(x, codebook=book)
-    assert bytes(b) == bl.write_blob(st.encode(x, 16, 64, lengths=book.lengths), 12, 64, 512)
+    assert bytes(b) == bl.write_blob(st.encode(x, 16, 64, lengths=book.lengths), 11, 64, 512)
     e = fields.split(x)[0]
     h2 = cb.histogram(e)
     h2[int(e[0])] = 0  # a present exponent without a code

@@ -15,29 +15,40 @@ from oracle import stream as st
 
 
 def parse_lut(tables: bytes, k: int):
-    lut = np.frombuffer(tables, dtype="<u8", count=1 << k)
-    rest = tables[8 << k:]
+    n = 1 << k
+    step = np.frombuffer(tables, dtype="<u4", count=n)
+    sym = np.frombuffer(tables, dtype="<u8", count=n, offset=4 * n)
+    mask = np.frombuffer(tables, dtype="<u2", count=n, offset=12 * n)
+    rest = tables[14 * n:]
     limit = np.frombuffer(rest, dtype="<u4", count=32, offset=0)
     first = np.frombuffer(rest, dtype="<u4", count=32, offset=128)
     base = np.frombuffer(rest, dtype="<u4", count=32, offset=256)
     order = np.frombuffer(rest, dtype=np.uint8, count=256, offset=384)
-    return lut, limit, first, base, order
+    return step, sym, mask, limit, first, base, order
+
+
+def unrotate(b):
+    return ((b << 1) | (b >> 7)) & 0xFF
 
 
 def table_walk_decode(p):
     """Decode every chunk using only the table section, the way a GPU lane
-    does: a counting pass over boundary masks, then a symbol pass that takes up
-    to four symbols per lookup and falls back to the per-length tables for
-    codes longer than k bits."""
+    does: a counting pass that adds step entries into one accumulator
+    (count in the high half, bit position in the low half) and corrects the
+    last lookup's overshoot with the boundary mask of the window at the
+    chunk's end, then a symbol pass that takes every symbol of a lookup and
+    falls back to the per-length tables for codes longer than k bits."""
     k = p["lut_bits"]
-    lut, limit, first, base, order = parse_lut(p["tables"], k)
+    step, sym, mask, limit, first, base, order = parse_lut(p["tables"], k)
     words = [int(w) for w in p["words"]]
     C = p["chunk_bytes"]
+    BIAS = 0x8000
 
     def window(pos, nbits):
         v = 0
         for b in range(pos, pos + nbits):
-            v = (v << 1) | ((words[b >> 5] >> (31 - (b & 31))) & 1)
+            k_ = b >> 5
+            v = (v << 1) | (((words[k_] >> (31 - (b & 31))) & 1) if k_ < len(words) else 0)
         return v
 
     def long_code(pos):
@@ -51,35 +62,34 @@ def table_walk_decode(p):
     for i in range(p["n_chunks"]):
         start = 8 * C * i + int(p["off"][i])
         end = min(8 * C * (i + 1) + int(p["off"][i + 1]), p["total_bits"])
-        # counting pass
-        pos, cnt, last = start, 0, None
+        if start >= end:
+            continue
+        # counting pass: acc = (count << 16) + (BIAS - (pos - start))
+        acc = BIAS
+        pos = start
         while pos < end:
-            e = int(lut[window(pos, k)])
-            mask, nbm = (e >> 40) & 0xFFF, (e >> 52) & 0xF
-            if mask == 0:
-                pos += long_code(pos)[1]
-                cnt += 1
-                last = None
-                continue
-            last = (pos, mask)
-            cnt += bin(mask).count("1")
-            pos += nbm
-        if last is not None and pos > end:
-            r = end - last[0]
-            cnt -= bin(last[1] >> r).count("1")
+            d = int(step[window(pos, k)])
+            if d == 0xFFFFF000:
+                d = (1 << 16) - long_code(pos)[1]
+            acc = (acc + d) & 0xFFFFFFFF
+            pos = start + BIAS - (acc & 0xFFFF)
+        cnt = acc >> 16
+        if pos > end:
+            cnt -= bin(int(mask[window(end, k)]) & ((1 << (pos - end)) - 1)).count("1")
         # symbol pass
         pos, got = start, []
         while len(got) < cnt:
-            e = int(lut[window(pos, k)])
-            ns, nb = (e >> 32) & 0xF, (e >> 36) & 0xF
-            if ns == 0:
+            idx = window(pos, k)
+            d = int(step[idx])
+            if d == 0xFFFFF000:
                 s, l = long_code(pos)
                 got.append(s)
                 pos += l
                 continue
-            take = min(ns, cnt - len(got))
-            got += [(e >> (8 * j)) & 0xFF for j in range(take)]
-            pos += nb
+            c, b = (d >> 16) + 1, 0x10000 - (d & 0xFFFF)
+            take = min(c, cnt - len(got))
+            got += [unrotate((int(sym[idx]) >> (8 * j)) & 0xFF) for j in range(take)]
+            pos += b
         out += got
     return np.array(out, dtype=np.uint8)
 
@@ -113,20 +123,19 @@ def test_golden_lut_entries(golden):
     for s, l in g["lengths"].items():
         lens[int(s)] = l
     k = g["lut_bits"]
-    lut, limit, first, base, order = parse_lut(bl.decode_tables(lens, k), k)
+    step, sym, mask, limit, first, base, order = parse_lut(bl.decode_tables(lens, k), k)
     for ent in g["lut_entries"]:
-        e = int(lut[int(ent["window"], 2)])
-        ns = (e >> 32) & 0xF
-        assert ns == ent["ns"]
-        assert [(e >> (8 * j)) & 0xFF for j in range(ns)] == ent["syms"]
-        assert (e >> 36) & 0xF == ent["nb"]
-        assert (e >> 40) & 0xFFF == sum(1 << j for j in ent["mask_bits"])
-        assert (e >> 52) & 0xF == ent["nbm"]
+        w = int(ent["window"], 2)
+        assert int(step[w]) == int(ent["step_hex"], 16)
+        assert int(step[w]) == ((ent["codes"] << 16) - ent["bits"]) & 0xFFFFFFFF
+        assert int(sym[w]) == int(ent["sym_hex"], 16)
+        assert int(mask[w]) == sum(1 << j for j in ent["mask_bits"])
     # canonical tables of the same code: 127:0, 126:10, 124:110, 125:111
     assert order[:4].tolist() == [127, 126, 124, 125]
     assert [int(first[l]) for l in (1, 2, 3)] == [0, 2, 6]
     assert [int(base[l]) for l in (1, 2, 3)] == [0, 1, 2]
     assert int(limit[3]) == 1 << 24 and int(limit[1]) == 1 << 23
+    assert [bl.rotate_exponent(e) for e in (127, 126, 125, 124)] == [0xBF, 0x3F, 0xBE, 0x3E]
 
 
 def test_long_codes_escape():
@@ -136,15 +145,15 @@ def test_long_codes_escape():
     h = np.zeros(256, dtype=np.uint64)
     h[:40] = fib
     lens = cb.package_merge_lengths(h, 24)
-    lut, *_ = parse_lut(bl.decode_tables(lens, 10), 10)
+    step, sym, mask, *_ = parse_lut(bl.decode_tables(lens, 8), 8)
     # the all-ones window starts with the longest code (24 bits) -> escape
-    assert int(lut[(1 << 10) - 1]) == 0
+    assert int(step[255]) == 0xFFFFF000 and int(sym[255]) == 0 and int(mask[255]) == 0
     # the all-zeros window starts with the shortest code
-    assert (int(lut[0]) >> 32) & 0xF >= 1
+    assert int(step[0]) != 0xFFFFF000 and int(mask[0]) != 0
 
 
 @pytest.mark.parametrize("kind", ["gauss", "ladder", "uniform", "constant"])
-@pytest.mark.parametrize("k", [8, 12])
+@pytest.mark.parametrize("k", [8, 11, 12])
 def test_table_walk_reproduces_data(kind, k):
     from lossless_entropy_coded_dfc_amd import synth
     n = 3000
@@ -155,6 +164,7 @@ def test_table_walk_reproduces_data(kind, k):
     for C in (4, 16, 32):
         enc = st.encode(x, C, 64)
         p = bl.parse_blob(bl.write_blob(enc, k))
+        assert p["lut_bits"] == bl.effective_lut_bits(enc["lengths"], k)
         e, _ = fields.split(x)
         assert np.array_equal(table_walk_decode(p), e)
 
@@ -167,3 +177,15 @@ def test_size_within_two_percent_of_entropy_bound():
         e, _ = fields.split(x)
         ratio = bl.coded_bytes(p) / bl.entropy_bound_bytes(cb.histogram(e))
         assert 1.0 < ratio < limit
+
+
+def test_effective_window_keeps_at_most_eight_codes():
+    # one used symbol (plus the phantom) has 1-bit codes: the window shrinks to 8
+    lens = np.zeros(256, dtype=np.uint8)
+    lens[3] = lens[4] = 1
+    assert bl.effective_lut_bits(lens, 12) == 8
+    step, *_ = parse_lut(bl.decode_tables(lens, 8), 8)
+    assert all(((int(d) >> 16) + 1) <= 8 for d in step)
+    g = np.zeros(256, dtype=np.uint8)
+    g[:4] = [2, 2, 2, 2]
+    assert bl.effective_lut_bits(g, 12) == 12
