@@ -56,8 +56,7 @@ typedef struct {
     uint32_t chunk_bytes;     /* C: bytes of code stream per lane: 4, 8, 16 or 32 (default 16) */
     uint32_t lanes_per_block; /* T: chunks per block: 64 (default; one wavefront), 128 or 256 */
     uint32_t max_code_len;    /* code length limit, 1..24 (default 24) */
-    uint32_t lut_bits;        /* k: bits indexed by the first-level decode table, 8..12 (default 11);
-                                 the container records min(k, 8 * shortest code length) */
+    uint32_t lut_bits;        /* k: bits indexed by the first-level decode table, 8..12 (default 11) */
     uint32_t layout;          /* DFC_LAYOUT_FLAT: elements in row-major order */
     uint32_t threads;         /* host encoder threads; 0 = min(hardware threads, 16) */
     uint64_t rows, cols;      /* matrix shape recorded in the header; 0,0 = 1 x n */

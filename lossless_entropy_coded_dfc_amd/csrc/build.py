@@ -16,9 +16,13 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libdfc.so")
 ARCH = "gfx950"
 
-# Packed FP32 instructions are kept out of every HIP object.
+# Packed FP32 instructions are kept out of every HIP object.  Unaligned
+# access mode is switched off so the compiler never merges narrow LDS stores
+# into wide ones at unaligned addresses: gfx950 executes those one lane at a
+# time.
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-Xclang", "-target-feature", "-Xclang", "-unaligned-access-mode",
              "-Wall", "-Wno-unused-function"]
 CXX_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-pthread", "-Wall", "-Wextra", "-Wno-unused-parameter"]
 

@@ -65,8 +65,8 @@ struct BatchArgs {
 };
 
 struct Tables {
-    const uint32_t *step;
-    const uint2 *sym;
+    const uint32_t *step;  // every whole code in the window (counting pass)
+    const uint2 *wsym;     // x: rotated exponents of the first <= 4 codes, y: their step
     const uint16_t *mask;
     const uint32_t *limit, *first, *base;
     const uint8_t *order;
@@ -189,46 +189,27 @@ __device__ __forceinline__ uint32_t count_codes(const Chunk<C> &ck, int start, i
     return cnt;
 }
 
-__device__ __forceinline__ void store_u64_unaligned(uint8_t *p, uint2 v) {
-    struct __attribute__((packed, aligned(1))) U64 {
-        uint32_t x, y;
-    };
-    reinterpret_cast<U64 *>(p)->x = v.x;
-    reinterpret_cast<U64 *>(p)->y = v.y;
-}
-
-// Writes the first r (1..7) bytes of v to p.
-__device__ __forceinline__ void store_tail(uint8_t *p, uint2 v, uint32_t r) {
-    struct __attribute__((packed, aligned(1))) U32 {
-        uint32_t x;
-    };
-    struct __attribute__((packed, aligned(1))) U16 {
-        uint16_t x;
-    };
-    uint32_t lo = v.x;
-    if (r & 4u) {
-        reinterpret_cast<U32 *>(p)->x = lo;
-        p += 4;
-        lo = v.y;
-    }
-    if (r & 2u) {
-        reinterpret_cast<U16 *>(p)->x = uint16_t(lo);
-        p += 2;
-        lo >>= 16;
-    }
-    if (r & 1u) *p = uint8_t(lo);
+// Stores the 4 bytes of v at p, one naturally aligned byte store each.  On
+// gfx950 a wide LDS store to an address that is not a multiple of its width
+// is carried out one lane at a time; byte stores never are.
+__device__ __forceinline__ void store_4_bytes(uint8_t *p, uint32_t v) {
+    p[0] = uint8_t(v);
+    p[1] = uint8_t(v >> 8);
+    p[2] = uint8_t(v >> 16);
+    p[3] = uint8_t(v >> 24);
 }
 
 // Phase two: decode the chunk again and write its cnt (rotated) exponents to
-// LDS.  While 8 or more codes remain, all 8 symbol bytes of a lookup are
-// stored: the bytes past the lookup's own codes fall on positions this lane
-// overwrites with its next lookup.  The last < 8 codes are written exactly.
+// LDS, at most four codes per lookup.  While four or more codes remain, all
+// four symbol bytes of a lookup are stored: bytes past the lookup's own codes
+// fall on positions this lane overwrites with its next lookup.  The last
+// < 4 codes are written exactly.
 template <int C>
 __device__ __forceinline__ void write_codes(const Chunk<C> &ck, int start, uint32_t cnt, uint8_t *out,
                                             const Tables &t) {
     constexpr int NW = C / 4;
     uint32_t acc = kBias - uint32_t(start);
-    const uint32_t lim = cnt >= 8u ? (cnt - 7u) << 16 : 0u;  // acc < lim <=> done <= cnt - 8
+    const uint32_t lim = cnt >= 4u ? (cnt - 3u) << 16 : 0u;  // acc < lim <=> done <= cnt - 4
 #pragma unroll
     for (int k = -1; k < NW; ++k) {
         const uint32_t hi = k < 0 ? 0u : ck.w[k < 0 ? 0 : k];
@@ -236,10 +217,9 @@ __device__ __forceinline__ void write_codes(const Chunk<C> &ck, int start, uint3
         for (;;) {
             while (uint16_t(acc) >= uint16_t(kBias) && acc < lim) {
                 const uint32_t win = __builtin_amdgcn_alignbit(hi, lo, acc);
-                const uint32_t idx = win >> t.kshift;
-                const uint32_t d = t.step[idx];
-                store_u64_unaligned(out + (acc >> 16), t.sym[idx]);
-                acc += d;
+                const uint2 e = t.wsym[win >> t.kshift];
+                store_4_bytes(out + (acc >> 16), e.x);
+                acc += e.y;
             }
             if (lo16(acc) >= kBias - 2048u) break;
             acc += 0x1000u;
@@ -255,18 +235,19 @@ __device__ __forceinline__ void write_codes(const Chunk<C> &ck, int start, uint3
     uint32_t pos = uint32_t(32 * (NW + 1)) - lo16(acc) + kBias;
     while (done < cnt && pos < uint32_t(32 * (NW + 1))) {
         const uint32_t win = window_at<NW>(ck.w, pos);
-        const uint32_t idx = win >> t.kshift;
-        const uint32_t d = t.step[idx];
-        if (d == kEscape) {
+        const uint2 e = t.wsym[win >> t.kshift];
+        if (e.y == kEscape) {
             uint32_t sym;
             pos += long_code(win >> 8, t, sym);
             out[done] = uint8_t(sym);
             done += 1;
         } else {
-            const uint32_t r = min((d >> 16) + 1u, cnt - done);
-            store_tail(out + done, t.sym[idx], r);
+            const uint32_t r = min((e.y >> 16) + 1u, cnt - done);
+            out[done] = uint8_t(e.x);
+            if (r > 1u) out[done + 1] = uint8_t(e.x >> 8);
+            if (r > 2u) out[done + 2] = uint8_t(e.x >> 16);
             done += r;
-            pos += 0x10000u - (d & 0xFFFFu);
+            pos += 0x10000u - (e.y & 0xFFFFu);
         }
     }
 }
@@ -317,6 +298,19 @@ __device__ __forceinline__ void store_group(const ItemArgs &a, uint32_t g, uint3
     }
 }
 
+// Makes the compiler wait for the loads into v now.  vmcnt also counts
+// stores on this chip, and the compiler cannot count the stores of the
+// divergent store paths below, so a register first used after a store would
+// make it wait for every store in flight to reach memory.
+template <typename T>
+__device__ __forceinline__ void wait_for(const T &v) {
+    static_assert(sizeof(T) % 4 == 0, "whole dwords only");
+    uint32_t w[sizeof(T) / 4];
+    __builtin_memcpy(w, &v, sizeof(T));
+#pragma unroll
+    for (unsigned i = 0; i < sizeof(T) / 4; ++i) asm volatile("" ::"v"(w[i]));
+}
+
 // Raw-byte groups prefetched into registers per lane before decoding.
 template <int C>
 struct Prefetch {
@@ -326,8 +320,8 @@ struct Prefetch {
 template <int C>
 __device__ __forceinline__ void decode_block(const ItemArgs &a, uint32_t b, uint32_t lane, const Chunk<C> &ck,
                                              uint8_t *stage, const Tables &t, uint32_t *status,
-                                             const uint4 (&R)[Prefetch<C>::N], uint32_t s_out,
-                                             uint32_t e_out) {
+                                             const uint4 (&R)[Prefetch<C>::N], uint32_t s_out, uint32_t e_out,
+                                             const Chunk<C> &nxt, bool more) {
     constexpr int PF = Prefetch<C>::N;
     const uint64_t chunk = uint64_t(b) * kWave + lane;
     const uint32_t offpair = __builtin_amdgcn_alignbit(ck.o1, ck.o0, uint32_t((5ull * chunk) & 31));
@@ -341,12 +335,17 @@ __device__ __forceinline__ void decode_block(const ItemArgs &a, uint32_t b, uint
     const uint32_t total = __builtin_amdgcn_readlane(incl, kWave - 1);
     // A chunk of 8C bits holds at most 8C code starts; anything else (or a
     // total that disagrees with the block offsets) means a corrupt stream.
-    if (total != e_out - s_out || __builtin_amdgcn_ballot_w64(cnt > 8u * C) != 0) {
+    const bool bad = (total != e_out - s_out) | (__builtin_amdgcn_ballot_w64(cnt > 8u * C) != 0);
+    const uint32_t lead = s_out & 15u;
+    if (!bad && cnt) write_codes<C>(ck, start, cnt, stage + lead + (incl - cnt), t);
+    // Everything prefetched must be in registers before the first store, on
+    // every path to the next block.
+    wait_for(R);
+    wait_for(nxt);
+    if (bad) {
         if (lane == 0 && status) atomicOr(status, 1u);
         return;
     }
-    const uint32_t lead = s_out & 15u;
-    if (cnt) write_codes<C>(ck, start, cnt, stage + lead + (incl - cnt), t);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -394,7 +393,7 @@ __global__ __launch_bounds__(1024) void dfc_decode_kernel(const BatchArgs args) 
     t.kb = a.lut_bits;
     t.kshift = 32u - t.kb;
     t.step = reinterpret_cast<const uint32_t *>(lds);
-    t.sym = reinterpret_cast<const uint2 *>(lds + (4u << t.kb));
+    t.wsym = reinterpret_cast<const uint2 *>(lds + (4u << t.kb));
     t.mask = reinterpret_cast<const uint16_t *>(lds + (12u << t.kb));
     t.limit = reinterpret_cast<const uint32_t *>(lds + (14u << t.kb));
     t.first = t.limit + 32;
@@ -412,6 +411,8 @@ __global__ __launch_bounds__(1024) void dfc_decode_kernel(const BatchArgs args) 
     if (b >= hi_b) return;
     Chunk<C> cur;
     load_chunk<C>(a, b, lane, cur);
+    // Resident on entry, as it is on every later iteration (see wait_for).
+    wait_for(cur);
     for (;;) {
         const uint32_t s_out = __builtin_amdgcn_readlane(cur.meta, 0);
         const uint32_t e_out = __builtin_amdgcn_readlane(cur.meta, 1);
@@ -426,9 +427,9 @@ __global__ __launch_bounds__(1024) void dfc_decode_kernel(const BatchArgs args) 
         // next block's stream words, offsets and output range
         const uint32_t bn = b + waves;
         const bool more = bn < hi_b;
-        Chunk<C> nxt;
+        Chunk<C> nxt{};
         if (more) load_chunk<C>(a, bn, lane, nxt);
-        decode_block<C>(a, b, lane, cur, stage, t, args.status, R, s_out, e_out);
+        decode_block<C>(a, b, lane, cur, stage, t, args.status, R, s_out, e_out, nxt, more);
         if (!more) break;
         cur = nxt;
         b = bn;
@@ -570,7 +571,7 @@ dfc_status check_item(const dfc_batch_item &it) {
     if (in.lanes_per_block != 64) return DFC_EUNSUPPORTED;
     const uint32_t C = in.chunk_bytes;
     if (C != 4 && C != 8 && C != 16 && C != 32) return DFC_EINVAL;
-    if (in.lut_bits < 8 || in.lut_bits > 12 || in.min_len < 1 || in.lut_bits > 8 * in.min_len) return DFC_EINVAL;
+    if (in.lut_bits < 8 || in.lut_bits > 12 || in.min_len < 1) return DFC_EINVAL;
     if (in.max_block_elems > 64u * dfc::ceil_div(8ull * C, in.min_len)) return DFC_EINVAL;
     return DFC_OK;
 }

@@ -30,9 +30,10 @@ constexpr int lengths = 256;
 
 enum Section { kTables = 0, kWords, kOffsets, kBlockout, kRaw, kPanels, kNumSections };
 
-// Decode-table section layout for a k-bit window: step[2^k] (u32),
-// sym[2^k] (u64), mask[2^k] (u16), then limit[32], first[32], base[32]
-// (u32, index = code length) and order[256] (u8).
+// Decode-table section layout for a k-bit window: step[2^k] (u32, every
+// whole code in the window), wsym[2^k] (u64: rotated exponents of the first
+// <= 4 codes | their step << 32), mask[2^k] (u16), then limit[32],
+// first[32], base[32] (u32, index = code length) and order[256] (u8).
 constexpr uint32_t kStepEscape = 0xFFFFF000u;
 inline uint64_t tables_bytes(uint32_t k) { return 14ull * (1ull << k) + 3 * 128 + 256; }
 inline uint64_t tables_sym_off(uint32_t k) { return 4ull << k; }

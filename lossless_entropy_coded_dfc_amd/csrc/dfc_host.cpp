@@ -152,13 +152,14 @@ dfc_status package_merge(const uint64_t hist[256], uint32_t limit, uint8_t len[2
 // First-level table entry for a k-bit window (next k stream bits, first bit
 // most significant): the whole codes that fit, decoded from its first bit.
 struct Entry {
-    uint32_t step;  // (codes << 16) - bits, or kStepEscape
-    uint64_t sym;   // rotated exponent of code j in byte j
+    uint32_t step;  // (codes << 16) - bits over every whole code, or kStepEscape
+    uint64_t wsym;  // rotated exponents of the first <= 4 codes | their step << 32
     uint16_t mask;  // bit j: a code ends j + 1 bits in
 };
 
 Entry lut_entry(uint32_t window, uint32_t k, const Canon &c) {
-    uint32_t o = 0, n = 0;
+    uint32_t o = 0, n = 0, o4 = 0;
+    uint32_t syms = 0;
     Entry e{0, 0, 0};
     while (o < k) {
         uint32_t found = 0, v = 0;
@@ -171,22 +172,19 @@ Entry lut_entry(uint32_t window, uint32_t k, const Canon &c) {
         }
         if (!found) break;
         const uint32_t sym = c.order[c.base[found] + v - c.first[found]];
-        e.sym |= uint64_t(rotate_exponent(sym)) << (8 * n);  // n < 8: k <= 8 * shortest length
+        if (n < 4) {
+            syms |= rotate_exponent(sym) << (8 * n);
+            o4 += found;
+        }
         o += found;
         e.mask = uint16_t(e.mask | (1u << (o - 1)));
         ++n;
     }
     e.step = n ? (n << 16) - o : kStepEscape;
+    const uint32_t n4 = std::min(n, 4u);
+    const uint32_t step4 = n ? (n4 << 16) - o4 : kStepEscape;
+    e.wsym = uint64_t(syms) | (uint64_t(step4) << 32);
     return e;
-}
-
-// Window size used for a code: at most 8 * (shortest length), so that no
-// window holds more than 8 whole codes.
-uint32_t effective_lut_bits(const uint8_t len[256], uint32_t requested) {
-    uint32_t mn = 0;
-    for (int s = 0; s < 256; ++s)
-        if (len[s] && (!mn || len[s] < mn)) mn = len[s];
-    return mn ? std::min(requested, 8 * mn) : requested;
 }
 
 void build_tables(const uint8_t len[256], uint32_t k, uint8_t *out) {
@@ -195,7 +193,7 @@ void build_tables(const uint8_t len[256], uint32_t k, uint8_t *out) {
     for (uint32_t w = 0; w < (1u << k); ++w) {
         const Entry e = lut_entry(w, k, c);
         store_le<uint32_t>(out + 4ull * w, e.step);
-        store_le<uint64_t>(out + tables_sym_off(k) + 8ull * w, e.sym);
+        store_le<uint64_t>(out + tables_sym_off(k) + 8ull * w, e.wsym);
         store_le<uint16_t>(out + tables_mask_off(k) + 2ull * w, e.mask);
     }
     uint8_t *limit = out + tables_limit_off(k), *first = out + tables_first_off(k), *base = out + tables_base_off(k);
@@ -322,7 +320,7 @@ dfc_status dfc_encode(const uint16_t *src, uint64_t n, const dfc_params *pin, co
     Canon canon;
     uint32_t code[256];
     canonical(len, canon, code);
-    const uint32_t lut_bits = effective_lut_bits(len, p.lut_bits);
+    const uint32_t lut_bits = p.lut_bits;
 
     // Pass 1: bits per thread range.
     std::vector<uint64_t> range_bits(nt + 1, 0);
@@ -498,7 +496,6 @@ dfc_status dfc_blob_info(const void *blob_v, uint64_t bytes, dfc_info *out) {
     in.n_used = used;
     in.min_len = mn;
     in.max_len = mx;
-    if (mn && in.lut_bits > 8 * mn) return DFC_ECORRUPT;
 
     Layout L = layout_sizes(in.total_bits, in.chunk_bytes, in.lanes_per_block);
     if (L.n_blocks != in.n_blocks || L.n_chunks != in.n_chunks) return DFC_ECORRUPT;

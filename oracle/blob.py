@@ -29,8 +29,7 @@ each starts at the next multiple of 256 bytes and padding is zero:
 * offsets: 5-bit fields off[0..n_chunks] packed as in ``stream.pack_offsets``
 * blockout: uint32 out[0..n_blocks]
 * raw: the raw bytes (sign << 7 | mantissa), padded to a multiple of 16
-* tables: derived from the code lengths alone (see ``decode_tables``); the
-  header's lut_bits is min(requested, 8 * shortest code length).
+* tables: derived from the code lengths alone (see ``decode_tables``).
 
 The decode tables are the "compact hierarchical lookup tables" of the
 DFloat11 blog (section 03 item 1): a first level indexed by the next k stream
@@ -72,13 +71,6 @@ def rotate_exponent(e: int) -> int:
     return ((e >> 1) | ((e & 1) << 7)) & 0xFF
 
 
-def effective_lut_bits(lengths, lut_bits: int) -> int:
-    """Window size actually used: at most 8 * (shortest code length), so that
-    no window holds more than 8 whole codes."""
-    used = [int(l) for l in np.asarray(lengths) if l > 0]
-    return min(lut_bits, 8 * min(used)) if used else lut_bits
-
-
 def window_codes(window: int, k: int, tables):
     """Codes that fit in a k-bit window (next k stream bits, first bit most
     significant), decoded one after another from its first bit: a list of
@@ -99,48 +91,53 @@ def window_codes(window: int, k: int, tables):
     return out
 
 
-def lut_entry(window: int, k: int, tables):
-    """(step, sym, mask) for one k-bit window.
+def step_value(codes) -> int:
+    """(c << 16) - b as a uint32 for c codes of total length b; 0xFFFFF000
+    when there are none.  Adding it to an accumulator (count << 16) + (bias -
+    position) advances both the code count and the bit position."""
+    if not codes:
+        return ESCAPE
+    return ((len(codes) << 16) - sum(l for _, l in codes)) & 0xFFFFFFFF
 
-    step: (c << 16) - b as a uint32, where c whole codes of total length b fit
-          in the window; 0xFFFFF000 when the first code is longer than k bits.
-          Adding step to an accumulator (count << 16) + (bias - position)
-          advances both the code count and the bit position.
-    sym:  uint64, byte j = rotate_exponent(symbol j) for j < c, else 0.
+
+def lut_entry(window: int, k: int, tables):
+    """(step, wsym, mask) for one k-bit window.
+
+    step: step_value of every whole code inside the window (counting pass).
+    wsym: uint64; bits 0..31 hold rotate_exponent of the first min(c, 4)
+          codes (byte j = code j, 0 past them), bits 32..63 the step_value of
+          those codes (symbol pass).
     mask: uint16, bit j set when a code ends exactly j + 1 bits in.
     """
     codes = window_codes(window, k, tables)
-    if not codes:
-        return ESCAPE, 0, 0
-    if len(codes) > 8:
-        raise ValueError("more than 8 codes fit in one window")
-    b = sum(l for _, l in codes)
-    step = ((len(codes) << 16) - b) & 0xFFFFFFFF
-    sym = 0
+    first4 = codes[:4]
+    syms = 0
+    for j, (s, _) in enumerate(first4):
+        syms |= rotate_exponent(int(s)) << (8 * j)
+    wsym = syms | (step_value(first4) << 32)
     mask = 0
     o = 0
-    for j, (s, l) in enumerate(codes):
-        sym |= rotate_exponent(int(s)) << (8 * j)
+    for _, l in codes:
         o += l
         mask |= 1 << (o - 1)
-    return step, sym, mask
+    return step_value(codes), wsym, mask
 
 
 def decode_tables(lengths, lut_bits: int) -> bytes:
-    """The tables section for a window of k = lut_bits bits (k must not exceed
-    8 * shortest code length): step[2^k] (uint32), sym[2^k] (uint64),
-    mask[2^k] (uint16), then limit[32], first[32], base[32] (uint32, index =
-    code length; entries 0 and 25..31 are 0) and the 256-byte list of used
-    symbols ordered by (length, symbol)."""
+    """The tables section for a window of k = lut_bits bits: step[2^k]
+    (uint32), wsym[2^k] (uint64), mask[2^k] (uint16), then limit[32],
+    first[32], base[32] (uint32, index = code length; entries 0 and 25..31
+    are 0) and the 256-byte list of used symbols ordered by (length,
+    symbol)."""
     t = cb.canonical_tables(lengths)
     if not 8 <= lut_bits <= 12:
         raise ValueError("lut_bits must be in 8..12")
     n = 1 << lut_bits
     step = np.zeros(n, dtype=np.uint32)
-    sym = np.zeros(n, dtype=np.uint64)
+    wsym = np.zeros(n, dtype=np.uint64)
     mask = np.zeros(n, dtype=np.uint16)
     for w in range(n):
-        step[w], sym[w], mask[w] = lut_entry(w, lut_bits, t)
+        step[w], wsym[w], mask[w] = lut_entry(w, lut_bits, t)
     limit = np.zeros(32, dtype=np.uint32)
     first = np.zeros(32, dtype=np.uint32)
     base = np.zeros(32, dtype=np.uint32)
@@ -150,8 +147,9 @@ def decode_tables(lengths, lut_bits: int) -> bytes:
         base[l] = t["base"][l]
     order = np.zeros(256, dtype=np.uint8)
     order[: len(t["order"])] = t["order"]
-    return (step.astype("<u4").tobytes() + sym.astype("<u8").tobytes() + mask.astype("<u2").tobytes() +
-            limit.tobytes() + first.tobytes() + base.tobytes() + order.tobytes())
+    return (step.astype("<u4").tobytes() + wsym.astype("<u8").tobytes() + mask.astype("<u2").tobytes() +
+            limit.astype("<u4").tobytes() + first.astype("<u4").tobytes() + base.astype("<u4").tobytes() +
+            order.tobytes())
 
 
 def tables_bytes(lut_bits: int) -> int:
@@ -178,7 +176,6 @@ def write_blob(enc, lut_bits: int = 11, rows: int | None = None, cols: int | Non
         rows, cols = 1, n
     if rows * cols != n:
         raise ValueError("rows * cols != n")
-    lut_bits = effective_lut_bits(enc["lengths"], lut_bits)
     sizes = section_sizes(enc, lut_bits)
     offsets = {}
     pos = HEADER_BYTES

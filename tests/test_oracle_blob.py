@@ -17,29 +17,33 @@ from oracle import stream as st
 def parse_lut(tables: bytes, k: int):
     n = 1 << k
     step = np.frombuffer(tables, dtype="<u4", count=n)
-    sym = np.frombuffer(tables, dtype="<u8", count=n, offset=4 * n)
+    wsym = np.frombuffer(tables, dtype="<u8", count=n, offset=4 * n)
     mask = np.frombuffer(tables, dtype="<u2", count=n, offset=12 * n)
     rest = tables[14 * n:]
     limit = np.frombuffer(rest, dtype="<u4", count=32, offset=0)
     first = np.frombuffer(rest, dtype="<u4", count=32, offset=128)
     base = np.frombuffer(rest, dtype="<u4", count=32, offset=256)
     order = np.frombuffer(rest, dtype=np.uint8, count=256, offset=384)
-    return step, sym, mask, limit, first, base, order
+    return step, wsym, mask, limit, first, base, order
 
 
 def unrotate(b):
     return ((b << 1) | (b >> 7)) & 0xFF
 
 
+ESC = 0xFFFFF000
+
+
 def table_walk_decode(p):
     """Decode every chunk using only the table section, the way a GPU lane
     does: a counting pass that adds step entries into one accumulator
     (count in the high half, bit position in the low half) and corrects the
-    last lookup's overshoot with the boundary mask of the window at the
-    chunk's end, then a symbol pass that takes every symbol of a lookup and
-    falls back to the per-length tables for codes longer than k bits."""
+    last lookup's overshoot with the boundary mask of the window that starts
+    at the chunk's end, then a symbol pass that takes up to four symbols per
+    lookup (advancing by the entry's own step value) and falls back to the
+    per-length tables for codes longer than k bits."""
     k = p["lut_bits"]
-    step, sym, mask, limit, first, base, order = parse_lut(p["tables"], k)
+    step, wsym, mask, limit, first, base, order = parse_lut(p["tables"], k)
     words = [int(w) for w in p["words"]]
     C = p["chunk_bytes"]
     BIAS = 0x8000
@@ -69,7 +73,7 @@ def table_walk_decode(p):
         pos = start
         while pos < end:
             d = int(step[window(pos, k)])
-            if d == 0xFFFFF000:
+            if d == ESC:
                 d = (1 << 16) - long_code(pos)[1]
             acc = (acc + d) & 0xFFFFFFFF
             pos = start + BIAS - (acc & 0xFFFF)
@@ -77,19 +81,21 @@ def table_walk_decode(p):
         if pos > end:
             cnt -= bin(int(mask[window(end, k)]) & ((1 << (pos - end)) - 1)).count("1")
         # symbol pass
+        acc = BIAS
         pos, got = start, []
         while len(got) < cnt:
-            idx = window(pos, k)
-            d = int(step[idx])
-            if d == 0xFFFFF000:
+            e = int(wsym[window(pos, k)])
+            d = e >> 32
+            if d == ESC:
                 s, l = long_code(pos)
                 got.append(s)
-                pos += l
-                continue
-            c, b = (d >> 16) + 1, 0x10000 - (d & 0xFFFF)
-            take = min(c, cnt - len(got))
-            got += [unrotate((int(sym[idx]) >> (8 * j)) & 0xFF) for j in range(take)]
-            pos += b
+                d = (1 << 16) - l
+            else:
+                c = (d >> 16) + 1
+                take = min(c, cnt - len(got))
+                got += [unrotate((e >> (8 * j)) & 0xFF) for j in range(take)]
+            acc = (acc + d) & 0xFFFFFFFF
+            pos = start + BIAS - (acc & 0xFFFF)
         out += got
     return np.array(out, dtype=np.uint8)
 
@@ -123,12 +129,12 @@ def test_golden_lut_entries(golden):
     for s, l in g["lengths"].items():
         lens[int(s)] = l
     k = g["lut_bits"]
-    step, sym, mask, limit, first, base, order = parse_lut(bl.decode_tables(lens, k), k)
+    step, wsym, mask, limit, first, base, order = parse_lut(bl.decode_tables(lens, k), k)
     for ent in g["lut_entries"]:
         w = int(ent["window"], 2)
         assert int(step[w]) == int(ent["step_hex"], 16)
         assert int(step[w]) == ((ent["codes"] << 16) - ent["bits"]) & 0xFFFFFFFF
-        assert int(sym[w]) == int(ent["sym_hex"], 16)
+        assert int(wsym[w]) == int(ent["wsym_hex"], 16)
         assert int(mask[w]) == sum(1 << j for j in ent["mask_bits"])
     # canonical tables of the same code: 127:0, 126:10, 124:110, 125:111
     assert order[:4].tolist() == [127, 126, 124, 125]
@@ -145,9 +151,9 @@ def test_long_codes_escape():
     h = np.zeros(256, dtype=np.uint64)
     h[:40] = fib
     lens = cb.package_merge_lengths(h, 24)
-    step, sym, mask, *_ = parse_lut(bl.decode_tables(lens, 8), 8)
+    step, wsym, mask, *_ = parse_lut(bl.decode_tables(lens, 8), 8)
     # the all-ones window starts with the longest code (24 bits) -> escape
-    assert int(step[255]) == 0xFFFFF000 and int(sym[255]) == 0 and int(mask[255]) == 0
+    assert int(step[255]) == ESC and int(wsym[255]) == ESC << 32 and int(mask[255]) == 0
     # the all-zeros window starts with the shortest code
     assert int(step[0]) != 0xFFFFF000 and int(mask[0]) != 0
 
@@ -164,7 +170,7 @@ def test_table_walk_reproduces_data(kind, k):
     for C in (4, 16, 32):
         enc = st.encode(x, C, 64)
         p = bl.parse_blob(bl.write_blob(enc, k))
-        assert p["lut_bits"] == bl.effective_lut_bits(enc["lengths"], k)
+        assert p["lut_bits"] == k
         e, _ = fields.split(x)
         assert np.array_equal(table_walk_decode(p), e)
 
@@ -179,13 +185,12 @@ def test_size_within_two_percent_of_entropy_bound():
         assert 1.0 < ratio < limit
 
 
-def test_effective_window_keeps_at_most_eight_codes():
-    # one used symbol (plus the phantom) has 1-bit codes: the window shrinks to 8
+def test_one_bit_codes_fill_a_window():
+    # one used symbol (plus the phantom) has 1-bit codes: a 12-bit window holds
+    # 12 whole codes; the symbol entry keeps the first 4
     lens = np.zeros(256, dtype=np.uint8)
     lens[3] = lens[4] = 1
-    assert bl.effective_lut_bits(lens, 12) == 8
-    step, *_ = parse_lut(bl.decode_tables(lens, 8), 8)
-    assert all(((int(d) >> 16) + 1) <= 8 for d in step)
-    g = np.zeros(256, dtype=np.uint8)
-    g[:4] = [2, 2, 2, 2]
-    assert bl.effective_lut_bits(g, 12) == 12
+    step, wsym, mask, *_ = parse_lut(bl.decode_tables(lens, 12), 12)
+    assert int(step[0]) == ((12 << 16) - 12) and int(mask[0]) == 0xFFF
+    assert int(wsym[0]) == (((4 << 16) - 4) << 32) | 0x81818181   # rotate(3) = 0x81
+    assert int(step[0xFFF]) == ((12 << 16) - 12) and int(wsym[0xFFF]) & 0xFFFFFFFF == 0x02020202
