@@ -41,14 +41,27 @@ constexpr uint32_t kBias = 0x8000u;
 constexpr uint32_t kEscape = dfc::kStepEscape;
 constexpr int kMaxWaves = 16;
 
+// Raw buffer resources (base, 32-bit byte range) for every stream of an
+// item: loads past the range return zero and stores past it are dropped, so
+// lanes without work need no branch around their memory accesses.
+constexpr uint32_t kBufferConfig = 0x00020000u;  // dword 3 of a raw buffer resource on gfx9-family chips
+constexpr uint32_t kNowhere = 0xFFFFFFF0u;       // byte offset past every range the launcher accepts
+
+using u32x2 = __attribute__((ext_vector_type(2))) uint32_t;
+using u32x4 = __attribute__((ext_vector_type(4))) uint32_t;
+// Read-only global memory through the constant address space: uniform
+// indices load with scalar instructions.
+typedef const uint32_t __attribute__((address_space(4))) *const_u32_ptr;
+
 struct ItemArgs {
-    const uint32_t *words;     // code stream
+    const uint32_t *words;     // code stream (with its guard words)
     const uint32_t *offw;      // packed 5-bit chunk offsets
     const uint32_t *blockout;  // u32 out[n_blocks + 1]
     const uint8_t *raw;        // raw bytes (sign << 7 | mantissa), padded to 16
     const uint8_t *tables;     // derived decode tables
     uint16_t *dst;             // bf16 output
     uint64_t total_bits;
+    uint32_t words_bytes, offw_bytes, raw_bytes, dst_bytes;  // buffer ranges
     uint32_t n_blocks;
     uint32_t wg_begin;         // first workgroup of this item in the grid
     uint32_t blocks_per_wg;
@@ -56,6 +69,19 @@ struct ItemArgs {
     uint32_t lut_bits;
     uint32_t pad;
 };
+
+struct Buffers {
+    __amdgpu_buffer_rsrc_t words, offw, raw, dst;
+};
+
+__device__ __forceinline__ Buffers make_buffers(const ItemArgs &a) {
+    Buffers r;
+    r.words = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t *>(a.words), 0, int(a.words_bytes), kBufferConfig);
+    r.offw = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t *>(a.offw), 0, int(a.offw_bytes), kBufferConfig);
+    r.raw = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(a.raw), 0, int(a.raw_bytes), kBufferConfig);
+    r.dst = __builtin_amdgcn_make_buffer_rsrc(a.dst, 0, int(a.dst_bytes), kBufferConfig);
+    return r;
+}
 
 struct BatchArgs {
     ItemArgs item[DFC_MAX_BATCH];
@@ -87,28 +113,26 @@ __device__ __forceinline__ uint32_t long_code(uint32_t w24, const Tables &t, uin
     return l;
 }
 
-// Per-lane view of one chunk: its words plus two lookahead words, the start
-// offset of its first code and the end of its last code (chunk-relative
-// bits), and the block's output range.
+// Per-lane view of one chunk: its words plus two lookahead words, and the
+// two offset-array words that hold its start offset and the next chunk's.
 template <int C>
 struct Chunk {
     static constexpr int NW = C / 4;
     uint32_t w[NW + 2];
-    uint32_t o0, o1;  // the two offset-array words holding this chunk's field and the next
-    uint32_t meta;    // lane 0: out[b], lane 1: out[b + 1]
+    uint32_t o0, o1;
 };
 
 template <int C>
-__device__ __forceinline__ void load_chunk(const ItemArgs &a, uint32_t b, uint32_t lane, Chunk<C> &ck) {
-    const uint64_t chunk = uint64_t(b) * kWave + lane;
-    const uint32_t *p = a.words + chunk * (C / 4);
+__device__ __forceinline__ void load_chunk(const Buffers &bf, uint32_t b, uint32_t lane, Chunk<C> &ck) {
+    const uint32_t chunk = b * kWave + lane;
+    const uint32_t at = chunk * C;
     if constexpr (C == 4) {
-        ck.w[0] = p[0];
-        ck.w[1] = p[1];
-        ck.w[2] = p[2];
+        ck.w[0] = __builtin_amdgcn_raw_buffer_load_b32(bf.words, at, 0, 0);
+        ck.w[1] = __builtin_amdgcn_raw_buffer_load_b32(bf.words, at + 4u, 0, 0);
+        ck.w[2] = __builtin_amdgcn_raw_buffer_load_b32(bf.words, at + 8u, 0, 0);
     } else if constexpr (C == 8) {
-        const uint2 v = *reinterpret_cast<const uint2 *>(p);
-        const uint2 u = *reinterpret_cast<const uint2 *>(p + 2);
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(bf.words, at, 0, 0);
+        const u32x2 u = __builtin_amdgcn_raw_buffer_load_b64(bf.words, at + 8u, 0, 0);
         ck.w[0] = v.x;
         ck.w[1] = v.y;
         ck.w[2] = u.x;
@@ -116,22 +140,22 @@ __device__ __forceinline__ void load_chunk(const ItemArgs &a, uint32_t b, uint32
     } else {
 #pragma unroll
         for (int q = 0; q < C / 16; ++q) {
-            const uint4 v = *reinterpret_cast<const uint4 *>(p + 4 * q);
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(bf.words, at + 16u * q, 0, 0);
             ck.w[4 * q + 0] = v.x;
             ck.w[4 * q + 1] = v.y;
             ck.w[4 * q + 2] = v.z;
             ck.w[4 * q + 3] = v.w;
         }
-        const uint2 u = *reinterpret_cast<const uint2 *>(p + C / 4);
+        const u32x2 u = __builtin_amdgcn_raw_buffer_load_b64(bf.words, at + C, 0, 0);
         ck.w[C / 4] = u.x;
         ck.w[C / 4 + 1] = u.y;
     }
     // Only loads here: combining the words right away would make the
     // compiler wait for every load in flight, prefetches included.
-    const uint32_t *o = a.offw + ((5ull * chunk) >> 5);
-    ck.o0 = o[0];
-    ck.o1 = o[1];
-    ck.meta = a.blockout[b + min(lane, 1u)];
+    // Field `chunk` starts at bit 5 chunk of the offset array.
+    const uint32_t word = (chunk >> 5) * 5u + (((chunk & 31u) * 5u) >> 5);
+    ck.o0 = __builtin_amdgcn_raw_buffer_load_b32(bf.offw, 4u * word, 0, 0);
+    ck.o1 = __builtin_amdgcn_raw_buffer_load_b32(bf.offw, 4u * word + 4u, 0, 0);
 }
 
 // 32 stream bits starting at chunk-relative bit pos, 0 <= pos <= 32 (NW + 1).
@@ -189,36 +213,52 @@ __device__ __forceinline__ uint32_t count_codes(const Chunk<C> &ck, int start, i
     return cnt;
 }
 
-// Stores the 4 bytes of v at p, one naturally aligned byte store each.  On
-// gfx950 a wide LDS store to an address that is not a multiple of its width
-// is carried out one lane at a time; byte stores never are.
-__device__ __forceinline__ void store_4_bytes(uint8_t *p, uint32_t v) {
-    p[0] = uint8_t(v);
-    p[1] = uint8_t(v >> 8);
-    p[2] = uint8_t(v >> 16);
-    p[3] = uint8_t(v >> 24);
+// Makes the compiler wait for the loads into v now.  vmcnt also counts
+// stores on this chip, and the compiler cannot count the stores of the
+// divergent store paths below, so a register first used after a store would
+// make it wait for every store in flight to reach memory.
+template <typename T>
+__device__ __forceinline__ void wait_for(const T &v) {
+    static_assert(sizeof(T) % 4 == 0, "whole dwords only");
+    uint32_t w[sizeof(T) / 4];
+    __builtin_memcpy(w, &v, sizeof(T));
+#pragma unroll
+    for (unsigned i = 0; i < sizeof(T) / 4; ++i) asm volatile("" ::"v"(w[i]));
 }
 
-// Phase two: decode the chunk again and write its cnt (rotated) exponents to
-// LDS, at most four codes per lookup.  While four or more codes remain, all
-// four symbol bytes of a lookup are stored: bytes past the lookup's own codes
-// fall on positions this lane overwrites with its next lookup.  The last
-// < 4 codes are written exactly.
+// ORs the 4 bytes of v into the zeroed LDS staging bytes [q, q + 4): two
+// aligned dword ORs.  OR is what lets lanes overlap: a byte is only ever
+// ORed with zero or with its own final value.
+__device__ __forceinline__ void or_4_bytes(uint8_t *lds_base, uint32_t q, uint32_t v) {
+    const uint64_t x = uint64_t(v) << (8u * (q & 3u));
+    uint32_t *d = reinterpret_cast<uint32_t *>(lds_base + (q & ~3u));
+    __hip_atomic_fetch_or(d, uint32_t(x), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+    __hip_atomic_fetch_or(d + 1, uint32_t(x >> 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+}
+
+// Phase two: decode the chunk again and OR its (rotated) exponents into the
+// zeroed staging area, from byte q0 on, up to four codes per lookup.  A
+// table entry holds zero bytes past its own codes, and codes decoded past
+// the chunk's last one are the next chunk's first codes, identical to what
+// the next lane writes there; so neither needs to be cut off.  Lookups stop
+// at the chunk's end bit, which bounds the spill past the block's last
+// exponent to three codes.
 template <int C>
-__device__ __forceinline__ void write_codes(const Chunk<C> &ck, int start, uint32_t cnt, uint8_t *out,
-                                            const Tables &t) {
+__device__ __forceinline__ void write_codes(const Chunk<C> &ck, int start, int end, uint8_t *lds_base,
+                                            uint32_t q0, const Tables &t) {
     constexpr int NW = C / 4;
     uint32_t acc = kBias - uint32_t(start);
-    const uint32_t lim = cnt >= 4u ? (cnt - 3u) << 16 : 0u;  // acc < lim <=> done <= cnt - 4
 #pragma unroll
     for (int k = -1; k < NW; ++k) {
         const uint32_t hi = k < 0 ? 0u : ck.w[k < 0 ? 0 : k];
         const uint32_t lo = ck.w[k + 1];
+        // stay while shift >= 0 (pos <= 32 (k + 1)) and pos < end
+        const uint16_t g = uint16_t(kBias + uint32_t(max(0, 32 * (k + 1) - end + 1)));
         for (;;) {
-            while (uint16_t(acc) >= uint16_t(kBias) && acc < lim) {
+            while (uint16_t(acc) >= g) {
                 const uint32_t win = __builtin_amdgcn_alignbit(hi, lo, acc);
                 const uint2 e = t.wsym[win >> t.kshift];
-                store_4_bytes(out + (acc >> 16), e.x);
+                or_4_bytes(lds_base, q0 + (acc >> 16), e.x);
                 acc += e.y;
             }
             if (lo16(acc) >= kBias - 2048u) break;
@@ -226,29 +266,10 @@ __device__ __forceinline__ void write_codes(const Chunk<C> &ck, int start, uint3
             uint32_t sym;
             const uint32_t win = __builtin_amdgcn_alignbit(hi, lo, acc);
             const uint32_t l = long_code(win >> 8, t, sym);
-            out[acc >> 16] = uint8_t(sym);
+            or_4_bytes(lds_base, q0 + (acc >> 16), sym);
             acc += 0x10000u - l;
         }
         acc += 32u;
-    }
-    uint32_t done = acc >> 16;
-    uint32_t pos = uint32_t(32 * (NW + 1)) - lo16(acc) + kBias;
-    while (done < cnt && pos < uint32_t(32 * (NW + 1))) {
-        const uint32_t win = window_at<NW>(ck.w, pos);
-        const uint2 e = t.wsym[win >> t.kshift];
-        if (e.y == kEscape) {
-            uint32_t sym;
-            pos += long_code(win >> 8, t, sym);
-            out[done] = uint8_t(sym);
-            done += 1;
-        } else {
-            const uint32_t r = min((e.y >> 16) + 1u, cnt - done);
-            out[done] = uint8_t(e.x);
-            if (r > 1u) out[done + 1] = uint8_t(e.x >> 8);
-            if (r > 2u) out[done + 2] = uint8_t(e.x >> 16);
-            done += r;
-            pos += 0x10000u - (e.y & 0xFFFFu);
-        }
     }
 }
 
@@ -264,15 +285,16 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
     return x;
 }
 
-// 16 bf16 values from 16 staged (rotated) exponents and 16 raw bytes.  Per
+// 8 bf16 values from 8 staged (rotated) exponents and 8 raw bytes.  Per
 // pair of values, x1 = [raw_a, exp_a, raw_b, exp_b] and x2 = [exp_a, raw_a,
 // exp_b, raw_b] (bytes, low first); each output byte keeps bits 6..0 of x1
 // and bit 7 of x2.
-__device__ __forceinline__ void assemble16(const uint4 &E, const uint4 &R, uint32_t o[8]) {
-    const uint32_t e[4] = {E.x, E.y, E.z, E.w};
-    const uint32_t r[4] = {R.x, R.y, R.z, R.w};
+__device__ __forceinline__ u32x4 assemble8(const u32x2 &E, const u32x2 &R) {
+    const uint32_t e[2] = {E.x, E.y};
+    const uint32_t r[2] = {R.x, R.y};
+    uint32_t o[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < 2; ++q) {
         const uint32_t a1 = __builtin_amdgcn_perm(e[q], r[q], 0x05010400u);
         const uint32_t a2 = __builtin_amdgcn_perm(e[q], r[q], 0x01050004u);
         const uint32_t b1 = __builtin_amdgcn_perm(e[q], r[q], 0x07030602u);
@@ -280,51 +302,77 @@ __device__ __forceinline__ void assemble16(const uint4 &E, const uint4 &R, uint3
         o[2 * q] = (a1 & 0x7F7F7F7Fu) | (a2 & 0x80808080u);
         o[2 * q + 1] = (b1 & 0x7F7F7F7Fu) | (b2 & 0x80808080u);
     }
+    return u32x4{o[0], o[1], o[2], o[3]};
 }
 
-__device__ __forceinline__ void store_group(const ItemArgs &a, uint32_t g, uint32_t s_out, uint32_t e_out,
-                                            const uint32_t o[8]) {
-    const uint32_t j0 = 16u * g;
-    uint16_t *d = a.dst + j0;
-    if (j0 >= s_out && j0 + 16u <= e_out) {
-        reinterpret_cast<uint4 *>(d)[0] = make_uint4(o[0], o[1], o[2], o[3]);
-        reinterpret_cast<uint4 *>(d)[1] = make_uint4(o[4], o[5], o[6], o[7]);
-    } else {
+// Rounds of raw-byte octets (512 values per wavefront per round) prefetched
+// into registers before decoding: enough for a block of 64 chunks at about
+// 4 bits per code.
+template <int C>
+struct Prefetch {
+    static constexpr int N = C >= 32 ? 12 : C / 2;
+};
+
+// Wavefronts per SIMD the register budget is sized for (512 VGPRs per lane
+// shared by the resident wavefronts): 64 VGPRs give 8, the 32-byte chunk
+// path needs more registers and settles for 5.
+template <int C>
+struct Occupancy {
+    static constexpr int kWavesPerSimd = C >= 32 ? 5 : 8;
+};
+
+// Output range of one block and its octets (8 values, 16 output bytes).
+// Octets [full0, full1) lie wholly inside [s_out, e_out); the first and the
+// last octet may be shared with the neighbouring blocks.
+struct BlockRange {
+    uint32_t s_out, e_out;
+    uint32_t h0, nh;  // first octet, number of octets
+    uint32_t full0, full1;
+};
+
+__device__ __forceinline__ BlockRange block_range(uint32_t s_out, uint32_t e_out) {
+    BlockRange r;
+    r.s_out = s_out;
+    r.e_out = e_out;
+    r.h0 = s_out >> 3;
+    r.nh = ((e_out + 7u) >> 3) - r.h0;
+    r.full0 = (s_out & 7u) ? 1u : 0u;
+    r.full1 = (e_out & 7u) ? r.nh - 1u : r.nh;
+    return r;
+}
+
+// Octet i of the block (one per lane): whole octets go out as one 16-byte
+// buffer store (1 KB contiguous per wavefront); a shared octet stores only
+// its values inside the block, one 16-bit store each.
+__device__ __forceinline__ void store_octet(const Buffers &bf, const BlockRange &br, uint32_t i, const u32x4 &o) {
+    const uint32_t h = br.h0 + i;
+    const bool full = i - br.full0 < br.full1 - br.full0;
+    __builtin_amdgcn_raw_buffer_store_b128(o, bf.dst, full ? 16u * h : kNowhere, 0, 0);
+    if (!full && i < br.nh) {
+        const uint32_t v[4] = {o.x, o.y, o.z, o.w};
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            const uint32_t j = j0 + uint32_t(q);
-            if (j >= s_out && j < e_out) d[q] = uint16_t(o[q >> 1] >> (16 * (q & 1)));
+        for (int q = 0; q < 8; ++q) {
+            const uint32_t j = 8u * h + uint32_t(q);
+            const uint32_t at = (j >= br.s_out && j < br.e_out) ? 2u * j : kNowhere;
+            __builtin_amdgcn_raw_buffer_store_b16(uint16_t(v[q >> 1] >> (16 * (q & 1))), bf.dst, at, 0, 0);
         }
     }
 }
 
-// Makes the compiler wait for the loads into v now.  vmcnt also counts
-// stores on this chip, and the compiler cannot count the stores of the
-// divergent store paths below, so a register first used after a store would
-// make it wait for every store in flight to reach memory.
-template <typename T>
-__device__ __forceinline__ void wait_for(const T &v) {
-    static_assert(sizeof(T) % 4 == 0, "whole dwords only");
-    uint32_t w[sizeof(T) / 4];
-    __builtin_memcpy(w, &v, sizeof(T));
-#pragma unroll
-    for (unsigned i = 0; i < sizeof(T) / 4; ++i) asm volatile("" ::"v"(w[i]));
-}
-
-// Raw-byte groups prefetched into registers per lane before decoding.
 template <int C>
-struct Prefetch {
-    static constexpr int N = C >= 32 ? 6 : C / 4;
-};
-
-template <int C>
-__device__ __forceinline__ void decode_block(const ItemArgs &a, uint32_t b, uint32_t lane, const Chunk<C> &ck,
-                                             uint8_t *stage, const Tables &t, uint32_t *status,
-                                             const uint4 (&R)[Prefetch<C>::N], uint32_t s_out, uint32_t e_out,
-                                             const Chunk<C> &nxt, bool more) {
+__device__ __forceinline__ void decode_block(const ItemArgs &a, const Buffers &bf, uint32_t b, uint32_t lane,
+                                             const Chunk<C> &ck, uint8_t *stage, uint32_t stage_off,
+                                             uint32_t stage_bytes, const Tables &t, uint32_t *status,
+                                             const u32x2 (&R)[Prefetch<C>::N], const BlockRange &br,
+                                             const Chunk<C> &nxt) {
     constexpr int PF = Prefetch<C>::N;
+    // Zero the staging bytes this block ORs its exponents into: lead, the
+    // block's exponents, and the spill of its last lookup.
+    const uint32_t nz = min((br.s_out & 7u) + (br.e_out - br.s_out) + 8u, stage_bytes);
+    for (uint32_t o = 16u * lane; o + 16u <= ((nz + 15u) & ~15u); o += 16u * kWave)
+        *reinterpret_cast<uint4 *>(stage + o) = make_uint4(0, 0, 0, 0);
     const uint64_t chunk = uint64_t(b) * kWave + lane;
-    const uint32_t offpair = __builtin_amdgcn_alignbit(ck.o1, ck.o0, uint32_t((5ull * chunk) & 31));
+    const uint32_t offpair = __builtin_amdgcn_alignbit(ck.o1, ck.o0, uint32_t((5u * lane) & 31u));
     const int start = int(offpair & 31u);
     const int next_off = int((offpair >> 5) & 31u);
     const int64_t rem = int64_t(a.total_bits) - int64_t(chunk * (8ull * C));
@@ -335,9 +383,9 @@ __device__ __forceinline__ void decode_block(const ItemArgs &a, uint32_t b, uint
     const uint32_t total = __builtin_amdgcn_readlane(incl, kWave - 1);
     // A chunk of 8C bits holds at most 8C code starts; anything else (or a
     // total that disagrees with the block offsets) means a corrupt stream.
-    const bool bad = (total != e_out - s_out) | (__builtin_amdgcn_ballot_w64(cnt > 8u * C) != 0);
-    const uint32_t lead = s_out & 15u;
-    if (!bad && cnt) write_codes<C>(ck, start, cnt, stage + lead + (incl - cnt), t);
+    const bool bad = (total != br.e_out - br.s_out) | (__builtin_amdgcn_ballot_w64(cnt > 8u * C) != 0);
+    const uint32_t lead = br.s_out & 7u;
+    if (!bad && cnt) write_codes<C>(ck, start, end, stage - stage_off, stage_off + lead + (incl - cnt), t);
     // Everything prefetched must be in registers before the first store, on
     // every path to the next block.
     wait_for(R);
@@ -350,23 +398,22 @@ __device__ __forceinline__ void decode_block(const ItemArgs &a, uint32_t b, uint
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    const uint32_t g0 = s_out >> 4, g1 = (e_out + 15u) >> 4;
+    // Lanes past the block's last octet read its last staged octet again and
+    // store nowhere.
+    const uint32_t last = br.nh - 1u;
 #pragma unroll
     for (int j = 0; j < PF; ++j) {
-        const uint32_t g = g0 + lane + uint32_t(kWave * j);
-        if (g < g1) {
-            const uint4 E = *reinterpret_cast<const uint4 *>(stage + 16u * (g - g0));
-            uint32_t o[8];
-            assemble16(E, R[j], o);
-            store_group(a, g, s_out, e_out, o);
+        if (uint32_t(kWave * j) < br.nh) {
+            const uint32_t i = lane + uint32_t(kWave * j);
+            const u32x2 E = *reinterpret_cast<const u32x2 *>(stage + 8u * min(i, last));
+            store_octet(bf, br, i, assemble8(E, R[j]));
         }
     }
-    for (uint32_t g = g0 + lane + uint32_t(kWave * PF); g < g1; g += kWave) {
-        const uint4 E = *reinterpret_cast<const uint4 *>(stage + 16u * (g - g0));
-        const uint4 Rg = *reinterpret_cast<const uint4 *>(a.raw + 16ull * g);
-        uint32_t o[8];
-        assemble16(E, Rg, o);
-        store_group(a, g, s_out, e_out, o);
+    for (uint32_t j0 = uint32_t(kWave * PF); j0 < br.nh; j0 += kWave) {
+        const uint32_t i = lane + j0;
+        const u32x2 Ri = __builtin_amdgcn_raw_buffer_load_b64(bf.raw, 8u * (br.h0 + i), 0, 0);
+        const u32x2 E = *reinterpret_cast<const u32x2 *>(stage + 8u * min(i, last));
+        store_octet(bf, br, i, assemble8(E, Ri));
     }
     // The next block reuses this wavefront's staging area.
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -375,14 +422,16 @@ __device__ __forceinline__ void decode_block(const ItemArgs &a, uint32_t b, uint
 }
 
 template <int C>
-__global__ __launch_bounds__(1024) void dfc_decode_kernel(const BatchArgs args) {
+__global__ __launch_bounds__(1024, Occupancy<C>::kWavesPerSimd) void dfc_decode_kernel(const BatchArgs args) {
     extern __shared__ __align__(16) uint8_t lds[];
     constexpr int PF = Prefetch<C>::N;
     const uint32_t wg = blockIdx.x;
     uint32_t it = 0;
     for (uint32_t k = 1; k < args.count; ++k)
         if (wg >= args.item[k].wg_begin) it = k;
-    const ItemArgs &a = args.item[it];
+    const ItemArgs a = args.item[it];
+    const Buffers bf = make_buffers(a);
+    const const_u32_ptr blockout = (const_u32_ptr)(a.blockout);
 
     // Stage the decode tables in LDS (16 bytes per thread per step).
     for (uint32_t o = threadIdx.x * 16u; o < a.tables_bytes; o += blockDim.x * 16u)
@@ -403,36 +452,41 @@ __global__ __launch_bounds__(1024) void dfc_decode_kernel(const BatchArgs args) 
     const uint32_t waves = blockDim.x / kWave;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const uint32_t lane = threadIdx.x % kWave;
-    uint8_t *stage = lds + a.tables_bytes + wave * args.stage_bytes;
+    const uint32_t stage_off = a.tables_bytes + wave * args.stage_bytes;
+    uint8_t *stage = lds + stage_off;
     const uint32_t lo_b = (wg - a.wg_begin) * a.blocks_per_wg;
     const uint32_t hi_b = min(lo_b + a.blocks_per_wg, a.n_blocks);
 
     uint32_t b = lo_b + wave;
     if (b >= hi_b) return;
     Chunk<C> cur;
-    load_chunk<C>(a, b, lane, cur);
+    load_chunk<C>(bf, b, lane, cur);
+    uint32_t s_out = blockout[b], e_out = blockout[b + 1];
     // Resident on entry, as it is on every later iteration (see wait_for).
     wait_for(cur);
     for (;;) {
-        const uint32_t s_out = __builtin_amdgcn_readlane(cur.meta, 0);
-        const uint32_t e_out = __builtin_amdgcn_readlane(cur.meta, 1);
-        // raw bytes of this block's first PF groups per lane
-        uint4 R[PF];
-        const uint32_t g0 = s_out >> 4, g1 = (e_out + 15u) >> 4;
+        const BlockRange br = block_range(s_out, e_out);
+        // raw bytes of this block's first PF octets per lane
+        u32x2 R[PF];
 #pragma unroll
-        for (int j = 0; j < PF; ++j) {
-            const uint32_t g = g0 + lane + uint32_t(kWave * j);
-            R[j] = g < g1 ? *reinterpret_cast<const uint4 *>(a.raw + 16ull * g) : make_uint4(0, 0, 0, 0);
-        }
+        for (int j = 0; j < PF; ++j)
+            R[j] = __builtin_amdgcn_raw_buffer_load_b64(bf.raw, 8u * (br.h0 + lane + uint32_t(kWave * j)), 0, 0);
         // next block's stream words, offsets and output range
         const uint32_t bn = b + waves;
         const bool more = bn < hi_b;
         Chunk<C> nxt{};
-        if (more) load_chunk<C>(a, bn, lane, nxt);
-        decode_block<C>(a, b, lane, cur, stage, t, args.status, R, s_out, e_out, nxt, more);
+        uint32_t s_nxt = 0, e_nxt = 0;
+        if (more) {
+            load_chunk<C>(bf, bn, lane, nxt);
+            s_nxt = blockout[bn];
+            e_nxt = blockout[bn + 1];
+        }
+        decode_block<C>(a, bf, b, lane, cur, stage, stage_off, args.stage_bytes, t, args.status, R, br, nxt);
         if (!more) break;
         cur = nxt;
         b = bn;
+        s_out = s_nxt;
+        e_out = e_nxt;
     }
 }
 
@@ -491,18 +545,35 @@ dfc_status launch_group(const dfc_batch_item *items, const uint32_t *idx, uint32
         max_block = std::max(max_block, in.max_block_elems);
     }
     if (live.empty()) return DFC_OK;
-    // staging: lead (< 16) + elements + one 16-byte group of slack, rounded to 16
+    // staging: lead (< 8) + elements + spill of the last lookup, rounded to 16
     const uint32_t stage = (max_block + 32u + 15u) & ~15u;
-    // waves per workgroup: the most resident wavefronts per CU under the LDS budget
+    static bool attr_set = false;
+    if (!attr_set) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void *>(&dfc_decode_kernel<C>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, int(kLdsBytes)) != hipSuccess)
+            return DFC_EHIP;
+        attr_set = true;
+    }
+    // Resident workgroups per CU for w wavefronts each, under both the LDS
+    // and the register budget.
+    auto resident = [&](uint32_t w) -> int {
+        const uint32_t lds = max_tables + w * stage;
+        if (lds > kLdsBytes) return 0;
+        int per_cu = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(&dfc_decode_kernel<C>),
+                                                         int(w * kWave), size_t(lds)) != hipSuccess)
+            per_cu = int(kLdsBytes / lds);
+        return per_cu;
+    };
+    // waves per workgroup: the most resident wavefronts per CU, then the
+    // larger workgroup (fewer table copies)
     uint32_t waves = g_launch.waves;
     if (!waves) {
         uint32_t best = 0;
         for (uint32_t w = 4; w <= kMaxWaves; ++w) {
-            const uint32_t per = max_tables + w * stage;
-            if (per > kLdsBytes) break;
-            const uint32_t resident = std::min<uint32_t>(kLdsBytes / per, 32 / w) * w;
-            if (resident > best) {
-                best = resident;
+            const uint32_t r = uint32_t(std::max(0, resident(w))) * w;
+            if (r >= best && r > 0) {
+                best = r;
                 waves = w;
             }
         }
@@ -511,18 +582,8 @@ dfc_status launch_group(const dfc_batch_item *items, const uint32_t *idx, uint32
     while (waves > 1 && max_tables + waves * stage > kLdsBytes) --waves;
     const uint32_t lds = max_tables + waves * stage;
     if (lds > kLdsBytes) return DFC_EUNSUPPORTED;
-    static bool attr_set = false;
-    if (!attr_set) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void *>(&dfc_decode_kernel<C>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, int(kLdsBytes)) != hipSuccess)
-            return DFC_EHIP;
-        attr_set = true;
-    }
-    int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(&dfc_decode_kernel<C>),
-                                                     int(waves * kWave), size_t(lds)) != hipSuccess ||
-        per_cu <= 0)
-        per_cu = int(std::max(1u, kLdsBytes / lds));
+    int per_cu = resident(waves);
+    if (per_cu <= 0) per_cu = 1;
     uint64_t slots = uint64_t(per_cu) * uint64_t(device_cu_count());
     if (g_launch.blocks_per_wave) {
         // fixed work per workgroup instead of filling the machine exactly
@@ -544,6 +605,10 @@ dfc_status launch_group(const dfc_batch_item *items, const uint32_t *idx, uint32
         a.raw = base + in.off_raw;
         a.tables = base + in.off_tables;
         a.dst = bi.dst_dev;
+        a.words_bytes = uint32_t(in.words_bytes);
+        a.offw_bytes = uint32_t(in.offsets_bytes);
+        a.raw_bytes = uint32_t(in.raw_bytes);
+        a.dst_bytes = uint32_t(2 * in.n);
         a.total_bits = in.total_bits;
         a.n_blocks = uint32_t(in.n_blocks);
         a.blocks_per_wg = uint32_t(dfc::ceil_div(in.n_blocks, g[k]));
@@ -573,6 +638,10 @@ dfc_status check_item(const dfc_batch_item &it) {
     if (C != 4 && C != 8 && C != 16 && C != 32) return DFC_EINVAL;
     if (in.lut_bits < 8 || in.lut_bits > 12 || in.min_len < 1) return DFC_EINVAL;
     if (in.max_block_elems > 64u * dfc::ceil_div(8ull * C, in.min_len)) return DFC_EINVAL;
+    // Every stream is addressed with 32-bit byte offsets below kNowhere.
+    const uint64_t limit = kNowhere - 64u * 1024u;
+    if (2 * in.n > limit || in.words_bytes > limit || in.offsets_bytes > limit || in.raw_bytes > limit)
+        return DFC_EUNSUPPORTED;
     return DFC_OK;
 }
 
