@@ -58,8 +58,28 @@ def check(x, C=16, k=12, oracle=True, label=""):
 @pytest.mark.parametrize("C", [4, 8, 16, 32])
 def test_single_matrix_small_all_chunks(C):
     x = synth.gaussian((300, 1000), 0.02, (40, C))   # many blocks, ragged tail
-    for k in (8, 12):
+    for k in (8, 10, 11, 12):
         check(x, C, k, label=f"gauss300x1000 C{C}")
+
+
+def test_mixed_chunk_sizes_in_one_batch():
+    """One batch call with matrices of every chunk size and table width:
+    one launch per chunk size, items of different widths share a launch."""
+    xs = [synth.gaussian_with_outliers((97 + 13 * j, 1024 + 7 * j), 0.02, (53, j)) for j in range(8)]
+    cfg = [(4, 11), (8, 12), (16, 11), (32, 10), (16, 8), (8, 11), (4, 12), (32, 11)]
+    blobs = [dfc.encode(x, chunk_bytes=C, lut_bits=k) for x, (C, k) in zip(xs, cfg)]
+    infos = [dfc.blob_info(b) for b in blobs]
+    devs = [torch.from_numpy(b).cuda() for b in blobs]
+    outs = [torch.empty(int(i.n), dtype=torch.int16, device="cuda") for i in infos]
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    say("case mixed batch", cfg)
+    dfc.decode_batch(list(zip(devs, infos, outs)), status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    for x, o, b in zip(xs, outs, blobs):
+        got = o.cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, x.ravel())
+        assert np.array_equal(got, bl.decode_blob(bytes(b)))
 
 
 @pytest.mark.parametrize("kind", ["outliers", "uniform", "ladder", "bimodal", "t"])
