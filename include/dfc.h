@@ -48,7 +48,17 @@ typedef enum {
     DFC_EHIP = -5          /* a HIP runtime call failed */
 } dfc_status;
 
-enum { DFC_LAYOUT_FLAT = 0 };
+/* Element order of a container.  FLAT: row-major.  PANEL: the order the
+ * fused decode + matrix product consumes (dfc_decode_gemm): the matrix is cut
+ * into items of 32 rows x panel_k columns (row panels in order, then column
+ * slices; the last slice may be narrower); inside an item come 32 x 16
+ * sub-tiles, columns ascending, and inside a sub-tile element 8 l + j
+ * (l = 0..63, j = 0..7) is W[32 p + l % 32][c0 + 16 t + 8 (l / 32) + j], the
+ * A-operand order of a 32x32x16 bf16 matrix instruction.  Every item's codes
+ * start on a fresh chunk and form their own blocks; a table of first chunk,
+ * first block and code bits per item travels in the container. */
+enum { DFC_LAYOUT_FLAT = 0, DFC_LAYOUT_PANEL = 1 };
+enum { DFC_PANEL_ROWS = 32, DFC_PANEL_K_DEFAULT = 1024 };
 enum { DFC_MAX_BATCH = 32 };
 
 /* Encoder parameters; dfc_default_params fills the defaults. */
@@ -57,9 +67,12 @@ typedef struct {
     uint32_t lanes_per_block; /* T: chunks per block: 64 (default; one wavefront), 128 or 256 */
     uint32_t max_code_len;    /* code length limit, 1..24 (default 24) */
     uint32_t lut_bits;        /* k: bits indexed by the first-level decode table, 8..12 (default 11) */
-    uint32_t layout;          /* DFC_LAYOUT_FLAT: elements in row-major order */
+    uint32_t layout;          /* DFC_LAYOUT_FLAT (row-major) or DFC_LAYOUT_PANEL */
     uint32_t threads;         /* host encoder threads; 0 = min(hardware threads, 16) */
-    uint64_t rows, cols;      /* matrix shape recorded in the header; 0,0 = 1 x n */
+    uint32_t panel_k;         /* PANEL: columns per item, a multiple of 16 (0 = 1024) */
+    uint32_t reserved;        /* must be 0 */
+    uint64_t rows, cols;      /* matrix shape recorded in the header; 0,0 = 1 x n (FLAT only);
+                                 PANEL needs rows % 32 == 0 and cols % 16 == 0 */
 } dfc_params;
 
 /* A codebook: code length and canonical code of every exponent value. */
@@ -87,6 +100,9 @@ typedef struct {
     uint32_t chunk_bytes, lanes_per_block, max_code_len, lut_bits, layout;
     uint32_t n_used, min_len, max_len;
     uint32_t max_block_elems;  /* most elements any one block decodes */
+    uint32_t panel_rows, panel_k;  /* PANEL: 32 and columns per item; 0 for FLAT */
+    uint64_t n_items;              /* PANEL: items (32-row x panel_k-column slices) */
+    uint64_t off_panels, panels_bytes;  /* PANEL: per-item table, (n_items + 1) x 4 u32 */
 } dfc_info;
 
 /* One matrix of a batched decode. */

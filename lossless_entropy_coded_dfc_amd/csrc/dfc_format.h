@@ -6,6 +6,7 @@
 // each at the next multiple of 256 bytes, zero padding.  Little-endian.
 #pragma once
 
+#include <algorithm>
 #include <cstdint>
 #include <cstring>
 
@@ -64,15 +65,41 @@ struct SectionSizes {
     uint64_t bytes[kNumSections];
 };
 inline SectionSizes section_sizes(uint64_t n, uint64_t n_chunks, uint64_t n_blocks, uint32_t chunk_bytes,
-                                  uint32_t lut_bits) {
+                                  uint32_t lut_bits, uint64_t n_items = 0) {
     SectionSizes s;
     s.bytes[kTables] = tables_bytes(lut_bits);
     s.bytes[kWords] = 4 * (n_chunks * (chunk_bytes / 4) + kGuardWords);
     s.bytes[kOffsets] = 4 * (ceil_div(kOffsetBits * (n_chunks + 1), 32) + 1);
     s.bytes[kBlockout] = 4 * (n_blocks + 1);
     s.bytes[kRaw] = 16 * ceil_div(n, 16);
-    s.bytes[kPanels] = 0;
+    s.bytes[kPanels] = n_items ? 16 * (n_items + 1) : 0;
     return s;
+}
+
+// Panel layout geometry: items of 32 rows x panel_k columns, row panels
+// first, then column slices.
+constexpr uint32_t kPanelRows = 32;
+constexpr uint32_t kSubtileK = 16;
+struct PanelGeom {
+    uint64_t rows, cols, panel_k, slices, n_items;
+    uint64_t item_row0(uint64_t q) const { return kPanelRows * (q / slices); }
+    uint64_t item_col0(uint64_t q) const { return panel_k * (q % slices); }
+    uint64_t item_width(uint64_t q) const { return std::min<uint64_t>(panel_k, cols - item_col0(q)); }
+    uint64_t item_elem0(uint64_t q) const { return kPanelRows * (item_row0(q) / kPanelRows * cols + item_col0(q)); }
+    // Row-major source index of element i of item q.
+    uint64_t source(uint64_t q, uint64_t i) const {
+        const uint64_t t = i >> 9, l = (i >> 3) & 63, j = i & 7;
+        return (item_row0(q) + (l & 31)) * cols + item_col0(q) + kSubtileK * t + 8 * (l >> 5) + j;
+    }
+};
+inline bool panel_geom(uint64_t rows, uint64_t cols, uint64_t panel_k, PanelGeom &g) {
+    if (!rows || !cols || rows % kPanelRows || cols % kSubtileK || !panel_k || panel_k % kSubtileK) return false;
+    g.rows = rows;
+    g.cols = cols;
+    g.panel_k = panel_k;
+    g.slices = ceil_div(cols, panel_k);
+    g.n_items = rows / kPanelRows * g.slices;
+    return true;
 }
 
 // Places the sections after the header; returns the container size.

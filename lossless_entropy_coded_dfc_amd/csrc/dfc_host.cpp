@@ -212,8 +212,144 @@ bool params_ok(const dfc_params &p) {
     if (T != 64 && T != 128 && T != 256) return false;
     if (p.max_code_len < 1 || p.max_code_len > kMaxLen) return false;
     if (p.lut_bits < 8 || p.lut_bits > 12) return false;
-    if (p.layout != DFC_LAYOUT_FLAT) return false;
+    if (p.layout != DFC_LAYOUT_FLAT && p.layout != DFC_LAYOUT_PANEL) return false;
+    if (p.reserved) return false;
     return true;
+}
+
+// Header, code lengths and decode tables of a container (sections zeroed).
+void write_header(uint8_t *dst, const dfc_params &p, uint64_t n, uint64_t total_bits, uint64_t n_chunks,
+                  uint64_t n_blocks, uint64_t rows, uint64_t cols, const SectionSizes &sz,
+                  const uint64_t off[kNumSections], uint64_t blob_bytes, const uint8_t len[256]) {
+    store_le<uint32_t>(dst + hdr::magic, kMagic);
+    store_le<uint32_t>(dst + hdr::version, kVersion);
+    store_le<uint64_t>(dst + hdr::n, n);
+    store_le<uint64_t>(dst + hdr::total_bits, total_bits);
+    store_le<uint64_t>(dst + hdr::n_chunks, n_chunks);
+    store_le<uint64_t>(dst + hdr::n_blocks, n_blocks);
+    store_le<uint32_t>(dst + hdr::chunk_bytes, p.chunk_bytes);
+    store_le<uint32_t>(dst + hdr::lanes, p.lanes_per_block);
+    store_le<uint32_t>(dst + hdr::max_code_len, p.max_code_len);
+    store_le<uint32_t>(dst + hdr::lut_bits, p.lut_bits);
+    store_le<uint32_t>(dst + hdr::layout, p.layout);
+    store_le<uint32_t>(dst + hdr::panel_rows, p.layout == DFC_LAYOUT_PANEL ? kPanelRows : 0);
+    store_le<uint64_t>(dst + hdr::rows, rows);
+    store_le<uint64_t>(dst + hdr::cols, cols);
+    store_le<uint32_t>(dst + hdr::tile_k, p.layout == DFC_LAYOUT_PANEL ? p.panel_k : 0);
+    for (int i = 0; i < kNumSections; ++i) {
+        store_le<uint64_t>(dst + hdr::sections + 16 * i, off[i]);
+        store_le<uint64_t>(dst + hdr::sections + 16 * i + 8, sz.bytes[i]);
+    }
+    store_le<uint64_t>(dst + hdr::blob_bytes, blob_bytes);
+    std::memcpy(dst + hdr::lengths, len, 256);
+    build_tables(len, p.lut_bits, dst + off[kTables]);
+}
+
+void zero_parallel(uint8_t *dst, uint64_t bytes, uint32_t threads) {
+    const unsigned zt = pick_threads(threads, bytes / 4);
+    parallel_for(zt, [&](unsigned t) {
+        uint64_t a = bytes * t / zt, b = bytes * (t + 1) / zt;
+        std::memset(dst + a, 0, b - a);
+    });
+}
+
+// 5-bit offset fields, little-endian bit order.
+void pack_offsets(const std::vector<uint8_t> &offs, uint8_t *ow) {
+    for (uint64_t i = 0; i < offs.size(); ++i) {
+        const uint64_t g = kOffsetBits * i;
+        const uint64_t v = uint64_t(offs[i]) << (g & 31);
+        uint8_t *w0 = ow + 4 * (g >> 5);
+        store_le<uint32_t>(w0, load_le<uint32_t>(w0) | uint32_t(v));
+        if (v >> 32) store_le<uint32_t>(w0 + 4, load_le<uint32_t>(w0 + 4) | uint32_t(v >> 32));
+    }
+}
+
+// Panel layout: every item is packed on its own, from a fresh chunk, with
+// its own blocks (see dfc.h).  Items are independent, so threads take whole
+// items and never share a stream word.
+dfc_status encode_panel(const uint16_t *src, uint64_t n, const dfc_params &p, const uint8_t len[256],
+                        const uint32_t code[256], uint8_t *dst, uint64_t cap, uint64_t *written) {
+    PanelGeom g;
+    if (!panel_geom(p.rows, p.cols, p.panel_k, g) || g.rows * g.cols != n) return DFC_EINVAL;
+    const uint32_t C = p.chunk_bytes, T = p.lanes_per_block;
+    const uint64_t chunk_bits = 8ull * C;
+    const unsigned nt = unsigned(std::min<uint64_t>(pick_threads(p.threads, n), g.n_items));
+    // Pass 1: code bits per item.
+    std::vector<uint64_t> bits(g.n_items, 0);
+    parallel_for(nt, [&](unsigned t) {
+        for (uint64_t q = g.n_items * t / nt; q < g.n_items * (t + 1) / nt; ++q) {
+            const uint64_t nq = kPanelRows * g.item_width(q);
+            uint64_t b = 0;
+            for (uint64_t i = 0; i < nq; ++i) b += len[exponent_of(src[g.source(q, i)])];
+            bits[q] = b;
+        }
+    });
+    std::vector<uint64_t> first_chunk(g.n_items + 1, 0), first_block(g.n_items + 1, 0);
+    uint64_t total_bits = 0;
+    for (uint64_t q = 0; q < g.n_items; ++q) {
+        const uint64_t chunks = ceil_div(bits[q], chunk_bits);
+        first_chunk[q + 1] = first_chunk[q] + chunks;
+        first_block[q + 1] = first_block[q] + ceil_div(chunks, T);
+        total_bits += bits[q];
+    }
+    const uint64_t n_chunks = first_chunk[g.n_items], n_blocks = first_block[g.n_items];
+    if (n_chunks >= (uint64_t(1) << 32) || n_blocks >= (uint64_t(1) << 32)) return DFC_ESIZE;
+    SectionSizes sz = section_sizes(n, n_chunks, n_blocks, C, p.lut_bits, g.n_items);
+    uint64_t off[kNumSections];
+    const uint64_t blob_bytes = place_sections(sz, off);
+    if (cap < blob_bytes) return DFC_ESIZE;
+    zero_parallel(dst, blob_bytes, p.threads);
+    write_header(dst, p, n, total_bits, n_chunks, n_blocks, g.rows, g.cols, sz, off, blob_bytes, len);
+
+    uint8_t *words = dst + off[kWords];
+    uint8_t *raw = dst + off[kRaw];
+    uint8_t *blockout = dst + off[kBlockout];
+    uint8_t *panels = dst + off[kPanels];
+    std::vector<uint8_t> offs(n_chunks + 1, 0);
+    // Pass 2: pack every item.
+    parallel_for(nt, [&](unsigned t) {
+        for (uint64_t q = g.n_items * t / nt; q < g.n_items * (t + 1) / nt; ++q) {
+            const uint64_t nq = kPanelRows * g.item_width(q), e0 = g.item_elem0(q);
+            const uint64_t c0 = first_chunk[q], b0 = first_block[q], chunks = first_chunk[q + 1] - c0;
+            uint8_t *w = words + 4 * c0 * (C / 4);
+            uint64_t pos = 0, acc = 0, wi = 0, ci = 0;
+            uint32_t nacc = 0;
+            for (uint64_t i = 0; i < nq; ++i) {
+                const uint16_t b = src[g.source(q, i)];
+                const uint32_t e = exponent_of(b);
+                raw[e0 + i] = raw_of(b);
+                while (ci < chunks && ci * chunk_bits <= pos) {
+                    offs[c0 + ci] = uint8_t(pos - ci * chunk_bits);
+                    if (ci % T == 0) store_le<uint32_t>(blockout + 4 * (b0 + ci / T), uint32_t(e0 + i));
+                    ++ci;
+                }
+                const uint32_t l = len[e];
+                acc = (acc << l) | code[e];
+                nacc += l;
+                pos += l;
+                if (nacc >= 32) {
+                    nacc -= 32;
+                    store_le<uint32_t>(w + 4 * wi++, uint32_t(acc >> nacc));
+                }
+            }
+            if (nacc > 0) store_le<uint32_t>(w + 4 * wi, uint32_t(acc << (32 - nacc)));
+            while (ci < chunks) {
+                offs[c0 + ci] = uint8_t(bits[q] - ci * chunk_bits);
+                if (ci % T == 0) store_le<uint32_t>(blockout + 4 * (b0 + ci / T), uint32_t(e0 + nq));
+                ++ci;
+            }
+            uint8_t *row = panels + 16 * q;
+            store_le<uint32_t>(row, uint32_t(c0));
+            store_le<uint32_t>(row + 4, uint32_t(b0));
+            store_le<uint32_t>(row + 8, uint32_t(bits[q]));
+        }
+    });
+    store_le<uint32_t>(panels + 16 * g.n_items, uint32_t(n_chunks));
+    store_le<uint32_t>(panels + 16 * g.n_items + 4, uint32_t(n_blocks));
+    store_le<uint32_t>(blockout + 4 * n_blocks, uint32_t(n));
+    pack_offsets(offs, dst + off[kOffsets]);
+    *written = blob_bytes;
+    return DFC_OK;
 }
 
 uint64_t kraft(const uint8_t len[256]) {
@@ -281,6 +417,12 @@ dfc_status dfc_encode_bound(uint64_t n, const dfc_params *pin, uint64_t *max_byt
     const uint64_t bits = n * uint64_t(p.max_code_len);
     Layout L = layout_sizes(bits, p.chunk_bytes, p.lanes_per_block);
     SectionSizes s = section_sizes(n, L.n_chunks, L.n_blocks, p.chunk_bytes, p.lut_bits);
+    if (p.layout == DFC_LAYOUT_PANEL) {
+        // every item may add one partly used chunk and one partly used block
+        PanelGeom g;
+        if (!panel_geom(p.rows, p.cols, p.panel_k ? p.panel_k : uint32_t(DFC_PANEL_K_DEFAULT), g)) return DFC_EINVAL;
+        s = section_sizes(n, L.n_chunks + g.n_items, L.n_blocks + g.n_items, p.chunk_bytes, p.lut_bits, g.n_items);
+    }
     uint64_t off[kNumSections];
     *max_bytes = place_sections(s, off);
     return DFC_OK;
@@ -292,6 +434,11 @@ dfc_status dfc_encode(const uint16_t *src, uint64_t n, const dfc_params *pin, co
     if (pin) p = *pin; else dfc_default_params(&p);
     if ((!src && n) || !dst_v || !written || !params_ok(p)) return DFC_EINVAL;
     if (n >= (uint64_t(1) << 32)) return DFC_ESIZE;
+    if (p.layout == DFC_LAYOUT_PANEL) {
+        if (!p.panel_k) p.panel_k = DFC_PANEL_K_DEFAULT;
+        PanelGeom g;
+        if (!panel_geom(p.rows, p.cols, p.panel_k, g) || p.rows * p.cols != n) return DFC_EINVAL;
+    }
     uint64_t rows = p.rows, cols = p.cols;
     if (rows == 0 && cols == 0) {
         rows = 1;
@@ -321,6 +468,7 @@ dfc_status dfc_encode(const uint16_t *src, uint64_t n, const dfc_params *pin, co
     uint32_t code[256];
     canonical(len, canon, code);
     const uint32_t lut_bits = p.lut_bits;
+    if (p.layout == DFC_LAYOUT_PANEL) return encode_panel(src, n, p, len, code, dst, cap, written);
 
     // Pass 1: bits per thread range.
     std::vector<uint64_t> range_bits(nt + 1, 0);
@@ -339,35 +487,8 @@ dfc_status dfc_encode(const uint16_t *src, uint64_t n, const dfc_params *pin, co
     if (cap < blob_bytes) return DFC_ESIZE;
 
     // Zero the container (padding, guard words and stream words are OR-ed).
-    {
-        const unsigned zt = pick_threads(p.threads, blob_bytes / 4);
-        parallel_for(zt, [&](unsigned t) {
-            uint64_t a = blob_bytes * t / zt, b = blob_bytes * (t + 1) / zt;
-            std::memset(dst + a, 0, b - a);
-        });
-    }
-    store_le<uint32_t>(dst + hdr::magic, kMagic);
-    store_le<uint32_t>(dst + hdr::version, kVersion);
-    store_le<uint64_t>(dst + hdr::n, n);
-    store_le<uint64_t>(dst + hdr::total_bits, total_bits);
-    store_le<uint64_t>(dst + hdr::n_chunks, L.n_chunks);
-    store_le<uint64_t>(dst + hdr::n_blocks, L.n_blocks);
-    store_le<uint32_t>(dst + hdr::chunk_bytes, C);
-    store_le<uint32_t>(dst + hdr::lanes, T);
-    store_le<uint32_t>(dst + hdr::max_code_len, p.max_code_len);
-    store_le<uint32_t>(dst + hdr::lut_bits, lut_bits);
-    store_le<uint32_t>(dst + hdr::layout, p.layout);
-    store_le<uint32_t>(dst + hdr::panel_rows, 0);
-    store_le<uint64_t>(dst + hdr::rows, rows);
-    store_le<uint64_t>(dst + hdr::cols, cols);
-    store_le<uint32_t>(dst + hdr::tile_k, 0);
-    for (int i = 0; i < kNumSections; ++i) {
-        store_le<uint64_t>(dst + hdr::sections + 16 * i, off[i]);
-        store_le<uint64_t>(dst + hdr::sections + 16 * i + 8, sz.bytes[i]);
-    }
-    store_le<uint64_t>(dst + hdr::blob_bytes, blob_bytes);
-    std::memcpy(dst + hdr::lengths, len, 256);
-    build_tables(len, lut_bits, dst + off[kTables]);
+    zero_parallel(dst, blob_bytes, p.threads);
+    write_header(dst, p, n, total_bits, L.n_chunks, L.n_blocks, rows, cols, sz, off, blob_bytes, len);
 
     // Pass 2: pack codes, raw bytes, chunk offsets and block offsets.
     uint8_t *words = dst + off[kWords];
@@ -429,15 +550,7 @@ dfc_status dfc_encode(const uint16_t *src, uint64_t n, const dfc_params *pin, co
         store_le<uint32_t>(w, load_le<uint32_t>(w) | head[t]);
     }
     store_le<uint32_t>(blockout + 4 * L.n_blocks, uint32_t(n));
-    // 5-bit offset fields, little-endian bit order.
-    uint8_t *ow = dst + off[kOffsets];
-    for (uint64_t i = 0; i <= L.n_chunks; ++i) {
-        const uint64_t g = kOffsetBits * i;
-        const uint64_t v = uint64_t(offs[i]) << (g & 31);
-        uint8_t *w0 = ow + 4 * (g >> 5);
-        store_le<uint32_t>(w0, load_le<uint32_t>(w0) | uint32_t(v));
-        if (v >> 32) store_le<uint32_t>(w0 + 4, load_le<uint32_t>(w0 + 4) | uint32_t(v >> 32));
-    }
+    pack_offsets(offs, dst + off[kOffsets]);
     *written = blob_bytes;
     return DFC_OK;
 }
@@ -462,7 +575,8 @@ dfc_status dfc_blob_info(const void *blob_v, uint64_t bytes, dfc_info *out) {
     in.rows = load_le<uint64_t>(b + hdr::rows);
     in.cols = load_le<uint64_t>(b + hdr::cols);
     in.blob_bytes = load_le<uint64_t>(b + hdr::blob_bytes);
-    if (in.layout != DFC_LAYOUT_FLAT) return DFC_EUNSUPPORTED;
+    if (in.layout != DFC_LAYOUT_FLAT && in.layout != DFC_LAYOUT_PANEL) return DFC_EUNSUPPORTED;
+    const bool panel = in.layout == DFC_LAYOUT_PANEL;
     dfc_params p;
     dfc_default_params(&p);
     p.chunk_bytes = in.chunk_bytes;
@@ -471,9 +585,16 @@ dfc_status dfc_blob_info(const void *blob_v, uint64_t bytes, dfc_info *out) {
     p.lut_bits = in.lut_bits;
     if (!params_ok(p)) return DFC_ECORRUPT;
     if (in.n >= (uint64_t(1) << 32) || in.rows * in.cols != in.n) return DFC_ECORRUPT;
-    if (load_le<uint32_t>(b + hdr::panel_rows) || load_le<uint32_t>(b + hdr::tile_k) ||
-        load_le<uint32_t>(b + hdr::reserved))
+    PanelGeom g{};
+    if (panel) {
+        in.panel_rows = load_le<uint32_t>(b + hdr::panel_rows);
+        in.panel_k = load_le<uint32_t>(b + hdr::tile_k);
+        if (in.panel_rows != kPanelRows || !panel_geom(in.rows, in.cols, in.panel_k, g)) return DFC_ECORRUPT;
+        in.n_items = g.n_items;
+    } else if (load_le<uint32_t>(b + hdr::panel_rows) || load_le<uint32_t>(b + hdr::tile_k)) {
         return DFC_ECORRUPT;
+    }
+    if (load_le<uint32_t>(b + hdr::reserved)) return DFC_ECORRUPT;
     for (int i = 192; i < 256; ++i)
         if (b[i]) return DFC_ECORRUPT;
 
@@ -497,9 +618,13 @@ dfc_status dfc_blob_info(const void *blob_v, uint64_t bytes, dfc_info *out) {
     in.min_len = mn;
     in.max_len = mx;
 
-    Layout L = layout_sizes(in.total_bits, in.chunk_bytes, in.lanes_per_block);
-    if (L.n_blocks != in.n_blocks || L.n_chunks != in.n_chunks) return DFC_ECORRUPT;
-    SectionSizes sz = section_sizes(in.n, in.n_chunks, in.n_blocks, in.chunk_bytes, in.lut_bits);
+    if (!panel) {
+        Layout L = layout_sizes(in.total_bits, in.chunk_bytes, in.lanes_per_block);
+        if (L.n_blocks != in.n_blocks || L.n_chunks != in.n_chunks) return DFC_ECORRUPT;
+    } else if (in.n_chunks >= (uint64_t(1) << 32) || in.n_blocks >= (uint64_t(1) << 32)) {
+        return DFC_ECORRUPT;
+    }
+    SectionSizes sz = section_sizes(in.n, in.n_chunks, in.n_blocks, in.chunk_bytes, in.lut_bits, in.n_items);
     uint64_t off[kNumSections];
     const uint64_t blob_bytes = place_sections(sz, off);
     if (blob_bytes != in.blob_bytes) return DFC_ECORRUPT;
@@ -518,13 +643,43 @@ dfc_status dfc_blob_info(const void *blob_v, uint64_t bytes, dfc_info *out) {
     in.blockout_bytes = sz.bytes[kBlockout];
     in.off_raw = off[kRaw];
     in.raw_bytes = sz.bytes[kRaw];
-    in.coded_bytes = kHeaderBytes + sz.bytes[kWords] + sz.bytes[kOffsets] + sz.bytes[kBlockout] + sz.bytes[kRaw];
+    in.off_panels = off[kPanels];
+    in.panels_bytes = sz.bytes[kPanels];
+    in.coded_bytes = kHeaderBytes + sz.bytes[kWords] + sz.bytes[kOffsets] + sz.bytes[kBlockout] + sz.bytes[kRaw] +
+                     sz.bytes[kPanels];
 
     // Derived tables must match the lengths exactly.
     {
         std::vector<uint8_t> t(sz.bytes[kTables], 0);
         build_tables(len, in.lut_bits, t.data());
         if (std::memcmp(t.data(), b + off[kTables], t.size()) != 0) return DFC_ECORRUPT;
+    }
+    // Panel table: chunk and block counts follow from every item's bits.
+    std::vector<uint64_t> item_block;  // first block of every item (+ sentinel)
+    if (panel) {
+        const uint8_t *pt = b + off[kPanels];
+        const uint64_t chunk_bits = 8ull * in.chunk_bytes;
+        uint64_t bits_sum = 0;
+        item_block.resize(g.n_items + 1);
+        if (load_le<uint32_t>(pt) != 0 || load_le<uint32_t>(pt + 4) != 0) return DFC_ECORRUPT;
+        for (uint64_t q = 0; q <= g.n_items; ++q) {
+            const uint8_t *r = pt + 16 * q;
+            item_block[q] = load_le<uint32_t>(r + 4);
+            if (load_le<uint32_t>(r + 12)) return DFC_ECORRUPT;
+            if (q == g.n_items) {
+                if (load_le<uint32_t>(r) != in.n_chunks || item_block[q] != in.n_blocks || load_le<uint32_t>(r + 8))
+                    return DFC_ECORRUPT;
+                break;
+            }
+            const uint64_t bits = load_le<uint32_t>(r + 8), nq = kPanelRows * g.item_width(q);
+            const uint64_t chunks = uint64_t(load_le<uint32_t>(r + 16)) - load_le<uint32_t>(r);
+            const uint64_t blocks = uint64_t(load_le<uint32_t>(r + 20)) - item_block[q];
+            if (bits < nq * mn || bits > nq * mx) return DFC_ECORRUPT;
+            if (chunks != ceil_div(bits, chunk_bits) || blocks != ceil_div(chunks, in.lanes_per_block))
+                return DFC_ECORRUPT;
+            bits_sum += bits;
+        }
+        if (bits_sum != in.total_bits) return DFC_ECORRUPT;
     }
     // Chunk offsets: at most (longest code - 1) for live chunks, 0 elsewhere.
     {
@@ -536,7 +691,7 @@ dfc_status dfc_blob_info(const void *blob_v, uint64_t bytes, dfc_info *out) {
             uint64_t pair = load_le<uint32_t>(ow + 4 * (g >> 5)) |
                             (uint64_t(load_le<uint32_t>(ow + 4 * (g >> 5) + 4)) << 32);
             const uint32_t v = uint32_t(pair >> (g & 31)) & 31u;
-            const bool live = i < in.n_chunks && i * chunk_bits < in.total_bits;
+            const bool live = i < in.n_chunks && (panel || i * chunk_bits < in.total_bits);
             if (live ? v > max_off : v != 0) return DFC_ECORRUPT;
         }
     }
@@ -552,6 +707,9 @@ dfc_status dfc_blob_info(const void *blob_v, uint64_t bytes, dfc_info *out) {
             widest = std::max(widest, v - prev);
             prev = v;
         }
+        // every item's blocks start at its first element
+        for (uint64_t q = 0; panel && q < g.n_items; ++q)
+            if (load_le<uint32_t>(bo + 4 * item_block[q]) != g.item_elem0(q)) return DFC_ECORRUPT;
         in.max_block_elems = widest;
     }
     *out = in;

@@ -174,3 +174,63 @@ def test_size_accounting_gaussian():
         info = dfc.blob_info(dfc.encode(x, chunk_bytes=C))
         assert 1.0 < info.coded_bytes / bound < lim, C
         assert 1.45 < 2 * x.size / info.coded_bytes < 1.55  # ~1.5:1
+
+
+# ------------------------------------------------------------- panel layout
+
+from oracle import panel as pn  # noqa: E402
+
+
+@pytest.mark.parametrize("C", [4, 8, 16, 32])
+@pytest.mark.parametrize("shape,panel_k", [((64, 96), 32), ((96, 1040), 1024), ((128, 512), 128)])
+def test_panel_encoder_matches_oracle_bytes(C, shape, panel_k):
+    x = synth.gaussian_with_outliers(shape, 0.02, (64, C, shape[1]))
+    got = dfc.encode(x, chunk_bytes=C, layout=dfc.LAYOUT_PANEL, panel_k=panel_k)
+    want = pn.write_panel_blob(pn.encode_panel(x, panel_k=panel_k, chunk_bytes=C), 11)
+    assert bytes(got) == want
+    info = dfc.blob_info(got)
+    assert info.layout == dfc.LAYOUT_PANEL and info.panel_rows == 32 and info.panel_k == panel_k
+    assert info.n_items == len(pn.panel_items(*shape, panel_k))
+    assert info.panels_bytes == 16 * (info.n_items + 1)
+
+
+def test_panel_stress_kinds_and_threads():
+    for kind in synth.STRESS_KINDS:
+        x = {"student_t": lambda: synth.student_t((96, 272), 3.0, 0.02, (65,)),
+             "bimodal": lambda: synth.bimodal((96, 272), 0.02, (66,)),
+             "uniform": lambda: synth.uniform_bits((96, 272), (67,)),
+             "ladder": lambda: synth.exponent_ladder((96, 272), (68,))}[kind]()
+        want = pn.write_panel_blob(pn.encode_panel(x, panel_k=64, chunk_bytes=8), 10)
+        for threads in (1, 3, 16):
+            got = dfc.encode(x, chunk_bytes=8, lut_bits=10, layout=dfc.LAYOUT_PANEL, panel_k=64, threads=threads)
+            assert bytes(got) == want, (kind, threads)
+
+
+def test_panel_bad_shapes_rejected():
+    for shape, panel_k in (((48, 64), 16), ((64, 72), 16), ((64, 64), 24)):
+        x = synth.gaussian(shape, 0.02, (69,))
+        with pytest.raises(dfc.DfcError) as ei:
+            dfc.encode(x, layout=dfc.LAYOUT_PANEL, panel_k=panel_k)
+        assert ei.value.status == dfc.EINVAL
+
+
+def test_panel_validation_rejects_corruption():
+    x = synth.gaussian((96, 2048), 0.02, (70,))
+    b = dfc.encode(x, chunk_bytes=16, layout=dfc.LAYOUT_PANEL, panel_k=512)
+    info = dfc.blob_info(b)
+    pt = info.off_panels
+    first_block1 = struct.unpack_from("<I", bytes(b), pt + 16 + 4)[0]
+    cases = {
+        "panel_rows": corrupt(b, 60, struct.pack("<I", 16)),
+        "panel_k": corrupt(b, 80, struct.pack("<I", 24)),
+        "bits": corrupt(b, pt + 8, struct.pack("<I", 7)),
+        "first_chunk": corrupt(b, pt + 16, struct.pack("<I", 1)),
+        "first_block": corrupt(b, pt + 16 + 4, struct.pack("<I", first_block1 + 1)),
+        "reserved": corrupt(b, pt + 12, struct.pack("<I", 1)),
+        "sentinel": corrupt(b, pt + 16 * info.n_items + 8, struct.pack("<I", 1)),
+        "item_start": corrupt(b, info.off_blockout + 4 * first_block1, struct.pack("<I", 32 * 512 + 1)),
+    }
+    for name, bad in cases.items():
+        with pytest.raises(dfc.DfcError) as ei:
+            dfc.blob_info(bad)
+        assert ei.value.status == dfc.ECORRUPT, name

@@ -1,0 +1,147 @@
+"""Pins of the oracle's panel layout (the element order the fused decode +
+matrix product consumes) against its definition: hand-worked positions,
+permutation and round-trip properties, and a brute-force recount of every
+item's chunk and block metadata."""
+import numpy as np
+import pytest
+
+from lossless_entropy_coded_dfc_amd import synth
+from oracle import codebook as cb
+from oracle import fields
+from oracle import panel as pn
+from oracle import stream as st
+
+
+def test_items_cover_the_matrix_in_order():
+    items = pn.panel_items(64, 80, 32)
+    # two row panels, each cut into column slices of 32, 32 and 16
+    assert items == [(0, 0, 32), (0, 32, 32), (0, 64, 16), (32, 0, 32), (32, 32, 32), (32, 64, 16)]
+    with pytest.raises(ValueError):
+        pn.panel_items(48, 80, 32)   # rows not a multiple of 32
+    with pytest.raises(ValueError):
+        pn.panel_items(64, 72, 32)   # cols not a multiple of 16
+    with pytest.raises(ValueError):
+        pn.panel_items(64, 80, 24)   # panel_k not a multiple of 16
+
+
+def test_hand_worked_positions():
+    # one 32 x 16 sub-tile: element 8 l + j is W[l % 32, 8 (l // 32) + j]
+    o = pn.panel_order(32, 16, 16)
+    cols = 16
+    assert o[0] == 0 * cols + 0          # l 0, j 0
+    assert o[7] == 0 * cols + 7          # l 0, j 7
+    assert o[8] == 1 * cols + 0          # l 1
+    assert o[8 * 31] == 31 * cols + 0    # l 31
+    assert o[8 * 32] == 0 * cols + 8     # l 32: second half of the columns
+    assert o[8 * 32 + 7] == 0 * cols + 15
+    assert o[511] == 31 * cols + 15      # l 63, j 7
+    # the second sub-tile of an item continues 16 columns to the right
+    o = pn.panel_order(32, 48, 48)
+    assert o[512] == 16 and o[1024] == 32 and o[1024 + 8 * 33 + 2] == 1 * 48 + 32 + 8 + 2
+    # the next item of the same row panel starts at column panel_k
+    o = pn.panel_order(64, 32, 16)
+    assert o[512] == 16                  # item (0, 16)
+    assert o[1024] == 32 * 32            # item (32, 0): second row panel
+
+
+@pytest.mark.parametrize("shape,panel_k", [((32, 16), 16), ((64, 96), 32), ((96, 272), 64), ((128, 64), 1024)])
+def test_order_is_a_permutation(shape, panel_k):
+    o = pn.panel_order(*shape, panel_k)
+    assert o.size == shape[0] * shape[1]
+    assert np.array_equal(np.sort(o), np.arange(o.size))
+
+
+def test_subtiles_reproduce_the_product():
+    """Reading every 512-element run as a 32 x 16 tile (row l % 32, column
+    8 (l // 32) + j) and summing tile x X-slice products gives W X exactly
+    (small integers, so every sum is exact)."""
+    rng = np.random.default_rng(3)
+    M, K, B, Kp = 64, 96, 5, 32
+    w = rng.integers(-3, 4, size=(M, K)).astype(np.int64)
+    x = rng.integers(-3, 4, size=(K, B)).astype(np.int64)
+    seq = w.ravel()[pn.panel_order(M, K, Kp)]
+    y = np.zeros((M, B), dtype=np.int64)
+    pos = 0
+    for r0, c0, width in pn.panel_items(M, K, Kp):
+        for t in range(width // 16):
+            tile = np.zeros((32, 16), dtype=np.int64)
+            for l in range(64):
+                for j in range(8):
+                    tile[l % 32, 8 * (l // 32) + j] = seq[pos + 8 * l + j]
+            y[r0: r0 + 32] += tile @ x[c0 + 16 * t: c0 + 16 * t + 16]
+            pos += 512
+    assert pos == M * K
+    assert np.array_equal(y, w @ x)
+
+
+@pytest.mark.parametrize("C", [4, 8, 16, 32])
+@pytest.mark.parametrize("shape,panel_k", [((64, 96), 32), ((32, 1040), 1024), ((96, 512), 128)])
+def test_round_trip(C, shape, panel_k):
+    x = synth.gaussian_with_outliers(shape, 0.02, (60, C, shape[1]))
+    enc = pn.encode_panel(x, panel_k=panel_k, chunk_bytes=C)
+    blob = pn.write_panel_blob(enc, 11)
+    assert np.array_equal(pn.decode_panel_blob(blob), x)
+
+
+def test_item_metadata_recount():
+    """Every item starts on a fresh chunk with offset 0, has exactly the
+    chunks its bits need, its own blocks, and block offsets that count the
+    codes before each block's first bit."""
+    x = synth.student_t((96, 400), 3.0, 0.02, (61,))
+    C, T, Kp = 8, 64, 64
+    enc = pn.encode_panel(x, panel_k=Kp, chunk_bytes=C, lanes=T)
+    items = pn.panel_items(96, 400, Kp)
+    table = enc["items"].astype(np.int64)
+    seq = x.ravel()[pn.panel_order(96, 400, Kp)]
+    e, _ = fields.split(seq)
+    lens = enc["lengths"].astype(np.int64)[e]
+    elem0 = 0
+    for q, (_, _, w) in enumerate(items):
+        nq = 32 * w
+        bits = int(lens[elem0: elem0 + nq].sum())
+        c0, b0 = table[q, 0], table[q, 1]
+        chunks = table[q + 1, 0] - c0
+        assert table[q, 2] == bits
+        assert chunks == -(-bits // (8 * C))
+        assert table[q + 1, 1] - b0 == -(-chunks // T)
+        assert enc["off"][c0] == 0
+        # brute force: code starts of this item, in item-relative bits
+        starts = np.concatenate([[0], np.cumsum(lens[elem0: elem0 + nq])[:-1]])
+        for c in range(chunks):
+            later = starts[starts >= 8 * C * c]
+            first = later[0] if later.size else bits
+            assert enc["off"][c0 + c] == first - 8 * C * c
+        for b in range(table[q + 1, 1] - b0):
+            assert enc["out"][b0 + b] == elem0 + np.count_nonzero(starts < 8 * C * T * b)
+        elem0 += nq
+    assert table[-1, 0] == enc["n_chunks"] and table[-1, 1] == enc["n_blocks"]
+    assert enc["out"][-1] == x.size
+
+
+def test_every_item_decodes_alone():
+    x = synth.gaussian((64, 160), 0.02, (62,))
+    C = 4
+    enc = pn.encode_panel(x, panel_k=48, chunk_bytes=C)
+    seq = x.ravel()[pn.panel_order(64, 160, 48)]
+    e, _ = fields.split(seq)
+    table = enc["items"].astype(np.int64)
+    elem0 = 0
+    for q, (_, _, w) in enumerate(pn.panel_items(64, 160, 48)):
+        c0, c1, bits = table[q, 0], table[q + 1, 0], table[q, 2]
+        words = enc["words"][c0 * (C // 4): c1 * (C // 4)]
+        got = st.decode_sequential(np.append(words, [0, 0]), 32 * w, enc["lengths"])
+        assert np.array_equal(got, e[elem0: elem0 + 32 * w])
+        elem0 += 32 * w
+
+
+def test_size_overhead_is_per_item_padding_only():
+    x = synth.gaussian((256, 2048), 0.02, (63,))
+    C = 16
+    flat = st.encode(x, C, 64)
+    enc = pn.encode_panel(x, panel_k=1024, chunk_bytes=C)
+    # same codebook, same code bits; at most one partly used chunk per item
+    assert np.array_equal(enc["lengths"], flat["lengths"])
+    assert enc["total_bits"] == flat["total_bits"]
+    used = -(-flat["total_bits"] // (8 * C))
+    assert used <= enc["n_chunks"] <= used + enc["n_items"]
+    assert cb.code_cost(enc["hist"], enc["lengths"]) == enc["total_bits"]
