@@ -174,6 +174,29 @@ dfc_status dfc_decode(const void *blob_dev, const dfc_info *info, uint16_t *dst_
 dfc_status dfc_decode_batch(const dfc_batch_item *items, uint32_t count, uint32_t *status_dev,
                             void *stream);
 
+enum { DFC_GEMM_MAX_BATCH = 64 };
+
+/* Fused decode + matrix product Y = W X (DFloat11 blog, introduction:
+ * weights are decompressed on the GPU just before use; here the decoded
+ * weights go from LDS straight into bf16 matrix instructions and never reach
+ * HBM).  Device, asynchronous on stream.
+ * w_blob_dev: device copy (256-byte aligned) of a DFC_LAYOUT_PANEL container
+ * of W (M x K bf16, M = info->rows, K = info->cols), described by info.
+ * x_dev: B activation vectors of K bf16 each, x_dev[b K + k] (i.e. X is
+ * K x B column-major), 16-byte aligned.  batch: B, 1..DFC_GEMM_MAX_BATCH.
+ * y_dev: B output vectors of M fp32, y_dev[b M + m] (Y = W X, M x B
+ * column-major), 4-byte aligned; overwritten (the call first zeroes it on the
+ * stream).  Products of bf16 pairs are exact and accumulate in fp32; the
+ * partial sums of different column slices of W are added with fp32 atomics,
+ * so the last bits of Y may differ from run to run.  status_dev: as in
+ * dfc_decode (nonzero if a block's decoded count disagrees with its block
+ * offsets; Y is then incomplete).  Errors before launch: DFC_EINVAL (null or
+ * misaligned pointers, batch out of range, bad decode parameters),
+ * DFC_EUNSUPPORTED (not a panel-layout container, lanes_per_block != 64,
+ * streams past 4 GiB), DFC_EHIP (launch failure). */
+dfc_status dfc_decode_gemm(const void *w_blob_dev, const dfc_info *info, const uint16_t *x_dev, uint32_t batch,
+                           float *y_dev, uint32_t *status_dev, void *stream);
+
 /* Launch tuning knob for benchmarks: wavefronts per workgroup (4, 8 or 16)
  * and wave-blocks each wavefront decodes (1..64).  0 = automatic.  Returns
  * DFC_EINVAL for other values.  Process-wide; not thread-safe. */

@@ -120,6 +120,9 @@ def library():
     lib.dfc_decode_batch.argtypes = [ctypes.POINTER(BatchItem), ctypes.c_uint32, ctypes.c_void_p,
                                      ctypes.c_void_p]
     lib.dfc_decode_batch.restype = st
+    lib.dfc_decode_gemm.argtypes = [ctypes.c_void_p, ctypes.POINTER(Info), ctypes.c_void_p, ctypes.c_uint32,
+                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.dfc_decode_gemm.restype = st
     lib.dfc_set_launch.argtypes = [ctypes.c_uint32, ctypes.c_uint32]
     lib.dfc_set_launch.restype = st
     lib.dfc_status_str.argtypes = [ctypes.c_int]
@@ -263,6 +266,25 @@ def decode_batch(items, status=None, stream=None):
         arr[k].n = info.n
     _check(library().dfc_decode_batch(arr, len(items), ctypes.c_void_p(_dev_ptr(status)), _stream(stream)),
            "dfc_decode_batch")
+
+
+GEMM_MAX_BATCH = 64
+
+
+def decode_gemm(blob_dev, info: Info, x, y, status=None, stream=None):
+    """Fused decode + product: y[b, :] = W @ x[b, :] for a panel-layout
+    container of W (M x K).  x: contiguous 16-bit device tensor of shape
+    (B, K) (bf16 bits); y: contiguous float32 device tensor of shape (B, M)."""
+    if info.layout != LAYOUT_PANEL:
+        raise ValueError("decode_gemm needs a panel-layout container")
+    if x.dim() != 2 or y.dim() != 2 or not x.is_contiguous() or not y.is_contiguous():
+        raise ValueError("x and y must be contiguous 2-D tensors")
+    B, K = x.shape
+    if x.element_size() != 2 or K != info.cols or tuple(y.shape) != (B, info.rows) or y.element_size() != 4:
+        raise ValueError("x must be (B, K) 16-bit and y (B, M) float32 for the container's M x K")
+    _check(library().dfc_decode_gemm(ctypes.c_void_p(_dev_ptr(blob_dev)), ctypes.byref(info),
+                                     ctypes.c_void_p(_dev_ptr(x)), B, ctypes.c_void_p(_dev_ptr(y)),
+                                     ctypes.c_void_p(_dev_ptr(status)), _stream(stream)), "dfc_decode_gemm")
 
 
 def set_launch(waves_per_group: int = 0, blocks_per_wave: int = 0):

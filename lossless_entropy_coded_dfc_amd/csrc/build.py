@@ -47,11 +47,14 @@ def build(verbose: bool = False, out: str = OUT) -> str:
     os.makedirs(objdir, exist_ok=True)
     inc = ["-I", INCLUDE, "-I", HERE]
     host_obj = os.path.join(objdir, "dfc_host.o")
-    dec_obj = os.path.join(objdir, "dfc_decode.o")
     _run(["g++", *CXX_FLAGS, *inc, "-c", os.path.join(HERE, "dfc_host.cpp"), "-o", host_obj], verbose)
-    _run([hipcc, *HIP_FLAGS, *inc, "-c", os.path.join(HERE, "dfc_decode.hip"), "-o", dec_obj], verbose)
+    dev_objs = []
+    for name in ("dfc_decode", "dfc_gemm"):
+        obj = os.path.join(objdir, name + ".o")
+        _run([hipcc, *HIP_FLAGS, *inc, "-c", os.path.join(HERE, name + ".hip"), "-o", obj], verbose)
+        dev_objs.append(obj)
     tmp = out + ".tmp"
-    _run([hipcc, "-shared", f"--offload-arch={ARCH}", "-fPIC", "-o", tmp, host_obj, dec_obj, "-pthread"], verbose)
+    _run([hipcc, "-shared", f"--offload-arch={ARCH}", "-fPIC", "-o", tmp, host_obj, *dev_objs, "-pthread"], verbose)
     os.replace(tmp, out)
     return out
 

@@ -1,0 +1,300 @@
+// dfc_decode_core.h - device-side building blocks shared by the gfx950
+// kernels of libdfc (the flat decoder and the fused decode + matrix product).
+//
+// DFloat11 blog ("70% Size, 100% Accuracy ... (DFloat11)"), section 03:
+// item 1, compact hierarchical lookup tables in on-chip memory (the k-bit
+// first-level tables and the per-length canonical tables, staged in LDS);
+// item 2, a two-phase decode (count the codes of every chunk, scan the counts
+// into write positions across the wavefront, then decode again and write).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "dfc.h"
+#include "dfc_format.h"
+
+namespace {
+
+constexpr int kWave = 64;
+// Accumulator = (codes << 16) + (kBias + shift), shift = bits from the
+// current position to the end of the current 32-bit word pair's first word.
+// kBias keeps the low half from borrowing and is a multiple of 32, so the
+// low 5 bits of the accumulator are the funnel-shift amount.
+constexpr uint32_t kBias = 0x8000u;
+constexpr uint32_t kEscape = dfc::kStepEscape;
+constexpr int kMaxWaves = 16;
+
+// Raw buffer resources (base, 32-bit byte range) for every stream of an
+// item: loads past the range return zero and stores past it are dropped, so
+// lanes without work need no branch around their memory accesses.
+constexpr uint32_t kBufferConfig = 0x00020000u;  // dword 3 of a raw buffer resource on gfx9-family chips
+constexpr uint32_t kNowhere = 0xFFFFFFF0u;       // byte offset past every range the launcher accepts
+
+using u32x2 = __attribute__((ext_vector_type(2))) uint32_t;
+using u32x4 = __attribute__((ext_vector_type(4))) uint32_t;
+// Read-only global memory through the constant address space: uniform
+// indices load with scalar instructions.
+typedef const uint32_t __attribute__((address_space(4))) *const_u32_ptr;
+
+struct Tables {
+    const uint32_t *step;  // every whole code in the window (counting pass)
+    const uint2 *wsym;     // x: rotated exponents of the first <= 4 codes, y: their step
+    const uint16_t *mask;
+    const uint32_t *limit, *first, *base;
+    const uint8_t *order;
+    uint32_t kshift;  // 32 - k
+    uint32_t kb;
+};
+
+__device__ __forceinline__ uint32_t lo16(uint32_t a) { return a & 0xFFFFu; }
+
+// Codes longer than the first-level window: the smallest length l with
+// window < limit[l] (left-justified 24-bit comparison), then the symbol by
+// canonical rank.  Returns the length; sym receives the rotated exponent.
+__device__ __forceinline__ uint32_t long_code(uint32_t w24, const Tables &t, uint32_t &sym) {
+    uint32_t l = t.kb + 1;
+    while (l < 24u && w24 >= t.limit[l]) ++l;
+    const uint32_t e = t.order[t.base[l] + (w24 >> (24u - l)) - t.first[l]];
+    sym = ((e >> 1) | (e << 7)) & 0xFFu;
+    return l;
+}
+
+// Per-lane view of one chunk: its words plus two lookahead words, and the
+// two offset-array words that hold its start offset and the next chunk's.
+template <int C>
+struct Chunk {
+    static constexpr int NW = C / 4;
+    uint32_t w[NW + 2];
+    uint32_t o0, o1;
+};
+
+// Chunk `chunk` of a stream: its words through the buffer resource `words`,
+// its offset-array words through `offw`.
+template <int C>
+__device__ __forceinline__ void load_chunk(__amdgpu_buffer_rsrc_t words, __amdgpu_buffer_rsrc_t offw, uint32_t chunk,
+                                           Chunk<C> &ck) {
+    const uint32_t at = chunk * C;
+    if constexpr (C == 4) {
+        ck.w[0] = __builtin_amdgcn_raw_buffer_load_b32(words, at, 0, 0);
+        ck.w[1] = __builtin_amdgcn_raw_buffer_load_b32(words, at + 4u, 0, 0);
+        ck.w[2] = __builtin_amdgcn_raw_buffer_load_b32(words, at + 8u, 0, 0);
+    } else if constexpr (C == 8) {
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(words, at, 0, 0);
+        const u32x2 u = __builtin_amdgcn_raw_buffer_load_b64(words, at + 8u, 0, 0);
+        ck.w[0] = v.x;
+        ck.w[1] = v.y;
+        ck.w[2] = u.x;
+        ck.w[3] = u.y;
+    } else {
+#pragma unroll
+        for (int q = 0; q < C / 16; ++q) {
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(words, at + 16u * q, 0, 0);
+            ck.w[4 * q + 0] = v.x;
+            ck.w[4 * q + 1] = v.y;
+            ck.w[4 * q + 2] = v.z;
+            ck.w[4 * q + 3] = v.w;
+        }
+        const u32x2 u = __builtin_amdgcn_raw_buffer_load_b64(words, at + C, 0, 0);
+        ck.w[C / 4] = u.x;
+        ck.w[C / 4 + 1] = u.y;
+    }
+    // Only loads here: combining the words right away would make the
+    // compiler wait for every load in flight, prefetches included.
+    // Field `chunk` starts at bit 5 chunk of the offset array.
+    const uint32_t word = (chunk >> 5) * 5u + (((chunk & 31u) * 5u) >> 5);
+    ck.o0 = __builtin_amdgcn_raw_buffer_load_b32(offw, 4u * word, 0, 0);
+    ck.o1 = __builtin_amdgcn_raw_buffer_load_b32(offw, 4u * word + 4u, 0, 0);
+}
+
+// 32 stream bits starting at chunk-relative bit pos, 0 <= pos <= 32 (NW + 1).
+template <int NW>
+__device__ __forceinline__ uint32_t window_at(const uint32_t (&w)[NW + 2], uint32_t pos) {
+    const uint32_t j = (pos + 31) >> 5;  // pos in (32 (j - 1), 32 j]
+    uint32_t hi = 0, lo = w[0];
+#pragma unroll
+    for (int q = 1; q <= NW + 1; ++q) {
+        if (j == uint32_t(q)) {
+            hi = w[q - 1];
+            lo = w[q];
+        }
+    }
+    return __builtin_amdgcn_alignbit(hi, lo, 32u * j - pos);
+}
+
+// Phase one: number of codes that start in [start, end) (chunk-relative).
+// The k-loop walks the chunk one word at a time so that every window is a
+// funnel shift of two registers: a code starting at pos in (32k, 32k + 32]
+// lies inside words k and k + 1.  Each lookup adds step = (codes << 16) -
+// bits for every whole code inside the k-bit window; the last lookup may
+// count codes that start at or after `end`, which are removed with the
+// boundary mask of the window that starts at `end`.
+template <int C>
+__device__ __forceinline__ uint32_t count_codes(const Chunk<C> &ck, int start, int end, const Tables &t) {
+    constexpr int NW = C / 4;
+    uint32_t acc = kBias - uint32_t(start);
+#pragma unroll
+    for (int k = -1; k < NW; ++k) {
+        const uint32_t hi = k < 0 ? 0u : ck.w[k < 0 ? 0 : k];
+        const uint32_t lo = ck.w[k + 1];
+        // stay while shift >= 0 (pos <= 32 (k + 1)) and pos < end
+        const uint16_t g = uint16_t(kBias + uint32_t(max(0, 32 * (k + 1) - end + 1)));
+        for (;;) {
+            while (uint16_t(acc) >= g) {
+                const uint32_t win = __builtin_amdgcn_alignbit(hi, lo, acc);
+                acc += t.step[win >> t.kshift];
+            }
+            if (lo16(acc) >= kBias - 2048u) break;
+            // escape: the code at pos is longer than the window
+            acc += 0x1000u;
+            uint32_t sym;
+            const uint32_t win = __builtin_amdgcn_alignbit(hi, lo, acc);
+            acc += 0x10000u - long_code(win >> 8, t, sym);
+        }
+        acc += 32u;
+    }
+    uint32_t cnt = acc >> 16;
+    const int pos = 32 * (NW + 1) - int(lo16(acc)) + int(kBias);
+    if (pos > end) {
+        const uint32_t we = window_at<NW>(ck.w, uint32_t(end));
+        cnt -= __popc(uint32_t(t.mask[we >> t.kshift]) & ((1u << (pos - end)) - 1u));
+    }
+    return cnt;
+}
+
+// Makes the compiler wait for the loads into v now.  vmcnt also counts
+// stores on this chip, and the compiler cannot count the stores of the
+// divergent store paths below, so a register first used after a store would
+// make it wait for every store in flight to reach memory.
+template <typename T>
+__device__ __forceinline__ void wait_for(const T &v) {
+    static_assert(sizeof(T) % 4 == 0, "whole dwords only");
+    uint32_t w[sizeof(T) / 4];
+    __builtin_memcpy(w, &v, sizeof(T));
+#pragma unroll
+    for (unsigned i = 0; i < sizeof(T) / 4; ++i) asm volatile("" ::"v"(w[i]));
+}
+
+// ORs the 4 bytes of v into the zeroed LDS staging bytes [q, q + 4): two
+// aligned dword ORs.  OR is what lets lanes overlap: a byte is only ever
+// ORed with zero or with its own final value.
+__device__ __forceinline__ void or_4_bytes(uint8_t *lds_base, uint32_t q, uint32_t v) {
+    const uint64_t x = uint64_t(v) << (8u * (q & 3u));
+    uint32_t *d = reinterpret_cast<uint32_t *>(lds_base + (q & ~3u));
+    __hip_atomic_fetch_or(d, uint32_t(x), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+    __hip_atomic_fetch_or(d + 1, uint32_t(x >> 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+}
+
+// Phase two: decode the chunk again and OR its (rotated) exponents into the
+// zeroed staging area, from byte q0 on, up to four codes per lookup.  A
+// table entry holds zero bytes past its own codes, and codes decoded past
+// the chunk's last one are the next chunk's first codes, identical to what
+// the next lane writes there; so neither needs to be cut off.  Lookups stop
+// at the chunk's end bit, which bounds the spill past the block's last
+// exponent to three codes.
+template <int C>
+__device__ __forceinline__ void write_codes(const Chunk<C> &ck, int start, int end, uint8_t *lds_base,
+                                            uint32_t q0, const Tables &t) {
+    constexpr int NW = C / 4;
+    uint32_t acc = kBias - uint32_t(start);
+#pragma unroll
+    for (int k = -1; k < NW; ++k) {
+        const uint32_t hi = k < 0 ? 0u : ck.w[k < 0 ? 0 : k];
+        const uint32_t lo = ck.w[k + 1];
+        // stay while shift >= 0 (pos <= 32 (k + 1)) and pos < end
+        const uint16_t g = uint16_t(kBias + uint32_t(max(0, 32 * (k + 1) - end + 1)));
+        for (;;) {
+            while (uint16_t(acc) >= g) {
+                const uint32_t win = __builtin_amdgcn_alignbit(hi, lo, acc);
+                const uint2 e = t.wsym[win >> t.kshift];
+                or_4_bytes(lds_base, q0 + (acc >> 16), e.x);
+                acc += e.y;
+            }
+            if (lo16(acc) >= kBias - 2048u) break;
+            acc += 0x1000u;
+            uint32_t sym;
+            const uint32_t win = __builtin_amdgcn_alignbit(hi, lo, acc);
+            const uint32_t l = long_code(win >> 8, t, sym);
+            or_4_bytes(lds_base, q0 + (acc >> 16), sym);
+            acc += 0x10000u - l;
+        }
+        acc += 32u;
+    }
+}
+
+// Inclusive prefix sum across the wavefront (DPP row shifts, then row
+// broadcasts 15 and 31).
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
+    x += uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x111, 0xf, 0xf, false));  // row_shr:1
+    x += uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x112, 0xf, 0xf, false));  // row_shr:2
+    x += uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x114, 0xf, 0xf, false));  // row_shr:4
+    x += uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x118, 0xf, 0xf, false));  // row_shr:8
+    x += uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x142, 0xa, 0xf, false));  // row_bcast:15
+    x += uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x143, 0xc, 0xf, false));  // row_bcast:31
+    return x;
+}
+
+// 8 bf16 values from 8 staged (rotated) exponents and 8 raw bytes.  Per
+// pair of values, x1 = [raw_a, exp_a, raw_b, exp_b] and x2 = [exp_a, raw_a,
+// exp_b, raw_b] (bytes, low first); each output byte keeps bits 6..0 of x1
+// and bit 7 of x2.
+__device__ __forceinline__ u32x4 assemble8(const u32x2 &E, const u32x2 &R) {
+    const uint32_t e[2] = {E.x, E.y};
+    const uint32_t r[2] = {R.x, R.y};
+    uint32_t o[4];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const uint32_t a1 = __builtin_amdgcn_perm(e[q], r[q], 0x05010400u);
+        const uint32_t a2 = __builtin_amdgcn_perm(e[q], r[q], 0x01050004u);
+        const uint32_t b1 = __builtin_amdgcn_perm(e[q], r[q], 0x07030602u);
+        const uint32_t b2 = __builtin_amdgcn_perm(e[q], r[q], 0x03070206u);
+        o[2 * q] = (a1 & 0x7F7F7F7Fu) | (a2 & 0x80808080u);
+        o[2 * q + 1] = (b1 & 0x7F7F7F7Fu) | (b2 & 0x80808080u);
+    }
+    return u32x4{o[0], o[1], o[2], o[3]};
+}
+
+// Stage the decode tables of a container in LDS (16 bytes per thread per
+// step) and describe them.  Every thread of the workgroup must call this.
+__device__ __forceinline__ Tables stage_tables(uint8_t *lds, const uint8_t *tables, uint32_t tables_bytes,
+                                               uint32_t lut_bits) {
+    for (uint32_t o = threadIdx.x * 16u; o < tables_bytes; o += blockDim.x * 16u)
+        *reinterpret_cast<uint4 *>(lds + o) = *reinterpret_cast<const uint4 *>(tables + o);
+    __syncthreads();
+    Tables t;
+    t.kb = lut_bits;
+    t.kshift = 32u - t.kb;
+    t.step = reinterpret_cast<const uint32_t *>(lds);
+    t.wsym = reinterpret_cast<const uint2 *>(lds + (4u << t.kb));
+    t.mask = reinterpret_cast<const uint16_t *>(lds + (12u << t.kb));
+    t.limit = reinterpret_cast<const uint32_t *>(lds + (14u << t.kb));
+    t.first = t.limit + 32;
+    t.base = t.limit + 64;
+    t.order = lds + (14u << t.kb) + 384;
+    return t;
+}
+
+// Chunk-relative first bit of a chunk's first code and end of its codes,
+// from the offset-array words and the number of stream bits left from the
+// chunk's first bit to the end of its stream (or item).
+template <int C>
+__device__ __forceinline__ void chunk_span(const Chunk<C> &ck, uint32_t chunk, int64_t bits_left, int &start,
+                                           int &end) {
+    const uint32_t offpair = __builtin_amdgcn_alignbit(ck.o1, ck.o0, (5u * chunk) & 31u);
+    start = int(offpair & 31u);
+    const int next_off = int((offpair >> 5) & 31u);
+    end = int(min(int64_t(8 * C + next_off), max(bits_left, int64_t(-1))));
+}
+
+constexpr uint32_t kLdsBytes = 160u * 1024u;
+
+inline int device_cu_count() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    return cus;
+}
+
+}  // namespace

@@ -1,0 +1,187 @@
+"""GPU parity of the fused decode + matrix product (dfc_decode_gemm), called
+through the C ABI.
+
+Two checks that do not depend on the summation order:
+
+* exactness of the decode inside the fused path: with X made of unit
+  vectors e_k, every product has one non-zero term, so Y's columns are W's
+  columns exactly (bf16 -> fp32 is exact);
+* the product for seeded random X against the oracle's float64 W X, within
+  the tolerance of the fp32 accumulation: |Y - Y_ref| <= 1e-3 max|Y_ref|
+  overall and <= 1e-3 (|W| |X|) per element.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import lossless_entropy_coded_dfc_amd as dfc
+from lossless_entropy_coded_dfc_amd import synth
+from oracle import gemm as og
+from oracle import panel as pn
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-3
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+
+
+def upload(w, C=16, k=11, panel_k=1024):
+    blob = dfc.encode(w, chunk_bytes=C, lut_bits=k, layout=dfc.LAYOUT_PANEL, panel_k=panel_k)
+    info = dfc.blob_info(blob)
+    return torch.from_numpy(blob).cuda(), info, blob
+
+
+def run(dev, info, x_bits):
+    """x_bits: (B, K) uint16 host array -> Y (B, M) float32 host array."""
+    x = torch.from_numpy(np.ascontiguousarray(x_bits).view(np.int16)).cuda()
+    y = torch.empty((x_bits.shape[0], info.rows), dtype=torch.float32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dfc.decode_gemm(dev, info, x, y, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    return y.cpu().numpy()
+
+
+def unit_vectors(K, cols):
+    x = np.zeros((len(cols), K), dtype=np.uint16)
+    x[np.arange(len(cols)), cols] = 0x3F80  # bf16 1.0
+    return x
+
+
+def normal_finite(w):
+    """Uniform bit patterns with every exponent moved into 1..254: the
+    product path is held to finite normal weights (the decode of zero,
+    subnormal, Inf and NaN patterns is checked bit-exactly by the flat
+    decoder's tests)."""
+    e = (w >> 7) & 0xFF
+    e = np.clip(e, 1, 254).astype(np.uint16)
+    return (w & np.uint16(0x807F)) | (e << 7)
+
+
+def w_as_f32(w):
+    return (w.astype(np.uint32) << 16).view(np.float32)
+
+
+def check_product(w, x_rows, y):
+    """y (B, M) against the oracle's float64 W X for X = x_rows^T."""
+    ref = og.gemm_reference(w, x_rows.T).T
+    bound = og.abs_product_bound(w, x_rows.T).T
+    err = np.abs(y.astype(np.float64) - ref)
+    assert err.max() <= TOL * np.abs(ref).max() + 1e-30
+    assert (err <= TOL * bound + 1e-30).all()
+
+
+@pytest.mark.parametrize("C", [4, 8, 16, 32])
+def test_unit_vectors_recover_w_exactly(C):
+    M, K = 96, 272
+    w = synth.gaussian_with_outliers((M, K), 0.02, (80, C))
+    dev, info, _ = upload(w, C=C, panel_k=64)
+    wf = w_as_f32(w)
+    for c0 in range(0, K, 64):
+        cols = list(range(c0, min(K, c0 + 64)))
+        say("case unit vectors C", C, "cols", cols[0], "..", cols[-1])
+        y = run(dev, info, unit_vectors(K, cols))
+        assert np.array_equal(y, wf[:, cols].T)
+
+
+@pytest.mark.parametrize("B", [1, 2, 16, 31, 32, 33, 64])
+def test_product_against_oracle(B):
+    M, K = 128, 1040     # two column slices of 1024 and 16
+    w = synth.gaussian_with_outliers((M, K), 0.02, (81, B))
+    x = synth.gaussian((B, K), 1.0, (82, B))
+    dev, info, _ = upload(w, C=16, panel_k=1024)
+    say("case product B", B)
+    check_product(w, x, run(dev, info, x))
+
+
+@pytest.mark.parametrize("kind", list(synth.STRESS_KINDS))
+def test_stress_distributions(kind):
+    M, K = 64, 512
+    w = {"student_t": lambda: synth.student_t((M, K), 3.0, 0.02, (83,)),
+         "bimodal": lambda: synth.bimodal((M, K), 0.02, (84,)),
+         "uniform": lambda: normal_finite(synth.uniform_bits((M, K), (85,))),
+         "ladder": lambda: synth.exponent_ladder((M, K), (86,))}[kind]()
+    dev, info, _ = upload(w, C=8, k=10, panel_k=128)
+    say("case stress", kind)
+    y = run(dev, info, unit_vectors(K, list(range(0, 64))))
+    assert np.array_equal(y, w_as_f32(w)[:, :64].T)
+
+
+def test_oracle_written_container():
+    w = synth.gaussian((64, 256), 0.02, (87,))
+    blob = pn.write_panel_blob(pn.encode_panel(w, panel_k=128, chunk_bytes=16), 11)
+    arr = np.frombuffer(blob, dtype=np.uint8)
+    info = dfc.blob_info(arr)
+    dev = torch.from_numpy(arr.copy()).cuda()
+    y = run(dev, info, unit_vectors(256, list(range(64, 128))))
+    assert np.array_equal(y, w_as_f32(w)[:, 64:128].T)
+
+
+def test_invalid_arguments():
+    w = synth.gaussian((64, 128), 0.02, (88,))
+    dev, info, _ = upload(w)
+    x = torch.zeros((65, 128), dtype=torch.int16, device="cuda")
+    y = torch.zeros((65, 64), dtype=torch.float32, device="cuda")
+    with pytest.raises(dfc.DfcError) as ei:
+        dfc.decode_gemm(dev, info, x, y)
+    assert ei.value.status == dfc.EINVAL
+    flat = dfc.encode(w)
+    finfo = dfc.blob_info(flat)
+    with pytest.raises(ValueError):
+        dfc.decode_gemm(torch.from_numpy(flat).cuda(), finfo, x[:4], y[:4])
+
+
+def test_status_flag_on_corrupt_block_offsets():
+    w = synth.gaussian((64, 2048), 0.02, (89,))
+    dev, info, blob = upload(w, panel_k=2048)
+    bad = torch.from_numpy(blob.copy()).cuda()
+    # second block offset of the first item moved by one
+    o = info.off_blockout + 4
+    v = int(np.frombuffer(blob[o: o + 4].tobytes(), dtype="<u4")[0])
+    bad[o: o + 4] = torch.from_numpy(np.frombuffer(np.uint32(v + 1).tobytes(), dtype=np.uint8).copy())
+    x = torch.zeros((1, 2048), dtype=torch.int16, device="cuda")
+    y = torch.empty((1, 64), dtype=torch.float32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dfc.decode_gemm(bad, info, x, y, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) != 0
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("B", [1, 16, 64])
+def test_full_28672x8192(B):
+    """The benchmark's matrix: W 28672 x 8192 ~ N(0, 0.015^2), X ~ N(0, 1).
+    The product is checked on sampled rows against the oracle; the decode
+    is checked exactly on every column with unit vectors (B = 64 only)."""
+    w = synth.gemm_weight()
+    dev, info, _ = upload(w)
+    x = synth.gaussian((B, 8192), 1.0, (4, 1, B))
+    say("case full gemm B", B)
+    y = run(dev, info, x)
+    rows = np.random.default_rng(5).choice(28672, 384, replace=False)
+    check_product(w[rows], x, y[:, rows])
+    if B == 64:
+        wt = torch.from_numpy(w.view(np.int16)).cuda()
+        wf = (wt.to(torch.int32) << 16).view(torch.float32)
+        xs = torch.zeros((64, 8192), dtype=torch.int16, device="cuda")
+        ys = torch.empty((64, 28672), dtype=torch.float32, device="cuda")
+        status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        for c0 in range(0, 8192, 64):
+            xs.zero_()
+            xs[torch.arange(64), torch.arange(c0, c0 + 64)] = 0x3F80
+            dfc.decode_gemm(dev, info, xs, ys, status)
+            assert torch.equal(ys, wf[:, c0: c0 + 64].T.contiguous())
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0
