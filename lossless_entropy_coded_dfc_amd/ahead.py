@@ -1,0 +1,73 @@
+"""Decode-just-before-use for layer-by-layer consumers.
+
+The DFloat11 blog's introduction describes weights kept compressed in GPU
+memory and decompressed online, just before they are used.  ``DecodeAhead``
+does that for a stack of layers: while the caller's stream computes with layer
+i, the matrices of layer i + 1 decode on a side stream into the other of two
+reused scratch sets, so at most two layers are ever held decompressed.
+
+Ordering uses HIP events only: ``weights(i)`` makes the caller's stream wait
+for layer i's decode, and ``release(i)`` marks the point after which its
+scratch set may be overwritten by the decode of layer i + 2.
+"""
+from __future__ import annotations
+
+from . import MAX_BATCH, Info, decode_batch
+
+
+class DecodeAhead:
+    """Double-buffered decode of ``layers`` (a list, per layer, of
+    ``(blob_dev, info, shape)`` with blob_dev a device uint8 tensor holding a
+    flat-layout container and shape the matrix shape)."""
+
+    def __init__(self, layers, device="cuda"):
+        import torch
+
+        self.torch = torch
+        self.layers = [list(layer) for layer in layers]
+        for layer in self.layers:
+            for _, info, shape in layer:
+                if not isinstance(info, Info) or int(info.n) != int(shape[0]) * int(shape[1]):
+                    raise ValueError("every matrix needs its container info and a matching 2-D shape")
+        width = max((len(layer) for layer in self.layers), default=0)
+        sizes = [max((int(layer[j][1].n) for layer in self.layers if j < len(layer)), default=0)
+                 for j in range(width)]
+        self.scratch = [[torch.empty(max(1, s), dtype=torch.int16, device=device) for s in sizes]
+                        for _ in range(2)]
+        self.side = torch.cuda.Stream(device=device)  # default priority
+        self.ready = [torch.cuda.Event() for _ in range(2)]
+        self.free = [torch.cuda.Event() for _ in range(2)]
+        self.free_recorded = [False, False]
+        self.status = torch.zeros(1, dtype=torch.int32, device=device)
+
+    def prefetch(self, i: int):
+        """Enqueue the decode of layer i on the side stream."""
+        slot = i % 2
+        with self.torch.cuda.stream(self.side):
+            if self.free_recorded[slot]:
+                self.side.wait_event(self.free[slot])
+            items = [(blob, info, self.scratch[slot][j][: int(info.n)])
+                     for j, (blob, info, _) in enumerate(self.layers[i])]
+            for k in range(0, len(items), MAX_BATCH):
+                decode_batch(items[k: k + MAX_BATCH], self.status, stream=self.side.cuda_stream)
+            self.ready[slot].record(self.side)
+
+    def weights(self, i: int):
+        """bf16 views of layer i's matrices; the current stream waits for
+        their decode."""
+        slot = i % 2
+        self.torch.cuda.current_stream().wait_event(self.ready[slot])
+        return [self.scratch[slot][j][: int(info.n)].view(self.torch.bfloat16).view(*shape)
+                for j, (_, info, shape) in enumerate(self.layers[i])]
+
+    def release(self, i: int):
+        """The current stream is done with layer i's matrices."""
+        slot = i % 2
+        self.free[slot].record(self.torch.cuda.current_stream())
+        self.free_recorded[slot] = True
+
+    def corrupt_blocks_seen(self) -> bool:
+        """True if any decode so far met a block whose count disagreed with
+        its block offsets (synchronizes the side stream)."""
+        self.side.synchronize()
+        return int(self.status.item()) != 0

@@ -1,0 +1,87 @@
+"""GPU checks of decode-just-before-use (DecodeAhead): every layer's weights,
+decoded on the side stream into the reused scratch sets, equal the originals
+bit for bit at the moment the compute stream uses them, and a chained
+computation over the layers matches the one with resident weights exactly."""
+import sys
+
+import numpy as np
+import pytest
+
+import lossless_entropy_coded_dfc_amd as dfc
+from lossless_entropy_coded_dfc_amd import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+
+
+def make_layers(n_layers, shapes, C=16):
+    layers, originals = [], []
+    for i in range(n_layers):
+        layer, orig = [], []
+        for j, (r, c) in enumerate(shapes):
+            x = synth.gaussian_with_outliers((r, c), 0.02, (90, i, j))
+            blob = dfc.encode(x, chunk_bytes=C)
+            layer.append((torch.from_numpy(blob).cuda(), dfc.blob_info(blob), (r, c)))
+            orig.append(x)
+        layers.append(layer)
+        originals.append(orig)
+    return layers, originals
+
+
+def test_weights_equal_originals_when_used():
+    from lossless_entropy_coded_dfc_amd.ahead import DecodeAhead
+    shapes = [(256, 512), (512, 256), (128, 512)]
+    layers, originals = make_layers(5, shapes)
+    dec = DecodeAhead(layers)
+    say("case decode-ahead 5 layers")
+    dec.prefetch(0)
+    for i in range(5):
+        if i + 1 < 5:
+            dec.prefetch(i + 1)
+        W = dec.weights(i)
+        # copies taken on the compute stream, before release
+        got = [w.view(torch.int16).clone() for w in W]
+        dec.release(i)
+        for g, x in zip(got, originals[i]):
+            assert torch.equal(g, torch.from_numpy(x.view(np.int16)).cuda())
+    assert not dec.corrupt_blocks_seen()
+
+
+def test_chained_products_match_resident_weights():
+    from lossless_entropy_coded_dfc_amd.ahead import DecodeAhead
+    d = 256
+    shapes = [(d, d), (d, d)]
+    layers, originals = make_layers(6, shapes, C=8)
+    resident = [[torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16) for x in orig] for orig in originals]
+    h0 = torch.from_numpy(synth.gaussian((64, d), 1.0, (91,)).view(np.int16)).cuda().view(torch.bfloat16)
+
+    def step(h, W):
+        h = (h @ W[0].t()) @ W[1].t()
+        return (h.float() / (h.float().abs().amax() + 1e-6)).to(torch.bfloat16)
+
+    h = h0
+    for W in resident:
+        h = step(h, W)
+    dec = DecodeAhead(layers)
+    g = h0
+    dec.prefetch(0)
+    for i in range(6):
+        if i + 1 < 6:
+            dec.prefetch(i + 1)
+        g = step(g, dec.weights(i))
+        dec.release(i)
+    torch.cuda.synchronize()
+    say("case decode-ahead chained products")
+    assert torch.equal(g, h)
+    assert not dec.corrupt_blocks_seen()
