@@ -197,6 +197,32 @@ enum { DFC_GEMM_MAX_BATCH = 64 };
 dfc_status dfc_decode_gemm(const void *w_blob_dev, const dfc_info *info, const uint16_t *x_dev, uint32_t batch,
                            float *y_dev, uint32_t *status_dev, void *stream);
 
+/* Workspace bytes dfc_encode_device needs for n elements.  Host. */
+dfc_status dfc_encode_device_workspace(uint64_t n, uint64_t *bytes);
+
+/* 256-bin exponent histogram of n bf16 values in device memory (bits 14..7),
+ * as 32-bit counts into hist_dev (256 device uint32, overwritten).  Device,
+ * asynchronous on stream.  DFC_EINVAL on null pointers. */
+dfc_status dfc_histogram_device(const uint16_t *src_dev, uint64_t n, uint32_t *hist_dev, void *stream);
+
+/* Encode n bf16 values already in device memory into a container in device
+ * memory, byte-identical to what dfc_encode writes for the same values and
+ * parameters (FLAT layout only).  The histogram is taken on the device and
+ * read back (the call synchronizes the stream), the code and the container
+ * layout are set on the host (the stream length is the histogram times the
+ * code lengths), and the code bits, chunk offsets, block offsets and raw
+ * bytes are written by kernels; the call returns after the stream is idle.
+ * src_dev: n uint16 (2-byte aligned).  cb: NULL = the data's own code.
+ * dst_dev: cap bytes (256-byte aligned), use dfc_encode_bound.
+ * work_dev: work_bytes >= dfc_encode_device_workspace(n) (256-byte aligned).
+ * *written (host) receives the container size.  Errors: DFC_EINVAL (null or
+ * misaligned pointers, bad parameters, an exponent without a code),
+ * DFC_ESIZE (cap or workspace too small, n >= 2^32), DFC_EUNSUPPORTED (PANEL
+ * layout), DFC_EHIP. */
+dfc_status dfc_encode_device(const uint16_t *src_dev, uint64_t n, const dfc_params *p, const dfc_codebook *cb,
+                             void *dst_dev, uint64_t cap, void *work_dev, uint64_t work_bytes, uint64_t *written,
+                             void *stream);
+
 /* Launch tuning knob for benchmarks: wavefronts per workgroup (4, 8 or 16)
  * and wave-blocks each wavefront decodes (1..64).  0 = automatic.  Returns
  * DFC_EINVAL for other values.  Process-wide; not thread-safe. */

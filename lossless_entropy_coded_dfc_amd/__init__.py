@@ -123,6 +123,14 @@ def library():
     lib.dfc_decode_gemm.argtypes = [ctypes.c_void_p, ctypes.POINTER(Info), ctypes.c_void_p, ctypes.c_uint32,
                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     lib.dfc_decode_gemm.restype = st
+    lib.dfc_encode_device_workspace.argtypes = [ctypes.c_uint64, u64p]
+    lib.dfc_encode_device_workspace.restype = st
+    lib.dfc_histogram_device.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
+    lib.dfc_histogram_device.restype = st
+    lib.dfc_encode_device.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.POINTER(Params),
+                                      ctypes.POINTER(Codebook), ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
+                                      ctypes.c_uint64, u64p, ctypes.c_void_p]
+    lib.dfc_encode_device.restype = st
     lib.dfc_set_launch.argtypes = [ctypes.c_uint32, ctypes.c_uint32]
     lib.dfc_set_launch.restype = st
     lib.dfc_status_str.argtypes = [ctypes.c_int]
@@ -266,6 +274,33 @@ def decode_batch(items, status=None, stream=None):
         arr[k].n = info.n
     _check(library().dfc_decode_batch(arr, len(items), ctypes.c_void_p(_dev_ptr(status)), _stream(stream)),
            "dfc_decode_batch")
+
+
+def encode_device(src, chunk_bytes: int = 16, lanes: int = 64, max_code_len: int = 24, lut_bits: int = 11,
+                  codebook: Codebook | None = None, shape=None, stream=None):
+    """Encode a contiguous 16-bit device tensor (bf16 bits) on the GPU.
+    Returns (container as a device uint8 tensor, its size in bytes)."""
+    import torch
+    n = src.numel()
+    if src.element_size() != 2 or not src.is_contiguous():
+        raise ValueError("src must be a contiguous 16-bit device tensor")
+    if shape is None:
+        shape = tuple(src.shape) if src.dim() == 2 else (1, n)
+    p = default_params(chunk_bytes=chunk_bytes, lanes_per_block=lanes, max_code_len=max_code_len,
+                       lut_bits=lut_bits, rows=int(shape[0]), cols=int(shape[1]))
+    if n == 0:
+        p.rows, p.cols = 0, 0
+    cap = encode_bound(n, p)
+    wb = ctypes.c_uint64()
+    _check(library().dfc_encode_device_workspace(n, ctypes.byref(wb)), "dfc_encode_device_workspace")
+    dst = torch.empty(cap, dtype=torch.uint8, device=src.device)
+    work = torch.empty(max(256, wb.value), dtype=torch.uint8, device=src.device)
+    written = ctypes.c_uint64()
+    _check(library().dfc_encode_device(ctypes.c_void_p(src.data_ptr() if n else 0), n, ctypes.byref(p),
+                                       ctypes.byref(codebook) if codebook is not None else None,
+                                       ctypes.c_void_p(dst.data_ptr()), cap, ctypes.c_void_p(work.data_ptr()),
+                                       wb.value, ctypes.byref(written), _stream(stream)), "dfc_encode_device")
+    return dst, written.value
 
 
 GEMM_MAX_BATCH = 64

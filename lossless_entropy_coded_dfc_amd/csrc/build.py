@@ -49,7 +49,7 @@ def build(verbose: bool = False, out: str = OUT) -> str:
     host_obj = os.path.join(objdir, "dfc_host.o")
     _run(["g++", *CXX_FLAGS, *inc, "-c", os.path.join(HERE, "dfc_host.cpp"), "-o", host_obj], verbose)
     dev_objs = []
-    for name in ("dfc_decode", "dfc_gemm"):
+    for name in ("dfc_decode", "dfc_gemm", "dfc_encode_gpu"):
         obj = os.path.join(objdir, name + ".o")
         _run([hipcc, *HIP_FLAGS, *inc, "-c", os.path.join(HERE, name + ".hip"), "-o", obj], verbose)
         dev_objs.append(obj)

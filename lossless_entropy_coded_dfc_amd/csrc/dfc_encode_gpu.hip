@@ -1,0 +1,324 @@
+// dfc_encode_gpu.hip - gfx950 encoder: the same DFC1 containers as the host
+// encoder, built from bf16 data already in device memory.
+//
+// DFloat11 blog ("70% Size, 100% Accuracy ... (DFloat11)"), section 02: an
+// entropy code from the weights' own statistics; section 03 item 2: the
+// per-chunk and per-block position variables the two-phase decoder needs.
+// The pages compress offline on the host; this moves the O(n) work to the
+// GPU:
+//   1. exponent histogram (LDS bins per workgroup, then global atomics);
+//   2. on the host: code lengths, canonical codes, total bits (the histogram
+//      times the lengths), section layout, header and decode tables;
+//   3. code bits per segment of 4096 elements, an exclusive scan over the
+//      segments, then every thread packs its 16 codes at its bit position
+//      (interior words stored, the two words shared with neighbours ORed)
+//      and writes the raw bytes; the element whose code covers a chunk's
+//      first bit writes that chunk's 5-bit offset (the next code starts where
+//      it ends) and, on block boundaries, the block's output offset.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#include "dfc.h"
+#include "dfc_format.h"
+#include "dfc_host_internal.h"
+
+namespace {
+
+constexpr uint32_t kSegThreads = 256;
+constexpr uint32_t kPerThread = 16;
+constexpr uint32_t kSegElems = kSegThreads * kPerThread;  // 4096
+
+__device__ __forceinline__ uint32_t exponent_of(uint32_t b) { return (b >> 7) & 0xFFu; }
+__device__ __forceinline__ uint32_t raw_of(uint32_t b) { return ((b >> 8) & 0x80u) | (b & 0x7Fu); }
+
+__global__ __launch_bounds__(256) void histogram_kernel(const uint16_t *src, uint64_t n, uint32_t *hist) {
+    __shared__ uint32_t bins[256];
+    bins[threadIdx.x] = 0;
+    __syncthreads();
+    for (uint64_t j = uint64_t(blockIdx.x) * blockDim.x + threadIdx.x; j < n; j += uint64_t(gridDim.x) * blockDim.x)
+        atomicAdd(&bins[exponent_of(src[j])], 1u);
+    __syncthreads();
+    if (bins[threadIdx.x]) atomicAdd(&hist[threadIdx.x], bins[threadIdx.x]);
+}
+
+__global__ void fill_zero_u32(uint32_t *p, uint64_t words) {
+    for (uint64_t i = uint64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < words; i += uint64_t(gridDim.x) * blockDim.x)
+        p[i] = 0u;
+}
+
+struct Book {
+    uint32_t code[256];
+    uint8_t len[256];
+};
+
+// Loads this thread's 16 elements (zero past n) and their code lengths.
+__device__ __forceinline__ void load16(const uint16_t *src, uint64_t n, uint64_t j0, uint16_t (&b)[kPerThread]) {
+#pragma unroll
+    for (uint32_t q = 0; q < kPerThread; ++q) b[q] = j0 + q < n ? src[j0 + q] : uint16_t(0);
+}
+
+// Block-wide exclusive scan of one u32 per thread (256 threads).
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *sh, uint32_t &total) {
+    const uint32_t t = threadIdx.x;
+    sh[t] = v;
+    __syncthreads();
+    for (uint32_t d = 1; d < kSegThreads; d <<= 1) {
+        const uint32_t add = t >= d ? sh[t - d] : 0u;
+        __syncthreads();
+        sh[t] += add;
+        __syncthreads();
+    }
+    total = sh[kSegThreads - 1];
+    const uint32_t incl = sh[t];
+    __syncthreads();
+    return incl - v;
+}
+
+__global__ __launch_bounds__(256) void segment_bits_kernel(const uint16_t *src, uint64_t n, Book book,
+                                                           uint32_t *seg_bits) {
+    __shared__ uint32_t sh[kSegThreads];
+    const uint64_t j0 = uint64_t(blockIdx.x) * kSegElems + uint64_t(threadIdx.x) * kPerThread;
+    uint16_t b[kPerThread];
+    load16(src, n, j0, b);
+    uint32_t bits = 0;
+#pragma unroll
+    for (uint32_t q = 0; q < kPerThread; ++q)
+        if (j0 + q < n) bits += book.len[exponent_of(b[q])];
+    uint32_t total;
+    block_exclusive_scan(bits, sh, total);
+    if (threadIdx.x == 0) seg_bits[blockIdx.x] = total;
+}
+
+// Exclusive prefix over the segments (one workgroup of 1024 threads).
+__global__ __launch_bounds__(1024) void segment_scan_kernel(const uint32_t *seg_bits, uint64_t nseg,
+                                                            uint64_t *seg_off) {
+    __shared__ uint64_t sh[1024];
+    uint64_t carry = 0;
+    for (uint64_t base = 0; base < nseg; base += 1024) {
+        const uint64_t i = base + threadIdx.x;
+        const uint64_t v = i < nseg ? seg_bits[i] : 0;
+        sh[threadIdx.x] = v;
+        __syncthreads();
+        for (uint32_t d = 1; d < 1024; d <<= 1) {
+            const uint64_t add = threadIdx.x >= d ? sh[threadIdx.x - d] : 0;
+            __syncthreads();
+            sh[threadIdx.x] += add;
+            __syncthreads();
+        }
+        if (i < nseg) seg_off[i] = carry + sh[threadIdx.x] - v;
+        carry += sh[1023];
+        __syncthreads();
+    }
+}
+
+struct PackArgs {
+    const uint16_t *src;
+    uint64_t n;
+    uint32_t *words;     // stream words (zeroed)
+    uint32_t *offw;      // packed 5-bit offsets (zeroed)
+    uint32_t *blockout;  // u32 out[n_blocks + 1]
+    uint8_t *raw;        // raw bytes
+    const uint64_t *seg_off;
+    uint64_t chunk_bits;  // 8 C
+    uint32_t lanes;       // T
+};
+
+__device__ __forceinline__ void or_word(uint32_t *words, uint64_t w, uint32_t v) {
+    if (v) atomicOr(&words[w], v);
+}
+
+__global__ __launch_bounds__(256) void pack_kernel(const PackArgs a, const Book book) {
+    __shared__ uint32_t sh[kSegThreads];
+    const uint64_t j0 = uint64_t(blockIdx.x) * kSegElems + uint64_t(threadIdx.x) * kPerThread;
+    uint16_t b[kPerThread];
+    load16(a.src, a.n, j0, b);
+    uint32_t bits = 0;
+#pragma unroll
+    for (uint32_t q = 0; q < kPerThread; ++q)
+        if (j0 + q < a.n) bits += book.len[exponent_of(b[q])];
+    uint32_t seg_total;
+    const uint32_t before = block_exclusive_scan(bits, sh, seg_total);
+    const uint64_t start = a.seg_off[blockIdx.x] + before;
+
+    // Raw bytes: 16 per thread, one store when all are in range.
+    if (j0 + kPerThread <= a.n) {
+        uint32_t r[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (uint32_t q = 0; q < kPerThread; ++q) r[q >> 2] |= raw_of(b[q]) << (8 * (q & 3));
+        *reinterpret_cast<uint4 *>(a.raw + j0) = make_uint4(r[0], r[1], r[2], r[3]);
+    } else {
+        for (uint32_t q = 0; q < kPerThread && j0 + q < a.n; ++q) a.raw[j0 + q] = uint8_t(raw_of(b[q]));
+    }
+
+    // Codes: MSB-first into 32-bit words.  Words wholly inside this thread's
+    // bit range are stored; the first and last are ORed (shared).
+    uint64_t pos = start;
+    uint64_t acc = 0;
+    uint32_t nacc = uint32_t(pos & 31);
+    uint64_t w = pos >> 5;
+    const uint64_t first_word = w, end_bit = start + bits;
+    const uint64_t last_word = bits ? (end_bit - 1) >> 5 : w;
+    for (uint32_t q = 0; q < kPerThread; ++q) {
+        const uint64_t j = j0 + q;
+        if (j >= a.n) break;
+        const uint32_t e = exponent_of(b[q]);
+        const uint32_t l = book.len[e];
+        // A chunk boundary inside (pos, pos + l]: the next code starts at pos + l.
+        const uint64_t c = pos / a.chunk_bits + 1;
+        if (c * a.chunk_bits <= pos + l) {
+            const uint32_t off = uint32_t(pos + l - c * a.chunk_bits);
+            const uint64_t g = 5ull * c;
+            const uint64_t v = uint64_t(off) << (g & 31);
+            or_word(a.offw, g >> 5, uint32_t(v));
+            or_word(a.offw, (g >> 5) + 1, uint32_t(v >> 32));
+            if (c % a.lanes == 0) a.blockout[c / a.lanes] = uint32_t(j + 1);
+        }
+        acc = (acc << l) | book.code[e];
+        nacc += l;
+        pos += l;
+        if (nacc >= 32) {
+            nacc -= 32;
+            const uint32_t v = uint32_t(acc >> nacc);
+            if (w == first_word || w == last_word) or_word(a.words, w, v);
+            else a.words[w] = v;
+            ++w;
+        }
+    }
+    if (nacc > 0) or_word(a.words, w, uint32_t(acc << (32 - nacc)));
+}
+
+// Host copy of a workspace layout.
+struct Workspace {
+    uint64_t hist_off, segbits_off, segoff_off, bytes, nseg;
+};
+Workspace workspace_layout(uint64_t n) {
+    Workspace w;
+    w.nseg = dfc::ceil_div(std::max<uint64_t>(n, 1), kSegElems);
+    w.hist_off = 0;
+    w.segbits_off = 1024;
+    w.segoff_off = dfc::align256(w.segbits_off + 4 * w.nseg);
+    w.bytes = dfc::align256(w.segoff_off + 8 * w.nseg);
+    return w;
+}
+
+dfc_status hip_ok(hipError_t e) { return e == hipSuccess ? DFC_OK : DFC_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+dfc_status dfc_encode_device_workspace(uint64_t n, uint64_t *bytes) {
+    if (!bytes) return DFC_EINVAL;
+    *bytes = workspace_layout(n).bytes;
+    return DFC_OK;
+}
+
+dfc_status dfc_histogram_device(const uint16_t *src_dev, uint64_t n, uint32_t *hist_dev, void *stream) {
+    if ((!src_dev && n) || !hist_dev) return DFC_EINVAL;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipLaunchKernelGGL(fill_zero_u32, dim3(1), dim3(256), 0, st, hist_dev, uint64_t(256));
+    if (n) {
+        const uint32_t grid = uint32_t(std::min<uint64_t>(4096, dfc::ceil_div(n, 256 * 16)));
+        hipLaunchKernelGGL(histogram_kernel, dim3(std::max(1u, grid)), dim3(256), 0, st, src_dev, n, hist_dev);
+    }
+    return hip_ok(hipGetLastError());
+}
+
+dfc_status dfc_encode_device(const uint16_t *src_dev, uint64_t n, const dfc_params *pin, const dfc_codebook *cb_in,
+                             void *dst_dev, uint64_t cap, void *work_dev, uint64_t work_bytes, uint64_t *written,
+                             void *stream) {
+    dfc_params p;
+    if (pin) p = *pin; else dfc_default_params(&p);
+    if ((!src_dev && n) || !dst_dev || !written || !work_dev || !dfc::encoder_params_ok(p)) return DFC_EINVAL;
+    if (p.layout != DFC_LAYOUT_FLAT) return DFC_EUNSUPPORTED;
+    if ((reinterpret_cast<uintptr_t>(dst_dev) & 255u) || (reinterpret_cast<uintptr_t>(work_dev) & 255u) ||
+        (reinterpret_cast<uintptr_t>(src_dev) & 1u))
+        return DFC_EINVAL;
+    if (n >= (uint64_t(1) << 32)) return DFC_ESIZE;
+    uint64_t rows = p.rows, cols = p.cols;
+    if (rows == 0 && cols == 0) {
+        rows = 1;
+        cols = n;
+    }
+    if (rows * cols != n) return DFC_EINVAL;
+    const Workspace ws = workspace_layout(n);
+    if (work_bytes < ws.bytes) return DFC_ESIZE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    uint8_t *work = static_cast<uint8_t *>(work_dev);
+    uint32_t *hist_dev = reinterpret_cast<uint32_t *>(work + ws.hist_off);
+
+    // 1. histogram -> host
+    dfc_status s = dfc_histogram_device(src_dev, n, hist_dev, stream);
+    if (s != DFC_OK) return s;
+    uint32_t h32[256];
+    if (hipMemcpyAsync(h32, hist_dev, sizeof(h32), hipMemcpyDeviceToHost, st) != hipSuccess ||
+        hipStreamSynchronize(st) != hipSuccess)
+        return DFC_EHIP;
+    uint64_t hist[256];
+    for (int i = 0; i < 256; ++i) hist[i] = h32[i];
+
+    // 2. codebook, layout, header and tables on the host
+    uint8_t len[256];
+    if (cb_in) {
+        std::memcpy(len, cb_in->len, 256);
+        uint32_t used = 0;
+        for (int i = 0; i < 256; ++i) {
+            if (len[i] > p.max_code_len || (hist[i] && !len[i])) return DFC_EINVAL;
+            used += len[i] != 0;
+        }
+        if (n && (used < 2 || dfc::kraft_sum(len) != (uint64_t(1) << dfc::kMaxLen))) return DFC_EINVAL;
+    } else {
+        s = dfc::code_lengths(hist, p.max_code_len, len);
+        if (s != DFC_OK) return s;
+    }
+    Book book;
+    dfc::canonical_codes(len, book.code);
+    std::memcpy(book.len, len, 256);
+    uint64_t total_bits = 0;
+    for (int i = 0; i < 256; ++i) total_bits += hist[i] * len[i];
+    const uint32_t C = p.chunk_bytes, T = p.lanes_per_block;
+    const dfc::Layout L = dfc::layout_sizes(total_bits, C, T);
+    const dfc::SectionSizes sz = dfc::section_sizes(n, L.n_chunks, L.n_blocks, C, p.lut_bits);
+    uint64_t off[dfc::kNumSections];
+    const uint64_t blob_bytes = dfc::place_sections(sz, off);
+    if (cap < blob_bytes) return DFC_ESIZE;
+    std::vector<uint8_t> head(off[dfc::kTables] + sz.bytes[dfc::kTables], 0);
+    dfc::container_header(head.data(), p, n, total_bits, L.n_chunks, L.n_blocks, rows, cols, sz, off, blob_bytes, len);
+
+    // 3. zero the container, upload header and tables, pack
+    uint8_t *dst = static_cast<uint8_t *>(dst_dev);
+    hipLaunchKernelGGL(fill_zero_u32, dim3(uint32_t(std::min<uint64_t>(65535, dfc::ceil_div(blob_bytes / 4, 256)))),
+                       dim3(256), 0, st, reinterpret_cast<uint32_t *>(dst), blob_bytes / 4);
+    if (hipMemcpyAsync(dst, head.data(), head.size(), hipMemcpyHostToDevice, st) != hipSuccess) return DFC_EHIP;
+    const uint32_t n_out = uint32_t(n);
+    if (hipMemcpyAsync(dst + off[dfc::kBlockout] + 4 * L.n_blocks, &n_out, 4, hipMemcpyHostToDevice, st) !=
+        hipSuccess)
+        return DFC_EHIP;
+    if (n) {
+        uint32_t *seg_bits = reinterpret_cast<uint32_t *>(work + ws.segbits_off);
+        uint64_t *seg_off = reinterpret_cast<uint64_t *>(work + ws.segoff_off);
+        hipLaunchKernelGGL(segment_bits_kernel, dim3(uint32_t(ws.nseg)), dim3(kSegThreads), 0, st, src_dev, n, book,
+                           seg_bits);
+        hipLaunchKernelGGL(segment_scan_kernel, dim3(1), dim3(1024), 0, st, seg_bits, ws.nseg, seg_off);
+        PackArgs a;
+        a.src = src_dev;
+        a.n = n;
+        a.words = reinterpret_cast<uint32_t *>(dst + off[dfc::kWords]);
+        a.offw = reinterpret_cast<uint32_t *>(dst + off[dfc::kOffsets]);
+        a.blockout = reinterpret_cast<uint32_t *>(dst + off[dfc::kBlockout]);
+        a.raw = dst + off[dfc::kRaw];
+        a.seg_off = seg_off;
+        a.chunk_bits = 8ull * C;
+        a.lanes = T;
+        hipLaunchKernelGGL(pack_kernel, dim3(uint32_t(ws.nseg)), dim3(kSegThreads), 0, st, a, book);
+    }
+    if (hipGetLastError() != hipSuccess || hipStreamSynchronize(st) != hipSuccess) return DFC_EHIP;
+    *written = blob_bytes;
+    return DFC_OK;
+}
+
+}  // extern "C"

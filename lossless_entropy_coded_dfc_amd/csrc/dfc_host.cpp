@@ -13,6 +13,7 @@
 
 #include "dfc.h"
 #include "dfc_format.h"
+#include "dfc_host_internal.h"
 
 using namespace dfc;
 
@@ -360,6 +361,25 @@ uint64_t kraft(const uint8_t len[256]) {
 }
 
 }  // namespace
+
+namespace dfc {
+
+dfc_status code_lengths(const uint64_t hist[256], uint32_t limit, uint8_t len[256]) {
+    return package_merge(hist, limit, len);
+}
+void canonical_codes(const uint8_t len[256], uint32_t code[256]) {
+    Canon c;
+    canonical(len, c, code);
+}
+bool encoder_params_ok(const dfc_params &p) { return params_ok(p); }
+uint64_t kraft_sum(const uint8_t len[256]) { return kraft(len); }
+void container_header(uint8_t *dst, const dfc_params &p, uint64_t n, uint64_t total_bits, uint64_t n_chunks,
+                      uint64_t n_blocks, uint64_t rows, uint64_t cols, const SectionSizes &sz,
+                      const uint64_t off[kNumSections], uint64_t blob_bytes, const uint8_t len[256]) {
+    write_header(dst, p, n, total_bits, n_chunks, n_blocks, rows, cols, sz, off, blob_bytes, len);
+}
+
+}  // namespace dfc
 
 extern "C" {
 

@@ -1,0 +1,109 @@
+"""GPU encoder (dfc_encode_device) through the C ABI: its containers must be
+byte-identical to the host encoder's (which the oracle pins byte for byte),
+and decode back to the input."""
+import sys
+
+import numpy as np
+import pytest
+
+import lossless_entropy_coded_dfc_amd as dfc
+from lossless_entropy_coded_dfc_amd import synth
+from oracle import blob as bl
+from oracle import codebook as cb
+from oracle import fields
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+
+
+def dev16(x):
+    return torch.from_numpy(np.ascontiguousarray(x).reshape(-1).view(np.int16)).cuda()
+
+
+def same_as_host(x, C=16, k=11, T=64, codebook=None, label=""):
+    say("case", label, np.shape(x), "C", C, "k", k, "T", T)
+    x = np.asarray(x, dtype=np.uint16)
+    shape = x.shape if x.ndim == 2 else None
+    host = dfc.encode(x, chunk_bytes=C, lut_bits=k, lanes=T, codebook=codebook, shape=shape)
+    d, size = dfc.encode_device(dev16(x), chunk_bytes=C, lut_bits=k, lanes=T, codebook=codebook, shape=shape)
+    got = d[:size].cpu().numpy()
+    assert size == host.size, label
+    assert np.array_equal(got, host), label
+    return got
+
+
+@pytest.mark.parametrize("C", [4, 8, 16, 32])
+def test_matches_host_all_chunk_sizes(C):
+    x = synth.gaussian_with_outliers((300, 1000), 0.02, (100, C))
+    for k in (8, 11, 12):
+        same_as_host(x, C, k, label=f"outliers C{C}")
+
+
+@pytest.mark.parametrize("kind", ["uniform", "ladder", "bimodal", "t"])
+def test_matches_host_distributions(kind):
+    shape = (257, 1031)
+    x = {"uniform": lambda: synth.uniform_bits(shape, (101,)),
+         "ladder": lambda: synth.exponent_ladder(shape, (102,)),
+         "bimodal": lambda: synth.bimodal(shape, 0.02, (103,)),
+         "t": lambda: synth.student_t(shape, 3.0, 0.02, (104,))}[kind]()
+    for C in (4, 16, 32):
+        same_as_host(x, C, label=kind)
+
+
+def test_edge_sizes_and_lanes():
+    for n in (1, 2, 15, 16, 17, 4095, 4096, 4097, 65537):
+        same_as_host(synth.gaussian((n,), 0.02, (105, n)), 4, label=f"n={n}")
+    x = synth.gaussian((64, 4099), 0.02, (106,))
+    for T in (64, 128, 256):
+        same_as_host(x, 8, T=T, label=f"T={T}")
+
+
+def test_special_values_and_constant():
+    specials = np.array([0x7FC1, 0xFF81, 0x7F80, 0xFF80, 0x0000, 0x8000, 0x0001, 0x807F], dtype=np.uint16)
+    same_as_host(np.tile(specials, 3001), 8, label="specials")
+    same_as_host(np.full((100, 100), 0x3F80, dtype=np.uint16), 4, label="constant")
+
+
+def test_external_codebook_and_decode():
+    g = synth.gaussian((512, 512), 0.02, (107,))
+    book = dfc.build_codebook(cb.histogram(fields.split(g)[0]) + 1, 24)
+    x = synth.uniform_bits((200, 999), (108,))
+    blob = same_as_host(x, 16, codebook=book, label="foreign codebook")
+    assert np.array_equal(bl.decode_blob(bytes(blob)), x.ravel())
+
+
+def test_errors():
+    x = synth.gaussian((64, 64), 0.02, (109,))
+    book = dfc.build_codebook(cb.histogram(fields.split(x)[0]), 24)
+    y = synth.uniform_bits((64, 64), (110,))   # exponents the book does not cover
+    with pytest.raises(dfc.DfcError) as ei:
+        dfc.encode_device(dev16(y), codebook=book, shape=(64, 64))
+    assert ei.value.status == dfc.EINVAL
+
+
+@pytest.mark.parametrize("name_shape", [("gate", (14336, 4096)), ("wk", (1024, 4096))])
+def test_full_size_block_matrices(name_shape):
+    name, shape = name_shape
+    x = dict(synth.llama3_8b_block())[name]
+    assert x.shape == shape
+    d, size = dfc.encode_device(dev16(x), shape=shape)
+    host = dfc.encode(x)
+    say("case full", name)
+    assert size == host.size
+    assert torch.equal(d[:size], torch.from_numpy(host).cuda())
+    info = dfc.blob_info(host)
+    out = torch.empty(int(info.n), dtype=torch.int16, device="cuda")
+    dfc.decode(d, info, out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, dev16(x))
