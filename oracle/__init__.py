@@ -40,12 +40,14 @@ Modules:
                  chunk-parallel decoders
 * ``blob``     - the serialized container and its derived decode tables
 * ``gemm``     - float64 reference product and the panel element order
+* ``panel``    - the panel layout consumed by the fused decode + product
+* ``padded``   - the offset-free padded-chunk layout and its decoders
 
 Parity status: every function is pinned by a test in ``tests/`` against
 something other than itself (closed forms, brute force, RFC 1951's worked
 example, hand-worked fixtures in ``tests/golden/``, or exact round trips).
 """
 
-from . import fields, codebook, stream, blob, gemm  # noqa: F401
+from . import fields, codebook, stream, blob, gemm, panel, padded  # noqa: F401
 
-__all__ = ["fields", "codebook", "stream", "blob", "gemm"]
+__all__ = ["fields", "codebook", "stream", "blob", "gemm", "panel", "padded"]

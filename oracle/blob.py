@@ -163,14 +163,17 @@ def section_sizes(enc, lut_bits: int):
     return {
         "tables": tables_bytes(lut_bits),
         "words": 4 * enc["words"].size,
-        "offsets": 4 * (-(-5 * (enc["n_chunks"] + 1) // 32) + 1),
+        "offsets": 0 if enc.get("off") is None else 4 * (-(-5 * (enc["n_chunks"] + 1) // 32) + 1),
         "blockout": 4 * (enc["n_blocks"] + 1),
         "raw": 16 * (-(-n // 16)),
         "panels": 0,
     }
 
 
-def write_blob(enc, lut_bits: int = 11, rows: int | None = None, cols: int | None = None) -> bytes:
+def write_blob(enc, lut_bits: int = 11, rows: int | None = None, cols: int | None = None,
+               layout: int = LAYOUT_FLAT) -> bytes:
+    """Container of a flat encoding (``stream.encode``), or of a padded one
+    (``padded.encode_padded``, layout 2: no offsets section)."""
     n = enc["n"]
     if rows is None or cols is None:
         rows, cols = 1, n
@@ -188,7 +191,7 @@ def write_blob(enc, lut_bits: int = 11, rows: int | None = None, cols: int | Non
     struct.pack_into("<IIQQQQIIIIIIQQII", buf, 0,
                      MAGIC, VERSION, n, enc["total_bits"], enc["n_chunks"], enc["n_blocks"],
                      enc["chunk_bytes"], enc["lanes"], enc["max_len_limit"], lut_bits,
-                     LAYOUT_FLAT, 0, rows, cols, 0, 0)
+                     layout, 0, rows, cols, 0, 0)
     fields = []
     for name in ("tables", "words", "offsets", "blockout", "raw", "panels"):
         fields += [offsets[name], sizes[name]]
@@ -201,7 +204,8 @@ def write_blob(enc, lut_bits: int = 11, rows: int | None = None, cols: int | Non
 
     put("tables", decode_tables(enc["lengths"], lut_bits))
     put("words", np.asarray(enc["words"], dtype="<u4").tobytes())
-    put("offsets", st.pack_offsets(enc["off"]).astype("<u4").tobytes())
+    if sizes["offsets"]:
+        put("offsets", st.pack_offsets(enc["off"]).astype("<u4").tobytes())
     put("blockout", np.asarray(enc["out"], dtype="<u4").tobytes())
     put("raw", np.asarray(enc["raw"], dtype=np.uint8).tobytes())
     return bytes(buf)
@@ -225,7 +229,7 @@ def parse_blob(blob: bytes):
         return np.frombuffer(b, dtype=dtype, count=s // np.dtype(dtype).itemsize, offset=o).copy()
 
     words = view("words", "<u4")
-    offsets = st.unpack_offsets(view("offsets", "<u4"), n_chunks + 1)
+    offsets = st.unpack_offsets(view("offsets", "<u4"), n_chunks + 1) if sec["offsets"][1] else None
     out = view("blockout", "<u4")
     raw = view("raw", np.uint8)[:n]
     return {
@@ -243,6 +247,9 @@ def decode_blob(blob: bytes) -> np.ndarray:
     """Original bf16 bit patterns from a container (chunk-parallel decoder)."""
     from .fields import merge
     p = parse_blob(blob)
+    if p["layout"] == 2:
+        from .padded import decode_padded_blob
+        return decode_padded_blob(blob)
     e = st.decode_chunked(p["words"], p["off"], p["total_bits"], p["chunk_bytes"],
                           p["n_chunks"], p["lengths"])
     if e.size != p["n"]:
