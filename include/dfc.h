@@ -56,8 +56,16 @@ typedef enum {
  * (l = 0..63, j = 0..7) is W[32 p + l % 32][c0 + 16 t + 8 (l / 32) + j], the
  * A-operand order of a 32x32x16 bf16 matrix instruction.  Every item's codes
  * start on a fresh chunk and form their own blocks; a table of first chunk,
- * first block and code bits per item travels in the container. */
-enum { DFC_LAYOUT_FLAT = 0, DFC_LAYOUT_PANEL = 1 };
+ * first block and code bits per item travels in the container.
+ * PADDED: row-major like FLAT, but no code crosses a chunk boundary: a code
+ * that does not fit in what is left of its chunk opens the next chunk, and
+ * the unused tail is set to ones.  Every chunk then decodes from its first
+ * bit, keeping the codes that end inside it, and the container has no
+ * chunk offsets (a reading of the two-phase decode of the DFloat11 blog,
+ * section 03 item 2, with one auxiliary variable fewer).  The tail stops the
+ * decode because it is shorter than the longest code and, in a complete
+ * canonical code, no codeword is a prefix of a run of ones that short. */
+enum { DFC_LAYOUT_FLAT = 0, DFC_LAYOUT_PANEL = 1, DFC_LAYOUT_PADDED = 2 };
 enum { DFC_PANEL_ROWS = 32, DFC_PANEL_K_DEFAULT = 1024 };
 enum { DFC_MAX_BATCH = 32 };
 
@@ -67,7 +75,7 @@ typedef struct {
     uint32_t lanes_per_block; /* T: chunks per block: 64 (default; one wavefront), 128 or 256 */
     uint32_t max_code_len;    /* code length limit, 1..24 (default 24) */
     uint32_t lut_bits;        /* k: bits indexed by the first-level decode table, 8..12 (default 11) */
-    uint32_t layout;          /* DFC_LAYOUT_FLAT (row-major) or DFC_LAYOUT_PANEL */
+    uint32_t layout;          /* DFC_LAYOUT_FLAT (row-major), DFC_LAYOUT_PANEL or DFC_LAYOUT_PADDED */
     uint32_t threads;         /* host encoder threads; 0 = min(hardware threads, 16) */
     uint32_t panel_k;         /* PANEL: columns per item, a multiple of 16 (0 = 1024) */
     uint32_t reserved;        /* must be 0 */
@@ -156,14 +164,15 @@ dfc_status dfc_blob_info(const void *blob, uint64_t bytes, dfc_info *out);
 /* Decode one container on the GPU (DFloat11 blog, section 03: the two-phase
  * kernel with lookup tables in on-chip memory).  Device, asynchronous on
  * stream.  blob_dev: device copy of the container described by info (256-byte
- * aligned).  dst_dev: n uint16 outputs (16-byte aligned), receives the
- * original bf16 bit patterns, row-major.  status_dev: NULL, or one device
+ * aligned), in the FLAT or the PADDED layout.  dst_dev: n uint16 outputs
+ * (16-byte aligned), receives the original bf16 bit patterns, row-major.
+ * status_dev: NULL, or one device
  * uint32 that the kernel sets to a nonzero value if a block's decoded count
  * disagrees with its block offsets (the caller clears it beforehand and reads
  * it after the stream completes; outputs of such a block are left
  * unwritten).  Synchronous errors: DFC_EINVAL (null/misaligned pointers),
- * DFC_ESIZE (n != info->n), DFC_EUNSUPPORTED (lanes_per_block != 64),
- * DFC_EHIP (launch failure). */
+ * DFC_ESIZE (n != info->n), DFC_EUNSUPPORTED (lanes_per_block != 64, a
+ * PANEL container, streams past 4 GiB), DFC_EHIP (launch failure). */
 dfc_status dfc_decode(const void *blob_dev, const dfc_info *info, uint16_t *dst_dev, uint64_t n,
                       uint32_t *status_dev, void *stream);
 

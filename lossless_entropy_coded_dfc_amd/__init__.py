@@ -27,6 +27,7 @@ __all__ = [
 MAX_BATCH = 32
 LAYOUT_FLAT = 0
 LAYOUT_PANEL = 1
+LAYOUT_PADDED = 2
 PANEL_ROWS = 32
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libdfc.so")
@@ -200,7 +201,9 @@ def encode(bits, chunk_bytes: int = 16, lanes: int = 64, max_code_len: int = 24,
            panel_k: int = 0) -> np.ndarray:
     """Encode bf16 bit patterns (any shape, row-major) into a DFC1 container
     (numpy uint8 array).  ``layout=LAYOUT_PANEL`` writes the order the fused
-    decode + GEMM consumes (2-D input, rows % 32 == 0, cols % 16 == 0)."""
+    decode + GEMM consumes (2-D input, rows % 32 == 0, cols % 16 == 0);
+    ``layout=LAYOUT_PADDED`` keeps codes inside their chunks and drops the
+    chunk offsets."""
     arr = np.asarray(bits)
     src = _u16(arr)
     if shape is None:

@@ -11,7 +11,9 @@
 //           offsets come from the container, each lane counts the codes of
 //           its chunk, a wavefront prefix scan turns counts into write
 //           positions, the exponents go to LDS and are merged with the raw
-//           bytes into bf16 with coalesced 16-byte stores.
+//           bytes into bf16 with coalesced 16-byte stores.  Containers in the
+//           padded layout have no chunk offsets: there every chunk starts
+//           with a code and ends with its last whole code.
 //
 // Work decomposition: one lane per chunk (C bytes of code stream), one
 // wavefront (64 lanes) per block of 64 chunks.  Workgroups are persistent:
@@ -123,7 +125,7 @@ __device__ __forceinline__ void store_octet(const Buffers &bf, const BlockRange 
     }
 }
 
-template <int C>
+template <int C, bool Padded>
 __device__ __forceinline__ void decode_block(const ItemArgs &a, const Buffers &bf, uint32_t b, uint32_t lane,
                                              const Chunk<C> &ck, uint8_t *stage, uint32_t stage_off,
                                              uint32_t stage_bytes, const Tables &t, uint32_t *status,
@@ -136,17 +138,27 @@ __device__ __forceinline__ void decode_block(const ItemArgs &a, const Buffers &b
     for (uint32_t o = 16u * lane; o + 16u <= ((nz + 15u) & ~15u); o += 16u * kWave)
         *reinterpret_cast<uint4 *>(stage + o) = make_uint4(0, 0, 0, 0);
     const uint32_t chunk = b * kWave + lane;
-    int start, end;
-    chunk_span<C>(ck, chunk, int64_t(a.total_bits) - int64_t(uint64_t(chunk) * (8ull * C)), start, end);
+    const int64_t bits_left = int64_t(a.total_bits) - int64_t(uint64_t(chunk) * (8ull * C));
+    int start = 0, end;
+    if constexpr (Padded)
+        end = int(min(int64_t(8 * C), max(bits_left, int64_t(-1))));
+    else
+        chunk_span<C>(ck, chunk, bits_left, start, end);
 
-    const uint32_t cnt = start < end ? count_codes<C>(ck, start, end, t) : 0u;
+    uint32_t cnt = 0;
+    if (start < end) cnt = Padded ? count_codes_padded<C>(ck, end, t) : count_codes<C>(ck, start, end, t);
     const uint32_t incl = wave_inclusive_scan(cnt);
     const uint32_t total = __builtin_amdgcn_readlane(incl, kWave - 1);
     // A chunk of 8C bits holds at most 8C code starts; anything else (or a
     // total that disagrees with the block offsets) means a corrupt stream.
     const bool bad = (total != br.e_out - br.s_out) | (__builtin_amdgcn_ballot_w64(cnt > 8u * C) != 0);
     const uint32_t lead = br.s_out & 7u;
-    if (!bad && cnt) write_codes<C>(ck, start, end, stage - stage_off, stage_off + lead + (incl - cnt), t);
+    if (!bad && cnt) {
+        if constexpr (Padded)
+            write_codes_padded<C>(ck, end, cnt, stage - stage_off, stage_off + lead + (incl - cnt), t);
+        else
+            write_codes<C>(ck, start, end, stage - stage_off, stage_off + lead + (incl - cnt), t);
+    }
     // Everything prefetched must be in registers before the first store, on
     // every path to the next block.
     wait_for(R);
@@ -182,7 +194,7 @@ __device__ __forceinline__ void decode_block(const ItemArgs &a, const Buffers &b
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int C>
+template <int C, bool Padded>
 __global__ __launch_bounds__(1024, Occupancy<C>::kWavesPerSimd) void dfc_decode_kernel(const BatchArgs args) {
     extern __shared__ __align__(16) uint8_t lds[];
     constexpr int PF = Prefetch<C>::N;
@@ -207,7 +219,7 @@ __global__ __launch_bounds__(1024, Occupancy<C>::kWavesPerSimd) void dfc_decode_
     uint32_t b = lo_b + wave;
     if (b >= hi_b) return;
     Chunk<C> cur;
-    load_chunk<C>(bf.words, bf.offw, b * kWave + lane, cur);
+    load_chunk<C, !Padded>(bf.words, bf.offw, b * kWave + lane, cur);
     uint32_t s_out = blockout[b], e_out = blockout[b + 1];
     // Resident on entry, as it is on every later iteration (see wait_for).
     wait_for(cur);
@@ -224,11 +236,11 @@ __global__ __launch_bounds__(1024, Occupancy<C>::kWavesPerSimd) void dfc_decode_
         Chunk<C> nxt{};
         uint32_t s_nxt = 0, e_nxt = 0;
         if (more) {
-            load_chunk<C>(bf.words, bf.offw, bn * kWave + lane, nxt);
+            load_chunk<C, !Padded>(bf.words, bf.offw, bn * kWave + lane, nxt);
             s_nxt = blockout[bn];
             e_nxt = blockout[bn + 1];
         }
-        decode_block<C>(a, bf, b, lane, cur, stage, stage_off, args.stage_bytes, t, args.status, R, br, nxt);
+        decode_block<C, Padded>(a, bf, b, lane, cur, stage, stage_off, args.stage_bytes, t, args.status, R, br, nxt);
         if (!more) break;
         cur = nxt;
         b = bn;
@@ -261,7 +273,7 @@ std::vector<uint32_t> share_workgroups(const std::vector<uint64_t> &blocks, uint
     return g;
 }
 
-template <int C>
+template <int C, bool Padded>
 dfc_status launch_group(const dfc_batch_item *items, const uint32_t *idx, uint32_t count, uint32_t *status,
                         hipStream_t stream) {
     BatchArgs args;
@@ -282,7 +294,7 @@ dfc_status launch_group(const dfc_batch_item *items, const uint32_t *idx, uint32
     const uint32_t stage = (max_block + 32u + 15u) & ~15u;
     static bool attr_set = false;
     if (!attr_set) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void *>(&dfc_decode_kernel<C>),
+        if (hipFuncSetAttribute(reinterpret_cast<const void *>(&dfc_decode_kernel<C, Padded>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, int(kLdsBytes)) != hipSuccess)
             return DFC_EHIP;
         attr_set = true;
@@ -293,7 +305,7 @@ dfc_status launch_group(const dfc_batch_item *items, const uint32_t *idx, uint32
         const uint32_t lds = max_tables + w * stage;
         if (lds > kLdsBytes) return 0;
         int per_cu = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(&dfc_decode_kernel<C>),
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(&dfc_decode_kernel<C, Padded>),
                                                          int(w * kWave), size_t(lds)) != hipSuccess)
             per_cu = int(kLdsBytes / lds);
         return per_cu;
@@ -353,7 +365,7 @@ dfc_status launch_group(const dfc_batch_item *items, const uint32_t *idx, uint32
     args.count = uint32_t(live.size());
     args.stage_bytes = stage;
     args.status = status;
-    hipLaunchKernelGGL(dfc_decode_kernel<C>, dim3(wg), dim3(waves * kWave), lds, stream, args);
+    dfc_decode_kernel<C, Padded><<<dim3(wg), dim3(waves * kWave), lds, stream>>>(args);
     return hipGetLastError() == hipSuccess ? DFC_OK : DFC_EHIP;
 }
 
@@ -365,7 +377,7 @@ dfc_status check_item(const dfc_batch_item &it) {
     if (!it.blob_dev || !it.dst_dev) return DFC_EINVAL;
     if ((reinterpret_cast<uintptr_t>(it.blob_dev) & 255u) || (reinterpret_cast<uintptr_t>(it.dst_dev) & 15u))
         return DFC_EINVAL;
-    if (in.layout != DFC_LAYOUT_FLAT) return DFC_EUNSUPPORTED;
+    if (in.layout != DFC_LAYOUT_FLAT && in.layout != DFC_LAYOUT_PADDED) return DFC_EUNSUPPORTED;
     if (in.lanes_per_block != 64) return DFC_EUNSUPPORTED;
     const uint32_t C = in.chunk_bytes;
     if (C != 4 && C != 8 && C != 16 && C != 32) return DFC_EINVAL;
@@ -399,19 +411,29 @@ dfc_status dfc_decode_batch(const dfc_batch_item *items, uint32_t count, uint32_
     }
     hipStream_t st = static_cast<hipStream_t>(stream);
     static const int sizes[4] = {4, 8, 16, 32};
-    for (int c : sizes) {
-        uint32_t idx[DFC_MAX_BATCH], m = 0;
-        for (uint32_t k = 0; k < count; ++k)
-            if (items[k].info->n && items[k].info->chunk_bytes == uint32_t(c)) idx[m++] = k;
-        if (!m) continue;
-        dfc_status s = DFC_OK;
-        switch (c) {
-            case 4: s = launch_group<4>(items, idx, m, status_dev, st); break;
-            case 8: s = launch_group<8>(items, idx, m, status_dev, st); break;
-            case 16: s = launch_group<16>(items, idx, m, status_dev, st); break;
-            default: s = launch_group<32>(items, idx, m, status_dev, st); break;
+    // one launch per (chunk size, layout) present in the batch
+    for (int pad = 0; pad < 2; ++pad) {
+        const uint32_t layout = pad ? DFC_LAYOUT_PADDED : DFC_LAYOUT_FLAT;
+        for (int c : sizes) {
+            uint32_t idx[DFC_MAX_BATCH], m = 0;
+            for (uint32_t k = 0; k < count; ++k) {
+                const dfc_info &in = *items[k].info;
+                if (in.n && in.chunk_bytes == uint32_t(c) && in.layout == layout) idx[m++] = k;
+            }
+            if (!m) continue;
+            dfc_status s = DFC_OK;
+            switch (c * 2 + pad) {
+                case 8: s = launch_group<4, false>(items, idx, m, status_dev, st); break;
+                case 9: s = launch_group<4, true>(items, idx, m, status_dev, st); break;
+                case 16: s = launch_group<8, false>(items, idx, m, status_dev, st); break;
+                case 17: s = launch_group<8, true>(items, idx, m, status_dev, st); break;
+                case 32: s = launch_group<16, false>(items, idx, m, status_dev, st); break;
+                case 33: s = launch_group<16, true>(items, idx, m, status_dev, st); break;
+                case 64: s = launch_group<32, false>(items, idx, m, status_dev, st); break;
+                default: s = launch_group<32, true>(items, idx, m, status_dev, st); break;
+            }
+            if (s != DFC_OK) return s;
         }
-        if (s != DFC_OK) return s;
     }
     return DFC_OK;
 }

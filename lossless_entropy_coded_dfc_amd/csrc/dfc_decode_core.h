@@ -71,8 +71,9 @@ struct Chunk {
 };
 
 // Chunk `chunk` of a stream: its words through the buffer resource `words`,
-// its offset-array words through `offw`.
-template <int C>
+// its offset-array words through `offw` (none for the padded layout, whose
+// chunks start with a code).
+template <int C, bool Offsets = true>
 __device__ __forceinline__ void load_chunk(__amdgpu_buffer_rsrc_t words, __amdgpu_buffer_rsrc_t offw, uint32_t chunk,
                                            Chunk<C> &ck) {
     const uint32_t at = chunk * C;
@@ -102,10 +103,14 @@ __device__ __forceinline__ void load_chunk(__amdgpu_buffer_rsrc_t words, __amdgp
     }
     // Only loads here: combining the words right away would make the
     // compiler wait for every load in flight, prefetches included.
-    // Field `chunk` starts at bit 5 chunk of the offset array.
-    const uint32_t word = (chunk >> 5) * 5u + (((chunk & 31u) * 5u) >> 5);
-    ck.o0 = __builtin_amdgcn_raw_buffer_load_b32(offw, 4u * word, 0, 0);
-    ck.o1 = __builtin_amdgcn_raw_buffer_load_b32(offw, 4u * word + 4u, 0, 0);
+    if constexpr (Offsets) {
+        // Field `chunk` starts at bit 5 chunk of the offset array.
+        const uint32_t word = (chunk >> 5) * 5u + (((chunk & 31u) * 5u) >> 5);
+        ck.o0 = __builtin_amdgcn_raw_buffer_load_b32(offw, 4u * word, 0, 0);
+        ck.o1 = __builtin_amdgcn_raw_buffer_load_b32(offw, 4u * word + 4u, 0, 0);
+    } else {
+        ck.o0 = ck.o1 = 0;
+    }
 }
 
 // 32 stream bits starting at chunk-relative bit pos, 0 <= pos <= 32 (NW + 1).
@@ -220,6 +225,97 @@ __device__ __forceinline__ void write_codes(const Chunk<C> &ck, int start, int e
             acc += 0x10000u - l;
         }
         acc += 32u;
+    }
+}
+
+// Padded layout, phase one: the number of codes, decoded from the chunk's
+// first bit, that end at or before `end` (<= 8C).  Whole-window lookups run
+// while the k-bit window lies inside [0, end), so every code they count is
+// the chunk's own.  After them, either a long code has run past `end` (it is
+// the unused tail of ones, read as a code longer than the tail, and is
+// dropped), or the codes that still end by `end` are read off the boundary
+// mask of the window at the current position.
+template <int C>
+__device__ __forceinline__ uint32_t count_codes_padded(const Chunk<C> &ck, int end, const Tables &t) {
+    constexpr int NW = C / 4;
+    const int stop = end - int(t.kb) + 1;  // whole-window lookups start before this bit
+    uint32_t acc = kBias;
+#pragma unroll
+    for (int k = -1; k < NW; ++k) {
+        const uint32_t hi = k < 0 ? 0u : ck.w[k < 0 ? 0 : k];
+        const uint32_t lo = ck.w[k + 1];
+        // stay while shift >= 0 (pos <= 32 (k + 1)) and pos < stop
+        const uint16_t g = uint16_t(kBias + uint32_t(max(0, 32 * (k + 1) - stop + 1)));
+        for (;;) {
+            while (uint16_t(acc) >= g) {
+                const uint32_t win = __builtin_amdgcn_alignbit(hi, lo, acc);
+                acc += t.step[win >> t.kshift];
+            }
+            if (lo16(acc) >= kBias - 2048u) break;
+            acc += 0x1000u;
+            uint32_t sym;
+            const uint32_t win = __builtin_amdgcn_alignbit(hi, lo, acc);
+            acc += 0x10000u - long_code(win >> 8, t, sym);
+        }
+        acc += 32u;
+    }
+    uint32_t cnt = acc >> 16;
+    const int pos = 32 * (NW + 1) - int(lo16(acc)) + int(kBias);
+    if (pos > end) return cnt - 1u;
+    if (pos < end) {
+        const uint32_t we = window_at<NW>(ck.w, uint32_t(pos));
+        cnt += __popc(uint32_t(t.mask[we >> t.kshift]) & ((1u << (end - pos)) - 1u));
+    }
+    return cnt;
+}
+
+// Padded layout, phase two: the chunk's cnt codes (from the counting pass)
+// ORed into the staging area from byte q0 on.  Nothing past them may be
+// written: what follows a chunk's last code is its tail of ones and the next
+// chunk's bits, not the next chunk's first codes.  Whole-window lookups need
+// no cut (their codes end by `end`); a long code is written only if it is
+// one of the cnt; the last few codes go out with their entry cut to the
+// codes still owed.
+template <int C>
+__device__ __forceinline__ void write_codes_padded(const Chunk<C> &ck, int end, uint32_t cnt, uint8_t *lds_base,
+                                                   uint32_t q0, const Tables &t) {
+    constexpr int NW = C / 4;
+    const int stop = end - int(t.kb) + 1;
+    uint32_t acc = kBias;
+#pragma unroll
+    for (int k = -1; k < NW; ++k) {
+        const uint32_t hi = k < 0 ? 0u : ck.w[k < 0 ? 0 : k];
+        const uint32_t lo = ck.w[k + 1];
+        const uint16_t g = uint16_t(kBias + uint32_t(max(0, 32 * (k + 1) - stop + 1)));
+        for (;;) {
+            while (uint16_t(acc) >= g) {
+                const uint32_t win = __builtin_amdgcn_alignbit(hi, lo, acc);
+                const uint2 e = t.wsym[win >> t.kshift];
+                or_4_bytes(lds_base, q0 + (acc >> 16), e.x);
+                acc += e.y;
+            }
+            if (lo16(acc) >= kBias - 2048u) break;
+            acc += 0x1000u;
+            uint32_t sym;
+            const uint32_t win = __builtin_amdgcn_alignbit(hi, lo, acc);
+            const uint32_t l = long_code(win >> 8, t, sym);
+            if ((acc >> 16) < cnt) or_4_bytes(lds_base, q0 + (acc >> 16), sym);
+            acc += 0x10000u - l;
+        }
+        acc += 32u;
+    }
+    // (done << 16) + kBias - pos, advanced by the symbol entries' steps.  The
+    // codes owed end within k - 1 <= 11 bits, so three entries hold them.
+    uint32_t a = (acc & 0xFFFF0000u) + (kBias - uint32_t(32 * (NW + 1) - int(lo16(acc)) + int(kBias)));
+#pragma unroll
+    for (int it = 0; it < 3; ++it) {
+        if ((a >> 16) >= cnt) break;
+        const uint32_t pos = kBias - lo16(a);
+        const uint2 e = t.wsym[window_at<NW>(ck.w, pos) >> t.kshift];
+        const uint32_t owed = cnt - (a >> 16);
+        const uint32_t keep = owed >= 4u ? 0xFFFFFFFFu : (1u << (8u * owed)) - 1u;
+        or_4_bytes(lds_base, q0 + (a >> 16), e.x & keep);
+        a += e.y;
     }
 }
 

@@ -2,8 +2,9 @@
 // and the device launcher (internal to libdfc).
 //
 // Container: 256-byte header, 256 code lengths, then the sections tables,
-// words, offsets, blockout, raw (and panels, unused by the flat layout),
-// each at the next multiple of 256 bytes, zero padding.  Little-endian.
+// words, offsets (empty in the padded layout), blockout, raw (and panels,
+// used by the panel layout only), each at the next multiple of 256 bytes,
+// zero padding.  Little-endian.
 #pragma once
 
 #include <algorithm>
@@ -64,12 +65,13 @@ inline Layout layout_sizes(uint64_t total_bits, uint32_t chunk_bytes, uint32_t l
 struct SectionSizes {
     uint64_t bytes[kNumSections];
 };
+// with_offsets = false: the padded layout, whose chunks need no offsets.
 inline SectionSizes section_sizes(uint64_t n, uint64_t n_chunks, uint64_t n_blocks, uint32_t chunk_bytes,
-                                  uint32_t lut_bits, uint64_t n_items = 0) {
+                                  uint32_t lut_bits, uint64_t n_items = 0, bool with_offsets = true) {
     SectionSizes s;
     s.bytes[kTables] = tables_bytes(lut_bits);
     s.bytes[kWords] = 4 * (n_chunks * (chunk_bytes / 4) + kGuardWords);
-    s.bytes[kOffsets] = 4 * (ceil_div(kOffsetBits * (n_chunks + 1), 32) + 1);
+    s.bytes[kOffsets] = with_offsets ? 4 * (ceil_div(kOffsetBits * (n_chunks + 1), 32) + 1) : 0;
     s.bytes[kBlockout] = 4 * (n_blocks + 1);
     s.bytes[kRaw] = 16 * ceil_div(n, 16);
     s.bytes[kPanels] = n_items ? 16 * (n_items + 1) : 0;

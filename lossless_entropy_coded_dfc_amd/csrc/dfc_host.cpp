@@ -213,7 +213,7 @@ bool params_ok(const dfc_params &p) {
     if (T != 64 && T != 128 && T != 256) return false;
     if (p.max_code_len < 1 || p.max_code_len > kMaxLen) return false;
     if (p.lut_bits < 8 || p.lut_bits > 12) return false;
-    if (p.layout != DFC_LAYOUT_FLAT && p.layout != DFC_LAYOUT_PANEL) return false;
+    if (p.layout != DFC_LAYOUT_FLAT && p.layout != DFC_LAYOUT_PANEL && p.layout != DFC_LAYOUT_PADDED) return false;
     if (p.reserved) return false;
     return true;
 }
@@ -353,6 +353,85 @@ dfc_status encode_panel(const uint16_t *src, uint64_t n, const dfc_params &p, co
     return DFC_OK;
 }
 
+// Padded layout: no code crosses a chunk boundary (see dfc.h).  Pass 1
+// places the chunk boundaries, which depend on every code before them, in
+// one sequential walk over the code lengths; chunks own whole stream words,
+// so pass 2 packs ranges of chunks on separate threads.
+dfc_status encode_padded(const uint16_t *src, uint64_t n, const dfc_params &p, const uint8_t len[256],
+                         const uint32_t code[256], uint64_t rows, uint64_t cols, uint8_t *dst, uint64_t cap,
+                         uint64_t *written) {
+    const uint32_t C = p.chunk_bytes, T = p.lanes_per_block;
+    const uint32_t chunk_bits = 8u * C;
+    // first element of every chunk that holds codes, then n
+    std::vector<uint32_t> first{0};
+    uint32_t fill = 0;
+    for (uint64_t j = 0; j < n; ++j) {
+        const uint32_t l = len[exponent_of(src[j])];
+        if (fill + l > chunk_bits) {
+            first.push_back(uint32_t(j));
+            fill = 0;
+        }
+        fill += l;
+    }
+    const uint64_t used = n ? first.size() : 0;
+    first.push_back(uint32_t(n));
+    const uint64_t total_bits = used ? (used - 1) * chunk_bits + fill : 0;
+    Layout L = layout_sizes(total_bits, C, T);
+    if (L.n_chunks_used != used || L.n_chunks >= (uint64_t(1) << 32)) return DFC_ESIZE;
+    SectionSizes sz = section_sizes(n, L.n_chunks, L.n_blocks, C, p.lut_bits, 0, false);
+    uint64_t off[kNumSections];
+    const uint64_t blob_bytes = place_sections(sz, off);
+    if (cap < blob_bytes) return DFC_ESIZE;
+    zero_parallel(dst, blob_bytes, p.threads);
+    write_header(dst, p, n, total_bits, L.n_chunks, L.n_blocks, rows, cols, sz, off, blob_bytes, len);
+
+    uint8_t *words = dst + off[kWords];
+    uint8_t *raw = dst + off[kRaw];
+    uint8_t *blockout = dst + off[kBlockout];
+    const unsigned nt = unsigned(std::min<uint64_t>(pick_threads(p.threads, n), std::max<uint64_t>(used, 1)));
+    parallel_for(nt, [&](unsigned t) {
+        for (uint64_t c = used * t / nt; c < used * (t + 1) / nt; ++c) {
+            uint8_t *w = words + uint64_t(C) * c;
+            uint64_t acc = 0;
+            uint32_t nacc = 0, wi = 0, bits = 0;
+            for (uint64_t j = first[c]; j < first[c + 1]; ++j) {
+                const uint16_t b = src[j];
+                const uint32_t e = exponent_of(b);
+                raw[j] = raw_of(b);
+                const uint32_t l = len[e];
+                acc = (acc << l) | code[e];
+                nacc += l;
+                bits += l;
+                if (nacc >= 32) {
+                    nacc -= 32;
+                    store_le<uint32_t>(w + 4 * wi++, uint32_t(acc >> nacc));
+                }
+            }
+            if (c + 1 < used) {
+                // unused tail of a chunk followed by another: ones
+                for (uint32_t r = chunk_bits - bits; r > 0;) {
+                    const uint32_t k = std::min<uint32_t>(r, 32u - nacc);
+                    acc = (acc << k) | ((uint64_t(1) << k) - 1u);
+                    nacc += k;
+                    r -= k;
+                    if (nacc == 32) {
+                        store_le<uint32_t>(w + 4 * wi++, uint32_t(acc));
+                        nacc = 0;
+                    }
+                }
+            }
+            if (nacc > 0) store_le<uint32_t>(w + 4 * wi, uint32_t(acc << (32 - nacc)));
+        }
+    });
+    for (uint64_t b = 0; b < L.n_blocks; ++b) {
+        const uint64_t c = b * T;
+        store_le<uint32_t>(blockout + 4 * b, c < used ? first[c] : uint32_t(n));
+    }
+    store_le<uint32_t>(blockout + 4 * L.n_blocks, uint32_t(n));
+    *written = blob_bytes;
+    return DFC_OK;
+}
+
 uint64_t kraft(const uint8_t len[256]) {
     uint64_t k = 0;
     for (int s = 0; s < 256; ++s)
@@ -442,6 +521,12 @@ dfc_status dfc_encode_bound(uint64_t n, const dfc_params *pin, uint64_t *max_byt
         PanelGeom g;
         if (!panel_geom(p.rows, p.cols, p.panel_k ? p.panel_k : uint32_t(DFC_PANEL_K_DEFAULT), g)) return DFC_EINVAL;
         s = section_sizes(n, L.n_chunks + g.n_items, L.n_blocks + g.n_items, p.chunk_bytes, p.lut_bits, g.n_items);
+    } else if (p.layout == DFC_LAYOUT_PADDED) {
+        // every chunk but the last holds one code, or more than 8C - limit bits
+        const uint64_t cb = 8ull * p.chunk_bytes, lim = p.max_code_len;
+        const uint64_t chunks = std::min<uint64_t>(n, ceil_div(bits, cb - lim + 1) + 1);
+        const uint64_t blocks = ceil_div(chunks, p.lanes_per_block);
+        s = section_sizes(n, blocks * p.lanes_per_block, blocks, p.chunk_bytes, p.lut_bits, 0, false);
     }
     uint64_t off[kNumSections];
     *max_bytes = place_sections(s, off);
@@ -489,6 +574,7 @@ dfc_status dfc_encode(const uint16_t *src, uint64_t n, const dfc_params *pin, co
     canonical(len, canon, code);
     const uint32_t lut_bits = p.lut_bits;
     if (p.layout == DFC_LAYOUT_PANEL) return encode_panel(src, n, p, len, code, dst, cap, written);
+    if (p.layout == DFC_LAYOUT_PADDED) return encode_padded(src, n, p, len, code, rows, cols, dst, cap, written);
 
     // Pass 1: bits per thread range.
     std::vector<uint64_t> range_bits(nt + 1, 0);
@@ -595,8 +681,10 @@ dfc_status dfc_blob_info(const void *blob_v, uint64_t bytes, dfc_info *out) {
     in.rows = load_le<uint64_t>(b + hdr::rows);
     in.cols = load_le<uint64_t>(b + hdr::cols);
     in.blob_bytes = load_le<uint64_t>(b + hdr::blob_bytes);
-    if (in.layout != DFC_LAYOUT_FLAT && in.layout != DFC_LAYOUT_PANEL) return DFC_EUNSUPPORTED;
+    if (in.layout != DFC_LAYOUT_FLAT && in.layout != DFC_LAYOUT_PANEL && in.layout != DFC_LAYOUT_PADDED)
+        return DFC_EUNSUPPORTED;
     const bool panel = in.layout == DFC_LAYOUT_PANEL;
+    const bool padded = in.layout == DFC_LAYOUT_PADDED;
     dfc_params p;
     dfc_default_params(&p);
     p.chunk_bytes = in.chunk_bytes;
@@ -630,7 +718,10 @@ dfc_status dfc_blob_info(const void *blob_v, uint64_t bytes, dfc_info *out) {
     }
     if (in.n) {
         if (used < 2 || kraft(len) != (uint64_t(1) << kMaxLen)) return DFC_ECORRUPT;
-        if (in.total_bits < in.n * mn || in.total_bits > in.n * mx) return DFC_ECORRUPT;
+        // padded: every chunk boundary before the last code may add a tail
+        // shorter than the longest code
+        const uint64_t tails = padded ? (ceil_div(in.total_bits, 8ull * in.chunk_bytes) - 1) * (mx - 1) : 0;
+        if (in.total_bits < in.n * mn || in.total_bits > in.n * mx + tails) return DFC_ECORRUPT;
     } else if (in.total_bits) {
         return DFC_ECORRUPT;
     }
@@ -644,7 +735,8 @@ dfc_status dfc_blob_info(const void *blob_v, uint64_t bytes, dfc_info *out) {
     } else if (in.n_chunks >= (uint64_t(1) << 32) || in.n_blocks >= (uint64_t(1) << 32)) {
         return DFC_ECORRUPT;
     }
-    SectionSizes sz = section_sizes(in.n, in.n_chunks, in.n_blocks, in.chunk_bytes, in.lut_bits, in.n_items);
+    SectionSizes sz =
+        section_sizes(in.n, in.n_chunks, in.n_blocks, in.chunk_bytes, in.lut_bits, in.n_items, !padded);
     uint64_t off[kNumSections];
     const uint64_t blob_bytes = place_sections(sz, off);
     if (blob_bytes != in.blob_bytes) return DFC_ECORRUPT;
@@ -702,7 +794,7 @@ dfc_status dfc_blob_info(const void *blob_v, uint64_t bytes, dfc_info *out) {
         if (bits_sum != in.total_bits) return DFC_ECORRUPT;
     }
     // Chunk offsets: at most (longest code - 1) for live chunks, 0 elsewhere.
-    {
+    if (!padded) {
         const uint8_t *ow = b + off[kOffsets];
         const uint64_t chunk_bits = 8ull * in.chunk_bytes;
         const uint32_t max_off = mx ? mx - 1 : 0;

@@ -234,3 +234,86 @@ def test_panel_validation_rejects_corruption():
         with pytest.raises(dfc.DfcError) as ei:
             dfc.blob_info(bad)
         assert ei.value.status == dfc.ECORRUPT, name
+
+
+# ------------------------------------------------------------ padded layout
+
+from oracle import padded as pdl  # noqa: E402
+
+
+def oracle_padded_blob(x, C, T=64, k=11, lengths=None):
+    shape = x.shape if x.ndim == 2 else (1, x.size)
+    if x.size == 0:
+        shape = (1, 0)
+    return pdl.write_padded_blob(pdl.encode_padded(x, C, T, lengths=lengths), k, *shape)
+
+
+@pytest.mark.parametrize("C", [4, 8, 16, 32])
+@pytest.mark.parametrize("kind", ["outliers", "uniform", "ladder", "t", "const"])
+def test_padded_encoder_matches_oracle_bytes(C, kind):
+    shape = (41, 997)
+    x = {"outliers": lambda: synth.gaussian_with_outliers(shape, 0.02, (60, C)),
+         "uniform": lambda: synth.uniform_bits(shape, (61, C)),
+         "ladder": lambda: synth.exponent_ladder(shape, (62, C)),
+         "t": lambda: synth.student_t(shape, 3.0, 0.02, (63, C)),
+         "const": lambda: np.full(shape, 0x3C00, dtype=np.uint16)}[kind]()
+    for k in (8, 12):
+        lib_blob = dfc.encode(x, chunk_bytes=C, lut_bits=k, layout=dfc.LAYOUT_PADDED)
+        assert bytes(lib_blob) == oracle_padded_blob(x, C, 64, k)
+        info = dfc.blob_info(lib_blob)
+        assert info.layout == dfc.LAYOUT_PADDED and info.offsets_bytes == 0 and info.off_offsets == 0
+
+
+def test_padded_lanes_threads_and_edge_sizes():
+    x = synth.gaussian_with_outliers((2500, 1000), 0.02, (64,))
+    for T in (64, 128, 256):
+        for threads in (1, 5, 16):
+            b = dfc.encode(x, chunk_bytes=8, lanes=T, threads=threads, layout=dfc.LAYOUT_PADDED)
+            assert bytes(b) == oracle_padded_blob(x, 8, T), (T, threads)
+    for n in (0, 1, 2, 15, 16, 17, 63, 64, 65, 1000):
+        y = synth.uniform_bits((n,), (65, n))
+        for C in (4, 32):
+            b = dfc.encode(y, chunk_bytes=C, layout=dfc.LAYOUT_PADDED)
+            assert bytes(b) == oracle_padded_blob(y, C), (n, C)
+            dfc.blob_info(b)
+
+
+def test_padded_external_codebook_bound_and_size():
+    g = synth.gaussian((256, 256), 0.02, (66,))
+    book = dfc.build_codebook(cb.histogram(fields.split(g)[0]) + 1, 24)
+    x = synth.uniform_bits((100, 999), (67,))
+    b = dfc.encode(x, chunk_bytes=4, codebook=book, layout=dfc.LAYOUT_PADDED)
+    assert bytes(b) == oracle_padded_blob(x, 4, lengths=np.frombuffer(bytes(book.len), dtype=np.uint8))
+    # the bound holds for the worst case: every code 24 bits long
+    for C in (4, 8, 16, 32):
+        p = dfc.default_params(chunk_bytes=C, layout=dfc.LAYOUT_PADDED)
+        assert len(dfc.encode(x, chunk_bytes=C, codebook=book, layout=dfc.LAYOUT_PADDED)) <= dfc.encode_bound(x.size, p)
+    # offsets gone: smaller than the flat container, within 2% of the
+    # entropy bound at every chunk size and within 1% from C = 16 on
+    y = synth.gaussian((1024, 4096), 0.02, (0,))
+    bound = bl.entropy_bound_bytes(cb.histogram(fields.split(y)[0]))
+    for C in (4, 8, 16, 32):
+        flat = dfc.blob_info(dfc.encode(y, chunk_bytes=C)).coded_bytes
+        pad = dfc.blob_info(dfc.encode(y, chunk_bytes=C, layout=dfc.LAYOUT_PADDED)).coded_bytes
+        assert pad < flat, C
+        assert pad / bound < (1.01 if C >= 16 else 1.02), C
+
+
+def test_padded_validation_rejects_corruption():
+    x = synth.gaussian((128, 1024), 0.02, (68,))
+    b = dfc.encode(x, layout=dfc.LAYOUT_PADDED)
+    info = dfc.blob_info(b)
+    flat = dfc.encode(x)
+    cases = {
+        "layout=3": (corrupt(b, 56, struct.pack("<I", 3)), dfc.EUNSUPPORTED),
+        # a flat header on a padded body: the section table no longer fits
+        "layout=flat": (corrupt(b, 56, struct.pack("<I", 0)), dfc.ECORRUPT),
+        "padded header on flat body": (corrupt(flat, 56, struct.pack("<I", 2)), dfc.ECORRUPT),
+        "total_bits": (corrupt(b, 16, struct.pack("<Q", info.total_bits + 8 * 16 * 64)), dfc.ECORRUPT),
+        "blockout_end": (corrupt(b, info.off_blockout + 4 * info.n_blocks, struct.pack("<I", info.n - 1)),
+                         dfc.ECORRUPT),
+    }
+    for name, (blob, want) in cases.items():
+        with pytest.raises(dfc.DfcError) as ei:
+            dfc.blob_info(blob)
+        assert ei.value.status == want, name
