@@ -42,12 +42,13 @@ Modules:
 * ``gemm``     - float64 reference product and the panel element order
 * ``panel``    - the panel layout consumed by the fused decode + product
 * ``padded``   - the offset-free padded-chunk layout and its decoders
+* ``ans``      - interleaved rANS coding of the exponents (layout 3)
 
 Parity status: every function is pinned by a test in ``tests/`` against
 something other than itself (closed forms, brute force, RFC 1951's worked
 example, hand-worked fixtures in ``tests/golden/``, or exact round trips).
 """
 
-from . import fields, codebook, stream, blob, gemm, panel, padded  # noqa: F401
+from . import fields, codebook, stream, blob, gemm, panel, padded, ans  # noqa: F401
 
-__all__ = ["fields", "codebook", "stream", "blob", "gemm", "panel", "padded"]
+__all__ = ["fields", "codebook", "stream", "blob", "gemm", "panel", "padded", "ans"]

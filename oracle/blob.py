@@ -229,7 +229,10 @@ def parse_blob(blob: bytes):
         return np.frombuffer(b, dtype=dtype, count=s // np.dtype(dtype).itemsize, offset=o).copy()
 
     words = view("words", "<u4")
-    offsets = st.unpack_offsets(view("offsets", "<u4"), n_chunks + 1) if sec["offsets"][1] else None
+    # 5-bit chunk offsets in the flat and panel layouts (the padded layout
+    # has none; the ANS layout keeps block stream offsets there instead)
+    five_bit = sec["offsets"][1] and layout in (0, 1)
+    offsets = st.unpack_offsets(view("offsets", "<u4"), n_chunks + 1) if five_bit else None
     out = view("blockout", "<u4")
     raw = view("raw", np.uint8)[:n]
     return {
