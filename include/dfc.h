@@ -65,7 +65,25 @@ typedef enum {
  * section 03 item 2, with one auxiliary variable fewer).  The tail stops the
  * decode because it is shorter than the longest code and, in a complete
  * canonical code, no codeword is a prefix of a run of ones that short. */
-enum { DFC_LAYOUT_FLAT = 0, DFC_LAYOUT_PANEL = 1, DFC_LAYOUT_PADDED = 2 };
+/* ANS: row-major; the exponents are coded with interleaved rANS instead of
+ * the prefix code (an arithmetic-family code of the kind the DFloat11 blog's
+ * section 02 names, as in the ANS decoder of the VcLLM page's introduction).
+ * The exponent histogram is quantised to frequencies f[s] summing to 2^12
+ * (proportional shares rounded down, at least 1 for a present symbol, the
+ * remaining units to the largest fractional parts, an excess taken back from
+ * the largest shares); states are 32-bit integers in [2^16, 2^32) and the
+ * stream is 16-bit words: decoding slot = x mod 2^12 gives the symbol s with
+ * cum[s] <= slot < cum[s] + f[s], then x = f[s] (x >> 12) + slot - cum[s], and
+ * if x < 2^16 the next word w enters as x = (x << 16) | w.  A block is 64
+ * lanes x S steps: element i * 64 + l of the block belongs to lane l, and at
+ * every step the lanes that need a word take the block's next words in lane
+ * order.  The container keeps f (u16[256]) and the derived slot table in its
+ * tables section, all blocks' word streams in the words section, the first
+ * word of every block (u32, n_blocks + 1) in the offsets section and the 64
+ * initial states of every block (u32) in the blockout section; chunk_bytes
+ * and n_chunks are 0, lut_bits holds 12, tile_k holds S. */
+enum { DFC_LAYOUT_FLAT = 0, DFC_LAYOUT_PANEL = 1, DFC_LAYOUT_PADDED = 2, DFC_LAYOUT_ANS = 3 };
+enum { DFC_ANS_STEPS_DEFAULT = 512, DFC_ANS_PROB_BITS = 12 };
 enum { DFC_PANEL_ROWS = 32, DFC_PANEL_K_DEFAULT = 1024 };
 enum { DFC_MAX_BATCH = 32 };
 
@@ -75,10 +93,13 @@ typedef struct {
     uint32_t lanes_per_block; /* T: chunks per block: 64 (default; one wavefront), 128 or 256 */
     uint32_t max_code_len;    /* code length limit, 1..24 (default 24) */
     uint32_t lut_bits;        /* k: bits indexed by the first-level decode table, 8..12 (default 11) */
-    uint32_t layout;          /* DFC_LAYOUT_FLAT (row-major), DFC_LAYOUT_PANEL or DFC_LAYOUT_PADDED */
+    uint32_t layout;          /* DFC_LAYOUT_FLAT (row-major), _PANEL, _PADDED or _ANS */
     uint32_t threads;         /* host encoder threads; 0 = min(hardware threads, 16) */
     uint32_t panel_k;         /* PANEL: columns per item, a multiple of 16 (0 = 1024) */
-    uint32_t reserved;        /* must be 0 */
+    uint32_t ans_steps;       /* ANS: steps per block S, a multiple of 8 in 8..65536 (0 = 512);
+                                 must be 0 for the other layouts.  ANS ignores chunk_bytes,
+                                 max_code_len and lut_bits (they must still be valid) and
+                                 needs lanes_per_block = 64 */
     uint64_t rows, cols;      /* matrix shape recorded in the header; 0,0 = 1 x n (FLAT only);
                                  PANEL needs rows % 32 == 0 and cols % 16 == 0 */
 } dfc_params;
@@ -111,6 +132,8 @@ typedef struct {
     uint32_t panel_rows, panel_k;  /* PANEL: 32 and columns per item; 0 for FLAT */
     uint64_t n_items;              /* PANEL: items (32-row x panel_k-column slices) */
     uint64_t off_panels, panels_bytes;  /* PANEL: per-item table, (n_items + 1) x 4 u32 */
+    uint32_t ans_steps;                 /* ANS: steps per block S; 0 otherwise */
+    uint32_t ans_prob_bits;             /* ANS: 12 (frequencies sum to 2^12); 0 otherwise */
 } dfc_info;
 
 /* One matrix of a batched decode. */

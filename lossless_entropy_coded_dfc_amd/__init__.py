@@ -28,6 +28,7 @@ MAX_BATCH = 32
 LAYOUT_FLAT = 0
 LAYOUT_PANEL = 1
 LAYOUT_PADDED = 2
+LAYOUT_ANS = 3
 PANEL_ROWS = 32
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libdfc.so")
@@ -50,7 +51,7 @@ class Params(ctypes.Structure):
     _fields_ = [("chunk_bytes", ctypes.c_uint32), ("lanes_per_block", ctypes.c_uint32),
                 ("max_code_len", ctypes.c_uint32), ("lut_bits", ctypes.c_uint32),
                 ("layout", ctypes.c_uint32), ("threads", ctypes.c_uint32),
-                ("panel_k", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
+                ("panel_k", ctypes.c_uint32), ("ans_steps", ctypes.c_uint32),
                 ("rows", ctypes.c_uint64), ("cols", ctypes.c_uint64)]
 
 
@@ -75,7 +76,8 @@ class Info(ctypes.Structure):
         [(name, ctypes.c_uint32) for name in (
             "chunk_bytes", "lanes_per_block", "max_code_len", "lut_bits", "layout",
             "n_used", "min_len", "max_len", "max_block_elems", "panel_rows", "panel_k")] + \
-        [(name, ctypes.c_uint64) for name in ("n_items", "off_panels", "panels_bytes")]
+        [(name, ctypes.c_uint64) for name in ("n_items", "off_panels", "panels_bytes")] + \
+        [(name, ctypes.c_uint32) for name in ("ans_steps", "ans_prob_bits")]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -198,19 +200,20 @@ def encode_bound(n: int, params: Params | None = None) -> int:
 
 def encode(bits, chunk_bytes: int = 16, lanes: int = 64, max_code_len: int = 24, lut_bits: int = 11,
            codebook: Codebook | None = None, threads: int = 0, shape=None, layout: int = LAYOUT_FLAT,
-           panel_k: int = 0) -> np.ndarray:
+           panel_k: int = 0, ans_steps: int = 0) -> np.ndarray:
     """Encode bf16 bit patterns (any shape, row-major) into a DFC1 container
     (numpy uint8 array).  ``layout=LAYOUT_PANEL`` writes the order the fused
     decode + GEMM consumes (2-D input, rows % 32 == 0, cols % 16 == 0);
     ``layout=LAYOUT_PADDED`` keeps codes inside their chunks and drops the
-    chunk offsets."""
+    chunk offsets; ``layout=LAYOUT_ANS`` codes the exponents with interleaved
+    rANS (``ans_steps`` steps of 64 elements per block, 0 = 512)."""
     arr = np.asarray(bits)
     src = _u16(arr)
     if shape is None:
         shape = arr.shape if arr.ndim == 2 else (1, src.size)
     p = default_params(chunk_bytes=chunk_bytes, lanes_per_block=lanes, max_code_len=max_code_len,
                        lut_bits=lut_bits, threads=threads, rows=int(shape[0]), cols=int(shape[1]),
-                       layout=layout, panel_k=panel_k)
+                       layout=layout, panel_k=panel_k, ans_steps=ans_steps)
     if src.size == 0:
         p.rows, p.cols = 0, 0
     cap = encode_bound(src.size, p)

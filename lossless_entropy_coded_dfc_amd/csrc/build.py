@@ -46,15 +46,18 @@ def build(verbose: bool = False, out: str = OUT) -> str:
     objdir = os.path.join(PKG, "_build")
     os.makedirs(objdir, exist_ok=True)
     inc = ["-I", INCLUDE, "-I", HERE]
-    host_obj = os.path.join(objdir, "dfc_host.o")
-    _run(["g++", *CXX_FLAGS, *inc, "-c", os.path.join(HERE, "dfc_host.cpp"), "-o", host_obj], verbose)
+    host_objs = []
+    for name in ("dfc_host", "dfc_ans_host"):
+        obj = os.path.join(objdir, name + ".o")
+        _run(["g++", *CXX_FLAGS, *inc, "-c", os.path.join(HERE, name + ".cpp"), "-o", obj], verbose)
+        host_objs.append(obj)
     dev_objs = []
-    for name in ("dfc_decode", "dfc_gemm", "dfc_encode_gpu"):
+    for name in ("dfc_decode", "dfc_ans", "dfc_gemm", "dfc_encode_gpu"):
         obj = os.path.join(objdir, name + ".o")
         _run([hipcc, *HIP_FLAGS, *inc, "-c", os.path.join(HERE, name + ".hip"), "-o", obj], verbose)
         dev_objs.append(obj)
     tmp = out + ".tmp"
-    _run([hipcc, "-shared", f"--offload-arch={ARCH}", "-fPIC", "-o", tmp, host_obj, *dev_objs, "-pthread"], verbose)
+    _run([hipcc, "-shared", f"--offload-arch={ARCH}", "-fPIC", "-o", tmp, *host_objs, *dev_objs, "-pthread"], verbose)
     os.replace(tmp, out)
     return out
 

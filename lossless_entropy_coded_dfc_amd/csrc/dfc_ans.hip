@@ -1,0 +1,213 @@
+// dfc_ans.hip - gfx950 decoder for containers in the interleaved rANS layout
+// (DFC_LAYOUT_ANS; the code and the container are stated in dfc.h).
+//
+// The exponents are coded with rANS, an arithmetic-family code (DFloat11
+// blog, section 02; the VcLLM page's introduction describes an ANS decoder);
+// sign and mantissa are one raw byte per value as in the Huffman layouts.
+//
+// One wavefront decodes one block: lane l holds the state of the block's
+// lane l and decodes elements i * 64 + l, one step i at a time.  Per step:
+// the slot table (in LDS, 16 KB per workgroup) gives symbol, frequency and
+// cumulative count; the lanes whose state drops below 2^16 take the block's
+// next 16-bit words in lane order (ballot, then each lane's rank among them),
+// read from a per-wavefront ring of 256 words in LDS that always holds the
+// next 128 words, refilled 64 words at a time from a register loaded one
+// refill ahead (so a word load is waited for only at a refill).  The
+// step's 64 exponent bytes go to an LDS stage; every 8 steps the stage holds
+// 512 consecutive exponents, which the lanes merge with the raw bytes (loaded
+// one round ahead) into bf16 octets and write with 16-byte stores (1 KB
+// contiguous per instruction).  At the end every lane's state must be back
+// at 2^16 and the block's words consumed exactly, else the status word is
+// set.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#include "dfc.h"
+#include "dfc_ans_launch.h"
+#include "dfc_decode_core.h"
+#include "dfc_format.h"
+
+namespace {
+
+constexpr uint32_t kAnsWaves = 4;  // wavefronts per workgroup, one block each
+
+struct AnsItem {
+    const uint16_t *words;     // all blocks' word streams
+    const uint32_t *offsets;   // first word of every block, n_blocks + 1
+    const uint32_t *states;    // 64 initial states per block
+    const uint8_t *raw;        // raw bytes, padded to 16
+    const uint32_t *table;     // slot table, 4096 entries
+    uint16_t *dst;
+    uint32_t words_bytes, states_bytes, raw_bytes, dst_bytes;
+    uint32_t n, n_blocks, steps;
+    uint32_t wg_begin;  // first workgroup of this item in the grid
+};
+
+struct AnsBatch {
+    AnsItem item[DFC_MAX_BATCH];
+    uint32_t count;
+    uint32_t *status;
+};
+
+__device__ __forceinline__ uint32_t load_word(__amdgpu_buffer_rsrc_t words, uint32_t index) {
+    return __builtin_amdgcn_raw_buffer_load_b16(words, 2u * index, 0, 0);
+}
+
+__global__ __launch_bounds__(kAnsWaves * kWave) void dfc_ans_kernel(const AnsBatch args) {
+    __shared__ __align__(16) uint32_t table[dfc::kAnsSlots];
+    __shared__ __align__(16) uint8_t stage_all[kAnsWaves][512];
+    __shared__ __align__(16) uint16_t ring_all[kAnsWaves][256];
+    const uint32_t wg = blockIdx.x;
+    uint32_t it = 0;
+    for (uint32_t k = 1; k < args.count; ++k)
+        if (wg >= args.item[k].wg_begin) it = k;
+    const AnsItem a = args.item[it];
+
+    for (uint32_t o = threadIdx.x; o < dfc::kAnsSlots / 4; o += blockDim.x)
+        reinterpret_cast<uint4 *>(table)[o] = reinterpret_cast<const uint4 *>(a.table)[o];
+    __syncthreads();
+
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const uint32_t lane = threadIdx.x % kWave;
+    const uint32_t b = (wg - a.wg_begin) * kAnsWaves + wave;
+    if (b >= a.n_blocks) return;
+    uint8_t *stage = stage_all[wave];
+    uint16_t *ring = ring_all[wave];
+
+    const __amdgpu_buffer_rsrc_t words =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(a.words), 0, int(a.words_bytes), kBufferConfig);
+    const __amdgpu_buffer_rsrc_t states =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t *>(a.states), 0, int(a.states_bytes), kBufferConfig);
+    const __amdgpu_buffer_rsrc_t raw =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(a.raw), 0, int(a.raw_bytes), kBufferConfig);
+    const __amdgpu_buffer_rsrc_t dst = __builtin_amdgcn_make_buffer_rsrc(a.dst, 0, int(a.dst_bytes), kBufferConfig);
+    const const_u32_ptr offsets = (const_u32_ptr)(a.offsets);
+
+    const uint32_t per = kWave * a.steps;
+    const uint32_t e0 = b * per;                 // first element of the block (a multiple of 8)
+    const uint32_t cnt = min(per, a.n - e0);     // elements in the block
+    const uint32_t nsteps = (cnt + kWave - 1) / kWave;
+    const uint32_t w_begin = offsets[b], w_end = offsets[b + 1];
+
+    uint32_t x = __builtin_amdgcn_raw_buffer_load_b32(states, 4u * (b * kWave + lane), 0, 0);
+    // ring: words [base, base + 128) at ring[(word) mod 256]; pend holds
+    // words [base + 128, base + 192) (lane l: base + 128 + l)
+    uint32_t base = w_begin, off = 0;
+    ring[(base + lane) & 255u] = uint16_t(load_word(words, base + lane));
+    ring[(base + 64u + lane) & 255u] = uint16_t(load_word(words, base + 64u + lane));
+    uint32_t pend = load_word(words, base + 128u + lane);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // raw bytes of the first round's octet (512 elements per round)
+    u32x2 R = __builtin_amdgcn_raw_buffer_load_b64(raw, e0 + 8u * lane, 0, 0);
+
+    for (uint32_t i = 0; i < nsteps; ++i) {
+        const bool live = i * kWave + lane < cnt;
+        const uint32_t e = table[x & (dfc::kAnsSlots - 1u)];
+        const uint32_t f = ((e >> 8) & 0xFFFu) + 1u;
+        const uint32_t xn = f * (x >> dfc::kAnsProbBits) + (x & (dfc::kAnsSlots - 1u)) - (e >> 20);
+        const bool need = live && xn < uint32_t(dfc::kAnsLow);
+        const uint64_t m = __builtin_amdgcn_ballot_w64(need);
+        const uint32_t rank = __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u));
+        const uint32_t w = ring[(base + off + rank) & 255u];  // off + rank < 128
+        x = need ? (xn << 16) | w : (live ? xn : x);
+        stage[(i & 7u) * kWave + lane] = uint8_t(e);
+        off += uint32_t(__builtin_popcountll(m));
+        if (off >= 64u) {
+            // words [base, base + 64) are consumed: their slots take pend
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            ring[(base + 128u + lane) & 255u] = uint16_t(pend);
+            base += 64u;
+            off -= 64u;
+            pend = load_word(words, base + 128u + lane);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
+        if ((i & 7u) == 7u || i + 1u == nsteps) {
+            const uint32_t r = i >> 3;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            const u32x2 E = *reinterpret_cast<const u32x2 *>(stage + 8u * lane);
+            const u32x4 o = assemble8(E, R);
+            const uint32_t first = 512u * r + 8u * lane;  // block-relative element of this octet
+            const uint32_t h = e0 / 8u + 64u * r + lane;   // octet index in the output
+            __builtin_amdgcn_raw_buffer_store_b128(o, dst, first + 8u <= cnt ? 16u * h : kNowhere, 0, 0);
+            if (cnt - 512u * r < 512u && (cnt & 7u)) {
+                // the block's last round ends inside an octet: its values one by one
+                const uint32_t v[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const bool in = first + 8u > cnt && first + uint32_t(j) < cnt;
+                    __builtin_amdgcn_raw_buffer_store_b16(uint16_t(v[j >> 1] >> (16 * (j & 1))), dst,
+                                                          in ? 2u * (8u * h + uint32_t(j)) : kNowhere, 0, 0);
+                }
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            R = __builtin_amdgcn_raw_buffer_load_b64(raw, e0 + 512u * (r + 1u) + 8u * lane, 0, 0);
+        }
+    }
+    // every lane back at the encoder's starting state, every word consumed
+    const bool bad = (base + off != w_end) | (__builtin_amdgcn_ballot_w64(x != uint32_t(dfc::kAnsLow)) != 0);
+    if (bad && lane == 0 && args.status) atomicOr(args.status, 1u);
+}
+
+}  // namespace
+
+namespace dfc {
+
+dfc_status ans_check_item(const dfc_batch_item &it) {
+    const dfc_info &in = *it.info;
+    if (in.lanes_per_block != kAnsLanes || in.ans_prob_bits != kAnsProbBits) return DFC_EUNSUPPORTED;
+    if (in.ans_steps < 8 || in.ans_steps > 65536 || in.ans_steps % 8) return DFC_EINVAL;
+    const uint64_t limit = kNowhere - 64u * 1024u;
+    if (2 * in.n > limit || in.words_bytes > limit || in.blockout_bytes > limit || in.raw_bytes > limit)
+        return DFC_EUNSUPPORTED;
+    return DFC_OK;
+}
+
+dfc_status ans_launch(const dfc_batch_item *items, const uint32_t *idx, uint32_t count, uint32_t *status,
+                      hipStream_t stream) {
+    AnsBatch args;
+    std::memset(&args, 0, sizeof(args));
+    uint32_t wg = 0, m = 0;
+    for (uint32_t k = 0; k < count; ++k) {
+        const dfc_batch_item &bi = items[idx[k]];
+        const dfc_info &in = *bi.info;
+        if (in.n_blocks == 0) continue;
+        const uint8_t *base = static_cast<const uint8_t *>(bi.blob_dev);
+        AnsItem &a = args.item[m++];
+        a.words = reinterpret_cast<const uint16_t *>(base + in.off_words);
+        a.offsets = reinterpret_cast<const uint32_t *>(base + in.off_offsets);
+        a.states = reinterpret_cast<const uint32_t *>(base + in.off_blockout);
+        a.raw = base + in.off_raw;
+        a.table = reinterpret_cast<const uint32_t *>(base + in.off_tables + 512);
+        a.dst = bi.dst_dev;
+        a.words_bytes = uint32_t(in.words_bytes);
+        a.states_bytes = uint32_t(in.blockout_bytes);
+        a.raw_bytes = uint32_t(in.raw_bytes);
+        a.dst_bytes = uint32_t(2 * in.n);
+        a.n = uint32_t(in.n);
+        a.n_blocks = uint32_t(in.n_blocks);
+        a.steps = in.ans_steps;
+        a.wg_begin = wg;
+        wg += uint32_t(ceil_div(in.n_blocks, kAnsWaves));
+    }
+    if (!m) return DFC_OK;
+    args.count = m;
+    args.status = status;
+    dfc_ans_kernel<<<dim3(wg), dim3(kAnsWaves * kWave), 0, stream>>>(args);
+    return hipGetLastError() == hipSuccess ? DFC_OK : DFC_EHIP;
+}
+
+}  // namespace dfc

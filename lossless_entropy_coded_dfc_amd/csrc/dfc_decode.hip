@@ -29,6 +29,7 @@
 #include <vector>
 
 #include "dfc.h"
+#include "dfc_ans_launch.h"
 #include "dfc_decode_core.h"
 #include "dfc_format.h"
 
@@ -377,6 +378,7 @@ dfc_status check_item(const dfc_batch_item &it) {
     if (!it.blob_dev || !it.dst_dev) return DFC_EINVAL;
     if ((reinterpret_cast<uintptr_t>(it.blob_dev) & 255u) || (reinterpret_cast<uintptr_t>(it.dst_dev) & 15u))
         return DFC_EINVAL;
+    if (in.layout == DFC_LAYOUT_ANS) return dfc::ans_check_item(it);
     if (in.layout != DFC_LAYOUT_FLAT && in.layout != DFC_LAYOUT_PADDED) return DFC_EUNSUPPORTED;
     if (in.lanes_per_block != 64) return DFC_EUNSUPPORTED;
     const uint32_t C = in.chunk_bytes;
@@ -411,6 +413,15 @@ dfc_status dfc_decode_batch(const dfc_batch_item *items, uint32_t count, uint32_
     }
     hipStream_t st = static_cast<hipStream_t>(stream);
     static const int sizes[4] = {4, 8, 16, 32};
+    {
+        uint32_t idx[DFC_MAX_BATCH], m = 0;
+        for (uint32_t k = 0; k < count; ++k)
+            if (items[k].info->n && items[k].info->layout == DFC_LAYOUT_ANS) idx[m++] = k;
+        if (m) {
+            dfc_status s = dfc::ans_launch(items, idx, m, status_dev, st);
+            if (s != DFC_OK) return s;
+        }
+    }
     // one launch per (chunk size, layout) present in the batch
     for (int pad = 0; pad < 2; ++pad) {
         const uint32_t layout = pad ? DFC_LAYOUT_PADDED : DFC_LAYOUT_FLAT;

@@ -78,6 +78,28 @@ inline SectionSizes section_sizes(uint64_t n, uint64_t n_chunks, uint64_t n_bloc
     return s;
 }
 
+// Interleaved rANS layout: 2^12 probability slots, states in [2^16, 2^32),
+// 16-bit words, 64 lanes per block.  Sections: tables = f (u16[256]) + the
+// slot table (u32[4096]: rotated exponent | (f - 1) << 8 | cum << 20);
+// words = the streams (u16, whole 16-byte units plus one guard unit);
+// offsets = the first word of every block (u32, n_blocks + 1); blockout =
+// the 64 initial states of every block (u32); raw as in the other layouts.
+constexpr uint32_t kAnsProbBits = 12;
+constexpr uint32_t kAnsSlots = 1u << kAnsProbBits;
+constexpr uint64_t kAnsLow = 1ull << 16;  // states live in [kAnsLow, 2^32)
+constexpr uint32_t kAnsLanes = 64;
+constexpr uint64_t kAnsTablesBytes = 2 * 256 + 4ull * kAnsSlots;
+inline SectionSizes ans_section_sizes(uint64_t n, uint64_t n_words, uint64_t n_blocks) {
+    SectionSizes s;
+    s.bytes[kTables] = kAnsTablesBytes;
+    s.bytes[kWords] = 2 * (ceil_div(n_words, 8) * 8 + 8);
+    s.bytes[kOffsets] = 4 * (n_blocks + 1);
+    s.bytes[kBlockout] = 4ull * kAnsLanes * n_blocks;
+    s.bytes[kRaw] = 16 * ceil_div(n, 16);
+    s.bytes[kPanels] = 0;
+    return s;
+}
+
 // Panel layout geometry: items of 32 rows x panel_k columns, row panels
 // first, then column slices.
 constexpr uint32_t kPanelRows = 32;

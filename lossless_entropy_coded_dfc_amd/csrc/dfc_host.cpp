@@ -19,44 +19,6 @@ using namespace dfc;
 
 namespace {
 
-unsigned pick_threads(uint32_t requested, uint64_t work) {
-    unsigned hw = std::thread::hardware_concurrency();
-    if (hw == 0) hw = 1;
-    uint64_t t = requested ? requested : std::min(hw, 16u);
-    uint64_t by_work = std::max<uint64_t>(1, work >> 20);  // >= ~1M elements per thread
-    return unsigned(std::max<uint64_t>(1, std::min(t, by_work)));
-}
-
-template <class F>
-void parallel_for(unsigned nt, F &&f) {
-    if (nt <= 1) {
-        f(0u);
-        return;
-    }
-    std::vector<std::thread> pool;
-    pool.reserve(nt - 1);
-    for (unsigned t = 1; t < nt; ++t) pool.emplace_back([&f, t] { f(t); });
-    f(0u);
-    for (auto &th : pool) th.join();
-}
-
-inline uint32_t exponent_of(uint16_t b) { return (b >> 7) & 0xFFu; }
-inline uint8_t raw_of(uint16_t b) { return uint8_t(((b >> 8) & 0x80u) | (b & 0x7Fu)); }
-
-void histogram_mt(const uint16_t *src, uint64_t n, uint64_t hist[256], unsigned nt) {
-    std::vector<uint64_t> local(size_t(nt) * 256, 0);
-    parallel_for(nt, [&](unsigned t) {
-        uint64_t j0 = n * t / nt, j1 = n * (t + 1) / nt;
-        uint64_t *h = &local[size_t(t) * 256];
-        for (uint64_t j = j0; j < j1; ++j) h[exponent_of(src[j])]++;
-    });
-    for (int s = 0; s < 256; ++s) {
-        uint64_t v = 0;
-        for (unsigned t = 0; t < nt; ++t) v += local[size_t(t) * 256 + s];
-        hist[s] = v;
-    }
-}
-
 // Canonical per-length tables (index = length 1..24).
 struct Canon {
     uint32_t count[kMaxLen + 1], first[kMaxLen + 1], limit[kMaxLen + 1], base[kMaxLen + 1];
@@ -213,8 +175,15 @@ bool params_ok(const dfc_params &p) {
     if (T != 64 && T != 128 && T != 256) return false;
     if (p.max_code_len < 1 || p.max_code_len > kMaxLen) return false;
     if (p.lut_bits < 8 || p.lut_bits > 12) return false;
-    if (p.layout != DFC_LAYOUT_FLAT && p.layout != DFC_LAYOUT_PANEL && p.layout != DFC_LAYOUT_PADDED) return false;
-    if (p.reserved) return false;
+    if (p.layout != DFC_LAYOUT_FLAT && p.layout != DFC_LAYOUT_PANEL && p.layout != DFC_LAYOUT_PADDED &&
+        p.layout != DFC_LAYOUT_ANS)
+        return false;
+    if (p.layout == DFC_LAYOUT_ANS) {
+        if (T != kAnsLanes) return false;
+        if (p.ans_steps && (p.ans_steps < 8 || p.ans_steps > 65536 || p.ans_steps % 8)) return false;
+    } else if (p.ans_steps) {
+        return false;
+    }
     return true;
 }
 
@@ -521,6 +490,9 @@ dfc_status dfc_encode_bound(uint64_t n, const dfc_params *pin, uint64_t *max_byt
         PanelGeom g;
         if (!panel_geom(p.rows, p.cols, p.panel_k ? p.panel_k : uint32_t(DFC_PANEL_K_DEFAULT), g)) return DFC_EINVAL;
         s = section_sizes(n, L.n_chunks + g.n_items, L.n_blocks + g.n_items, p.chunk_bytes, p.lut_bits, g.n_items);
+    } else if (p.layout == DFC_LAYOUT_ANS) {
+        *max_bytes = ans_encode_bound(n, p.ans_steps);
+        return DFC_OK;
     } else if (p.layout == DFC_LAYOUT_PADDED) {
         // every chunk but the last holds one code, or more than 8C - limit bits
         const uint64_t cb = 8ull * p.chunk_bytes, lim = p.max_code_len;
@@ -551,6 +523,10 @@ dfc_status dfc_encode(const uint16_t *src, uint64_t n, const dfc_params *pin, co
     }
     if (rows * cols != n) return DFC_EINVAL;
     uint8_t *dst = static_cast<uint8_t *>(dst_v);
+    if (p.layout == DFC_LAYOUT_ANS) {
+        if (cb_in) return DFC_EINVAL;  // frequencies always come from src's own histogram
+        return encode_ans(src, n, p, rows, cols, dst, cap, written);
+    }
     const unsigned nt = pick_threads(p.threads, n);
 
     uint64_t hist[256];
@@ -681,8 +657,14 @@ dfc_status dfc_blob_info(const void *blob_v, uint64_t bytes, dfc_info *out) {
     in.rows = load_le<uint64_t>(b + hdr::rows);
     in.cols = load_le<uint64_t>(b + hdr::cols);
     in.blob_bytes = load_le<uint64_t>(b + hdr::blob_bytes);
-    if (in.layout != DFC_LAYOUT_FLAT && in.layout != DFC_LAYOUT_PANEL && in.layout != DFC_LAYOUT_PADDED)
+    if (in.layout != DFC_LAYOUT_FLAT && in.layout != DFC_LAYOUT_PANEL && in.layout != DFC_LAYOUT_PADDED &&
+        in.layout != DFC_LAYOUT_ANS)
         return DFC_EUNSUPPORTED;
+    if (in.layout == DFC_LAYOUT_ANS) {
+        dfc_status st = ans_blob_info(b, bytes, in);
+        if (st == DFC_OK) *out = in;
+        return st;
+    }
     const bool panel = in.layout == DFC_LAYOUT_PANEL;
     const bool padded = in.layout == DFC_LAYOUT_PADDED;
     dfc_params p;

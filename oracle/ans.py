@@ -337,7 +337,9 @@ def decode_ans_blob(blob: bytes) -> np.ndarray:
 
 
 def coded_bytes(enc) -> int:
-    """Header, frequencies, stream, block offsets, initial states, raw bytes
-    (the decode table is derived from the frequencies and not counted)."""
-    return (bl.HEADER_BYTES + 512 + 2 * int(enc["words"].size) + 4 * (enc["n_blocks"] + 1) +
-            4 * enc["lanes"] * enc["n_blocks"] + int(enc["n"]))
+    """Header, frequencies and the words, offsets, states and raw sections
+    (the slot table is derived from the frequencies and not counted; neither
+    is alignment padding between sections)."""
+    nw = int(enc["words"].size)
+    return (bl.HEADER_BYTES + 512 + 2 * (-(-nw // 8) * 8 + 8) + 4 * (enc["n_blocks"] + 1) +
+            4 * enc["lanes"] * enc["n_blocks"] + 16 * (-(-int(enc["n"]) // 16)))

@@ -305,7 +305,8 @@ def test_padded_validation_rejects_corruption():
     info = dfc.blob_info(b)
     flat = dfc.encode(x)
     cases = {
-        "layout=3": (corrupt(b, 56, struct.pack("<I", 3)), dfc.EUNSUPPORTED),
+        "layout=4": (corrupt(b, 56, struct.pack("<I", 4)), dfc.EUNSUPPORTED),
+        "layout=ans": (corrupt(b, 56, struct.pack("<I", 3)), dfc.ECORRUPT),
         # a flat header on a padded body: the section table no longer fits
         "layout=flat": (corrupt(b, 56, struct.pack("<I", 0)), dfc.ECORRUPT),
         "padded header on flat body": (corrupt(flat, 56, struct.pack("<I", 2)), dfc.ECORRUPT),
@@ -317,3 +318,93 @@ def test_padded_validation_rejects_corruption():
         with pytest.raises(dfc.DfcError) as ei:
             dfc.blob_info(blob)
         assert ei.value.status == want, name
+
+
+# --------------------------------------------------------------- ANS layout
+
+from oracle import ans as oans  # noqa: E402
+
+
+def oracle_ans_blob(x, steps):
+    shape = x.shape if x.ndim == 2 else (1, x.size)
+    if x.size == 0:
+        shape = (1, 0)
+    return oans.write_ans_blob(oans.encode_ans(x, steps), *shape)
+
+
+@pytest.mark.parametrize("steps", [8, 64, 512])
+@pytest.mark.parametrize("kind", ["outliers", "uniform", "ladder", "t", "const"])
+def test_ans_encoder_matches_oracle_bytes(steps, kind):
+    shape = (41, 997)
+    x = {"outliers": lambda: synth.gaussian_with_outliers(shape, 0.02, (120, steps)),
+         "uniform": lambda: synth.uniform_bits(shape, (121, steps)),
+         "ladder": lambda: synth.exponent_ladder(shape, (122, steps)),
+         "t": lambda: synth.student_t(shape, 3.0, 0.02, (123, steps)),
+         "const": lambda: np.full(shape, 0x3C00, dtype=np.uint16)}[kind]()
+    b = dfc.encode(x, layout=dfc.LAYOUT_ANS, ans_steps=steps)
+    assert bytes(b) == oracle_ans_blob(x, steps)
+    info = dfc.blob_info(b)
+    assert info.layout == dfc.LAYOUT_ANS and info.ans_steps == steps and info.ans_prob_bits == 12
+    assert info.coded_bytes == oans.coded_bytes(oans.encode_ans(x, steps))
+
+
+def test_ans_threads_edge_sizes_and_bound():
+    x = synth.gaussian_with_outliers((1500, 1000), 0.02, (124,))
+    for threads in (1, 3, 16):
+        b = dfc.encode(x, layout=dfc.LAYOUT_ANS, ans_steps=64, threads=threads)
+        assert bytes(b) == oracle_ans_blob(x, 64), threads
+    for n in (0, 1, 2, 63, 64, 65, 511, 512, 513, 5000):
+        y = synth.uniform_bits((n,), (125, n))
+        b = dfc.encode(y, layout=dfc.LAYOUT_ANS, ans_steps=8)
+        assert bytes(b) == oracle_ans_blob(y, 8), n
+        dfc.blob_info(b)
+        assert len(b) <= dfc.encode_bound(n, dfc.default_params(layout=dfc.LAYOUT_ANS, ans_steps=8))
+    assert dfc.blob_info(dfc.encode(x, layout=dfc.LAYOUT_ANS)).ans_steps == 512   # default
+
+
+def test_ans_bad_params_rejected():
+    x = synth.gaussian((4, 64), 0.02, (126,))
+    for kw in ({"ans_steps": 12}, {"ans_steps": 4}, {"ans_steps": 65544}, {"lanes": 128}):
+        with pytest.raises(dfc.DfcError) as ei:
+            dfc.encode(x, layout=dfc.LAYOUT_ANS, **kw)
+        assert ei.value.status == dfc.EINVAL, kw
+    with pytest.raises(dfc.DfcError):
+        dfc.encode(x, ans_steps=64)   # only the ANS layout takes steps
+    book = dfc.build_codebook(cb.histogram(fields.split(x)[0]), 24)
+    with pytest.raises(dfc.DfcError):
+        dfc.encode(x, layout=dfc.LAYOUT_ANS, codebook=book)
+
+
+def test_ans_size_near_entropy_bound():
+    y = synth.gaussian((1024, 4096), 0.02, (0,))
+    bound = bl.entropy_bound_bytes(cb.histogram(fields.split(y)[0]))
+    pad = dfc.blob_info(dfc.encode(y, layout=dfc.LAYOUT_PADDED)).coded_bytes
+    for steps, lim in ((256, 1.012), (512, 1.006), (1024, 1.004)):
+        c = dfc.blob_info(dfc.encode(y, layout=dfc.LAYOUT_ANS, ans_steps=steps)).coded_bytes
+        assert c / bound < lim, steps
+        if steps >= 512:
+            assert c < pad, steps
+
+
+def test_ans_validation_rejects_corruption():
+    x = synth.gaussian((128, 1024), 0.02, (127,))
+    b = dfc.encode(x, layout=dfc.LAYOUT_ANS, ans_steps=64)
+    info = dfc.blob_info(b)
+    t = info.off_tables
+    cases = {
+        "steps": corrupt(b, 80, struct.pack("<I", 60)),
+        "chunk_bytes": corrupt(b, 40, struct.pack("<I", 16)),
+        "prob_bits": corrupt(b, 52, struct.pack("<I", 11)),
+        "lengths area": corrupt(b, 300, b"\x01"),
+        "freq sum": corrupt(b, t + 2 * int(np.argmax(np.frombuffer(bytes(b[t: t + 512]), dtype="<u2"))),
+                            struct.pack("<H", 1)),
+        "slot table": corrupt(b, t + 512 + 40, b"\x07"),
+        "offsets end": corrupt(b, info.off_offsets + 4 * info.n_blocks, struct.pack("<I", 1)),
+        "offsets order": corrupt(b, info.off_offsets + 4, struct.pack("<I", 0xFFFFFF)),
+        "state below 2^16": corrupt(b, info.off_blockout + 8, struct.pack("<I", 5)),
+        "total_bits": corrupt(b, 16, struct.pack("<Q", info.total_bits + 8)),
+    }
+    for name, blob in cases.items():
+        with pytest.raises(dfc.DfcError) as ei:
+            dfc.blob_info(blob)
+        assert ei.value.status == dfc.ECORRUPT, name
