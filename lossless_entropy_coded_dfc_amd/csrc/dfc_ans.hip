@@ -10,9 +10,12 @@
 // the slot table (in LDS, 16 KB per workgroup) gives symbol, frequency and
 // cumulative count; the lanes whose state drops below 2^16 take the block's
 // next 16-bit words in lane order (ballot, then each lane's rank among them),
-// read from a per-wavefront ring of 256 words in LDS that always holds the
-// next 128 words, refilled 64 words at a time from a register loaded one
-// refill ahead (so a word load is waited for only at a refill).  The
+// read from a per-wavefront ring of 1024 words in LDS.  A round of eight
+// steps consumes at most 512 words, so the ring is refilled only between
+// rounds, 512 words at a time from registers loaded one refill ahead: the
+// loop waits for a word load only there, and the eight steps of a round run
+// with no memory waits.  Only a block's last step tests which lanes take
+// part.  The
 // step's 64 exponent bytes go to an LDS stage; every 8 steps the stage holds
 // 512 consecutive exponents, which the lanes merge with the raw bytes (loaded
 // one round ahead) into bf16 octets and write with 16-byte stores (1 KB
@@ -24,6 +27,7 @@
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
+#include <type_traits>
 #include <vector>
 
 #include "dfc.h"
@@ -33,7 +37,9 @@
 
 namespace {
 
-constexpr uint32_t kAnsWaves = 4;  // wavefronts per workgroup, one block each
+constexpr uint32_t kAnsWaves = 8;  // wavefronts per workgroup, one block each
+constexpr uint32_t kRing = 1024;   // words of a wavefront's LDS ring
+constexpr uint32_t kSeg = 512;     // words per ring refill (eight per lane)
 
 struct AnsItem {
     const uint16_t *words;     // all blocks' word streams
@@ -53,14 +59,10 @@ struct AnsBatch {
     uint32_t *status;
 };
 
-__device__ __forceinline__ uint32_t load_word(__amdgpu_buffer_rsrc_t words, uint32_t index) {
-    return __builtin_amdgcn_raw_buffer_load_b16(words, 2u * index, 0, 0);
-}
-
 __global__ __launch_bounds__(kAnsWaves * kWave) void dfc_ans_kernel(const AnsBatch args) {
     __shared__ __align__(16) uint32_t table[dfc::kAnsSlots];
     __shared__ __align__(16) uint8_t stage_all[kAnsWaves][512];
-    __shared__ __align__(16) uint16_t ring_all[kAnsWaves][256];
+    __shared__ __align__(16) uint16_t ring_all[kAnsWaves][kRing];
     const uint32_t wg = blockIdx.x;
     uint32_t it = 0;
     for (uint32_t k = 1; k < args.count; ++k)
@@ -94,68 +96,101 @@ __global__ __launch_bounds__(kAnsWaves * kWave) void dfc_ans_kernel(const AnsBat
     const uint32_t w_begin = offsets[b], w_end = offsets[b + 1];
 
     uint32_t x = __builtin_amdgcn_raw_buffer_load_b32(states, 4u * (b * kWave + lane), 0, 0);
-    // ring: words [base, base + 128) at ring[(word) mod 256]; pend holds
-    // words [base + 128, base + 192) (lane l: base + 128 + l)
-    uint32_t base = w_begin, off = 0;
-    ring[(base + lane) & 255u] = uint16_t(load_word(words, base + lane));
-    ring[(base + 64u + lane) & 255u] = uint16_t(load_word(words, base + 64u + lane));
-    uint32_t pend = load_word(words, base + 128u + lane);
+    // ring: words [base, base + kRing) at ring[word mod kRing], base a
+    // multiple of 8; pend: words [base + kRing, base + kRing + kSeg), eight
+    // per lane
+    uint32_t base = w_begin & ~7u, off = w_begin & 7u;
+#pragma unroll
+    for (uint32_t q = 0; q < kRing; q += kSeg)
+        *reinterpret_cast<u32x4 *>(ring + ((base + q + 8u * lane) & (kRing - 1u))) =
+            __builtin_amdgcn_raw_buffer_load_b128(words, 2u * (base + q) + 16u * lane, 0, 0);
+    u32x4 pend = __builtin_amdgcn_raw_buffer_load_b128(words, 2u * (base + kRing) + 16u * lane, 0, 0);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     // raw bytes of the first round's octet (512 elements per round)
     u32x2 R = __builtin_amdgcn_raw_buffer_load_b64(raw, e0 + 8u * lane, 0, 0);
 
-    for (uint32_t i = 0; i < nsteps; ++i) {
-        const bool live = i * kWave + lane < cnt;
+    // One step: every lane decodes its element of step i.  Only the block's
+    // last step can be partial, so only it tests which lanes take part.
+    auto step = [&](uint32_t i, auto tail) {
+        constexpr bool kTail = decltype(tail)::value;
+        const bool live = !kTail || i * kWave + lane < cnt;
         const uint32_t e = table[x & (dfc::kAnsSlots - 1u)];
         const uint32_t f = ((e >> 8) & 0xFFFu) + 1u;
         const uint32_t xn = f * (x >> dfc::kAnsProbBits) + (x & (dfc::kAnsSlots - 1u)) - (e >> 20);
         const bool need = live && xn < uint32_t(dfc::kAnsLow);
         const uint64_t m = __builtin_amdgcn_ballot_w64(need);
         const uint32_t rank = __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u));
-        const uint32_t w = ring[(base + off + rank) & 255u];  // off + rank < 128
-        x = need ? (xn << 16) | w : (live ? xn : x);
+        const uint32_t w = ring[(base + off + rank) & (kRing - 1u)];  // off + rank < kRing
+        if constexpr (kTail)
+            x = need ? (xn << 16) | w : (live ? xn : x);
+        else
+            x = need ? (xn << 16) | w : xn;
         stage[(i & 7u) * kWave + lane] = uint8_t(e);
         off += uint32_t(__builtin_popcountll(m));
-        if (off >= 64u) {
-            // words [base, base + 64) are consumed: their slots take pend
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            ring[(base + 128u + lane) & 255u] = uint16_t(pend);
-            base += 64u;
-            off -= 64u;
-            pend = load_word(words, base + 128u + lane);
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        }
-        if ((i & 7u) == 7u || i + 1u == nsteps) {
-            const uint32_t r = i >> 3;
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            const u32x2 E = *reinterpret_cast<const u32x2 *>(stage + 8u * lane);
-            const u32x4 o = assemble8(E, R);
-            const uint32_t first = 512u * r + 8u * lane;  // block-relative element of this octet
-            const uint32_t h = e0 / 8u + 64u * r + lane;   // octet index in the output
-            __builtin_amdgcn_raw_buffer_store_b128(o, dst, first + 8u <= cnt ? 16u * h : kNowhere, 0, 0);
-            if (cnt - 512u * r < 512u && (cnt & 7u)) {
-                // the block's last round ends inside an octet: its values one by one
-                const uint32_t v[4] = {o.x, o.y, o.z, o.w};
+    };
+    // Round r (steps 8r .. 8r + 7) is staged: merge with its raw bytes, store.
+    auto flush = [&](uint32_t r) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const u32x2 E = *reinterpret_cast<const u32x2 *>(stage + 8u * lane);
+        const u32x4 o = assemble8(E, R);
+        const uint32_t first = 512u * r + 8u * lane;  // block-relative element of this octet
+        const uint32_t h = e0 / 8u + 64u * r + lane;   // octet index in the output
+        __builtin_amdgcn_raw_buffer_store_b128(o, dst, first + 8u <= cnt ? 16u * h : kNowhere, 0, 0);
+        if (cnt - 512u * r < 512u && (cnt & 7u)) {
+            // the block's last round ends inside an octet: its values one by one
+            const uint32_t v[4] = {o.x, o.y, o.z, o.w};
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const bool in = first + 8u > cnt && first + uint32_t(j) < cnt;
-                    __builtin_amdgcn_raw_buffer_store_b16(uint16_t(v[j >> 1] >> (16 * (j & 1))), dst,
-                                                          in ? 2u * (8u * h + uint32_t(j)) : kNowhere, 0, 0);
-                }
+            for (int j = 0; j < 8; ++j) {
+                const bool in = first + 8u > cnt && first + uint32_t(j) < cnt;
+                __builtin_amdgcn_raw_buffer_store_b16(uint16_t(v[j >> 1] >> (16 * (j & 1))), dst,
+                                                      in ? 2u * (8u * h + uint32_t(j)) : kNowhere, 0, 0);
             }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        R = __builtin_amdgcn_raw_buffer_load_b64(raw, e0 + 512u * (r + 1u) + 8u * lane, 0, 0);
+    };
+
+    // Whole rounds: eight steps consume at most 512 words, so the ring (which
+    // holds at least kRing - kSeg words ahead at a round's start) needs
+    // refilling only between rounds, and then by one segment.
+    // The flush comes first: its wait for R (loaded by the previous flush)
+    // then never has to cover this round's refill load, and the refill's
+    // wait for pend (loaded a refill earlier) lets the flush's stores run.
+    const uint32_t rounds = (cnt / kWave) / 8u;
+    wait_for(x);
+    for (uint32_t r = 0; r < rounds; ++r) {
+#pragma unroll
+        for (uint32_t j = 0; j < 8u; ++j) step(8u * r + j, std::false_type{});
+        flush(r);
+        if (off >= kSeg) {
+            // words [base, base + kSeg) are consumed: their slots take pend
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            R = __builtin_amdgcn_raw_buffer_load_b64(raw, e0 + 512u * (r + 1u) + 8u * lane, 0, 0);
+            *reinterpret_cast<u32x4 *>(ring + ((base + kRing + 8u * lane) & (kRing - 1u))) = pend;
+            base += kSeg;
+            off -= kSeg;
+            pend = __builtin_amdgcn_raw_buffer_load_b128(words, 2u * (base + kRing) + 16u * lane, 0, 0);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
+    }
+    // The last, partial round.
+    if (8u * rounds < nsteps) {
+        for (uint32_t i = 8u * rounds; i < nsteps; ++i) {
+            if (i < cnt / kWave)
+                step(i, std::false_type{});
+            else
+                step(i, std::true_type{});
+        }
+        flush(rounds);
     }
     // every lane back at the encoder's starting state, every word consumed
     const bool bad = (base + off != w_end) | (__builtin_amdgcn_ballot_w64(x != uint32_t(dfc::kAnsLow)) != 0);
