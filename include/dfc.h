@@ -77,7 +77,8 @@ typedef enum {
  * if x < 2^16 the next word w enters as x = (x << 16) | w.  A block is 64
  * lanes x S steps: element i * 64 + l of the block belongs to lane l, and at
  * every step the lanes that need a word take the block's next words in lane
- * order.  The container keeps f (u16[256]) and the derived slot table in its
+ * order.  The container keeps f (u16[256]) and the derived slot table (per
+ * slot: rotated exponent | (f - 1) << 8 | (slot - cum) << 20) in its
  * tables section, all blocks' word streams in the words section, the first
  * word of every block (u32, n_blocks + 1) in the offsets section and the 64
  * initial states of every block (u32) in the blockout section; chunk_bytes

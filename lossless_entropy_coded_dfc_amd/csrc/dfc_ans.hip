@@ -62,7 +62,9 @@ struct AnsBatch {
 __global__ __launch_bounds__(kAnsWaves * kWave) void dfc_ans_kernel(const AnsBatch args) {
     __shared__ __align__(16) uint32_t table[dfc::kAnsSlots];
     __shared__ __align__(16) uint8_t stage_all[kAnsWaves][512];
-    __shared__ __align__(16) uint16_t ring_all[kAnsWaves][kRing];
+    // the ring's first 64 words are mirrored after its end, so a word index
+    // (start mod kRing) + rank needs no wrap
+    __shared__ __align__(16) uint16_t ring_all[kAnsWaves][kRing + kWave];
     const uint32_t wg = blockIdx.x;
     uint32_t it = 0;
     for (uint32_t k = 1; k < args.count; ++k)
@@ -100,10 +102,15 @@ __global__ __launch_bounds__(kAnsWaves * kWave) void dfc_ans_kernel(const AnsBat
     // multiple of 8; pend: words [base + kRing, base + kRing + kSeg), eight
     // per lane
     uint32_t base = w_begin & ~7u, off = w_begin & 7u;
+    // eight words at ring slot p (a multiple of 8), and their mirror
+    auto put8 = [&](uint32_t p, const u32x4 &v) {
+        *reinterpret_cast<u32x4 *>(ring + p) = v;
+        if (p < kWave) *reinterpret_cast<u32x4 *>(ring + kRing + p) = v;
+    };
 #pragma unroll
     for (uint32_t q = 0; q < kRing; q += kSeg)
-        *reinterpret_cast<u32x4 *>(ring + ((base + q + 8u * lane) & (kRing - 1u))) =
-            __builtin_amdgcn_raw_buffer_load_b128(words, 2u * (base + q) + 16u * lane, 0, 0);
+        put8((base + q + 8u * lane) & (kRing - 1u),
+             __builtin_amdgcn_raw_buffer_load_b128(words, 2u * (base + q) + 16u * lane, 0, 0));
     u32x4 pend = __builtin_amdgcn_raw_buffer_load_b128(words, 2u * (base + kRing) + 16u * lane, 0, 0);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -118,11 +125,13 @@ __global__ __launch_bounds__(kAnsWaves * kWave) void dfc_ans_kernel(const AnsBat
         const bool live = !kTail || i * kWave + lane < cnt;
         const uint32_t e = table[x & (dfc::kAnsSlots - 1u)];
         const uint32_t f = ((e >> 8) & 0xFFFu) + 1u;
-        const uint32_t xn = f * (x >> dfc::kAnsProbBits) + (x & (dfc::kAnsSlots - 1u)) - (e >> 20);
+        const uint32_t xn = f * (x >> dfc::kAnsProbBits) + (e >> 20);  // e >> 20 = slot - cum
         const bool need = live && xn < uint32_t(dfc::kAnsLow);
         const uint64_t m = __builtin_amdgcn_ballot_w64(need);
-        const uint32_t rank = __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u));
-        const uint32_t w = ring[(base + off + rank) & (kRing - 1u)];  // off + rank < kRing
+        // ring index of this lane's word: the next unread word's slot + rank
+        const uint32_t at = __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo(uint32_t(m), (base + off) & (kRing - 1u)));
+        const uint32_t w = ring[at];
         if constexpr (kTail)
             x = need ? (xn << 16) | w : (live ? xn : x);
         else
@@ -173,7 +182,7 @@ __global__ __launch_bounds__(kAnsWaves * kWave) void dfc_ans_kernel(const AnsBat
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            *reinterpret_cast<u32x4 *>(ring + ((base + kRing + 8u * lane) & (kRing - 1u))) = pend;
+            put8((base + kRing + 8u * lane) & (kRing - 1u), pend);
             base += kSeg;
             off -= kSeg;
             pend = __builtin_amdgcn_raw_buffer_load_b128(words, 2u * (base + kRing) + 16u * lane, 0, 0);

@@ -64,14 +64,14 @@ void cumulative(const uint32_t f[256], uint32_t cum[256]) {
     }
 }
 
-// Slot table: rotated exponent | (f - 1) << 8 | cum << 20 per slot.
+// Slot table: rotated exponent | (f - 1) << 8 | (slot - cum) << 20 per slot.
 void slot_table(const uint32_t f[256], uint8_t *out) {
     uint32_t cum[256];
     cumulative(f, cum);
     for (int s = 0; s < 256; ++s)
         for (uint32_t k = 0; k < f[s]; ++k)
             store_le<uint32_t>(out + 4ull * (cum[s] + k),
-                               rotate_exponent(uint32_t(s)) | ((f[s] - 1u) << 8) | (cum[s] << 20));
+                               rotate_exponent(uint32_t(s)) | ((f[s] - 1u) << 8) | (k << 20));
 }
 
 // One block of cnt elements: initial decoder states and words in decode order.

@@ -80,7 +80,7 @@ inline SectionSizes section_sizes(uint64_t n, uint64_t n_chunks, uint64_t n_bloc
 
 // Interleaved rANS layout: 2^12 probability slots, states in [2^16, 2^32),
 // 16-bit words, 64 lanes per block.  Sections: tables = f (u16[256]) + the
-// slot table (u32[4096]: rotated exponent | (f - 1) << 8 | cum << 20);
+// slot table (u32[4096]: rotated exponent | (f - 1) << 8 | (slot - cum) << 20);
 // words = the streams (u16, whole 16-byte units plus one guard unit);
 // offsets = the first word of every block (u32, n_blocks + 1); blockout =
 // the 64 initial states of every block (u32); raw as in the other layouts.

@@ -33,7 +33,7 @@ plainest standard choice is taken.
   element exists take part.
 * Container (header layout field 3): the code-lengths area is zero; the
   tables section holds f[256] (u16) and the decode table (u32 per slot:
-  rotated exponent | (f - 1) << 8 | cum << 20, where a rotated exponent is
+  rotated exponent | (f - 1) << 8 | (slot - cum) << 20, where a rotated exponent is
   the exponent byte rotated right by one bit, as in the Huffman tables); the
   words section holds every block's stream (u16) back to back, the offsets
   section the first word of every block (u32, n_blocks + 1 entries), the
@@ -95,13 +95,14 @@ def cumulative(f) -> np.ndarray:
 
 
 def decode_table(f) -> np.ndarray:
-    """u32 per slot: rotated exponent | (f - 1) << 8 | cum << 20."""
+    """u32 per slot: rotated exponent | (f - 1) << 8 | (slot - cum) << 20
+    (the decoder's new state is then f * (x // M) + the top 12 bits)."""
     f = np.asarray(f, dtype=np.int64)
     c = cumulative(f)
     t = np.zeros(M, dtype=np.uint32)
     for s in range(256):
-        if f[s]:
-            t[c[s]: c[s] + f[s]] = bl.rotate_exponent(s) | ((int(f[s]) - 1) << 8) | (int(c[s]) << 20)
+        for k in range(int(f[s])):
+            t[c[s] + k] = bl.rotate_exponent(s) | ((int(f[s]) - 1) << 8) | (k << 20)
     return t
 
 

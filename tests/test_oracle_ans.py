@@ -107,7 +107,7 @@ def test_decode_table_matches_definition():
             e = int(t[slot])
             assert e & 0xFF == bl.rotate_exponent(s)
             assert (e >> 8) & 0xFFF == f[s] - 1
-            assert e >> 20 == cum
+            assert e >> 20 == slot - cum
         cum += int(f[s])
     assert cum == ans.M
 
