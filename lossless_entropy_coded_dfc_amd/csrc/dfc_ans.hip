@@ -128,10 +128,10 @@ __global__ __launch_bounds__(kAnsWaves * kWave) void dfc_ans_kernel(const AnsBat
         const uint32_t xn = f * (x >> dfc::kAnsProbBits) + (e >> 20);  // e >> 20 = slot - cum
         const bool need = live && xn < uint32_t(dfc::kAnsLow);
         const uint64_t m = __builtin_amdgcn_ballot_w64(need);
-        // ring index of this lane's word: the next unread word's slot + rank
-        const uint32_t at = __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32),
-                                                      __builtin_amdgcn_mbcnt_lo(uint32_t(m), (base + off) & (kRing - 1u)));
-        const uint32_t w = ring[at];
+        // this lane's word: the next unread word's slot + the lane's rank
+        const uint32_t rank = __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u));
+        const uint16_t *next = ring + ((base + off) & (kRing - 1u));
+        const uint32_t w = next[rank];
         if constexpr (kTail)
             x = need ? (xn << 16) | w : (live ? xn : x);
         else
