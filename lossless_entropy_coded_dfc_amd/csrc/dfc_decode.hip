@@ -116,11 +116,15 @@ __device__ __forceinline__ void store_octet(const Buffers &bf, const BlockRange 
     const bool full = i - br.full0 < br.full1 - br.full0;
     __builtin_amdgcn_raw_buffer_store_b128(o, bf.dst, full ? 16u * h : kNowhere, 0, 0);
     if (!full && i < br.nh) {
+        // values [lo, hi) of the octet are the block's; value q goes out iff
+        // q - lo < hi - lo (unsigned)
+        const uint32_t lo = uint32_t(max(int(br.s_out) - int(8u * h), 0));
+        const uint32_t span = min(br.e_out - 8u * h, 8u) - lo;
         const uint32_t v[4] = {o.x, o.y, o.z, o.w};
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-            const uint32_t j = 8u * h + uint32_t(q);
-            const uint32_t at = (j >= br.s_out && j < br.e_out) ? 2u * j : kNowhere;
+            // (kNowhere + 14 is still past every range)
+            const uint32_t at = (uint32_t(q) - lo < span ? 16u * h : kNowhere) + 2u * uint32_t(q);
             __builtin_amdgcn_raw_buffer_store_b16(uint16_t(v[q >> 1] >> (16 * (q & 1))), bf.dst, at, 0, 0);
         }
     }
