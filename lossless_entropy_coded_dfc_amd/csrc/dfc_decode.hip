@@ -143,10 +143,15 @@ __device__ __forceinline__ void decode_block(const ItemArgs &a, const Buffers &b
     for (uint32_t o = 16u * lane; o + 16u <= ((nz + 15u) & ~15u); o += 16u * kWave)
         *reinterpret_cast<uint4 *>(stage + o) = make_uint4(0, 0, 0, 0);
     const uint32_t chunk = b * kWave + lane;
-    const int64_t bits_left = int64_t(a.total_bits) - int64_t(uint64_t(chunk) * (8ull * C));
+    // Stream bits from this lane's chunk to the end of the stream: only the
+    // last block needs them per lane (a uniform 64-bit test, then 32 bits).
+    const int64_t block_left = int64_t(a.total_bits) - int64_t(uint64_t(b) * (uint64_t(kWave) * 8u * C));
+    const int bits_left = block_left >= int64_t(kWave) * (8 * C + 32)
+                              ? (8 * C + 32)
+                              : max(int(block_left) - int(lane) * (8 * C), -1);
     int start = 0, end;
     if constexpr (Padded)
-        end = int(min(int64_t(8 * C), max(bits_left, int64_t(-1))));
+        end = min(8 * C, bits_left);
     else
         chunk_span<C>(ck, chunk, bits_left, start, end);
 
@@ -213,7 +218,7 @@ __global__ __launch_bounds__(1024, Occupancy<C>::kWavesPerSimd) void dfc_decode_
 
     const Tables t = stage_tables(lds, a.tables, a.tables_bytes, a.lut_bits);
 
-    const uint32_t waves = blockDim.x / kWave;
+    const uint32_t waves = __builtin_amdgcn_readfirstlane(blockDim.x / kWave);
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const uint32_t lane = threadIdx.x % kWave;
     const uint32_t stage_off = a.tables_bytes + wave * args.stage_bytes;
@@ -229,6 +234,8 @@ __global__ __launch_bounds__(1024, Occupancy<C>::kWavesPerSimd) void dfc_decode_
     // Resident on entry, as it is on every later iteration (see wait_for).
     wait_for(cur);
     for (;;) {
+        // the block index is the same in every lane
+        b = __builtin_amdgcn_readfirstlane(b);
         const BlockRange br = block_range(s_out, e_out);
         // raw bytes of this block's first PF octets per lane
         u32x2 R[PF];

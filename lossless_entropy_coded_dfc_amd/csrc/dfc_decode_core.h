@@ -373,14 +373,14 @@ __device__ __forceinline__ Tables stage_tables(uint8_t *lds, const uint8_t *tabl
 
 // Chunk-relative first bit of a chunk's first code and end of its codes,
 // from the offset-array words and the number of stream bits left from the
-// chunk's first bit to the end of its stream (or item).
+// chunk's first bit to the end of its stream (or item), clamped to at most
+// 8C + 32 by the caller.
 template <int C>
-__device__ __forceinline__ void chunk_span(const Chunk<C> &ck, uint32_t chunk, int64_t bits_left, int &start,
-                                           int &end) {
+__device__ __forceinline__ void chunk_span(const Chunk<C> &ck, uint32_t chunk, int bits_left, int &start, int &end) {
     const uint32_t offpair = __builtin_amdgcn_alignbit(ck.o1, ck.o0, (5u * chunk) & 31u);
     start = int(offpair & 31u);
     const int next_off = int((offpair >> 5) & 31u);
-    end = int(min(int64_t(8 * C + next_off), max(bits_left, int64_t(-1))));
+    end = min(8 * C + next_off, max(bits_left, -1));
 }
 
 constexpr uint32_t kLdsBytes = 160u * 1024u;

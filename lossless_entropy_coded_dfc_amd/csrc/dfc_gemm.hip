@@ -109,7 +109,9 @@ __global__ __launch_bounds__(1024) void dfc_gemm_kernel(const GemmArgs g) {
             for (int j = 0; j < PF; ++j)
                 R[j] = __builtin_amdgcn_raw_buffer_load_b64(raw, e0 + base + 512u * j + 8u * lane, 0, 0);
             int start, end;
-            chunk_span<C>(ck, c0 + ci, int64_t(bits) - int64_t(ci) * (8 * C), start, end);
+            chunk_span<C>(ck, c0 + ci,
+                          int(min(max(int64_t(bits) - int64_t(ci) * (8 * C), int64_t(-1)), int64_t(8 * C + 32))),
+                          start, end);
             const uint32_t cnt = start < end ? count_codes<C>(ck, start, end, t) : 0u;
             const uint32_t incl = wave_inclusive_scan(cnt);
             const uint32_t total = __builtin_amdgcn_readlane(incl, kWave - 1);
