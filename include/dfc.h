@@ -188,15 +188,18 @@ dfc_status dfc_blob_info(const void *blob, uint64_t bytes, dfc_info *out);
 /* Decode one container on the GPU (DFloat11 blog, section 03: the two-phase
  * kernel with lookup tables in on-chip memory).  Device, asynchronous on
  * stream.  blob_dev: device copy of the container described by info (256-byte
- * aligned), in the FLAT or the PADDED layout.  dst_dev: n uint16 outputs
+ * aligned), in the FLAT, PADDED or ANS layout.  dst_dev: n uint16 outputs
  * (16-byte aligned), receives the original bf16 bit patterns, row-major.
- * status_dev: NULL, or one device
- * uint32 that the kernel sets to a nonzero value if a block's decoded count
- * disagrees with its block offsets (the caller clears it beforehand and reads
- * it after the stream completes; outputs of such a block are left
- * unwritten).  Synchronous errors: DFC_EINVAL (null/misaligned pointers),
+ * status_dev: NULL, or one device uint32 that the kernel sets to DFC_ECORRUPT
+ * (its two's-complement bit pattern) when a block fails its check: a decoded
+ * code count that disagrees with the block offsets (FLAT, PADDED; the block's
+ * outputs are then left unwritten), or lanes that do not end at the start
+ * state or words not consumed exactly (ANS; the block's outputs are then
+ * undefined).  The caller clears it beforehand and reads it after the stream
+ * completes.  Synchronous errors: DFC_EINVAL (null/misaligned pointers),
  * DFC_ESIZE (n != info->n), DFC_EUNSUPPORTED (lanes_per_block != 64, a
- * PANEL container, streams past 4 GiB), DFC_EHIP (launch failure). */
+ * PANEL container, streams past 4 GiB), DFC_EHIP (launch failure).  The ANS
+ * layout is the interleaved rANS variant (see DFC_LAYOUT_ANS above). */
 dfc_status dfc_decode(const void *blob_dev, const dfc_info *info, uint16_t *dst_dev, uint64_t n,
                       uint32_t *status_dev, void *stream);
 

@@ -203,7 +203,7 @@ __global__ __launch_bounds__(kAnsWaves * kWave) void dfc_ans_kernel(const AnsBat
     }
     // every lane back at the encoder's starting state, every word consumed
     const bool bad = (base + off != w_end) | (__builtin_amdgcn_ballot_w64(x != uint32_t(dfc::kAnsLow)) != 0);
-    if (bad && lane == 0 && args.status) atomicOr(args.status, 1u);
+    if (bad && lane == 0 && args.status) atomicOr(args.status, kStatusCorrupt);
 }
 
 }  // namespace

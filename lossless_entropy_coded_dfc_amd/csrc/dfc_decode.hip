@@ -174,7 +174,7 @@ __device__ __forceinline__ void decode_block(const ItemArgs &a, const Buffers &b
     wait_for(R);
     wait_for(nxt);
     if (bad) {
-        if (lane == 0 && status) atomicOr(status, 1u);
+        if (lane == 0 && status) atomicOr(status, kStatusCorrupt);
         return;
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

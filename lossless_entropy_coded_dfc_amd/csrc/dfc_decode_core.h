@@ -25,6 +25,9 @@ constexpr int kWave = 64;
 constexpr uint32_t kBias = 0x8000u;
 constexpr uint32_t kEscape = dfc::kStepEscape;
 constexpr int kMaxWaves = 16;
+// What a kernel ORs into the caller's status word when a block fails its
+// checks: the bit pattern of DFC_ECORRUPT (every writer ORs the same value).
+constexpr uint32_t kStatusCorrupt = uint32_t(DFC_ECORRUPT);
 
 // Raw buffer resources (base, 32-bit byte range) for every stream of an
 // item: loads past the range return zero and stores past it are dropped, so

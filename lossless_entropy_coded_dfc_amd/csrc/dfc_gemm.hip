@@ -119,7 +119,7 @@ __global__ __launch_bounds__(1024) void dfc_gemm_kernel(const GemmArgs g) {
             if (!bad && cnt) write_codes<C>(ck, start, end, lds, stage_off + lead + (incl - cnt), t);
             wait_for(R);
             if (bad) {
-                if (lane == 0 && g.status) atomicOr(g.status, 1u);
+                if (lane == 0 && g.status) atomicOr(g.status, kStatusCorrupt);
                 ok = false;
                 break;
             }

@@ -119,12 +119,12 @@ def test_status_flag_on_corrupt_stream():
     v = struct.unpack_from("<I", bytes(blob[o: o + 4]))[0]
     bad[o: o + 4] = np.frombuffer(struct.pack("<I", v ^ 0x100), dtype=np.uint8)
     got, status = gpu_decode(bad, dfc.blob_info(bad))
-    assert status != 0
+    assert status == dfc.ECORRUPT
     # a flipped stream bit either trips the check or changes a value
     flip = blob.copy()
     flip[info.off_words + 1000] ^= 0x10
     got, status = gpu_decode(flip, info)
-    assert status != 0 or not np.array_equal(got, x.ravel())
+    assert status == dfc.ECORRUPT or (status == 0 and not np.array_equal(got, x.ravel()))
 
 
 # ---------------------------------------------------------------- full size

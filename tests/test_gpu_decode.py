@@ -160,12 +160,12 @@ def test_status_flags_count_mismatch():
     bad[16:24] = np.frombuffer(struct.pack("<Q", info.total_bits + 3), dtype=np.uint8)
     binfo = dfc.blob_info(bad)
     got, status = gpu_decode(bad, binfo)
-    assert status != 0
+    assert status == dfc.ECORRUPT
     # a flipped stream bit either changes a count or changes a value
     flip = blob.copy()
     flip[info.off_words + 1000] ^= 0x10
     got, status = gpu_decode(flip, info)
-    assert status != 0 or not np.array_equal(got, x.ravel())
+    assert status == dfc.ECORRUPT or (status == 0 and not np.array_equal(got, x.ravel()))
 
 
 def test_invalid_arguments_rejected():

@@ -156,7 +156,7 @@ def test_status_flag_on_corrupt_block_offsets():
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
     dfc.decode_gemm(bad, info, x, y, status)
     torch.cuda.synchronize()
-    assert int(status.item()) != 0
+    assert int(status.item()) == dfc.ECORRUPT
 
 
 @pytest.mark.slow

@@ -147,7 +147,7 @@ def test_status_flag_on_count_mismatch():
     v = struct.unpack_from("<I", bytes(blob[o: o + 4]))[0]
     bad[o: o + 4] = np.frombuffer(struct.pack("<I", v + 1), dtype=np.uint8)
     got, status = gpu_decode(bad, dfc.blob_info(bad))
-    assert status != 0
+    assert status == dfc.ECORRUPT
 
 
 # ---------------------------------------------------------------- full size
