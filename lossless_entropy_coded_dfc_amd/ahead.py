@@ -18,7 +18,8 @@ from . import MAX_BATCH, Info, decode_batch
 class DecodeAhead:
     """Double-buffered decode of ``layers`` (a list, per layer, of
     ``(blob_dev, info, shape)`` with blob_dev a device uint8 tensor holding a
-    flat-layout container and shape the matrix shape)."""
+    container in the flat, padded or rANS layout and shape the matrix
+    shape)."""
 
     def __init__(self, layers, device="cuda"):
         import torch
@@ -67,7 +68,7 @@ class DecodeAhead:
         self.free_recorded[slot] = True
 
     def corrupt_blocks_seen(self) -> bool:
-        """True if any decode so far met a block whose count disagreed with
-        its block offsets (synchronizes the side stream)."""
+        """True if any decode so far met a block that failed its check (the
+        status word then holds DFC_ECORRUPT; synchronizes the side stream)."""
         self.side.synchronize()
         return int(self.status.item()) != 0
