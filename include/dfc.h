@@ -221,15 +221,15 @@ enum { DFC_GEMM_MAX_BATCH = 64 };
  * x_dev: B activation vectors of K bf16 each, x_dev[b K + k] (i.e. X is
  * K x B column-major), 16-byte aligned.  batch: B, 1..DFC_GEMM_MAX_BATCH.
  * y_dev: B output vectors of M fp32, y_dev[b M + m] (Y = W X, M x B
- * column-major), 4-byte aligned; overwritten (the call first zeroes it on the
- * stream).  Products of bf16 pairs are exact and accumulate in fp32; the
- * partial sums of different column slices of W are added with fp32 atomics,
- * so the last bits of Y may differ from run to run.  status_dev: as in
- * dfc_decode (nonzero if a block's decoded count disagrees with its block
- * offsets; Y is then incomplete).  Errors before launch: DFC_EINVAL (null or
+ * column-major), 4-byte aligned; every element is overwritten.  Products of
+ * bf16 pairs are exact and accumulate in fp32; the partial sums of a panel's
+ * column slices are added in a fixed order, so the same inputs give the
+ * same bits on every run.  status_dev: as in dfc_decode (nonzero if a
+ * block's decoded count disagrees with its block offsets; Y is then
+ * unspecified).  Errors before launch: DFC_EINVAL (null or
  * misaligned pointers, batch out of range, bad decode parameters),
  * DFC_EUNSUPPORTED (not a panel-layout container, lanes_per_block != 64,
- * streams past 4 GiB), DFC_EHIP (launch failure). */
+ * streams or Y past 4 GiB), DFC_EHIP (launch failure). */
 dfc_status dfc_decode_gemm(const void *w_blob_dev, const dfc_info *info, const uint16_t *x_dev, uint32_t batch,
                            float *y_dev, uint32_t *status_dev, void *stream);
 

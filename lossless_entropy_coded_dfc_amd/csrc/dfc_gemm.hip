@@ -8,13 +8,15 @@
 // exponents and raw bytes straight into the A operand of one 32x32x16 bf16
 // MFMA per 32 output columns, and the products accumulate in fp32 registers.
 //
-// Work decomposition: one wavefront per item (32 rows x panel_k columns of
-// W), persistent over items; a block of the item (64 chunks) decodes into the
-// wavefront's staging area, whose start is the first sub-tile the block
-// touches.  The exponents of a sub-tile the block only begins are carried in
-// registers into the next block's staging area.  Every item adds its 32 x B
-// partial product into Y with fp32 atomics (items that share rows are
-// different column slices of W).
+// Work decomposition: a workgroup takes whole panels (32 rows of W), a few
+// wavefronts per panel; each wavefront decodes some of the panel's items
+// (32 rows x panel_k columns) and accumulates their products in registers.
+// A block of an item (64 chunks) decodes into the wavefront's staging area,
+// whose start is the first sub-tile the block touches; the exponents of a
+// sub-tile the block only begins are carried in registers into the next
+// block's staging area.  The partial 32 x B products of a panel's wavefronts
+// are then summed in LDS in wavefront order and written to Y with plain
+// stores: no atomics, and the same bits on every run.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -38,9 +40,10 @@ struct GemmArgs {
     const uint8_t *raw;        // raw bytes in panel order
     const uint8_t *tables;     // derived decode tables
     const uint16_t *x;         // B vectors of K bf16: x[b K + k]
-    float *y;                  // B vectors of M fp32: y[b M + m], zeroed before the launch
-    uint32_t words_bytes, offw_bytes, raw_bytes, x_bytes;
-    uint32_t n_items, slices, panel_k, cols, rows, batch;
+    float *y;                  // B vectors of M fp32: y[b M + m]
+    uint32_t words_bytes, offw_bytes, raw_bytes, x_bytes, y_bytes;
+    uint32_t n_panels, slices, panel_k, cols, rows, batch;
+    uint32_t wpp, group;       // wavefronts per panel, panels per workgroup
     uint32_t tables_bytes, lut_bits, stage_bytes;
     uint32_t *status;
 };
@@ -55,14 +58,111 @@ struct GemmPrefetch {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4 &v) { return __builtin_bit_cast(bf16x8, v); }
 
+// One item (32 rows x panel_k columns of W, item q of the container): its
+// blocks are decoded and each complete sub-tile is multiplied into acc.
+// Returns false (and sets the status word) if a block's decoded count
+// disagrees with its block offsets; acc then holds a partial sum.
+template <int C, int NT>
+__device__ __forceinline__ bool gemm_item(const GemmArgs &g, uint32_t q, const Tables &t, uint8_t *stage,
+                                          uint32_t stage_off, uint32_t lane, const __amdgpu_buffer_rsrc_t &words,
+                                          const __amdgpu_buffer_rsrc_t &offw, const __amdgpu_buffer_rsrc_t &raw,
+                                          const __amdgpu_buffer_rsrc_t &xr, uint32_t xcol, f32x16 (&acc)[NT]) {
+    constexpr int PF = GemmPrefetch<C>::N;
+    extern __shared__ __align__(16) uint8_t lds[];
+    const const_u32_ptr items = (const_u32_ptr)(g.items);
+    const const_u32_ptr blockout = (const_u32_ptr)(g.blockout);
+    const uint32_t c0 = items[4 * q], b0 = items[4 * q + 1], bits = items[4 * q + 2];
+    const uint32_t b1 = items[4 * q + 5];
+    const uint32_t p = q / g.slices, col0 = (q % g.slices) * g.panel_k;
+    const uint32_t e0 = 32u * (p * g.cols + col0);
+    u32x2 carry = {0u, 0u};
+    for (uint32_t b = b0; b < b1; ++b) {
+        const uint32_t s_out = blockout[b], e_out = blockout[b + 1];
+        const uint32_t rs = s_out - e0, base = rs & ~511u, lead = rs - base;
+        const uint32_t total_want = e_out - s_out;
+        // Zero the staging bytes this block ORs into, then put back the
+        // exponents carried from the previous block in front of them.
+        const uint32_t nz = min(lead + total_want + 8u, g.stage_bytes);
+        for (uint32_t o = 16u * lane; o + 16u <= ((nz + 15u) & ~15u); o += 16u * kWave)
+            *reinterpret_cast<uint4 *>(stage + o) = make_uint4(0, 0, 0, 0);
+        if (8u * lane < lead) *reinterpret_cast<u32x2 *>(stage + 8u * lane) = carry;
+
+        const uint32_t ci = (b - b0) * kWave + lane;  // item-relative chunk
+        Chunk<C> ck;
+        load_chunk<C>(words, offw, c0 + ci, ck);
+        u32x2 R[PF];
+#pragma unroll
+        for (int j = 0; j < PF; ++j)
+            R[j] = __builtin_amdgcn_raw_buffer_load_b64(raw, e0 + base + 512u * j + 8u * lane, 0, 0);
+        int start, end;
+        chunk_span<C>(ck, c0 + ci,
+                      int(min(max(int64_t(bits) - int64_t(ci) * (8 * C), int64_t(-1)), int64_t(8 * C + 32))),
+                      start, end);
+        const uint32_t cnt = start < end ? count_codes<C>(ck, start, end, t) : 0u;
+        const uint32_t incl = wave_inclusive_scan(cnt);
+        const uint32_t total = __builtin_amdgcn_readlane(incl, kWave - 1);
+        const bool bad = (total != total_want) | (__builtin_amdgcn_ballot_w64(cnt > 8u * C) != 0);
+        if (!bad && cnt) write_codes<C>(ck, start, end, lds, stage_off + lead + (incl - cnt), t);
+        wait_for(R);
+        if (bad) {
+            if (lane == 0 && g.status) atomicOr(g.status, kStatusCorrupt);
+            return false;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+        // Complete sub-tiles: W operand from the staged exponents and the
+        // raw bytes, X operand from global memory (cached).
+        const uint32_t extent = lead + total;
+        const uint32_t nfull = extent >> 9;
+        const uint32_t kcol = col0 + 16u * (base >> 9);
+#pragma unroll
+        for (int j = 0; j < PF; ++j) {
+            if (uint32_t(j) < nfull) {
+                const u32x2 E = *reinterpret_cast<const u32x2 *>(stage + 512u * j + 8u * lane);
+                const bf16x8 A = as_bf16x8(assemble8(E, R[j]));
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    const u32x4 X = __builtin_amdgcn_raw_buffer_load_b128(
+                        xr, xcol + 2u * (32u * nt * g.cols + kcol + 16u * j), 0, 0);
+                    acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, as_bf16x8(X), acc[nt], 0, 0, 0);
+                }
+            }
+        }
+        for (uint32_t j = PF; j < nfull; ++j) {
+            const u32x2 Rj = __builtin_amdgcn_raw_buffer_load_b64(raw, e0 + base + 512u * j + 8u * lane, 0, 0);
+            const u32x2 E = *reinterpret_cast<const u32x2 *>(stage + 512u * j + 8u * lane);
+            const bf16x8 A = as_bf16x8(assemble8(E, Rj));
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const u32x4 X =
+                    __builtin_amdgcn_raw_buffer_load_b128(xr, xcol + 2u * (32u * nt * g.cols + kcol + 16u * j), 0, 0);
+                acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, as_bf16x8(X), acc[nt], 0, 0, 0);
+            }
+        }
+        // The sub-tile this block only began moves to the next block.
+        const uint32_t tail = extent - 512u * nfull;
+        carry = 8u * lane < tail ? *reinterpret_cast<const u32x2 *>(stage + 512u * nfull + 8u * lane) : u32x2{0u, 0u};
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    return true;
+}
+
+// Workgroup of group x wpp wavefronts: each round takes `group` consecutive
+// panels; wavefront w works on panel w / wpp and takes its slices w % wpp,
+// w % wpp + wpp, ...  Every staging area holds at least 4 KB, which the
+// reduction reuses for one 32 x 32 fp32 tile per wavefront.
 template <int C, int NT>
 __global__ __launch_bounds__(1024) void dfc_gemm_kernel(const GemmArgs g) {
     extern __shared__ __align__(16) uint8_t lds[];
-    constexpr int PF = GemmPrefetch<C>::N;
     const Tables t = stage_tables(lds, g.tables, g.tables_bytes, g.lut_bits);
-    const uint32_t waves = blockDim.x / kWave;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const uint32_t lane = threadIdx.x % kWave;
+    const uint32_t wpp = g.wpp;
+    const uint32_t pw = wave / wpp, sw = wave % wpp;  // panel in the round, first slice
     const uint32_t stage_off = g.tables_bytes + wave * g.stage_bytes;
     uint8_t *stage = lds + stage_off;
     const __amdgpu_buffer_rsrc_t words =
@@ -73,122 +173,59 @@ __global__ __launch_bounds__(1024) void dfc_gemm_kernel(const GemmArgs g) {
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(g.raw), 0, int(g.raw_bytes), kBufferConfig);
     const __amdgpu_buffer_rsrc_t xr =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(g.x), 0, int(g.x_bytes), kBufferConfig);
-    const const_u32_ptr items = (const_u32_ptr)(g.items);
-    const const_u32_ptr blockout = (const_u32_ptr)(g.blockout);
-    const uint32_t total_waves = gridDim.x * waves;
+    const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(g.y, 0, int(g.y_bytes), kBufferConfig);
     // B operand rows of this lane: column n = 32 nt + lane % 32 of X, k offset
     // 8 (lane / 32) inside the sub-tile (rows past B load zeros).
     const uint32_t xcol = 2u * (lane % 32u) * g.cols + 16u * (lane / 32u);
 
-    for (uint32_t q = blockIdx.x * waves + wave; q < g.n_items; q += total_waves) {
-        const uint32_t c0 = items[4 * q], b0 = items[4 * q + 1], bits = items[4 * q + 2];
-        const uint32_t b1 = items[4 * q + 5];
-        const uint32_t p = q / g.slices, col0 = (q % g.slices) * g.panel_k, row0 = 32u * p;
-        const uint32_t e0 = 32u * (p * g.cols + col0);
+    // the round count is the same for every wavefront of the workgroup
+    for (uint32_t p0 = blockIdx.x * g.group; p0 < g.n_panels; p0 += gridDim.x * g.group) {
+        const uint32_t p = p0 + pw;
         f32x16 acc[NT];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x16{};
-        u32x2 carry = {0u, 0u};
-        bool ok = true;
-        for (uint32_t b = b0; b < b1; ++b) {
-            const uint32_t s_out = blockout[b], e_out = blockout[b + 1];
-            const uint32_t rs = s_out - e0, base = rs & ~511u, lead = rs - base;
-            const uint32_t total_want = e_out - s_out;
-            // Zero the staging bytes this block ORs into, then put back the
-            // exponents carried from the previous block in front of them.
-            const uint32_t nz = min(lead + total_want + 8u, g.stage_bytes);
-            for (uint32_t o = 16u * lane; o + 16u <= ((nz + 15u) & ~15u); o += 16u * kWave)
-                *reinterpret_cast<uint4 *>(stage + o) = make_uint4(0, 0, 0, 0);
-            if (8u * lane < lead) *reinterpret_cast<u32x2 *>(stage + 8u * lane) = carry;
-
-            const uint32_t ci = (b - b0) * kWave + lane;  // item-relative chunk
-            Chunk<C> ck;
-            load_chunk<C>(words, offw, c0 + ci, ck);
-            u32x2 R[PF];
-#pragma unroll
-            for (int j = 0; j < PF; ++j)
-                R[j] = __builtin_amdgcn_raw_buffer_load_b64(raw, e0 + base + 512u * j + 8u * lane, 0, 0);
-            int start, end;
-            chunk_span<C>(ck, c0 + ci,
-                          int(min(max(int64_t(bits) - int64_t(ci) * (8 * C), int64_t(-1)), int64_t(8 * C + 32))),
-                          start, end);
-            const uint32_t cnt = start < end ? count_codes<C>(ck, start, end, t) : 0u;
-            const uint32_t incl = wave_inclusive_scan(cnt);
-            const uint32_t total = __builtin_amdgcn_readlane(incl, kWave - 1);
-            const bool bad = (total != total_want) | (__builtin_amdgcn_ballot_w64(cnt > 8u * C) != 0);
-            if (!bad && cnt) write_codes<C>(ck, start, end, lds, stage_off + lead + (incl - cnt), t);
-            wait_for(R);
-            if (bad) {
-                if (lane == 0 && g.status) atomicOr(g.status, kStatusCorrupt);
-                ok = false;
-                break;
-            }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-            // Complete sub-tiles: W operand from the staged exponents and the
-            // raw bytes, X operand from global memory (cached).
-            const uint32_t extent = lead + total;
-            const uint32_t nfull = extent >> 9;
-            const uint32_t kcol = col0 + 16u * (base >> 9);
-#pragma unroll
-            for (int j = 0; j < PF; ++j) {
-                if (uint32_t(j) < nfull) {
-                    const u32x2 E = *reinterpret_cast<const u32x2 *>(stage + 512u * j + 8u * lane);
-                    const bf16x8 A = as_bf16x8(assemble8(E, R[j]));
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) {
-                        const u32x4 X = __builtin_amdgcn_raw_buffer_load_b128(
-                            xr, xcol + 2u * (32u * nt * g.cols + kcol + 16u * j), 0, 0);
-                        acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, as_bf16x8(X), acc[nt], 0, 0, 0);
-                    }
-                }
-            }
-            for (uint32_t j = PF; j < nfull; ++j) {
-                const u32x2 Rj = __builtin_amdgcn_raw_buffer_load_b64(raw, e0 + base + 512u * j + 8u * lane, 0, 0);
-                const u32x2 E = *reinterpret_cast<const u32x2 *>(stage + 512u * j + 8u * lane);
-                const bf16x8 A = as_bf16x8(assemble8(E, Rj));
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    const u32x4 X =
-                        __builtin_amdgcn_raw_buffer_load_b128(xr, xcol + 2u * (32u * nt * g.cols + kcol + 16u * j), 0, 0);
-                    acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, as_bf16x8(X), acc[nt], 0, 0, 0);
-                }
-            }
-            // The sub-tile this block only began moves to the next block.
-            const uint32_t tail = extent - 512u * nfull;
-            carry = 8u * lane < tail ? *reinterpret_cast<const u32x2 *>(stage + 512u * nfull + 8u * lane)
-                                     : u32x2{0u, 0u};
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        }
-        if (!ok) continue;
+        if (p < g.n_panels)
+            for (uint32_t s = sw; s < g.slices; s += wpp)
+                if (!gemm_item<C, NT>(g, p * g.slices + s, t, stage, stage_off, lane, words, offw, raw, xr, xcol, acc))
+                    break;
         // D[i][j] of a 32x32 tile: i = 8 (r / 4) + 4 (lane / 32) + r % 4,
-        // j = lane % 32.
+        // j = lane % 32.  Value r of lane L goes to slot 4 (64 (r / 4) + L) +
+        // r % 4 of the wavefront's tile, so that element e of a float4 slot
+        // holds rows 8 (e / 64) + 4 ((e % 64) / 32) + 0..3 of column e % 32.
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-            const uint32_t n = 32u * nt + lane % 32u;
-            if (n < g.batch) {
-                float *yc = g.y + uint64_t(n) * g.rows + row0 + 4u * (lane / 32u);
+            if (nt > 0) __syncthreads();  // the previous tile has been read
 #pragma unroll
-                for (int r = 0; r < 16; ++r) unsafeAtomicAdd(yc + 8 * (r / 4) + (r % 4), acc[nt][r]);
+            for (int r4 = 0; r4 < 4; ++r4)
+                *reinterpret_cast<float4 *>(stage + 16u * (64u * r4 + lane)) =
+                    make_float4(acc[nt][4 * r4], acc[nt][4 * r4 + 1], acc[nt][4 * r4 + 2], acc[nt][4 * r4 + 3]);
+            __syncthreads();
+            for (uint32_t e = sw * kWave + lane; e < 256u; e += wpp * kWave) {
+                const uint8_t *slot = lds + g.tables_bytes + pw * wpp * g.stage_bytes + 16u * e;
+                float4 v = *reinterpret_cast<const float4 *>(slot);
+                for (uint32_t w = 1; w < wpp; ++w) {
+                    const float4 u = *reinterpret_cast<const float4 *>(slot + w * g.stage_bytes);
+                    v.x += u.x;
+                    v.y += u.y;
+                    v.z += u.z;
+                    v.w += u.w;
+                }
+                const uint32_t n = 32u * uint32_t(nt) + e % 32u;
+                const uint32_t m = 32u * p + 8u * (e / 64u) + 4u * ((e % 64u) / 32u);
+                if (p < g.n_panels && n < g.batch)
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), yr, 4u * (n * g.rows + m), 0, 0);
             }
         }
+        __syncthreads();  // tiles read before the next round's staging
     }
-}
-
-__global__ void fill_zero_kernel(float *y, uint64_t n) {
-    for (uint64_t i = uint64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += uint64_t(gridDim.x) * blockDim.x)
-        y[i] = 0.0f;
 }
 
 template <int C, int NT>
 dfc_status launch_gemm(const GemmArgs &proto, uint32_t max_block, hipStream_t stream) {
     GemmArgs g = proto;
-    // staging: a carried partial sub-tile (< 512) + the block + spill, rounded to 16
-    const uint32_t stage = (511u + max_block + 32u + 15u) & ~15u;
+    // staging: a carried partial sub-tile (< 512) + the block + spill, rounded
+    // to 16, and at least one 32 x 32 fp32 tile for the reduction
+    const uint32_t stage = std::max(4096u, (511u + max_block + 32u + 15u) & ~15u);
     g.stage_bytes = stage;
     static bool attr_set = false;
     if (!attr_set) {
@@ -197,26 +234,24 @@ dfc_status launch_gemm(const GemmArgs &proto, uint32_t max_block, hipStream_t st
             return DFC_EHIP;
         attr_set = true;
     }
-    uint32_t waves = 0, best = 0;
-    int best_per_cu = 0;
-    for (uint32_t w = 1; w <= kMaxWaves; ++w) {
-        const uint32_t lds = g.tables_bytes + w * stage;
-        if (lds > kLdsBytes) break;
-        int per_cu = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(&dfc_gemm_kernel<C, NT>),
-                                                         int(w * kWave), size_t(lds)) != hipSuccess)
-            per_cu = int(kLdsBytes / lds);
-        if (per_cu > 0 && uint32_t(per_cu) * w >= best) {
-            best = uint32_t(per_cu) * w;
-            waves = w;
-            best_per_cu = per_cu;
-        }
+    // about 8 wavefronts per workgroup: up to 8 per panel (one slice each
+    // when the panel has 8 slices or fewer), several panels when it has few
+    uint32_t wpp = std::min<uint32_t>(g.slices, 8u);
+    uint32_t group = std::max<uint32_t>(1u, 8u / wpp);
+    while (wpp * group > 1 && g.tables_bytes + wpp * group * stage > kLdsBytes) {
+        if (group > 1)
+            --group;
+        else
+            --wpp;
     }
-    if (!waves) return DFC_EUNSUPPORTED;
-    const uint64_t slots = uint64_t(best_per_cu) * uint64_t(device_cu_count());
-    const uint64_t grid = std::max<uint64_t>(1, std::min<uint64_t>(slots, dfc::ceil_div(g.n_items, waves)));
+    const uint32_t waves = wpp * group;
     const size_t lds = size_t(g.tables_bytes) + size_t(waves) * stage;
-    hipLaunchKernelGGL(fill_zero_kernel, dim3(256), dim3(256), 0, stream, g.y, uint64_t(g.batch) * g.rows);
+    if (lds > kLdsBytes) return DFC_EUNSUPPORTED;
+    g.wpp = wpp;
+    g.group = group;
+    // one workgroup per round of panels: the hardware hands out the tail
+    const uint64_t grid = dfc::ceil_div(uint64_t(g.n_panels), uint64_t(group));
+    if (grid > 0x7fffffffull) return DFC_EUNSUPPORTED;
     hipLaunchKernelGGL((dfc_gemm_kernel<C, NT>), dim3(uint32_t(grid)), dim3(waves * kWave), lds, stream, g);
     return hipGetLastError() == hipSuccess ? DFC_OK : DFC_EHIP;
 }
@@ -246,7 +281,7 @@ dfc_status dfc_decode_gemm(const void *w_blob_dev, const dfc_info *info, const u
     if (in.max_block_elems > 64u * dfc::ceil_div(8ull * C, in.min_len)) return DFC_EINVAL;
     const uint64_t limit = kNowhere - 64u * 1024u;
     if (in.words_bytes > limit || in.offsets_bytes > limit || in.raw_bytes > limit ||
-        2ull * DFC_GEMM_MAX_BATCH * in.cols > limit || in.rows >= (uint64_t(1) << 32))
+        2ull * DFC_GEMM_MAX_BATCH * in.cols > limit || 4ull * DFC_GEMM_MAX_BATCH * in.rows > limit)
         return DFC_EUNSUPPORTED;
     const uint8_t *base = static_cast<const uint8_t *>(w_blob_dev);
     GemmArgs g;
@@ -263,7 +298,8 @@ dfc_status dfc_decode_gemm(const void *w_blob_dev, const dfc_info *info, const u
     g.offw_bytes = uint32_t(in.offsets_bytes);
     g.raw_bytes = uint32_t(in.raw_bytes);
     g.x_bytes = uint32_t(2ull * batch * in.cols);
-    g.n_items = uint32_t(in.n_items);
+    g.y_bytes = uint32_t(4ull * batch * in.rows);
+    g.n_panels = uint32_t(in.rows / dfc::kPanelRows);
     g.panel_k = in.panel_k;
     g.slices = uint32_t(dfc::ceil_div(in.cols, in.panel_k));
     g.cols = uint32_t(in.cols);

@@ -1,7 +1,8 @@
 """GPU parity of the fused decode + matrix product (dfc_decode_gemm), called
 through the C ABI.
 
-Two checks that do not depend on the summation order:
+Y starts as NaN in every case, so an element the kernel leaves unwritten
+fails.  Two checks that do not depend on the summation order:
 
 * exactness of the decode inside the fused path: with X made of unit
   vectors e_k, every product has one non-zero term, so Y's columns are W's
@@ -46,7 +47,8 @@ def upload(w, C=16, k=11, panel_k=1024):
 def run(dev, info, x_bits):
     """x_bits: (B, K) uint16 host array -> Y (B, M) float32 host array."""
     x = torch.from_numpy(np.ascontiguousarray(x_bits).view(np.int16)).cuda()
-    y = torch.empty((x_bits.shape[0], info.rows), dtype=torch.float32, device="cuda")
+    # every element must be written
+    y = torch.full((x_bits.shape[0], info.rows), float("nan"), dtype=torch.float32, device="cuda")
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
     dfc.decode_gemm(dev, info, x, y, status)
     torch.cuda.synchronize()
@@ -104,6 +106,29 @@ def test_product_against_oracle(B):
     dev, info, _ = upload(w, C=16, panel_k=1024)
     say("case product B", B)
     check_product(w, x, run(dev, info, x))
+
+
+@pytest.mark.parametrize("M,K,panel_k", [
+    (160, 1040, 1024),   # 2 slices, 5 panels: four panels per workgroup, ragged last round
+    (96, 1040, 64),      # 17 slices (last one 16 wide): wavefronts take 3, 2, 2, ... slices
+    (64, 2048, 2048),    # 1 slice: eight panels per workgroup, six of them idle
+    (288, 512, 32),      # 16 slices of one sub-tile width, 9 panels
+    (32, 48, 16),        # one panel of 3 one-sub-tile slices
+])
+@pytest.mark.parametrize("B", [5, 33])
+def test_slices_and_panel_groups(M, K, panel_k, B):
+    """Panels of 1 to 17 column slices, split over a workgroup's wavefronts
+    and summed in LDS: against the oracle, and the same bits on a second
+    run (the slices are summed in a fixed order)."""
+    w = synth.gaussian_with_outliers((M, K), 0.02, (90, M, K))
+    x = synth.gaussian((B, K), 1.0, (91, B))
+    dev, info, _ = upload(w, C=8, panel_k=panel_k)
+    say("case slices M", M, "K", K, "panel_k", panel_k, "B", B)
+    y = run(dev, info, x)
+    check_product(w, x, y)
+    assert np.array_equal(y.view(np.uint32), run(dev, info, x).view(np.uint32))
+    cols = list(range(K - min(K, 64), K))
+    assert np.array_equal(run(dev, info, unit_vectors(K, cols)), w_as_f32(w)[:, cols].T)
 
 
 @pytest.mark.parametrize("kind", list(synth.STRESS_KINDS))
