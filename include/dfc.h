@@ -224,7 +224,11 @@ enum { DFC_GEMM_MAX_BATCH = 64 };
  * column-major), 4-byte aligned; every element is overwritten.  Products of
  * bf16 pairs are exact and accumulate in fp32; the partial sums of a panel's
  * column slices are added in a fixed order, so the same inputs give the
- * same bits on every run.  status_dev: as in dfc_decode (nonzero if a
+ * same bits on every run.  Exception: a matrix with more than 8 column
+ * slices per panel and too few 32-row panels to occupy the GPU has each
+ * panel shared by several workgroups, whose sums are added into Y (zeroed
+ * first, on the stream) with fp32 atomics; with three or more per panel the
+ * last bits of Y may then differ between runs.  status_dev: as in dfc_decode (nonzero if a
  * block's decoded count disagrees with its block offsets; Y is then
  * unspecified).  Errors before launch: DFC_EINVAL (null or
  * misaligned pointers, batch out of range, bad decode parameters),

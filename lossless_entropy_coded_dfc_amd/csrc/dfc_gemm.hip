@@ -9,14 +9,17 @@
 // MFMA per 32 output columns, and the products accumulate in fp32 registers.
 //
 // Work decomposition: a workgroup takes whole panels (32 rows of W), a few
-// wavefronts per panel; each wavefront decodes some of the panel's items
-// (32 rows x panel_k columns) and accumulates their products in registers.
+// wavefronts per panel, or, for matrices with too few panels to fill the
+// GPU, a share of one panel's items; each wavefront decodes some items (32
+// rows x panel_k columns) and accumulates their products in registers.
 // A block of an item (64 chunks) decodes into the wavefront's staging area,
 // whose start is the first sub-tile the block touches; the exponents of a
 // sub-tile the block only begins are carried in registers into the next
 // block's staging area.  The partial 32 x B products of a panel's wavefronts
 // are then summed in LDS in wavefront order and written to Y with plain
-// stores: no atomics, and the same bits on every run.
+// stores: no atomics, and the same bits on every run.  Only when a panel is
+// shared by several workgroups are their sums added into Y (zeroed first)
+// with fp32 atomics.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -43,7 +46,8 @@ struct GemmArgs {
     float *y;                  // B vectors of M fp32: y[b M + m]
     uint32_t words_bytes, offw_bytes, raw_bytes, x_bytes, y_bytes;
     uint32_t n_panels, slices, panel_k, cols, rows, batch;
-    uint32_t wpp, group;       // wavefronts per panel, panels per workgroup
+    uint32_t wpp, group;       // wavefronts per panel in a workgroup, panels per workgroup
+    uint32_t split, rounds;    // workgroups per panel; rounds = ceil(n_panels / group) * split
     uint32_t tables_bytes, lut_bits, stage_bytes;
     uint32_t *status;
 };
@@ -151,10 +155,12 @@ __device__ __forceinline__ bool gemm_item(const GemmArgs &g, uint32_t q, const T
     return true;
 }
 
-// Workgroup of group x wpp wavefronts: each round takes `group` consecutive
-// panels; wavefront w works on panel w / wpp and takes its slices w % wpp,
-// w % wpp + wpp, ...  Every staging area holds at least 4 KB, which the
-// reduction reuses for one 32 x 32 fp32 tile per wavefront.
+// Workgroup of group x wpp wavefronts.  A round takes `group` consecutive
+// panels (split == 1) or the part-th of split workgroups on one panel
+// (group == 1); a panel's split * wpp wavefronts take its slices in turn:
+// wavefront v of the panel takes slices v, v + split wpp, ...  Every staging
+// area holds at least 4 KB, which the reduction reuses for one 32 x 32 fp32
+// tile per wavefront.
 template <int C, int NT>
 __global__ __launch_bounds__(1024) void dfc_gemm_kernel(const GemmArgs g) {
     extern __shared__ __align__(16) uint8_t lds[];
@@ -178,14 +184,16 @@ __global__ __launch_bounds__(1024) void dfc_gemm_kernel(const GemmArgs g) {
     // 8 (lane / 32) inside the sub-tile (rows past B load zeros).
     const uint32_t xcol = 2u * (lane % 32u) * g.cols + 16u * (lane / 32u);
 
+    const uint32_t stride = g.split * wpp;
     // the round count is the same for every wavefront of the workgroup
-    for (uint32_t p0 = blockIdx.x * g.group; p0 < g.n_panels; p0 += gridDim.x * g.group) {
-        const uint32_t p = p0 + pw;
+    for (uint32_t r = blockIdx.x; r < g.rounds; r += gridDim.x) {
+        const uint32_t part = r % g.split;
+        const uint32_t p = (r / g.split) * g.group + pw;
         f32x16 acc[NT];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x16{};
         if (p < g.n_panels)
-            for (uint32_t s = sw; s < g.slices; s += wpp)
+            for (uint32_t s = part * wpp + sw; s < g.slices; s += stride)
                 if (!gemm_item<C, NT>(g, p * g.slices + s, t, stage, stage_off, lane, words, offw, raw, xr, xcol, acc))
                     break;
         // D[i][j] of a 32x32 tile: i = 8 (r / 4) + 4 (lane / 32) + r % 4,
@@ -212,12 +220,26 @@ __global__ __launch_bounds__(1024) void dfc_gemm_kernel(const GemmArgs g) {
                 }
                 const uint32_t n = 32u * uint32_t(nt) + e % 32u;
                 const uint32_t m = 32u * p + 8u * (e / 64u) + 4u * ((e % 64u) / 32u);
-                if (p < g.n_panels && n < g.batch)
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), yr, 4u * (n * g.rows + m), 0, 0);
+                if (p < g.n_panels && n < g.batch) {
+                    if (g.split == 1) {
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), yr, 4u * (n * g.rows + m), 0, 0);
+                    } else {
+                        float *yp = g.y + (uint64_t(n) * g.rows + m);
+                        unsafeAtomicAdd(yp, v.x);
+                        unsafeAtomicAdd(yp + 1, v.y);
+                        unsafeAtomicAdd(yp + 2, v.z);
+                        unsafeAtomicAdd(yp + 3, v.w);
+                    }
+                }
             }
         }
         __syncthreads();  // tiles read before the next round's staging
     }
+}
+
+__global__ void fill_zero_kernel(float *y, uint64_t n) {
+    for (uint64_t i = uint64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += uint64_t(gridDim.x) * blockDim.x)
+        y[i] = 0.0f;
 }
 
 template <int C, int NT>
@@ -247,12 +269,33 @@ dfc_status launch_gemm(const GemmArgs &proto, uint32_t max_block, hipStream_t st
     const uint32_t waves = wpp * group;
     const size_t lds = size_t(g.tables_bytes) + size_t(waves) * stage;
     if (lds > kLdsBytes) return DFC_EUNSUPPORTED;
+    // Too few panels for the resident wavefronts: share each panel among
+    // `split` workgroups, with as few slices per wavefront as the resident
+    // count allows, spread evenly.
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(&dfc_gemm_kernel<C, NT>),
+                                                     int(waves * kWave), lds) != hipSuccess ||
+        per_cu < 1)
+        per_cu = 1;
+    const uint64_t resident = uint64_t(per_cu) * waves * uint64_t(device_cu_count());
+    uint32_t split = 1;
+    if (group == 1 && uint64_t(g.n_panels) * wpp < resident && g.slices > wpp) {
+        const uint64_t want = std::min<uint64_t>(g.slices, dfc::ceil_div(resident, uint64_t(g.n_panels)));
+        const uint64_t per_wave = dfc::ceil_div(uint64_t(g.slices), want);
+        const uint64_t per_panel = dfc::ceil_div(uint64_t(g.slices), per_wave);
+        split = uint32_t(dfc::ceil_div(per_panel, uint64_t(wpp)));
+    }
     g.wpp = wpp;
     g.group = group;
-    // one workgroup per round of panels: the hardware hands out the tail
-    const uint64_t grid = dfc::ceil_div(uint64_t(g.n_panels), uint64_t(group));
-    if (grid > 0x7fffffffull) return DFC_EUNSUPPORTED;
-    hipLaunchKernelGGL((dfc_gemm_kernel<C, NT>), dim3(uint32_t(grid)), dim3(waves * kWave), lds, stream, g);
+    g.split = split;
+    const uint64_t rounds = dfc::ceil_div(uint64_t(g.n_panels), uint64_t(group)) * split;
+    if (rounds > 0x7fffffffull) return DFC_EUNSUPPORTED;
+    g.rounds = uint32_t(rounds);
+    // one workgroup per round: the hardware hands out the tail
+    const uint32_t grid = g.rounds;
+    if (split > 1)
+        hipLaunchKernelGGL(fill_zero_kernel, dim3(256), dim3(256), 0, stream, g.y, uint64_t(g.batch) * g.rows);
+    hipLaunchKernelGGL((dfc_gemm_kernel<C, NT>), dim3(grid), dim3(waves * kWave), lds, stream, g);
     return hipGetLastError() == hipSuccess ? DFC_OK : DFC_EHIP;
 }
 

@@ -118,15 +118,18 @@ def test_product_against_oracle(B):
 @pytest.mark.parametrize("B", [5, 33])
 def test_slices_and_panel_groups(M, K, panel_k, B):
     """Panels of 1 to 17 column slices, split over a workgroup's wavefronts
-    and summed in LDS: against the oracle, and the same bits on a second
-    run (the slices are summed in a fixed order)."""
+    (and, past 8 slices, over several workgroups added with atomics) and
+    summed in LDS: against the oracle, and, with at most 8 slices (one
+    workgroup per panel, fixed summation order), the same bits on a second
+    run."""
     w = synth.gaussian_with_outliers((M, K), 0.02, (90, M, K))
     x = synth.gaussian((B, K), 1.0, (91, B))
     dev, info, _ = upload(w, C=8, panel_k=panel_k)
     say("case slices M", M, "K", K, "panel_k", panel_k, "B", B)
     y = run(dev, info, x)
     check_product(w, x, y)
-    assert np.array_equal(y.view(np.uint32), run(dev, info, x).view(np.uint32))
+    if -(-K // panel_k) <= 8:
+        assert np.array_equal(y.view(np.uint32), run(dev, info, x).view(np.uint32))
     cols = list(range(K - min(K, 64), K))
     assert np.array_equal(run(dev, info, unit_vectors(K, cols)), w_as_f32(w)[:, cols].T)
 
