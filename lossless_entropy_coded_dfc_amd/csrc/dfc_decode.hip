@@ -304,13 +304,7 @@ dfc_status launch_group(const dfc_batch_item *items, const uint32_t *idx, uint32
     if (live.empty()) return DFC_OK;
     // staging: lead (< 8) + elements + spill of the last lookup, rounded to 16
     const uint32_t stage = (max_block + 32u + 15u) & ~15u;
-    static bool attr_set = false;
-    if (!attr_set) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void *>(&dfc_decode_kernel<C, Padded>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, int(kLdsBytes)) != hipSuccess)
-            return DFC_EHIP;
-        attr_set = true;
-    }
+    if (!allow_full_lds(reinterpret_cast<const void *>(&dfc_decode_kernel<C, Padded>))) return DFC_EHIP;
     // Resident workgroups per CU for w wavefronts each, under both the LDS
     // and the register budget.
     auto resident = [&](uint32_t w) -> int {

@@ -10,6 +10,10 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+#include <set>
+#include <utility>
+
 #include <cstdint>
 
 #include "dfc.h"
@@ -387,6 +391,22 @@ __device__ __forceinline__ void chunk_span(const Chunk<C> &ck, uint32_t chunk, i
 }
 
 constexpr uint32_t kLdsBytes = 160u * 1024u;
+
+// Raises a kernel's dynamic LDS limit to kLdsBytes on the current device,
+// once per (kernel, device): the attribute is per device, and concurrent
+// first calls from several host threads are serialized.
+inline bool allow_full_lds(const void *kernel) {
+    static std::mutex mu;
+    static std::set<std::pair<const void *, int>> done;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return false;
+    std::lock_guard<std::mutex> lock(mu);
+    if (done.count({kernel, dev})) return true;
+    if (hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, int(kLdsBytes)) != hipSuccess)
+        return false;
+    done.insert({kernel, dev});
+    return true;
+}
 
 inline int device_cu_count() {
     int dev = 0, cus = 0;

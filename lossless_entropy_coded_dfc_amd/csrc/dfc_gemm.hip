@@ -249,13 +249,7 @@ dfc_status launch_gemm(const GemmArgs &proto, uint32_t max_block, hipStream_t st
     // to 16, and at least one 32 x 32 fp32 tile for the reduction
     const uint32_t stage = std::max(4096u, (511u + max_block + 32u + 15u) & ~15u);
     g.stage_bytes = stage;
-    static bool attr_set = false;
-    if (!attr_set) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void *>(&dfc_gemm_kernel<C, NT>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, int(kLdsBytes)) != hipSuccess)
-            return DFC_EHIP;
-        attr_set = true;
-    }
+    if (!allow_full_lds(reinterpret_cast<const void *>(&dfc_gemm_kernel<C, NT>))) return DFC_EHIP;
     // about 8 wavefronts per workgroup: up to 8 per panel (one slice each
     // when the panel has 8 slices or fewer), several panels when it has few
     uint32_t wpp = std::min<uint32_t>(g.slices, 8u);

@@ -134,6 +134,25 @@ def test_slices_and_panel_groups(M, K, panel_k, B):
     assert np.array_equal(run(dev, info, unit_vectors(K, cols)), w_as_f32(w)[:, cols].T)
 
 
+@pytest.mark.parametrize("M,K", [(1024, 4096), (4096, 14336)])
+def test_transformer_block_shapes(M, K):
+    """Wk/Wv- and down-shaped matrices of a Llama-3-8B block with 256-column
+    items: 16 or 56 slices per panel and too few panels to fill the GPU, so
+    each panel is shared by several workgroups whose sums are added with
+    atomics.  Sampled rows against the oracle at B = 1 and 16; one 64-column
+    window bit-exact with unit vectors."""
+    w = synth.gaussian_with_outliers((M, K), 0.02, (92, M, K))
+    dev, info, _ = upload(w, C=16, panel_k=256)
+    rows = np.random.default_rng(7).choice(M, 256, replace=False)
+    for B in (1, 16):
+        x = synth.gaussian((B, K), 1.0, (93, B))
+        say("case block shape M", M, "K", K, "B", B)
+        y = run(dev, info, x)
+        check_product(w[rows], x, y[:, rows])
+    cols = list(range(K // 2, K // 2 + 64))
+    assert np.array_equal(run(dev, info, unit_vectors(K, cols)), w_as_f32(w)[:, cols].T)
+
+
 @pytest.mark.parametrize("kind", list(synth.STRESS_KINDS))
 def test_stress_distributions(kind):
     M, K = 64, 512
