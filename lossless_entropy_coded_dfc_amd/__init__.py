@@ -252,14 +252,34 @@ def _dev_ptr(t) -> int:
     return t.data_ptr()
 
 
+def _blob_ptr(blob_dev, info: Info) -> int:
+    """Device address of a container tensor that holds info.blob_bytes:
+    the kernels read the sections at the offsets the info records, so a
+    shorter buffer would be read past its end."""
+    if not getattr(blob_dev, "is_cuda", False) or not blob_dev.is_contiguous():
+        raise TypeError("the container must be a contiguous device (cuda) tensor")
+    if blob_dev.numel() * blob_dev.element_size() < info.blob_bytes:
+        raise ValueError(f"the device container holds {blob_dev.numel() * blob_dev.element_size()} bytes, "
+                         f"fewer than the {info.blob_bytes} its info describes")
+    return blob_dev.data_ptr()
+
+
+def _status_ptr(status) -> int:
+    if status is None:
+        return 0
+    if status.element_size() != 4 or status.numel() < 1:
+        raise ValueError("status must be a device tensor of at least one 32-bit element")
+    return _dev_ptr(status)
+
+
 def decode(blob_dev, info: Info, out, status=None, stream=None):
     """Decode a container held in device memory (torch uint8 tensor) into
     ``out`` (torch tensor of info.n 16-bit elements).  Asynchronous."""
     if not out.is_contiguous() or out.element_size() != 2 or out.numel() != info.n:
         raise ValueError("out must be a contiguous 16-bit tensor with info.n elements")
-    _check(library().dfc_decode(ctypes.c_void_p(_dev_ptr(blob_dev)), ctypes.byref(info),
+    _check(library().dfc_decode(ctypes.c_void_p(_blob_ptr(blob_dev, info)), ctypes.byref(info),
                                 ctypes.c_void_p(_dev_ptr(out)), info.n,
-                                ctypes.c_void_p(_dev_ptr(status)), _stream(stream)), "dfc_decode")
+                                ctypes.c_void_p(_status_ptr(status)), _stream(stream)), "dfc_decode")
     return out
 
 
@@ -274,11 +294,11 @@ def decode_batch(items, status=None, stream=None):
         if not out.is_contiguous() or out.element_size() != 2 or out.numel() != info.n:
             raise ValueError("out must be a contiguous 16-bit tensor with info.n elements")
         keep.append(info)
-        arr[k].blob_dev = _dev_ptr(blob_dev)
+        arr[k].blob_dev = _blob_ptr(blob_dev, info)
         arr[k].info = ctypes.pointer(info)
         arr[k].dst_dev = _dev_ptr(out)
         arr[k].n = info.n
-    _check(library().dfc_decode_batch(arr, len(items), ctypes.c_void_p(_dev_ptr(status)), _stream(stream)),
+    _check(library().dfc_decode_batch(arr, len(items), ctypes.c_void_p(_status_ptr(status)), _stream(stream)),
            "dfc_decode_batch")
 
 
@@ -306,6 +326,10 @@ def encode_device(src, chunk_bytes: int = 16, lanes: int = 64, max_code_len: int
                                        ctypes.byref(codebook) if codebook is not None else None,
                                        ctypes.c_void_p(dst.data_ptr()), cap, ctypes.c_void_p(work.data_ptr()),
                                        wb.value, ctypes.byref(written), _stream(stream)), "dfc_encode_device")
+    if stream is not None:
+        # the packing kernels may still run on that stream: keep torch's
+        # allocator from handing the workspace to other streams' work first
+        work.record_stream(torch.cuda.ExternalStream(int(stream), device=src.device))
     return dst, written.value
 
 
@@ -323,9 +347,9 @@ def decode_gemm(blob_dev, info: Info, x, y, status=None, stream=None):
     B, K = x.shape
     if x.element_size() != 2 or K != info.cols or tuple(y.shape) != (B, info.rows) or y.element_size() != 4:
         raise ValueError("x must be (B, K) 16-bit and y (B, M) float32 for the container's M x K")
-    _check(library().dfc_decode_gemm(ctypes.c_void_p(_dev_ptr(blob_dev)), ctypes.byref(info),
+    _check(library().dfc_decode_gemm(ctypes.c_void_p(_blob_ptr(blob_dev, info)), ctypes.byref(info),
                                      ctypes.c_void_p(_dev_ptr(x)), B, ctypes.c_void_p(_dev_ptr(y)),
-                                     ctypes.c_void_p(_dev_ptr(status)), _stream(stream)), "dfc_decode_gemm")
+                                     ctypes.c_void_p(_status_ptr(status)), _stream(stream)), "dfc_decode_gemm")
 
 
 def set_launch(waves_per_group: int = 0, blocks_per_wave: int = 0):

@@ -183,6 +183,16 @@ def test_invalid_arguments_rejected():
     s = lib.dfc_decode(torch.from_numpy(b128).cuda().data_ptr(), dfc.blob_info(b128),
                                  out.data_ptr(), info.n, None, None)
     assert s == dfc.EUNSUPPORTED
+    # the binding refuses a device container shorter than its info, a host
+    # container and a status word that is not 32-bit, before any launch
+    with pytest.raises(ValueError):
+        dfc.decode(dev[: info.blob_bytes - 1], info, out[: info.n])
+    with pytest.raises(TypeError):
+        dfc.decode(torch.from_numpy(blob), info, out[: info.n])
+    with pytest.raises(ValueError):
+        dfc.decode(dev, info, out[: info.n], torch.zeros(1, dtype=torch.int16, device="cuda"))
+    with pytest.raises(ValueError):
+        dfc.decode_batch([(dev[:256], info, out[: info.n])])
 
 
 # ---------------------------------------------------------------- full size
