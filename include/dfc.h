@@ -263,9 +263,10 @@ dfc_status dfc_encode_device(const uint16_t *src_dev, uint64_t n, const dfc_para
                              void *dst_dev, uint64_t cap, void *work_dev, uint64_t work_bytes, uint64_t *written,
                              void *stream);
 
-/* Launch tuning knob for benchmarks: wavefronts per workgroup (4, 8 or 16)
- * and wave-blocks each wavefront decodes (1..64).  0 = automatic.  Returns
- * DFC_EINVAL for other values.  Process-wide; not thread-safe. */
+/* Launch tuning knob for benchmarks (Huffman layouts): wavefronts per
+ * workgroup (1..16) and wave-blocks each wavefront decodes (1..64); 0 =
+ * automatic.  Returns DFC_EINVAL for other values.  Process-wide; each value
+ * is read atomically by every later launch, on any thread. */
 dfc_status dfc_set_launch(uint32_t waves_per_group, uint32_t blocks_per_wave);
 
 /* Human-readable name of a status code. */

@@ -24,6 +24,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdint>
 #include <cstring>
 #include <vector>
@@ -263,8 +264,9 @@ __global__ __launch_bounds__(1024, Occupancy<C>::kWavesPerSimd) void dfc_decode_
 
 // ------------------------------------------------------------------ launch
 
+// Set by dfc_set_launch, read by every launch (possibly on other threads).
 struct LaunchCfg {
-    uint32_t waves = 0, blocks_per_wave = 0;
+    std::atomic<uint32_t> waves{0}, blocks_per_wave{0};
 } g_launch;
 
 // Split `slots` workgroups across items so that the largest per-workgroup
@@ -318,7 +320,8 @@ dfc_status launch_group(const dfc_batch_item *items, const uint32_t *idx, uint32
     };
     // waves per workgroup: the most resident wavefronts per CU, then the
     // larger workgroup (fewer table copies)
-    uint32_t waves = g_launch.waves;
+    uint32_t waves = g_launch.waves.load(std::memory_order_relaxed);
+    const uint32_t blocks_per_wave = g_launch.blocks_per_wave.load(std::memory_order_relaxed);
     if (!waves) {
         uint32_t best = 0;
         for (uint32_t w = 4; w <= kMaxWaves; ++w) {
@@ -336,10 +339,10 @@ dfc_status launch_group(const dfc_batch_item *items, const uint32_t *idx, uint32
     int per_cu = resident(waves);
     if (per_cu <= 0) per_cu = 1;
     uint64_t slots = uint64_t(per_cu) * uint64_t(device_cu_count());
-    if (g_launch.blocks_per_wave) {
+    if (blocks_per_wave) {
         // fixed work per workgroup instead of filling the machine exactly
         uint64_t total = 0;
-        for (uint64_t nb : blocks) total += dfc::ceil_div(nb, uint64_t(waves) * g_launch.blocks_per_wave);
+        for (uint64_t nb : blocks) total += dfc::ceil_div(nb, uint64_t(waves) * blocks_per_wave);
         slots = total;
     }
     const std::vector<uint32_t> g =
@@ -404,8 +407,8 @@ extern "C" {
 dfc_status dfc_set_launch(uint32_t waves_per_group, uint32_t blocks_per_wave) {
     if (waves_per_group > kMaxWaves) return DFC_EINVAL;
     if (blocks_per_wave > 64) return DFC_EINVAL;
-    g_launch.waves = waves_per_group;
-    g_launch.blocks_per_wave = blocks_per_wave;
+    g_launch.waves.store(waves_per_group, std::memory_order_relaxed);
+    g_launch.blocks_per_wave.store(blocks_per_wave, std::memory_order_relaxed);
     return DFC_OK;
 }
 
