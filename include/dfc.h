@@ -44,7 +44,7 @@ typedef enum {
     DFC_EINVAL = -1,       /* bad argument (null pointer, bad parameter value, misaligned buffer) */
     DFC_ESIZE = -2,        /* a buffer is too small, or n does not match the container */
     DFC_ECORRUPT = -3,     /* the container fails validation (or a decoded block count mismatched) */
-    DFC_EUNSUPPORTED = -4, /* valid container, but this build cannot decode that variant */
+    DFC_EUNSUPPORTED = -4, /* valid container, but this library cannot decode that variant */
     DFC_EHIP = -5          /* a HIP runtime call failed */
 } dfc_status;
 
