@@ -21,6 +21,7 @@ import numpy as np
 __all__ = [
     "round_to_bf16_bits",
     "gaussian",
+    "gaussian_pieces",
     "gaussian_with_outliers",
     "student_t",
     "bimodal",
@@ -76,6 +77,24 @@ def gaussian(shape, std: float, seed) -> np.ndarray:
     """i.i.d. N(0, std^2) rounded to bf16."""
     n = int(np.prod(shape))
     return _normal_bits(_rng(seed), n, std).reshape(shape)
+
+
+def gaussian_pieces(n: int, std: float, seed, piece: int = 1 << 26, threads: int = 16) -> np.ndarray:
+    """n i.i.d. N(0, std^2) bf16 values drawn in independent pieces of `piece`
+    values, piece j from the seed tuple (*seed, j), on up to `threads` host
+    threads: for tensors of billions of values, where one generator would take
+    minutes.  No two pieces repeat each other."""
+    from concurrent.futures import ThreadPoolExecutor
+    seed = (seed,) if isinstance(seed, int) else tuple(seed)
+    out = np.empty(n, dtype=np.uint16)
+
+    def fill(j):
+        lo = j * piece
+        out[lo: min(n, lo + piece)] = _normal_bits(_rng(seed + (j,)), min(n, lo + piece) - lo, std)
+
+    with ThreadPoolExecutor(max_workers=max(1, threads)) as pool:
+        list(pool.map(fill, range((n + piece - 1) // piece)))
+    return out
 
 
 def gaussian_with_outliers(shape, std: float, seed, frac: float = 1e-3,

@@ -258,3 +258,40 @@ def test_full_stress_8192x28672(kind):
         got, status = gpu_decode(blob)
         assert status == 0 and np.array_equal(got, x.ravel()), (kind, C)
     sampled_oracle_check(blob, got, n_samples=2)
+
+
+@pytest.mark.slow
+def test_largest_accepted_matrix():
+    """The largest matrix the launcher accepts: every stream is addressed
+    with 32-bit byte offsets that stay 64 KiB below the top, so n = 777 under
+    (2^32 - 16 - 2^16) / 2, i.e. 2,147,450,095 weights and 4.29 GB of bf16
+    output, ragged against blocks and octets.  Drawn in independent pieces
+    (no period that a wrapped offset could hide behind), decoded in the
+    flat, padded and rANS layouts and compared bit for bit on the device.
+    One weight more is refused before any launch."""
+    import ctypes
+    limit = 0xFFFFFFF0 - (1 << 16)
+    n = limit // 2 - 777
+    say("case largest matrix: generating", n, "weights")
+    x = synth.gaussian_pieces(n, 0.02, (150,))
+    ref = torch.from_numpy(x.view(np.int16)).cuda()
+    lib = dfc.library()
+    for layout, kw in ((dfc.LAYOUT_FLAT, {}), (dfc.LAYOUT_PADDED, {}), (dfc.LAYOUT_ANS, {"ans_steps": 512})):
+        blob = dfc.encode(x, layout=layout, **kw)
+        info = dfc.blob_info(blob)
+        dev = torch.from_numpy(blob).cuda()
+        del blob
+        out = torch.empty(n, dtype=torch.int16, device="cuda")
+        status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        say("case largest matrix layout", layout, "container bytes", info.blob_bytes)
+        dfc.decode(dev, info, out, status)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0, layout
+        assert torch.equal(out, ref), layout
+        over = dfc.Info.from_buffer_copy(info)
+        over.n = limit // 2 + 1
+        s = lib.dfc_decode(ctypes.c_void_p(dev.data_ptr()), ctypes.byref(over), ctypes.c_void_p(out.data_ptr()),
+                           over.n, None, None)
+        assert s == dfc.EUNSUPPORTED, layout
+        del dev, out
+        torch.cuda.empty_cache()
