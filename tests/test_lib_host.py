@@ -408,3 +408,26 @@ def test_ans_validation_rejects_corruption():
         with pytest.raises(dfc.DfcError) as ei:
             dfc.blob_info(blob)
         assert ei.value.status == dfc.ECORRUPT, name
+
+
+def test_header_is_c99_and_host_abi_links_from_c(tmp_path):
+    """include/dfc.h compiles as strict C99 and a C program linked to
+    libdfc.so encodes and inspects a container through the host entry
+    points (tests/c_abi_host.c)."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("no gcc")
+    here = os.path.dirname(os.path.abspath(__file__))
+    root = os.path.dirname(here)
+    libdir = os.path.dirname(dfc.library_path())
+    dfc.library()
+    exe = str(tmp_path / "c_abi_host")
+    r = subprocess.run(["gcc", "-std=c99", "-pedantic", "-Wall", "-Wextra", "-Werror",
+                        "-I", os.path.join(root, "include"), os.path.join(here, "c_abi_host.c"),
+                        "-L", libdir, "-ldfc", "-Wl,-rpath," + libdir, "-o", exe],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, (r.stdout + r.stderr)[-2000:]
+    assert "c abi ok" in r.stdout
