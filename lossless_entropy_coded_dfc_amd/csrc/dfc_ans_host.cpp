@@ -99,46 +99,18 @@ void encode_block(const uint16_t *src, uint64_t cnt, const uint32_t f[256], cons
     for (uint32_t l = 0; l < kAnsLanes; ++l) states[l] = uint32_t(x[l]);
 }
 
-uint32_t steps_or_default(uint32_t s) { return s ? s : uint32_t(DFC_ANS_STEPS_DEFAULT); }
-
 }  // namespace
 
-uint64_t ans_encode_bound(uint64_t n, uint32_t steps) {
-    const uint64_t nb = ceil_div(n, uint64_t(kAnsLanes) * steps_or_default(steps));
-    uint64_t off[kNumSections];
-    return place_sections(ans_section_sizes(n, n, nb), off);  // at most one word per element
-}
+uint32_t ans_steps_or_default(uint32_t s) { return s ? s : uint32_t(DFC_ANS_STEPS_DEFAULT); }
 
-dfc_status encode_ans(const uint16_t *src, uint64_t n, const dfc_params &p, uint64_t rows, uint64_t cols,
-                      uint8_t *dst, uint64_t cap, uint64_t *written) {
-    const uint32_t S = steps_or_default(p.ans_steps);
-    const uint64_t per = uint64_t(kAnsLanes) * S;
-    const uint64_t nb = ceil_div(n, per);
-    const unsigned nt = unsigned(std::min<uint64_t>(pick_threads(p.threads, n), std::max<uint64_t>(nb, 1)));
-    uint64_t hist[256];
-    histogram_mt(src, n, hist, nt);
-    uint32_t f[256], cum[256];
+void ans_frequencies(const uint64_t hist[256], uint32_t f[256], uint32_t cum[256]) {
     quantize(hist, f);
     cumulative(f, cum);
+}
 
-    // Pass 1: every block's states and words.
-    std::vector<uint32_t> states(nb * kAnsLanes);
-    std::vector<std::vector<uint16_t>> words(nb);
-    parallel_for(nt, [&](unsigned t) {
-        for (uint64_t b = nb * t / nt; b < nb * (t + 1) / nt; ++b)
-            encode_block(src + b * per, std::min(per, n - b * per), f, cum, &states[b * kAnsLanes], words[b]);
-    });
-    std::vector<uint64_t> first(nb + 1, 0);
-    for (uint64_t b = 0; b < nb; ++b) first[b + 1] = first[b] + words[b].size();
-    const uint64_t nw = first[nb];
-    if (nw >= (uint64_t(1) << 32)) return DFC_ESIZE;
-
-    // Pass 2: the container.
-    const SectionSizes sz = ans_section_sizes(n, nw, nb);
-    uint64_t off[kNumSections];
-    const uint64_t blob_bytes = place_sections(sz, off);
-    if (cap < blob_bytes) return DFC_ESIZE;
-    std::memset(dst, 0, blob_bytes);
+void ans_container_head(uint8_t *dst, uint64_t n, uint64_t nw, uint64_t nb, uint32_t S, uint64_t rows,
+                        uint64_t cols, const SectionSizes &sz, const uint64_t off[kNumSections], uint64_t blob_bytes,
+                        const uint32_t f[256]) {
     store_le<uint32_t>(dst + hdr::magic, kMagic);
     store_le<uint32_t>(dst + hdr::version, kVersion);
     store_le<uint64_t>(dst + hdr::n, n);
@@ -159,6 +131,44 @@ dfc_status encode_ans(const uint16_t *src, uint64_t n, const dfc_params &p, uint
     uint8_t *tab = dst + off[kTables];
     for (int s = 0; s < 256; ++s) store_le<uint16_t>(tab + 2 * s, uint16_t(f[s]));
     slot_table(f, tab + 512);
+}
+
+uint64_t ans_encode_bound(uint64_t n, uint32_t steps) {
+    const uint64_t nb = ceil_div(n, uint64_t(kAnsLanes) * ans_steps_or_default(steps));
+    uint64_t off[kNumSections];
+    return place_sections(ans_section_sizes(n, n, nb), off);  // at most one word per element
+}
+
+dfc_status encode_ans(const uint16_t *src, uint64_t n, const dfc_params &p, uint64_t rows, uint64_t cols,
+                      uint8_t *dst, uint64_t cap, uint64_t *written) {
+    const uint32_t S = ans_steps_or_default(p.ans_steps);
+    const uint64_t per = uint64_t(kAnsLanes) * S;
+    const uint64_t nb = ceil_div(n, per);
+    const unsigned nt = unsigned(std::min<uint64_t>(pick_threads(p.threads, n), std::max<uint64_t>(nb, 1)));
+    uint64_t hist[256];
+    histogram_mt(src, n, hist, nt);
+    uint32_t f[256], cum[256];
+    ans_frequencies(hist, f, cum);
+
+    // Pass 1: every block's states and words.
+    std::vector<uint32_t> states(nb * kAnsLanes);
+    std::vector<std::vector<uint16_t>> words(nb);
+    parallel_for(nt, [&](unsigned t) {
+        for (uint64_t b = nb * t / nt; b < nb * (t + 1) / nt; ++b)
+            encode_block(src + b * per, std::min(per, n - b * per), f, cum, &states[b * kAnsLanes], words[b]);
+    });
+    std::vector<uint64_t> first(nb + 1, 0);
+    for (uint64_t b = 0; b < nb; ++b) first[b + 1] = first[b] + words[b].size();
+    const uint64_t nw = first[nb];
+    if (nw >= (uint64_t(1) << 32)) return DFC_ESIZE;
+
+    // Pass 2: the container.
+    const SectionSizes sz = ans_section_sizes(n, nw, nb);
+    uint64_t off[kNumSections];
+    const uint64_t blob_bytes = place_sections(sz, off);
+    if (cap < blob_bytes) return DFC_ESIZE;
+    std::memset(dst, 0, blob_bytes);
+    ans_container_head(dst, n, nw, nb, S, rows, cols, sz, off, blob_bytes, f);
     uint8_t *wd = dst + off[kWords], *ofs = dst + off[kOffsets], *st = dst + off[kBlockout], *raw = dst + off[kRaw];
     for (uint64_t b = 0; b <= nb; ++b) store_le<uint32_t>(ofs + 4 * b, uint32_t(first[b]));
     parallel_for(nt, [&](unsigned t) {

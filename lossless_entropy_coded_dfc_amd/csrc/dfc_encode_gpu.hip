@@ -15,6 +15,14 @@
 //      and writes the raw bytes; the element whose code covers a chunk's
 //      first bit writes that chunk's 5-bit offset (the next code starts where
 //      it ends) and, on block boundaries, the block's output offset.
+// Containers in the interleaved rANS layout (an arithmetic-family code, the
+// blog's section 02) take steps 1-2 with frequencies instead of code
+// lengths, then one wavefront per block runs the block's encoder twice: a
+// first pass counts the block's 16-bit words, an exclusive scan over the
+// blocks gives every block's first word (its total is read back to place the
+// sections), and a second pass writes each word at its place in decode
+// order, then the final states; the raw bytes are written by a plain
+// streaming kernel.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -191,21 +199,181 @@ __global__ __launch_bounds__(256) void pack_kernel(const PackArgs a, const Book 
     if (nacc > 0) or_word(a.words, w, uint32_t(acc << (32 - nacc)));
 }
 
+// ------------------------------------------------------------------ rANS
+
+// Per-symbol coding constants: frequency, cumulative frequency and
+// ceil(2^32 / f) (0 for f = 1), so that v / f needs no divide: the high half
+// of v * magic is the quotient or one more.
+struct AnsBook {
+    uint16_t f[256], cum[256];
+    uint32_t magic[256];
+};
+
+struct AnsArgs {
+    const uint16_t *src;
+    uint32_t n, steps, n_blocks;
+    uint32_t *counts;        // pass 1: 16-bit words per block (counts[n_blocks] = 0)
+    const uint64_t *first;   // pass 2: first word of every block (n_blocks + 1)
+    uint16_t *words;         // pass 2: the words section
+    uint32_t *offsets;       // pass 2: the offsets section (n_blocks + 1)
+    uint32_t *states;        // pass 2: 64 initial decoder states per block
+};
+
+constexpr uint32_t kAnsEncWaves = 4;
+
+// One wavefront per block, lane l coding the elements 64 i + l.  The steps
+// run backwards (a decoder reads them forwards) and, inside a step, lanes
+// 63 down to 0 emit first: a word's place in decode order is the block's
+// word count minus one minus the words emitted before it.
+template <bool Write>
+__global__ __launch_bounds__(kAnsEncWaves * 64) void ans_encode_kernel(const AnsArgs a, const AnsBook book) {
+    __shared__ uint32_t fc[256], mg[256];  // f | cum << 16, magic
+    for (uint32_t s = threadIdx.x; s < 256; s += blockDim.x) {
+        fc[s] = uint32_t(book.f[s]) | (uint32_t(book.cum[s]) << 16);
+        mg[s] = book.magic[s];
+    }
+    __syncthreads();
+    const uint32_t wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+    const uint32_t b = blockIdx.x * kAnsEncWaves + wave;
+    if (b >= a.n_blocks) return;
+    const uint32_t per = 64u * a.steps, e0 = b * per;
+    const uint32_t cnt = min(per, a.n - e0), steps = (cnt + 63u) / 64u;
+    uint32_t x = uint32_t(dfc::kAnsLow), emitted = 0;
+    uint64_t base = 0;
+    uint32_t last = 0;
+    if constexpr (Write) {
+        base = a.first[b];
+        last = uint32_t(a.first[b + 1] - base) - 1u;  // unused when the block has no words
+    }
+    for (uint32_t i = steps; i-- > 0;) {
+        const uint32_t j = 64u * i + lane;
+        const bool live = j < cnt;
+        const uint32_t sym = live ? (uint32_t(a.src[e0 + j]) >> 7) & 0xFFu : 0u;
+        const uint32_t e = fc[sym], f = e & 0xFFFFu, cum = e >> 16;
+        // x >= f 2^20, without forming f << 20 (2^32 for a lone symbol)
+        const bool emit = live && (x >> 20) >= f;
+        const uint64_t m = __builtin_amdgcn_ballot_w64(emit);
+        if constexpr (Write) {
+            if (emit) {
+                const uint32_t above = uint32_t(__builtin_popcountll(lane == 63 ? 0ull : m >> (lane + 1)));
+                a.words[base + (last - emitted - above)] = uint16_t(x & 0xFFFFu);
+            }
+        }
+        const uint32_t v = emit ? x >> 16 : x;
+        // q = v / f, r = v mod f
+        uint32_t q = f == 1u ? v : __umulhi(v, mg[sym]);
+        uint32_t r = v - q * f;
+        if (r >= f) {  // q was one too large
+            --q;
+            r += f;
+        }
+        if (live) x = q * uint32_t(dfc::kAnsSlots) + r + cum;
+        emitted += uint32_t(__builtin_popcountll(m));
+    }
+    if constexpr (!Write) {
+        if (lane == 0) {
+            a.counts[b] = emitted;
+            if (b == 0) a.counts[a.n_blocks] = 0u;
+        }
+    } else {
+        a.states[64ull * b + lane] = x;
+        if (lane == 0) {
+            a.offsets[b] = uint32_t(base);
+            if (b + 1 == a.n_blocks) a.offsets[a.n_blocks] = uint32_t(a.first[a.n_blocks]);
+        }
+    }
+}
+
+// Raw bytes (sign << 7 | mantissa) of n elements, 16 per thread.
+__global__ __launch_bounds__(256) void raw_kernel(const uint16_t *src, uint64_t n, uint8_t *raw) {
+    for (uint64_t j0 = (uint64_t(blockIdx.x) * blockDim.x + threadIdx.x) * 16; j0 < n;
+         j0 += uint64_t(gridDim.x) * blockDim.x * 16) {
+        if (j0 + 16 <= n) {
+            uint32_t r[4] = {0, 0, 0, 0};
+#pragma unroll
+            for (uint32_t q = 0; q < 16; ++q) r[q >> 2] |= raw_of(src[j0 + q]) << (8 * (q & 3));
+            *reinterpret_cast<uint4 *>(raw + j0) = make_uint4(r[0], r[1], r[2], r[3]);
+        } else {
+            for (uint64_t j = j0; j < n; ++j) raw[j] = uint8_t(raw_of(src[j]));
+        }
+    }
+}
+
 // Host copy of a workspace layout.
+// segbits/segoff hold one entry per 4096-element segment (FLAT) or per rANS
+// block plus one (the smallest rANS block is 64 x 8 elements).
 struct Workspace {
-    uint64_t hist_off, segbits_off, segoff_off, bytes, nseg;
+    uint64_t hist_off, segbits_off, segoff_off, bytes, nseg, slots;
 };
 Workspace workspace_layout(uint64_t n) {
     Workspace w;
     w.nseg = dfc::ceil_div(std::max<uint64_t>(n, 1), kSegElems);
+    w.slots = std::max<uint64_t>(w.nseg, dfc::ceil_div(std::max<uint64_t>(n, 1), uint64_t(dfc::kAnsLanes) * 8) + 1);
     w.hist_off = 0;
     w.segbits_off = 1024;
-    w.segoff_off = dfc::align256(w.segbits_off + 4 * w.nseg);
-    w.bytes = dfc::align256(w.segoff_off + 8 * w.nseg);
+    w.segoff_off = dfc::align256(w.segbits_off + 4 * w.slots);
+    w.bytes = dfc::align256(w.segoff_off + 8 * w.slots);
     return w;
 }
 
 dfc_status hip_ok(hipError_t e) { return e == hipSuccess ? DFC_OK : DFC_EHIP; }
+
+// The rANS layout from the device histogram: count pass, scan, section
+// layout and header on the host, write pass, raw bytes.
+dfc_status encode_ans_device(const uint16_t *src_dev, uint64_t n, const dfc_params &p, uint64_t rows, uint64_t cols,
+                             const uint64_t hist[256], uint8_t *dst, uint64_t cap, uint8_t *work, const Workspace &ws,
+                             uint64_t *written, hipStream_t st) {
+    const uint32_t S = dfc::ans_steps_or_default(p.ans_steps);
+    const uint64_t nb = dfc::ceil_div(n, uint64_t(dfc::kAnsLanes) * S);
+    if (nb + 1 > ws.slots) return DFC_ESIZE;
+    uint32_t f[256], cum[256];
+    dfc::ans_frequencies(hist, f, cum);
+    AnsBook book;
+    for (int s = 0; s < 256; ++s) {
+        book.f[s] = uint16_t(f[s]);
+        book.cum[s] = uint16_t(cum[s]);
+        book.magic[s] = f[s] >= 2 ? uint32_t(((uint64_t(1) << 32) + f[s] - 1) / f[s]) : 0u;
+    }
+    AnsArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.src = src_dev;
+    a.n = uint32_t(n);
+    a.steps = S;
+    a.n_blocks = uint32_t(nb);
+    a.counts = reinterpret_cast<uint32_t *>(work + ws.segbits_off);
+    uint64_t *first = reinterpret_cast<uint64_t *>(work + ws.segoff_off);
+    a.first = first;
+    const uint32_t grid = uint32_t(dfc::ceil_div(nb, uint64_t(kAnsEncWaves)));
+    uint64_t nw = 0;
+    if (nb) {
+        hipLaunchKernelGGL(ans_encode_kernel<false>, dim3(grid), dim3(kAnsEncWaves * 64), 0, st, a, book);
+        hipLaunchKernelGGL(segment_scan_kernel, dim3(1), dim3(1024), 0, st, a.counts, nb + 1, first);
+        if (hipMemcpyAsync(&nw, first + nb, sizeof(nw), hipMemcpyDeviceToHost, st) != hipSuccess ||
+            hipStreamSynchronize(st) != hipSuccess)
+            return DFC_EHIP;
+    }
+    if (nw >= (uint64_t(1) << 32)) return DFC_ESIZE;
+    const dfc::SectionSizes sz = dfc::ans_section_sizes(n, nw, nb);
+    uint64_t off[dfc::kNumSections];
+    const uint64_t blob_bytes = dfc::place_sections(sz, off);
+    if (cap < blob_bytes) return DFC_ESIZE;
+    std::vector<uint8_t> head(off[dfc::kTables] + sz.bytes[dfc::kTables], 0);
+    dfc::ans_container_head(head.data(), n, nw, nb, S, rows, cols, sz, off, blob_bytes, f);
+    hipLaunchKernelGGL(fill_zero_u32, dim3(uint32_t(std::min<uint64_t>(65535, dfc::ceil_div(blob_bytes / 4, 256)))),
+                       dim3(256), 0, st, reinterpret_cast<uint32_t *>(dst), blob_bytes / 4);
+    if (hipMemcpyAsync(dst, head.data(), head.size(), hipMemcpyHostToDevice, st) != hipSuccess) return DFC_EHIP;
+    if (nb) {
+        a.words = reinterpret_cast<uint16_t *>(dst + off[dfc::kWords]);
+        a.offsets = reinterpret_cast<uint32_t *>(dst + off[dfc::kOffsets]);
+        a.states = reinterpret_cast<uint32_t *>(dst + off[dfc::kBlockout]);
+        hipLaunchKernelGGL(ans_encode_kernel<true>, dim3(grid), dim3(kAnsEncWaves * 64), 0, st, a, book);
+        hipLaunchKernelGGL(raw_kernel, dim3(uint32_t(std::min<uint64_t>(65535, dfc::ceil_div(n, 256 * 16)))), dim3(256),
+                           0, st, src_dev, n, dst + off[dfc::kRaw]);
+    }
+    if (hipGetLastError() != hipSuccess || hipStreamSynchronize(st) != hipSuccess) return DFC_EHIP;
+    *written = blob_bytes;
+    return DFC_OK;
+}
 
 }  // namespace
 
@@ -234,7 +402,8 @@ dfc_status dfc_encode_device(const uint16_t *src_dev, uint64_t n, const dfc_para
     dfc_params p;
     if (pin) p = *pin; else dfc_default_params(&p);
     if ((!src_dev && n) || !dst_dev || !written || !work_dev || !dfc::encoder_params_ok(p)) return DFC_EINVAL;
-    if (p.layout != DFC_LAYOUT_FLAT) return DFC_EUNSUPPORTED;
+    if (p.layout != DFC_LAYOUT_FLAT && p.layout != DFC_LAYOUT_ANS) return DFC_EUNSUPPORTED;
+    if (p.layout == DFC_LAYOUT_ANS && cb_in) return DFC_EINVAL;  // frequencies come from src's own histogram
     if ((reinterpret_cast<uintptr_t>(dst_dev) & 255u) || (reinterpret_cast<uintptr_t>(work_dev) & 255u) ||
         (reinterpret_cast<uintptr_t>(src_dev) & 1u))
         return DFC_EINVAL;
@@ -260,6 +429,9 @@ dfc_status dfc_encode_device(const uint16_t *src_dev, uint64_t n, const dfc_para
         return DFC_EHIP;
     uint64_t hist[256];
     for (int i = 0; i < 256; ++i) hist[i] = h32[i];
+    if (p.layout == DFC_LAYOUT_ANS)
+        return encode_ans_device(src_dev, n, p, rows, cols, hist, static_cast<uint8_t *>(dst_dev), cap, work, ws,
+                                 written, st);
 
     // 2. codebook, layout, header and tables on the host
     uint8_t len[256];

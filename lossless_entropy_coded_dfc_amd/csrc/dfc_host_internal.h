@@ -71,6 +71,14 @@ void container_header(uint8_t *dst, const dfc_params &p, uint64_t n, uint64_t to
 dfc_status encode_ans(const uint16_t *src, uint64_t n, const dfc_params &p, uint64_t rows, uint64_t cols,
                       uint8_t *dst, uint64_t cap, uint64_t *written);
 uint64_t ans_encode_bound(uint64_t n, uint32_t steps);
+uint32_t ans_steps_or_default(uint32_t s);
+// Frequencies summing to 2^12 from a histogram, and their cumulative sums.
+void ans_frequencies(const uint64_t hist[256], uint32_t f[256], uint32_t cum[256]);
+// Header and tables section of an ANS container (dst zeroed at least up to
+// the end of the tables section).
+void ans_container_head(uint8_t *dst, uint64_t n, uint64_t nw, uint64_t nb, uint32_t S, uint64_t rows,
+                        uint64_t cols, const SectionSizes &sz, const uint64_t off[kNumSections], uint64_t blob_bytes,
+                        const uint32_t f[256]);
 dfc_status ans_blob_info(const uint8_t *b, uint64_t bytes, dfc_info &in);
 
 }  // namespace dfc

@@ -1,6 +1,6 @@
-"""GPU encoder (dfc_encode_device) through the C ABI: its containers must be
-byte-identical to the host encoder's (which the oracle pins byte for byte),
-and decode back to the input."""
+"""GPU encoder (dfc_encode_device) through the C ABI, in the flat and the
+rANS layouts: its containers must be byte-identical to the host encoder's
+(which the oracle pins byte for byte), and decode back to the input."""
 import sys
 
 import numpy as np
@@ -106,4 +106,70 @@ def test_full_size_block_matrices(name_shape):
     out = torch.empty(int(info.n), dtype=torch.int16, device="cuda")
     dfc.decode(d, info, out)
     torch.cuda.synchronize()
+    assert torch.equal(out, dev16(x))
+
+
+# ---------------------------------------------------------------- rANS layout
+
+ANS = dfc.LAYOUT_ANS
+
+
+def ans_same_as_host(x, steps, label=""):
+    say("case ans", label, np.shape(x), "steps", steps)
+    x = np.asarray(x, dtype=np.uint16)
+    shape = x.shape if x.ndim == 2 else None
+    host = dfc.encode(x, shape=shape, layout=ANS, ans_steps=steps)
+    d, size = dfc.encode_device(dev16(x), shape=shape, layout=ANS, ans_steps=steps)
+    got = d[:size].cpu().numpy()
+    assert size == host.size, label
+    assert np.array_equal(got, host), label
+    return got
+
+
+@pytest.mark.parametrize("steps", [8, 64, 512, 1024])
+def test_ans_matches_host_block_sizes(steps):
+    x = synth.gaussian_with_outliers((300, 1000), 0.02, (120, steps))
+    ans_same_as_host(x, steps, label="outliers")
+
+
+@pytest.mark.parametrize("kind", ["uniform", "ladder", "bimodal", "t"])
+def test_ans_matches_host_distributions(kind):
+    shape = (257, 1031)
+    x = {"uniform": lambda: synth.uniform_bits(shape, (121,)),
+         "ladder": lambda: synth.exponent_ladder(shape, (122,)),
+         "bimodal": lambda: synth.bimodal(shape, 0.02, (123,)),
+         "t": lambda: synth.student_t(shape, 3.0, 0.02, (124,))}[kind]()
+    for steps in (16, 256):
+        ans_same_as_host(x, steps, label=kind)
+
+
+def test_ans_edge_sizes_specials_and_one_symbol():
+    for n in (0, 1, 2, 63, 64, 65, 511, 512, 513, 4097):
+        ans_same_as_host(synth.gaussian((n,), 0.02, (125, n)), 8, label=f"n={n}")
+    specials = np.array([0x7FC1, 0xFF81, 0x7F80, 0xFF80, 0x0000, 0x8000, 0x0001, 0x807F], dtype=np.uint16)
+    ans_same_as_host(np.tile(specials, 3001), 64, label="specials")
+    ans_same_as_host(np.full((100, 100), 0x3F80, dtype=np.uint16), 16, label="one symbol (f = 4096)")
+
+
+def test_ans_rejects_external_codebook():
+    x = synth.gaussian((64, 64), 0.02, (126,))
+    book = dfc.build_codebook(cb.histogram(fields.split(x)[0]), 24)
+    with pytest.raises(dfc.DfcError) as ei:
+        dfc.encode_device(dev16(x), codebook=book, shape=(64, 64), layout=ANS)
+    assert ei.value.status == dfc.EINVAL
+
+
+def test_ans_full_size_gate_matrix_and_decode():
+    x = dict(synth.llama3_8b_block())["gate"]
+    say("case ans full gate")
+    d, size = dfc.encode_device(dev16(x), shape=x.shape, layout=ANS, ans_steps=512)
+    host = dfc.encode(x, layout=ANS, ans_steps=512)
+    assert size == host.size
+    assert torch.equal(d[:size], torch.from_numpy(host).cuda())
+    info = dfc.blob_info(host)
+    out = torch.empty(int(info.n), dtype=torch.int16, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dfc.decode(d, info, out, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
     assert torch.equal(out, dev16(x))
