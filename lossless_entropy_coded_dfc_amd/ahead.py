@@ -8,7 +8,10 @@ reused scratch sets, so at most two layers are ever held decompressed.
 
 Ordering uses HIP events only: ``weights(i)`` makes the caller's stream wait
 for layer i's decode, and ``release(i)`` marks the point after which its
-scratch set may be overwritten by the decode of layer i + 2.
+scratch set may be overwritten by the decode of layer i + 2.  The calls must
+come in that order for every layer (prefetch, weights, release); a prefetch
+into a set whose layer has not been released, or weights of a layer that is
+not in its set, raises instead of racing.
 """
 from __future__ import annotations
 
@@ -39,11 +42,16 @@ class DecodeAhead:
         self.ready = [torch.cuda.Event() for _ in range(2)]
         self.free = [torch.cuda.Event() for _ in range(2)]
         self.free_recorded = [False, False]
+        self.held = [None, None]  # layer decoded (or decoding) into each set, until released
         self.status = torch.zeros(1, dtype=torch.int32, device=device)
 
     def prefetch(self, i: int):
         """Enqueue the decode of layer i on the side stream."""
         slot = i % 2
+        if self.held[slot] is not None:
+            raise RuntimeError(f"layer {self.held[slot]} still holds scratch set {slot}: release it before "
+                               f"prefetching layer {i}")
+        self.held[slot] = i
         with self.torch.cuda.stream(self.side):
             if self.free_recorded[slot]:
                 self.side.wait_event(self.free[slot])
@@ -57,6 +65,8 @@ class DecodeAhead:
         """bf16 views of layer i's matrices; the current stream waits for
         their decode."""
         slot = i % 2
+        if self.held[slot] != i:
+            raise RuntimeError(f"layer {i} is not in scratch set {slot} (prefetch it first)")
         self.torch.cuda.current_stream().wait_event(self.ready[slot])
         return [self.scratch[slot][j][: int(info.n)].view(self.torch.bfloat16).view(*shape)
                 for j, (_, info, shape) in enumerate(self.layers[i])]
@@ -64,8 +74,11 @@ class DecodeAhead:
     def release(self, i: int):
         """The current stream is done with layer i's matrices."""
         slot = i % 2
+        if self.held[slot] != i:
+            raise RuntimeError(f"layer {i} is not in scratch set {slot}")
         self.free[slot].record(self.torch.cuda.current_stream())
         self.free_recorded[slot] = True
+        self.held[slot] = None
 
     def corrupt_blocks_seen(self) -> bool:
         """True if any decode so far met a block that failed its check (the

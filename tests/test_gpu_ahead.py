@@ -85,3 +85,29 @@ def test_chained_products_match_resident_weights():
     say("case decode-ahead chained products")
     assert torch.equal(g, h)
     assert not dec.corrupt_blocks_seen()
+
+
+def test_out_of_order_use_raises():
+    """Prefetching into a scratch set whose layer is still held, asking for
+    weights of a layer not in its set, or releasing one twice raises before
+    any decode is enqueued."""
+    from lossless_entropy_coded_dfc_amd.ahead import DecodeAhead
+    layers, originals = make_layers(4, [(64, 256)])
+    dec = DecodeAhead(layers)
+    dec.prefetch(0)
+    dec.prefetch(1)
+    with pytest.raises(RuntimeError):
+        dec.prefetch(2)          # layer 0 still holds set 0
+    with pytest.raises(RuntimeError):
+        dec.weights(2)           # never prefetched
+    w0 = dec.weights(0)[0].view(torch.int16).clone()
+    dec.release(0)
+    with pytest.raises(RuntimeError):
+        dec.release(0)           # already released
+    dec.prefetch(2)              # set 0 is free again
+    w2 = dec.weights(2)[0].view(torch.int16).clone()
+    dec.release(1)
+    dec.release(2)
+    assert torch.equal(w0, torch.from_numpy(originals[0][0].view(np.int16)).cuda())
+    assert torch.equal(w2, torch.from_numpy(originals[2][0].view(np.int16)).cuda())
+    assert not dec.corrupt_blocks_seen()
