@@ -431,3 +431,20 @@ def test_header_is_c99_and_host_abi_links_from_c(tmp_path):
     r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, (r.stdout + r.stderr)[-2000:]
     assert "c abi ok" in r.stdout
+
+
+def test_ans_frequencies_take_back_tie():
+    """The host encoder's frequencies for the hand-worked take-back tie (two
+    equal largest shares, an odd number of units to take back: the smaller
+    symbol gives one more), read from the container it writes."""
+    from oracle import ans as oans
+    h = np.zeros(256, dtype=np.uint64)
+    h[10] = h[20] = 10 ** 6
+    h[100:201] = 1
+    e = np.repeat(np.arange(256, dtype=np.uint16), h.astype(np.int64))
+    x = (e << 7) | np.uint16(0x0011)
+    np.random.default_rng(11).shuffle(x)
+    blob = dfc.encode(x, layout=dfc.LAYOUT_ANS, ans_steps=64)
+    f = oans.parse_ans_blob(bytes(blob))["freqs"]
+    assert int(f[10]) == 1997 and int(f[20]) == 1998
+    assert all(int(f[s]) == 1 for s in range(100, 201)) and int(np.asarray(f).sum()) == 4096

@@ -63,6 +63,26 @@ def test_quantize_hand_cases():
     assert not ans.quantize_freqs(np.zeros(256, dtype=np.uint64)).any()
 
 
+def take_back_tie_histogram():
+    """Two equal large symbols (10 and 20, 10^6 each) and 101 rare ones
+    (100..200, one each): n = 2,000,101; 4096 * 10^6 / n = 2047.90, so both
+    large shares floor to 2047 and the rare ones are raised to 1, summing to
+    4094 + 101 = 4195.  The 99 units of excess are taken one at a time from
+    the largest share, the smaller symbol first on ties: symbol 10 gives on
+    the 1st, 3rd, ... 99th take (50 units), symbol 20 on the others (49)."""
+    h = np.zeros(256, dtype=np.uint64)
+    h[10] = h[20] = 10 ** 6
+    h[100:201] = 1
+    return h
+
+
+def test_quantize_take_back_ties_go_to_the_smaller_symbol():
+    f = ans.quantize_freqs(take_back_tie_histogram())
+    assert int(f[10]) == 2047 - 50 and int(f[20]) == 2047 - 49
+    assert all(int(f[s]) == 1 for s in range(100, 201))
+    assert int(f.sum()) == 4096
+
+
 def test_quantize_is_largest_remainder_when_no_share_rounds_to_zero():
     rng = np.random.default_rng(90)
     for _ in range(200):

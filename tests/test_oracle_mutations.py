@@ -1,0 +1,117 @@
+"""Pin strength: plausible mistakes planted in a copy of the oracle must make
+its pins fail.
+
+Each case copies ``oracle/``, the oracle pin tests and their golden files into
+a temporary folder, changes one expression of the copy (a dropped bit, a
+shifted field, an off-by-one, a reversed tie-break, a flipped sign, a wrong
+index), and runs the pin tests that should notice it against the copy in a
+fresh interpreter.  They must fail (pytest exit status 1); a mutant that
+survives means a pin is missing.  The real oracle is never modified.
+"""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+
+# (name, oracle file, original text, planted text, pin test files)
+MUTANTS = [
+    ("raw byte drops a mantissa bit", "fields.py",
+     "mantissa = (b & 0x7F).astype(np.uint8)", "mantissa = (b & 0x3F).astype(np.uint8)",
+     ["test_oracle_codebook.py", "test_oracle_stream.py"]),
+    ("exponent taken one bit too high", "fields.py",
+     "exponent = ((b >> 7) & 0xFF).astype(np.uint8)", "exponent = ((b >> 8) & 0xFF).astype(np.uint8)",
+     ["test_oracle_codebook.py", "test_oracle_stream.py"]),
+    ("package-merge keeps one item too many", "codebook.py",
+     "chosen = current[: 2 * m - 2]", "chosen = current[: 2 * m - 1]",
+     ["test_oracle_codebook.py"]),
+    ("package-merge runs one round too few", "codebook.py",
+     "for _ in range(max_len - 1):", "for _ in range(max_len - 2):",
+     ["test_oracle_codebook.py"]),
+    ("canonical codes skip a value between lengths", "codebook.py",
+     "code = (code + count[l - 1]) << 1 if l > 1 else 0", "code = (code + count[l - 1] + 1) << 1 if l > 1 else 0",
+     ["test_oracle_codebook.py"]),
+    ("packer writes bits LSB-first", "stream.py",
+     "words[pos >> 5] |= 1 << (31 - (pos & 31))", "words[pos >> 5] |= 1 << (pos & 31)",
+     ["test_oracle_stream.py"]),
+    ("vectorised packer places codes one bit off", "stream.py",
+     "v = c << (np.uint64(64) - r - l.astype(np.uint64))", "v = c << (np.uint64(63) - r - l.astype(np.uint64))",
+     ["test_oracle_stream.py", "test_oracle_blob.py"]),
+    ("chunk offset skips a code starting on the boundary", "stream.py",
+     'idx = np.searchsorted(starts, chunk_first[live], side="left")',
+     'idx = np.searchsorted(starts, chunk_first[live], side="right")',
+     ["test_oracle_stream.py"]),
+    ("block offsets count codes starting on the boundary", "stream.py",
+     'out[:n_blocks] = np.searchsorted(starts, block_first, side="left")',
+     'out[:n_blocks] = np.searchsorted(starts, block_first, side="right")',
+     ["test_oracle_stream.py"]),
+    ("5-bit offset fields bit-reversed", "stream.py",
+     "g = 5 * np.arange(off.size, dtype=np.int64) + k", "g = 5 * np.arange(off.size, dtype=np.int64) + (4 - k)",
+     ["test_oracle_stream.py", "test_oracle_blob.py"]),
+    ("entropy bound drops a raw bit", "blob.py",
+     "return n * (8.0 + cb.entropy_bits(hist)) / 8.0", "return n * (7.0 + cb.entropy_bits(hist)) / 8.0",
+     ["test_oracle_blob.py"]),
+    ("rANS frequencies: larger symbol first on tied remainders", "ans.py",
+     "order = sorted(present, key=lambda s: (-(h[s] * m % total), s))",
+     "order = sorted(present, key=lambda s: (-(h[s] * m % total), -s))",
+     ["test_oracle_ans.py"]),
+    ("rANS frequencies: take back from the larger symbol on ties", "ans.py",
+     "s = max(present, key=lambda t: (f[t], -t))", "s = max(present, key=lambda t: (f[t], t))",
+     ["test_oracle_ans.py"]),
+    ("rANS renormalises one bit early", "ans.py",
+     "if x >= fs << (32 - PROB_BITS):", "if x >= fs << (31 - PROB_BITS):",
+     ["test_oracle_ans.py"]),
+    ("rANS decoder adds the cumulative frequency", "ans.py",
+     "x = int(f[s]) * (x // M) + slot - int(c[s])", "x = int(f[s]) * (x // M) + slot + int(c[s])",
+     ["test_oracle_ans.py"]),
+    ("padded tails filled with zeros", "padded.py",
+     "ones = (np.uint64(1) << gl.astype(np.uint64)) - np.uint64(1)", "ones = np.zeros(gl.shape, dtype=np.uint64)",
+     ["test_oracle_padded.py"]),
+    ("panel order takes rows from the wrong lane bits", "panel.py",
+     "r = r0 + l % 32", "r = r0 + l // 2",
+     ["test_oracle_panel.py"]),
+    ("GEMM reference reverses K", "gemm.py",
+     "return w @ x", "return w @ x[::-1]",
+     ["test_oracle_gemm.py"]),
+]
+
+
+def sandbox(tmp_path, files):
+    """tmp_path/oracle (a copy) and tmp_path/tests (conftest, golden, files)."""
+    ignore = shutil.ignore_patterns("__pycache__", "*.pyc")
+    shutil.copytree(os.path.join(ROOT, "oracle"), tmp_path / "oracle", ignore=ignore)
+    tests = tmp_path / "tests"
+    shutil.copytree(os.path.join(HERE, "golden"), tests / "golden", ignore=ignore)
+    shutil.copy(os.path.join(HERE, "conftest.py"), tests / "conftest.py")
+    for f in files:
+        shutil.copy(os.path.join(HERE, f), tests / f)
+    return tests
+
+
+def run_pins(tmp_path, tests, files):
+    # the copy first, then the repository for the package (seeded generators)
+    env = {**os.environ, "PYTHONPATH": os.pathsep.join([str(tmp_path), ROOT]), "PYTHONDONTWRITEBYTECODE": "1"}
+    return subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider", "-m", "not gpu",
+                           *files], cwd=tests, env=env, capture_output=True, text=True, timeout=600)
+
+
+def test_unmutated_copy_passes(tmp_path):
+    files = ["test_oracle_gemm.py", "test_oracle_panel.py"]
+    r = run_pins(tmp_path, sandbox(tmp_path, files), files)
+    assert r.returncode == 0, (r.stdout + r.stderr)[-3000:]
+
+
+@pytest.mark.parametrize("mutant", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_planted_mistake(tmp_path, mutant):
+    name, fname, old, new, files = mutant
+    tests = sandbox(tmp_path, files)
+    path = tmp_path / "oracle" / fname
+    src = path.read_text()
+    assert src.count(old) == 1, f"{name}: the original text must occur exactly once in oracle/{fname}"
+    path.write_text(src.replace(old, new))
+    r = run_pins(tmp_path, tests, files)
+    assert r.returncode == 1, f"{name}: the pins did not fail (exit {r.returncode})\n" + (r.stdout + r.stderr)[-3000:]
