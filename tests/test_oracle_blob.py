@@ -185,6 +185,24 @@ def test_size_within_two_percent_of_entropy_bound():
         assert 1.0 < ratio < limit
 
 
+@pytest.mark.parametrize("C", [4, 8, 16, 32])
+def test_coded_bytes_closed_form(C):
+    """Coded size = 512-byte header and code lengths + the stream words
+    (n_chunks C bytes plus 4 guard words) + the 5-bit chunk offsets (n_chunks
+    + 1 fields, rounded up to 32-bit words, plus one word of slack) + the
+    block offsets (n_blocks + 1 words) + the raw bytes (n rounded up to 16):
+    written out from n and the chunk and block counts alone."""
+    from lossless_entropy_coded_dfc_amd import synth
+    for n, seed in ((1, 1), (1000, 2), (64 * 1024 + 3, 3)):
+        x = synth.gaussian((n,), 0.02, (150, seed))
+        enc = st.encode(x, C, 64)
+        p = bl.parse_blob(bl.write_blob(enc, 11))
+        nc, nb = enc["n_chunks"], enc["n_blocks"]
+        want = (512 + (nc * C + 16) + 4 * ((5 * (nc + 1) + 31) // 32 + 1) + 4 * (nb + 1)
+                + 16 * ((n + 15) // 16))
+        assert bl.coded_bytes(p) == want, (C, n)
+
+
 def test_one_bit_codes_fill_a_window():
     # one used symbol (plus the phantom) has 1-bit codes: a 12-bit window holds
     # 12 whole codes; the symbol entry keeps the first 4

@@ -77,6 +77,38 @@ MUTANTS = [
     ("GEMM reference reverses K", "gemm.py",
      "return w @ x", "return w @ x[::-1]",
      ["test_oracle_gemm.py"]),
+    ("merge puts the sign one bit low", "fields.py",
+     "return ((sign << 15) | (e << 7) | mantissa).astype(np.uint16)",
+     "return ((sign << 14) | (e << 7) | mantissa).astype(np.uint16)",
+     ["test_oracle_codebook.py", "test_oracle_stream.py"]),
+    ("entropy in nats", "codebook.py",
+     "return float(-(p * np.log2(p)).sum())", "return float(-(p * np.log(p)).sum())",
+     ["test_oracle_codebook.py"]),
+    ("canonical decode accepts a window equal to the limit", "codebook.py",
+     'if window24 < tables["limit"][l]:', 'if window24 <= tables["limit"][l]:',
+     ["test_oracle_codebook.py", "test_oracle_stream.py"]),
+    ("chunk decoder starts from the next chunk's offset", "stream.py",
+     "pos = i * bits + off[:n_chunks]", "pos = i * bits + off[1: n_chunks + 1]",
+     ["test_oracle_stream.py"]),
+    ("rANS cumulative frequencies shifted by one symbol", "ans.py",
+     "c[1:] = np.cumsum(f)[:-1]", "c[1:] = np.cumsum(f)[1:]",
+     ["test_oracle_ans.py"]),
+    ("rANS lanes interleaved in ascending order", "ans.py",
+     "for l in range(lanes - 1, -1, -1):", "for l in range(lanes):",
+     ["test_oracle_ans.py"]),
+    ("panel items column slices first", "panel.py",
+     "for p in range(rows // PANEL_ROWS):\n        for c0 in range(0, cols, panel_k):",
+     "for c0 in range(0, cols, panel_k):\n        for p in range(rows // PANEL_ROWS):",
+     ["test_oracle_panel.py"]),
+    ("boundary mask bit one place too high", "blob.py",
+     "mask |= 1 << (o - 1)", "mask |= 1 << o",
+     ["test_oracle_blob.py"]),
+    ("padded decoder drops a code ending on the chunk end", "padded.py",
+     "if pos + l > end:", "if pos + l >= end:",
+     ["test_oracle_padded.py"]),
+    ("coded size leaves out the chunk offsets", "blob.py",
+     'for nm in ("words", "offsets", "blockout", "raw", "panels"))', 'for nm in ("words", "blockout", "raw", "panels"))',
+     ["test_oracle_blob.py", "test_oracle_stream.py"]),
 ]
 
 
