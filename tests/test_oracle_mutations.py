@@ -106,6 +106,27 @@ MUTANTS = [
     ("padded decoder drops a code ending on the chunk end", "padded.py",
      "if pos + l > end:", "if pos + l >= end:",
      ["test_oracle_padded.py"]),
+    ("rANS slot table stores f instead of f - 1", "ans.py",
+     "t[c[s] + k] = bl.rotate_exponent(s) | ((int(f[s]) - 1) << 8) | (k << 20)",
+     "t[c[s] + k] = bl.rotate_exponent(s) | (int(f[s]) << 8) | (k << 20)",
+     ["test_oracle_ans.py"]),
+    ("padded chunk refuses a code ending on its last bit", "padded.py",
+     'last = int(np.searchsorted(flat_end, flat_start[first] + bits, side="right"))',
+     'last = int(np.searchsorted(flat_end, flat_start[first] + bits, side="left"))',
+     ["test_oracle_padded.py"]),
+    ("an extra block when the chunks fill whole blocks", "stream.py",
+     "blocks = -(-used // lanes)", "blocks = used // lanes + 1",
+     ["test_oracle_stream.py", "test_oracle_blob.py"]),
+    ("canonical limit one code short", "codebook.py",
+     "limit[l] = (first[l] + count[l]) << (MAX_LEN - l)", "limit[l] = (first[l] + count[l] - 1) << (MAX_LEN - l)",
+     ["test_oracle_codebook.py", "test_oracle_stream.py"]),
+    ("panel item table records the block count for the chunk count", "panel.py",
+     "table.append((chunk_base, block_base, bits_q, 0))", "table.append((block_base, block_base, bits_q, 0))",
+     ["test_oracle_panel.py"]),
+    ("panel block offsets count from the item, not the matrix", "panel.py",
+     'outs.append(elem_base + np.searchsorted(starts, first, side="left"))',
+     'outs.append(np.searchsorted(starts, first, side="left"))',
+     ["test_oracle_panel.py"]),
     ("coded size leaves out the chunk offsets", "blob.py",
      'for nm in ("words", "offsets", "blockout", "raw", "panels"))', 'for nm in ("words", "blockout", "raw", "panels"))',
      ["test_oracle_blob.py", "test_oracle_stream.py"]),
