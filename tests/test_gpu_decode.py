@@ -295,3 +295,71 @@ def test_largest_accepted_matrix():
         assert s == dfc.EUNSUPPORTED, layout
         del dev, out
         torch.cuda.empty_cache()
+
+
+def test_concurrent_calls_from_host_threads():
+    """Four host threads, each with its own stream and its own containers
+    (flat, padded, rANS, and a fused product), call the library at the same
+    time, repeatedly; every result is exact (the product against unit
+    vectors).  Launch set-up (the per-kernel LDS limit, the launch knob) is
+    shared process state."""
+    import threading
+    xs = [synth.gaussian_with_outliers((512, 1024), 0.02, (160, i)) for i in range(3)]
+    cfg = [{}, {"layout": dfc.LAYOUT_PADDED}, {"layout": dfc.LAYOUT_ANS, "ans_steps": 64}]
+    jobs = []
+    for x, kw in zip(xs, cfg):
+        b = dfc.encode(x, **kw)
+        jobs.append((torch.from_numpy(b).cuda(), dfc.blob_info(b), torch.from_numpy(x.ravel().view(np.int16)).cuda()))
+    w = synth.gaussian((256, 512), 0.02, (161,))
+    pb = dfc.encode(w, layout=dfc.LAYOUT_PANEL, panel_k=128)
+    pinfo = dfc.blob_info(pb)
+    pdev = torch.from_numpy(pb).cuda()
+    cols = list(range(100, 132))
+    xg = np.zeros((len(cols), 512), dtype=np.uint16)
+    xg[np.arange(len(cols)), cols] = 0x3F80
+    xdev = torch.from_numpy(xg.view(np.int16)).cuda()
+    want = torch.from_numpy(((w[:, cols].T.astype(np.uint32) << 16).view(np.float32)).copy()).cuda()
+    errors = []
+    barrier = threading.Barrier(4)
+
+    def decoder(k):
+        try:
+            dev, info, ref = jobs[k]
+            s = torch.cuda.Stream()
+            out = torch.empty(int(info.n), dtype=torch.int16, device="cuda")
+            st_ = torch.zeros(1, dtype=torch.int32, device="cuda")
+            barrier.wait()
+            for _ in range(20):
+                with torch.cuda.stream(s):
+                    out.fill_(0)
+                    dfc.decode(dev, info, out, st_, stream=s.cuda_stream)
+                s.synchronize()
+                if not torch.equal(out, ref) or int(st_.item()) != 0:
+                    errors.append(f"decoder {k}")
+                    return
+        except Exception as e:  # reported below
+            errors.append(f"decoder {k}: {e!r}")
+
+    def product():
+        try:
+            s = torch.cuda.Stream()
+            y = torch.empty((len(cols), 256), dtype=torch.float32, device="cuda")
+            barrier.wait()
+            for _ in range(20):
+                with torch.cuda.stream(s):
+                    dfc.decode_gemm(pdev, pinfo, xdev, y, stream=s.cuda_stream)
+                s.synchronize()
+                if not torch.equal(y, want):
+                    errors.append("product")
+                    return
+        except Exception as e:
+            errors.append(f"product: {e!r}")
+
+    say("case concurrent host threads")
+    threads = [threading.Thread(target=decoder, args=(k,)) for k in range(3)] + [threading.Thread(target=product)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not any(t.is_alive() for t in threads)
+    assert not errors, errors
