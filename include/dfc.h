@@ -247,21 +247,25 @@ dfc_status dfc_histogram_device(const uint16_t *src_dev, uint64_t n, uint32_t *h
 
 /* Encode n bf16 values already in device memory into a container in device
  * memory, byte-identical to what dfc_encode writes for the same values and
- * parameters (FLAT or ANS layout).  The histogram is taken on the device and
+ * parameters (FLAT, PANEL or ANS layout).  The histogram is taken on the device and
  * read back (the call synchronizes the stream), the code and the container
  * layout are set on the host (FLAT: the stream length is the histogram
  * times the code lengths), and the code bits, chunk offsets, block offsets
  * and raw bytes are written by kernels.  ANS: the frequencies are set on the
  * host, one wavefront per block counts the block's words, their scan is read
  * back to place the sections, and a second pass writes the words, word
- * offsets and states.  The call returns after the stream is idle.
+ * offsets and states.  PANEL: one workgroup per item sums the item's code
+ * bits, the host places the items and the sections, and a second pass packs
+ * every item from its first chunk.  The call returns after the stream is
+ * idle.
  * src_dev: n uint16 (2-byte aligned).  cb: NULL = the data's own code.
  * dst_dev: cap bytes (256-byte aligned), use dfc_encode_bound.
  * work_dev: work_bytes >= dfc_encode_device_workspace(n) (256-byte aligned).
  * *written (host) receives the container size.  Errors: DFC_EINVAL (null or
  * misaligned pointers, bad parameters, an exponent without a code, a
  * codebook with ANS), DFC_ESIZE (cap or workspace too small, n >= 2^32),
- * DFC_EUNSUPPORTED (PANEL or PADDED layout), DFC_EHIP. */
+ * DFC_EUNSUPPORTED (PADDED layout, PANEL items wider than 5.5 M columns),
+ * DFC_EHIP. */
 dfc_status dfc_encode_device(const uint16_t *src_dev, uint64_t n, const dfc_params *p, const dfc_codebook *cb,
                              void *dst_dev, uint64_t cap, void *work_dev, uint64_t work_bytes, uint64_t *written,
                              void *stream);

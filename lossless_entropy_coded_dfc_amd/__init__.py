@@ -304,10 +304,10 @@ def decode_batch(items, status=None, stream=None):
 
 def encode_device(src, chunk_bytes: int = 16, lanes: int = 64, max_code_len: int = 24, lut_bits: int = 11,
                   codebook: Codebook | None = None, shape=None, stream=None, layout: int = LAYOUT_FLAT,
-                  ans_steps: int = 0):
+                  ans_steps: int = 0, panel_k: int = 0):
     """Encode a contiguous 16-bit device tensor (bf16 bits) on the GPU, in the
-    flat or the rANS layout.  Returns (container as a device uint8 tensor, its
-    size in bytes); the container is byte-identical to ``encode``'s."""
+    flat, panel or rANS layout.  Returns (container as a device uint8 tensor,
+    its size in bytes); the container is byte-identical to ``encode``'s."""
     import torch
     n = src.numel()
     if src.element_size() != 2 or not src.is_contiguous():
@@ -316,7 +316,7 @@ def encode_device(src, chunk_bytes: int = 16, lanes: int = 64, max_code_len: int
         shape = tuple(src.shape) if src.dim() == 2 else (1, n)
     p = default_params(chunk_bytes=chunk_bytes, lanes_per_block=lanes, max_code_len=max_code_len,
                        lut_bits=lut_bits, rows=int(shape[0]), cols=int(shape[1]), layout=layout,
-                       ans_steps=ans_steps)
+                       ans_steps=ans_steps, panel_k=panel_k)
     if n == 0:
         p.rows, p.cols = 0, 0
     cap = encode_bound(n, p)

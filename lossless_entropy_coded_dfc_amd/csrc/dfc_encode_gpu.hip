@@ -299,6 +299,105 @@ __global__ __launch_bounds__(256) void raw_kernel(const uint16_t *src, uint64_t 
     }
 }
 
+// ----------------------------------------------------------------- panels
+
+// Panel layout: items of 32 rows x panel_k columns, row panels first; inside
+// an item, element i = 512 t + 8 l + j is W[r0 + l mod 32][c0 + 16 t +
+// 8 (l div 32) + j].  Every item is packed on its own from a fresh chunk.
+struct PanelArgs {
+    const uint16_t *src;
+    uint64_t cols;
+    uint32_t slices, panel_k;
+    uint32_t *item_bits;    // pass 1: code bits per item
+    const uint32_t *first;  // pass 2: (first chunk, first block) per item, n_items + 1 pairs
+    uint32_t *words, *offw, *blockout;
+    uint8_t *raw;
+    uint32_t chunk_bits, lanes;
+};
+
+struct PanelItem {
+    uint64_t row0, col0, e0;
+    uint32_t nq;
+};
+
+__device__ __forceinline__ PanelItem panel_item(const PanelArgs &a, uint32_t q) {
+    PanelItem it;
+    const uint64_t p = q / a.slices;
+    it.row0 = 32ull * p;
+    it.col0 = uint64_t(a.panel_k) * (q % a.slices);
+    it.nq = 32u * uint32_t(min(uint64_t(a.panel_k), a.cols - it.col0));
+    it.e0 = 32ull * (p * a.cols + it.col0);
+    return it;
+}
+
+__device__ __forceinline__ uint16_t panel_elem(const PanelArgs &a, const PanelItem &it, uint32_t i) {
+    const uint32_t t = i >> 9, l = (i >> 3) & 63u, j = i & 7u;
+    return a.src[(it.row0 + (l & 31u)) * a.cols + it.col0 + 16u * t + 8u * (l >> 5) + j];
+}
+
+// One workgroup per item: its code bits.
+__global__ __launch_bounds__(256) void panel_bits_kernel(const PanelArgs a, const Book book) {
+    __shared__ uint32_t sh[kSegThreads];
+    const PanelItem it = panel_item(a, blockIdx.x);
+    uint32_t bits = 0;
+    for (uint32_t i = threadIdx.x; i < it.nq; i += kSegThreads) bits += book.len[exponent_of(panel_elem(a, it, i))];
+    uint32_t total;
+    block_exclusive_scan(bits, sh, total);
+    if (threadIdx.x == 0) a.item_bits[blockIdx.x] = total;
+}
+
+// One workgroup per item: thread t packs elements [i0, i1) of the item at
+// its bit position (interior words stored, the two words shared with
+// neighbours ORed), writes their raw bytes, and, for every chunk of the item
+// whose first bit its codes cover, that chunk's 5-bit offset (the next code
+// starts where the covering code ends) and, on block boundaries, the block's
+// first element (panel order).
+__global__ __launch_bounds__(256) void panel_pack_kernel(const PanelArgs a, const Book book) {
+    __shared__ uint32_t sh[kSegThreads];
+    const uint32_t q = blockIdx.x;
+    const PanelItem it = panel_item(a, q);
+    const uint32_t per = (it.nq + kSegThreads - 1) / kSegThreads;
+    const uint32_t i0 = min(threadIdx.x * per, it.nq), i1 = min(i0 + per, it.nq);
+    uint32_t bits = 0;
+    for (uint32_t i = i0; i < i1; ++i) bits += book.len[exponent_of(panel_elem(a, it, i))];
+    uint32_t total;
+    const uint64_t start = block_exclusive_scan(bits, sh, total);
+    const uint32_t c0 = a.first[2 * q], b0 = a.first[2 * q + 1];
+    const uint32_t chunks = a.first[2 * q + 2] - c0;
+    if (threadIdx.x == 0) a.blockout[b0] = uint32_t(it.e0);
+    uint32_t *words = a.words + uint64_t(c0) * (a.chunk_bits / 32);
+    uint64_t pos = start, acc = 0;
+    uint32_t nacc = uint32_t(pos & 31);
+    uint64_t w = pos >> 5;
+    const uint64_t first_word = w, last_word = bits ? (start + bits - 1) >> 5 : w;
+    for (uint32_t i = i0; i < i1; ++i) {
+        const uint16_t b = panel_elem(a, it, i);
+        a.raw[it.e0 + i] = uint8_t(raw_of(b));
+        const uint32_t e = exponent_of(b);
+        const uint32_t l = book.len[e];
+        const uint64_t c = pos / a.chunk_bits + 1;
+        if (c < chunks && c * a.chunk_bits <= pos + l) {
+            const uint32_t off = uint32_t(pos + l - c * a.chunk_bits);
+            const uint64_t g = 5ull * (c0 + c);
+            const uint64_t v = uint64_t(off) << (g & 31);
+            or_word(a.offw, g >> 5, uint32_t(v));
+            or_word(a.offw, (g >> 5) + 1, uint32_t(v >> 32));
+            if (c % a.lanes == 0) a.blockout[b0 + c / a.lanes] = uint32_t(it.e0 + i + 1);
+        }
+        acc = (acc << l) | book.code[e];
+        nacc += l;
+        pos += l;
+        if (nacc >= 32) {
+            nacc -= 32;
+            const uint32_t v = uint32_t(acc >> nacc);
+            if (w == first_word || w == last_word) or_word(words, w, v);
+            else words[w] = v;
+            ++w;
+        }
+    }
+    if (nacc > 0) or_word(words, w, uint32_t(acc << (32 - nacc)));
+}
+
 // Host copy of a workspace layout.
 // segbits/segoff hold one entry per 4096-element segment (FLAT) or per rANS
 // block plus one (the smallest rANS block is 64 x 8 elements).
@@ -375,6 +474,80 @@ dfc_status encode_ans_device(const uint16_t *src_dev, uint64_t n, const dfc_para
     return DFC_OK;
 }
 
+// The panel layout from the device histogram and the code: bits per item,
+// item placement and sections on the host, then every item packed on the
+// device.
+dfc_status encode_panel_device(const uint16_t *src_dev, uint64_t n, const dfc_params &p, const Book &book,
+                               const uint8_t len[256], uint8_t *dst, uint64_t cap, uint8_t *work,
+                               const Workspace &ws, uint64_t *written, hipStream_t st) {
+    dfc::PanelGeom g;
+    if (!dfc::panel_geom(p.rows, p.cols, p.panel_k, g) || g.rows * g.cols != n) return DFC_EINVAL;
+    // item bit counts are 32-bit on the device
+    if (32ull * std::min<uint64_t>(g.panel_k, g.cols) * dfc::kMaxLen >= (uint64_t(1) << 32)) return DFC_EUNSUPPORTED;
+    if (g.n_items + 1 > ws.slots) return DFC_ESIZE;
+    const uint32_t C = p.chunk_bytes, T = p.lanes_per_block;
+    PanelArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.src = src_dev;
+    a.cols = g.cols;
+    a.slices = uint32_t(g.slices);
+    a.panel_k = uint32_t(g.panel_k);
+    a.item_bits = reinterpret_cast<uint32_t *>(work + ws.segbits_off);
+    a.chunk_bits = 8u * C;
+    a.lanes = T;
+    hipLaunchKernelGGL(panel_bits_kernel, dim3(uint32_t(g.n_items)), dim3(kSegThreads), 0, st, a, book);
+    std::vector<uint32_t> bits(g.n_items);
+    if (hipMemcpyAsync(bits.data(), a.item_bits, 4 * g.n_items, hipMemcpyDeviceToHost, st) != hipSuccess ||
+        hipStreamSynchronize(st) != hipSuccess)
+        return DFC_EHIP;
+    std::vector<uint32_t> first(2 * (g.n_items + 1), 0);
+    uint64_t chunks = 0, blocks = 0, total_bits = 0;
+    for (uint64_t q = 0; q < g.n_items; ++q) {
+        first[2 * q] = uint32_t(chunks);
+        first[2 * q + 1] = uint32_t(blocks);
+        const uint64_t cq = dfc::ceil_div(uint64_t(bits[q]), 8ull * C);
+        chunks += cq;
+        blocks += dfc::ceil_div(cq, uint64_t(T));
+        total_bits += bits[q];
+        if (chunks >= (uint64_t(1) << 32) || blocks >= (uint64_t(1) << 32)) return DFC_ESIZE;
+    }
+    first[2 * g.n_items] = uint32_t(chunks);
+    first[2 * g.n_items + 1] = uint32_t(blocks);
+    const dfc::SectionSizes sz = dfc::section_sizes(n, chunks, blocks, C, p.lut_bits, g.n_items);
+    uint64_t off[dfc::kNumSections];
+    const uint64_t blob_bytes = dfc::place_sections(sz, off);
+    if (cap < blob_bytes) return DFC_ESIZE;
+    std::vector<uint8_t> head(off[dfc::kTables] + sz.bytes[dfc::kTables], 0);
+    dfc::container_header(head.data(), p, n, total_bits, chunks, blocks, g.rows, g.cols, sz, off, blob_bytes, len);
+    // the item table: (first chunk, first block, code bits, 0) per item and a sentinel
+    std::vector<uint32_t> table(4 * (g.n_items + 1), 0);
+    for (uint64_t q = 0; q <= g.n_items; ++q) {
+        table[4 * q] = first[2 * q];
+        table[4 * q + 1] = first[2 * q + 1];
+        table[4 * q + 2] = q < g.n_items ? bits[q] : 0u;
+    }
+    const uint32_t n_out = uint32_t(n);
+    uint32_t *first_dev = reinterpret_cast<uint32_t *>(work + ws.segoff_off);
+    hipLaunchKernelGGL(fill_zero_u32, dim3(uint32_t(std::min<uint64_t>(65535, dfc::ceil_div(blob_bytes / 4, 256)))),
+                       dim3(256), 0, st, reinterpret_cast<uint32_t *>(dst), blob_bytes / 4);
+    if (hipMemcpyAsync(dst, head.data(), head.size(), hipMemcpyHostToDevice, st) != hipSuccess ||
+        hipMemcpyAsync(dst + off[dfc::kPanels], table.data(), 4 * table.size(), hipMemcpyHostToDevice, st) !=
+            hipSuccess ||
+        hipMemcpyAsync(dst + off[dfc::kBlockout] + 4 * blocks, &n_out, 4, hipMemcpyHostToDevice, st) != hipSuccess ||
+        hipMemcpyAsync(first_dev, first.data(), 4 * first.size(), hipMemcpyHostToDevice, st) != hipSuccess)
+        return DFC_EHIP;
+    a.first = first_dev;
+    a.words = reinterpret_cast<uint32_t *>(dst + off[dfc::kWords]);
+    a.offw = reinterpret_cast<uint32_t *>(dst + off[dfc::kOffsets]);
+    a.blockout = reinterpret_cast<uint32_t *>(dst + off[dfc::kBlockout]);
+    a.raw = dst + off[dfc::kRaw];
+    hipLaunchKernelGGL(panel_pack_kernel, dim3(uint32_t(g.n_items)), dim3(kSegThreads), 0, st, a, book);
+    // the host vectors must outlive the copies above
+    if (hipGetLastError() != hipSuccess || hipStreamSynchronize(st) != hipSuccess) return DFC_EHIP;
+    *written = blob_bytes;
+    return DFC_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -402,7 +575,8 @@ dfc_status dfc_encode_device(const uint16_t *src_dev, uint64_t n, const dfc_para
     dfc_params p;
     if (pin) p = *pin; else dfc_default_params(&p);
     if ((!src_dev && n) || !dst_dev || !written || !work_dev || !dfc::encoder_params_ok(p)) return DFC_EINVAL;
-    if (p.layout != DFC_LAYOUT_FLAT && p.layout != DFC_LAYOUT_ANS) return DFC_EUNSUPPORTED;
+    if (p.layout == DFC_LAYOUT_PADDED) return DFC_EUNSUPPORTED;
+    if (p.layout == DFC_LAYOUT_PANEL && !p.panel_k) p.panel_k = DFC_PANEL_K_DEFAULT;
     if (p.layout == DFC_LAYOUT_ANS && cb_in) return DFC_EINVAL;  // frequencies come from src's own histogram
     if ((reinterpret_cast<uintptr_t>(dst_dev) & 255u) || (reinterpret_cast<uintptr_t>(work_dev) & 255u) ||
         (reinterpret_cast<uintptr_t>(src_dev) & 1u))
@@ -450,6 +624,9 @@ dfc_status dfc_encode_device(const uint16_t *src_dev, uint64_t n, const dfc_para
     Book book;
     dfc::canonical_codes(len, book.code);
     std::memcpy(book.len, len, 256);
+    if (p.layout == DFC_LAYOUT_PANEL)
+        return encode_panel_device(src_dev, n, p, book, len, static_cast<uint8_t *>(dst_dev), cap, work, ws, written,
+                                   st);
     uint64_t total_bits = 0;
     for (int i = 0; i < 256; ++i) total_bits += hist[i] * len[i];
     const uint32_t C = p.chunk_bytes, T = p.lanes_per_block;

@@ -1,4 +1,4 @@
-"""GPU encoder (dfc_encode_device) through the C ABI, in the flat and the
+"""GPU encoder (dfc_encode_device) through the C ABI, in the flat, panel and
 rANS layouts: its containers must be byte-identical to the host encoder's
 (which the oracle pins byte for byte), and decode back to the input."""
 import sys
@@ -173,3 +173,48 @@ def test_ans_full_size_gate_matrix_and_decode():
     torch.cuda.synchronize()
     assert int(status.item()) == 0
     assert torch.equal(out, dev16(x))
+
+
+# --------------------------------------------------------------- panel layout
+
+PANEL = dfc.LAYOUT_PANEL
+
+
+@pytest.mark.parametrize("shape,panel_k,C", [
+    ((64, 1040), 1024, 16),     # a narrow last slice (16 columns)
+    ((96, 272), 64, 4),         # five slices, the last one 16 wide
+    ((128, 512), 512, 8),       # one item per panel
+    ((32, 48), 16, 32),         # one-sub-tile items
+    ((256, 4096), 256, 16),
+])
+def test_panel_matches_host(shape, panel_k, C):
+    x = synth.gaussian_with_outliers(shape, 0.02, (180, shape[0], panel_k))
+    say("case panel", shape, "panel_k", panel_k, "C", C)
+    host = dfc.encode(x, chunk_bytes=C, layout=PANEL, panel_k=panel_k)
+    d, size = dfc.encode_device(dev16(x), chunk_bytes=C, shape=shape, layout=PANEL, panel_k=panel_k)
+    assert size == host.size
+    assert np.array_equal(d[:size].cpu().numpy(), host)
+
+
+@pytest.mark.parametrize("kind", ["uniform", "ladder"])
+def test_panel_matches_host_distributions_and_codebook(kind):
+    shape = (96, 1024)
+    x = {"uniform": lambda: synth.uniform_bits(shape, (181,)),
+         "ladder": lambda: synth.exponent_ladder(shape, (182,))}[kind]()
+    host = dfc.encode(x, layout=PANEL, panel_k=256)
+    d, size = dfc.encode_device(dev16(x), shape=shape, layout=PANEL, panel_k=256)
+    assert size == host.size and np.array_equal(d[:size].cpu().numpy(), host), kind
+    g = synth.gaussian((512, 512), 0.02, (183,))
+    book = dfc.build_codebook(cb.histogram(fields.split(g)[0]) + 1, 24)
+    host = dfc.encode(x, layout=PANEL, panel_k=256, codebook=book)
+    d, size = dfc.encode_device(dev16(x), shape=shape, layout=PANEL, panel_k=256, codebook=book)
+    assert size == host.size and np.array_equal(d[:size].cpu().numpy(), host), kind + " foreign codebook"
+
+
+def test_panel_full_size_gemm_matrix():
+    w = synth.gemm_weight()
+    say("case panel full 28672 x 8192")
+    d, size = dfc.encode_device(dev16(w), shape=w.shape, layout=PANEL)
+    host = dfc.encode(w, layout=PANEL)
+    assert size == host.size
+    assert torch.equal(d[:size], torch.from_numpy(host).cuda())
