@@ -348,7 +348,8 @@ def decode_gemm(blob_dev, info: Info, x, y, status=None, stream=None):
     if x.dim() != 2 or y.dim() != 2 or not x.is_contiguous() or not y.is_contiguous():
         raise ValueError("x and y must be contiguous 2-D tensors")
     B, K = x.shape
-    if x.element_size() != 2 or K != info.cols or tuple(y.shape) != (B, info.rows) or y.element_size() != 4:
+    import torch
+    if x.element_size() != 2 or K != info.cols or tuple(y.shape) != (B, info.rows) or y.dtype != torch.float32:
         raise ValueError("x must be (B, K) 16-bit and y (B, M) float32 for the container's M x K")
     _check(library().dfc_decode_gemm(ctypes.c_void_p(_blob_ptr(blob_dev, info)), ctypes.byref(info),
                                      ctypes.c_void_p(_dev_ptr(x)), B, ctypes.c_void_p(_dev_ptr(y)),

@@ -184,6 +184,8 @@ def test_invalid_arguments():
     with pytest.raises(dfc.DfcError) as ei:
         dfc.decode_gemm(dev, info, x, y)
     assert ei.value.status == dfc.EINVAL
+    with pytest.raises(ValueError):   # Y must be float32
+        dfc.decode_gemm(dev, info, x[:4], torch.zeros((4, 64), dtype=torch.int32, device="cuda"))
     flat = dfc.encode(w)
     finfo = dfc.blob_info(flat)
     with pytest.raises(ValueError):
