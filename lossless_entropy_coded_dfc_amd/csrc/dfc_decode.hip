@@ -244,11 +244,14 @@ __global__ __launch_bounds__(1024, Occupancy<C>::kWavesPerSimd) void dfc_decode_
         // the block index is the same in every lane
         b = __builtin_amdgcn_readfirstlane(b);
         const BlockRange br = block_range(s_out, e_out);
-        // raw bytes of this block's first PF octets per lane
+        // raw bytes of this block's first PF octets per lane (rounds past the
+        // block's last octet load nothing)
         u32x2 R[PF];
 #pragma unroll
         for (int j = 0; j < PF; ++j)
-            R[j] = __builtin_amdgcn_raw_buffer_load_b64(bf.raw, 8u * (br.h0 + lane + uint32_t(kWave * j)), 0, 0);
+            R[j] = uint32_t(kWave * j) < br.nh
+                       ? __builtin_amdgcn_raw_buffer_load_b64(bf.raw, 8u * (br.h0 + lane + uint32_t(kWave * j)), 0, 0)
+                       : u32x2{0u, 0u};
         // next block's stream words, offsets and output range
         const uint32_t bn = b + waves;
         const bool more = bn < hi_b;

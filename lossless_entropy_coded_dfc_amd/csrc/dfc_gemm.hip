@@ -94,10 +94,13 @@ __device__ __forceinline__ bool gemm_item(const GemmArgs &g, uint32_t q, const T
         const uint32_t ci = (b - b0) * kWave + lane;  // item-relative chunk
         Chunk<C> ck;
         load_chunk<C>(words, offw, c0 + ci, ck);
+        // rounds past the block's last sub-tile load nothing
+        const uint32_t rounds = (lead + total_want + 511u) >> 9;
         u32x2 R[PF];
 #pragma unroll
         for (int j = 0; j < PF; ++j)
-            R[j] = __builtin_amdgcn_raw_buffer_load_b64(raw, e0 + base + 512u * j + 8u * lane, 0, 0);
+            R[j] = uint32_t(j) < rounds ? __builtin_amdgcn_raw_buffer_load_b64(raw, e0 + base + 512u * j + 8u * lane, 0, 0)
+                                        : u32x2{0u, 0u};
         int start, end;
         chunk_span<C>(ck, c0 + ci,
                       int(min(max(int64_t(bits) - int64_t(ci) * (8 * C), int64_t(-1)), int64_t(8 * C + 32))),
