@@ -14,7 +14,8 @@
 // steps consumes at most 512 words, so the ring is refilled only between
 // rounds, 512 words at a time from registers loaded one refill ahead: the
 // loop waits for a word load only there, and the eight steps of a round run
-// with no memory waits.  Only a block's last step tests which lanes take
+// with no memory waits.  Word and raw-byte loads stop at the block's end, so
+// no block fetches another's bytes.  Only a block's last step tests which lanes take
 // part.  The
 // step's 64 exponent bytes go to an LDS stage; every 8 steps the stage holds
 // 512 consecutive exponents, which the lanes merge with the raw bytes (loaded
@@ -102,6 +103,15 @@ __global__ __launch_bounds__(kAnsWaves * kWave) void dfc_ans_kernel(const AnsBat
     // multiple of 8; pend: words [base + kRing, base + kRing + kSeg), eight
     // per lane
     uint32_t base = w_begin & ~7u, off = w_begin & 7u;
+    // eight words from word w on; none (zeros, no memory access) from the
+    // block's end on, so the ring never reads the next block's words
+    auto load8 = [&](uint32_t w) {
+        return __builtin_amdgcn_raw_buffer_load_b128(words, w < w_end ? 2u * w : kNowhere, 0, 0);
+    };
+    // raw bytes of the octet at block-relative element q; none past the block
+    auto load_raw = [&](uint32_t q) {
+        return __builtin_amdgcn_raw_buffer_load_b64(raw, q < cnt ? e0 + q : kNowhere, 0, 0);
+    };
     // eight words at ring slot p (a multiple of 8), and their mirror
     auto put8 = [&](uint32_t p, const u32x4 &v) {
         *reinterpret_cast<u32x4 *>(ring + p) = v;
@@ -109,14 +119,13 @@ __global__ __launch_bounds__(kAnsWaves * kWave) void dfc_ans_kernel(const AnsBat
     };
 #pragma unroll
     for (uint32_t q = 0; q < kRing; q += kSeg)
-        put8((base + q + 8u * lane) & (kRing - 1u),
-             __builtin_amdgcn_raw_buffer_load_b128(words, 2u * (base + q) + 16u * lane, 0, 0));
-    u32x4 pend = __builtin_amdgcn_raw_buffer_load_b128(words, 2u * (base + kRing) + 16u * lane, 0, 0);
+        put8((base + q + 8u * lane) & (kRing - 1u), load8(base + q + 8u * lane));
+    u32x4 pend = load8(base + kRing + 8u * lane);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     // raw bytes of the first round's octet (512 elements per round)
-    u32x2 R = __builtin_amdgcn_raw_buffer_load_b64(raw, e0 + 8u * lane, 0, 0);
+    u32x2 R = load_raw(8u * lane);
 
     // One step: every lane decodes its element of step i.  Only the block's
     // last step can be partial, so only it tests which lanes take part.
@@ -162,7 +171,7 @@ __global__ __launch_bounds__(kAnsWaves * kWave) void dfc_ans_kernel(const AnsBat
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        R = __builtin_amdgcn_raw_buffer_load_b64(raw, e0 + 512u * (r + 1u) + 8u * lane, 0, 0);
+        R = load_raw(512u * (r + 1u) + 8u * lane);
     };
 
     // Whole rounds: eight steps consume at most 512 words, so the ring (which
@@ -189,7 +198,7 @@ __global__ __launch_bounds__(kAnsWaves * kWave) void dfc_ans_kernel(const AnsBat
             put8((base + kRing + 8u * lane) & (kRing - 1u), pend);
             base += kSeg;
             off -= kSeg;
-            pend = __builtin_amdgcn_raw_buffer_load_b128(words, 2u * (base + kRing) + 16u * lane, 0, 0);
+            pend = load8(base + kRing + 8u * lane);
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
