@@ -125,7 +125,9 @@ __device__ __forceinline__ bool gemm_item(const GemmArgs &g, uint32_t q, const T
 
         __builtin_amdgcn_s_setprio(0);
         // Complete sub-tiles: W operand from the staged exponents and the
-        // raw bytes, X operand from global memory (cached).
+        // raw bytes, X operand from global memory (cached); the X fragments of
+        // all column tiles are requested before their products, so that their
+        // cache round trips overlap (1-2% at 64 columns).
         const uint32_t extent = lead + total;
         const uint32_t nfull = extent >> 9;
         const uint32_t kcol = col0 + 16u * (base >> 9);
@@ -134,24 +136,26 @@ __device__ __forceinline__ bool gemm_item(const GemmArgs &g, uint32_t q, const T
             if (uint32_t(j) < nfull) {
                 const u32x2 E = *reinterpret_cast<const u32x2 *>(stage + 512u * j + 8u * lane);
                 const bf16x8 A = as_bf16x8(assemble8(E, R[j]));
+                u32x4 X[NT];
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    const u32x4 X = __builtin_amdgcn_raw_buffer_load_b128(
-                        xr, xcol + 2u * (32u * nt * g.cols + kcol + 16u * j), 0, 0);
-                    acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, as_bf16x8(X), acc[nt], 0, 0, 0);
-                }
+                for (int nt = 0; nt < NT; ++nt)
+                    X[nt] = __builtin_amdgcn_raw_buffer_load_b128(xr, xcol + 2u * (32u * nt * g.cols + kcol + 16u * j), 0, 0);
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+                    acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, as_bf16x8(X[nt]), acc[nt], 0, 0, 0);
             }
         }
         for (uint32_t j = PF; j < nfull; ++j) {
             const u32x2 Rj = __builtin_amdgcn_raw_buffer_load_b64(raw, e0 + base + 512u * j + 8u * lane, 0, 0);
             const u32x2 E = *reinterpret_cast<const u32x2 *>(stage + 512u * j + 8u * lane);
             const bf16x8 A = as_bf16x8(assemble8(E, Rj));
+            u32x4 X[NT];
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                const u32x4 X =
-                    __builtin_amdgcn_raw_buffer_load_b128(xr, xcol + 2u * (32u * nt * g.cols + kcol + 16u * j), 0, 0);
-                acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, as_bf16x8(X), acc[nt], 0, 0, 0);
-            }
+            for (int nt = 0; nt < NT; ++nt)
+                X[nt] = __builtin_amdgcn_raw_buffer_load_b128(xr, xcol + 2u * (32u * nt * g.cols + kcol + 16u * j), 0, 0);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, as_bf16x8(X[nt]), acc[nt], 0, 0, 0);
         }
         // The sub-tile this block only began moves to the next block.
         const uint32_t tail = extent - 512u * nfull;
