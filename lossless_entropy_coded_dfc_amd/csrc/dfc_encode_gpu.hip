@@ -340,30 +340,45 @@ __global__ __launch_bounds__(kAnsEncWaves * 64) void ans_encode_kernel(const Ans
         base = a.first[b];
         last = uint32_t(a.first[b + 1] - base) - 1u;  // unused when the block has no words
     }
-    for (uint32_t i = steps; i-- > 0;) {
-        const uint32_t j = 64u * i + lane;
-        const bool live = j < cnt;
-        const uint32_t sym = live ? (uint32_t(a.src[e0 + j]) >> 7) & 0xFFu : 0u;
-        const uint32_t e = fc[sym], f = e & 0xFFFFu, cum = e >> 16;
-        // x >= f 2^20, without forming f << 20 (2^32 for a lone symbol)
-        const bool emit = live && (x >> 20) >= f;
-        const uint64_t m = __builtin_amdgcn_ballot_w64(emit);
-        if constexpr (Write) {
-            if (emit) {
-                const uint32_t above = uint32_t(__builtin_popcountll(lane == 63 ? 0ull : m >> (lane + 1)));
-                a.words[base + (last - emitted - above)] = uint16_t(x & 0xFFFFu);
+    // Steps run from the block's last to its first, eight at a time: the eight
+    // symbols are loaded first (independent loads in flight together), then
+    // the eight dependent state updates run.
+    for (uint32_t top = steps; top > 0;) {
+        const uint32_t g = min(top, 8u);
+        uint32_t syms[8];
+#pragma unroll
+        for (uint32_t k = 0; k < 8; ++k) {
+            const uint32_t j = 64u * (top - 1u - k) + lane;
+            syms[k] = k < g && j < cnt ? (uint32_t(a.src[e0 + j]) >> 7) & 0xFFu : 0u;
+        }
+#pragma unroll
+        for (uint32_t k = 0; k < 8; ++k) {
+            if (k >= g) break;
+            const uint32_t j = 64u * (top - 1u - k) + lane;
+            const bool live = j < cnt;
+            const uint32_t sym = syms[k];
+            const uint32_t e = fc[sym], f = e & 0xFFFFu, cum = e >> 16;
+            // x >= f 2^20, without forming f << 20 (2^32 for a lone symbol)
+            const bool emit = live && (x >> 20) >= f;
+            const uint64_t m = __builtin_amdgcn_ballot_w64(emit);
+            if constexpr (Write) {
+                if (emit) {
+                    const uint32_t above = uint32_t(__builtin_popcountll(lane == 63 ? 0ull : m >> (lane + 1)));
+                    a.words[base + (last - emitted - above)] = uint16_t(x & 0xFFFFu);
+                }
             }
+            const uint32_t v = emit ? x >> 16 : x;
+            // q = v / f, r = v mod f
+            uint32_t q = f == 1u ? v : __umulhi(v, mg[sym]);
+            uint32_t r = v - q * f;
+            if (r >= f) {  // q was one too large
+                --q;
+                r += f;
+            }
+            if (live) x = q * uint32_t(dfc::kAnsSlots) + r + cum;
+            emitted += uint32_t(__builtin_popcountll(m));
         }
-        const uint32_t v = emit ? x >> 16 : x;
-        // q = v / f, r = v mod f
-        uint32_t q = f == 1u ? v : __umulhi(v, mg[sym]);
-        uint32_t r = v - q * f;
-        if (r >= f) {  // q was one too large
-            --q;
-            r += f;
-        }
-        if (live) x = q * uint32_t(dfc::kAnsSlots) + r + cum;
-        emitted += uint32_t(__builtin_popcountll(m));
+        top -= g;
     }
     if constexpr (!Write) {
         if (lane == 0) {
@@ -384,9 +399,11 @@ __global__ __launch_bounds__(256) void raw_kernel(const uint16_t *src, uint64_t 
     for (uint64_t j0 = (uint64_t(blockIdx.x) * blockDim.x + threadIdx.x) * 16; j0 < n;
          j0 += uint64_t(gridDim.x) * blockDim.x * 16) {
         if (j0 + 16 <= n) {
+            uint16_t b[16];
+            load16(src, n, j0, b);
             uint32_t r[4] = {0, 0, 0, 0};
 #pragma unroll
-            for (uint32_t q = 0; q < 16; ++q) r[q >> 2] |= raw_of(src[j0 + q]) << (8 * (q & 3));
+            for (uint32_t q = 0; q < 16; ++q) r[q >> 2] |= raw_of(b[q]) << (8 * (q & 3));
             *reinterpret_cast<uint4 *>(raw + j0) = make_uint4(r[0], r[1], r[2], r[3]);
         } else {
             for (uint64_t j = j0; j < n; ++j) raw[j] = uint8_t(raw_of(src[j]));
@@ -425,10 +442,25 @@ __device__ __forceinline__ PanelItem panel_item(const PanelArgs &a, uint32_t q) 
     return it;
 }
 
-__device__ __forceinline__ uint16_t panel_elem(const PanelArgs &a, const PanelItem &it, uint32_t i) {
-    const uint32_t t = i >> 9, l = (i >> 3) & 63u, j = i & 7u;
-    return a.src[(it.row0 + (l & 31u)) * a.cols + it.col0 + 16u * t + 8u * (l >> 5) + j];
+// Octet o of an item (its values 8 o .. 8 o + 7 in panel order) is eight
+// consecutive columns of one row (columns and slice widths are multiples of
+// 16): one 16-byte load when the source is 16-byte aligned.
+__device__ __forceinline__ uint4 panel_octet(const PanelArgs &a, const PanelItem &it, uint32_t o, bool vec) {
+    const uint32_t t = o >> 6, l = o & 63u;
+    const uint64_t at = (it.row0 + (l & 31u)) * a.cols + it.col0 + 16u * t + 8u * (l >> 5);
+    if (vec) return *reinterpret_cast<const uint4 *>(a.src + at);
+    uint32_t w[4];
+#pragma unroll
+    for (uint32_t k = 0; k < 4; ++k) w[k] = uint32_t(a.src[at + 2 * k]) | (uint32_t(a.src[at + 2 * k + 1]) << 16);
+    return make_uint4(w[0], w[1], w[2], w[3]);
 }
+
+__device__ __forceinline__ uint32_t octet_value(const uint4 &v, uint32_t j) {
+    const uint32_t w = j < 2 ? v.x : j < 4 ? v.y : j < 6 ? v.z : v.w;
+    return (w >> (16 * (j & 1))) & 0xFFFFu;
+}
+
+constexpr uint32_t kOctBatch = 4;  // octets loaded together (independent loads in flight)
 
 // One workgroup per item: its code bits.
 __global__ __launch_bounds__(256) void panel_bits_kernel(const PanelArgs a, const Book book) {
@@ -436,29 +468,53 @@ __global__ __launch_bounds__(256) void panel_bits_kernel(const PanelArgs a, cons
     __shared__ BookLds bk;
     stage_book(book, bk);
     const PanelItem it = panel_item(a, blockIdx.x);
+    const bool vec = (reinterpret_cast<uintptr_t>(a.src) & 15u) == 0;
+    const uint32_t n_oct = it.nq / 8;
     uint32_t bits = 0;
-    for (uint32_t i = threadIdx.x; i < it.nq; i += kSegThreads) bits += bk.len[exponent_of(panel_elem(a, it, i))];
+    for (uint32_t ob = threadIdx.x; ob < n_oct; ob += kSegThreads * kOctBatch) {
+        uint4 v[kOctBatch];
+#pragma unroll
+        for (uint32_t k = 0; k < kOctBatch; ++k)
+            v[k] = ob + k * kSegThreads < n_oct ? panel_octet(a, it, ob + k * kSegThreads, vec) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (uint32_t k = 0; k < kOctBatch; ++k)
+            if (ob + k * kSegThreads < n_oct)
+#pragma unroll
+                for (uint32_t j = 0; j < 8; ++j) bits += bk.len[exponent_of(octet_value(v[k], j))];
+    }
     uint32_t total;
     block_exclusive_scan(bits, sh, total);
     if (threadIdx.x == 0) a.item_bits[blockIdx.x] = total;
 }
 
-// One workgroup per item: thread t packs elements [i0, i1) of the item at
-// its bit position (interior words stored, the two words shared with
-// neighbours ORed), writes their raw bytes, and, for every chunk of the item
-// whose first bit its codes cover, that chunk's 5-bit offset (the next code
-// starts where the covering code ends) and, on block boundaries, the block's
-// first element (panel order).
+// One workgroup per item: thread t packs a contiguous run of the item's
+// octets at its bit position (interior words stored, the two words shared
+// with neighbours ORed), writes their raw bytes (8 per octet), and, for
+// every chunk of the item whose first bit its codes cover, that chunk's
+// 5-bit offset (the next code starts where the covering code ends) and, on
+// block boundaries, the block's first element (panel order).
 __global__ __launch_bounds__(256) void panel_pack_kernel(const PanelArgs a, const Book book) {
     __shared__ uint32_t sh[kSegThreads];
     __shared__ BookLds bk;
     stage_book(book, bk);
     const uint32_t q = blockIdx.x;
     const PanelItem it = panel_item(a, q);
-    const uint32_t per = (it.nq + kSegThreads - 1) / kSegThreads;
-    const uint32_t i0 = min(threadIdx.x * per, it.nq), i1 = min(i0 + per, it.nq);
+    const bool vec = (reinterpret_cast<uintptr_t>(a.src) & 15u) == 0;
+    const uint32_t n_oct = it.nq / 8;
+    const uint32_t per = (n_oct + kSegThreads - 1) / kSegThreads;
+    const uint32_t o0 = min(threadIdx.x * per, n_oct), o1 = min(o0 + per, n_oct);
     uint32_t bits = 0;
-    for (uint32_t i = i0; i < i1; ++i) bits += bk.len[exponent_of(panel_elem(a, it, i))];
+    for (uint32_t ob = o0; ob < o1; ob += kOctBatch) {
+        uint4 v[kOctBatch];
+#pragma unroll
+        for (uint32_t k = 0; k < kOctBatch; ++k)
+            v[k] = ob + k < o1 ? panel_octet(a, it, ob + k, vec) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (uint32_t k = 0; k < kOctBatch; ++k)
+            if (ob + k < o1)
+#pragma unroll
+                for (uint32_t j = 0; j < 8; ++j) bits += bk.len[exponent_of(octet_value(v[k], j))];
+    }
     uint32_t total;
     const uint64_t start = block_exclusive_scan(bits, sh, total);
     const uint32_t c0 = a.first[2 * q], b0 = a.first[2 * q + 1];
@@ -469,29 +525,44 @@ __global__ __launch_bounds__(256) void panel_pack_kernel(const PanelArgs a, cons
     uint32_t nacc = uint32_t(pos & 31);
     uint64_t w = pos >> 5;
     const uint64_t first_word = w, last_word = bits ? (start + bits - 1) >> 5 : w;
-    for (uint32_t i = i0; i < i1; ++i) {
-        const uint16_t b = panel_elem(a, it, i);
-        a.raw[it.e0 + i] = uint8_t(raw_of(b));
-        const uint32_t e = exponent_of(b);
-        const uint32_t l = bk.len[e];
-        const uint64_t c = (pos >> a.chunk_shift) + 1;
-        if (c < chunks && (c << a.chunk_shift) <= pos + l) {
-            const uint32_t off = uint32_t(pos + l - (c << a.chunk_shift));
-            const uint64_t g = 5ull * (c0 + c);
-            const uint64_t v = uint64_t(off) << (g & 31);
-            or_word(a.offw, g >> 5, uint32_t(v));
-            or_word(a.offw, (g >> 5) + 1, uint32_t(v >> 32));
-            if ((c & ((uint64_t(1) << a.lanes_shift) - 1)) == 0) a.blockout[b0 + (c >> a.lanes_shift)] = uint32_t(it.e0 + i + 1);
-        }
-        acc = (acc << l) | bk.code[e];
-        nacc += l;
-        pos += l;
-        if (nacc >= 32) {
-            nacc -= 32;
-            const uint32_t v = uint32_t(acc >> nacc);
-            if (w == first_word || w == last_word) or_word(words, w, v);
-            else words[w] = v;
-            ++w;
+    for (uint32_t ob = o0; ob < o1; ob += kOctBatch) {
+        uint4 v[kOctBatch];
+#pragma unroll
+        for (uint32_t k = 0; k < kOctBatch; ++k)
+            v[k] = ob + k < o1 ? panel_octet(a, it, ob + k, vec) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (uint32_t k = 0; k < kOctBatch; ++k) {
+            if (ob + k >= o1) break;
+            const uint32_t o = ob + k;
+            uint32_t r[2] = {0u, 0u};
+#pragma unroll
+            for (uint32_t j = 0; j < 8; ++j) {
+                const uint32_t b = octet_value(v[k], j), i = 8u * o + j;
+                r[j >> 2] |= raw_of(b) << (8 * (j & 3));
+                const uint32_t e = exponent_of(b);
+                const uint32_t l = bk.len[e];
+                const uint64_t c = (pos >> a.chunk_shift) + 1;
+                if (c < chunks && (c << a.chunk_shift) <= pos + l) {
+                    const uint32_t off = uint32_t(pos + l - (c << a.chunk_shift));
+                    const uint64_t g = 5ull * (c0 + c);
+                    const uint64_t vv = uint64_t(off) << (g & 31);
+                    or_word(a.offw, g >> 5, uint32_t(vv));
+                    or_word(a.offw, (g >> 5) + 1, uint32_t(vv >> 32));
+                    if ((c & ((uint64_t(1) << a.lanes_shift) - 1)) == 0)
+                        a.blockout[b0 + (c >> a.lanes_shift)] = uint32_t(it.e0 + i + 1);
+                }
+                acc = (acc << l) | bk.code[e];
+                nacc += l;
+                pos += l;
+                if (nacc >= 32) {
+                    nacc -= 32;
+                    const uint32_t wv = uint32_t(acc >> nacc);
+                    if (w == first_word || w == last_word) or_word(words, w, wv);
+                    else words[w] = wv;
+                    ++w;
+                }
+            }
+            *reinterpret_cast<uint2 *>(a.raw + it.e0 + 8u * o) = make_uint2(r[0], r[1]);
         }
     }
     if (nacc > 0) or_word(words, w, uint32_t(acc << (32 - nacc)));
