@@ -152,25 +152,30 @@ __global__ __launch_bounds__(256) void segment_bits_kernel(const uint16_t *src, 
     if (threadIdx.x == 0) seg_bits[blockIdx.x] = total;
 }
 
-// Exclusive prefix over the segments (one workgroup of 1024 threads).
+// Exclusive prefix over the segments (one workgroup of 1024 threads): each
+// thread sums a contiguous run of segments, one workgroup scan places the
+// runs, and each thread writes its run's prefixes.
 __global__ __launch_bounds__(1024) void segment_scan_kernel(const uint32_t *seg_bits, uint64_t nseg,
                                                             uint64_t *seg_off) {
     __shared__ uint64_t sh[1024];
-    uint64_t carry = 0;
-    for (uint64_t base = 0; base < nseg; base += 1024) {
-        const uint64_t i = base + threadIdx.x;
-        const uint64_t v = i < nseg ? seg_bits[i] : 0;
-        sh[threadIdx.x] = v;
+    const uint32_t t = threadIdx.x;
+    const uint64_t per = (nseg + 1023) / 1024;
+    const uint64_t i0 = min(uint64_t(t) * per, nseg), i1 = min(i0 + per, nseg);
+    uint64_t sum = 0;
+    for (uint64_t i = i0; i < i1; ++i) sum += seg_bits[i];
+    sh[t] = sum;
+    __syncthreads();
+    for (uint32_t d = 1; d < 1024; d <<= 1) {
+        const uint64_t add = t >= d ? sh[t - d] : 0;
         __syncthreads();
-        for (uint32_t d = 1; d < 1024; d <<= 1) {
-            const uint64_t add = threadIdx.x >= d ? sh[threadIdx.x - d] : 0;
-            __syncthreads();
-            sh[threadIdx.x] += add;
-            __syncthreads();
-        }
-        if (i < nseg) seg_off[i] = carry + sh[threadIdx.x] - v;
-        carry += sh[1023];
+        sh[t] += add;
         __syncthreads();
+    }
+    uint64_t run = sh[t] - sum;
+    for (uint64_t i = i0; i < i1; ++i) {
+        const uint64_t v = seg_bits[i];
+        seg_off[i] = run;
+        run += v;
     }
 }
 
