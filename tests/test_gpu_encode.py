@@ -218,3 +218,23 @@ def test_panel_full_size_gemm_matrix():
     host = dfc.encode(w, layout=PANEL)
     assert size == host.size
     assert torch.equal(d[:size], torch.from_numpy(host).cuda())
+
+
+@pytest.mark.parametrize("layout", ["flat", "panel", "ans"])
+def test_source_not_16_byte_aligned(layout):
+    """A source two bytes past a 16-byte boundary takes the encoder's scalar
+    load paths (histogram, segment loads, raw bytes, panel octets); the
+    container must still equal the host encoder's."""
+    shape = (64, 1040) if layout == "panel" else (1, 200003)
+    x = synth.gaussian_with_outliers(shape, 0.02, (181, shape[0], shape[1])).astype(np.uint16)
+    n = x.size
+    base = torch.empty(n + 8, dtype=torch.int16, device="cuda")
+    src = base[1: n + 1]
+    src.copy_(dev16(x))
+    assert src.data_ptr() % 16 == 2 and src.is_contiguous()
+    say("case unaligned", layout, shape)
+    kw = {"flat": {}, "panel": {"layout": PANEL, "panel_k": 1024}, "ans": {"layout": dfc.LAYOUT_ANS}}[layout]
+    host = dfc.encode(x, shape=shape, **kw)
+    d, size = dfc.encode_device(src, shape=shape, **kw)
+    assert size == host.size
+    assert np.array_equal(d[:size].cpu().numpy(), host)
