@@ -201,7 +201,7 @@ __device__ __forceinline__ void decode_block(const ItemArgs &a, const Buffers &b
     }
     for (uint32_t j0 = uint32_t(kWave * PF); j0 < br.nh; j0 += kWave) {
         const uint32_t i = lane + j0;
-        const u32x2 Ri = __builtin_amdgcn_raw_buffer_load_b64(bf.raw, 8u * (br.h0 + i), 0, 0);
+        const u32x2 Ri = __builtin_amdgcn_raw_buffer_load_b64(bf.raw, i < br.nh ? 8u * (br.h0 + i) : kNowhere, 0, 0);
         const u32x2 E = *reinterpret_cast<const u32x2 *>(stage + 8u * min(i, last));
         store_octet(bf, br, i, assemble8(E, Ri));
     }
@@ -248,10 +248,12 @@ __global__ __launch_bounds__(1024, Occupancy<C>::kWavesPerSimd) void dfc_decode_
         // block's last octet load nothing)
         u32x2 R[PF];
 #pragma unroll
-        for (int j = 0; j < PF; ++j)
+        for (int j = 0; j < PF; ++j) {
+            const uint32_t i = lane + uint32_t(kWave * j);
             R[j] = uint32_t(kWave * j) < br.nh
-                       ? __builtin_amdgcn_raw_buffer_load_b64(bf.raw, 8u * (br.h0 + lane + uint32_t(kWave * j)), 0, 0)
+                       ? __builtin_amdgcn_raw_buffer_load_b64(bf.raw, i < br.nh ? 8u * (br.h0 + i) : kNowhere, 0, 0)
                        : u32x2{0u, 0u};
+        }
         // next block's stream words, offsets and output range
         const uint32_t bn = b + waves;
         const bool more = bn < hi_b;

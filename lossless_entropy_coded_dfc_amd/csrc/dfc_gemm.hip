@@ -94,8 +94,10 @@ __device__ __forceinline__ bool gemm_item(const GemmArgs &g, uint32_t q, const T
         const uint32_t ci = (b - b0) * kWave + lane;  // item-relative chunk
         Chunk<C> ck;
         load_chunk<C>(words, offw, c0 + ci, ck);
-        // rounds past the block's last sub-tile load nothing
-        const uint32_t rounds = (lead + total_want + 511u) >> 9;
+        // raw bytes only for the sub-tiles this block completes: the one it
+        // only begins is carried as exponents, and the next block loads its
+        // raw bytes
+        const uint32_t rounds = (lead + total_want) >> 9;
         u32x2 R[PF];
 #pragma unroll
         for (int j = 0; j < PF; ++j)
