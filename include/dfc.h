@@ -241,7 +241,8 @@ dfc_status dfc_decode_gemm(const void *w_blob_dev, const dfc_info *info, const u
 dfc_status dfc_encode_device_workspace(uint64_t n, uint64_t *bytes);
 
 /* 256-bin exponent histogram of n bf16 values in device memory (bits 14..7),
- * as 32-bit counts into hist_dev (256 device uint32, overwritten).  Device,
+ * as 32-bit counts into hist_dev (256 device uint32, overwritten; a bin's
+ * count wraps past 2^32 - 1, so n below 2^32 is exact).  Device,
  * asynchronous on stream.  DFC_EINVAL on null pointers. */
 dfc_status dfc_histogram_device(const uint16_t *src_dev, uint64_t n, uint32_t *hist_dev, void *stream);
 
