@@ -130,6 +130,28 @@ MUTANTS = [
     ("coded size leaves out the chunk offsets", "blob.py",
      'for nm in ("words", "offsets", "blockout", "raw", "panels"))', 'for nm in ("words", "blockout", "raw", "panels"))',
      ["test_oracle_blob.py", "test_oracle_stream.py"]),
+    ("rANS frequencies without the floor of one", "ans.py",
+     "f[s] = max(1, h[s] * m // total)", "f[s] = h[s] * m // total",
+     ["test_oracle_ans.py"]),
+    ("rANS encoder lanes start one above the lower state bound", "ans.py",
+     "x = [L] * lanes", "x = [L + 1] * lanes",
+     ["test_oracle_ans.py"]),
+    ("vectorised rANS encoder renormalises only above the bound", "ans.py",
+     "emit = live & (x >= (fs << np.uint64(32 - PROB_BITS)))", "emit = live & (x > (fs << np.uint64(32 - PROB_BITS)))",
+     ["test_oracle_ans.py"]),
+    ("vectorised rANS encoder keeps a step's words in ascending lane order", "ans.py",
+     "out.append((x[emit] & np.uint64(0xFFFF))[::-1])", "out.append(x[emit] & np.uint64(0xFFFF))",
+     ["test_oracle_ans.py"]),
+    ("panel sub-tiles eight columns wide", "panel.py",
+     "c = c0 + SUBTILE_K * t + 8 * (l // 32) + j", "c = c0 + 8 * t + 8 * (l // 32) + j",
+     ["test_oracle_panel.py"]),
+    ("bf16 widened to float32 one bit short", "gemm.py",
+     "<< np.uint32(16)", "<< np.uint32(15)",
+     ["test_oracle_gemm.py"]),
+    ("padded chunks start their codes one bit in", "padded.py",
+     "starts[first:last] = chunk * bits + (flat_start[first:last] - flat_start[first])",
+     "starts[first:last] = chunk * bits + 1 + (flat_start[first:last] - flat_start[first])",
+     ["test_oracle_padded.py"]),
 ]
 
 
