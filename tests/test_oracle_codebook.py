@@ -222,3 +222,31 @@ def test_canonical_tables_decode_every_code():
                 for tail in (0, (1 << (24 - l)) - 1):
                     w = (int(codes[s]) << (24 - l)) | tail
                     assert cb.decode_window(w, t) == (s, l)
+
+
+def test_tie_rule_leaves_in_symbol_order():
+    """Ties between optimal length assignments follow the stated reading
+    (the pages are silent): leaves of equal count are ordered by symbol, so
+    package-merge pairs the smaller symbols first and they end up deeper.
+    Worked by hand for counts 1, 1, 1 on symbols 5, 9, 200: the kept items
+    are the three leaves and the package (5, 9), giving 5 and 9 length 2 and
+    200 length 1 (the mirror choice, 200 deeper, costs the same)."""
+    hist = np.zeros(256, dtype=np.int64)
+    hist[[5, 9, 200]] = 1
+    lengths = cb.package_merge_lengths(hist, 24)
+    assert {s: int(lengths[s]) for s in (5, 9, 200)} == {5: 2, 9: 2, 200: 1}
+    assert int(np.count_nonzero(lengths)) == 3
+
+
+def test_tie_rule_leaves_before_packages():
+    """Same reading, second half: of items with equal weight, leaves come
+    before packages.  Counts 1, 1, 2, 2 on symbols 1..4, worked by hand: the
+    package (1, 2) of weight 2 ties the leaves 3 and 4; leaves first keeps
+    1, 2, 3, 4, (1, 2) and (3, 4), so every symbol has length 2.  Packages
+    first would keep (1, 2) ahead of 3 and give lengths 3, 3, 2, 1 at the
+    same cost 12."""
+    hist = np.zeros(256, dtype=np.int64)
+    hist[[1, 2, 3, 4]] = [1, 1, 2, 2]
+    lengths = cb.package_merge_lengths(hist, 24)
+    assert [int(lengths[s]) for s in (1, 2, 3, 4)] == [2, 2, 2, 2]
+    assert int((hist * lengths).sum()) == 12

@@ -148,6 +148,17 @@ MUTANTS = [
     ("bf16 widened to float32 one bit short", "gemm.py",
      "<< np.uint32(16)", "<< np.uint32(15)",
      ["test_oracle_gemm.py"]),
+    ("package-merge breaks leaf ties by the larger symbol", "codebook.py",
+     "order = sorted(range(m), key=lambda i: (int(hist[used[i]]), used[i]))",
+     "order = sorted(range(m), key=lambda i: (int(hist[used[i]]), -used[i]))",
+     ["test_oracle_codebook.py"]),
+    ("package-merge puts packages before leaves of equal weight", "codebook.py",
+     "key=lambda it: (it[0], it[1], it[2]))", "key=lambda it: (it[0], -it[1], it[2]))",
+     ["test_oracle_codebook.py"]),
+    ("canonical codes of one length in decreasing symbol order", "codebook.py",
+     "    for s in range(256):\n        l = int(lengths[s])\n        if l > 0:\n            codes[s] = next_code[l]",
+     "    for s in range(255, -1, -1):\n        l = int(lengths[s])\n        if l > 0:\n            codes[s] = next_code[l]",
+     ["test_oracle_codebook.py"]),
     ("padded chunks start their codes one bit in", "padded.py",
      "starts[first:last] = chunk * bits + (flat_start[first:last] - flat_start[first])",
      "starts[first:last] = chunk * bits + 1 + (flat_start[first:last] - flat_start[first])",
