@@ -159,6 +159,14 @@ MUTANTS = [
      "    for s in range(256):\n        l = int(lengths[s])\n        if l > 0:\n            codes[s] = next_code[l]",
      "    for s in range(255, -1, -1):\n        l = int(lengths[s])\n        if l > 0:\n            codes[s] = next_code[l]",
      ["test_oracle_codebook.py"]),
+    ('code starts shifted by one code', 'stream.py',
+     'np.cumsum(l[:-1], out=starts[1:])',
+     'np.cumsum(l[1:], out=starts[1:])',
+     ['test_oracle_stream.py']),
+    ('block offsets section one entry short', 'blob.py',
+     '"blockout": 4 * (enc["n_blocks"] + 1),',
+     '"blockout": 4 * enc["n_blocks"],',
+     ['test_oracle_blob.py']),
     ("padded chunks start their codes one bit in", "padded.py",
      "starts[first:last] = chunk * bits + (flat_start[first:last] - flat_start[first])",
      "starts[first:last] = chunk * bits + 1 + (flat_start[first:last] - flat_start[first])",
