@@ -22,12 +22,18 @@
  * start offset (bits from the chunk start to its first code) and each block
  * of T chunks carries a 32-bit output offset (number of codes before it).
  *
- * Everything is stateless and re-entrant.  The library never allocates
- * device memory and never synchronises a stream: the caller owns every
- * buffer.  Host functions take host pointers; device functions take device
- * pointers and enqueue work on the given HIP stream (a hipStream_t passed as
- * void*, NULL = the default stream) and return before it runs.  No C++
- * exception crosses this interface.
+ * A container holds the code (the 256 code lengths, or the rANS
+ * frequencies) and the coded data, nothing derived: every GPU workgroup that
+ * decodes derives its lookup tables from the code in its own LDS.
+ *
+ * Every entry point is re-entrant and keeps no state between calls, with one
+ * exception: dfc_set_launch sets a process-wide launch shape that later
+ * Huffman decode launches read.  The library never allocates device memory:
+ * the caller owns every buffer.  Host functions take host pointers; device
+ * functions take device pointers and enqueue work on the given HIP stream (a
+ * hipStream_t passed as void*, NULL = the default stream) and return before
+ * it runs; only dfc_encode_device waits for its stream (it reads the
+ * histogram back).  No C++ exception crosses this interface.
  */
 #ifndef DFC_H
 #define DFC_H
@@ -77,9 +83,9 @@ typedef enum {
  * if x < 2^16 the next word w enters as x = (x << 16) | w.  A block is 64
  * lanes x S steps: element i * 64 + l of the block belongs to lane l, and at
  * every step the lanes that need a word take the block's next words in lane
- * order.  The container keeps f (u16[256]) and the derived slot table (per
- * slot: rotated exponent | (f - 1) << 8 | (slot - cum) << 20) in its
- * tables section, all blocks' word streams in the words section, the first
+ * order.  The container keeps f (u16[256]) in its tables section (the
+ * decoder derives its slot table from them), all blocks' word streams in the
+ * words section, the first
  * word of every block (u32, n_blocks + 1) in the offsets section and the 64
  * initial states of every block (u32) in the blockout section; chunk_bytes
  * and n_chunks are 0, lut_bits holds 12, tile_k holds S. */
@@ -91,9 +97,10 @@ enum { DFC_MAX_BATCH = 32 };
 /* Encoder parameters; dfc_default_params fills the defaults. */
 typedef struct {
     uint32_t chunk_bytes;     /* C: bytes of code stream per lane: 4, 8, 16 or 32 (default 16) */
-    uint32_t lanes_per_block; /* T: chunks per block: 64 (default; one wavefront), 128 or 256 */
+    uint32_t lanes_per_block; /* T: chunks per block: 64 (one wavefront; the only value accepted) */
     uint32_t max_code_len;    /* code length limit, 1..24 (default 24) */
-    uint32_t lut_bits;        /* k: bits indexed by the first-level decode table, 8..12 (default 11) */
+    uint32_t lut_bits;        /* k: bits indexed by the first-level decode table the GPU derives,
+                                 8..12 (default 11); recorded in the header for the decoder */
     uint32_t layout;          /* DFC_LAYOUT_FLAT (row-major), _PANEL, _PADDED or _ANS */
     uint32_t threads;         /* host encoder threads; 0 = min(hardware threads, 16) */
     uint32_t panel_k;         /* PANEL: columns per item, a multiple of 16 (0 = 1024) */
@@ -122,7 +129,7 @@ typedef struct {
                               (excludes derived decode tables and alignment padding) */
     uint64_t total_bits;   /* code stream length */
     uint64_t n_chunks, n_blocks;
-    uint64_t off_tables, tables_bytes;
+    uint64_t off_tables, tables_bytes;  /* Huffman layouts: 0, 0; ANS: the frequencies f (512 B) */
     uint64_t off_words, words_bytes;
     uint64_t off_offsets, offsets_bytes;
     uint64_t off_blockout, blockout_bytes;
@@ -179,9 +186,9 @@ dfc_status dfc_encode(const uint16_t *src, uint64_t n, const dfc_params *p,
                       const dfc_codebook *cb, void *dst, uint64_t cap, uint64_t *written);
 
 /* Validate a host copy of a container and describe it.  Host.  Checks the
- * header, section placement, code lengths (complete code, limit 24), the
- * derived decode tables (rebuilt and compared), every chunk offset and every
- * block offset.  DFC_ECORRUPT on any inconsistency, DFC_EUNSUPPORTED on an
+ * header, section placement, code lengths (complete code, limit 24; or the
+ * rANS frequencies, summing to 2^12), every chunk offset and every block
+ * offset.  DFC_ECORRUPT on any inconsistency, DFC_EUNSUPPORTED on an
  * unknown version/layout, DFC_ESIZE if bytes < the declared size. */
 dfc_status dfc_blob_info(const void *blob, uint64_t bytes, dfc_info *out);
 
@@ -273,9 +280,30 @@ dfc_status dfc_encode_device(const uint16_t *src_dev, uint64_t n, const dfc_para
 
 /* Launch tuning knob for benchmarks (Huffman layouts): wavefronts per
  * workgroup (1..16) and wave-blocks each wavefront decodes (1..64); 0 =
- * automatic.  Returns DFC_EINVAL for other values.  Process-wide; each value
- * is read atomically by every later launch, on any thread. */
+ * automatic.  Returns DFC_EINVAL for other values.  The library's only
+ * process-wide state: each value is read atomically by every later decode
+ * launch, on any thread, so a caller that changes it while other threads
+ * decode changes their launch shape (never their results). */
 dfc_status dfc_set_launch(uint32_t waves_per_group, uint32_t blocks_per_wave);
+
+/* Bytes of the decode tables the GPU kernels derive from a container's code
+ * (dfc_derive_tables writes that many).  Host.  Huffman layouts: the k-bit
+ * first level (step u32, symbols u64, boundary mask u16 per window) and the
+ * canonical per-length tables, 14 * 2^k + 640 bytes; ANS: the slot table,
+ * 4 * 2^12 bytes.  DFC_EINVAL / DFC_EUNSUPPORTED on a bad info. */
+dfc_status dfc_derived_tables_bytes(const dfc_info *info, uint64_t *bytes);
+
+/* Diagnostic: one workgroup of `threads` threads (a multiple of 64, at most
+ * 1024; 0 = 256) derives the decode tables of a container exactly as every
+ * decoding workgroup does in its LDS (DFloat11 blog, section 03 item 1:
+ * compact lookup tables in on-chip memory), and writes them to dst_dev
+ * (cap >= dfc_derived_tables_bytes, 16-byte aligned).  Device,
+ * asynchronous.  The layout of these bytes is private to the library and
+ * may change; they exist so that tests can check the derivation itself.
+ * Errors: DFC_EINVAL (null or misaligned pointers, bad thread count, an
+ * empty container), DFC_ESIZE (cap), DFC_EHIP. */
+dfc_status dfc_derive_tables(const void *blob_dev, const dfc_info *info, uint32_t threads, void *dst_dev,
+                             uint64_t cap, void *stream);
 
 /* Human-readable name of a status code. */
 const char *dfc_status_str(dfc_status s);

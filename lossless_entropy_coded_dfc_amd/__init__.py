@@ -21,7 +21,7 @@ __all__ = [
     "DfcError", "DfcLibraryMissing", "Params", "Codebook", "Info", "BatchItem",
     "library", "library_path", "default_params", "histogram", "build_codebook",
     "encode_bound", "encode", "blob_info", "decode", "decode_batch", "set_launch",
-    "status_str", "MAX_BATCH",
+    "status_str", "MAX_BATCH", "derived_tables_bytes", "derive_tables",
 ]
 
 MAX_BATCH = 32
@@ -134,6 +134,11 @@ def library():
                                       ctypes.POINTER(Codebook), ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
                                       ctypes.c_uint64, u64p, ctypes.c_void_p]
     lib.dfc_encode_device.restype = st
+    lib.dfc_derived_tables_bytes.argtypes = [ctypes.POINTER(Info), u64p]
+    lib.dfc_derived_tables_bytes.restype = st
+    lib.dfc_derive_tables.argtypes = [ctypes.c_void_p, ctypes.POINTER(Info), ctypes.c_uint32, ctypes.c_void_p,
+                                      ctypes.c_uint64, ctypes.c_void_p]
+    lib.dfc_derive_tables.restype = st
     lib.dfc_set_launch.argtypes = [ctypes.c_uint32, ctypes.c_uint32]
     lib.dfc_set_launch.restype = st
     lib.dfc_status_str.argtypes = [ctypes.c_int]
@@ -354,6 +359,24 @@ def decode_gemm(blob_dev, info: Info, x, y, status=None, stream=None):
     _check(library().dfc_decode_gemm(ctypes.c_void_p(_blob_ptr(blob_dev, info)), ctypes.byref(info),
                                      ctypes.c_void_p(_dev_ptr(x)), B, ctypes.c_void_p(_dev_ptr(y)),
                                      ctypes.c_void_p(_status_ptr(status)), _stream(stream)), "dfc_decode_gemm")
+
+
+def derived_tables_bytes(info: Info) -> int:
+    out = ctypes.c_uint64()
+    _check(library().dfc_derived_tables_bytes(ctypes.byref(info), ctypes.byref(out)), "dfc_derived_tables_bytes")
+    return out.value
+
+
+def derive_tables(blob_dev, info: Info, threads: int = 0, stream=None):
+    """The decode tables the GPU kernels derive from the container's code, as
+    one workgroup of ``threads`` threads builds them in LDS (a device uint8
+    tensor; the byte layout is the library's own).  Asynchronous."""
+    import torch
+    nbytes = derived_tables_bytes(info)
+    out = torch.empty(nbytes, dtype=torch.uint8, device=blob_dev.device)
+    _check(library().dfc_derive_tables(ctypes.c_void_p(_blob_ptr(blob_dev, info)), ctypes.byref(info), threads,
+                                       ctypes.c_void_p(out.data_ptr()), nbytes, _stream(stream)), "dfc_derive_tables")
+    return out
 
 
 def set_launch(waves_per_group: int = 0, blocks_per_wave: int = 0):

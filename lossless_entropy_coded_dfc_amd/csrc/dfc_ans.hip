@@ -7,7 +7,8 @@
 //
 // One wavefront decodes one block: lane l holds the state of the block's
 // lane l and decodes elements i * 64 + l, one step i at a time.  Per step:
-// the slot table (in LDS, 16 KB per workgroup) gives symbol, frequency and
+// the slot table (derived from the frequencies into LDS by every workgroup,
+// 16 KB) gives symbol, frequency and
 // cumulative count; the lanes whose state drops below 2^16 take the block's
 // next 16-bit words in lane order (ballot, then each lane's rank among them),
 // read from a per-wavefront ring of 1024 words in LDS.  A round of eight
@@ -47,7 +48,7 @@ struct AnsItem {
     const uint32_t *offsets;   // first word of every block, n_blocks + 1
     const uint32_t *states;    // 64 initial states per block
     const uint8_t *raw;        // raw bytes, padded to 16
-    const uint32_t *table;     // slot table, 4096 entries
+    const uint16_t *freqs;     // quantised frequencies f[256] (sum 4096)
     uint16_t *dst;
     uint32_t words_bytes, states_bytes, raw_bytes, dst_bytes;
     uint32_t n, n_blocks, steps;
@@ -72,9 +73,8 @@ __global__ __launch_bounds__(kAnsWaves * kWave) void dfc_ans_kernel(const AnsBat
         if (wg >= args.item[k].wg_begin) it = k;
     const AnsItem a = args.item[it];
 
-    for (uint32_t o = threadIdx.x; o < dfc::kAnsSlots / 4; o += blockDim.x)
-        reinterpret_cast<uint4 *>(table)[o] = reinterpret_cast<const uint4 *>(a.table)[o];
-    __syncthreads();
+    // the slot table from the frequencies (the stage areas serve as scratch)
+    derive_slot_table(table, &stage_all[0][0], a.freqs);
 
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const uint32_t lane = threadIdx.x % kWave;
@@ -219,9 +219,25 @@ __global__ __launch_bounds__(kAnsWaves * kWave) void dfc_ans_kernel(const AnsBat
     if (bad && lane == 0 && args.status) atomicOr(args.status, kStatusCorrupt);
 }
 
+// The slot table as the decoder derives it, copied out (for inspection).
+__global__ __launch_bounds__(1024) void derive_slot_table_kernel(const uint16_t *freqs, uint32_t *dst) {
+    __shared__ __align__(16) uint32_t table[dfc::kAnsSlots];
+    __shared__ __align__(16) uint8_t scratch[kSlotScratchBytes];
+    derive_slot_table(table, scratch, freqs);
+    for (uint32_t o = threadIdx.x; o < dfc::kAnsSlots / 4; o += blockDim.x)
+        reinterpret_cast<uint4 *>(dst)[o] = reinterpret_cast<const uint4 *>(table)[o];
+}
+
 }  // namespace
 
 namespace dfc {
+
+dfc_status ans_derive_tables(const void *blob_dev, const dfc_info &info, uint32_t threads, void *dst,
+                             hipStream_t stream) {
+    const uint16_t *freqs = reinterpret_cast<const uint16_t *>(static_cast<const uint8_t *>(blob_dev) + info.off_tables);
+    derive_slot_table_kernel<<<dim3(1), dim3(threads), 0, stream>>>(freqs, static_cast<uint32_t *>(dst));
+    return hipGetLastError() == hipSuccess ? DFC_OK : DFC_EHIP;
+}
 
 dfc_status ans_check_item(const dfc_batch_item &it) {
     const dfc_info &in = *it.info;
@@ -248,7 +264,7 @@ dfc_status ans_launch(const dfc_batch_item *items, const uint32_t *idx, uint32_t
         a.offsets = reinterpret_cast<const uint32_t *>(base + in.off_offsets);
         a.states = reinterpret_cast<const uint32_t *>(base + in.off_blockout);
         a.raw = base + in.off_raw;
-        a.table = reinterpret_cast<const uint32_t *>(base + in.off_tables + 512);
+        a.freqs = reinterpret_cast<const uint16_t *>(base + in.off_tables);
         a.dst = bi.dst_dev;
         a.words_bytes = uint32_t(in.words_bytes);
         a.states_bytes = uint32_t(in.blockout_bytes);

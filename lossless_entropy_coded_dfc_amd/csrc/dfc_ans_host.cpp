@@ -1,6 +1,5 @@
 // dfc_ans_host.cpp - host half of the interleaved rANS layout (DFC_LAYOUT_ANS):
-// frequency quantisation, the slot table, the block encoder and container
-// validation.
+// frequency quantisation, the block encoder and container validation.
 //
 // The exponent bytes are coded with range asymmetric numeral systems, an
 // arithmetic-family entropy code (DFloat11 blog, section 02, names Huffman-
@@ -64,16 +63,6 @@ void cumulative(const uint32_t f[256], uint32_t cum[256]) {
     }
 }
 
-// Slot table: rotated exponent | (f - 1) << 8 | (slot - cum) << 20 per slot.
-void slot_table(const uint32_t f[256], uint8_t *out) {
-    uint32_t cum[256];
-    cumulative(f, cum);
-    for (int s = 0; s < 256; ++s)
-        for (uint32_t k = 0; k < f[s]; ++k)
-            store_le<uint32_t>(out + 4ull * (cum[s] + k),
-                               rotate_exponent(uint32_t(s)) | ((f[s] - 1u) << 8) | (k << 20));
-}
-
 // One block of cnt elements: initial decoder states and words in decode order.
 void encode_block(const uint16_t *src, uint64_t cnt, const uint32_t f[256], const uint32_t cum[256],
                   uint32_t states[kAnsLanes], std::vector<uint16_t> &words) {
@@ -130,7 +119,6 @@ void ans_container_head(uint8_t *dst, uint64_t n, uint64_t nw, uint64_t nb, uint
     store_le<uint64_t>(dst + hdr::blob_bytes, blob_bytes);
     uint8_t *tab = dst + off[kTables];
     for (int s = 0; s < 256; ++s) store_le<uint16_t>(tab + 2 * s, uint16_t(f[s]));
-    slot_table(f, tab + 512);
 }
 
 uint64_t ans_encode_bound(uint64_t n, uint32_t steps) {
@@ -206,7 +194,7 @@ dfc_status ans_blob_info(const uint8_t *b, uint64_t bytes, dfc_info &in) {
     }
     if (bytes < blob_bytes) return DFC_ESIZE;
 
-    // frequencies and the slot table derived from them
+    // frequencies (the decoder derives its slot table from them)
     uint32_t f[256];
     uint64_t fsum = 0;
     uint32_t used = 0;
@@ -216,11 +204,6 @@ dfc_status ans_blob_info(const uint8_t *b, uint64_t bytes, dfc_info &in) {
         used += f[s] != 0;
     }
     if (fsum != (in.n ? kAnsSlots : 0)) return DFC_ECORRUPT;
-    {
-        std::vector<uint8_t> t(4ull * kAnsSlots, 0);
-        slot_table(f, t.data());
-        if (std::memcmp(t.data(), b + off[kTables] + 512, t.size()) != 0) return DFC_ECORRUPT;
-    }
     // block word offsets: from 0 to the stream length, at most one word per element
     const uint8_t *ofs = b + off[kOffsets];
     if (load_le<uint32_t>(ofs) != 0 || load_le<uint32_t>(ofs + 4 * in.n_blocks) != nw) return DFC_ECORRUPT;
@@ -248,8 +231,8 @@ dfc_status ans_blob_info(const uint8_t *b, uint64_t bytes, dfc_info &in) {
     in.blockout_bytes = sz.bytes[kBlockout];
     in.off_raw = off[kRaw];
     in.raw_bytes = sz.bytes[kRaw];
-    // header + frequencies + streams, offsets, states, raw (the slot table is derived)
-    in.coded_bytes = kHeaderBytes + 512 + sz.bytes[kWords] + sz.bytes[kOffsets] + sz.bytes[kBlockout] + sz.bytes[kRaw];
+    // header + frequencies + streams, offsets, states, raw
+    in.coded_bytes = kHeaderBytes + sz.bytes[kTables] + sz.bytes[kWords] + sz.bytes[kOffsets] + sz.bytes[kBlockout] + sz.bytes[kRaw];
     return DFC_OK;
 }
 

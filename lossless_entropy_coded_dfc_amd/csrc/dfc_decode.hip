@@ -41,14 +41,14 @@ struct ItemArgs {
     const uint32_t *offw;      // packed 5-bit chunk offsets
     const uint32_t *blockout;  // u32 out[n_blocks + 1]
     const uint8_t *raw;        // raw bytes (sign << 7 | mantissa), padded to 16
-    const uint8_t *tables;     // derived decode tables
+    const uint8_t *lengths;    // the 256 code lengths (container bytes 256..511)
     uint16_t *dst;             // bf16 output
     uint64_t total_bits;
     uint32_t words_bytes, offw_bytes, raw_bytes, dst_bytes;  // buffer ranges
     uint32_t n_blocks;
     uint32_t wg_begin;         // first workgroup of this item in the grid
     uint32_t blocks_per_wg;
-    uint32_t tables_bytes;     // multiple of 16
+    uint32_t tables_bytes;     // LDS image of the derived tables, a multiple of 16
     uint32_t lut_bits;
     uint32_t pad;
 };
@@ -223,7 +223,8 @@ __global__ __launch_bounds__(1024, Occupancy<C>::kWavesPerSimd) void dfc_decode_
     const Buffers bf = make_buffers(a);
     const const_u32_ptr blockout = (const_u32_ptr)(a.blockout);
 
-    const Tables t = stage_tables(lds, a.tables, a.tables_bytes, a.lut_bits);
+    derive_tables(lds, lds + a.tables_bytes, a.lengths, a.lut_bits);
+    const Tables t = tables_view(lds, a.lut_bits);
 
     const uint32_t waves = __builtin_amdgcn_readfirstlane(blockDim.x / kWave);
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -273,6 +274,16 @@ __global__ __launch_bounds__(1024, Occupancy<C>::kWavesPerSimd) void dfc_decode_
     }
 }
 
+// The decode tables as one workgroup derives them, copied out of LDS (for
+// inspection; the decoders keep them in LDS).
+__global__ __launch_bounds__(1024) void derive_tables_kernel(const uint8_t *lengths, uint32_t lut_bits,
+                                                             uint32_t tables_bytes, uint8_t *dst) {
+    extern __shared__ __align__(16) uint8_t lds[];
+    derive_tables(lds, lds + tables_bytes, lengths, lut_bits);
+    for (uint32_t o = 16u * threadIdx.x; o < tables_bytes; o += 16u * blockDim.x)
+        *reinterpret_cast<uint4 *>(dst + o) = *reinterpret_cast<const uint4 *>(lds + o);
+}
+
 // ------------------------------------------------------------------ launch
 
 // Set by dfc_set_launch, read by every launch (possibly on other threads).
@@ -303,7 +314,7 @@ dfc_status launch_group(const dfc_batch_item *items, const uint32_t *idx, uint32
                         hipStream_t stream) {
     BatchArgs args;
     std::memset(&args, 0, sizeof(args));
-    uint32_t max_tables = 0, max_block = 0;
+    uint32_t max_tables = 0, max_block = 0, max_scratch = 0;
     std::vector<uint64_t> blocks;
     std::vector<uint32_t> live;
     for (uint32_t k = 0; k < count; ++k) {
@@ -311,17 +322,21 @@ dfc_status launch_group(const dfc_batch_item *items, const uint32_t *idx, uint32
         if (in.n_blocks == 0) continue;
         live.push_back(idx[k]);
         blocks.push_back(in.n_blocks);
-        max_tables = std::max<uint32_t>(max_tables, uint32_t((in.tables_bytes + 15) & ~15ull));
+        max_tables = std::max<uint32_t>(max_tables, uint32_t(dfc::tables_bytes(in.lut_bits)));
+        max_scratch = std::max<uint32_t>(max_scratch, derive_scratch_bytes(in.lut_bits));
         max_block = std::max(max_block, in.max_block_elems);
     }
     if (live.empty()) return DFC_OK;
     // staging: lead (< 8) + elements + spill of the last lookup, rounded to 16
     const uint32_t stage = (max_block + 32u + 15u) & ~15u;
     if (!allow_full_lds(reinterpret_cast<const void *>(&dfc_decode_kernel<C, Padded>))) return DFC_EHIP;
+    // LDS of a workgroup of w wavefronts: the tables, then the staging
+    // areas, which hold the derivation's scratch before the first block.
+    auto lds_for = [&](uint32_t w) { return max_tables + std::max(w * stage, max_scratch); };
     // Resident workgroups per CU for w wavefronts each, under both the LDS
     // and the register budget.
     auto resident = [&](uint32_t w) -> int {
-        const uint32_t lds = max_tables + w * stage;
+        const uint32_t lds = lds_for(w);
         if (lds > kLdsBytes) return 0;
         int per_cu = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(&dfc_decode_kernel<C, Padded>),
@@ -344,8 +359,8 @@ dfc_status launch_group(const dfc_batch_item *items, const uint32_t *idx, uint32
         }
     }
     if (!waves) waves = 1;
-    while (waves > 1 && max_tables + waves * stage > kLdsBytes) --waves;
-    const uint32_t lds = max_tables + waves * stage;
+    while (waves > 1 && lds_for(waves) > kLdsBytes) --waves;
+    const uint32_t lds = lds_for(waves);
     if (lds > kLdsBytes) return DFC_EUNSUPPORTED;
     int per_cu = resident(waves);
     if (per_cu <= 0) per_cu = 1;
@@ -368,7 +383,7 @@ dfc_status launch_group(const dfc_batch_item *items, const uint32_t *idx, uint32
         a.offw = reinterpret_cast<const uint32_t *>(base + in.off_offsets);
         a.blockout = reinterpret_cast<const uint32_t *>(base + in.off_blockout);
         a.raw = base + in.off_raw;
-        a.tables = base + in.off_tables;
+        a.lengths = base + dfc::hdr::lengths;
         a.dst = bi.dst_dev;
         a.words_bytes = uint32_t(in.words_bytes);
         a.offw_bytes = uint32_t(in.offsets_bytes);
@@ -378,7 +393,7 @@ dfc_status launch_group(const dfc_batch_item *items, const uint32_t *idx, uint32
         a.n_blocks = uint32_t(in.n_blocks);
         a.blocks_per_wg = uint32_t(dfc::ceil_div(in.n_blocks, g[k]));
         a.wg_begin = wg;
-        a.tables_bytes = uint32_t((in.tables_bytes + 15) & ~15ull);
+        a.tables_bytes = uint32_t(dfc::tables_bytes(in.lut_bits));
         a.lut_bits = in.lut_bits;
         wg += uint32_t(dfc::ceil_div(in.n_blocks, a.blocks_per_wg));
     }
@@ -421,6 +436,41 @@ dfc_status dfc_set_launch(uint32_t waves_per_group, uint32_t blocks_per_wave) {
     g_launch.waves.store(waves_per_group, std::memory_order_relaxed);
     g_launch.blocks_per_wave.store(blocks_per_wave, std::memory_order_relaxed);
     return DFC_OK;
+}
+
+dfc_status dfc_derived_tables_bytes(const dfc_info *info, uint64_t *bytes) {
+    if (!info || !bytes) return DFC_EINVAL;
+    if (info->layout == DFC_LAYOUT_ANS) {
+        *bytes = 4ull * dfc::kAnsSlots;
+        return DFC_OK;
+    }
+    if (info->layout != DFC_LAYOUT_FLAT && info->layout != DFC_LAYOUT_PADDED && info->layout != DFC_LAYOUT_PANEL)
+        return DFC_EUNSUPPORTED;
+    if (info->lut_bits < 8 || info->lut_bits > 12) return DFC_EINVAL;
+    *bytes = dfc::tables_bytes(info->lut_bits);
+    return DFC_OK;
+}
+
+dfc_status dfc_derive_tables(const void *blob_dev, const dfc_info *info, uint32_t threads, void *dst_dev,
+                             uint64_t cap, void *stream) {
+    uint64_t need = 0;
+    const dfc_status s = dfc_derived_tables_bytes(info, &need);
+    if (s != DFC_OK) return s;
+    if (!blob_dev || !dst_dev || (reinterpret_cast<uintptr_t>(blob_dev) & 255u) ||
+        (reinterpret_cast<uintptr_t>(dst_dev) & 15u))
+        return DFC_EINVAL;
+    if (threads == 0) threads = 256;
+    if (threads % kWave || threads > 1024) return DFC_EINVAL;
+    if (cap < need) return DFC_ESIZE;
+    if (info->n == 0) return DFC_EINVAL;  // an empty container has no code
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (info->layout == DFC_LAYOUT_ANS) return dfc::ans_derive_tables(blob_dev, *info, threads, dst_dev, st);
+    const uint32_t tb = uint32_t(need);
+    const size_t lds = size_t(tb) + derive_scratch_bytes(info->lut_bits);
+    if (!allow_full_lds(reinterpret_cast<const void *>(&derive_tables_kernel))) return DFC_EHIP;
+    derive_tables_kernel<<<dim3(1), dim3(threads), lds, st>>>(
+        static_cast<const uint8_t *>(blob_dev) + dfc::hdr::lengths, info->lut_bits, tb, static_cast<uint8_t *>(dst_dev));
+    return hipGetLastError() == hipSuccess ? DFC_OK : DFC_EHIP;
 }
 
 dfc_status dfc_decode_batch(const dfc_batch_item *items, uint32_t count, uint32_t *status_dev, void *stream) {

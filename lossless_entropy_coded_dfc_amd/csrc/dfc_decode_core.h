@@ -18,6 +18,7 @@
 
 #include "dfc.h"
 #include "dfc_format.h"
+#include "dfc_tables.h"
 
 namespace {
 
@@ -326,18 +327,6 @@ __device__ __forceinline__ void write_codes_padded(const Chunk<C> &ck, int end, 
     }
 }
 
-// Inclusive prefix sum across the wavefront (DPP row shifts, then row
-// broadcasts 15 and 31).
-__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
-    x += uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x111, 0xf, 0xf, false));  // row_shr:1
-    x += uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x112, 0xf, 0xf, false));  // row_shr:2
-    x += uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x114, 0xf, 0xf, false));  // row_shr:4
-    x += uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x118, 0xf, 0xf, false));  // row_shr:8
-    x += uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x142, 0xa, 0xf, false));  // row_bcast:15
-    x += uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x143, 0xc, 0xf, false));  // row_bcast:31
-    return x;
-}
-
 // 8 bf16 values from 8 staged (rotated) exponents and 8 raw bytes.  Per
 // pair of values, x1 = [raw_a, exp_a, raw_b, exp_b] and x2 = [exp_a, raw_a,
 // exp_b, raw_b] (bytes, low first); each output byte keeps bits 6..0 of x1
@@ -358,13 +347,8 @@ __device__ __forceinline__ u32x4 assemble8(const u32x2 &E, const u32x2 &R) {
     return u32x4{o[0], o[1], o[2], o[3]};
 }
 
-// Stage the decode tables of a container in LDS (16 bytes per thread per
-// step) and describe them.  Every thread of the workgroup must call this.
-__device__ __forceinline__ Tables stage_tables(uint8_t *lds, const uint8_t *tables, uint32_t tables_bytes,
-                                               uint32_t lut_bits) {
-    for (uint32_t o = threadIdx.x * 16u; o < tables_bytes; o += blockDim.x * 16u)
-        *reinterpret_cast<uint4 *>(lds + o) = *reinterpret_cast<const uint4 *>(tables + o);
-    __syncthreads();
+// Pointers into the LDS image of derive_tables for a k-bit first level.
+__device__ __forceinline__ Tables tables_view(uint8_t *lds, uint32_t lut_bits) {
     Tables t;
     t.kb = lut_bits;
     t.kshift = 32u - t.kb;

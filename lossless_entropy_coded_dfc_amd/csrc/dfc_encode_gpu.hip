@@ -8,7 +8,7 @@
 // GPU:
 //   1. exponent histogram (LDS bins per workgroup, then global atomics);
 //   2. on the host: code lengths, canonical codes, total bits (the histogram
-//      times the lengths), section layout, header and decode tables;
+//      times the lengths), section layout and header;
 //   3. code bits per segment of 4096 elements, an exclusive scan over the
 //      segments, then every thread packs its 16 codes at its bit position
 //      (interior words stored, the two words shared with neighbours ORed)
@@ -631,7 +631,7 @@ dfc_status encode_ans_device(const uint16_t *src_dev, uint64_t n, const dfc_para
     uint64_t off[dfc::kNumSections];
     const uint64_t blob_bytes = dfc::place_sections(sz, off);
     if (cap < blob_bytes) return DFC_ESIZE;
-    std::vector<uint8_t> head(off[dfc::kTables] + sz.bytes[dfc::kTables], 0);
+    std::vector<uint8_t> head(dfc::head_bytes(sz, off), 0);
     dfc::ans_container_head(head.data(), n, nw, nb, S, rows, cols, sz, off, blob_bytes, f);
     hipLaunchKernelGGL(fill_zero_u32, dim3(uint32_t(std::min<uint64_t>(65535, dfc::ceil_div(blob_bytes / 4, 256)))),
                        dim3(256), 0, st, reinterpret_cast<uint32_t *>(dst), blob_bytes / 4);
@@ -692,7 +692,7 @@ dfc_status encode_panel_device(const uint16_t *src_dev, uint64_t n, const dfc_pa
     uint64_t off[dfc::kNumSections];
     const uint64_t blob_bytes = dfc::place_sections(sz, off);
     if (cap < blob_bytes) return DFC_ESIZE;
-    std::vector<uint8_t> head(off[dfc::kTables] + sz.bytes[dfc::kTables], 0);
+    std::vector<uint8_t> head(dfc::head_bytes(sz, off), 0);
     dfc::container_header(head.data(), p, n, total_bits, chunks, blocks, g.rows, g.cols, sz, off, blob_bytes, len);
     // the item table: (first chunk, first block, code bits, 0) per item and a sentinel
     std::vector<uint32_t> table(4 * (g.n_items + 1), 0);
@@ -785,7 +785,7 @@ dfc_status dfc_encode_device(const uint16_t *src_dev, uint64_t n, const dfc_para
         return encode_ans_device(src_dev, n, p, rows, cols, hist, static_cast<uint8_t *>(dst_dev), cap, work, ws,
                                  written, st);
 
-    // 2. codebook, layout, header and tables on the host
+    // 2. codebook, layout and header on the host
     uint8_t len[256];
     if (cb_in) {
         std::memcpy(len, cb_in->len, 256);
@@ -813,11 +813,11 @@ dfc_status dfc_encode_device(const uint16_t *src_dev, uint64_t n, const dfc_para
     uint64_t off[dfc::kNumSections];
     const uint64_t blob_bytes = dfc::place_sections(sz, off);
     if (cap < blob_bytes) return DFC_ESIZE;
-    std::vector<uint8_t> head(off[dfc::kTables] + sz.bytes[dfc::kTables], 0);
+    std::vector<uint8_t> head(dfc::head_bytes(sz, off), 0);
     dfc::container_header(head.data(), p, n, total_bits, L.n_chunks, L.n_blocks, rows, cols, sz, off, blob_bytes, len);
 
     // 3. zero the container (all but the raw bytes' whole 16-byte groups,
-    // which the packer writes), upload header and tables, pack
+    // which the packer writes), upload the header, pack
     uint8_t *dst = static_cast<uint8_t *>(dst_dev);
     auto zero = [&](uint64_t from, uint64_t to) {
         if (to > from)

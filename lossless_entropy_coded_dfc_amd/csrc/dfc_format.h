@@ -1,10 +1,12 @@
 // dfc_format.h - byte layout of the DFC1 container shared by the host codec
 // and the device launcher (internal to libdfc).
 //
-// Container: 256-byte header, 256 code lengths, then the sections tables,
+// Container: 256-byte header, 256 code lengths, then the sections tables
+// (empty in the Huffman layouts; the rANS frequencies in the ANS layout),
 // words, offsets (empty in the padded layout), blockout, raw (and panels,
 // used by the panel layout only), each at the next multiple of 256 bytes,
-// zero padding.  Little-endian.
+// zero padding.  Little-endian.  A container holds the code and the coded
+// data only: the decode tables are derived from the code by the kernels.
 #pragma once
 
 #include <algorithm>
@@ -32,21 +34,12 @@ constexpr int lengths = 256;
 
 enum Section { kTables = 0, kWords, kOffsets, kBlockout, kRaw, kPanels, kNumSections };
 
-// Decode-table section layout for a k-bit window: step[2^k] (u32, every
-// whole code in the window), wsym[2^k] (u64: rotated exponents of the first
-// <= 4 codes | their step << 32), mask[2^k] (u16), then limit[32],
+// LDS image of the decode tables the kernels derive from the code lengths
+// for a k-bit first level (see dfc_tables.h; never stored in a container):
+// step[2^k] (u32), wsym[2^k] (u64), mask[2^k] (u16), then limit[32],
 // first[32], base[32] (u32, index = code length) and order[256] (u8).
 constexpr uint32_t kStepEscape = 0xFFFFF000u;
 inline uint64_t tables_bytes(uint32_t k) { return 14ull * (1ull << k) + 3 * 128 + 256; }
-inline uint64_t tables_sym_off(uint32_t k) { return 4ull << k; }
-inline uint64_t tables_mask_off(uint32_t k) { return 12ull << k; }
-inline uint64_t tables_limit_off(uint32_t k) { return 14ull << k; }
-inline uint64_t tables_first_off(uint32_t k) { return (14ull << k) + 128; }
-inline uint64_t tables_base_off(uint32_t k) { return (14ull << k) + 256; }
-inline uint64_t tables_order_off(uint32_t k) { return (14ull << k) + 384; }
-
-// Exponent byte as staged by the decoder: rotated right by one bit.
-inline uint32_t rotate_exponent(uint32_t e) { return ((e >> 1) | ((e & 1u) << 7)) & 0xFFu; }
 
 inline uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 inline uint64_t ceil_div(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
@@ -69,7 +62,7 @@ struct SectionSizes {
 inline SectionSizes section_sizes(uint64_t n, uint64_t n_chunks, uint64_t n_blocks, uint32_t chunk_bytes,
                                   uint32_t lut_bits, uint64_t n_items = 0, bool with_offsets = true) {
     SectionSizes s;
-    s.bytes[kTables] = tables_bytes(lut_bits);
+    s.bytes[kTables] = 0;
     s.bytes[kWords] = 4 * (n_chunks * (chunk_bytes / 4) + kGuardWords);
     s.bytes[kOffsets] = with_offsets ? 4 * (ceil_div(kOffsetBits * (n_chunks + 1), 32) + 1) : 0;
     s.bytes[kBlockout] = 4 * (n_blocks + 1);
@@ -79,16 +72,15 @@ inline SectionSizes section_sizes(uint64_t n, uint64_t n_chunks, uint64_t n_bloc
 }
 
 // Interleaved rANS layout: 2^12 probability slots, states in [2^16, 2^32),
-// 16-bit words, 64 lanes per block.  Sections: tables = f (u16[256]) + the
-// slot table (u32[4096]: rotated exponent | (f - 1) << 8 | (slot - cum) << 20);
-// words = the streams (u16, whole 16-byte units plus one guard unit);
+// 16-bit words, 64 lanes per block.  Sections: tables = f (u16[256]; the
+// kernel derives its slot table from them); words = the streams (u16, whole 16-byte units plus one guard unit);
 // offsets = the first word of every block (u32, n_blocks + 1); blockout =
 // the 64 initial states of every block (u32); raw as in the other layouts.
 constexpr uint32_t kAnsProbBits = 12;
 constexpr uint32_t kAnsSlots = 1u << kAnsProbBits;
 constexpr uint64_t kAnsLow = 1ull << 16;  // states live in [kAnsLow, 2^32)
 constexpr uint32_t kAnsLanes = 64;
-constexpr uint64_t kAnsTablesBytes = 2 * 256 + 4ull * kAnsSlots;
+constexpr uint64_t kAnsTablesBytes = 2 * 256;
 inline SectionSizes ans_section_sizes(uint64_t n, uint64_t n_words, uint64_t n_blocks) {
     SectionSizes s;
     s.bytes[kTables] = kAnsTablesBytes;
@@ -135,6 +127,12 @@ inline uint64_t place_sections(const SectionSizes &s, uint64_t off[kNumSections]
         pos += s.bytes[i];
     }
     return align256(pos);
+}
+
+// Bytes from the container's start through the end of its tables section
+// (at least the header and code lengths): what a host writes before the data.
+inline uint64_t head_bytes(const SectionSizes &s, const uint64_t off[kNumSections]) {
+    return std::max<uint64_t>(kHeaderBytes, off[kTables] + s.bytes[kTables]);
 }
 
 template <typename T>

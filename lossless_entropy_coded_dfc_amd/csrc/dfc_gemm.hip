@@ -41,7 +41,7 @@ struct GemmArgs {
     const uint32_t *blockout;  // u32 out[n_blocks + 1], indices in panel order
     const uint32_t *items;     // (n_items + 1) x {first chunk, first block, code bits, 0}
     const uint8_t *raw;        // raw bytes in panel order
-    const uint8_t *tables;     // derived decode tables
+    const uint8_t *lengths;    // the 256 code lengths (container bytes 256..511)
     const uint16_t *x;         // B vectors of K bf16: x[b K + k]
     float *y;                  // B vectors of M fp32: y[b M + m]
     uint32_t words_bytes, offw_bytes, raw_bytes, x_bytes, y_bytes;
@@ -178,7 +178,8 @@ __device__ __forceinline__ bool gemm_item(const GemmArgs &g, uint32_t q, const T
 template <int C, int NT>
 __global__ __launch_bounds__(1024) void dfc_gemm_kernel(const GemmArgs g) {
     extern __shared__ __align__(16) uint8_t lds[];
-    const Tables t = stage_tables(lds, g.tables, g.tables_bytes, g.lut_bits);
+    derive_tables(lds, lds + g.tables_bytes, g.lengths, g.lut_bits);
+    const Tables t = tables_view(lds, g.lut_bits);
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const uint32_t lane = threadIdx.x % kWave;
     const uint32_t wpp = g.wpp;
@@ -268,14 +269,17 @@ dfc_status launch_gemm(const GemmArgs &proto, uint32_t max_block, hipStream_t st
     // when the panel has 8 slices or fewer), several panels when it has few
     uint32_t wpp = std::min<uint32_t>(g.slices, 8u);
     uint32_t group = std::max<uint32_t>(1u, 8u / wpp);
-    while (wpp * group > 1 && g.tables_bytes + wpp * group * stage > kLdsBytes) {
+    // the staging areas hold the table derivation's scratch before the first item
+    const uint32_t scratch = derive_scratch_bytes(g.lut_bits);
+    auto lds_for = [&](uint32_t w) { return size_t(g.tables_bytes) + std::max<size_t>(size_t(w) * stage, scratch); };
+    while (wpp * group > 1 && lds_for(wpp * group) > kLdsBytes) {
         if (group > 1)
             --group;
         else
             --wpp;
     }
     const uint32_t waves = wpp * group;
-    const size_t lds = size_t(g.tables_bytes) + size_t(waves) * stage;
+    const size_t lds = lds_for(waves);
     if (lds > kLdsBytes) return DFC_EUNSUPPORTED;
     // Too few panels for the resident wavefronts: share each panel among
     // `split` workgroups, with as few slices per wavefront as the resident
@@ -342,7 +346,7 @@ dfc_status dfc_decode_gemm(const void *w_blob_dev, const dfc_info *info, const u
     g.blockout = reinterpret_cast<const uint32_t *>(base + in.off_blockout);
     g.items = reinterpret_cast<const uint32_t *>(base + in.off_panels);
     g.raw = base + in.off_raw;
-    g.tables = base + in.off_tables;
+    g.lengths = base + dfc::hdr::lengths;
     g.x = x_dev;
     g.y = y_dev;
     g.words_bytes = uint32_t(in.words_bytes);
@@ -356,7 +360,7 @@ dfc_status dfc_decode_gemm(const void *w_blob_dev, const dfc_info *info, const u
     g.cols = uint32_t(in.cols);
     g.rows = uint32_t(in.rows);
     g.batch = batch;
-    g.tables_bytes = uint32_t((in.tables_bytes + 15) & ~15ull);
+    g.tables_bytes = uint32_t(dfc::tables_bytes(in.lut_bits));
     g.lut_bits = in.lut_bits;
     g.status = status_dev;
     hipStream_t st = static_cast<hipStream_t>(stream);

@@ -112,67 +112,12 @@ dfc_status package_merge(const uint64_t hist[256], uint32_t limit, uint8_t len[2
     return DFC_OK;
 }
 
-// First-level table entry for a k-bit window (next k stream bits, first bit
-// most significant): the whole codes that fit, decoded from its first bit.
-struct Entry {
-    uint32_t step;  // (codes << 16) - bits over every whole code, or kStepEscape
-    uint64_t wsym;  // rotated exponents of the first <= 4 codes | their step << 32
-    uint16_t mask;  // bit j: a code ends j + 1 bits in
-};
-
-Entry lut_entry(uint32_t window, uint32_t k, const Canon &c) {
-    uint32_t o = 0, n = 0, o4 = 0;
-    uint32_t syms = 0;
-    Entry e{0, 0, 0};
-    while (o < k) {
-        uint32_t found = 0, v = 0;
-        for (uint32_t l = 1; l <= k - o; ++l) {
-            v = (window >> (k - o - l)) & ((1u << l) - 1u);
-            if (v < c.first[l] + c.count[l]) {
-                found = l;
-                break;
-            }
-        }
-        if (!found) break;
-        const uint32_t sym = c.order[c.base[found] + v - c.first[found]];
-        if (n < 4) {
-            syms |= rotate_exponent(sym) << (8 * n);
-            o4 += found;
-        }
-        o += found;
-        e.mask = uint16_t(e.mask | (1u << (o - 1)));
-        ++n;
-    }
-    e.step = n ? (n << 16) - o : kStepEscape;
-    const uint32_t n4 = std::min(n, 4u);
-    const uint32_t step4 = n ? (n4 << 16) - o4 : kStepEscape;
-    e.wsym = uint64_t(syms) | (uint64_t(step4) << 32);
-    return e;
-}
-
-void build_tables(const uint8_t len[256], uint32_t k, uint8_t *out) {
-    Canon c;
-    canonical(len, c, nullptr);
-    for (uint32_t w = 0; w < (1u << k); ++w) {
-        const Entry e = lut_entry(w, k, c);
-        store_le<uint32_t>(out + 4ull * w, e.step);
-        store_le<uint64_t>(out + tables_sym_off(k) + 8ull * w, e.wsym);
-        store_le<uint16_t>(out + tables_mask_off(k) + 2ull * w, e.mask);
-    }
-    uint8_t *limit = out + tables_limit_off(k), *first = out + tables_first_off(k), *base = out + tables_base_off(k);
-    std::memset(limit, 0, 3 * 128 + 256);
-    for (uint32_t l = 1; l <= kMaxLen; ++l) {
-        store_le<uint32_t>(limit + 4 * l, c.limit[l]);
-        store_le<uint32_t>(first + 4 * l, c.first[l]);
-        store_le<uint32_t>(base + 4 * l, c.base[l]);
-    }
-    std::memcpy(out + tables_order_off(k), c.order, c.n_used);
-}
-
 bool params_ok(const dfc_params &p) {
     const uint32_t C = p.chunk_bytes, T = p.lanes_per_block;
     if (C != 4 && C != 8 && C != 16 && C != 32) return false;
-    if (T != 64 && T != 128 && T != 256) return false;
+    // one wavefront (64 lanes) decodes a block: the only block width the
+    // decoders take, so the only one written
+    if (T != 64) return false;
     if (p.max_code_len < 1 || p.max_code_len > kMaxLen) return false;
     if (p.lut_bits < 8 || p.lut_bits > 12) return false;
     if (p.layout != DFC_LAYOUT_FLAT && p.layout != DFC_LAYOUT_PANEL && p.layout != DFC_LAYOUT_PADDED &&
@@ -187,7 +132,7 @@ bool params_ok(const dfc_params &p) {
     return true;
 }
 
-// Header, code lengths and decode tables of a container (sections zeroed).
+// Header and code lengths of a container (sections zeroed).
 void write_header(uint8_t *dst, const dfc_params &p, uint64_t n, uint64_t total_bits, uint64_t n_chunks,
                   uint64_t n_blocks, uint64_t rows, uint64_t cols, const SectionSizes &sz,
                   const uint64_t off[kNumSections], uint64_t blob_bytes, const uint8_t len[256]) {
@@ -212,7 +157,6 @@ void write_header(uint8_t *dst, const dfc_params &p, uint64_t n, uint64_t total_
     }
     store_le<uint64_t>(dst + hdr::blob_bytes, blob_bytes);
     std::memcpy(dst + hdr::lengths, len, 256);
-    build_tables(len, p.lut_bits, dst + off[kTables]);
 }
 
 void zero_parallel(uint8_t *dst, uint64_t bytes, uint32_t threads) {
@@ -742,12 +686,6 @@ dfc_status dfc_blob_info(const void *blob_v, uint64_t bytes, dfc_info *out) {
     in.coded_bytes = kHeaderBytes + sz.bytes[kWords] + sz.bytes[kOffsets] + sz.bytes[kBlockout] + sz.bytes[kRaw] +
                      sz.bytes[kPanels];
 
-    // Derived tables must match the lengths exactly.
-    {
-        std::vector<uint8_t> t(sz.bytes[kTables], 0);
-        build_tables(len, in.lut_bits, t.data());
-        if (std::memcmp(t.data(), b + off[kTables], t.size()) != 0) return DFC_ECORRUPT;
-    }
     // Panel table: chunk and block counts follow from every item's bits.
     std::vector<uint64_t> item_block;  // first block of every item (+ sentinel)
     if (panel) {

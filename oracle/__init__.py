@@ -21,6 +21,11 @@ Lossless LLM Compression for Efficient GPU Inference via Dynamic-Length Float
   and write positions through small auxiliary variables, then rebuild the
   weights.
 
+The oracle fixes what is coded and how the container lays it out.  The
+lookup tables of section 03 item 1 are a decoder's own means of finding code
+boundaries fast; they are a function of the code lengths, no container
+carries them, and nothing here builds them.
+
 Readings taken where the pages leave a step open (each is listed, with its
 reason, in the design notes of the repository):
 
@@ -38,7 +43,7 @@ Modules:
 * ``codebook`` - histogram, entropy, package-merge lengths, canonical codes
 * ``stream``   - bit packing, chunk/block metadata, sequential and
                  chunk-parallel decoders
-* ``blob``     - the serialized container and its derived decode tables
+* ``blob``     - the serialized container (code lengths and coded data)
 * ``gemm``     - float64 reference product and the panel element order
 * ``panel``    - the panel layout consumed by the fused decode + product
 * ``padded``   - the offset-free padded-chunk layout and its decoders

@@ -20,7 +20,7 @@ plainest standard choice is taken.
   words.  Encoding symbol s: if x >= f[s] * 2^20, emit x mod 2^16 and set
   x = x // 2^16 (at most once); then x = (x // f[s]) * M + x mod f[s] +
   cum[s].  Decoding inverts it: slot = x mod M, s is the symbol with cum[s]
-  <= slot < cum[s] + f[s], x = f[s] * (x // M) + slot - cum[s], and if x < L
+  <= slot < cum[s] + f[s], x = f[s] * (x // M) - cum[s] + slot, and if x < L
   the next word w is read: x = x * 2^16 + w.
 * Interleaving: a block is W = 64 lanes x S steps of elements; element
   j = i * W + l of the block (step i, lane l) is coded by lane l's state.
@@ -32,10 +32,8 @@ plainest standard choice is taken.
   decoder's initial states.  In a block's last step only the lanes whose
   element exists take part.
 * Container (header layout field 3): the code-lengths area is zero; the
-  tables section holds f[256] (u16) and the decode table (u32 per slot:
-  rotated exponent | (f - 1) << 8 | (slot - cum) << 20, where a rotated exponent is
-  the exponent byte rotated right by one bit, as in the Huffman tables); the
-  words section holds every block's stream (u16) back to back, the offsets
+  tables section holds f[256] (u16), from which a decoder builds whatever
+  slot lookup it uses; the words section holds every block's stream (u16) back to back, the offsets
   section the first word of every block (u32, n_blocks + 1 entries), the
   blockout section the W initial states of every block (u32), the raw
   section the raw bytes.  Header: chunk_bytes = 0, lanes_per_block = W,
@@ -92,18 +90,6 @@ def cumulative(f) -> np.ndarray:
     c = np.zeros(256, dtype=np.int64)
     c[1:] = np.cumsum(f)[:-1]
     return c
-
-
-def decode_table(f) -> np.ndarray:
-    """u32 per slot: rotated exponent | (f - 1) << 8 | (slot - cum) << 20
-    (the decoder's new state is then f * (x // M) + the top 12 bits)."""
-    f = np.asarray(f, dtype=np.int64)
-    c = cumulative(f)
-    t = np.zeros(M, dtype=np.uint32)
-    for s in range(256):
-        for k in range(int(f[s])):
-            t[c[s] + k] = bl.rotate_exponent(s) | ((int(f[s]) - 1) << 8) | (k << 20)
-    return t
 
 
 def symbol_of_slot(f) -> np.ndarray:
@@ -265,7 +251,7 @@ def decode_ans(enc) -> np.ndarray:
 # ---------------------------------------------------------------- container
 
 def tables_bytes() -> int:
-    return 2 * 256 + 4 * M
+    return 2 * 256
 
 
 def write_ans_blob(enc, rows: int | None = None, cols: int | None = None) -> bytes:
@@ -304,8 +290,7 @@ def write_ans_blob(enc, rows: int | None = None, cols: int | None = None) -> byt
         o = offsets[name]
         buf[o: o + len(data)] = data
 
-    put("tables", np.asarray(enc["freqs"], dtype="<u2").tobytes() +
-        decode_table(enc["freqs"]).astype("<u4").tobytes())
+    put("tables", np.asarray(enc["freqs"], dtype="<u2").tobytes())
     put("words", np.asarray(enc["words"], dtype="<u2").tobytes())
     put("offsets", np.asarray(enc["offsets"], dtype="<u4").tobytes())
     put("blockout", np.asarray(enc["states"], dtype="<u4").tobytes())
@@ -328,8 +313,7 @@ def parse_ans_blob(blob: bytes):
     states = (np.frombuffer(b, dtype="<u4", count=nb * p["lanes"], offset=sec["blockout"][0]).reshape(nb, p["lanes"])
               if nb else np.zeros((0, p["lanes"]), dtype=np.uint32))
     return {"n": p["n"], "lanes": p["lanes"], "steps": p["tile_k"], "freqs": freqs, "n_blocks": nb,
-            "states": states, "offsets": offsets, "words": words, "raw": p["raw"],
-            "table": np.frombuffer(b, dtype="<u4", count=M, offset=to + 512).copy()}
+            "states": states, "offsets": offsets, "words": words, "raw": p["raw"]}
 
 
 def decode_ans_blob(blob: bytes) -> np.ndarray:
@@ -339,8 +323,7 @@ def decode_ans_blob(blob: bytes) -> np.ndarray:
 
 def coded_bytes(enc) -> int:
     """Header, frequencies and the words, offsets, states and raw sections
-    (the slot table is derived from the frequencies and not counted; neither
-    is alignment padding between sections)."""
+    (alignment padding between sections is not counted)."""
     nw = int(enc["words"].size)
     return (bl.HEADER_BYTES + 512 + 2 * (-(-nw // 8) * 8 + 8) + 4 * (enc["n_blocks"] + 1) +
             4 * enc["lanes"] * enc["n_blocks"] + 16 * (-(-int(enc["n"]) // 16)))

@@ -1,4 +1,4 @@
-"""Serialized container ("DFC1") and its derived decode tables (oracle).
+"""Serialized container ("DFC1") of the flat and padded layouts (oracle).
 
 The container is one contiguous byte buffer so that one host-to-device copy
 moves it.  All integers are little-endian.
@@ -29,18 +29,16 @@ each starts at the next multiple of 256 bytes and padding is zero:
 * offsets: 5-bit fields off[0..n_chunks] packed as in ``stream.pack_offsets``
 * blockout: uint32 out[0..n_blocks]
 * raw: the raw bytes (sign << 7 | mantissa), padded to a multiple of 16
-* tables: derived from the code lengths alone (see ``decode_tables``).
+* tables: empty (offset and size 0) in the Huffman layouts.
 
-The decode tables are the "compact hierarchical lookup tables" of the
-DFloat11 blog (section 03 item 1): a first level indexed by the next k stream
-bits that resolves every whole code inside those k bits at once, and
-canonical per-length tables that resolve the rare codes longer than k bits.
-They are stored in the container so that a decoder only has to copy them
-into on-chip memory.
+A container holds the code (the code lengths) and the coded data only.  The
+lookup tables a decoder uses to find code boundaries quickly (the DFloat11
+blog's section 03 item 1) are a function of the code lengths, built by the
+decoder itself, and never written here; ``lut_bits`` only records the width
+of the first-level window the decoder should use.
 """
 from __future__ import annotations
 
-import math
 import struct
 
 import numpy as np
@@ -58,110 +56,12 @@ def _align(x: int, a: int = 256) -> int:
     return -(-x // a) * a
 
 
-# ------------------------------------------------------------ decode tables
-
-ESCAPE = 0xFFFFF000
-
-
-def rotate_exponent(e: int) -> int:
-    """The byte a decoder stages for exponent e: e rotated right by one bit
-    (bit 0 moves to bit 7).  With the raw byte sign << 7 | mantissa, the two
-    bytes of a bf16 value are then (e' & 0x80 | raw & 0x7F, raw & 0x80 |
-    e' & 0x7F), i.e. a byte-wise merge under a constant mask."""
-    return ((e >> 1) | ((e & 1) << 7)) & 0xFF
-
-
-def window_codes(window: int, k: int, tables):
-    """Codes that fit in a k-bit window (next k stream bits, first bit most
-    significant), decoded one after another from its first bit: a list of
-    (symbol, length)."""
-    out = []
-    o = 0
-    while o < k:
-        found = None
-        for l in range(1, k - o + 1):
-            v = (window >> (k - o - l)) & ((1 << l) - 1)
-            if v < tables["first"][l] + tables["count"][l]:
-                found = (tables["order"][tables["base"][l] + v - tables["first"][l]], l)
-                break
-        if found is None:
-            break
-        out.append(found)
-        o += found[1]
-    return out
-
-
-def step_value(codes) -> int:
-    """(c << 16) - b as a uint32 for c codes of total length b; 0xFFFFF000
-    when there are none.  Adding it to an accumulator (count << 16) + (bias -
-    position) advances both the code count and the bit position."""
-    if not codes:
-        return ESCAPE
-    return ((len(codes) << 16) - sum(l for _, l in codes)) & 0xFFFFFFFF
-
-
-def lut_entry(window: int, k: int, tables):
-    """(step, wsym, mask) for one k-bit window.
-
-    step: step_value of every whole code inside the window (counting pass).
-    wsym: uint64; bits 0..31 hold rotate_exponent of the first min(c, 4)
-          codes (byte j = code j, 0 past them), bits 32..63 the step_value of
-          those codes (symbol pass).
-    mask: uint16, bit j set when a code ends exactly j + 1 bits in.
-    """
-    codes = window_codes(window, k, tables)
-    first4 = codes[:4]
-    syms = 0
-    for j, (s, _) in enumerate(first4):
-        syms |= rotate_exponent(int(s)) << (8 * j)
-    wsym = syms | (step_value(first4) << 32)
-    mask = 0
-    o = 0
-    for _, l in codes:
-        o += l
-        mask |= 1 << (o - 1)
-    return step_value(codes), wsym, mask
-
-
-def decode_tables(lengths, lut_bits: int) -> bytes:
-    """The tables section for a window of k = lut_bits bits: step[2^k]
-    (uint32), wsym[2^k] (uint64), mask[2^k] (uint16), then limit[32],
-    first[32], base[32] (uint32, index = code length; entries 0 and 25..31
-    are 0) and the 256-byte list of used symbols ordered by (length,
-    symbol)."""
-    t = cb.canonical_tables(lengths)
-    if not 8 <= lut_bits <= 12:
-        raise ValueError("lut_bits must be in 8..12")
-    n = 1 << lut_bits
-    step = np.zeros(n, dtype=np.uint32)
-    wsym = np.zeros(n, dtype=np.uint64)
-    mask = np.zeros(n, dtype=np.uint16)
-    for w in range(n):
-        step[w], wsym[w], mask[w] = lut_entry(w, lut_bits, t)
-    limit = np.zeros(32, dtype=np.uint32)
-    first = np.zeros(32, dtype=np.uint32)
-    base = np.zeros(32, dtype=np.uint32)
-    for l in range(1, cb.MAX_LEN + 1):
-        limit[l] = t["limit"][l]
-        first[l] = t["first"][l]
-        base[l] = t["base"][l]
-    order = np.zeros(256, dtype=np.uint8)
-    order[: len(t["order"])] = t["order"]
-    return (step.astype("<u4").tobytes() + wsym.astype("<u8").tobytes() + mask.astype("<u2").tobytes() +
-            limit.astype("<u4").tobytes() + first.astype("<u4").tobytes() + base.astype("<u4").tobytes() +
-            order.tobytes())
-
-
-def tables_bytes(lut_bits: int) -> int:
-    return 14 * (1 << lut_bits) + 3 * 128 + 256
-
-
 # ----------------------------------------------------------------- container
 
-def section_sizes(enc, lut_bits: int):
+def section_sizes(enc):
     n = enc["n"]
     return {
-        "tables": tables_bytes(lut_bits),
+        "tables": 0,
         "words": 4 * enc["words"].size,
         "offsets": 0 if enc.get("off") is None else 4 * (-(-5 * (enc["n_chunks"] + 1) // 32) + 1),
         "blockout": 4 * (enc["n_blocks"] + 1),
@@ -179,7 +79,9 @@ def write_blob(enc, lut_bits: int = 11, rows: int | None = None, cols: int | Non
         rows, cols = 1, n
     if rows * cols != n:
         raise ValueError("rows * cols != n")
-    sizes = section_sizes(enc, lut_bits)
+    if not 8 <= lut_bits <= 12:
+        raise ValueError("lut_bits must be in 8..12")
+    sizes = section_sizes(enc)
     offsets = {}
     pos = HEADER_BYTES
     for name in ("tables", "words", "offsets", "blockout", "raw", "panels"):
@@ -202,7 +104,6 @@ def write_blob(enc, lut_bits: int = 11, rows: int | None = None, cols: int | Non
         o = offsets[name]
         buf[o: o + len(data)] = data
 
-    put("tables", decode_tables(enc["lengths"], lut_bits))
     put("words", np.asarray(enc["words"], dtype="<u4").tobytes())
     if sizes["offsets"]:
         put("offsets", st.pack_offsets(enc["off"]).astype("<u4").tobytes())
@@ -242,7 +143,6 @@ def parse_blob(blob: bytes):
         "rows": rows, "cols": cols, "tile_k": tile_k, "sections": sec,
         "blob_bytes": vals[12], "lengths": lengths, "words": words, "off": offsets,
         "out": out, "raw": raw,
-        "tables": b[sec["tables"][0]: sec["tables"][0] + sec["tables"][1]],
     }
 
 
@@ -264,8 +164,7 @@ def decode_blob(blob: bytes) -> np.ndarray:
 
 def coded_bytes(p) -> int:
     """Bytes a reader must store: header, code lengths, stream, offsets, block
-    offsets and raw bytes.  Alignment padding and the derived decode tables
-    (a pure function of the code lengths) are not counted."""
+    offsets and raw bytes.  Alignment padding is not counted."""
     s = p["sections"]
     return HEADER_BYTES + sum(s[nm][1] for nm in ("words", "offsets", "blockout", "raw", "panels"))
 
@@ -275,6 +174,3 @@ def entropy_bound_bytes(hist) -> float:
     n = float(np.asarray(hist, dtype=np.float64).sum())
     return n * (8.0 + cb.entropy_bits(hist)) / 8.0
 
-
-def log2(x):
-    return math.log2(x)

@@ -27,7 +27,7 @@ ones, so no codeword can be a prefix of r ones (it would be a proper prefix of
 another codeword), and whatever the tail and the next chunk's bits decode to
 is longer than r and ends past the chunk.
 
-Everything else (code, tables, bit order, raw bytes, header) is the flat
+Everything else (code, bit order, raw bytes, header) is the flat
 layout's; the header's layout field is 2.
 """
 from __future__ import annotations

@@ -25,7 +25,7 @@ layout for decoding straight into a matrix product.  The reading taken here:
 * a table of items + 1 entries (first chunk, first block, code bits of the
   item, 0), the last entry (n_chunks, n_blocks, 0, 0).
 
-Everything else (codebook, tables, bit order, raw bytes) is the flat layout's,
+Everything else (codebook, bit order, raw bytes) is the flat layout's,
 applied to the permuted sequence.
 """
 from __future__ import annotations
@@ -122,8 +122,10 @@ def encode_panel(bits: np.ndarray, panel_k: int = 1024, chunk_bytes: int = 16, l
 def write_panel_blob(enc, lut_bits: int = 11) -> bytes:
     """The DFC1 container of a panel-layout encoding."""
     n = enc["n"]
+    if not 8 <= lut_bits <= 12:
+        raise ValueError("lut_bits must be in 8..12")
     sizes = {
-        "tables": bl.tables_bytes(lut_bits),
+        "tables": 0,
         "words": 4 * enc["words"].size,
         "offsets": 4 * (-(-5 * (enc["n_chunks"] + 1) // 32) + 1),
         "blockout": 4 * (enc["n_blocks"] + 1),
@@ -153,7 +155,6 @@ def write_panel_blob(enc, lut_bits: int = 11) -> bytes:
         o = offsets[name]
         buf[o: o + len(data)] = data
 
-    put("tables", bl.decode_tables(enc["lengths"], lut_bits))
     put("words", np.asarray(enc["words"], dtype="<u4").tobytes())
     put("offsets", st.pack_offsets(enc["off"]).astype("<u4").tobytes())
     put("blockout", np.asarray(enc["out"], dtype="<u4").tobytes())

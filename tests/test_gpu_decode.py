@@ -179,9 +179,13 @@ def test_invalid_arguments_rejected():
     assert s == dfc.EINVAL
     s = lib.dfc_decode(dev.data_ptr(), info, out.data_ptr(), info.n + 1, None, None)
     assert s == dfc.ESIZE
-    b128 = dfc.encode(x, lanes=128)
-    s = lib.dfc_decode(torch.from_numpy(b128).cuda().data_ptr(), dfc.blob_info(b128),
-                                 out.data_ptr(), info.n, None, None)
+    # a block wider than one wavefront is refused at encode time, and a
+    # description claiming one is refused before launch
+    with pytest.raises(dfc.DfcError):
+        dfc.encode(x, lanes=128)
+    wide = dfc.blob_info(blob)
+    wide.lanes_per_block = 128
+    s = lib.dfc_decode(dev.data_ptr(), wide, out.data_ptr(), info.n, None, None)
     assert s == dfc.EUNSUPPORTED
     # the binding refuses a device container shorter than its info, a host
     # container and a status word that is not 32-bit, before any launch

@@ -56,12 +56,25 @@ def test_encoder_matches_oracle_bytes(C, kind):
         assert bytes(lib_blob) == oracle_blob(x, C, 64, k)
 
 
-@pytest.mark.parametrize("T", [64, 128, 256])
-def test_encoder_lanes_and_threads(T):
+def test_encoder_threads():
     x = synth.gaussian((3000, 1000), 0.02, (26,))  # 3M elements -> several encoder threads
     for threads in (1, 3, 8):
-        b = dfc.encode(x, chunk_bytes=8, lanes=T, threads=threads)
-        assert bytes(b) == oracle_blob(x, 8, T), threads
+        b = dfc.encode(x, chunk_bytes=8, threads=threads)
+        assert bytes(b) == oracle_blob(x, 8, 64), threads
+
+
+@pytest.mark.parametrize("layout", [0, 1, 2, 3])
+@pytest.mark.parametrize("T", [32, 128, 256])
+def test_encoder_refuses_blocks_wider_than_a_wavefront(T, layout):
+    """One wavefront (64 lanes) decodes one block, so 64 chunks per block is
+    the only width the encoder writes: a container no decoder could take is
+    refused before anything is written."""
+    x = synth.gaussian((64, 256), 0.02, (27,))
+    with pytest.raises(dfc.DfcError) as e:
+        dfc.encode(x, lanes=T, layout=layout)
+    assert e.value.status == dfc.EINVAL
+    with pytest.raises(dfc.DfcError):
+        dfc.encode_bound(x.size, dfc.default_params(lanes_per_block=T, layout=layout))
 
 
 def test_edge_sizes_match_oracle():
@@ -136,7 +149,8 @@ def test_validation_rejects_corruption():
         "total_bits": (corrupt(b, 16, struct.pack("<Q", info.total_bits + 8 * 16 * 64)), dfc.ECORRUPT),
         "length>24": (corrupt(b, 256 + 120, bytes([25])), dfc.ECORRUPT),
         "kraft": (corrupt(b, 256 + int(np.argmax(b[256:512])), bytes([int(b[256:512].max()) + 1])), dfc.ECORRUPT),
-        "table": (corrupt(b, info.off_tables + 8, b"\x01"), dfc.ECORRUPT),
+        # a tables section where the Huffman layouts have none
+        "tables section": (corrupt(b, 88, struct.pack("<QQ", 512, 256)), dfc.ECORRUPT),
         "section": (corrupt(b, 88 + 16, struct.pack("<Q", info.off_words + 256)), dfc.ECORRUPT),
         "blockout_end": (corrupt(b, info.off_blockout + 4 * info.n_blocks, struct.pack("<I", info.n - 1)), dfc.ECORRUPT),
         "blockout_order": (corrupt(b, info.off_blockout + 4, struct.pack("<I", 0xFFFFFF)), dfc.ECORRUPT),
@@ -266,10 +280,9 @@ def test_padded_encoder_matches_oracle_bytes(C, kind):
 
 def test_padded_lanes_threads_and_edge_sizes():
     x = synth.gaussian_with_outliers((2500, 1000), 0.02, (64,))
-    for T in (64, 128, 256):
-        for threads in (1, 5, 16):
-            b = dfc.encode(x, chunk_bytes=8, lanes=T, threads=threads, layout=dfc.LAYOUT_PADDED)
-            assert bytes(b) == oracle_padded_blob(x, 8, T), (T, threads)
+    for threads in (1, 5, 16):
+        b = dfc.encode(x, chunk_bytes=8, threads=threads, layout=dfc.LAYOUT_PADDED)
+        assert bytes(b) == oracle_padded_blob(x, 8, 64), threads
     for n in (0, 1, 2, 15, 16, 17, 63, 64, 65, 1000):
         y = synth.uniform_bits((n,), (65, n))
         for C in (4, 32):
@@ -398,7 +411,7 @@ def test_ans_validation_rejects_corruption():
         "lengths area": corrupt(b, 300, b"\x01"),
         "freq sum": corrupt(b, t + 2 * int(np.argmax(np.frombuffer(bytes(b[t: t + 512]), dtype="<u2"))),
                             struct.pack("<H", 1)),
-        "slot table": corrupt(b, t + 512 + 40, b"\x07"),
+        "frequency table size": corrupt(b, 96, struct.pack("<Q", 512 + 4 * 4096)),
         "offsets end": corrupt(b, info.off_offsets + 4 * info.n_blocks, struct.pack("<I", 1)),
         "offsets order": corrupt(b, info.off_offsets + 4, struct.pack("<I", 0xFFFFFF)),
         "state below 2^16": corrupt(b, info.off_blockout + 8, struct.pack("<I", 5)),

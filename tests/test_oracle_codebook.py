@@ -148,6 +148,40 @@ def test_dyadic_lengths_closed_form():
     assert cb.mean_code_length(h, lens) == pytest.approx(cb.entropy_bits(h))
 
 
+@pytest.mark.parametrize("counts,depth", [
+    ([5], 1),                      # one symbol: one bit under the single-symbol reading
+    ([1, 1], 1),
+    ([1, 1, 1, 1], 2),             # balanced: 2 bits each
+    ([1, 1, 1, 1, 1], 3),          # lengths 2, 2, 2, 3, 3
+    ([4, 2, 1, 1], 3),             # dyadic: lengths 1, 2, 3, 3
+    ([1, 1, 2, 4, 8], 4),          # doubling: 8 -> 1, 4 -> 2, 2 -> 3, 1 and 1 -> 4
+    ([1] * 256, 8),
+    ([1] * 257 + [0] * 3, 9),      # (counts past 256 symbols only for the tree)
+])
+def test_huffman_depth_hand_worked(counts, depth):
+    """Depths of textbook Huffman trees worked by hand: the longest code of an
+    optimal unconstrained code for these counts."""
+    assert cb.huffman_depth(np.array(counts, dtype=np.uint64)) == depth
+
+
+def test_huffman_depth_fibonacci_and_empty():
+    # Fibonacci counts make the textbook tree a chain: each merge joins the
+    # next leaf and the running package (fib[i + 1] < fib[i + 2] - 1 <
+    # fib[i + 2]), so 40 leaves sit at depths 1 .. 39 (the two lightest at 39)
+    fib = [1, 1]
+    while len(fib) < 40:
+        fib.append(fib[-1] + fib[-2])
+    assert cb.huffman_depth(np.array(fib, dtype=np.uint64)) == 39
+    assert cb.huffman_depth(np.array(fib[:25], dtype=np.uint64)) == 24
+    assert cb.huffman_depth(np.zeros(256, dtype=np.uint64)) == 0
+    # the depth equals the longest of the package-merge lengths whenever the
+    # limit does not bind
+    rng = np.random.default_rng(12)
+    for _ in range(30):
+        h = hist_from([int(x) for x in rng.integers(1, 1 << 12, 40)], list(range(40)))
+        assert cb.huffman_depth(h) == int(cb.package_merge_lengths(h, 24).max())
+
+
 def test_limit_binds_on_deep_ladder():
     # Fibonacci-like counts force an unconstrained depth > 24
     fib = [1, 1]
