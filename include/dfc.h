@@ -150,6 +150,8 @@ typedef struct {
     const dfc_info *info;  /* host description of that container (from dfc_blob_info) */
     uint16_t *dst_dev;     /* n bf16 outputs (16-byte aligned), row-major */
     uint64_t n;            /* must equal info->n */
+    const void *tables_dev; /* NULL, or this container's decode tables from dfc_derive_tables
+                               (16-byte aligned): see dfc_decode */
 } dfc_batch_item;
 
 /* Fills *p with the defaults (C = 16, T = 64, limit 24, k = 11, flat). */
@@ -195,7 +197,13 @@ dfc_status dfc_blob_info(const void *blob, uint64_t bytes, dfc_info *out);
 /* Decode one container on the GPU (DFloat11 blog, section 03: the two-phase
  * kernel with lookup tables in on-chip memory).  Device, asynchronous on
  * stream.  blob_dev: device copy of the container described by info (256-byte
- * aligned), in the FLAT, PADDED or ANS layout.  dst_dev: n uint16 outputs
+ * aligned), in the FLAT, PADDED or ANS layout.  tables_dev: NULL, or the
+ * decode tables dfc_derive_tables wrote for this container (16-byte aligned):
+ * every workgroup then copies them into LDS instead of deriving them from
+ * the code (a few microseconds per workgroup, which matters for small
+ * launches; prepare them once per container and reuse them).  Tables of
+ * another container give wrong values or a corrupt-block status; bytes that
+ * dfc_derive_tables did not write are not allowed.  dst_dev: n uint16 outputs
  * (16-byte aligned), receives the original bf16 bit patterns, row-major.
  * status_dev: NULL, or one device uint32 that the kernel sets to DFC_ECORRUPT
  * (its two's-complement bit pattern) when a block fails its check: a decoded
@@ -207,8 +215,8 @@ dfc_status dfc_blob_info(const void *blob, uint64_t bytes, dfc_info *out);
  * DFC_ESIZE (n != info->n), DFC_EUNSUPPORTED (lanes_per_block != 64, a
  * PANEL container, streams past 4 GiB), DFC_EHIP (launch failure).  The ANS
  * layout is the interleaved rANS variant (see DFC_LAYOUT_ANS above). */
-dfc_status dfc_decode(const void *blob_dev, const dfc_info *info, uint16_t *dst_dev, uint64_t n,
-                      uint32_t *status_dev, void *stream);
+dfc_status dfc_decode(const void *blob_dev, const dfc_info *info, const void *tables_dev, uint16_t *dst_dev,
+                      uint64_t n, uint32_t *status_dev, void *stream);
 
 /* Decode up to DFC_MAX_BATCH containers with one kernel launch (the
  * whole-model, matrix-by-matrix decode just before use that the DFloat11
@@ -225,6 +233,8 @@ enum { DFC_GEMM_MAX_BATCH = 64 };
  * HBM).  Device, asynchronous on stream.
  * w_blob_dev: device copy (256-byte aligned) of a DFC_LAYOUT_PANEL container
  * of W (M x K bf16, M = info->rows, K = info->cols), described by info.
+ * tables_dev: NULL or its decode tables from dfc_derive_tables, as in
+ * dfc_decode.
  * x_dev: B activation vectors of K bf16 each, x_dev[b K + k] (i.e. X is
  * K x B column-major), 16-byte aligned.  batch: B, 1..DFC_GEMM_MAX_BATCH.
  * y_dev: B output vectors of M fp32, y_dev[b M + m] (Y = W X, M x B
@@ -241,8 +251,8 @@ enum { DFC_GEMM_MAX_BATCH = 64 };
  * misaligned pointers, batch out of range, bad decode parameters),
  * DFC_EUNSUPPORTED (not a panel-layout container, lanes_per_block != 64,
  * streams or Y past 4 GiB), DFC_EHIP (launch failure). */
-dfc_status dfc_decode_gemm(const void *w_blob_dev, const dfc_info *info, const uint16_t *x_dev, uint32_t batch,
-                           float *y_dev, uint32_t *status_dev, void *stream);
+dfc_status dfc_decode_gemm(const void *w_blob_dev, const dfc_info *info, const void *tables_dev, const uint16_t *x_dev,
+                           uint32_t batch, float *y_dev, uint32_t *status_dev, void *stream);
 
 /* Workspace bytes dfc_encode_device needs for n elements.  Host. */
 dfc_status dfc_encode_device_workspace(uint64_t n, uint64_t *bytes);
@@ -293,15 +303,17 @@ dfc_status dfc_set_launch(uint32_t waves_per_group, uint32_t blocks_per_wave);
  * 4 * 2^12 bytes.  DFC_EINVAL / DFC_EUNSUPPORTED on a bad info. */
 dfc_status dfc_derived_tables_bytes(const dfc_info *info, uint64_t *bytes);
 
-/* Diagnostic: one workgroup of `threads` threads (a multiple of 64, at most
- * 1024; 0 = 256) derives the decode tables of a container exactly as every
- * decoding workgroup does in its LDS (DFloat11 blog, section 03 item 1:
- * compact lookup tables in on-chip memory), and writes them to dst_dev
- * (cap >= dfc_derived_tables_bytes, 16-byte aligned).  Device,
- * asynchronous.  The layout of these bytes is private to the library and
- * may change; they exist so that tests can check the derivation itself.
- * Errors: DFC_EINVAL (null or misaligned pointers, bad thread count, an
- * empty container), DFC_ESIZE (cap), DFC_EHIP. */
+/* The decode tables of a container (DFloat11 blog, section 03 item 1:
+ * compact lookup tables in on-chip memory), derived from its code by one
+ * workgroup of `threads` threads (a multiple of 64, at most 1024; 0 = 1024)
+ * with the same device code every decoding workgroup runs when it is given
+ * no tables, and written to dst_dev (cap >= dfc_derived_tables_bytes,
+ * 16-byte aligned).  Device, asynchronous.  Pass them to dfc_decode,
+ * dfc_decode_batch (tables_dev of the item) or dfc_decode_gemm to skip the
+ * derivation in every launch.  Their layout is private to the library (and
+ * may change with it); tests read them to check the derivation.  Errors:
+ * DFC_EINVAL (null or misaligned pointers, bad thread count, an empty
+ * container), DFC_ESIZE (cap), DFC_EHIP. */
 dfc_status dfc_derive_tables(const void *blob_dev, const dfc_info *info, uint32_t threads, void *dst_dev,
                              uint64_t cap, void *stream);
 

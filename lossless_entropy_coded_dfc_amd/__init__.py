@@ -85,7 +85,7 @@ class Info(ctypes.Structure):
 
 class BatchItem(ctypes.Structure):
     _fields_ = [("blob_dev", ctypes.c_void_p), ("info", ctypes.POINTER(Info)),
-                ("dst_dev", ctypes.c_void_p), ("n", ctypes.c_uint64)]
+                ("dst_dev", ctypes.c_void_p), ("n", ctypes.c_uint64), ("tables_dev", ctypes.c_void_p)]
 
 
 def library_path() -> str:
@@ -117,14 +117,14 @@ def library():
     lib.dfc_encode.restype = st
     lib.dfc_blob_info.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.POINTER(Info)]
     lib.dfc_blob_info.restype = st
-    lib.dfc_decode.argtypes = [ctypes.c_void_p, ctypes.POINTER(Info), ctypes.c_void_p, ctypes.c_uint64,
-                               ctypes.c_void_p, ctypes.c_void_p]
+    lib.dfc_decode.argtypes = [ctypes.c_void_p, ctypes.POINTER(Info), ctypes.c_void_p, ctypes.c_void_p,
+                               ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
     lib.dfc_decode.restype = st
     lib.dfc_decode_batch.argtypes = [ctypes.POINTER(BatchItem), ctypes.c_uint32, ctypes.c_void_p,
                                      ctypes.c_void_p]
     lib.dfc_decode_batch.restype = st
-    lib.dfc_decode_gemm.argtypes = [ctypes.c_void_p, ctypes.POINTER(Info), ctypes.c_void_p, ctypes.c_uint32,
-                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.dfc_decode_gemm.argtypes = [ctypes.c_void_p, ctypes.POINTER(Info), ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     lib.dfc_decode_gemm.restype = st
     lib.dfc_encode_device_workspace.argtypes = [ctypes.c_uint64, u64p]
     lib.dfc_encode_device_workspace.restype = st
@@ -277,25 +277,41 @@ def _status_ptr(status) -> int:
     return _dev_ptr(status)
 
 
-def decode(blob_dev, info: Info, out, status=None, stream=None):
+def _tables_ptr(tables, info: Info) -> int:
+    """Device address of prepared decode tables (from ``derive_tables``), or 0."""
+    if tables is None:
+        return 0
+    if not getattr(tables, "is_cuda", False) or not tables.is_contiguous():
+        raise TypeError("tables must be a contiguous device tensor from derive_tables")
+    if tables.numel() * tables.element_size() < derived_tables_bytes(info):
+        raise ValueError("tables are shorter than the container's decode tables")
+    return tables.data_ptr()
+
+
+def decode(blob_dev, info: Info, out, status=None, stream=None, tables=None):
     """Decode a container held in device memory (torch uint8 tensor) into
-    ``out`` (torch tensor of info.n 16-bit elements).  Asynchronous."""
+    ``out`` (torch tensor of info.n 16-bit elements).  ``tables``: the
+    container's decode tables from ``derive_tables`` (else every workgroup
+    derives them).  Asynchronous."""
     if not out.is_contiguous() or out.element_size() != 2 or out.numel() != info.n:
         raise ValueError("out must be a contiguous 16-bit tensor with info.n elements")
     _check(library().dfc_decode(ctypes.c_void_p(_blob_ptr(blob_dev, info)), ctypes.byref(info),
-                                ctypes.c_void_p(_dev_ptr(out)), info.n,
+                                ctypes.c_void_p(_tables_ptr(tables, info)), ctypes.c_void_p(_dev_ptr(out)), info.n,
                                 ctypes.c_void_p(_status_ptr(status)), _stream(stream)), "dfc_decode")
     return out
 
 
 def decode_batch(items, status=None, stream=None):
-    """Decode up to MAX_BATCH (blob_dev, info, out) triples with one launch."""
+    """Decode up to MAX_BATCH (blob_dev, info, out) or (blob_dev, info, out,
+    tables) tuples with one launch."""
     items = list(items)
     if len(items) > MAX_BATCH:
         raise ValueError(f"at most {MAX_BATCH} items per batch")
     arr = (BatchItem * max(1, len(items)))()
     keep = []
-    for k, (blob_dev, info, out) in enumerate(items):
+    for k, item in enumerate(items):
+        blob_dev, info, out = item[:3]
+        tables = item[3] if len(item) > 3 else None
         if not out.is_contiguous() or out.element_size() != 2 or out.numel() != info.n:
             raise ValueError("out must be a contiguous 16-bit tensor with info.n elements")
         keep.append(info)
@@ -303,6 +319,7 @@ def decode_batch(items, status=None, stream=None):
         arr[k].info = ctypes.pointer(info)
         arr[k].dst_dev = _dev_ptr(out)
         arr[k].n = info.n
+        arr[k].tables_dev = _tables_ptr(tables, info)
     _check(library().dfc_decode_batch(arr, len(items), ctypes.c_void_p(_status_ptr(status)), _stream(stream)),
            "dfc_decode_batch")
 
@@ -344,10 +361,11 @@ def encode_device(src, chunk_bytes: int = 16, lanes: int = 64, max_code_len: int
 GEMM_MAX_BATCH = 64
 
 
-def decode_gemm(blob_dev, info: Info, x, y, status=None, stream=None):
+def decode_gemm(blob_dev, info: Info, x, y, status=None, stream=None, tables=None):
     """Fused decode + product: y[b, :] = W @ x[b, :] for a panel-layout
     container of W (M x K).  x: contiguous 16-bit device tensor of shape
-    (B, K) (bf16 bits); y: contiguous float32 device tensor of shape (B, M)."""
+    (B, K) (bf16 bits); y: contiguous float32 device tensor of shape (B, M);
+    tables: as in ``decode``."""
     if info.layout != LAYOUT_PANEL:
         raise ValueError("decode_gemm needs a panel-layout container")
     if x.dim() != 2 or y.dim() != 2 or not x.is_contiguous() or not y.is_contiguous():
@@ -357,7 +375,7 @@ def decode_gemm(blob_dev, info: Info, x, y, status=None, stream=None):
     if x.element_size() != 2 or K != info.cols or tuple(y.shape) != (B, info.rows) or y.dtype != torch.float32:
         raise ValueError("x must be (B, K) 16-bit and y (B, M) float32 for the container's M x K")
     _check(library().dfc_decode_gemm(ctypes.c_void_p(_blob_ptr(blob_dev, info)), ctypes.byref(info),
-                                     ctypes.c_void_p(_dev_ptr(x)), B, ctypes.c_void_p(_dev_ptr(y)),
+                                     ctypes.c_void_p(_tables_ptr(tables, info)), ctypes.c_void_p(_dev_ptr(x)), B, ctypes.c_void_p(_dev_ptr(y)),
                                      ctypes.c_void_p(_status_ptr(status)), _stream(stream)), "dfc_decode_gemm")
 
 
@@ -368,9 +386,10 @@ def derived_tables_bytes(info: Info) -> int:
 
 
 def derive_tables(blob_dev, info: Info, threads: int = 0, stream=None):
-    """The decode tables the GPU kernels derive from the container's code, as
-    one workgroup of ``threads`` threads builds them in LDS (a device uint8
-    tensor; the byte layout is the library's own).  Asynchronous."""
+    """The decode tables of a container, derived from its code on the GPU by
+    one workgroup of ``threads`` threads (0 = 1024) exactly as a decoding
+    workgroup builds them in LDS: a device uint8 tensor (the byte layout is
+    the library's own) to pass as ``tables`` to the decoders.  Asynchronous."""
     import torch
     nbytes = derived_tables_bytes(info)
     out = torch.empty(nbytes, dtype=torch.uint8, device=blob_dev.device)

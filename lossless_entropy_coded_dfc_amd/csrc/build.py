@@ -1,4 +1,5 @@
-"""Build libdfc.so in place (host codec with g++, gfx950 decoder with hipcc).
+"""Build libdfc.so in place (host codec with g++, gfx950 decoder with hipcc),
+and libdfc_probe.so, the benchmark's streaming-ceiling kernel.
 
 Usage: python -m lossless_entropy_coded_dfc_amd.csrc.build [-v]
 """
@@ -14,6 +15,8 @@ PKG = os.path.dirname(HERE)
 ROOT = os.path.dirname(PKG)
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libdfc.so")
+# the benchmark's streaming ceiling (not part of the codec)
+PROBE_OUT = os.path.join(PKG, "libdfc_probe.so")
 ARCH = "gfx950"
 
 # Packed FP32 instructions are kept out of every HIP object.  Unaligned
@@ -59,6 +62,10 @@ def build(verbose: bool = False, out: str = OUT) -> str:
     tmp = out + ".tmp"
     _run([hipcc, "-shared", f"--offload-arch={ARCH}", "-fPIC", "-o", tmp, *host_objs, *dev_objs, "-pthread"], verbose)
     os.replace(tmp, out)
+    if out == OUT:
+        tmp = PROBE_OUT + ".tmp"
+        _run([hipcc, *HIP_FLAGS, "-shared", "-o", tmp, os.path.join(HERE, "dfc_probe.hip")], verbose)
+        os.replace(tmp, PROBE_OUT)
     return out
 
 

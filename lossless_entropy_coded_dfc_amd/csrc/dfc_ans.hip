@@ -49,6 +49,7 @@ struct AnsItem {
     const uint32_t *states;    // 64 initial states per block
     const uint8_t *raw;        // raw bytes, padded to 16
     const uint16_t *freqs;     // quantised frequencies f[256] (sum 4096)
+    const uint32_t *table;     // slot table from dfc_derive_tables, or null: derive it here
     uint16_t *dst;
     uint32_t words_bytes, states_bytes, raw_bytes, dst_bytes;
     uint32_t n, n_blocks, steps;
@@ -73,8 +74,15 @@ __global__ __launch_bounds__(kAnsWaves * kWave) void dfc_ans_kernel(const AnsBat
         if (wg >= args.item[k].wg_begin) it = k;
     const AnsItem a = args.item[it];
 
-    // the slot table from the frequencies (the stage areas serve as scratch)
-    derive_slot_table(table, &stage_all[0][0], a.freqs);
+    // the slot table: prepared, or derived from the frequencies (the stage
+    // areas serve as scratch)
+    if (a.table) {
+        for (uint32_t o = threadIdx.x; o < dfc::kAnsSlots / 4; o += blockDim.x)
+            reinterpret_cast<uint4 *>(table)[o] = reinterpret_cast<const uint4 *>(a.table)[o];
+        __syncthreads();
+    } else {
+        derive_slot_table(table, &stage_all[0][0], a.freqs);
+    }
 
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const uint32_t lane = threadIdx.x % kWave;
@@ -265,6 +273,7 @@ dfc_status ans_launch(const dfc_batch_item *items, const uint32_t *idx, uint32_t
         a.states = reinterpret_cast<const uint32_t *>(base + in.off_blockout);
         a.raw = base + in.off_raw;
         a.freqs = reinterpret_cast<const uint16_t *>(base + in.off_tables);
+        a.table = static_cast<const uint32_t *>(bi.tables_dev);
         a.dst = bi.dst_dev;
         a.words_bytes = uint32_t(in.words_bytes);
         a.states_bytes = uint32_t(in.blockout_bytes);

@@ -42,6 +42,7 @@ struct ItemArgs {
     const uint32_t *blockout;  // u32 out[n_blocks + 1]
     const uint8_t *raw;        // raw bytes (sign << 7 | mantissa), padded to 16
     const uint8_t *lengths;    // the 256 code lengths (container bytes 256..511)
+    const uint8_t *tables;     // tables from dfc_derive_tables, or null: derive them here
     uint16_t *dst;             // bf16 output
     uint64_t total_bits;
     uint32_t words_bytes, offw_bytes, raw_bytes, dst_bytes;  // buffer ranges
@@ -223,9 +224,6 @@ __global__ __launch_bounds__(1024, Occupancy<C>::kWavesPerSimd) void dfc_decode_
     const Buffers bf = make_buffers(a);
     const const_u32_ptr blockout = (const_u32_ptr)(a.blockout);
 
-    derive_tables(lds, lds + a.tables_bytes, a.lengths, a.lut_bits);
-    const Tables t = tables_view(lds, a.lut_bits);
-
     const uint32_t waves = __builtin_amdgcn_readfirstlane(blockDim.x / kWave);
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const uint32_t lane = threadIdx.x % kWave;
@@ -234,11 +232,20 @@ __global__ __launch_bounds__(1024, Occupancy<C>::kWavesPerSimd) void dfc_decode_
     const uint32_t lo_b = (wg - a.wg_begin) * a.blocks_per_wg;
     const uint32_t hi_b = min(lo_b + a.blocks_per_wg, a.n_blocks);
 
+    // The first block's stream words and output range are requested before
+    // the tables are derived (the derivation's barriers wait for LDS only),
+    // so their memory latency overlaps it.
     uint32_t b = lo_b + wave;
+    Chunk<C> cur{};
+    uint32_t s_out = 0, e_out = 0;
+    if (b < hi_b) {
+        load_chunk<C, !Padded>(bf.words, bf.offw, b * kWave + lane, cur);
+        s_out = blockout[b];
+        e_out = blockout[b + 1];
+    }
+    load_or_derive_tables(lds, a.tables, a.tables_bytes, a.lengths, a.lut_bits);
+    const Tables t = tables_view(lds, a.lut_bits);
     if (b >= hi_b) return;
-    Chunk<C> cur;
-    load_chunk<C, !Padded>(bf.words, bf.offw, b * kWave + lane, cur);
-    uint32_t s_out = blockout[b], e_out = blockout[b + 1];
     // Resident on entry, as it is on every later iteration (see wait_for).
     wait_for(cur);
     for (;;) {
@@ -323,7 +330,7 @@ dfc_status launch_group(const dfc_batch_item *items, const uint32_t *idx, uint32
         live.push_back(idx[k]);
         blocks.push_back(in.n_blocks);
         max_tables = std::max<uint32_t>(max_tables, uint32_t(dfc::tables_bytes(in.lut_bits)));
-        max_scratch = std::max<uint32_t>(max_scratch, derive_scratch_bytes(in.lut_bits));
+        if (!items[idx[k]].tables_dev) max_scratch = std::max<uint32_t>(max_scratch, derive_scratch_bytes(in.lut_bits));
         max_block = std::max(max_block, in.max_block_elems);
     }
     if (live.empty()) return DFC_OK;
@@ -384,6 +391,7 @@ dfc_status launch_group(const dfc_batch_item *items, const uint32_t *idx, uint32
         a.blockout = reinterpret_cast<const uint32_t *>(base + in.off_blockout);
         a.raw = base + in.off_raw;
         a.lengths = base + dfc::hdr::lengths;
+        a.tables = static_cast<const uint8_t *>(bi.tables_dev);
         a.dst = bi.dst_dev;
         a.words_bytes = uint32_t(in.words_bytes);
         a.offw_bytes = uint32_t(in.offsets_bytes);
@@ -410,7 +418,8 @@ dfc_status check_item(const dfc_batch_item &it) {
     if (it.n != in.n) return DFC_ESIZE;
     if (in.n == 0) return DFC_OK;
     if (!it.blob_dev || !it.dst_dev) return DFC_EINVAL;
-    if ((reinterpret_cast<uintptr_t>(it.blob_dev) & 255u) || (reinterpret_cast<uintptr_t>(it.dst_dev) & 15u))
+    if ((reinterpret_cast<uintptr_t>(it.blob_dev) & 255u) || (reinterpret_cast<uintptr_t>(it.dst_dev) & 15u) ||
+        (reinterpret_cast<uintptr_t>(it.tables_dev) & 15u))
         return DFC_EINVAL;
     if (in.layout == DFC_LAYOUT_ANS) return dfc::ans_check_item(it);
     if (in.layout != DFC_LAYOUT_FLAT && in.layout != DFC_LAYOUT_PADDED) return DFC_EUNSUPPORTED;
@@ -459,7 +468,7 @@ dfc_status dfc_derive_tables(const void *blob_dev, const dfc_info *info, uint32_
     if (!blob_dev || !dst_dev || (reinterpret_cast<uintptr_t>(blob_dev) & 255u) ||
         (reinterpret_cast<uintptr_t>(dst_dev) & 15u))
         return DFC_EINVAL;
-    if (threads == 0) threads = 256;
+    if (threads == 0) threads = 1024;
     if (threads % kWave || threads > 1024) return DFC_EINVAL;
     if (cap < need) return DFC_ESIZE;
     if (info->n == 0) return DFC_EINVAL;  // an empty container has no code
@@ -518,11 +527,12 @@ dfc_status dfc_decode_batch(const dfc_batch_item *items, uint32_t count, uint32_
     return DFC_OK;
 }
 
-dfc_status dfc_decode(const void *blob_dev, const dfc_info *info, uint16_t *dst_dev, uint64_t n,
-                      uint32_t *status_dev, void *stream) {
+dfc_status dfc_decode(const void *blob_dev, const dfc_info *info, const void *tables_dev, uint16_t *dst_dev,
+                      uint64_t n, uint32_t *status_dev, void *stream) {
     dfc_batch_item it;
     it.blob_dev = blob_dev;
     it.info = info;
+    it.tables_dev = tables_dev;
     it.dst_dev = dst_dev;
     it.n = n;
     return dfc_decode_batch(&it, 1, status_dev, stream);

@@ -347,6 +347,22 @@ __device__ __forceinline__ u32x4 assemble8(const u32x2 &E, const u32x2 &R) {
     return u32x4{o[0], o[1], o[2], o[3]};
 }
 
+// The decode tables of a container into LDS at `lds`: copied from `tables`
+// (what dfc_derive_tables wrote for the container, tables_bytes bytes, a
+// multiple of 16) when there are any, else derived from the code lengths,
+// with the LDS after the tables as scratch.  Every thread of the workgroup
+// calls it; it ends with a barrier.
+__device__ __forceinline__ void load_or_derive_tables(uint8_t *lds, const uint8_t *tables, uint32_t tables_bytes,
+                                                      const uint8_t *lengths, uint32_t lut_bits) {
+    if (tables) {
+        for (uint32_t o = threadIdx.x * 16u; o < tables_bytes; o += blockDim.x * 16u)
+            *reinterpret_cast<uint4 *>(lds + o) = *reinterpret_cast<const uint4 *>(tables + o);
+        __syncthreads();
+    } else {
+        derive_tables(lds, lds + tables_bytes, lengths, lut_bits);
+    }
+}
+
 // Pointers into the LDS image of derive_tables for a k-bit first level.
 __device__ __forceinline__ Tables tables_view(uint8_t *lds, uint32_t lut_bits) {
     Tables t;

@@ -42,6 +42,7 @@ struct GemmArgs {
     const uint32_t *items;     // (n_items + 1) x {first chunk, first block, code bits, 0}
     const uint8_t *raw;        // raw bytes in panel order
     const uint8_t *lengths;    // the 256 code lengths (container bytes 256..511)
+    const uint8_t *tables;     // tables from dfc_derive_tables, or null: derive them here
     const uint16_t *x;         // B vectors of K bf16: x[b K + k]
     float *y;                  // B vectors of M fp32: y[b M + m]
     uint32_t words_bytes, offw_bytes, raw_bytes, x_bytes, y_bytes;
@@ -178,7 +179,7 @@ __device__ __forceinline__ bool gemm_item(const GemmArgs &g, uint32_t q, const T
 template <int C, int NT>
 __global__ __launch_bounds__(1024) void dfc_gemm_kernel(const GemmArgs g) {
     extern __shared__ __align__(16) uint8_t lds[];
-    derive_tables(lds, lds + g.tables_bytes, g.lengths, g.lut_bits);
+    load_or_derive_tables(lds, g.tables, g.tables_bytes, g.lengths, g.lut_bits);
     const Tables t = tables_view(lds, g.lut_bits);
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const uint32_t lane = threadIdx.x % kWave;
@@ -270,7 +271,7 @@ dfc_status launch_gemm(const GemmArgs &proto, uint32_t max_block, hipStream_t st
     uint32_t wpp = std::min<uint32_t>(g.slices, 8u);
     uint32_t group = std::max<uint32_t>(1u, 8u / wpp);
     // the staging areas hold the table derivation's scratch before the first item
-    const uint32_t scratch = derive_scratch_bytes(g.lut_bits);
+    const uint32_t scratch = g.tables ? 0u : derive_scratch_bytes(g.lut_bits);
     auto lds_for = [&](uint32_t w) { return size_t(g.tables_bytes) + std::max<size_t>(size_t(w) * stage, scratch); };
     while (wpp * group > 1 && lds_for(wpp * group) > kLdsBytes) {
         if (group > 1)
@@ -320,12 +321,12 @@ dfc_status launch_gemm_c(const GemmArgs &g, uint32_t max_block, hipStream_t stre
 
 extern "C" {
 
-dfc_status dfc_decode_gemm(const void *w_blob_dev, const dfc_info *info, const uint16_t *x_dev, uint32_t batch,
-                           float *y_dev, uint32_t *status_dev, void *stream) {
+dfc_status dfc_decode_gemm(const void *w_blob_dev, const dfc_info *info, const void *tables_dev, const uint16_t *x_dev,
+                           uint32_t batch, float *y_dev, uint32_t *status_dev, void *stream) {
     if (!info || !w_blob_dev || !x_dev || !y_dev) return DFC_EINVAL;
     if (batch < 1 || batch > DFC_GEMM_MAX_BATCH) return DFC_EINVAL;
     if ((reinterpret_cast<uintptr_t>(w_blob_dev) & 255u) || (reinterpret_cast<uintptr_t>(x_dev) & 15u) ||
-        (reinterpret_cast<uintptr_t>(y_dev) & 3u))
+        (reinterpret_cast<uintptr_t>(y_dev) & 3u) || (reinterpret_cast<uintptr_t>(tables_dev) & 15u))
         return DFC_EINVAL;
     const dfc_info &in = *info;
     if (in.layout != DFC_LAYOUT_PANEL || in.panel_rows != dfc::kPanelRows || in.lanes_per_block != 64)
@@ -347,6 +348,7 @@ dfc_status dfc_decode_gemm(const void *w_blob_dev, const dfc_info *info, const u
     g.items = reinterpret_cast<const uint32_t *>(base + in.off_panels);
     g.raw = base + in.off_raw;
     g.lengths = base + dfc::hdr::lengths;
+    g.tables = static_cast<const uint8_t *>(tables_dev);
     g.x = x_dev;
     g.y = y_dev;
     g.words_bytes = uint32_t(in.words_bytes);

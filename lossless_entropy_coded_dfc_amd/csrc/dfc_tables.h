@@ -39,8 +39,14 @@ namespace {
 
 // LDS bytes derive_tables needs beside the tables: per-group length counts
 // (4 x 32 u32), per-symbol ranks and lengths (2 x 256 u8), and the
-// single-code table of the k-bit windows (2^k u16).
-__host__ __device__ constexpr uint32_t derive_scratch_bytes(uint32_t k) { return 512u + 512u + (2u << k); }
+// single-code table of the k-bit windows (2^k u32).
+__host__ __device__ constexpr uint32_t derive_scratch_bytes(uint32_t k) { return 512u + 512u + (4u << k); }
+
+// Slot of window j in the single-code table.  The first-level pass reads
+// entry (w << o) mod 2^k for consecutive w in a wavefront's lanes, 2^o
+// entries apart; XOR-ing the bank bits with the entry's 64-entry row puts
+// those reads in different LDS banks (or on one address) for every o.
+__device__ __forceinline__ uint32_t t1_slot(uint32_t j) { return j ^ ((j >> 6) & 63u); }
 
 // LDS bytes derive_slot_table needs beside the slot table: cum[256] u32.
 constexpr uint32_t kSlotScratchBytes = 1024u;
@@ -71,7 +77,7 @@ __device__ void derive_tables(uint8_t *tab, uint8_t *scratch, const uint8_t *len
     uint32_t *grp = reinterpret_cast<uint32_t *>(scratch);  // [4][32]: group g, length l
     uint8_t *rank = scratch + 512;                          // [256]
     uint8_t *lens = scratch + 768;                          // [256]
-    uint16_t *t1 = reinterpret_cast<uint16_t *>(scratch + 1024);
+    uint32_t *t1 = reinterpret_cast<uint32_t *>(scratch + 1024);
     uint32_t *limit = reinterpret_cast<uint32_t *>(tab + (14u << k));
     uint32_t *first = limit + 32, *base = limit + 64;
     uint8_t *order = tab + (14u << k) + 384;
@@ -135,21 +141,18 @@ __device__ void derive_tables(uint8_t *tab, uint8_t *scratch, const uint8_t *len
     }
     __syncthreads();
     // 4. The first code of every k-bit window (its low bits zero past the
-    //    window): symbol | length << 8, or 0 when it is longer than k.  By
-    //    the monotone limits, the length is 1 + the number of l <= k with
-    //    limit[l] <= w24.
+    //    window): its exponent rotated right by one bit | length << 8, or 0
+    //    when it is longer than k.  By the monotone limits, the length is
+    //    1 + the number of l <= k with limit[l] <= w24.
     const uint32_t kmask = (1u << k) - 1u;
     for (uint32_t j = tid; j <= kmask; j += nt) {
         const uint32_t x = j << (dfc::kMaxLen - k);
         uint32_t l = 1;
 #pragma unroll
         for (uint32_t i = 1; i <= 12u; ++i) l += (i <= k && x >= limit[i]) ? 1u : 0u;
-        uint16_t v = 0;
-        if (l <= k) {
-            const uint32_t sym = order[base[l] + (x >> (dfc::kMaxLen - l)) - first[l]];
-            v = uint16_t(sym | (l << 8));
-        }
-        t1[j] = v;
+        uint32_t v = 0;
+        if (l <= k) v = rotr8_1(order[base[l] + (x >> (dfc::kMaxLen - l)) - first[l]]) | (l << 8);
+        t1[t1_slot(j)] = v;
     }
     __syncthreads();
     // 5. First-level entries: the codes of window w decoded one after
@@ -159,14 +162,13 @@ __device__ void derive_tables(uint8_t *tab, uint8_t *scratch, const uint8_t *len
     for (uint32_t w = tid; w <= kmask; w += nt) {
         uint32_t o = 0, n = 0, o4 = 0, syms = 0, m = 0;
         for (uint32_t it = 0; it < k; ++it) {
-            const uint32_t e = t1[(w << o) & kmask];
+            const uint32_t e = t1[t1_slot((w << o) & kmask)];
             const uint32_t l = e >> 8;
             if (l == 0u || o + l > k) break;
-            if (n < 4u) {
-                syms |= rotr8_1(e & 0xFFu) << (8u * n);
-                o4 += l;
-            }
+            const bool first4 = n < 4u;
+            syms |= first4 ? (e & 0xFFu) << (8u * n) : 0u;
             o += l;
+            o4 = first4 ? o : o4;
             m |= 1u << (o - 1u);
             ++n;
         }

@@ -175,9 +175,9 @@ def test_invalid_arguments_rejected():
     dev = torch.from_numpy(blob).cuda()
     out = torch.empty(info.n + 8, dtype=torch.int16, device="cuda")
     lib = dfc.library()
-    s = lib.dfc_decode(dev.data_ptr(), info, out.data_ptr() + 2, info.n, None, None)   # misaligned dst
+    s = lib.dfc_decode(dev.data_ptr(), info, None, out.data_ptr() + 2, info.n, None, None)   # misaligned dst
     assert s == dfc.EINVAL
-    s = lib.dfc_decode(dev.data_ptr(), info, out.data_ptr(), info.n + 1, None, None)
+    s = lib.dfc_decode(dev.data_ptr(), info, None, out.data_ptr(), info.n + 1, None, None)
     assert s == dfc.ESIZE
     # a block wider than one wavefront is refused at encode time, and a
     # description claiming one is refused before launch
@@ -185,7 +185,7 @@ def test_invalid_arguments_rejected():
         dfc.encode(x, lanes=128)
     wide = dfc.blob_info(blob)
     wide.lanes_per_block = 128
-    s = lib.dfc_decode(dev.data_ptr(), wide, out.data_ptr(), info.n, None, None)
+    s = lib.dfc_decode(dev.data_ptr(), wide, None, out.data_ptr(), info.n, None, None)
     assert s == dfc.EUNSUPPORTED
     # the binding refuses a device container shorter than its info, a host
     # container and a status word that is not 32-bit, before any launch
@@ -255,13 +255,26 @@ def test_full_llama_block_batched():
 
 @pytest.mark.parametrize("kind", list(synth.STRESS_KINDS))
 def test_full_stress_8192x28672(kind):
+    """The stress tensors at full size, every chunk size (the persistent
+    kernel's next-block path runs at every C here: each wavefront decodes
+    several blocks), compared on the device; sampled blocks by the oracle."""
     say("stress", kind)
     x = synth.stress(kind)
-    for C in ((4, 16, 32) if kind == "student_t" else (16,)):
+    ref = torch.from_numpy(x.ravel().view(np.int16)).cuda()
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for C in (4, 8, 16, 32):
         blob = dfc.encode(x, chunk_bytes=C)
-        got, status = gpu_decode(blob)
-        assert status == 0 and np.array_equal(got, x.ravel()), (kind, C)
-    sampled_oracle_check(blob, got, n_samples=2)
+        info = dfc.blob_info(blob)
+        assert info.n_blocks > 2 * 8192, (kind, C)   # several blocks per resident wavefront
+        dev = torch.from_numpy(blob).cuda()
+        out = torch.empty(int(info.n), dtype=torch.int16, device="cuda")
+        tables = dfc.derive_tables(dev, info) if C in (8, 32) else None
+        status.zero_()
+        dfc.decode(dev, info, out, status, tables=tables)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0 and torch.equal(out, ref), (kind, C)
+        if C == 8:
+            sampled_oracle_check(blob, out.cpu().numpy().view(np.uint16), n_samples=2)
 
 
 @pytest.mark.slow
@@ -294,8 +307,8 @@ def test_largest_accepted_matrix():
         assert torch.equal(out, ref), layout
         over = dfc.Info.from_buffer_copy(info)
         over.n = limit // 2 + 1
-        s = lib.dfc_decode(ctypes.c_void_p(dev.data_ptr()), ctypes.byref(over), ctypes.c_void_p(out.data_ptr()),
-                           over.n, None, None)
+        s = lib.dfc_decode(ctypes.c_void_p(dev.data_ptr()), ctypes.byref(over), None,
+                           ctypes.c_void_p(out.data_ptr()), over.n, None, None)
         assert s == dfc.EUNSUPPORTED, layout
         del dev, out
         torch.cuda.empty_cache()

@@ -239,3 +239,30 @@ def test_source_not_16_byte_aligned(layout):
     d, size = dfc.encode_device(src, shape=shape, **kw)
     assert size == host.size
     assert np.array_equal(d[:size].cpu().numpy(), host)
+
+
+@pytest.mark.parametrize("layout", ["flat", "ans", "panel"])
+def test_device_containers_equal_the_oracles(layout):
+    """Containers written by the GPU encoder compared byte for byte with the
+    oracle's own writers (not only with the host encoder)."""
+    from oracle import ans as oans
+    from oracle import panel as opanel
+    from oracle import stream as ost
+    for j, shape in enumerate(((64, 1008), (96, 2048), (1, 4097), (32, 16))):
+        if layout == "panel" and shape[0] % 32:
+            continue
+        x = synth.gaussian_with_outliers(shape, 0.02, (108, j))
+        say("oracle vs device", layout, shape)
+        if layout == "flat":
+            for C in (4, 16):
+                d, size = dfc.encode_device(dev16(x), chunk_bytes=C, shape=shape)
+                want = bl.write_blob(ost.encode(x, C, 64), 11, *shape)
+                assert size == len(want) and bytes(d[:size].cpu().numpy()) == want, (shape, C)
+        elif layout == "ans":
+            d, size = dfc.encode_device(dev16(x), layout=dfc.LAYOUT_ANS, ans_steps=64, shape=shape)
+            want = oans.write_ans_blob(oans.encode_ans(x, 64), *shape)
+            assert size == len(want) and bytes(d[:size].cpu().numpy()) == want, shape
+        else:
+            d, size = dfc.encode_device(dev16(x), layout=dfc.LAYOUT_PANEL, panel_k=256, chunk_bytes=8, shape=shape)
+            want = opanel.write_panel_blob(opanel.encode_panel(x, 256, 8, 64), 11)
+            assert size == len(want) and bytes(d[:size].cpu().numpy()) == want, shape
