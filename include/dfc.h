@@ -288,6 +288,25 @@ dfc_status dfc_encode_device(const uint16_t *src_dev, uint64_t n, const dfc_para
                              void *dst_dev, uint64_t cap, void *work_dev, uint64_t work_bytes, uint64_t *written,
                              void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * encoder as dfc_encode_device, with the same arguments except the
+ * workspace, which is a fixed array of DFC_NOALLOC_WORKSPACE_BYTES (16 MiB)
+ * in device memory that the library holds on every GPU it runs on until the
+ * process ends.  The call allocates no device memory.  It takes inputs up to
+ * dfc_encode_device_workspace(n) <= DFC_NOALLOC_WORKSPACE_BYTES, that is
+ * n <= 715,000,000 weights; larger inputs return DFC_ESIZE before any work.
+ * Calls on one GPU share its array: the library serializes them (each call
+ * holds that GPU's array until its stream is idle, which is when it
+ * returns), so concurrent calls from several host threads wait for each
+ * other rather than race.  The array keeps the last call's contents; what
+ * must start at zero (the histogram) is cleared by every call.  The GPU is
+ * the one the stream belongs to (the current device for the NULL stream).
+ * Errors as dfc_encode_device, plus DFC_ESIZE for n above the limit. */
+enum { DFC_NOALLOC_WORKSPACE_BYTES = 16 << 20 };
+dfc_status dfc_encode_device_noalloc(const uint16_t *src_dev, uint64_t n, const dfc_params *p, const dfc_codebook *cb,
+                                     void *dst_dev, uint64_t cap, uint64_t *written, void *stream);
+
 /* Launch tuning knob for benchmarks (Huffman layouts): wavefronts per
  * workgroup (1..16) and wave-blocks each wavefront decodes (1..64); 0 =
  * automatic.  Returns DFC_EINVAL for other values.  The library's only

@@ -134,6 +134,10 @@ def library():
                                       ctypes.POINTER(Codebook), ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
                                       ctypes.c_uint64, u64p, ctypes.c_void_p]
     lib.dfc_encode_device.restype = st
+    lib.dfc_encode_device_noalloc.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.POINTER(Params),
+                                              ctypes.POINTER(Codebook), ctypes.c_void_p, ctypes.c_uint64, u64p,
+                                              ctypes.c_void_p]
+    lib.dfc_encode_device_noalloc.restype = st
     lib.dfc_derived_tables_bytes.argtypes = [ctypes.POINTER(Info), u64p]
     lib.dfc_derived_tables_bytes.restype = st
     lib.dfc_derive_tables.argtypes = [ctypes.c_void_p, ctypes.POINTER(Info), ctypes.c_uint32, ctypes.c_void_p,

@@ -28,6 +28,9 @@
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
+#include <map>
+#include <memory>
+#include <mutex>
 #include <vector>
 
 #include "dfc.h"
@@ -723,9 +726,59 @@ dfc_status encode_panel_device(const uint16_t *src_dev, uint64_t n, const dfc_pa
     return DFC_OK;
 }
 
+// The workspace of dfc_encode_device_noalloc: a fixed array in device
+// memory, one copy per GPU the library runs on, held until the process
+// ends.  In host code `scratch` names a host-side stand-in, never the
+// device memory: kernels and copies get the address hipGetSymbolAddress
+// returns for the device, kept per device below.
+__device__ __align__(256) uint8_t scratch[DFC_NOALLOC_WORKSPACE_BYTES];
+
+struct DeviceScratch {
+    void *ptr = nullptr;  // this device's copy of `scratch`
+    std::mutex mu;        // held for a whole call: the copy is shared
+};
+
+// The scratch of device `dev`: its address is looked up once, with that
+// device current, and kept.
+dfc_status device_scratch(int dev, DeviceScratch **out) {
+    static std::mutex table_mu;
+    static std::map<int, std::unique_ptr<DeviceScratch>> table;
+    std::lock_guard<std::mutex> lock(table_mu);
+    auto it = table.find(dev);
+    if (it == table.end()) {
+        int cur = 0;
+        if (hipGetDevice(&cur) != hipSuccess) return DFC_EHIP;
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) return DFC_EHIP;
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (cur != dev && hipSetDevice(cur) != hipSuccess) return DFC_EHIP;
+        if (e != hipSuccess || !ptr) return DFC_EHIP;
+        auto s = std::make_unique<DeviceScratch>();
+        s->ptr = ptr;
+        it = table.emplace(dev, std::move(s)).first;
+    }
+    *out = it->second.get();
+    return DFC_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+dfc_status dfc_encode_device_noalloc(const uint16_t *src_dev, uint64_t n, const dfc_params *p, const dfc_codebook *cb,
+                                     void *dst_dev, uint64_t cap, uint64_t *written, void *stream) {
+    if (workspace_layout(n).bytes > DFC_NOALLOC_WORKSPACE_BYTES) return DFC_ESIZE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int dev = 0;
+    if ((st ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev)) != hipSuccess) return DFC_EHIP;
+    DeviceScratch *ds = nullptr;
+    const dfc_status s = device_scratch(dev, &ds);
+    if (s != DFC_OK) return s;
+    // dfc_encode_device returns with its stream idle, so holding the lock
+    // for the call keeps every other call on this device off the scratch
+    std::lock_guard<std::mutex> lock(ds->mu);
+    return dfc_encode_device(src_dev, n, p, cb, dst_dev, cap, ds->ptr, DFC_NOALLOC_WORKSPACE_BYTES, written, stream);
+}
 
 dfc_status dfc_encode_device_workspace(uint64_t n, uint64_t *bytes) {
     if (!bytes) return DFC_EINVAL;
