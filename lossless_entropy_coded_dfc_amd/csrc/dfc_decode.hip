@@ -90,126 +90,55 @@ struct Occupancy {
     static constexpr int kWavesPerSimd = C >= 32 ? 5 : 8;
 };
 
-// Output range of one block and its octets (8 values, 16 output bytes).
-// Octets [full0, full1) lie wholly inside [s_out, e_out); the first and the
-// last octet may be shared with the neighbouring blocks.
-struct BlockRange {
-    uint32_t s_out, e_out;
-    uint32_t h0, nh;  // first octet, number of octets
-    uint32_t full0, full1;
-};
+// Output rounds.  A wavefront decodes a contiguous run of blocks and writes
+// its output in rounds of 512 values (1 KB of bf16, one 16-byte store per
+// lane) aligned to multiples of 512 in the output: a block's exponents are
+// staged in LDS behind the values still pending from the blocks before it
+// (fewer than 512, kept in registers in between), every complete round is
+// merged with its raw bytes and stored, and the rest is carried on.  Only
+// the first and last round of a run can be partial; values outside the
+// run's [lo, hi) are not written (an octet cut by lo or hi goes out with
+// 16-bit stores).
+constexpr uint32_t kRound = 512;
 
-__device__ __forceinline__ BlockRange block_range(uint32_t s_out, uint32_t e_out) {
-    BlockRange r;
-    r.s_out = s_out;
-    r.e_out = e_out;
-    r.h0 = s_out >> 3;
-    r.nh = ((e_out + 7u) >> 3) - r.h0;
-    r.full0 = (s_out & 7u) ? 1u : 0u;
-    r.full1 = (e_out & 7u) ? r.nh - 1u : r.nh;
-    return r;
-}
-
-// Octet i of the block (one per lane): whole octets go out as one 16-byte
-// buffer store (1 KB contiguous per wavefront); a shared octet stores only
-// its values inside the block, one 16-bit store each.
-__device__ __forceinline__ void store_octet(const Buffers &bf, const BlockRange &br, uint32_t i, const u32x4 &o) {
-    const uint32_t h = br.h0 + i;
-    const bool full = i - br.full0 < br.full1 - br.full0;
-    __builtin_amdgcn_raw_buffer_store_b128(o, bf.dst, full ? 16u * h : kNowhere, 0, 0);
-    if (!full && i < br.nh) {
-        // values [lo, hi) of the octet are the block's; value q goes out iff
-        // q - lo < hi - lo (unsigned)
-        const uint32_t lo = uint32_t(max(int(br.s_out) - int(8u * h), 0));
-        const uint32_t span = min(br.e_out - 8u * h, 8u) - lo;
+// One round of 512 values from output index base (a multiple of 512): this
+// lane's octet v0 = base + 8 lane, exponents E, raw bytes R.  `edge` is
+// uniform: false when the whole round lies inside [lo, hi).
+__device__ __forceinline__ void store_round(const Buffers &bf, uint32_t base, uint32_t lane, const u32x2 &E,
+                                            const u32x2 &R, bool edge, uint32_t lo, uint32_t hi) {
+    const u32x4 o = assemble8(E, R);
+    const uint32_t v0 = base + 8u * lane;
+    if (!edge) {
+        __builtin_amdgcn_raw_buffer_store_b128(o, bf.dst, 2u * v0, 0, 0);
+        return;
+    }
+    const bool full = v0 >= lo && v0 + 8u <= hi;
+    __builtin_amdgcn_raw_buffer_store_b128(o, bf.dst, full ? 2u * v0 : kNowhere, 0, 0);
+    if (!full && v0 + 8u > lo && v0 < hi) {
         const uint32_t v[4] = {o.x, o.y, o.z, o.w};
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-            // (kNowhere + 14 is still past every range)
-            const uint32_t at = (uint32_t(q) - lo < span ? 16u * h : kNowhere) + 2u * uint32_t(q);
+            const uint32_t at = (v0 + q >= lo && v0 + q < hi ? 2u * v0 : kNowhere) + 2u * uint32_t(q);
             __builtin_amdgcn_raw_buffer_store_b16(uint16_t(v[q >> 1] >> (16 * (q & 1))), bf.dst, at, 0, 0);
         }
     }
 }
 
-template <int C, bool Padded>
-__device__ __forceinline__ void decode_block(const ItemArgs &a, const Buffers &bf, uint32_t b, uint32_t lane,
-                                             const Chunk<C> &ck, uint8_t *stage, uint32_t stage_off,
-                                             uint32_t stage_bytes, const Tables &t, uint32_t *status,
-                                             const u32x2 (&R)[Prefetch<C>::N], const BlockRange &br,
-                                             const Chunk<C> &nxt) {
-    constexpr int PF = Prefetch<C>::N;
-    // Zero the staging bytes this block ORs its exponents into: lead, the
-    // block's exponents, and the spill of its last lookup.
-    const uint32_t nz = min((br.s_out & 7u) + (br.e_out - br.s_out) + 8u, stage_bytes);
-    for (uint32_t o = 16u * lane; o + 16u <= ((nz + 15u) & ~15u); o += 16u * kWave)
-        *reinterpret_cast<uint4 *>(stage + o) = make_uint4(0, 0, 0, 0);
-    const uint32_t chunk = b * kWave + lane;
-    // Stream bits from this lane's chunk to the end of the stream: only the
-    // last block needs them per lane (a uniform 64-bit test, then 32 bits).
-    const int64_t block_left = int64_t(a.total_bits) - int64_t(uint64_t(b) * (uint64_t(kWave) * 8u * C));
-    const int bits_left = block_left >= int64_t(kWave) * (8 * C + 32)
-                              ? (8 * C + 32)
-                              : max(int(block_left) - int(lane) * (8 * C), -1);
-    int start = 0, end;
-    if constexpr (Padded)
-        end = min(8 * C, bits_left);
-    else
-        chunk_span<C>(ck, chunk, bits_left, start, end);
+// Raw bytes of this lane's octet of the round at base, or nothing (zeros, no
+// memory access) for an octet wholly outside [lo, hi).
+__device__ __forceinline__ u32x2 load_raw_octet(const Buffers &bf, uint32_t base, uint32_t lane, uint32_t lo,
+                                                uint32_t hi) {
+    const uint32_t v0 = base + 8u * lane;
+    return __builtin_amdgcn_raw_buffer_load_b64(bf.raw, v0 + 8u > lo && v0 < hi ? v0 : kNowhere, 0, 0);
+}
 
-    // The count and write passes run at a raised wave priority, so that the
-    // wavefronts that are decoding get issue slots ahead of those that are
-    // storing, which keeps stores queued behind the decode (1% in one-process
-    // timing); the store rounds drop back to the normal priority.
-    __builtin_amdgcn_s_setprio(1);
-    uint32_t cnt = 0;
-    if (start < end) cnt = Padded ? count_codes_padded<C>(ck, end, t) : count_codes<C>(ck, start, end, t);
-    const uint32_t incl = wave_inclusive_scan(cnt);
-    const uint32_t total = __builtin_amdgcn_readlane(incl, kWave - 1);
-    // A chunk of 8C bits holds at most 8C code starts; anything else (or a
-    // total that disagrees with the block offsets) means a corrupt stream.
-    const bool bad = (total != br.e_out - br.s_out) | (__builtin_amdgcn_ballot_w64(cnt > 8u * C) != 0);
-    const uint32_t lead = br.s_out & 7u;
-    if (!bad && cnt) {
-        if constexpr (Padded)
-            write_codes_padded<C>(ck, end, cnt, stage - stage_off, stage_off + lead + (incl - cnt), t);
-        else
-            write_codes<C>(ck, start, end, stage - stage_off, stage_off + lead + (incl - cnt), t);
-    }
-    // Everything prefetched must be in registers before the first store, on
-    // every path to the next block.
-    wait_for(R);
-    wait_for(nxt);
-    if (bad) {
-        if (lane == 0 && status) atomicOr(status, kStatusCorrupt);
-        return;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-    __builtin_amdgcn_s_setprio(0);
-    // Lanes past the block's last octet read its last staged octet again and
-    // store nowhere.
-    const uint32_t last = br.nh - 1u;
-#pragma unroll
-    for (int j = 0; j < PF; ++j) {
-        if (uint32_t(kWave * j) < br.nh) {
-            const uint32_t i = lane + uint32_t(kWave * j);
-            const u32x2 E = *reinterpret_cast<const u32x2 *>(stage + 8u * min(i, last));
-            store_octet(bf, br, i, assemble8(E, R[j]));
-        }
-    }
-    for (uint32_t j0 = uint32_t(kWave * PF); j0 < br.nh; j0 += kWave) {
-        const uint32_t i = lane + j0;
-        const u32x2 Ri = __builtin_amdgcn_raw_buffer_load_b64(bf.raw, i < br.nh ? 8u * (br.h0 + i) : kNowhere, 0, 0);
-        const u32x2 E = *reinterpret_cast<const u32x2 *>(stage + 8u * min(i, last));
-        store_octet(bf, br, i, assemble8(E, Ri));
-    }
-    // The next block reuses this wavefront's staging area.
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+// The values still pending in the carry registers, [base, hi) minus what
+// lies below lo, stored as a last (partial) round.
+__device__ __forceinline__ void flush_round(const Buffers &bf, uint32_t base, uint32_t lane, const u32x2 &carry,
+                                            uint32_t lo, uint32_t hi) {
+    if (hi <= base) return;
+    const u32x2 R = load_raw_octet(bf, base, lane, lo, hi);
+    store_round(bf, base, lane, carry, R, true, lo, hi);
 }
 
 template <int C, bool Padded>
@@ -229,42 +158,47 @@ __global__ __launch_bounds__(1024, Occupancy<C>::kWavesPerSimd) void dfc_decode_
     const uint32_t lane = threadIdx.x % kWave;
     const uint32_t stage_off = a.tables_bytes + wave * args.stage_bytes;
     uint8_t *stage = lds + stage_off;
-    const uint32_t lo_b = (wg - a.wg_begin) * a.blocks_per_wg;
-    const uint32_t hi_b = min(lo_b + a.blocks_per_wg, a.n_blocks);
+    // this wavefront's run: a contiguous share of the workgroup's blocks
+    const uint32_t lo_wg = (wg - a.wg_begin) * a.blocks_per_wg;
+    const uint32_t hi_wg = min(lo_wg + a.blocks_per_wg, a.n_blocks);
+    const uint32_t per = (hi_wg - min(lo_wg, hi_wg) + waves - 1u) / waves;
+    const uint32_t b_end = min(lo_wg + (wave + 1u) * per, hi_wg);
+    uint32_t b = lo_wg + wave * per;
 
     // The first block's stream words and output range are requested before
     // the tables are derived (the derivation's barriers wait for LDS only),
     // so their memory latency overlaps it.
-    uint32_t b = lo_b + wave;
     Chunk<C> cur{};
     uint32_t s_out = 0, e_out = 0;
-    if (b < hi_b) {
+    if (b < b_end) {
         load_chunk<C, !Padded>(bf.words, bf.offw, b * kWave + lane, cur);
         s_out = blockout[b];
         e_out = blockout[b + 1];
     }
     load_or_derive_tables(lds, a.tables, a.tables_bytes, a.lengths, a.lut_bits);
     const Tables t = tables_view(lds, a.lut_bits);
-    if (b >= hi_b) return;
+    if (b >= b_end) return;
     // Resident on entry, as it is on every later iteration (see wait_for).
     wait_for(cur);
+
+    // run state: rounds start at base (a multiple of 512); values below lo
+    // belong to another run; the carry holds [base, s_out)
+    uint32_t base = s_out & ~(kRound - 1u), lo = s_out;
+    u32x2 carry = {0u, 0u};
     for (;;) {
         // the block index is the same in every lane
         b = __builtin_amdgcn_readfirstlane(b);
-        const BlockRange br = block_range(s_out, e_out);
-        // raw bytes of this block's first PF octets per lane (rounds past the
-        // block's last octet load nothing)
+        const uint32_t lead = s_out - base;  // pending values, < 512
+        const uint32_t want = e_out - s_out;
+        const uint32_t rounds = (lead + want) / kRound;  // rounds this block completes
+        // raw bytes of those rounds (the first PF of them) per lane
         u32x2 R[PF];
 #pragma unroll
-        for (int j = 0; j < PF; ++j) {
-            const uint32_t i = lane + uint32_t(kWave * j);
-            R[j] = uint32_t(kWave * j) < br.nh
-                       ? __builtin_amdgcn_raw_buffer_load_b64(bf.raw, i < br.nh ? 8u * (br.h0 + i) : kNowhere, 0, 0)
-                       : u32x2{0u, 0u};
-        }
+        for (int j = 0; j < PF; ++j)
+            R[j] = uint32_t(j) < rounds ? load_raw_octet(bf, base + kRound * j, lane, lo, e_out) : u32x2{0u, 0u};
         // next block's stream words, offsets and output range
-        const uint32_t bn = b + waves;
-        const bool more = bn < hi_b;
+        const uint32_t bn = b + 1u;
+        const bool more = bn < b_end;
         Chunk<C> nxt{};
         uint32_t s_nxt = 0, e_nxt = 0;
         if (more) {
@@ -272,8 +206,88 @@ __global__ __launch_bounds__(1024, Occupancy<C>::kWavesPerSimd) void dfc_decode_
             s_nxt = blockout[bn];
             e_nxt = blockout[bn + 1];
         }
-        decode_block<C, Padded>(a, bf, b, lane, cur, stage, stage_off, args.stage_bytes, t, args.status, R, br, nxt);
-        if (!more) break;
+        // Zero the staging bytes this block ORs its exponents into (the
+        // pending values, the block's, and the spill of its last lookup),
+        // then put the pending values back in front.
+        const uint32_t nz = min(lead + want + 8u, args.stage_bytes);
+        for (uint32_t o = 16u * lane; o < nz; o += 16u * kWave)
+            *reinterpret_cast<uint4 *>(stage + o) = make_uint4(0, 0, 0, 0);
+        if (8u * lane < lead) *reinterpret_cast<u32x2 *>(stage + 8u * lane) = carry;
+
+        const uint32_t chunk = b * kWave + lane;
+        // Stream bits from this lane's chunk to the end of the stream: only
+        // the last block needs them per lane (a uniform 64-bit test, then 32 bits).
+        const int64_t block_left = int64_t(a.total_bits) - int64_t(uint64_t(b) * (uint64_t(kWave) * 8u * C));
+        const int bits_left = block_left >= int64_t(kWave) * (8 * C + 32)
+                                  ? (8 * C + 32)
+                                  : max(int(block_left) - int(lane) * (8 * C), -1);
+        int start = 0, end;
+        if constexpr (Padded)
+            end = min(8 * C, bits_left);
+        else
+            chunk_span<C>(cur, chunk, bits_left, start, end);
+
+        // The count and write passes run at a raised wave priority, so that
+        // the wavefronts that are decoding get issue slots ahead of those
+        // that are storing; the store rounds drop back to the normal priority.
+        __builtin_amdgcn_s_setprio(1);
+        uint32_t cnt = 0;
+        if (start < end) cnt = Padded ? count_codes_padded<C>(cur, end, t) : count_codes<C>(cur, start, end, t);
+        const uint32_t incl = wave_inclusive_scan(cnt);
+        const uint32_t total = __builtin_amdgcn_readlane(incl, kWave - 1);
+        // A chunk of 8C bits holds at most 8C code starts; anything else (or
+        // a total that disagrees with the block offsets) means a corrupt stream.
+        const bool bad = (total != want) | (__builtin_amdgcn_ballot_w64(cnt > 8u * C) != 0);
+        if (!bad && cnt) {
+            if constexpr (Padded)
+                write_codes_padded<C>(cur, end, cnt, stage - stage_off, stage_off + lead + (incl - cnt), t);
+            else
+                write_codes<C>(cur, start, end, stage - stage_off, stage_off + lead + (incl - cnt), t);
+        }
+        // Everything prefetched must be in registers before the first store,
+        // on every path to the next block.
+        wait_for(R);
+        wait_for(nxt);
+        __builtin_amdgcn_s_setprio(0);
+        if (bad) {
+            // the block stays unwritten: store what is pending before it and
+            // start a new run after it
+            if (lane == 0 && args.status) atomicOr(args.status, kStatusCorrupt);
+            flush_round(bf, base, lane, carry, lo, s_out);
+            base = e_out & ~(kRound - 1u);
+            lo = e_out;
+            carry = u32x2{0u, 0u};
+        } else {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            // complete rounds; only the first round of a run can start below lo
+#pragma unroll
+            for (int j = 0; j < PF; ++j) {
+                if (uint32_t(j) < rounds) {
+                    const u32x2 E = *reinterpret_cast<const u32x2 *>(stage + kRound * j + 8u * lane);
+                    store_round(bf, base + kRound * j, lane, E, R[j], base + kRound * j < lo, lo, e_out);
+                }
+            }
+            for (uint32_t j = PF; j < rounds; ++j) {
+                const u32x2 Rj = load_raw_octet(bf, base + kRound * j, lane, lo, e_out);
+                const u32x2 E = *reinterpret_cast<const u32x2 *>(stage + kRound * j + 8u * lane);
+                store_round(bf, base + kRound * j, lane, E, Rj, base + kRound * j < lo, lo, e_out);
+            }
+            // the values of the round this block only began move on
+            const uint32_t tail = lead + want - kRound * rounds;
+            carry = 8u * lane < tail ? *reinterpret_cast<const u32x2 *>(stage + kRound * rounds + 8u * lane)
+                                     : u32x2{0u, 0u};
+            base += kRound * rounds;
+        }
+        // The next block reuses this wavefront's staging area.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (!more) {
+            flush_round(bf, base, lane, carry, lo, e_out);
+            break;
+        }
         cur = nxt;
         b = bn;
         s_out = s_nxt;
@@ -334,8 +348,9 @@ dfc_status launch_group(const dfc_batch_item *items, const uint32_t *idx, uint32
         max_block = std::max(max_block, in.max_block_elems);
     }
     if (live.empty()) return DFC_OK;
-    // staging: lead (< 8) + elements + spill of the last lookup, rounded to 16
-    const uint32_t stage = (max_block + 32u + 15u) & ~15u;
+    // staging: pending values of the round in progress (< 512) + the block's
+    // values + the spill of its last lookup, rounded to 16
+    const uint32_t stage = (511u + max_block + 32u + 15u) & ~15u;
     if (!allow_full_lds(reinterpret_cast<const void *>(&dfc_decode_kernel<C, Padded>))) return DFC_EHIP;
     // LDS of a workgroup of w wavefronts: the tables, then the staging
     // areas, which hold the derivation's scratch before the first block.

@@ -431,3 +431,38 @@ def test_hip_graph_capture_and_replay():
         for (_, _, out), ref in zip(items, refs):
             assert torch.equal(out, ref), rep
         assert torch.equal(y, want), rep
+
+
+@pytest.mark.parametrize("layout", [dfc.LAYOUT_FLAT, dfc.LAYOUT_PADDED])
+@pytest.mark.parametrize("waves,bpw", [(0, 0), (1, 8), (4, 2)])
+def test_corrupt_block_leaves_the_rest_exact(layout, waves, bpw):
+    """A block offset moved by one makes the two blocks around it fail their
+    count check: those two blocks stay unwritten, the status word is set,
+    and every other block -- before them in the same run of blocks, and
+    after them -- is still decoded exactly."""
+    import struct
+    x = synth.gaussian((256, 4096), 0.02, (54, layout))
+    blob = dfc.encode(x, layout=layout)
+    info = dfc.blob_info(blob)
+    assert info.n_blocks > 40
+    bad = blob.copy()
+    b = info.n_blocks // 2 + 1
+    o = info.off_blockout + 4 * b
+    ob = struct.unpack_from("<III", bytes(blob[o - 4: o + 8]))
+    bad[o: o + 4] = np.frombuffer(struct.pack("<I", ob[1] + 1), dtype=np.uint8)
+    binfo = dfc.blob_info(bad)
+    dfc.set_launch(waves, bpw)
+    try:
+        dev = torch.from_numpy(bad).cuda()
+        out = torch.full((int(info.n),), 0x7E7E, dtype=torch.int16, device="cuda")
+        status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        dfc.decode(dev, binfo, out, status)
+        torch.cuda.synchronize()
+    finally:
+        dfc.set_launch(0, 0)
+    got = out.cpu().numpy().view(np.uint16)
+    assert int(status.item()) == dfc.ECORRUPT
+    lo, hi = ob[0], ob[2]   # blocks b - 1 and b
+    assert np.array_equal(got[:lo], x.ravel()[:lo])
+    assert np.array_equal(got[hi:], x.ravel()[hi:])
+    assert (got[lo:hi] == 0x7E7E).all()
