@@ -207,7 +207,7 @@ def encode_bound(n: int, params: Params | None = None) -> int:
     return out.value
 
 
-def encode(bits, chunk_bytes: int = 16, lanes: int = 64, max_code_len: int = 24, lut_bits: int = 11,
+def encode(bits, chunk_bytes: int = 0, lanes: int = 64, max_code_len: int = 24, lut_bits: int = 11,
            codebook: Codebook | None = None, threads: int = 0, shape=None, layout: int = LAYOUT_FLAT,
            panel_k: int = 0, ans_steps: int = 0) -> np.ndarray:
     """Encode bf16 bit patterns (any shape, row-major) into a DFC1 container
@@ -328,7 +328,7 @@ def decode_batch(items, status=None, stream=None):
            "dfc_decode_batch")
 
 
-def encode_device(src, chunk_bytes: int = 16, lanes: int = 64, max_code_len: int = 24, lut_bits: int = 11,
+def encode_device(src, chunk_bytes: int = 0, lanes: int = 64, max_code_len: int = 24, lut_bits: int = 11,
                   codebook: Codebook | None = None, shape=None, stream=None, layout: int = LAYOUT_FLAT,
                   ans_steps: int = 0, panel_k: int = 0):
     """Encode a contiguous 16-bit device tensor (bf16 bits) on the GPU, in the

@@ -852,6 +852,8 @@ dfc_status dfc_encode_device(const uint16_t *src_dev, uint64_t n, const dfc_para
         s = dfc::code_lengths(hist, p.max_code_len, len);
         if (s != DFC_OK) return s;
     }
+    if (p.chunk_bytes == 0)
+        p.chunk_bytes = p.layout == DFC_LAYOUT_FLAT ? dfc::choose_chunk_bytes(hist, len, p.lanes_per_block) : 16u;
     Book book;
     dfc::canonical_codes(len, book.code);
     std::memcpy(book.len, len, 256);

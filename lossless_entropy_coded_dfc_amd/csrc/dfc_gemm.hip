@@ -63,38 +63,55 @@ struct GemmPrefetch {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4 &v) { return __builtin_bit_cast(bf16x8, v); }
 
-// One item (32 rows x panel_k columns of W, item q of the container): its
-// blocks are decoded and each complete sub-tile is multiplied into acc.
-// Returns false (and sets the status word) if a block's decoded count
-// disagrees with its block offsets; acc then holds a partial sum.
+// Position of an item (32 rows x panel_k columns of W, item q of the
+// container): its first chunk and block, its block end, its code bits and
+// its first element and column.
+struct ItemPos {
+    uint32_t q, c0, b0, b1, bits, e0, col0;
+};
+
+__device__ __forceinline__ ItemPos item_pos(const GemmArgs &g, uint32_t q) {
+    const const_u32_ptr items = (const_u32_ptr)(g.items);
+    ItemPos it;
+    it.q = q;
+    it.c0 = items[4 * q];
+    it.b0 = items[4 * q + 1];
+    it.bits = items[4 * q + 2];
+    it.b1 = items[4 * q + 5];
+    const uint32_t p = q / g.slices;
+    it.col0 = (q % g.slices) * g.panel_k;
+    it.e0 = 32u * (p * g.cols + it.col0);
+    return it;
+}
+
+// The blocks of a wavefront's items (q0, q0 + qstep, ... below qend), one
+// after another: each complete sub-tile is multiplied into acc.  The next
+// block's stream words, chunk offsets and output range (in the same item or
+// the next one) are requested before the current block is decoded, so their
+// memory latency overlaps its decoding.  Returns false (and sets the status
+// word) if a block's decoded count disagrees with its block offsets; acc then
+// holds a partial sum.
 template <int C, int NT>
-__device__ __forceinline__ bool gemm_item(const GemmArgs &g, uint32_t q, const Tables &t, uint8_t *stage,
-                                          uint32_t stage_off, uint32_t lane, const __amdgpu_buffer_rsrc_t &words,
-                                          const __amdgpu_buffer_rsrc_t &offw, const __amdgpu_buffer_rsrc_t &raw,
-                                          const __amdgpu_buffer_rsrc_t &xr, uint32_t xcol, f32x16 (&acc)[NT]) {
+__device__ __forceinline__ bool gemm_items(const GemmArgs &g, uint32_t q0, uint32_t qstep, uint32_t qend,
+                                           const Tables &t, uint8_t *stage, uint32_t stage_off, uint32_t lane,
+                                           const __amdgpu_buffer_rsrc_t &words, const __amdgpu_buffer_rsrc_t &offw,
+                                           const __amdgpu_buffer_rsrc_t &raw, const __amdgpu_buffer_rsrc_t &xr,
+                                           uint32_t xcol, f32x16 (&acc)[NT]) {
     constexpr int PF = GemmPrefetch<C>::N;
     extern __shared__ __align__(16) uint8_t lds[];
-    const const_u32_ptr items = (const_u32_ptr)(g.items);
     const const_u32_ptr blockout = (const_u32_ptr)(g.blockout);
-    const uint32_t c0 = items[4 * q], b0 = items[4 * q + 1], bits = items[4 * q + 2];
-    const uint32_t b1 = items[4 * q + 5];
-    const uint32_t p = q / g.slices, col0 = (q % g.slices) * g.panel_k;
-    const uint32_t e0 = 32u * (p * g.cols + col0);
+    if (q0 >= qend) return true;
+    ItemPos cur = item_pos(g, q0);
+    uint32_t b = cur.b0;
+    Chunk<C> ck;
+    load_chunk<C>(words, offw, cur.c0 + lane, ck);
+    uint32_t s_out = blockout[b], e_out = blockout[b + 1];
+    wait_for(ck);
     u32x2 carry = {0u, 0u};
-    for (uint32_t b = b0; b < b1; ++b) {
-        const uint32_t s_out = blockout[b], e_out = blockout[b + 1];
-        const uint32_t rs = s_out - e0, base = rs & ~511u, lead = rs - base;
+    for (;;) {
+        b = __builtin_amdgcn_readfirstlane(b);
+        const uint32_t rs = s_out - cur.e0, base = rs & ~511u, lead = rs - base;
         const uint32_t total_want = e_out - s_out;
-        // Zero the staging bytes this block ORs into, then put back the
-        // exponents carried from the previous block in front of them.
-        const uint32_t nz = min(lead + total_want + 8u, g.stage_bytes);
-        for (uint32_t o = 16u * lane; o + 16u <= ((nz + 15u) & ~15u); o += 16u * kWave)
-            *reinterpret_cast<uint4 *>(stage + o) = make_uint4(0, 0, 0, 0);
-        if (8u * lane < lead) *reinterpret_cast<u32x2 *>(stage + 8u * lane) = carry;
-
-        const uint32_t ci = (b - b0) * kWave + lane;  // item-relative chunk
-        Chunk<C> ck;
-        load_chunk<C>(words, offw, c0 + ci, ck);
         // raw bytes only for the sub-tiles this block completes: the one it
         // only begins is carried as exponents, and the next block loads its
         // raw bytes
@@ -102,15 +119,36 @@ __device__ __forceinline__ bool gemm_item(const GemmArgs &g, uint32_t q, const T
         u32x2 R[PF];
 #pragma unroll
         for (int j = 0; j < PF; ++j)
-            R[j] = uint32_t(j) < rounds ? __builtin_amdgcn_raw_buffer_load_b64(raw, e0 + base + 512u * j + 8u * lane, 0, 0)
-                                        : u32x2{0u, 0u};
+            R[j] = uint32_t(j) < rounds
+                       ? __builtin_amdgcn_raw_buffer_load_b64(raw, cur.e0 + base + 512u * j + 8u * lane, 0, 0)
+                       : u32x2{0u, 0u};
+        // the next block: this item's next, or the first of the next item
+        const bool same = b + 1u < cur.b1;
+        const bool more = same || cur.q + qstep < qend;
+        ItemPos nit = cur;
+        if (!same && more) nit = item_pos(g, cur.q + qstep);
+        const uint32_t bn = same ? b + 1u : nit.b0;
+        Chunk<C> nxt{};
+        uint32_t s_nxt = 0, e_nxt = 0;
+        if (more) {
+            load_chunk<C>(words, offw, nit.c0 + (bn - nit.b0) * kWave + lane, nxt);
+            s_nxt = blockout[bn];
+            e_nxt = blockout[bn + 1];
+        }
+        // Zero the staging bytes this block ORs into, then put back the
+        // exponents carried from the previous block in front of them.
+        const uint32_t nz = min(lead + total_want + 8u, g.stage_bytes);
+        for (uint32_t o = 16u * lane; o < nz; o += 16u * kWave)
+            *reinterpret_cast<uint4 *>(stage + o) = make_uint4(0, 0, 0, 0);
+        if (8u * lane < lead) *reinterpret_cast<u32x2 *>(stage + 8u * lane) = carry;
+
+        const uint32_t ci = (b - cur.b0) * kWave + lane;  // item-relative chunk
         int start, end;
-        chunk_span<C>(ck, c0 + ci,
-                      int(min(max(int64_t(bits) - int64_t(ci) * (8 * C), int64_t(-1)), int64_t(8 * C + 32))),
+        chunk_span<C>(ck, cur.c0 + ci,
+                      int(min(max(int64_t(cur.bits) - int64_t(ci) * (8 * C), int64_t(-1)), int64_t(8 * C + 32))),
                       start, end);
         // count and write passes at a raised wave priority, the products at the
-        // normal one (wavefronts that are decoding issue first; 1-3% in
-        // one-process timing)
+        // normal one (wavefronts that are decoding issue first)
         __builtin_amdgcn_s_setprio(1);
         const uint32_t cnt = start < end ? count_codes<C>(ck, start, end, t) : 0u;
         const uint32_t incl = wave_inclusive_scan(cnt);
@@ -118,6 +156,7 @@ __device__ __forceinline__ bool gemm_item(const GemmArgs &g, uint32_t q, const T
         const bool bad = (total != total_want) | (__builtin_amdgcn_ballot_w64(cnt > 8u * C) != 0);
         if (!bad && cnt) write_codes<C>(ck, start, end, lds, stage_off + lead + (incl - cnt), t);
         wait_for(R);
+        wait_for(nxt);
         if (bad) {
             if (lane == 0 && g.status) atomicOr(g.status, kStatusCorrupt);
             return false;
@@ -130,10 +169,10 @@ __device__ __forceinline__ bool gemm_item(const GemmArgs &g, uint32_t q, const T
         // Complete sub-tiles: W operand from the staged exponents and the
         // raw bytes, X operand from global memory (cached); the X fragments of
         // all column tiles are requested before their products, so that their
-        // cache round trips overlap (1-2% at 64 columns).
+        // cache round trips overlap.
         const uint32_t extent = lead + total;
         const uint32_t nfull = extent >> 9;
-        const uint32_t kcol = col0 + 16u * (base >> 9);
+        const uint32_t kcol = cur.col0 + 16u * (base >> 9);
 #pragma unroll
         for (int j = 0; j < PF; ++j) {
             if (uint32_t(j) < nfull) {
@@ -149,7 +188,7 @@ __device__ __forceinline__ bool gemm_item(const GemmArgs &g, uint32_t q, const T
             }
         }
         for (uint32_t j = PF; j < nfull; ++j) {
-            const u32x2 Rj = __builtin_amdgcn_raw_buffer_load_b64(raw, e0 + base + 512u * j + 8u * lane, 0, 0);
+            const u32x2 Rj = __builtin_amdgcn_raw_buffer_load_b64(raw, cur.e0 + base + 512u * j + 8u * lane, 0, 0);
             const u32x2 E = *reinterpret_cast<const u32x2 *>(stage + 512u * j + 8u * lane);
             const bf16x8 A = as_bf16x8(assemble8(E, Rj));
             u32x4 X[NT];
@@ -160,12 +199,20 @@ __device__ __forceinline__ bool gemm_item(const GemmArgs &g, uint32_t q, const T
             for (int nt = 0; nt < NT; ++nt)
                 acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, as_bf16x8(X[nt]), acc[nt], 0, 0, 0);
         }
-        // The sub-tile this block only began moves to the next block.
+        // The sub-tile this block only began moves to the next block (an
+        // item ends on a whole sub-tile, so nothing moves to the next item).
         const uint32_t tail = extent - 512u * nfull;
-        carry = 8u * lane < tail ? *reinterpret_cast<const u32x2 *>(stage + 512u * nfull + 8u * lane) : u32x2{0u, 0u};
+        carry = same && 8u * lane < tail ? *reinterpret_cast<const u32x2 *>(stage + 512u * nfull + 8u * lane)
+                                         : u32x2{0u, 0u};
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (!more) break;
+        cur = nit;
+        b = bn;
+        ck = nxt;
+        s_out = s_nxt;
+        e_out = e_nxt;
     }
     return true;
 }
@@ -209,9 +256,8 @@ __global__ __launch_bounds__(1024) void dfc_gemm_kernel(const GemmArgs g) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x16{};
         if (p < g.n_panels)
-            for (uint32_t s = part * wpp + sw; s < g.slices; s += stride)
-                if (!gemm_item<C, NT>(g, p * g.slices + s, t, stage, stage_off, lane, words, offw, raw, xr, xcol, acc))
-                    break;
+            gemm_items<C, NT>(g, p * g.slices + part * wpp + sw, stride, (p + 1) * g.slices, t, stage, stage_off, lane,
+                              words, offw, raw, xr, xcol, acc);
         // D[i][j] of a 32x32 tile: i = 8 (r / 4) + 4 (lane / 32) + r % 4,
         // j = lane % 32.  Value r of lane L goes to slot 4 (64 (r / 4) + L) +
         // r % 4 of the wavefront's tile, so that element e of a float4 slot

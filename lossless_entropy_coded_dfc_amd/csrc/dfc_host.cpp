@@ -6,6 +6,7 @@
 // item 2: decoding threads coordinate through small per-chunk and per-block
 // position variables, which this encoder writes.
 #include <algorithm>
+#include <cmath>
 #include <cstdint>
 #include <cstring>
 #include <thread>
@@ -112,9 +113,10 @@ dfc_status package_merge(const uint64_t hist[256], uint32_t limit, uint8_t len[2
     return DFC_OK;
 }
 
-bool params_ok(const dfc_params &p) {
+// Encoder parameters; chunk_bytes 0 (automatic) only when auto_chunk.
+bool params_ok(const dfc_params &p, bool auto_chunk = true) {
     const uint32_t C = p.chunk_bytes, T = p.lanes_per_block;
-    if (C != 4 && C != 8 && C != 16 && C != 32) return false;
+    if (C != 4 && C != 8 && C != 16 && C != 32 && !(auto_chunk && C == 0)) return false;
     // one wavefront (64 lanes) decodes a block: the only block width the
     // decoders take, so the only one written
     if (T != 64) return false;
@@ -356,6 +358,34 @@ uint64_t kraft(const uint8_t len[256]) {
 
 namespace dfc {
 
+uint32_t choose_chunk_bytes(const uint64_t hist[256], const uint8_t len[256], uint32_t lanes) {
+    uint64_t n = 0, total_bits = 0;
+    for (int s = 0; s < 256; ++s) {
+        n += hist[s];
+        total_bits += hist[s] * len[s];
+    }
+    // exponent-entropy bound n (8 + H) / 8, H = sum (f / n) log2(n / f)
+    double h = 0.0;
+    for (int s = 0; s < 256; ++s)
+        if (hist[s]) h += double(hist[s]) / double(n) * std::log2(double(n) / double(hist[s]));
+    const double bound = double(n) * (8.0 + h) / 8.0;
+    static const uint32_t order[4] = {16, 32, 8, 4};  // the decoder's fastest first
+    uint32_t best = order[0];
+    uint64_t best_size = ~uint64_t(0);
+    for (uint32_t c : order) {
+        const Layout L = layout_sizes(total_bits, c, lanes);
+        const SectionSizes sz = section_sizes(n, L.n_chunks, L.n_blocks, c, 11);
+        const uint64_t coded = kHeaderBytes + sz.bytes[kWords] + sz.bytes[kOffsets] + sz.bytes[kBlockout] +
+                               sz.bytes[kRaw];
+        if (double(coded) <= 1.02 * bound) return c;
+        if (coded < best_size) {
+            best_size = coded;
+            best = c;
+        }
+    }
+    return best;
+}
+
 dfc_status code_lengths(const uint64_t hist[256], uint32_t limit, uint8_t len[256]) {
     return package_merge(hist, limit, len);
 }
@@ -363,7 +393,7 @@ void canonical_codes(const uint8_t len[256], uint32_t code[256]) {
     Canon c;
     canonical(len, c, code);
 }
-bool encoder_params_ok(const dfc_params &p) { return params_ok(p); }
+bool encoder_params_ok(const dfc_params &p) { return params_ok(p, true); }
 uint64_t kraft_sum(const uint8_t len[256]) { return kraft(len); }
 void container_header(uint8_t *dst, const dfc_params &p, uint64_t n, uint64_t total_bits, uint64_t n_chunks,
                       uint64_t n_blocks, uint64_t rows, uint64_t cols, const SectionSizes &sz,
@@ -378,7 +408,7 @@ extern "C" {
 void dfc_default_params(dfc_params *p) {
     if (!p) return;
     std::memset(p, 0, sizeof(*p));
-    p->chunk_bytes = 16;
+    p->chunk_bytes = 0;  // automatic
     p->lanes_per_block = 64;
     p->max_code_len = kMaxLen;
     p->lut_bits = 11;
@@ -426,6 +456,19 @@ dfc_status dfc_encode_bound(uint64_t n, const dfc_params *pin, uint64_t *max_byt
     dfc_params p;
     if (pin) p = *pin; else dfc_default_params(&p);
     if (!max_bytes || !params_ok(p)) return DFC_EINVAL;
+    if (p.chunk_bytes == 0) {
+        // automatic: room for whichever chunk size the encoder picks
+        uint64_t most = 0;
+        for (uint32_t c : {4u, 8u, 16u, 32u}) {
+            p.chunk_bytes = c;
+            uint64_t b = 0;
+            const dfc_status st = dfc_encode_bound(n, &p, &b);
+            if (st != DFC_OK) return st;
+            most = std::max(most, b);
+        }
+        *max_bytes = most;
+        return DFC_OK;
+    }
     const uint64_t bits = n * uint64_t(p.max_code_len);
     Layout L = layout_sizes(bits, p.chunk_bytes, p.lanes_per_block);
     SectionSizes s = section_sizes(n, L.n_chunks, L.n_blocks, p.chunk_bytes, p.lut_bits);
@@ -489,6 +532,8 @@ dfc_status dfc_encode(const uint16_t *src, uint64_t n, const dfc_params *pin, co
         dfc_status st = package_merge(hist, p.max_code_len, len);
         if (st != DFC_OK) return st;
     }
+    if (p.chunk_bytes == 0)
+        p.chunk_bytes = p.layout == DFC_LAYOUT_FLAT ? choose_chunk_bytes(hist, len, p.lanes_per_block) : 16u;
     Canon canon;
     uint32_t code[256];
     canonical(len, canon, code);
@@ -617,7 +662,7 @@ dfc_status dfc_blob_info(const void *blob_v, uint64_t bytes, dfc_info *out) {
     p.lanes_per_block = in.lanes_per_block;
     p.max_code_len = in.max_code_len;
     p.lut_bits = in.lut_bits;
-    if (!params_ok(p)) return DFC_ECORRUPT;
+    if (!params_ok(p, false)) return DFC_ECORRUPT;
     if (in.n >= (uint64_t(1) << 32) || in.rows * in.cols != in.n) return DFC_ECORRUPT;
     PanelGeom g{};
     if (panel) {

@@ -56,6 +56,10 @@ inline void histogram_mt(const uint16_t *src, uint64_t n, uint64_t hist[256], un
 dfc_status code_lengths(const uint64_t hist[256], uint32_t limit, uint8_t len[256]);
 // Canonical codes (RFC 1951 section 3.2.2) for code lengths.
 void canonical_codes(const uint8_t len[256], uint32_t code[256]);
+// Automatic chunk size of the flat layout: the first of 16, 32, 8, 4 bytes
+// whose coded size is within 2% of the exponent-entropy bound, else the
+// smallest container.
+uint32_t choose_chunk_bytes(const uint64_t hist[256], const uint8_t len[256], uint32_t lanes);
 // Encoder parameters in range.
 bool encoder_params_ok(const dfc_params &p);
 // Kraft sum of the lengths scaled by 2^24 (2^24 for a complete code).

@@ -174,3 +174,36 @@ def entropy_bound_bytes(hist) -> float:
     n = float(np.asarray(hist, dtype=np.float64).sum())
     return n * (8.0 + cb.entropy_bits(hist)) / 8.0
 
+
+# Chunk sizes in the order an automatic choice tries them: the decoder's
+# fastest first (16 bytes per lane), then the larger chunk with half the
+# offset overhead, then the smaller ones.
+AUTO_CHUNK_ORDER = (16, 32, 8, 4)
+AUTO_SIZE_TARGET = 1.02
+
+
+def flat_coded_bytes(n: int, total_bits: int, chunk_bytes: int, lanes: int = 64) -> int:
+    """Coded size of a flat container, written out from n, the stream length
+    and the chunk geometry alone: 512-byte header and code lengths, the
+    stream words (whole blocks plus 4 guard words), the 5-bit chunk offsets
+    (n_chunks + 1 fields in 32-bit words plus one word of slack), the block
+    offsets (n_blocks + 1 words) and the raw bytes (n rounded up to 16)."""
+    _, n_blocks, n_chunks = st.layout_sizes(total_bits, chunk_bytes, lanes)
+    return (HEADER_BYTES + (n_chunks * chunk_bytes + 16) + 4 * (-(-5 * (n_chunks + 1) // 32) + 1) +
+            4 * (n_blocks + 1) + 16 * (-(-n // 16)))
+
+
+def choose_chunk_bytes(hist, lengths, lanes: int = 64) -> int:
+    """Automatic chunk size of the flat layout: the first of AUTO_CHUNK_ORDER
+    whose coded size is within 2% of the exponent-entropy bound, else the one
+    with the smallest coded size (the earlier one on a tie)."""
+    h = np.asarray(hist, dtype=np.int64)
+    n = int(h.sum())
+    total_bits = int((h * np.asarray(lengths, dtype=np.int64)).sum())
+    bound = entropy_bound_bytes(h)
+    sizes = [(flat_coded_bytes(n, total_bits, c, lanes), c) for c in AUTO_CHUNK_ORDER]
+    for size, c in sizes:
+        if size <= AUTO_SIZE_TARGET * bound:
+            return c
+    return min(sizes, key=lambda t: t[0])[1]
+

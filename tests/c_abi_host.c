@@ -61,7 +61,7 @@ int main(void) {
     CHECK(kraft_num == ((uint64_t)1 << 24));
 
     dfc_default_params(&p);
-    CHECK(p.chunk_bytes == 16 && p.lanes_per_block == 64 && p.max_code_len == 24);
+    CHECK(p.chunk_bytes == 0 && p.lanes_per_block == 64 && p.max_code_len == 24); /* 0: automatic */
     CHECK(dfc_encode_bound(n, &p, &bound) == DFC_OK && bound > n);
     blob = malloc((size_t)bound);
     CHECK(blob != NULL);

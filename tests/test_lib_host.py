@@ -113,7 +113,8 @@ def test_external_codebook_and_missing_symbol():
     h = cb.histogram(fields.split(x)[0]) + 1  # smoothed: every exponent has a code
     book = dfc.build_codebook(h, 24)
     b = dfc.encode(x, codebook=book)
-    assert bytes(b) == bl.write_blob(st.encode(x, 16, 64, lengths=book.lengths), 11, 64, 512)
+    C = bl.choose_chunk_bytes(cb.histogram(fields.split(x)[0]), book.lengths)
+    assert bytes(b) == bl.write_blob(st.encode(x, C, 64, lengths=book.lengths), 11, 64, 512)
     e = fields.split(x)[0]
     h2 = cb.histogram(e)
     h2[int(e[0])] = 0  # a present exponent without a code
@@ -461,3 +462,33 @@ def test_ans_frequencies_take_back_tie():
     f = oans.parse_ans_blob(bytes(blob))["freqs"]
     assert int(f[10]) == 1997 and int(f[20]) == 1998
     assert all(int(f[s]) == 1 for s in range(100, 201)) and int(np.asarray(f).sum()) == 4096
+
+
+@pytest.mark.parametrize("kind", ["gauss", "outliers", "student_t", "bimodal", "uniform", "ladder", "tiny"])
+def test_automatic_chunk_size_matches_oracle(kind):
+    """The default chunk size is automatic: the library's choice and its
+    container equal the oracle's (flat layout), and the result is within 2%
+    of the exponent-entropy bound whenever some chunk size is."""
+    x = {"gauss": lambda: synth.gaussian((512, 1024), 0.02, (150,)),
+         "outliers": lambda: synth.gaussian_with_outliers((512, 1024), 0.02, (151,)),
+         "student_t": lambda: synth.stress("student_t", 512, 1024),
+         "bimodal": lambda: synth.stress("bimodal", 512, 1024),
+         "uniform": lambda: synth.stress("uniform", 512, 1024),
+         "ladder": lambda: synth.stress("ladder", 512, 1024),
+         "tiny": lambda: synth.gaussian((3, 37), 0.02, (152,))}[kind]()
+    e = fields.split(x)[0]
+    h = cb.histogram(e)
+    lengths = cb.package_merge_lengths(h, 24)
+    C = bl.choose_chunk_bytes(h, lengths)
+    b = dfc.encode(x)
+    info = dfc.blob_info(b)
+    assert info.chunk_bytes == C, kind
+    assert bytes(b) == bl.write_blob(st.encode(x, C, 64), 11, *x.shape), kind
+    bound = bl.entropy_bound_bytes(h)
+    sizes = [dfc.blob_info(dfc.encode(x, chunk_bytes=c)).coded_bytes for c in (4, 8, 16, 32)]
+    if min(sizes) <= 1.02 * bound:
+        assert info.coded_bytes <= 1.02 * bound, kind
+    if kind == "uniform":
+        assert C == 32
+    if kind in ("gauss", "outliers"):
+        assert C == 16

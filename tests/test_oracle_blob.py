@@ -62,3 +62,64 @@ def test_coded_bytes_closed_form(C):
         want = (512 + (nc * C + 16) + 4 * ((5 * (nc + 1) + 31) // 32 + 1) + 4 * (nb + 1)
                 + 16 * ((n + 15) // 16))
         assert bl.coded_bytes(p) == want, (C, n)
+
+
+@pytest.mark.parametrize("kind", ["gauss", "uniform", "ladder", "bimodal", "tiny", "empty"])
+def test_automatic_chunk_choice_against_real_containers(kind):
+    """choose_chunk_bytes against the rule applied to containers actually
+    written at every chunk size: the first of 16, 32, 8, 4 whose coded size
+    is within 2% of the bound, else the smallest container (earlier on a
+    tie); and flat_coded_bytes equal to those containers' coded size."""
+    from lossless_entropy_coded_dfc_amd import synth
+    x = {"gauss": lambda: synth.gaussian((256, 1024), 0.02, (160,)),
+         "uniform": lambda: synth.uniform_bits((256, 1024), (161,)),
+         "ladder": lambda: synth.exponent_ladder((256, 1024), (162,)),
+         "bimodal": lambda: synth.bimodal((256, 1024), 0.02, (163,)),
+         "tiny": lambda: synth.gaussian((5, 7), 0.02, (164,)),
+         "empty": lambda: np.zeros(0, dtype=np.uint16)}[kind]()
+    e, _ = fields.split(x)
+    h = cb.histogram(e)
+    lengths = cb.package_merge_lengths(h, 24)
+    size = {}
+    for C in (4, 8, 16, 32):
+        enc = st.encode(x, C, 64, lengths=lengths)
+        size[C] = bl.coded_bytes(bl.parse_blob(bl.write_blob(enc, 11)))
+        assert bl.flat_coded_bytes(x.size, enc["total_bits"], C) == size[C], (kind, C)
+    if x.size == 0:
+        return
+    bound = bl.entropy_bound_bytes(h)
+    within = [C for C in (16, 32, 8, 4) if size[C] <= 1.02 * bound]
+    want = within[0] if within else min((16, 32, 8, 4), key=lambda c: size[c])
+    assert bl.choose_chunk_bytes(h, lengths) == want, kind
+    if kind == "uniform":
+        assert want == 32
+    if kind == "gauss":
+        assert want == 16
+
+
+def test_automatic_chunk_choice_hand_worked():
+    """Two hand-worked cases.  16 exponents of 4096 values each, every code 4
+    bits (entropy 4 bits): n = 65536, 262144 code bits.  At 16 bytes per
+    chunk: 2048 chunks in 32 blocks; coded = 512 + (2048 * 16 + 16) + 4 *
+    (ceil(5 * 2049 / 32) + 1) + 4 * 33 + 65536 = 512 + 32784 + 1288 + 132 +
+    65536 = 100252 bytes against a bound of 65536 * 12 / 8 = 98304 (1.0198):
+    16, the first tried, is chosen.  Two exponents of 8192 values each, one
+    bit per code (entropy 1 bit): n = 16384, 16384 code bits, bound 18432.
+    16 bytes: 128 chunks, 2 blocks, 512 + 2064 + 4 * (21 + 1) + 12 + 16384 =
+    19060; 32 bytes: 64 chunks, 1 block, 512 + 2064 + 4 * (11 + 1) + 8 +
+    16384 = 19016; 8 bytes: 256 chunks, 4 blocks, 512 + 2064 + 4 * (41 + 1) +
+    20 + 16384 = 19148; 4 bytes: 512 chunks, 8 blocks, 512 + 2064 + 4 * (81 +
+    1) + 36 + 16384 = 19324.  None is within 2% (18800.64), so the smallest
+    container, 32 bytes, is chosen."""
+    h = np.zeros(256, dtype=np.int64)
+    h[100:116] = 4096
+    lengths = np.zeros(256, dtype=np.uint8)
+    lengths[100:116] = 4
+    assert bl.flat_coded_bytes(65536, 262144, 16) == 100252
+    assert bl.choose_chunk_bytes(h, lengths) == 16
+    h2 = np.zeros(256, dtype=np.int64)
+    h2[7] = h2[8] = 8192
+    l2 = np.zeros(256, dtype=np.uint8)
+    l2[7] = l2[8] = 1
+    assert [bl.flat_coded_bytes(16384, 16384, c) for c in (16, 32, 8, 4)] == [19060, 19016, 19148, 19324]
+    assert bl.choose_chunk_bytes(h2, l2) == 32

@@ -92,6 +92,15 @@ MUTANTS = [
     ("Huffman depth of one symbol is zero", "codebook.py",
      "return 1 if items else 0", "return 0",
      ["test_oracle_codebook.py"]),
+    ("automatic chunk size tries 32 bytes first", "blob.py",
+     "AUTO_CHUNK_ORDER = (16, 32, 8, 4)", "AUTO_CHUNK_ORDER = (32, 16, 8, 4)",
+     ["test_oracle_blob.py"]),
+    ("automatic chunk size compares against 2.5%", "blob.py",
+     "AUTO_SIZE_TARGET = 1.02", "AUTO_SIZE_TARGET = 1.025",
+     ["test_oracle_blob.py"]),
+    ("closed-form size forgets the guard words", "blob.py",
+     "return (HEADER_BYTES + (n_chunks * chunk_bytes + 16) +", "return (HEADER_BYTES + (n_chunks * chunk_bytes) +",
+     ["test_oracle_blob.py"]),
     ("entropy in nats", "codebook.py",
      "return float(-(p * np.log2(p)).sum())", "return float(-(p * np.log(p)).sum())",
      ["test_oracle_codebook.py"]),
