@@ -62,7 +62,11 @@ typedef enum {
  * (l = 0..63, j = 0..7) is W[32 p + l % 32][c0 + 16 t + 8 (l / 32) + j], the
  * A-operand order of a 32x32x16 bf16 matrix instruction.  Every item's codes
  * start on a fresh chunk and form their own blocks; a table of first chunk,
- * first block and code bits per item travels in the container.
+ * first block and code bits per item travels in the container, and so does
+ * the number of codes whose first bit lies in each chunk (u16 per chunk), an
+ * auxiliary variable of the two-phase decode (DFloat11 blog, section 03
+ * item 2) that gives a decoding lane its write position by a prefix sum
+ * instead of a counting pass over its chunk.
  * PADDED: row-major like FLAT, but no code crosses a chunk boundary: a code
  * that does not fit in what is left of its chunk opens the next chunk, and
  * the unused tail is set to ones.  Every chunk then decodes from its first
@@ -126,7 +130,8 @@ typedef struct {
     uint64_t rows, cols;
     uint64_t blob_bytes;   /* whole container */
     uint64_t coded_bytes;  /* header + lengths + stream + offsets + block offsets + raw
-                              (excludes derived decode tables and alignment padding) */
+                              (+ the panel table and chunk counts in the panel layout;
+                              excludes derived decode tables and alignment padding) */
     uint64_t total_bits;   /* code stream length */
     uint64_t n_chunks, n_blocks;
     uint64_t off_tables, tables_bytes;  /* Huffman layouts: 0, 0; ANS: the frequencies f (512 B) */
@@ -142,6 +147,8 @@ typedef struct {
     uint64_t off_panels, panels_bytes;  /* PANEL: per-item table, (n_items + 1) x 4 u32 */
     uint32_t ans_steps;                 /* ANS: steps per block S; 0 otherwise */
     uint32_t ans_prob_bits;             /* ANS: 12 (frequencies sum to 2^12); 0 otherwise */
+    uint64_t off_counts, counts_bytes;  /* PANEL: codes starting in every chunk, n_chunks x u16
+                                           (padded to 16 bytes); 0, 0 otherwise */
 } dfc_info;
 
 /* One matrix of a batched decode. */

@@ -77,7 +77,8 @@ class Info(ctypes.Structure):
             "chunk_bytes", "lanes_per_block", "max_code_len", "lut_bits", "layout",
             "n_used", "min_len", "max_len", "max_block_elems", "panel_rows", "panel_k")] + \
         [(name, ctypes.c_uint64) for name in ("n_items", "off_panels", "panels_bytes")] + \
-        [(name, ctypes.c_uint32) for name in ("ans_steps", "ans_prob_bits")]
+        [(name, ctypes.c_uint32) for name in ("ans_steps", "ans_prob_bits")] + \
+        [(name, ctypes.c_uint64) for name in ("off_counts", "counts_bytes")]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}

@@ -113,8 +113,8 @@ void ans_container_head(uint8_t *dst, uint64_t n, uint64_t nw, uint64_t nb, uint
     store_le<uint64_t>(dst + hdr::cols, cols);
     store_le<uint32_t>(dst + hdr::tile_k, S);
     for (int i = 0; i < kNumSections; ++i) {
-        store_le<uint64_t>(dst + hdr::sections + 16 * i, off[i]);
-        store_le<uint64_t>(dst + hdr::sections + 16 * i + 8, sz.bytes[i]);
+        store_le<uint64_t>(dst + hdr::section(i), off[i]);
+        store_le<uint64_t>(dst + hdr::section(i) + 8, sz.bytes[i]);
     }
     store_le<uint64_t>(dst + hdr::blob_bytes, blob_bytes);
     uint8_t *tab = dst + off[kTables];
@@ -189,8 +189,8 @@ dfc_status ans_blob_info(const uint8_t *b, uint64_t bytes, dfc_info &in) {
     const uint64_t blob_bytes = place_sections(sz, off);
     if (blob_bytes != in.blob_bytes) return DFC_ECORRUPT;
     for (int i = 0; i < kNumSections; ++i) {
-        if (load_le<uint64_t>(b + hdr::sections + 16 * i) != off[i]) return DFC_ECORRUPT;
-        if (load_le<uint64_t>(b + hdr::sections + 16 * i + 8) != sz.bytes[i]) return DFC_ECORRUPT;
+        if (load_le<uint64_t>(b + hdr::section(i)) != off[i]) return DFC_ECORRUPT;
+        if (load_le<uint64_t>(b + hdr::section(i) + 8) != sz.bytes[i]) return DFC_ECORRUPT;
     }
     if (bytes < blob_bytes) return DFC_ESIZE;
 

@@ -205,11 +205,16 @@ __device__ __forceinline__ void or_4_bytes(uint8_t *lds_base, uint32_t q, uint32
 // the chunk's last one are the next chunk's first codes, identical to what
 // the next lane writes there; so neither needs to be cut off.  Lookups stop
 // at the chunk's end bit, which bounds the spill past the block's last
-// exponent to three codes.
+// exponent to three codes.  Returns the number of codes that start in
+// [start, end), as count_codes does (callers that take their positions
+// from stored counts check them with it; for the others it is dead code).
 template <int C>
-__device__ __forceinline__ void write_codes(const Chunk<C> &ck, int start, int end, uint8_t *lds_base,
-                                            uint32_t q0, const Tables &t) {
+__device__ __forceinline__ uint32_t write_codes(const Chunk<C> &ck, int start, int end, uint8_t *lds_base,
+                                                uint32_t q0, const Tables &t) {
     constexpr int NW = C / 4;
+    // the boundary mask at `end`, looked up first so that the stream words
+    // need not outlive the loop
+    const uint32_t end_mask = t.mask[window_at<NW>(ck.w, uint32_t(end)) >> t.kshift];
     uint32_t acc = kBias - uint32_t(start);
 #pragma unroll
     for (int k = -1; k < NW; ++k) {
@@ -234,6 +239,10 @@ __device__ __forceinline__ void write_codes(const Chunk<C> &ck, int start, int e
         }
         acc += 32u;
     }
+    uint32_t cnt = acc >> 16;
+    const int pos = 32 * (NW + 1) - int(lo16(acc)) + int(kBias);
+    if (pos > end) cnt -= __popc(end_mask & ((1u << (pos - end)) - 1u));
+    return cnt;
 }
 
 // Padded layout, phase one: the number of codes, decoded from the chunk's

@@ -431,6 +431,7 @@ struct PanelArgs {
     uint32_t *item_bits;    // pass 1: code bits per item
     const uint32_t *first;  // pass 2: (first chunk, first block) per item, n_items + 1 pairs
     uint32_t *words, *offw, *blockout;
+    uint32_t *counts;  // u16 per chunk, two to a word
     uint8_t *raw;
     uint32_t chunk_shift, lanes_shift;  // log2(8 C), log2(T)
 };
@@ -500,7 +501,10 @@ __global__ __launch_bounds__(256) void panel_bits_kernel(const PanelArgs a, cons
 // with neighbours ORed), writes their raw bytes (8 per octet), and, for
 // every chunk of the item whose first bit its codes cover, that chunk's
 // 5-bit offset (the next code starts where the covering code ends) and, on
-// block boundaries, the block's first element (panel order).
+// block boundaries, the block's first element (panel order).  Its codes
+// start in consecutive chunks: it adds the number that start in each chunk
+// to that chunk's u16 count when it moves on (atomically, since the first
+// and last chunk, and the word of two counts, may be shared).
 __global__ __launch_bounds__(256) void panel_pack_kernel(const PanelArgs a, const Book book) {
     __shared__ uint32_t sh[kSegThreads];
     __shared__ BookLds bk;
@@ -533,6 +537,14 @@ __global__ __launch_bounds__(256) void panel_pack_kernel(const PanelArgs a, cons
     uint32_t nacc = uint32_t(pos & 31);
     uint64_t w = pos >> 5;
     const uint64_t first_word = w, last_word = bits ? (start + bits - 1) >> 5 : w;
+    uint64_t cur = pos >> a.chunk_shift;
+    uint32_t ncur = 0;
+    auto flush_count = [&]() {
+        if (ncur) {
+            const uint64_t c = c0 + cur;
+            atomicAdd(a.counts + (c >> 1), ncur << (16 * uint32_t(c & 1)));
+        }
+    };
     for (uint32_t ob = o0; ob < o1; ob += kOctBatch) {
         uint4 v[kOctBatch];
 #pragma unroll
@@ -549,6 +561,12 @@ __global__ __launch_bounds__(256) void panel_pack_kernel(const PanelArgs a, cons
                 r[j >> 2] |= raw_of(b) << (8 * (j & 3));
                 const uint32_t e = exponent_of(b);
                 const uint32_t l = bk.len[e];
+                if ((pos >> a.chunk_shift) != cur) {
+                    flush_count();
+                    cur = pos >> a.chunk_shift;
+                    ncur = 0;
+                }
+                ++ncur;
                 const uint64_t c = (pos >> a.chunk_shift) + 1;
                 if (c < chunks && (c << a.chunk_shift) <= pos + l) {
                     const uint32_t off = uint32_t(pos + l - (c << a.chunk_shift));
@@ -574,6 +592,7 @@ __global__ __launch_bounds__(256) void panel_pack_kernel(const PanelArgs a, cons
         }
     }
     if (nacc > 0) or_word(words, w, uint32_t(acc << (32 - nacc)));
+    flush_count();
 }
 
 // Host copy of a workspace layout.
@@ -718,6 +737,7 @@ dfc_status encode_panel_device(const uint16_t *src_dev, uint64_t n, const dfc_pa
     a.words = reinterpret_cast<uint32_t *>(dst + off[dfc::kWords]);
     a.offw = reinterpret_cast<uint32_t *>(dst + off[dfc::kOffsets]);
     a.blockout = reinterpret_cast<uint32_t *>(dst + off[dfc::kBlockout]);
+    a.counts = reinterpret_cast<uint32_t *>(dst + off[dfc::kCounts]);
     a.raw = dst + off[dfc::kRaw];
     hipLaunchKernelGGL(panel_pack_kernel, dim3(uint32_t(g.n_items)), dim3(kSegThreads), 0, st, a, book);
     // the host vectors must outlive the copies above

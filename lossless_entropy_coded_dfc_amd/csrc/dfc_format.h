@@ -3,8 +3,8 @@
 //
 // Container: 256-byte header, 256 code lengths, then the sections tables
 // (empty in the Huffman layouts; the rANS frequencies in the ANS layout),
-// words, offsets (empty in the padded layout), blockout, raw (and panels,
-// used by the panel layout only), each at the next multiple of 256 bytes,
+// words, offsets (empty in the padded layout), blockout, raw (and panels and
+// counts, used by the panel layout only), each at the next multiple of 256 bytes,
 // zero padding.  Little-endian.  A container holds the code and the coded
 // data only: the decode tables are derived from the code by the kernels.
 #pragma once
@@ -29,10 +29,13 @@ constexpr int chunk_bytes = 40, lanes = 44, max_code_len = 48, lut_bits = 52, la
 constexpr int panel_rows = 60, rows = 64, cols = 72, tile_k = 80, reserved = 84;
 constexpr int sections = 88;  // 6 x (u64 offset, u64 bytes): tables, words, offsets, blockout, raw, panels
 constexpr int blob_bytes = 184;
+constexpr int counts = 192;   // (u64 offset, u64 bytes) of the counts section
+// Header byte offset of section i's (offset, bytes) pair.
+constexpr int section(int i) { return i < 6 ? sections + 16 * i : counts; }
 constexpr int lengths = 256;
 }  // namespace hdr
 
-enum Section { kTables = 0, kWords, kOffsets, kBlockout, kRaw, kPanels, kNumSections };
+enum Section { kTables = 0, kWords, kOffsets, kBlockout, kRaw, kPanels, kCounts, kNumSections };
 
 // LDS image of the decode tables the kernels derive from the code lengths
 // for a k-bit first level (see dfc_tables.h; never stored in a container):
@@ -68,6 +71,7 @@ inline SectionSizes section_sizes(uint64_t n, uint64_t n_chunks, uint64_t n_bloc
     s.bytes[kBlockout] = 4 * (n_blocks + 1);
     s.bytes[kRaw] = 16 * ceil_div(n, 16);
     s.bytes[kPanels] = n_items ? 16 * (n_items + 1) : 0;
+    s.bytes[kCounts] = n_items ? 16 * ceil_div(2 * n_chunks, 16) : 0;
     return s;
 }
 
@@ -89,11 +93,13 @@ inline SectionSizes ans_section_sizes(uint64_t n, uint64_t n_words, uint64_t n_b
     s.bytes[kBlockout] = 4ull * kAnsLanes * n_blocks;
     s.bytes[kRaw] = 16 * ceil_div(n, 16);
     s.bytes[kPanels] = 0;
+    s.bytes[kCounts] = 0;
     return s;
 }
 
 // Panel layout geometry: items of 32 rows x panel_k columns, row panels
-// first, then column slices.
+// first, then column slices.  The counts section holds, per chunk (u16), the
+// number of codes whose first bit lies in that chunk.
 constexpr uint32_t kPanelRows = 32;
 constexpr uint32_t kSubtileK = 16;
 struct PanelGeom {

@@ -2,9 +2,13 @@
 // stored as a panel-layout DFC1 container (bf16 weights whose exponents are
 // Huffman-coded, DFloat11 blog, sections 02 and 03).
 //
-// The weights are decoded exactly as by the flat decoder (count pass,
-// wavefront scan, write pass into LDS), but the decoded values never reach
-// HBM: each complete 32 x 16 sub-tile of W is assembled from its staged
+// The weights are decoded as by the flat decoder's two phases, except that
+// the first phase reads every chunk's code count from the container (the
+// panel layout stores them) instead of decoding the chunk to count them: a
+// wavefront scan of the counts gives each lane its write position, the
+// write pass puts the exponents into LDS and checks that the lane's chunk
+// held exactly its stored count.  The decoded values never reach HBM: each
+// complete 32 x 16 sub-tile of W is assembled from its staged
 // exponents and raw bytes straight into the A operand of one 32x32x16 bf16
 // MFMA per 32 output columns, and the products accumulate in fp32 registers.
 //
@@ -40,16 +44,18 @@ struct GemmArgs {
     const uint32_t *offw;      // packed 5-bit chunk offsets
     const uint32_t *blockout;  // u32 out[n_blocks + 1], indices in panel order
     const uint32_t *items;     // (n_items + 1) x {first chunk, first block, code bits, 0}
+    const uint16_t *counts;    // codes starting in every chunk
     const uint8_t *raw;        // raw bytes in panel order
     const uint8_t *lengths;    // the 256 code lengths (container bytes 256..511)
     const uint8_t *tables;     // tables from dfc_derive_tables, or null: derive them here
     const uint16_t *x;         // B vectors of K bf16: x[b K + k]
     float *y;                  // B vectors of M fp32: y[b M + m]
-    uint32_t words_bytes, offw_bytes, raw_bytes, x_bytes, y_bytes;
+    uint32_t words_bytes, offw_bytes, raw_bytes, x_bytes, y_bytes, counts_bytes;
     uint32_t n_panels, slices, panel_k, cols, rows, batch;
     uint32_t wpp, group;       // wavefronts per panel in a workgroup, panels per workgroup
     uint32_t split, rounds;    // workgroups per panel; rounds = ceil(n_panels / group) * split
     uint32_t tables_bytes, lut_bits, stage_bytes;
+    uint32_t max_block;        // most codes a block may place (the staging capacity)
     uint32_t *status;
 };
 
@@ -86,17 +92,20 @@ __device__ __forceinline__ ItemPos item_pos(const GemmArgs &g, uint32_t q) {
 
 // The blocks of a wavefront's items (q0, q0 + qstep, ... below qend), one
 // after another: each complete sub-tile is multiplied into acc.  The next
-// block's stream words, chunk offsets and output range (in the same item or
-// the next one) are requested before the current block is decoded, so their
-// memory latency overlaps its decoding.  Returns false (and sets the status
-// word) if a block's decoded count disagrees with its block offsets; acc then
-// holds a partial sum.
+// block's stream words, chunk offsets, chunk counts and output range (in the
+// same item or the next one) are requested before the current block is
+// decoded, so their memory latency overlaps its decoding.  Returns false (and
+// sets the status word) if a block's stored counts disagree with its block
+// offsets or exceed the staging capacity (at once: acc then holds a partial
+// sum), or if a chunk held a different number of codes than stored (noted
+// per lane and reported after the last block, which keeps the write pass's
+// result off the critical path of the loop).
 template <int C, int NT>
 __device__ __forceinline__ bool gemm_items(const GemmArgs &g, uint32_t q0, uint32_t qstep, uint32_t qend,
                                            const Tables &t, uint8_t *stage, uint32_t stage_off, uint32_t lane,
                                            const __amdgpu_buffer_rsrc_t &words, const __amdgpu_buffer_rsrc_t &offw,
-                                           const __amdgpu_buffer_rsrc_t &raw, const __amdgpu_buffer_rsrc_t &xr,
-                                           uint32_t xcol, f32x16 (&acc)[NT]) {
+                                           const __amdgpu_buffer_rsrc_t &raw, const __amdgpu_buffer_rsrc_t &cr,
+                                           const __amdgpu_buffer_rsrc_t &xr, uint32_t xcol, f32x16 (&acc)[NT]) {
     constexpr int PF = GemmPrefetch<C>::N;
     extern __shared__ __align__(16) uint8_t lds[];
     const const_u32_ptr blockout = (const_u32_ptr)(g.blockout);
@@ -105,9 +114,12 @@ __device__ __forceinline__ bool gemm_items(const GemmArgs &g, uint32_t q0, uint3
     uint32_t b = cur.b0;
     Chunk<C> ck;
     load_chunk<C>(words, offw, cur.c0 + lane, ck);
+    uint32_t stored = __builtin_amdgcn_raw_buffer_load_b16(cr, 2u * (cur.c0 + lane), 0, 0);
     uint32_t s_out = blockout[b], e_out = blockout[b + 1];
     wait_for(ck);
+    wait_for(stored);
     u32x2 carry = {0u, 0u};
+    bool miss = false;  // a chunk whose codes disagree with its stored count
     for (;;) {
         b = __builtin_amdgcn_readfirstlane(b);
         const uint32_t rs = s_out - cur.e0, base = rs & ~511u, lead = rs - base;
@@ -129,9 +141,11 @@ __device__ __forceinline__ bool gemm_items(const GemmArgs &g, uint32_t q0, uint3
         if (!same && more) nit = item_pos(g, cur.q + qstep);
         const uint32_t bn = same ? b + 1u : nit.b0;
         Chunk<C> nxt{};
-        uint32_t s_nxt = 0, e_nxt = 0;
+        uint32_t s_nxt = 0, e_nxt = 0, stored_nxt = 0;
         if (more) {
-            load_chunk<C>(words, offw, nit.c0 + (bn - nit.b0) * kWave + lane, nxt);
+            const uint32_t cn = nit.c0 + (bn - nit.b0) * kWave + lane;
+            load_chunk<C>(words, offw, cn, nxt);
+            stored_nxt = __builtin_amdgcn_raw_buffer_load_b16(cr, 2u * cn, 0, 0);
             s_nxt = blockout[bn];
             e_nxt = blockout[bn + 1];
         }
@@ -147,16 +161,20 @@ __device__ __forceinline__ bool gemm_items(const GemmArgs &g, uint32_t q0, uint3
         chunk_span<C>(ck, cur.c0 + ci,
                       int(min(max(int64_t(cur.bits) - int64_t(ci) * (8 * C), int64_t(-1)), int64_t(8 * C + 32))),
                       start, end);
-        // count and write passes at a raised wave priority, the products at the
-        // normal one (wavefronts that are decoding issue first)
+        // the write pass at a raised wave priority, the products at the normal
+        // one (wavefronts that are decoding issue first)
         __builtin_amdgcn_s_setprio(1);
-        const uint32_t cnt = start < end ? count_codes<C>(ck, start, end, t) : 0u;
+        const uint32_t cnt = start < end ? stored : 0u;
         const uint32_t incl = wave_inclusive_scan(cnt);
         const uint32_t total = __builtin_amdgcn_readlane(incl, kWave - 1);
-        const bool bad = (total != total_want) | (__builtin_amdgcn_ballot_w64(cnt > 8u * C) != 0);
-        if (!bad && cnt) write_codes<C>(ck, start, end, lds, stage_off + lead + (incl - cnt), t);
+        const bool bad = (total != total_want) | (total_want > g.max_block) |
+                   (__builtin_amdgcn_ballot_w64(cnt > 8u * C) != 0);
+        uint32_t got = cnt;
+        if (!bad && cnt) got = write_codes<C>(ck, start, end, lds, stage_off + lead + (incl - cnt), t);
+        miss |= (got != cnt) | ((start < end) & (cnt == 0));
         wait_for(R);
         wait_for(nxt);
+        wait_for(stored_nxt);
         if (bad) {
             if (lane == 0 && g.status) atomicOr(g.status, kStatusCorrupt);
             return false;
@@ -211,8 +229,13 @@ __device__ __forceinline__ bool gemm_items(const GemmArgs &g, uint32_t q0, uint3
         cur = nit;
         b = bn;
         ck = nxt;
+        stored = stored_nxt;
         s_out = s_nxt;
         e_out = e_nxt;
+    }
+    if (__builtin_amdgcn_ballot_w64(miss) != 0) {
+        if (lane == 0 && g.status) atomicOr(g.status, kStatusCorrupt);
+        return false;
     }
     return true;
 }
@@ -224,7 +247,7 @@ __device__ __forceinline__ bool gemm_items(const GemmArgs &g, uint32_t q0, uint3
 // area holds at least 4 KB, which the reduction reuses for one 32 x 32 fp32
 // tile per wavefront.
 template <int C, int NT>
-__global__ __launch_bounds__(1024) void dfc_gemm_kernel(const GemmArgs g) {
+__global__ __launch_bounds__(512) void dfc_gemm_kernel(const GemmArgs g) {
     extern __shared__ __align__(16) uint8_t lds[];
     load_or_derive_tables(lds, g.tables, g.tables_bytes, g.lengths, g.lut_bits);
     const Tables t = tables_view(lds, g.lut_bits);
@@ -240,6 +263,8 @@ __global__ __launch_bounds__(1024) void dfc_gemm_kernel(const GemmArgs g) {
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t *>(g.offw), 0, int(g.offw_bytes), kBufferConfig);
     const __amdgpu_buffer_rsrc_t raw =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(g.raw), 0, int(g.raw_bytes), kBufferConfig);
+    const __amdgpu_buffer_rsrc_t cr =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(g.counts), 0, int(g.counts_bytes), kBufferConfig);
     const __amdgpu_buffer_rsrc_t xr =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(g.x), 0, int(g.x_bytes), kBufferConfig);
     const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(g.y, 0, int(g.y_bytes), kBufferConfig);
@@ -257,7 +282,7 @@ __global__ __launch_bounds__(1024) void dfc_gemm_kernel(const GemmArgs g) {
         for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x16{};
         if (p < g.n_panels)
             gemm_items<C, NT>(g, p * g.slices + part * wpp + sw, stride, (p + 1) * g.slices, t, stage, stage_off, lane,
-                              words, offw, raw, xr, xcol, acc);
+                              words, offw, raw, cr, xr, xcol, acc);
         // D[i][j] of a 32x32 tile: i = 8 (r / 4) + 4 (lane / 32) + r % 4,
         // j = lane % 32.  Value r of lane L goes to slot 4 (64 (r / 4) + L) +
         // r % 4 of the wavefront's tile, so that element e of a float4 slot
@@ -308,9 +333,14 @@ template <int C, int NT>
 dfc_status launch_gemm(const GemmArgs &proto, uint32_t max_block, hipStream_t stream) {
     GemmArgs g = proto;
     // staging: a carried partial sub-tile (< 512) + the block + spill, rounded
-    // to 16, and at least one 32 x 32 fp32 tile for the reduction
-    const uint32_t stage = std::max(4096u, (511u + max_block + 32u + 15u) & ~15u);
+    // to 16, and at least one 32 x 32 fp32 tile for the reduction.  The spill
+    // allows for one lane whose chunk holds more codes than stored (the
+    // write pass stops at the chunk's end bit: at most 8C + 31 codes and
+    // three past them, each ORed as two aligned dwords); the kernel then
+    // reports it.
+    const uint32_t stage = std::max(4096u, (511u + max_block + 8u * C + 48u + 15u) & ~15u);
     g.stage_bytes = stage;
+    g.max_block = max_block;
     if (!allow_full_lds(reinterpret_cast<const void *>(&dfc_gemm_kernel<C, NT>))) return DFC_EHIP;
     // about 8 wavefronts per workgroup: up to 8 per panel (one slice each
     // when the panel has 8 slices or fewer), several panels when it has few
@@ -382,7 +412,8 @@ dfc_status dfc_decode_gemm(const void *w_blob_dev, const dfc_info *info, const v
     if (in.lut_bits < 8 || in.lut_bits > 12 || in.min_len < 1) return DFC_EINVAL;
     if (in.max_block_elems > 64u * dfc::ceil_div(8ull * C, in.min_len)) return DFC_EINVAL;
     const uint64_t limit = kNowhere - 64u * 1024u;
-    if (in.words_bytes > limit || in.offsets_bytes > limit || in.raw_bytes > limit ||
+    if (in.counts_bytes < 2 * in.n_chunks) return DFC_EINVAL;
+    if (in.words_bytes > limit || in.offsets_bytes > limit || in.raw_bytes > limit || in.counts_bytes > limit ||
         2ull * DFC_GEMM_MAX_BATCH * in.cols > limit || 4ull * DFC_GEMM_MAX_BATCH * in.rows > limit)
         return DFC_EUNSUPPORTED;
     const uint8_t *base = static_cast<const uint8_t *>(w_blob_dev);
@@ -392,6 +423,8 @@ dfc_status dfc_decode_gemm(const void *w_blob_dev, const dfc_info *info, const v
     g.offw = reinterpret_cast<const uint32_t *>(base + in.off_offsets);
     g.blockout = reinterpret_cast<const uint32_t *>(base + in.off_blockout);
     g.items = reinterpret_cast<const uint32_t *>(base + in.off_panels);
+    g.counts = reinterpret_cast<const uint16_t *>(base + in.off_counts);
+    g.counts_bytes = uint32_t(in.counts_bytes);
     g.raw = base + in.off_raw;
     g.lengths = base + dfc::hdr::lengths;
     g.tables = static_cast<const uint8_t *>(tables_dev);

@@ -154,8 +154,8 @@ void write_header(uint8_t *dst, const dfc_params &p, uint64_t n, uint64_t total_
     store_le<uint64_t>(dst + hdr::cols, cols);
     store_le<uint32_t>(dst + hdr::tile_k, p.layout == DFC_LAYOUT_PANEL ? p.panel_k : 0);
     for (int i = 0; i < kNumSections; ++i) {
-        store_le<uint64_t>(dst + hdr::sections + 16 * i, off[i]);
-        store_le<uint64_t>(dst + hdr::sections + 16 * i + 8, sz.bytes[i]);
+        store_le<uint64_t>(dst + hdr::section(i), off[i]);
+        store_le<uint64_t>(dst + hdr::section(i) + 8, sz.bytes[i]);
     }
     store_le<uint64_t>(dst + hdr::blob_bytes, blob_bytes);
     std::memcpy(dst + hdr::lengths, len, 256);
@@ -221,6 +221,7 @@ dfc_status encode_panel(const uint16_t *src, uint64_t n, const dfc_params &p, co
     uint8_t *raw = dst + off[kRaw];
     uint8_t *blockout = dst + off[kBlockout];
     uint8_t *panels = dst + off[kPanels];
+    uint8_t *counts = dst + off[kCounts];
     std::vector<uint8_t> offs(n_chunks + 1, 0);
     // Pass 2: pack every item.
     parallel_for(nt, [&](unsigned t) {
@@ -240,6 +241,8 @@ dfc_status encode_panel(const uint16_t *src, uint64_t n, const dfc_params &p, co
                     ++ci;
                 }
                 const uint32_t l = len[e];
+                uint8_t *cnt = counts + 2 * (c0 + pos / chunk_bits);
+                store_le<uint16_t>(cnt, uint16_t(load_le<uint16_t>(cnt) + 1));
                 acc = (acc << l) | code[e];
                 nacc += l;
                 pos += l;
@@ -674,7 +677,7 @@ dfc_status dfc_blob_info(const void *blob_v, uint64_t bytes, dfc_info *out) {
         return DFC_ECORRUPT;
     }
     if (load_le<uint32_t>(b + hdr::reserved)) return DFC_ECORRUPT;
-    for (int i = 192; i < 256; ++i)
+    for (int i = hdr::counts + 16; i < 256; ++i)
         if (b[i]) return DFC_ECORRUPT;
 
     // Code lengths: complete code under the limit (or empty for n == 0).
@@ -712,8 +715,8 @@ dfc_status dfc_blob_info(const void *blob_v, uint64_t bytes, dfc_info *out) {
     const uint64_t blob_bytes = place_sections(sz, off);
     if (blob_bytes != in.blob_bytes) return DFC_ECORRUPT;
     for (int i = 0; i < kNumSections; ++i) {
-        if (load_le<uint64_t>(b + hdr::sections + 16 * i) != off[i]) return DFC_ECORRUPT;
-        if (load_le<uint64_t>(b + hdr::sections + 16 * i + 8) != sz.bytes[i]) return DFC_ECORRUPT;
+        if (load_le<uint64_t>(b + hdr::section(i)) != off[i]) return DFC_ECORRUPT;
+        if (load_le<uint64_t>(b + hdr::section(i) + 8) != sz.bytes[i]) return DFC_ECORRUPT;
     }
     if (bytes < blob_bytes) return DFC_ESIZE;
     in.off_tables = off[kTables];
@@ -728,8 +731,10 @@ dfc_status dfc_blob_info(const void *blob_v, uint64_t bytes, dfc_info *out) {
     in.raw_bytes = sz.bytes[kRaw];
     in.off_panels = off[kPanels];
     in.panels_bytes = sz.bytes[kPanels];
+    in.off_counts = off[kCounts];
+    in.counts_bytes = sz.bytes[kCounts];
     in.coded_bytes = kHeaderBytes + sz.bytes[kWords] + sz.bytes[kOffsets] + sz.bytes[kBlockout] + sz.bytes[kRaw] +
-                     sz.bytes[kPanels];
+                     sz.bytes[kPanels] + sz.bytes[kCounts];
 
     // Panel table: chunk and block counts follow from every item's bits.
     std::vector<uint64_t> item_block;  // first block of every item (+ sentinel)
@@ -788,6 +793,30 @@ dfc_status dfc_blob_info(const void *blob_v, uint64_t bytes, dfc_info *out) {
         for (uint64_t q = 0; panel && q < g.n_items; ++q)
             if (load_le<uint32_t>(bo + 4 * item_block[q]) != g.item_elem0(q)) return DFC_ECORRUPT;
         in.max_block_elems = widest;
+    }
+    // Panel chunk counts: at most the codes one chunk can start, and every
+    // block's counts add up to its block offsets' difference, so a decoder
+    // that places codes by prefix sums of them stays inside its block.
+    if (panel) {
+        const uint8_t *pt = b + off[kPanels], *cn = b + off[kCounts], *bo = b + off[kBlockout];
+        const uint64_t max_count = mn ? ceil_div(8ull * in.chunk_bytes, mn) : 0;
+        for (uint64_t q = 0; q < g.n_items; ++q) {
+            const uint64_t c0 = load_le<uint32_t>(pt + 16 * q), c1 = load_le<uint32_t>(pt + 16 * q + 16);
+            for (uint64_t k = item_block[q]; k < item_block[q + 1]; ++k) {
+                const uint64_t lo = c0 + uint64_t(in.lanes_per_block) * (k - item_block[q]);
+                const uint64_t hi = std::min<uint64_t>(c1, lo + in.lanes_per_block);
+                uint64_t sum = 0;
+                for (uint64_t c = lo; c < hi; ++c) {
+                    const uint32_t v = load_le<uint16_t>(cn + 2 * c);
+                    if (v > max_count) return DFC_ECORRUPT;
+                    sum += v;
+                }
+                if (sum != uint64_t(load_le<uint32_t>(bo + 4 * (k + 1))) - load_le<uint32_t>(bo + 4 * k))
+                    return DFC_ECORRUPT;
+            }
+        }
+        for (uint64_t i = 2 * in.n_chunks; i < sz.bytes[kCounts]; ++i)
+            if (cn[i]) return DFC_ECORRUPT;
     }
     *out = in;
     return DFC_OK;

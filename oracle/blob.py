@@ -19,7 +19,9 @@ Header (bytes 0..255)::
     136 u64 off_blockout 144 u64 blockout_bytes
     152 u64 off_raw      160 u64 raw_bytes
     168 u64 off_panels   176 u64 panels_bytes
-    184 u64 blob_bytes   192..255 zero
+    184 u64 blob_bytes
+    192 u64 off_counts   200 u64 counts_bytes (panel layout; 0 otherwise)
+    208..255 zero
 
 Bytes 256..511 hold the code length of every exponent value (0 = unused).
 Sections follow in the order tables, words, offsets, blockout, raw, panels;
@@ -123,6 +125,7 @@ def parse_blob(blob: bytes):
     vals = struct.unpack_from("<12QQ", b, 88)
     names = ("tables", "words", "offsets", "blockout", "raw", "panels")
     sec = {nm: (vals[2 * i], vals[2 * i + 1]) for i, nm in enumerate(names)}
+    sec["counts"] = struct.unpack_from("<QQ", b, 192)
     lengths = np.frombuffer(b, dtype=np.uint8, count=256, offset=256).copy()
 
     def view(name, dtype):
@@ -136,13 +139,14 @@ def parse_blob(blob: bytes):
     offsets = st.unpack_offsets(view("offsets", "<u4"), n_chunks + 1) if five_bit else None
     out = view("blockout", "<u4")
     raw = view("raw", np.uint8)[:n]
+    counts = view("counts", "<u2")[:n_chunks] if sec["counts"][1] else None
     return {
         "n": n, "total_bits": total_bits, "n_chunks": n_chunks, "n_blocks": n_blocks,
         "chunk_bytes": chunk_bytes, "lanes": lanes, "max_len_limit": max_len,
         "lut_bits": lut_bits, "layout": layout, "panel_rows": panel_rows,
         "rows": rows, "cols": cols, "tile_k": tile_k, "sections": sec,
         "blob_bytes": vals[12], "lengths": lengths, "words": words, "off": offsets,
-        "out": out, "raw": raw,
+        "out": out, "raw": raw, "counts": counts,
     }
 
 
@@ -166,7 +170,7 @@ def coded_bytes(p) -> int:
     """Bytes a reader must store: header, code lengths, stream, offsets, block
     offsets and raw bytes.  Alignment padding is not counted."""
     s = p["sections"]
-    return HEADER_BYTES + sum(s[nm][1] for nm in ("words", "offsets", "blockout", "raw", "panels"))
+    return HEADER_BYTES + sum(s[nm][1] for nm in ("words", "offsets", "blockout", "raw", "panels", "counts"))
 
 
 def entropy_bound_bytes(hist) -> float:

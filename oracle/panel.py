@@ -23,7 +23,12 @@ layout for decoding straight into a matrix product.  The reading taken here:
   short); out[b] = index, in panel order, of the first element whose code
   starts at or after the block's first bit; out[n_blocks] = n;
 * a table of items + 1 entries (first chunk, first block, code bits of the
-  item, 0), the last entry (n_chunks, n_blocks, 0, 0).
+  item, 0), the last entry (n_chunks, n_blocks, 0, 0);
+* per chunk, the number of codes whose first bit lies in it (u16 per chunk,
+  a ``counts`` section): one more auxiliary variable of the two-phase
+  decode (DFloat11 blog, section 03 item 2), with which a decoding lane
+  learns its output position from a prefix sum of stored counts instead of
+  decoding its chunk once more to count them.
 
 Everything else (codebook, bit order, raw bytes) is the flat layout's,
 applied to the permuted sequence.
@@ -84,7 +89,7 @@ def encode_panel(bits: np.ndarray, panel_k: int = 1024, chunk_bytes: int = 16, l
     if n and (lengths[exponent] == 0).any():
         raise ValueError("an exponent has no code")
     codes = cb.canonical_codes(lengths)
-    words, offs, outs, table = [], [], [], []
+    words, offs, outs, table, counts = [], [], [], [], []
     chunk_base = block_base = elem_base = total_bits = 0
     for _, _, w in items:
         nq = PANEL_ROWS * w
@@ -95,6 +100,8 @@ def encode_panel(bits: np.ndarray, panel_k: int = 1024, chunk_bytes: int = 16, l
         wq = st.pack_words(e, lengths, codes, chunks_q * (chunk_bytes // 4))
         words.append(wq)
         offs.append(st.chunk_offsets(starts, bits_q, chunk_bytes, chunks_q)[:chunks_q])
+        counts.append(np.bincount(np.asarray(starts, dtype=np.int64) // (8 * chunk_bytes), minlength=chunks_q)
+                      if nq else np.zeros(chunks_q, dtype=np.int64))
         first = np.arange(blocks_q, dtype=np.int64) * (8 * chunk_bytes * lanes)
         outs.append(elem_base + np.searchsorted(starts, first, side="left"))
         table.append((chunk_base, block_base, bits_q, 0))
@@ -115,6 +122,7 @@ def encode_panel(bits: np.ndarray, panel_k: int = 1024, chunk_bytes: int = 16, l
         "off": np.concatenate(offs).astype(np.uint8),
         "out": np.concatenate(outs).astype(np.uint32),
         "items": np.array(table, dtype=np.uint32),
+        "counts": (np.concatenate(counts) if counts else np.zeros(0)).astype(np.uint16),
         "raw": raw,
     }
 
@@ -131,8 +139,9 @@ def write_panel_blob(enc, lut_bits: int = 11) -> bytes:
         "blockout": 4 * (enc["n_blocks"] + 1),
         "raw": 16 * (-(-n // 16)),
         "panels": 16 * (enc["n_items"] + 1),
+        "counts": 16 * (-(-2 * enc["n_chunks"] // 16)),
     }
-    names = ("tables", "words", "offsets", "blockout", "raw", "panels")
+    names = ("tables", "words", "offsets", "blockout", "raw", "panels", "counts")
     offsets = {}
     pos = bl.HEADER_BYTES
     for name in names:
@@ -146,9 +155,10 @@ def write_panel_blob(enc, lut_bits: int = 11) -> bytes:
                      enc["chunk_bytes"], enc["lanes"], enc["max_len_limit"], lut_bits,
                      LAYOUT_PANEL, PANEL_ROWS, enc["rows"], enc["cols"], enc["panel_k"], 0)
     fields = []
-    for name in names:
+    for name in names[:6]:
         fields += [offsets[name], sizes[name]]
     struct.pack_into("<12QQ", buf, 88, *fields, blob_bytes)
+    struct.pack_into("<QQ", buf, 192, offsets["counts"], sizes["counts"])
     buf[256:512] = np.asarray(enc["lengths"], dtype=np.uint8).tobytes()
 
     def put(name, data: bytes):
@@ -160,6 +170,7 @@ def write_panel_blob(enc, lut_bits: int = 11) -> bytes:
     put("blockout", np.asarray(enc["out"], dtype="<u4").tobytes())
     put("raw", np.asarray(enc["raw"], dtype=np.uint8).tobytes())
     put("panels", np.asarray(enc["items"], dtype="<u4").tobytes())
+    put("counts", np.asarray(enc["counts"], dtype="<u2").tobytes())
     return bytes(buf)
 
 
@@ -181,7 +192,10 @@ def decode_panel_blob(blob: bytes) -> np.ndarray:
         nch = c1 - c0
         words = np.concatenate([p["words"][c0 * wpc: c1 * wpc], np.zeros(st.GUARD_WORDS, dtype=np.uint32)])
         off = np.append(p["off"][c0:c1], 0)
-        exps.append(st.decode_chunked(words, off, int(bits_q), C, int(nch), p["lengths"]))
+        e, cnt = st.decode_chunked(words, off, int(bits_q), C, int(nch), p["lengths"], return_counts=True)
+        if p["counts"] is None or not np.array_equal(p["counts"][c0:c1], cnt):
+            raise ValueError("stored chunk code counts do not match the stream")
+        exps.append(e)
     exponent = np.concatenate(exps) if exps else np.zeros(0, dtype=np.uint8)
     seq = merge(exponent, p["raw"])
     out = np.empty(p["n"], dtype=np.uint16)

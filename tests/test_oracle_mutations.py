@@ -141,7 +141,8 @@ MUTANTS = [
      'outs.append(np.searchsorted(starts, first, side="left"))',
      ["test_oracle_panel.py"]),
     ("coded size leaves out the chunk offsets", "blob.py",
-     'for nm in ("words", "offsets", "blockout", "raw", "panels"))', 'for nm in ("words", "blockout", "raw", "panels"))',
+     'for nm in ("words", "offsets", "blockout", "raw", "panels", "counts"))',
+     'for nm in ("words", "blockout", "raw", "panels", "counts"))',
      ["test_oracle_blob.py", "test_oracle_stream.py"]),
     ("rANS frequencies without the floor of one", "ans.py",
      "f[s] = max(1, h[s] * m // total)", "f[s] = h[s] * m // total",
@@ -155,6 +156,14 @@ MUTANTS = [
     ("vectorised rANS encoder keeps a step's words in ascending lane order", "ans.py",
      "out.append((x[emit] & np.uint64(0xFFFF))[::-1])", "out.append(x[emit] & np.uint64(0xFFFF))",
      ["test_oracle_ans.py"]),
+    ("panel chunk counts take a code ending a chunk for one starting there", "panel.py",
+     "np.bincount(np.asarray(starts, dtype=np.int64) // (8 * chunk_bytes), minlength=chunks_q)",
+     "np.bincount((np.asarray(starts, dtype=np.int64) + 1) // (8 * chunk_bytes), minlength=chunks_q)",
+     ["test_oracle_panel.py"]),
+    ("coded size leaves out the chunk counts", "blob.py",
+     'for nm in ("words", "offsets", "blockout", "raw", "panels", "counts"))',
+     'for nm in ("words", "offsets", "blockout", "raw", "panels"))',
+     ["test_oracle_panel.py"]),
     ("panel sub-tiles eight columns wide", "panel.py",
      "c = c0 + SUBTILE_K * t + 8 * (l // 32) + j", "c = c0 + 8 * t + 8 * (l // 32) + j",
      ["test_oracle_panel.py"]),

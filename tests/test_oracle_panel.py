@@ -6,6 +6,7 @@ import numpy as np
 import pytest
 
 from lossless_entropy_coded_dfc_amd import synth
+from oracle import blob as bl
 from oracle import codebook as cb
 from oracle import fields
 from oracle import panel as pn
@@ -111,11 +112,39 @@ def test_item_metadata_recount():
             later = starts[starts >= 8 * C * c]
             first = later[0] if later.size else bits
             assert enc["off"][c0 + c] == first - 8 * C * c
+            # codes whose first bit lies in chunk c
+            assert enc["counts"][c0 + c] == np.count_nonzero((starts >= 8 * C * c) & (starts < 8 * C * (c + 1)))
         for b in range(table[q + 1, 1] - b0):
             assert enc["out"][b0 + b] == elem0 + np.count_nonzero(starts < 8 * C * T * b)
         elem0 += nq
     assert table[-1, 0] == enc["n_chunks"] and table[-1, 1] == enc["n_blocks"]
     assert enc["out"][-1] == x.size
+    assert enc["counts"].dtype == np.uint16 and enc["counts"].size == enc["n_chunks"]
+    assert int(enc["counts"].sum()) == x.size
+
+
+def test_counts_section_in_the_container():
+    """The counts section sits after the item table, in header slot 192,
+    two bytes per chunk rounded up to 16; a wrong stored count is refused
+    by the oracle's decoder, which recounts every chunk."""
+    x = synth.gaussian((64, 160), 0.02, (64,))
+    enc = pn.encode_panel(x, panel_k=48, chunk_bytes=8)
+    blob = bytearray(pn.write_panel_blob(enc, 11))
+    p = bl.parse_blob(bytes(blob))
+    off, size = p["sections"]["counts"]
+    assert size == 16 * -(-2 * enc["n_chunks"] // 16)
+    assert off % 256 == 0 and off >= p["sections"]["panels"][0] + p["sections"]["panels"][1]
+    assert p["blob_bytes"] >= off + size
+    assert np.array_equal(p["counts"], enc["counts"])
+    assert bl.coded_bytes(p) == 512 + sum(p["sections"][k][1] for k in
+                                           ("words", "offsets", "blockout", "raw", "panels", "counts"))
+    c = int(np.flatnonzero(enc["counts"])[3])
+    blob[off + 2 * c] ^= 1
+    with pytest.raises(ValueError, match="counts"):
+        pn.decode_panel_blob(bytes(blob))
+    # the flat layout has no counts section
+    flat = bl.write_blob(st.encode(x, 8, 64), 11)
+    assert bl.parse_blob(flat)["sections"]["counts"] == (0, 0) and bl.parse_blob(flat)["counts"] is None
 
 
 def test_every_item_decodes_alone():
