@@ -6,12 +6,18 @@ does that for a stack of layers: while the caller's stream computes with layer
 i, the matrices of layer i + 1 decode on a side stream into the other of two
 reused scratch sets, so at most two layers are ever held decompressed.
 
-Ordering uses HIP events only: ``weights(i)`` makes the caller's stream wait
-for layer i's decode, and ``release(i)`` marks the point after which its
-scratch set may be overwritten by the decode of layer i + 2.  The calls must
-come in that order for every layer (prefetch, weights, release); a prefetch
-into a set whose layer has not been released, or weights of a layer that is
-not in its set, raises instead of racing.
+Ordering uses HIP stream waits and events only: every ``prefetch(i)`` first
+makes the side stream wait for the caller's stream as it stands (so a
+container written, or memory freed and reused, earlier on the caller's stream
+is settled before the decode reads or writes it), ``weights(i)`` makes the
+caller's stream wait for layer i's decode, and ``release(i)`` marks the point
+after which its scratch set may be overwritten by the decode of layer i + 2.
+The calls must come in that order for every layer (prefetch, weights,
+release); a prefetch into a set whose layer has not been released, or weights
+of a layer that is not in its set, raises instead of racing.  ``close()``
+waits for the side stream and drops the scratch sets; the scratch tensors are
+also marked as used by the side stream, so the caching allocator does not
+hand their memory out while a decode into them is pending.
 """
 from __future__ import annotations
 
@@ -44,14 +50,23 @@ class DecodeAhead:
         self.free_recorded = [False, False]
         self.held = [None, None]  # layer decoded (or decoding) into each set, until released
         self.status = torch.zeros(1, dtype=torch.int32, device=device)
+        for t in [self.status] + [t for s in self.scratch for t in s]:
+            t.record_stream(self.side)
+        # the scratch and status allocations (and the zero fill) were ordered
+        # on the caller's stream
+        self.side.wait_stream(torch.cuda.current_stream())
 
     def prefetch(self, i: int):
-        """Enqueue the decode of layer i on the side stream."""
+        """Enqueue the decode of layer i on the side stream, after everything
+        the caller's stream holds so far."""
+        if self.scratch is None:
+            raise RuntimeError("DecodeAhead is closed")
         slot = i % 2
         if self.held[slot] is not None:
             raise RuntimeError(f"layer {self.held[slot]} still holds scratch set {slot}: release it before "
                                f"prefetching layer {i}")
         self.held[slot] = i
+        self.side.wait_stream(self.torch.cuda.current_stream())
         with self.torch.cuda.stream(self.side):
             if self.free_recorded[slot]:
                 self.side.wait_event(self.free[slot])
@@ -65,6 +80,8 @@ class DecodeAhead:
         """bf16 views of layer i's matrices; the current stream waits for
         their decode."""
         slot = i % 2
+        if self.scratch is None:
+            raise RuntimeError("DecodeAhead is closed")
         if self.held[slot] != i:
             raise RuntimeError(f"layer {i} is not in scratch set {slot} (prefetch it first)")
         self.torch.cuda.current_stream().wait_event(self.ready[slot])
@@ -79,6 +96,20 @@ class DecodeAhead:
         self.free[slot].record(self.torch.cuda.current_stream())
         self.free_recorded[slot] = True
         self.held[slot] = None
+
+    def close(self):
+        """Waits for the side stream's decodes and drops the scratch sets."""
+        if self.scratch is not None:
+            self.side.synchronize()
+            self.scratch = None
+            self.held = [None, None]
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+        return False
 
     def corrupt_blocks_seen(self) -> bool:
         """True if any decode so far met a block that failed its check (the

@@ -336,22 +336,23 @@ __device__ __forceinline__ void write_codes_padded(const Chunk<C> &ck, int end, 
     }
 }
 
-// 8 bf16 values from 8 staged (rotated) exponents and 8 raw bytes.  Per
-// pair of values, x1 = [raw_a, exp_a, raw_b, exp_b] and x2 = [exp_a, raw_a,
-// exp_b, raw_b] (bytes, low first); each output byte keeps bits 6..0 of x1
-// and bit 7 of x2.
+// 8 bf16 values from 8 staged (rotated) exponents and 8 raw bytes.  A
+// staged byte holds exponent bits 0 | 7..1 (bit 7 = the exponent's lowest
+// bit), a raw byte sign | mantissa: a value's low byte is bit 7 of the one
+// and bits 6..0 of the other, its high byte the other way round.  Per 4
+// values, two bit-field selects make the 4 low and the 4 high bytes and two
+// byte permutes interleave them.
 __device__ __forceinline__ u32x4 assemble8(const u32x2 &E, const u32x2 &R) {
     const uint32_t e[2] = {E.x, E.y};
     const uint32_t r[2] = {R.x, R.y};
+    constexpr uint32_t kTop = 0x80808080u;
     uint32_t o[4];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-        const uint32_t a1 = __builtin_amdgcn_perm(e[q], r[q], 0x05010400u);
-        const uint32_t a2 = __builtin_amdgcn_perm(e[q], r[q], 0x01050004u);
-        const uint32_t b1 = __builtin_amdgcn_perm(e[q], r[q], 0x07030602u);
-        const uint32_t b2 = __builtin_amdgcn_perm(e[q], r[q], 0x03070206u);
-        o[2 * q] = (a1 & 0x7F7F7F7Fu) | (a2 & 0x80808080u);
-        o[2 * q + 1] = (b1 & 0x7F7F7F7Fu) | (b2 & 0x80808080u);
+        const uint32_t lo = (e[q] & kTop) | (r[q] & ~kTop);
+        const uint32_t hi = (r[q] & kTop) | (e[q] & ~kTop);
+        o[2 * q] = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+        o[2 * q + 1] = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
     }
     return u32x4{o[0], o[1], o[2], o[3]};
 }

@@ -128,12 +128,21 @@ __device__ __forceinline__ bool gemm_items(const GemmArgs &g, uint32_t q0, uint3
         // only begins is carried as exponents, and the next block loads its
         // raw bytes
         const uint32_t rounds = (lead + total_want) >> 9;
+        const uint32_t kcol = cur.col0 + 16u * (base >> 9);
         u32x2 R[PF];
 #pragma unroll
         for (int j = 0; j < PF; ++j)
             R[j] = uint32_t(j) < rounds
                        ? __builtin_amdgcn_raw_buffer_load_b64(raw, cur.e0 + base + 512u * j + 8u * lane, 0, 0)
                        : u32x2{0u, 0u};
+        // With one column tile, the X fragments of those sub-tiles too: their
+        // cache round trips then overlap the decoding instead of each product.
+        u32x4 XP[NT == 1 ? PF : 1];
+#pragma unroll
+        for (int j = 0; j < (NT == 1 ? PF : 0); ++j)
+            XP[j] = uint32_t(j) < rounds
+                        ? __builtin_amdgcn_raw_buffer_load_b128(xr, xcol + 2u * (kcol + 16u * j), 0, 0)
+                        : u32x4{0u, 0u, 0u, 0u};
         // the next block: this item's next, or the first of the next item
         const bool same = b + 1u < cur.b1;
         const bool more = same || cur.q + qstep < qend;
@@ -173,6 +182,7 @@ __device__ __forceinline__ bool gemm_items(const GemmArgs &g, uint32_t q0, uint3
         if (!bad && cnt) got = write_codes<C>(ck, start, end, lds, stage_off + lead + (incl - cnt), t);
         miss |= (got != cnt) | ((start < end) & (cnt == 0));
         wait_for(R);
+        if constexpr (NT == 1) wait_for(XP);
         wait_for(nxt);
         wait_for(stored_nxt);
         if (bad) {
@@ -185,12 +195,11 @@ __device__ __forceinline__ bool gemm_items(const GemmArgs &g, uint32_t q0, uint3
 
         __builtin_amdgcn_s_setprio(0);
         // Complete sub-tiles: W operand from the staged exponents and the
-        // raw bytes, X operand from global memory (cached); the X fragments of
-        // all column tiles are requested before their products, so that their
-        // cache round trips overlap.
+        // raw bytes, X operand from global memory (cached); with several
+        // column tiles, their X fragments are requested before their
+        // products, so that their cache round trips overlap.
         const uint32_t extent = lead + total;
         const uint32_t nfull = extent >> 9;
-        const uint32_t kcol = cur.col0 + 16u * (base >> 9);
 #pragma unroll
         for (int j = 0; j < PF; ++j) {
             if (uint32_t(j) < nfull) {
@@ -198,8 +207,13 @@ __device__ __forceinline__ bool gemm_items(const GemmArgs &g, uint32_t q0, uint3
                 const bf16x8 A = as_bf16x8(assemble8(E, R[j]));
                 u32x4 X[NT];
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt)
-                    X[nt] = __builtin_amdgcn_raw_buffer_load_b128(xr, xcol + 2u * (32u * nt * g.cols + kcol + 16u * j), 0, 0);
+                for (int nt = 0; nt < NT; ++nt) {
+                    if constexpr (NT == 1)
+                        X[nt] = XP[j];
+                    else
+                        X[nt] = __builtin_amdgcn_raw_buffer_load_b128(xr, xcol + 2u * (32u * nt * g.cols + kcol + 16u * j),
+                                                                      0, 0);
+                }
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt)
                     acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, as_bf16x8(X[nt]), acc[nt], 0, 0, 0);
@@ -238,6 +252,16 @@ __device__ __forceinline__ bool gemm_items(const GemmArgs &g, uint32_t q0, uint3
         return false;
     }
     return true;
+}
+
+// Value r of lane L of a 32 x 32 accumulator tile goes to float4 slot
+// 64 (r / 4) + L, element r % 4, of a wavefront's tile in LDS (see the
+// reduction below for the rows and columns a slot holds).
+__device__ __forceinline__ void put_tile(uint8_t *stage, uint32_t lane, const f32x16 &a) {
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4)
+        *reinterpret_cast<float4 *>(stage + 16u * (64u * r4 + lane)) =
+            make_float4(a[4 * r4], a[4 * r4 + 1], a[4 * r4 + 2], a[4 * r4 + 3]);
 }
 
 // Workgroup of group x wpp wavefronts.  A round takes `group` consecutive
@@ -290,10 +314,7 @@ __global__ __launch_bounds__(512) void dfc_gemm_kernel(const GemmArgs g) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             if (nt > 0) __syncthreads();  // the previous tile has been read
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4)
-                *reinterpret_cast<float4 *>(stage + 16u * (64u * r4 + lane)) =
-                    make_float4(acc[nt][4 * r4], acc[nt][4 * r4 + 1], acc[nt][4 * r4 + 2], acc[nt][4 * r4 + 3]);
+            put_tile(stage, lane, acc[nt]);
             __syncthreads();
             for (uint32_t e = sw * kWave + lane; e < 256u; e += wpp * kWave) {
                 const uint8_t *slot = lds + g.tables_bytes + pw * wpp * g.stage_bytes + 16u * e;

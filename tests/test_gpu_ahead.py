@@ -111,3 +111,28 @@ def test_out_of_order_use_raises():
     assert torch.equal(w0, torch.from_numpy(originals[0][0].view(np.int16)).cuda())
     assert torch.equal(w2, torch.from_numpy(originals[2][0].view(np.int16)).cuda())
     assert not dec.corrupt_blocks_seen()
+
+
+def test_prefetch_waits_for_the_callers_stream():
+    """A container written on the caller's stream right before prefetch (the
+    copy queued behind a few large products) is what the side stream
+    decodes: prefetch orders the side stream after the caller's work."""
+    from lossless_entropy_coded_dfc_amd.ahead import DecodeAhead
+    x = synth.gaussian_with_outliers((512, 1024), 0.02, (92,))
+    blob = dfc.encode(x, chunk_bytes=16)
+    info = dfc.blob_info(blob)
+    host = torch.from_numpy(blob).pin_memory()
+    dev = torch.zeros(host.numel(), dtype=torch.uint8, device="cuda")
+    with DecodeAhead([[(dev, info, (512, 1024))]]) as dec:
+        a = torch.ones((4096, 4096), dtype=torch.bfloat16, device="cuda")
+        for _ in range(8):
+            a = (a @ a) * (1.0 / 4096)
+        dev.copy_(host, non_blocking=True)
+        say("case decode-ahead after a producer on the caller's stream")
+        dec.prefetch(0)
+        got = dec.weights(0)[0].view(torch.int16).clone()
+        dec.release(0)
+        assert torch.equal(got, torch.from_numpy(x.view(np.int16)).cuda())
+        assert not dec.corrupt_blocks_seen()
+    with pytest.raises(RuntimeError):
+        dec.prefetch(0)          # closed
