@@ -252,14 +252,29 @@ enum { DFC_GEMM_MAX_BATCH = 64 };
  * slices per panel and too few 32-row panels to occupy the GPU has each
  * panel shared by several workgroups, whose sums are added into Y (zeroed
  * first, on the stream) with fp32 atomics; with three or more per panel the
- * last bits of Y may then differ between runs.  status_dev: as in dfc_decode (nonzero if a
- * block's decoded count disagrees with its block offsets; Y is then
- * unspecified).  Errors before launch: DFC_EINVAL (null or
- * misaligned pointers, batch out of range, bad decode parameters),
- * DFC_EUNSUPPORTED (not a panel-layout container, lanes_per_block != 64,
- * streams or Y past 4 GiB), DFC_EHIP (launch failure). */
+ * last bits of Y may then differ between runs.
+ * workspace_dev: NULL, or workspace_bytes >= dfc_gemm_workspace_bytes(B, K)
+ * bytes of device memory (16-byte aligned) that nothing else touches until
+ * this call's work has run on the stream.  With it, a batch above 32 first
+ * copies X there in the order the matrix instructions read it (one 1 KB run
+ * per 16 columns and 32 vectors), and the products read X from the copy;
+ * without it, they gather each operand from X in place (32-byte pieces of
+ * 32 vectors), which is slower.  Batches up to 32 never use it.
+ * status_dev: as in dfc_decode (nonzero if a block's stored chunk counts
+ * disagree with its block offsets or with the codes in its chunks; Y is then
+ * unspecified).  Errors before launch: DFC_EINVAL (null or misaligned
+ * pointers, batch out of range, bad decode parameters), DFC_ESIZE (a
+ * workspace smaller than needed), DFC_EUNSUPPORTED (not a panel-layout
+ * container, lanes_per_block != 64, streams or Y past 4 GiB), DFC_EHIP
+ * (launch failure). */
 dfc_status dfc_decode_gemm(const void *w_blob_dev, const dfc_info *info, const void *tables_dev, const uint16_t *x_dev,
-                           uint32_t batch, float *y_dev, uint32_t *status_dev, void *stream);
+                           uint32_t batch, float *y_dev, void *workspace_dev, uint64_t workspace_bytes,
+                           uint32_t *status_dev, void *stream);
+
+/* Device bytes of the workspace dfc_decode_gemm can use for B vectors of K
+ * values: 0 for B <= 32, else 2 x 64 x K rounded up to 16-column steps (X in
+ * operand order, two tiles of 32 vectors).  Host. */
+uint64_t dfc_gemm_workspace_bytes(uint32_t batch, uint64_t cols);
 
 /* Workspace bytes dfc_encode_device needs for n elements.  Host. */
 dfc_status dfc_encode_device_workspace(uint64_t n, uint64_t *bytes);

@@ -125,8 +125,11 @@ def library():
                                      ctypes.c_void_p]
     lib.dfc_decode_batch.restype = st
     lib.dfc_decode_gemm.argtypes = [ctypes.c_void_p, ctypes.POINTER(Info), ctypes.c_void_p, ctypes.c_void_p,
-                                    ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+                                    ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64,
+                                    ctypes.c_void_p, ctypes.c_void_p]
     lib.dfc_decode_gemm.restype = st
+    lib.dfc_gemm_workspace_bytes.argtypes = [ctypes.c_uint32, ctypes.c_uint64]
+    lib.dfc_gemm_workspace_bytes.restype = ctypes.c_uint64
     lib.dfc_encode_device_workspace.argtypes = [ctypes.c_uint64, u64p]
     lib.dfc_encode_device_workspace.restype = st
     lib.dfc_histogram_device.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
@@ -366,11 +369,20 @@ def encode_device(src, chunk_bytes: int = 0, lanes: int = 64, max_code_len: int 
 GEMM_MAX_BATCH = 64
 
 
-def decode_gemm(blob_dev, info: Info, x, y, status=None, stream=None, tables=None):
+def gemm_workspace_bytes(batch: int, cols: int) -> int:
+    """Device bytes of the workspace decode_gemm uses for B vectors of K values
+    (0 for B <= 32)."""
+    return int(library().dfc_gemm_workspace_bytes(batch, cols))
+
+
+def decode_gemm(blob_dev, info: Info, x, y, status=None, stream=None, tables=None, workspace=None):
     """Fused decode + product: y[b, :] = W @ x[b, :] for a panel-layout
     container of W (M x K).  x: contiguous 16-bit device tensor of shape
     (B, K) (bf16 bits); y: contiguous float32 device tensor of shape (B, M);
-    tables: as in ``decode``."""
+    tables: as in ``decode``; workspace: None or a device uint8 tensor of at
+    least gemm_workspace_bytes(B, K) bytes that nothing else uses until the
+    call's work has run (for B > 32 one is allocated on the device of x when
+    none is given; pass False to read X in place)."""
     if info.layout != LAYOUT_PANEL:
         raise ValueError("decode_gemm needs a panel-layout container")
     if x.dim() != 2 or y.dim() != 2 or not x.is_contiguous() or not y.is_contiguous():
@@ -379,8 +391,20 @@ def decode_gemm(blob_dev, info: Info, x, y, status=None, stream=None, tables=Non
     import torch
     if x.element_size() != 2 or K != info.cols or tuple(y.shape) != (B, info.rows) or y.dtype != torch.float32:
         raise ValueError("x must be (B, K) 16-bit and y (B, M) float32 for the container's M x K")
+    need = gemm_workspace_bytes(B, K)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        if stream is not None:
+            # the caching allocator must not hand this memory out before the
+            # call's work on that stream has run
+            workspace.record_stream(torch.cuda.ExternalStream(int(stream), device=x.device))
+    if workspace is False or workspace is None:
+        ws_ptr, ws_bytes = 0, 0
+    else:
+        ws_ptr, ws_bytes = _dev_ptr(workspace), workspace.numel() * workspace.element_size()
     _check(library().dfc_decode_gemm(ctypes.c_void_p(_blob_ptr(blob_dev, info)), ctypes.byref(info),
-                                     ctypes.c_void_p(_tables_ptr(tables, info)), ctypes.c_void_p(_dev_ptr(x)), B, ctypes.c_void_p(_dev_ptr(y)),
+                                     ctypes.c_void_p(_tables_ptr(tables, info)), ctypes.c_void_p(_dev_ptr(x)), B,
+                                     ctypes.c_void_p(_dev_ptr(y)), ctypes.c_void_p(ws_ptr), ws_bytes,
                                      ctypes.c_void_p(_status_ptr(status)), _stream(stream)), "dfc_decode_gemm")
 
 

@@ -49,6 +49,8 @@ struct GemmArgs {
     const uint8_t *lengths;    // the 256 code lengths (container bytes 256..511)
     const uint8_t *tables;     // tables from dfc_derive_tables, or null: derive them here
     const uint16_t *x;         // B vectors of K bf16: x[b K + k]
+    void *xp;                  // X in operand order (pack_x_kernel), or null
+    uint32_t xp_bytes;
     float *y;                  // B vectors of M fp32: y[b M + m]
     uint32_t words_bytes, offw_bytes, raw_bytes, x_bytes, y_bytes, counts_bytes;
     uint32_t n_panels, slices, panel_k, cols, rows, batch;
@@ -90,6 +92,30 @@ __device__ __forceinline__ ItemPos item_pos(const GemmArgs &g, uint32_t q) {
     return it;
 }
 
+// The B operand of column tile nt for the sub-tile at column k: lane L
+// holds X[32 nt + L % 32][k + 8 (L / 32) .. + 8].  In place (x[b K + k],
+// rows past B read as zeros), that is 32 pieces of 32 bytes, one per vector;
+// from the packed copy (pack_x_kernel), one run of 1 KB.
+template <int NT, bool XPACK>
+__device__ __forceinline__ u32x4 load_x(const __amdgpu_buffer_rsrc_t &xr, uint32_t xcol, uint32_t cols, uint32_t k,
+                                        int nt, uint32_t lane) {
+    if constexpr (XPACK)
+        return __builtin_amdgcn_raw_buffer_load_b128(xr, (((k >> 4) * NT + uint32_t(nt)) * 64u + lane) * 16u, 0, 0);
+    else
+        return __builtin_amdgcn_raw_buffer_load_b128(xr, xcol + 2u * (32u * uint32_t(nt) * cols + k), 0, 0);
+}
+
+// X copied in the order load_x reads it: 16-byte unit ((k / 16) NT + nt)
+// 64 + L holds X[32 nt + L % 32][k + 8 (L / 32) .. + 8] (zeros past B).
+__global__ void pack_x_kernel(const uint16_t *x, uint32_t batch, uint32_t cols, uint32_t nt_count, uint4 *xp,
+                              uint32_t units) {
+    for (uint32_t u = blockIdx.x * blockDim.x + threadIdx.x; u < units; u += gridDim.x * blockDim.x) {
+        const uint32_t lane = u % 64u, nt = (u / 64u) % nt_count, kt = u / (64u * nt_count);
+        const uint32_t n = 32u * nt + lane % 32u, k = 16u * kt + 8u * (lane / 32u);
+        xp[u] = n < batch ? *reinterpret_cast<const uint4 *>(x + uint64_t(n) * cols + k) : make_uint4(0, 0, 0, 0);
+    }
+}
+
 // The blocks of a wavefront's items (q0, q0 + qstep, ... below qend), one
 // after another: each complete sub-tile is multiplied into acc.  The next
 // block's stream words, chunk offsets, chunk counts and output range (in the
@@ -100,7 +126,7 @@ __device__ __forceinline__ ItemPos item_pos(const GemmArgs &g, uint32_t q) {
 // sum), or if a chunk held a different number of codes than stored (noted
 // per lane and reported after the last block, which keeps the write pass's
 // result off the critical path of the loop).
-template <int C, int NT>
+template <int C, int NT, bool XPACK>
 __device__ __forceinline__ bool gemm_items(const GemmArgs &g, uint32_t q0, uint32_t qstep, uint32_t qend,
                                            const Tables &t, uint8_t *stage, uint32_t stage_off, uint32_t lane,
                                            const __amdgpu_buffer_rsrc_t &words, const __amdgpu_buffer_rsrc_t &offw,
@@ -211,8 +237,7 @@ __device__ __forceinline__ bool gemm_items(const GemmArgs &g, uint32_t q0, uint3
                     if constexpr (NT == 1)
                         X[nt] = XP[j];
                     else
-                        X[nt] = __builtin_amdgcn_raw_buffer_load_b128(xr, xcol + 2u * (32u * nt * g.cols + kcol + 16u * j),
-                                                                      0, 0);
+                        X[nt] = load_x<NT, XPACK>(xr, xcol, g.cols, kcol + 16u * j, nt, lane);
                 }
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt)
@@ -226,7 +251,7 @@ __device__ __forceinline__ bool gemm_items(const GemmArgs &g, uint32_t q0, uint3
             u32x4 X[NT];
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
-                X[nt] = __builtin_amdgcn_raw_buffer_load_b128(xr, xcol + 2u * (32u * nt * g.cols + kcol + 16u * j), 0, 0);
+                X[nt] = load_x<NT, XPACK>(xr, xcol, g.cols, kcol + 16u * j, nt, lane);
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
                 acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, as_bf16x8(X[nt]), acc[nt], 0, 0, 0);
@@ -270,7 +295,7 @@ __device__ __forceinline__ void put_tile(uint8_t *stage, uint32_t lane, const f3
 // wavefront v of the panel takes slices v, v + split wpp, ...  Every staging
 // area holds at least 4 KB, which the reduction reuses for one 32 x 32 fp32
 // tile per wavefront.
-template <int C, int NT>
+template <int C, int NT, bool XPACK>
 __global__ __launch_bounds__(512) void dfc_gemm_kernel(const GemmArgs g) {
     extern __shared__ __align__(16) uint8_t lds[];
     load_or_derive_tables(lds, g.tables, g.tables_bytes, g.lengths, g.lut_bits);
@@ -290,7 +315,8 @@ __global__ __launch_bounds__(512) void dfc_gemm_kernel(const GemmArgs g) {
     const __amdgpu_buffer_rsrc_t cr =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(g.counts), 0, int(g.counts_bytes), kBufferConfig);
     const __amdgpu_buffer_rsrc_t xr =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(g.x), 0, int(g.x_bytes), kBufferConfig);
+        XPACK ? __builtin_amdgcn_make_buffer_rsrc(g.xp, 0, int(g.xp_bytes), kBufferConfig)
+              : __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(g.x), 0, int(g.x_bytes), kBufferConfig);
     const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(g.y, 0, int(g.y_bytes), kBufferConfig);
     // B operand rows of this lane: column n = 32 nt + lane % 32 of X, k offset
     // 8 (lane / 32) inside the sub-tile (rows past B load zeros).
@@ -305,7 +331,7 @@ __global__ __launch_bounds__(512) void dfc_gemm_kernel(const GemmArgs g) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x16{};
         if (p < g.n_panels)
-            gemm_items<C, NT>(g, p * g.slices + part * wpp + sw, stride, (p + 1) * g.slices, t, stage, stage_off, lane,
+            gemm_items<C, NT, XPACK>(g, p * g.slices + part * wpp + sw, stride, (p + 1) * g.slices, t, stage, stage_off, lane,
                               words, offw, raw, cr, xr, xcol, acc);
         // D[i][j] of a 32x32 tile: i = 8 (r / 4) + 4 (lane / 32) + r % 4,
         // j = lane % 32.  Value r of lane L goes to slot 4 (64 (r / 4) + L) +
@@ -350,7 +376,7 @@ __global__ void fill_zero_kernel(float *y, uint64_t n) {
         y[i] = 0.0f;
 }
 
-template <int C, int NT>
+template <int C, int NT, bool XPACK>
 dfc_status launch_gemm(const GemmArgs &proto, uint32_t max_block, hipStream_t stream) {
     GemmArgs g = proto;
     // staging: a carried partial sub-tile (< 512) + the block + spill, rounded
@@ -362,7 +388,7 @@ dfc_status launch_gemm(const GemmArgs &proto, uint32_t max_block, hipStream_t st
     const uint32_t stage = std::max(4096u, (511u + max_block + 8u * C + 48u + 15u) & ~15u);
     g.stage_bytes = stage;
     g.max_block = max_block;
-    if (!allow_full_lds(reinterpret_cast<const void *>(&dfc_gemm_kernel<C, NT>))) return DFC_EHIP;
+    if (!allow_full_lds(reinterpret_cast<const void *>(&dfc_gemm_kernel<C, NT, XPACK>))) return DFC_EHIP;
     // about 8 wavefronts per workgroup: up to 8 per panel (one slice each
     // when the panel has 8 slices or fewer), several panels when it has few
     uint32_t wpp = std::min<uint32_t>(g.slices, 8u);
@@ -383,7 +409,7 @@ dfc_status launch_gemm(const GemmArgs &proto, uint32_t max_block, hipStream_t st
     // `split` workgroups, with as few slices per wavefront as the resident
     // count allows, spread evenly.
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(&dfc_gemm_kernel<C, NT>),
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(&dfc_gemm_kernel<C, NT, XPACK>),
                                                      int(waves * kWave), lds) != hipSuccess ||
         per_cu < 1)
         per_cu = 1;
@@ -405,25 +431,37 @@ dfc_status launch_gemm(const GemmArgs &proto, uint32_t max_block, hipStream_t st
     const uint32_t grid = g.rounds;
     if (split > 1)
         hipLaunchKernelGGL(fill_zero_kernel, dim3(256), dim3(256), 0, stream, g.y, uint64_t(g.batch) * g.rows);
-    hipLaunchKernelGGL((dfc_gemm_kernel<C, NT>), dim3(grid), dim3(waves * kWave), lds, stream, g);
+    if constexpr (XPACK) {
+        const uint32_t units = g.xp_bytes / 16u;
+        hipLaunchKernelGGL(pack_x_kernel, dim3(std::min<uint32_t>(1024u, (units + 255u) / 256u)), dim3(256), 0, stream,
+                           g.x, g.batch, g.cols, uint32_t(NT), static_cast<uint4 *>(g.xp), units);
+    }
+    hipLaunchKernelGGL((dfc_gemm_kernel<C, NT, XPACK>), dim3(grid), dim3(waves * kWave), lds, stream, g);
     return hipGetLastError() == hipSuccess ? DFC_OK : DFC_EHIP;
 }
 
 template <int C>
 dfc_status launch_gemm_c(const GemmArgs &g, uint32_t max_block, hipStream_t stream) {
-    return g.batch <= 32 ? launch_gemm<C, 1>(g, max_block, stream) : launch_gemm<C, 2>(g, max_block, stream);
+    if (g.batch <= 32) return launch_gemm<C, 1, false>(g, max_block, stream);
+    return g.xp ? launch_gemm<C, 2, true>(g, max_block, stream) : launch_gemm<C, 2, false>(g, max_block, stream);
 }
 
 }  // namespace
 
 extern "C" {
 
+uint64_t dfc_gemm_workspace_bytes(uint32_t batch, uint64_t cols) {
+    return batch > 32 ? 2ull * 64ull * dfc::ceil_div(cols, 16) * 16ull : 0ull;
+}
+
 dfc_status dfc_decode_gemm(const void *w_blob_dev, const dfc_info *info, const void *tables_dev, const uint16_t *x_dev,
-                           uint32_t batch, float *y_dev, uint32_t *status_dev, void *stream) {
+                           uint32_t batch, float *y_dev, void *workspace_dev, uint64_t workspace_bytes,
+                           uint32_t *status_dev, void *stream) {
     if (!info || !w_blob_dev || !x_dev || !y_dev) return DFC_EINVAL;
     if (batch < 1 || batch > DFC_GEMM_MAX_BATCH) return DFC_EINVAL;
     if ((reinterpret_cast<uintptr_t>(w_blob_dev) & 255u) || (reinterpret_cast<uintptr_t>(x_dev) & 15u) ||
-        (reinterpret_cast<uintptr_t>(y_dev) & 3u) || (reinterpret_cast<uintptr_t>(tables_dev) & 15u))
+        (reinterpret_cast<uintptr_t>(y_dev) & 3u) || (reinterpret_cast<uintptr_t>(tables_dev) & 15u) ||
+        (reinterpret_cast<uintptr_t>(workspace_dev) & 15u))
         return DFC_EINVAL;
     const dfc_info &in = *info;
     if (in.layout != DFC_LAYOUT_PANEL || in.panel_rows != dfc::kPanelRows || in.lanes_per_block != 64)
@@ -463,6 +501,12 @@ dfc_status dfc_decode_gemm(const void *w_blob_dev, const dfc_info *info, const v
     g.rows = uint32_t(in.rows);
     g.batch = batch;
     g.tables_bytes = uint32_t(dfc::tables_bytes(in.lut_bits));
+    const uint64_t ws = dfc_gemm_workspace_bytes(batch, in.cols);
+    if (workspace_dev && ws) {
+        if (workspace_bytes < ws) return DFC_ESIZE;
+        g.xp = workspace_dev;
+        g.xp_bytes = uint32_t(ws);
+    }
     g.lut_bits = in.lut_bits;
     g.status = status_dev;
     hipStream_t st = static_cast<hipStream_t>(stream);

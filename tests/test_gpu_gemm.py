@@ -192,6 +192,51 @@ def test_invalid_arguments():
         dfc.decode_gemm(torch.from_numpy(flat).cuda(), finfo, x[:4], y[:4])
 
 
+@pytest.mark.parametrize("B", [33, 47, 64])
+def test_packed_x_same_bits_as_in_place(B):
+    """Batches above 32 read X through the packed copy in the workspace (the
+    default) or in place (workspace=False): the same products in the same
+    order, so the same bits; both against the oracle."""
+    M, K = 160, 1040
+    w = synth.gaussian_with_outliers((M, K), 0.02, (95, B))
+    x = synth.gaussian((B, K), 1.0, (96, B))
+    dev, info, _ = upload(w, C=16, panel_k=256)
+    xd = torch.from_numpy(x.view(np.int16)).cuda()
+    ys = []
+    for ws in (None, False, torch.empty(dfc.gemm_workspace_bytes(B, K) + 64, dtype=torch.uint8, device="cuda")):
+        y = torch.full((B, M), float("nan"), dtype=torch.float32, device="cuda")
+        status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        dfc.decode_gemm(dev, info, xd, y, status, workspace=ws)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0
+        ys.append(y.cpu().numpy())
+    say("case packed X B", B)
+    check_product(w, x, ys[0])
+    assert np.array_equal(ys[0].view(np.uint32), ys[1].view(np.uint32))
+    assert np.array_equal(ys[0].view(np.uint32), ys[2].view(np.uint32))
+
+
+def test_workspace_arguments():
+    assert dfc.gemm_workspace_bytes(32, 8192) == 0
+    assert dfc.gemm_workspace_bytes(33, 8192) == 2 * 64 * 8192
+    assert dfc.gemm_workspace_bytes(64, 1040) == 2 * 64 * 1040
+    w = synth.gaussian((64, 128), 0.02, (97,))
+    dev, info, _ = upload(w)
+    x = torch.zeros((40, 128), dtype=torch.int16, device="cuda")
+    y = torch.zeros((40, 64), dtype=torch.float32, device="cuda")
+    small = torch.empty(dfc.gemm_workspace_bytes(40, 128) - 16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(dfc.DfcError) as ei:
+        dfc.decode_gemm(dev, info, x, y, workspace=small)
+    assert ei.value.status == dfc.ESIZE
+    odd = torch.empty(dfc.gemm_workspace_bytes(40, 128) + 32, dtype=torch.uint8, device="cuda")[8:]
+    with pytest.raises(dfc.DfcError) as ei:
+        dfc.decode_gemm(dev, info, x, y, workspace=odd)
+    assert ei.value.status == dfc.EINVAL
+    # batches up to 32 ignore a workspace
+    dfc.decode_gemm(dev, info, x[:32], y[:32], workspace=small)
+    torch.cuda.synchronize()
+
+
 def test_status_flag_on_corrupt_block_offsets():
     w = synth.gaussian((64, 2048), 0.02, (89,))
     dev, info, blob = upload(w, panel_k=2048)
