@@ -63,7 +63,8 @@ typedef enum {
  * A-operand order of a 32x32x16 bf16 matrix instruction.  Every item's codes
  * start on a fresh chunk and form their own blocks; a table of first chunk,
  * first block and code bits per item travels in the container, and so does
- * the number of codes whose first bit lies in each chunk (u16 per chunk), an
+ * the number of codes whose first bit lies in each chunk (one byte per chunk
+ * for C <= 16, two for C = 32), an
  * auxiliary variable of the two-phase decode (DFloat11 blog, section 03
  * item 2) that gives a decoding lane its write position by a prefix sum
  * instead of a counting pass over its chunk.
@@ -147,8 +148,8 @@ typedef struct {
     uint64_t off_panels, panels_bytes;  /* PANEL: per-item table, (n_items + 1) x 4 u32 */
     uint32_t ans_steps;                 /* ANS: steps per block S; 0 otherwise */
     uint32_t ans_prob_bits;             /* ANS: 12 (frequencies sum to 2^12); 0 otherwise */
-    uint64_t off_counts, counts_bytes;  /* PANEL: codes starting in every chunk, n_chunks x u16
-                                           (padded to 16 bytes); 0, 0 otherwise */
+    uint64_t off_counts, counts_bytes;  /* PANEL: codes starting in every chunk, n_chunks x u8
+                                           (u16 when C = 32), padded to 16 bytes; 0, 0 otherwise */
 } dfc_info;
 
 /* One matrix of a batched decode. */

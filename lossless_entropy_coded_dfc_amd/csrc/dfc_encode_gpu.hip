@@ -431,9 +431,10 @@ struct PanelArgs {
     uint32_t *item_bits;    // pass 1: code bits per item
     const uint32_t *first;  // pass 2: (first chunk, first block) per item, n_items + 1 pairs
     uint32_t *words, *offw, *blockout;
-    uint32_t *counts;  // u16 per chunk, two to a word
+    uint32_t *counts;  // one count per chunk, count_shift = log2(32 / count bits) to a word
     uint8_t *raw;
     uint32_t chunk_shift, lanes_shift;  // log2(8 C), log2(T)
+    uint32_t count_shift;               // 2 (byte counts) or 1 (16-bit counts)
 };
 
 struct PanelItem {
@@ -503,8 +504,8 @@ __global__ __launch_bounds__(256) void panel_bits_kernel(const PanelArgs a, cons
 // 5-bit offset (the next code starts where the covering code ends) and, on
 // block boundaries, the block's first element (panel order).  Its codes
 // start in consecutive chunks: it adds the number that start in each chunk
-// to that chunk's u16 count when it moves on (atomically, since the first
-// and last chunk, and the word of two counts, may be shared).
+// to that chunk's count when it moves on (atomically, since the first and
+// last chunk, and the word that holds several counts, may be shared).
 __global__ __launch_bounds__(256) void panel_pack_kernel(const PanelArgs a, const Book book) {
     __shared__ uint32_t sh[kSegThreads];
     __shared__ BookLds bk;
@@ -541,8 +542,10 @@ __global__ __launch_bounds__(256) void panel_pack_kernel(const PanelArgs a, cons
     uint32_t ncur = 0;
     auto flush_count = [&]() {
         if (ncur) {
+            // a chunk's final count fits its field, so no carry crosses fields
             const uint64_t c = c0 + cur;
-            atomicAdd(a.counts + (c >> 1), ncur << (16 * uint32_t(c & 1)));
+            const uint32_t per_word = 1u << a.count_shift;
+            atomicAdd(a.counts + (c >> a.count_shift), ncur << ((32u / per_word) * uint32_t(c & (per_word - 1u))));
         }
     };
     for (uint32_t ob = o0; ob < o1; ob += kOctBatch) {
@@ -738,6 +741,7 @@ dfc_status encode_panel_device(const uint16_t *src_dev, uint64_t n, const dfc_pa
     a.offw = reinterpret_cast<uint32_t *>(dst + off[dfc::kOffsets]);
     a.blockout = reinterpret_cast<uint32_t *>(dst + off[dfc::kBlockout]);
     a.counts = reinterpret_cast<uint32_t *>(dst + off[dfc::kCounts]);
+    a.count_shift = dfc::count_width(C) == 1 ? 2u : 1u;
     a.raw = dst + off[dfc::kRaw];
     hipLaunchKernelGGL(panel_pack_kernel, dim3(uint32_t(g.n_items)), dim3(kSegThreads), 0, st, a, book);
     // the host vectors must outlive the copies above

@@ -45,6 +45,9 @@ constexpr uint32_t kStepEscape = 0xFFFFF000u;
 inline uint64_t tables_bytes(uint32_t k) { return 14ull * (1ull << k) + 3 * 128 + 256; }
 
 inline uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
+// Bytes per stored chunk count (panel layout): a chunk of 8C bits starts at
+// most 8C codes, so one byte up to C = 16 (128 codes), two at C = 32.
+inline uint32_t count_width(uint32_t chunk_bytes) { return 8u * chunk_bytes <= 255u ? 1u : 2u; }
 inline uint64_t ceil_div(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
 
 struct Layout {
@@ -71,7 +74,7 @@ inline SectionSizes section_sizes(uint64_t n, uint64_t n_chunks, uint64_t n_bloc
     s.bytes[kBlockout] = 4 * (n_blocks + 1);
     s.bytes[kRaw] = 16 * ceil_div(n, 16);
     s.bytes[kPanels] = n_items ? 16 * (n_items + 1) : 0;
-    s.bytes[kCounts] = n_items ? 16 * ceil_div(2 * n_chunks, 16) : 0;
+    s.bytes[kCounts] = n_items ? 16 * ceil_div(count_width(chunk_bytes) * n_chunks, 16) : 0;
     return s;
 }
 
@@ -98,8 +101,8 @@ inline SectionSizes ans_section_sizes(uint64_t n, uint64_t n_words, uint64_t n_b
 }
 
 // Panel layout geometry: items of 32 rows x panel_k columns, row panels
-// first, then column slices.  The counts section holds, per chunk (u16), the
-// number of codes whose first bit lies in that chunk.
+// first, then column slices.  The counts section holds, per chunk
+// (count_width bytes), the number of codes whose first bit lies in that chunk.
 constexpr uint32_t kPanelRows = 32;
 constexpr uint32_t kSubtileK = 16;
 struct PanelGeom {

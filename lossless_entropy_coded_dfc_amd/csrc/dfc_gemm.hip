@@ -44,7 +44,7 @@ struct GemmArgs {
     const uint32_t *offw;      // packed 5-bit chunk offsets
     const uint32_t *blockout;  // u32 out[n_blocks + 1], indices in panel order
     const uint32_t *items;     // (n_items + 1) x {first chunk, first block, code bits, 0}
-    const uint16_t *counts;    // codes starting in every chunk
+    const uint8_t *counts;     // codes starting in every chunk (count_width(C) bytes each)
     const uint8_t *raw;        // raw bytes in panel order
     const uint8_t *lengths;    // the 256 code lengths (container bytes 256..511)
     const uint8_t *tables;     // tables from dfc_derive_tables, or null: derive them here
@@ -90,6 +90,15 @@ __device__ __forceinline__ ItemPos item_pos(const GemmArgs &g, uint32_t q) {
     it.col0 = (q % g.slices) * g.panel_k;
     it.e0 = 32u * (p * g.cols + it.col0);
     return it;
+}
+
+// The stored code count of chunk c: a byte up to C = 16, 16 bits at C = 32.
+template <int C>
+__device__ __forceinline__ uint32_t load_count(const __amdgpu_buffer_rsrc_t &cr, uint32_t c) {
+    if constexpr (8 * C <= 255)
+        return __builtin_amdgcn_raw_buffer_load_b8(cr, c, 0, 0);
+    else
+        return __builtin_amdgcn_raw_buffer_load_b16(cr, 2u * c, 0, 0);
 }
 
 // The B operand of column tile nt for the sub-tile at column k: lane L
@@ -140,7 +149,7 @@ __device__ __forceinline__ bool gemm_items(const GemmArgs &g, uint32_t q0, uint3
     uint32_t b = cur.b0;
     Chunk<C> ck;
     load_chunk<C>(words, offw, cur.c0 + lane, ck);
-    uint32_t stored = __builtin_amdgcn_raw_buffer_load_b16(cr, 2u * (cur.c0 + lane), 0, 0);
+    uint32_t stored = load_count<C>(cr, cur.c0 + lane);
     uint32_t s_out = blockout[b], e_out = blockout[b + 1];
     wait_for(ck);
     wait_for(stored);
@@ -180,7 +189,7 @@ __device__ __forceinline__ bool gemm_items(const GemmArgs &g, uint32_t q0, uint3
         if (more) {
             const uint32_t cn = nit.c0 + (bn - nit.b0) * kWave + lane;
             load_chunk<C>(words, offw, cn, nxt);
-            stored_nxt = __builtin_amdgcn_raw_buffer_load_b16(cr, 2u * cn, 0, 0);
+            stored_nxt = load_count<C>(cr, cn);
             s_nxt = blockout[bn];
             e_nxt = blockout[bn + 1];
         }
@@ -313,7 +322,7 @@ __global__ __launch_bounds__(512) void dfc_gemm_kernel(const GemmArgs g) {
     const __amdgpu_buffer_rsrc_t raw =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(g.raw), 0, int(g.raw_bytes), kBufferConfig);
     const __amdgpu_buffer_rsrc_t cr =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(g.counts), 0, int(g.counts_bytes), kBufferConfig);
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(g.counts), 0, int(g.counts_bytes), kBufferConfig);
     const __amdgpu_buffer_rsrc_t xr =
         XPACK ? __builtin_amdgcn_make_buffer_rsrc(g.xp, 0, int(g.xp_bytes), kBufferConfig)
               : __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(g.x), 0, int(g.x_bytes), kBufferConfig);
@@ -471,7 +480,7 @@ dfc_status dfc_decode_gemm(const void *w_blob_dev, const dfc_info *info, const v
     if (in.lut_bits < 8 || in.lut_bits > 12 || in.min_len < 1) return DFC_EINVAL;
     if (in.max_block_elems > 64u * dfc::ceil_div(8ull * C, in.min_len)) return DFC_EINVAL;
     const uint64_t limit = kNowhere - 64u * 1024u;
-    if (in.counts_bytes < 2 * in.n_chunks) return DFC_EINVAL;
+    if (in.counts_bytes < dfc::count_width(C) * in.n_chunks) return DFC_EINVAL;
     if (in.words_bytes > limit || in.offsets_bytes > limit || in.raw_bytes > limit || in.counts_bytes > limit ||
         2ull * DFC_GEMM_MAX_BATCH * in.cols > limit || 4ull * DFC_GEMM_MAX_BATCH * in.rows > limit)
         return DFC_EUNSUPPORTED;
@@ -482,7 +491,7 @@ dfc_status dfc_decode_gemm(const void *w_blob_dev, const dfc_info *info, const v
     g.offw = reinterpret_cast<const uint32_t *>(base + in.off_offsets);
     g.blockout = reinterpret_cast<const uint32_t *>(base + in.off_blockout);
     g.items = reinterpret_cast<const uint32_t *>(base + in.off_panels);
-    g.counts = reinterpret_cast<const uint16_t *>(base + in.off_counts);
+    g.counts = base + in.off_counts;
     g.counts_bytes = uint32_t(in.counts_bytes);
     g.raw = base + in.off_raw;
     g.lengths = base + dfc::hdr::lengths;

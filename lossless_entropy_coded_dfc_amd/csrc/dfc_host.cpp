@@ -222,6 +222,7 @@ dfc_status encode_panel(const uint16_t *src, uint64_t n, const dfc_params &p, co
     uint8_t *blockout = dst + off[kBlockout];
     uint8_t *panels = dst + off[kPanels];
     uint8_t *counts = dst + off[kCounts];
+    const uint32_t cw = count_width(C);
     std::vector<uint8_t> offs(n_chunks + 1, 0);
     // Pass 2: pack every item.
     parallel_for(nt, [&](unsigned t) {
@@ -241,8 +242,12 @@ dfc_status encode_panel(const uint16_t *src, uint64_t n, const dfc_params &p, co
                     ++ci;
                 }
                 const uint32_t l = len[e];
-                uint8_t *cnt = counts + 2 * (c0 + pos / chunk_bits);
-                store_le<uint16_t>(cnt, uint16_t(load_le<uint16_t>(cnt) + 1));
+                if (cw == 1) {
+                    ++counts[c0 + pos / chunk_bits];
+                } else {
+                    uint8_t *cnt = counts + 2 * (c0 + pos / chunk_bits);
+                    store_le<uint16_t>(cnt, uint16_t(load_le<uint16_t>(cnt) + 1));
+                }
                 acc = (acc << l) | code[e];
                 nacc += l;
                 pos += l;
@@ -800,6 +805,7 @@ dfc_status dfc_blob_info(const void *blob_v, uint64_t bytes, dfc_info *out) {
     if (panel) {
         const uint8_t *pt = b + off[kPanels], *cn = b + off[kCounts], *bo = b + off[kBlockout];
         const uint64_t max_count = mn ? ceil_div(8ull * in.chunk_bytes, mn) : 0;
+        const uint32_t cw = count_width(in.chunk_bytes);
         for (uint64_t q = 0; q < g.n_items; ++q) {
             const uint64_t c0 = load_le<uint32_t>(pt + 16 * q), c1 = load_le<uint32_t>(pt + 16 * q + 16);
             for (uint64_t k = item_block[q]; k < item_block[q + 1]; ++k) {
@@ -807,7 +813,7 @@ dfc_status dfc_blob_info(const void *blob_v, uint64_t bytes, dfc_info *out) {
                 const uint64_t hi = std::min<uint64_t>(c1, lo + in.lanes_per_block);
                 uint64_t sum = 0;
                 for (uint64_t c = lo; c < hi; ++c) {
-                    const uint32_t v = load_le<uint16_t>(cn + 2 * c);
+                    const uint32_t v = cw == 1 ? cn[c] : load_le<uint16_t>(cn + 2 * c);
                     if (v > max_count) return DFC_ECORRUPT;
                     sum += v;
                 }
@@ -815,7 +821,7 @@ dfc_status dfc_blob_info(const void *blob_v, uint64_t bytes, dfc_info *out) {
                     return DFC_ECORRUPT;
             }
         }
-        for (uint64_t i = 2 * in.n_chunks; i < sz.bytes[kCounts]; ++i)
+        for (uint64_t i = cw * in.n_chunks; i < sz.bytes[kCounts]; ++i)
             if (cn[i]) return DFC_ECORRUPT;
     }
     *out = in;

@@ -20,7 +20,8 @@ Header (bytes 0..255)::
     152 u64 off_raw      160 u64 raw_bytes
     168 u64 off_panels   176 u64 panels_bytes
     184 u64 blob_bytes
-    192 u64 off_counts   200 u64 counts_bytes (panel layout; 0 otherwise)
+    192 u64 off_counts   200 u64 counts_bytes (panel layout; 0 otherwise;
+                         one count per chunk, u8 for C <= 16, u16 for C = 32)
     208..255 zero
 
 Bytes 256..511 hold the code length of every exponent value (0 = unused).
@@ -139,7 +140,8 @@ def parse_blob(blob: bytes):
     offsets = st.unpack_offsets(view("offsets", "<u4"), n_chunks + 1) if five_bit else None
     out = view("blockout", "<u4")
     raw = view("raw", np.uint8)[:n]
-    counts = view("counts", "<u2")[:n_chunks] if sec["counts"][1] else None
+    counts = (view("counts", "<u2" if 8 * chunk_bytes > 255 else np.uint8)[:n_chunks].astype(np.uint16)
+              if sec["counts"][1] else None)
     return {
         "n": n, "total_bits": total_bits, "n_chunks": n_chunks, "n_blocks": n_blocks,
         "chunk_bytes": chunk_bytes, "lanes": lanes, "max_len_limit": max_len,

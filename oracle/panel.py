@@ -24,8 +24,10 @@ layout for decoding straight into a matrix product.  The reading taken here:
   starts at or after the block's first bit; out[n_blocks] = n;
 * a table of items + 1 entries (first chunk, first block, code bits of the
   item, 0), the last entry (n_chunks, n_blocks, 0, 0);
-* per chunk, the number of codes whose first bit lies in it (u16 per chunk,
-  a ``counts`` section): one more auxiliary variable of the two-phase
+* per chunk, the number of codes whose first bit lies in it (a ``counts``
+  section, one byte per chunk for C <= 16 -- a chunk of 8C <= 128 bits
+  starts at most 128 codes -- and two bytes for C = 32): one more auxiliary
+  variable of the two-phase
   decode (DFloat11 blog, section 03 item 2), with which a decoding lane
   learns its output position from a prefix sum of stored counts instead of
   decoding its chunk once more to count them.
@@ -47,6 +49,11 @@ from .fields import merge, split
 PANEL_ROWS = 32
 SUBTILE_K = 16
 LAYOUT_PANEL = 1
+
+
+def count_width(chunk_bytes: int) -> int:
+    """Bytes per stored chunk count: enough for 8C codes (codes of one bit)."""
+    return 1 if 8 * chunk_bytes <= 255 else 2
 
 
 def panel_items(rows: int, cols: int, panel_k: int):
@@ -123,6 +130,7 @@ def encode_panel(bits: np.ndarray, panel_k: int = 1024, chunk_bytes: int = 16, l
         "out": np.concatenate(outs).astype(np.uint32),
         "items": np.array(table, dtype=np.uint32),
         "counts": (np.concatenate(counts) if counts else np.zeros(0)).astype(np.uint16),
+        "count_width": count_width(chunk_bytes),
         "raw": raw,
     }
 
@@ -139,7 +147,7 @@ def write_panel_blob(enc, lut_bits: int = 11) -> bytes:
         "blockout": 4 * (enc["n_blocks"] + 1),
         "raw": 16 * (-(-n // 16)),
         "panels": 16 * (enc["n_items"] + 1),
-        "counts": 16 * (-(-2 * enc["n_chunks"] // 16)),
+        "counts": 16 * (-(-enc["count_width"] * enc["n_chunks"] // 16)),
     }
     names = ("tables", "words", "offsets", "blockout", "raw", "panels", "counts")
     offsets = {}
@@ -170,7 +178,7 @@ def write_panel_blob(enc, lut_bits: int = 11) -> bytes:
     put("blockout", np.asarray(enc["out"], dtype="<u4").tobytes())
     put("raw", np.asarray(enc["raw"], dtype=np.uint8).tobytes())
     put("panels", np.asarray(enc["items"], dtype="<u4").tobytes())
-    put("counts", np.asarray(enc["counts"], dtype="<u2").tobytes())
+    put("counts", np.asarray(enc["counts"], dtype="<u2" if enc["count_width"] == 2 else np.uint8).tobytes())
     return bytes(buf)
 
 

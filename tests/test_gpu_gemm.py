@@ -253,25 +253,25 @@ def test_status_flag_on_corrupt_block_offsets():
     assert int(status.item()) == dfc.ECORRUPT
 
 
-def put_u16(t, offset, values):
-    raw = np.asarray(values, dtype="<u2").view(np.uint8)
+def put_u8(t, offset, values):
+    raw = np.asarray(values, dtype=np.uint8)
     t[offset: offset + raw.size] = torch.from_numpy(raw.copy()).cuda()
 
 
 @pytest.mark.parametrize("case", ["moved", "sum", "huge"])
 def test_status_flag_on_wrong_chunk_counts(case):
-    """Stored chunk counts that the stream contradicts: one count moved to
-    the next chunk of the same block (every sum still matches, so the
-    container validates and only the kernel's per-chunk check can tell),
-    one count raised (the block's sum no longer matches its offsets), and a
-    count above what a chunk can hold."""
+    """Stored chunk counts (one byte each at C = 16) that the stream
+    contradicts: one count moved to the next chunk of the same block (every
+    sum still matches, so the container validates and only the kernel's
+    per-chunk check can tell), one count raised (the block's sum no longer
+    matches its offsets), and a count above what a chunk can hold."""
     w = synth.gaussian((64, 2048), 0.02, (90,))
     dev, info, blob = upload(w, C=16, panel_k=2048)
     bad = torch.from_numpy(blob.copy()).cuda()
-    o = info.off_counts + 2 * 5
-    v0, v1 = (int(v) for v in np.frombuffer(blob[o: o + 4].tobytes(), dtype="<u2"))
-    new = {"moved": [v0 - 1, v1 + 1], "sum": [v0 + 1, v1], "huge": [60000, v1]}[case]
-    put_u16(bad, o, new)
+    o = info.off_counts + 5
+    v0, v1 = (int(v) for v in blob[o: o + 2])
+    new = {"moved": [v0 - 1, v1 + 1], "sum": [v0 + 1, v1], "huge": [255, v1]}[case]
+    put_u8(bad, o, new)
     if case == "moved":
         assert dfc.blob_info(bad.cpu().numpy()).n == info.n
     say("case wrong chunk counts", case)

@@ -207,7 +207,8 @@ def test_panel_encoder_matches_oracle_bytes(C, shape, panel_k):
     assert info.layout == dfc.LAYOUT_PANEL and info.panel_rows == 32 and info.panel_k == panel_k
     assert info.n_items == len(pn.panel_items(*shape, panel_k))
     assert info.panels_bytes == 16 * (info.n_items + 1)
-    assert info.counts_bytes == 16 * -(-2 * info.n_chunks // 16) and info.off_counts % 256 == 0
+    width = 1 if C <= 16 else 2
+    assert info.counts_bytes == 16 * -(-width * info.n_chunks // 16) and info.off_counts % 256 == 0
     assert info.coded_bytes == 512 + (info.words_bytes + info.offsets_bytes + info.blockout_bytes + info.raw_bytes
                                       + info.panels_bytes + info.counts_bytes)
 
@@ -249,12 +250,12 @@ def test_panel_validation_rejects_corruption():
         "item_start": corrupt(b, info.off_blockout + 4 * first_block1, struct.pack("<I", 32 * 512 + 1)),
         # a chunk count one higher: its block's counts no longer add up to
         # the block's offsets
-        "count_sum": corrupt(b, info.off_counts + 6, struct.pack("<H", struct.unpack_from(
-            "<H", bytes(b), info.off_counts + 6)[0] + 1)),
+        "count_sum": corrupt(b, info.off_counts + 3, struct.pack("<B", struct.unpack_from(
+            "<B", bytes(b), info.off_counts + 3)[0] + 1)),
         # more codes than a chunk can start (8C codes of at least min_len bits)
-        "count_max": corrupt(b, info.off_counts, struct.pack("<HH", 8 * 16 + 1, 0)),
+        "count_max": corrupt(b, info.off_counts, struct.pack("<BB", 8 * 16 + 1, 0)),
         "count_padding": corrupt(b, info.off_counts + info.counts_bytes - 1, b"\x01")
-        if info.counts_bytes > 2 * info.n_chunks else corrupt(b, 208, b"\x01"),
+        if info.counts_bytes > info.n_chunks else corrupt(b, 208, b"\x01"),
         "counts_slot": corrupt(b, 200, struct.pack("<Q", info.counts_bytes + 16)),
     }
     for name, bad in cases.items():
@@ -265,8 +266,8 @@ def test_panel_validation_rejects_corruption():
     # the container still validates (only the decoder, which checks every
     # chunk's codes, can tell)
     c = bytearray(b)
-    v0, v1 = struct.unpack_from("<HH", c, info.off_counts + 4)
-    struct.pack_into("<HH", c, info.off_counts + 4, v0 - 1, v1 + 1)
+    v0, v1 = struct.unpack_from("<BB", c, info.off_counts + 2)
+    struct.pack_into("<BB", c, info.off_counts + 2, v0 - 1, v1 + 1)
     assert dfc.blob_info(np.frombuffer(bytes(c), dtype=np.uint8)).n == info.n
 
 

@@ -132,16 +132,22 @@ def test_counts_section_in_the_container():
     blob = bytearray(pn.write_panel_blob(enc, 11))
     p = bl.parse_blob(bytes(blob))
     off, size = p["sections"]["counts"]
-    assert size == 16 * -(-2 * enc["n_chunks"] // 16)
+    assert size == 16 * -(-enc["n_chunks"] // 16)      # one byte per count at C = 8
     assert off % 256 == 0 and off >= p["sections"]["panels"][0] + p["sections"]["panels"][1]
     assert p["blob_bytes"] >= off + size
     assert np.array_equal(p["counts"], enc["counts"])
     assert bl.coded_bytes(p) == 512 + sum(p["sections"][k][1] for k in
                                            ("words", "offsets", "blockout", "raw", "panels", "counts"))
     c = int(np.flatnonzero(enc["counts"])[3])
-    blob[off + 2 * c] ^= 1
+    blob[off + c] ^= 1
     with pytest.raises(ValueError, match="counts"):
         pn.decode_panel_blob(bytes(blob))
+    # two bytes per count at C = 32, where a chunk may start 256 codes
+    assert pn.count_width(16) == 1 and pn.count_width(32) == 2
+    enc32 = pn.encode_panel(x, panel_k=48, chunk_bytes=32)
+    p32 = bl.parse_blob(pn.write_panel_blob(enc32, 11))
+    assert p32["sections"]["counts"][1] == 16 * -(-2 * enc32["n_chunks"] // 16)
+    assert np.array_equal(p32["counts"], enc32["counts"])
     # the flat layout has no counts section
     flat = bl.write_blob(st.encode(x, 8, 64), 11)
     assert bl.parse_blob(flat)["sections"]["counts"] == (0, 0) and bl.parse_blob(flat)["counts"] is None
