@@ -4,7 +4,9 @@
 //   item 1: compact hierarchical lookup tables in on-chip memory find code
 //           boundaries fast -> the first-level k-bit tables (step, symbols,
 //           boundary mask) and the per-length canonical tables for longer
-//           codes are copied into LDS once per workgroup;
+//           codes live in LDS: every workgroup derives them from the 256
+//           code lengths, or copies the image dfc_derive_tables prepared
+//           once per container;
 //   item 2: a two-phase kernel; in phase one threads agree on read and write
 //           positions through small auxiliary variables, phase two rebuilds
 //           the weights -> per-chunk start offsets and per-block output
@@ -18,9 +20,10 @@
 // Work decomposition: one lane per chunk (C bytes of code stream), one
 // wavefront (64 lanes) per block of 64 chunks.  Workgroups are persistent:
 // the grid is sized to the resident capacity of the GPU, each workgroup owns
-// a contiguous run of blocks of one matrix, and its wavefronts take those
-// blocks in turn while prefetching the next block's stream words, offsets
-// and raw bytes.  All decoding is integer work on bit patterns.
+// a contiguous run of blocks of one matrix, and each of its wavefronts a
+// contiguous share of that run, decoded block after block while the next
+// block's stream words, offsets and output range are in flight.  All
+// decoding is integer work on bit patterns.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
