@@ -61,6 +61,9 @@ struct GemmArgs {
     uint32_t *status;
 };
 
+// Cache-policy operand of a buffer load on gfx950: the non-temporal bit.
+constexpr int kLoadNT = 2;
+
 // Sub-tiles (512 values) whose raw bytes are prefetched into registers per
 // block: a 64-chunk block of about 3 bits per code completes at most this
 // many; the rest load when used.
@@ -164,11 +167,13 @@ __device__ __forceinline__ bool gemm_items(const GemmArgs &g, uint32_t q0, uint3
         // raw bytes
         const uint32_t rounds = (lead + total_want) >> 9;
         const uint32_t kcol = cur.col0 + 16u * (base >> 9);
+        // (non-temporal: W's raw bytes are read once; X and the tables are
+        // what the caches should keep)
         u32x2 R[PF];
 #pragma unroll
         for (int j = 0; j < PF; ++j)
             R[j] = uint32_t(j) < rounds
-                       ? __builtin_amdgcn_raw_buffer_load_b64(raw, cur.e0 + base + 512u * j + 8u * lane, 0, 0)
+                       ? __builtin_amdgcn_raw_buffer_load_b64(raw, cur.e0 + base + 512u * j + 8u * lane, 0, kLoadNT)
                        : u32x2{0u, 0u};
         // With one column tile, the X fragments of those sub-tiles too: their
         // cache round trips then overlap the decoding instead of each product.
@@ -254,7 +259,7 @@ __device__ __forceinline__ bool gemm_items(const GemmArgs &g, uint32_t q0, uint3
             }
         }
         for (uint32_t j = PF; j < nfull; ++j) {
-            const u32x2 Rj = __builtin_amdgcn_raw_buffer_load_b64(raw, cur.e0 + base + 512u * j + 8u * lane, 0, 0);
+            const u32x2 Rj = __builtin_amdgcn_raw_buffer_load_b64(raw, cur.e0 + base + 512u * j + 8u * lane, 0, kLoadNT);
             const u32x2 E = *reinterpret_cast<const u32x2 *>(stage + 512u * j + 8u * lane);
             const bf16x8 A = as_bf16x8(assemble8(E, Rj));
             u32x4 X[NT];
