@@ -21,16 +21,20 @@ hand their memory out while a decode into them is pending.
 """
 from __future__ import annotations
 
-from . import MAX_BATCH, Info, decode_batch
+from . import MAX_BATCH, Info, decode_batch, derive_tables
 
 
 class DecodeAhead:
     """Double-buffered decode of ``layers`` (a list, per layer, of
     ``(blob_dev, info, shape)`` with blob_dev a device uint8 tensor holding a
     container in the flat, padded or rANS layout and shape the matrix
-    shape)."""
+    shape).  With ``prepare_tables`` every container's decode tables are
+    derived once, on the side stream before its first decode
+    (``derive_tables``), and every decode copies them instead of deriving
+    them in each workgroup; a container must therefore not change after its
+    layer's first prefetch."""
 
-    def __init__(self, layers, device="cuda"):
+    def __init__(self, layers, device="cuda", prepare_tables: bool = True):
         import torch
 
         self.torch = torch
@@ -50,6 +54,8 @@ class DecodeAhead:
         self.free_recorded = [False, False]
         self.held = [None, None]  # layer decoded (or decoding) into each set, until released
         self.status = torch.zeros(1, dtype=torch.int32, device=device)
+        self.prepare_tables = prepare_tables
+        self.tables = [[None] * len(layer) for layer in self.layers]
         for t in [self.status] + [t for s in self.scratch for t in s]:
             t.record_stream(self.side)
         # the scratch and status allocations (and the zero fill) were ordered
@@ -70,7 +76,11 @@ class DecodeAhead:
         with self.torch.cuda.stream(self.side):
             if self.free_recorded[slot]:
                 self.side.wait_event(self.free[slot])
-            items = [(blob, info, self.scratch[slot][j][: int(info.n)])
+            if self.prepare_tables:
+                for j, (blob, info, _) in enumerate(self.layers[i]):
+                    if self.tables[i][j] is None:
+                        self.tables[i][j] = derive_tables(blob, info, stream=self.side.cuda_stream)
+            items = [(blob, info, self.scratch[slot][j][: int(info.n)], self.tables[i][j])
                      for j, (blob, info, _) in enumerate(self.layers[i])]
             for k in range(0, len(items), MAX_BATCH):
                 decode_batch(items[k: k + MAX_BATCH], self.status, stream=self.side.cuda_stream)
@@ -102,6 +112,7 @@ class DecodeAhead:
         if self.scratch is not None:
             self.side.synchronize()
             self.scratch = None
+            self.tables = None
             self.held = [None, None]
 
     def __enter__(self):

@@ -39,12 +39,15 @@ def make_layers(n_layers, shapes, C=16):
     return layers, originals
 
 
-def test_weights_equal_originals_when_used():
+@pytest.mark.parametrize("prepare", [True, False])
+def test_weights_equal_originals_when_used(prepare):
+    """Tables prepared once per container on the side stream, or derived by
+    every decoding workgroup: the same weights either way."""
     from lossless_entropy_coded_dfc_amd.ahead import DecodeAhead
     shapes = [(256, 512), (512, 256), (128, 512)]
     layers, originals = make_layers(5, shapes)
-    dec = DecodeAhead(layers)
-    say("case decode-ahead 5 layers")
+    dec = DecodeAhead(layers, prepare_tables=prepare)
+    say("case decode-ahead 5 layers, prepared tables" if prepare else "case decode-ahead 5 layers, derived tables")
     dec.prefetch(0)
     for i in range(5):
         if i + 1 < 5:
