@@ -161,6 +161,7 @@ __global__ __launch_bounds__(1024, Occupancy<C>::kWavesPerSimd) void dfc_decode_
     const uint32_t lane = threadIdx.x % kWave;
     const uint32_t stage_off = a.tables_bytes + wave * args.stage_bytes;
     uint8_t *stage = lds + stage_off;
+    const uint32_t stage_addr = lds_address(stage);  // its LDS address
     // this wavefront's run: a contiguous share of the workgroup's blocks
     const uint32_t lo_wg = (wg - a.wg_begin) * a.blocks_per_wg;
     const uint32_t hi_wg = min(lo_wg + a.blocks_per_wg, a.n_blocks);
@@ -243,9 +244,9 @@ __global__ __launch_bounds__(1024, Occupancy<C>::kWavesPerSimd) void dfc_decode_
         const bool bad = (total != want) | (__builtin_amdgcn_ballot_w64(cnt > 8u * C) != 0);
         if (!bad && cnt) {
             if constexpr (Padded)
-                write_codes_padded<C>(cur, end, cnt, stage - stage_off, stage_off + lead + (incl - cnt), t);
+                write_codes_padded<C>(cur, end, cnt, stage_addr + lead + (incl - cnt), t);
             else
-                write_codes<C>(cur, start, end, stage - stage_off, stage_off + lead + (incl - cnt), t);
+                write_codes<C>(cur, start, end, stage_addr + lead + (incl - cnt), t);
         }
         // Everything prefetched must be in registers before the first store,
         // on every path to the next block.

@@ -189,18 +189,26 @@ __device__ __forceinline__ void wait_for(const T &v) {
     for (unsigned i = 0; i < sizeof(T) / 4; ++i) asm volatile("" ::"v"(w[i]));
 }
 
-// ORs the 4 bytes of v into the zeroed LDS staging bytes [q, q + 4): two
-// aligned dword ORs.  OR is what lets lanes overlap: a byte is only ever
-// ORed with zero or with its own final value.
-__device__ __forceinline__ void or_4_bytes(uint8_t *lds_base, uint32_t q, uint32_t v) {
+// LDS address (byte offset in the workgroup's LDS) of a pointer into it.
+typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
+typedef __attribute__((address_space(3))) uint32_t lds_u32_t;
+__device__ __forceinline__ uint32_t lds_address(const uint8_t *p) {
+    return uint32_t(reinterpret_cast<size_t>((const lds_u8_t *)p));
+}
+
+// ORs the 4 bytes of v into the zeroed LDS staging bytes at LDS address
+// [q, q + 4): two aligned dword ORs.  OR is what lets lanes overlap: a byte
+// is only ever ORed with zero or with its own final value.  q is an LDS
+// address, not an offset from a pointer, so that the address needs no add.
+__device__ __forceinline__ void or_4_bytes(uint32_t q, uint32_t v) {
     const uint64_t x = uint64_t(v) << (8u * (q & 3u));
-    uint32_t *d = reinterpret_cast<uint32_t *>(lds_base + (q & ~3u));
+    lds_u32_t *d = reinterpret_cast<lds_u32_t *>(size_t(q & ~3u));
     __hip_atomic_fetch_or(d, uint32_t(x), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
     __hip_atomic_fetch_or(d + 1, uint32_t(x >> 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
 }
 
 // Phase two: decode the chunk again and OR its (rotated) exponents into the
-// zeroed staging area, from byte q0 on, up to four codes per lookup.  A
+// zeroed staging area, from LDS address q0 on, up to four codes per lookup.  A
 // table entry holds zero bytes past its own codes, and codes decoded past
 // the chunk's last one are the next chunk's first codes, identical to what
 // the next lane writes there; so neither needs to be cut off.  Lookups stop
@@ -209,8 +217,8 @@ __device__ __forceinline__ void or_4_bytes(uint8_t *lds_base, uint32_t q, uint32
 // [start, end), as count_codes does (callers that take their positions
 // from stored counts check them with it; for the others it is dead code).
 template <int C>
-__device__ __forceinline__ uint32_t write_codes(const Chunk<C> &ck, int start, int end, uint8_t *lds_base,
-                                                uint32_t q0, const Tables &t) {
+__device__ __forceinline__ uint32_t write_codes(const Chunk<C> &ck, int start, int end, uint32_t q0,
+                                                const Tables &t) {
     constexpr int NW = C / 4;
     // the boundary mask at `end`, looked up first so that the stream words
     // need not outlive the loop
@@ -226,7 +234,7 @@ __device__ __forceinline__ uint32_t write_codes(const Chunk<C> &ck, int start, i
             while (uint16_t(acc) >= g) {
                 const uint32_t win = __builtin_amdgcn_alignbit(hi, lo, acc);
                 const uint2 e = t.wsym[win >> t.kshift];
-                or_4_bytes(lds_base, q0 + (acc >> 16), e.x);
+                or_4_bytes(q0 + (acc >> 16), e.x);
                 acc += e.y;
             }
             if (lo16(acc) >= kBias - 2048u) break;
@@ -234,7 +242,7 @@ __device__ __forceinline__ uint32_t write_codes(const Chunk<C> &ck, int start, i
             uint32_t sym;
             const uint32_t win = __builtin_amdgcn_alignbit(hi, lo, acc);
             const uint32_t l = long_code(win >> 8, t, sym);
-            or_4_bytes(lds_base, q0 + (acc >> 16), sym);
+            or_4_bytes(q0 + (acc >> 16), sym);
             acc += 0x10000u - l;
         }
         acc += 32u;
@@ -287,15 +295,15 @@ __device__ __forceinline__ uint32_t count_codes_padded(const Chunk<C> &ck, int e
 }
 
 // Padded layout, phase two: the chunk's cnt codes (from the counting pass)
-// ORed into the staging area from byte q0 on.  Nothing past them may be
+// ORed into the staging area from LDS address q0 on.  Nothing past them may be
 // written: what follows a chunk's last code is its tail of ones and the next
 // chunk's bits, not the next chunk's first codes.  Whole-window lookups need
 // no cut (their codes end by `end`); a long code is written only if it is
 // one of the cnt; the last few codes go out with their entry cut to the
 // codes still owed.
 template <int C>
-__device__ __forceinline__ void write_codes_padded(const Chunk<C> &ck, int end, uint32_t cnt, uint8_t *lds_base,
-                                                   uint32_t q0, const Tables &t) {
+__device__ __forceinline__ void write_codes_padded(const Chunk<C> &ck, int end, uint32_t cnt, uint32_t q0,
+                                                   const Tables &t) {
     constexpr int NW = C / 4;
     const int stop = end - int(t.kb) + 1;
     uint32_t acc = kBias;
@@ -308,7 +316,7 @@ __device__ __forceinline__ void write_codes_padded(const Chunk<C> &ck, int end, 
             while (uint16_t(acc) >= g) {
                 const uint32_t win = __builtin_amdgcn_alignbit(hi, lo, acc);
                 const uint2 e = t.wsym[win >> t.kshift];
-                or_4_bytes(lds_base, q0 + (acc >> 16), e.x);
+                or_4_bytes(q0 + (acc >> 16), e.x);
                 acc += e.y;
             }
             if (lo16(acc) >= kBias - 2048u) break;
@@ -316,7 +324,7 @@ __device__ __forceinline__ void write_codes_padded(const Chunk<C> &ck, int end, 
             uint32_t sym;
             const uint32_t win = __builtin_amdgcn_alignbit(hi, lo, acc);
             const uint32_t l = long_code(win >> 8, t, sym);
-            if ((acc >> 16) < cnt) or_4_bytes(lds_base, q0 + (acc >> 16), sym);
+            if ((acc >> 16) < cnt) or_4_bytes(q0 + (acc >> 16), sym);
             acc += 0x10000u - l;
         }
         acc += 32u;
@@ -331,7 +339,7 @@ __device__ __forceinline__ void write_codes_padded(const Chunk<C> &ck, int end, 
         const uint2 e = t.wsym[window_at<NW>(ck.w, pos) >> t.kshift];
         const uint32_t owed = cnt - (a >> 16);
         const uint32_t keep = owed >= 4u ? 0xFFFFFFFFu : (1u << (8u * owed)) - 1u;
-        or_4_bytes(lds_base, q0 + (a >> 16), e.x & keep);
+        or_4_bytes(q0 + (a >> 16), e.x & keep);
         a += e.y;
     }
 }

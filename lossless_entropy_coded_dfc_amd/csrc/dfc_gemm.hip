@@ -140,7 +140,7 @@ __global__ void pack_x_kernel(const uint16_t *x, uint32_t batch, uint32_t cols, 
 // result off the critical path of the loop).
 template <int C, int NT, bool XPACK>
 __device__ __forceinline__ bool gemm_items(const GemmArgs &g, uint32_t q0, uint32_t qstep, uint32_t qend,
-                                           const Tables &t, uint8_t *stage, uint32_t stage_off, uint32_t lane,
+                                           const Tables &t, uint8_t *stage, uint32_t lane,
                                            const __amdgpu_buffer_rsrc_t &words, const __amdgpu_buffer_rsrc_t &offw,
                                            const __amdgpu_buffer_rsrc_t &raw, const __amdgpu_buffer_rsrc_t &cr,
                                            const __amdgpu_buffer_rsrc_t &xr, uint32_t xcol, f32x16 (&acc)[NT]) {
@@ -219,7 +219,7 @@ __device__ __forceinline__ bool gemm_items(const GemmArgs &g, uint32_t q0, uint3
         const bool bad = (total != total_want) | (total_want > g.max_block) |
                    (__builtin_amdgcn_ballot_w64(cnt > 8u * C) != 0);
         uint32_t got = cnt;
-        if (!bad && cnt) got = write_codes<C>(ck, start, end, lds, stage_off + lead + (incl - cnt), t);
+        if (!bad && cnt) got = write_codes<C>(ck, start, end, lds_address(stage) + lead + (incl - cnt), t);
         miss |= (got != cnt) | ((start < end) & (cnt == 0));
         wait_for(R);
         if constexpr (NT == 1) wait_for(XP);
@@ -345,7 +345,7 @@ __global__ __launch_bounds__(512) void dfc_gemm_kernel(const GemmArgs g) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x16{};
         if (p < g.n_panels)
-            gemm_items<C, NT, XPACK>(g, p * g.slices + part * wpp + sw, stride, (p + 1) * g.slices, t, stage, stage_off, lane,
+            gemm_items<C, NT, XPACK>(g, p * g.slices + part * wpp + sw, stride, (p + 1) * g.slices, t, stage, lane,
                               words, offw, raw, cr, xr, xcol, acc);
         // D[i][j] of a 32x32 tile: i = 8 (r / 4) + 4 (lane / 32) + r % 4,
         // j = lane % 32.  Value r of lane L goes to slot 4 (64 (r / 4) + L) +
