@@ -196,10 +196,11 @@ __global__ __launch_bounds__(1024, Occupancy<C>::kWavesPerSimd) void dfc_decode_
         const uint32_t want = e_out - s_out;
         const uint32_t rounds = (lead + want) / kRound;  // rounds this block completes
         // raw bytes of those rounds (the first PF of them) per lane
+        // (rounds past them load nothing: their lanes' octets all lie
+        // outside [lo, 0), so no branch is needed around the loads)
         u32x2 R[PF];
 #pragma unroll
-        for (int j = 0; j < PF; ++j)
-            R[j] = uint32_t(j) < rounds ? load_raw_octet(bf, base + kRound * j, lane, lo, e_out) : u32x2{0u, 0u};
+        for (int j = 0; j < PF; ++j) R[j] = load_raw_octet(bf, base + kRound * j, lane, lo, uint32_t(j) < rounds ? e_out : 0u);
         // next block's stream words, offsets and output range
         const uint32_t bn = b + 1u;
         const bool more = bn < b_end;

@@ -136,6 +136,20 @@ __device__ __forceinline__ uint32_t window_at(const uint32_t (&w)[NW + 2], uint3
     return __builtin_amdgcn_alignbit(hi, lo, 32u * j - pos);
 }
 
+// window_at for a chunk's end bit, which lies past 32 (NW - 1) in every
+// chunk but a stream's last few: two candidate word pairs there, the full
+// selection only for the others.
+template <int NW>
+__device__ __forceinline__ uint32_t window_at_end(const uint32_t (&w)[NW + 2], uint32_t pos) {
+    if (pos > 32u * (NW - 1)) {
+        const bool second = pos > 32u * NW;
+        const uint32_t hi = second ? w[NW] : w[NW - 1];
+        const uint32_t lo = second ? w[NW + 1] : w[NW];
+        return __builtin_amdgcn_alignbit(hi, lo, (second ? 32u * (NW + 1) : 32u * NW) - pos);
+    }
+    return window_at<NW>(w, pos);
+}
+
 // Phase one: number of codes that start in [start, end) (chunk-relative).
 // The k-loop walks the chunk one word at a time so that every window is a
 // funnel shift of two registers: a code starting at pos in (32k, 32k + 32]
@@ -147,12 +161,15 @@ template <int C>
 __device__ __forceinline__ uint32_t count_codes(const Chunk<C> &ck, int start, int end, const Tables &t) {
     constexpr int NW = C / 4;
     uint32_t acc = kBias - uint32_t(start);
+    // the lookups of word k go on while the low half of acc is at least
+    // max(kBias, g0 + 32 (k + 1)): shift >= 0 and pos < end
+    const int g0 = int(kBias) + 1 - end;
 #pragma unroll
     for (int k = -1; k < NW; ++k) {
         const uint32_t hi = k < 0 ? 0u : ck.w[k < 0 ? 0 : k];
         const uint32_t lo = ck.w[k + 1];
         // stay while shift >= 0 (pos <= 32 (k + 1)) and pos < end
-        const uint16_t g = uint16_t(kBias + uint32_t(max(0, 32 * (k + 1) - end + 1)));
+        const uint16_t g = uint16_t(max(int(kBias), g0 + 32 * (k + 1)));
         for (;;) {
             while (uint16_t(acc) >= g) {
                 const uint32_t win = __builtin_amdgcn_alignbit(hi, lo, acc);
@@ -170,7 +187,7 @@ __device__ __forceinline__ uint32_t count_codes(const Chunk<C> &ck, int start, i
     uint32_t cnt = acc >> 16;
     const int pos = 32 * (NW + 1) - int(lo16(acc)) + int(kBias);
     if (pos > end) {
-        const uint32_t we = window_at<NW>(ck.w, uint32_t(end));
+        const uint32_t we = window_at_end<NW>(ck.w, uint32_t(end));
         cnt -= __popc(uint32_t(t.mask[we >> t.kshift]) & ((1u << (pos - end)) - 1u));
     }
     return cnt;
@@ -222,14 +239,15 @@ __device__ __forceinline__ uint32_t write_codes(const Chunk<C> &ck, int start, i
     constexpr int NW = C / 4;
     // the boundary mask at `end`, looked up first so that the stream words
     // need not outlive the loop
-    const uint32_t end_mask = t.mask[window_at<NW>(ck.w, uint32_t(end)) >> t.kshift];
+    const uint32_t end_mask = t.mask[window_at_end<NW>(ck.w, uint32_t(end)) >> t.kshift];
     uint32_t acc = kBias - uint32_t(start);
+    const int g0 = int(kBias) + 1 - end;  // as in count_codes
 #pragma unroll
     for (int k = -1; k < NW; ++k) {
         const uint32_t hi = k < 0 ? 0u : ck.w[k < 0 ? 0 : k];
         const uint32_t lo = ck.w[k + 1];
         // stay while shift >= 0 (pos <= 32 (k + 1)) and pos < end
-        const uint16_t g = uint16_t(kBias + uint32_t(max(0, 32 * (k + 1) - end + 1)));
+        const uint16_t g = uint16_t(max(int(kBias), g0 + 32 * (k + 1)));
         for (;;) {
             while (uint16_t(acc) >= g) {
                 const uint32_t win = __builtin_amdgcn_alignbit(hi, lo, acc);
@@ -265,12 +283,13 @@ __device__ __forceinline__ uint32_t count_codes_padded(const Chunk<C> &ck, int e
     constexpr int NW = C / 4;
     const int stop = end - int(t.kb) + 1;  // whole-window lookups start before this bit
     uint32_t acc = kBias;
+    const int g0 = int(kBias) + 1 - stop;  // as in count_codes, with stop for end
 #pragma unroll
     for (int k = -1; k < NW; ++k) {
         const uint32_t hi = k < 0 ? 0u : ck.w[k < 0 ? 0 : k];
         const uint32_t lo = ck.w[k + 1];
         // stay while shift >= 0 (pos <= 32 (k + 1)) and pos < stop
-        const uint16_t g = uint16_t(kBias + uint32_t(max(0, 32 * (k + 1) - stop + 1)));
+        const uint16_t g = uint16_t(max(int(kBias), g0 + 32 * (k + 1)));
         for (;;) {
             while (uint16_t(acc) >= g) {
                 const uint32_t win = __builtin_amdgcn_alignbit(hi, lo, acc);
@@ -307,11 +326,12 @@ __device__ __forceinline__ void write_codes_padded(const Chunk<C> &ck, int end, 
     constexpr int NW = C / 4;
     const int stop = end - int(t.kb) + 1;
     uint32_t acc = kBias;
+    const int g0 = int(kBias) + 1 - stop;  // as in count_codes, with stop for end
 #pragma unroll
     for (int k = -1; k < NW; ++k) {
         const uint32_t hi = k < 0 ? 0u : ck.w[k < 0 ? 0 : k];
         const uint32_t lo = ck.w[k + 1];
-        const uint16_t g = uint16_t(kBias + uint32_t(max(0, 32 * (k + 1) - stop + 1)));
+        const uint16_t g = uint16_t(max(int(kBias), g0 + 32 * (k + 1)));
         for (;;) {
             while (uint16_t(acc) >= g) {
                 const uint32_t win = __builtin_amdgcn_alignbit(hi, lo, acc);

@@ -69,7 +69,7 @@ constexpr int kLoadNT = 2;
 // many; the rest load when used.
 template <int C>
 struct GemmPrefetch {
-    static constexpr int N = C >= 32 ? 10 : (C == 16 ? 8 : (C == 8 ? 4 : 3));
+    static constexpr int N = C >= 32 ? 10 : (C == 16 ? 7 : (C == 8 ? 4 : 3));
 };
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4 &v) { return __builtin_bit_cast(bf16x8, v); }
@@ -168,21 +168,20 @@ __device__ __forceinline__ bool gemm_items(const GemmArgs &g, uint32_t q0, uint3
         const uint32_t rounds = (lead + total_want) >> 9;
         const uint32_t kcol = cur.col0 + 16u * (base >> 9);
         // (non-temporal: W's raw bytes are read once; X and the tables are
-        // what the caches should keep)
+        // what the caches should keep); the loads past them go out of range
+        // and return zeros, with no branch around them
         u32x2 R[PF];
 #pragma unroll
         for (int j = 0; j < PF; ++j)
-            R[j] = uint32_t(j) < rounds
-                       ? __builtin_amdgcn_raw_buffer_load_b64(raw, cur.e0 + base + 512u * j + 8u * lane, 0, kLoadNT)
-                       : u32x2{0u, 0u};
+            R[j] = __builtin_amdgcn_raw_buffer_load_b64(
+                raw, uint32_t(j) < rounds ? cur.e0 + base + 512u * j + 8u * lane : kNowhere, 0, kLoadNT);
         // With one column tile, the X fragments of those sub-tiles too: their
         // cache round trips then overlap the decoding instead of each product.
         u32x4 XP[NT == 1 ? PF : 1];
 #pragma unroll
         for (int j = 0; j < (NT == 1 ? PF : 0); ++j)
-            XP[j] = uint32_t(j) < rounds
-                        ? __builtin_amdgcn_raw_buffer_load_b128(xr, xcol + 2u * (kcol + 16u * j), 0, 0)
-                        : u32x4{0u, 0u, 0u, 0u};
+            XP[j] = __builtin_amdgcn_raw_buffer_load_b128(
+                xr, uint32_t(j) < rounds ? xcol + 2u * (kcol + 16u * j) : kNowhere, 0, 0);
         // the next block: this item's next, or the first of the next item
         const bool same = b + 1u < cur.b1;
         const bool more = same || cur.q + qstep < qend;
@@ -239,7 +238,11 @@ __device__ __forceinline__ bool gemm_items(const GemmArgs &g, uint32_t q0, uint3
         // column tiles, their X fragments are requested before their
         // products, so that their cache round trips overlap.
         const uint32_t extent = lead + total;
-        const uint32_t nfull = extent >> 9;
+        // (equal to `rounds` here; kept opaque so that the compiler does not
+        // hold the prefetch's eight conditions in registers across the write
+        // pass to reuse them)
+        uint32_t nfull = extent >> 9;
+        asm volatile("" : "+s"(nfull));
 #pragma unroll
         for (int j = 0; j < PF; ++j) {
             if (uint32_t(j) < nfull) {
