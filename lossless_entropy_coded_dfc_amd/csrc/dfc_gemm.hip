@@ -63,6 +63,9 @@ struct GemmArgs {
 
 // Cache-policy operand of a buffer load on gfx950: the non-temporal bit.
 constexpr int kLoadNT = 2;
+// A byte offset from which every step of the prefetch (< 8 KB) stays past
+// every range the launcher accepts (below kNowhere - 64 KB) and below 2^32.
+constexpr uint32_t kFar = kNowhere - 8192u;
 
 // Sub-tiles (512 values) whose raw bytes are prefetched into registers per
 // block: a 64-chunk block of about 3 bits per code completes at most this
@@ -170,18 +173,30 @@ __device__ __forceinline__ bool gemm_items(const GemmArgs &g, uint32_t q0, uint3
         // (non-temporal: W's raw bytes are read once; X and the tables are
         // what the caches should keep); the loads past them go out of range
         // and return zeros, with no branch around them
+        // (the step between sub-tiles goes into the loads' immediate offsets:
+        // only the per-lane base is selected, between the sub-tiles' base
+        // and kFar, from which every step stays out of range; the selection
+        // is kept opaque so that the compiler does not fold the steps back
+        // into it)
+        static_assert(512 * (PF - 1) <= 8192, "prefetch steps from kFar");
+        const uint32_t rbase = cur.e0 + base + 8u * lane;
         u32x2 R[PF];
 #pragma unroll
-        for (int j = 0; j < PF; ++j)
-            R[j] = __builtin_amdgcn_raw_buffer_load_b64(
-                raw, uint32_t(j) < rounds ? cur.e0 + base + 512u * j + 8u * lane : kNowhere, 0, kLoadNT);
+        for (int j = 0; j < PF; ++j) {
+            uint32_t at = uint32_t(j) < rounds ? rbase : kFar;
+            asm volatile("" : "+v"(at));
+            R[j] = __builtin_amdgcn_raw_buffer_load_b64(raw, at + 512u * j, 0, kLoadNT);
+        }
         // With one column tile, the X fragments of those sub-tiles too: their
         // cache round trips then overlap the decoding instead of each product.
+        const uint32_t xbase = xcol + 2u * kcol;
         u32x4 XP[NT == 1 ? PF : 1];
 #pragma unroll
-        for (int j = 0; j < (NT == 1 ? PF : 0); ++j)
-            XP[j] = __builtin_amdgcn_raw_buffer_load_b128(
-                xr, uint32_t(j) < rounds ? xcol + 2u * (kcol + 16u * j) : kNowhere, 0, 0);
+        for (int j = 0; j < (NT == 1 ? PF : 0); ++j) {
+            uint32_t at = uint32_t(j) < rounds ? xbase : kFar;
+            asm volatile("" : "+v"(at));
+            XP[j] = __builtin_amdgcn_raw_buffer_load_b128(xr, at + 32u * j, 0, 0);
+        }
         // the next block: this item's next, or the first of the next item
         const bool same = b + 1u < cur.b1;
         const bool more = same || cur.q + qstep < qend;
