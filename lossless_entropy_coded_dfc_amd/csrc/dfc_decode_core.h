@@ -58,6 +58,12 @@ struct Tables {
 
 __device__ __forceinline__ uint32_t lo16(uint32_t a) { return a & 0xFFFFu; }
 
+// After a word's whole-window lookups: lo16(acc) >= kBias - 2048 unless the
+// code at the current position is longer than the window.  Written with a
+// shift rather than lo16, so that the compiler can fold the loop test's own
+// low-half mask into its comparison.
+__device__ __forceinline__ bool no_escape(uint32_t acc) { return (acc << 16) >= ((kBias - 2048u) << 16); }
+
 // Codes longer than the first-level window: the smallest length l with
 // window < limit[l] (left-justified 24-bit comparison), then the symbol by
 // canonical rank.  Returns the length; sym receives the rotated exponent.
@@ -175,7 +181,7 @@ __device__ __forceinline__ uint32_t count_codes(const Chunk<C> &ck, int start, i
                 const uint32_t win = __builtin_amdgcn_alignbit(hi, lo, acc);
                 acc += t.step[win >> t.kshift];
             }
-            if (lo16(acc) >= kBias - 2048u) break;
+            if (no_escape(acc)) break;
             // escape: the code at pos is longer than the window
             acc += 0x1000u;
             uint32_t sym;
@@ -255,7 +261,7 @@ __device__ __forceinline__ uint32_t write_codes(const Chunk<C> &ck, int start, i
                 or_4_bytes(q0 + (acc >> 16), e.x);
                 acc += e.y;
             }
-            if (lo16(acc) >= kBias - 2048u) break;
+            if (no_escape(acc)) break;
             acc += 0x1000u;
             uint32_t sym;
             const uint32_t win = __builtin_amdgcn_alignbit(hi, lo, acc);
@@ -295,7 +301,7 @@ __device__ __forceinline__ uint32_t count_codes_padded(const Chunk<C> &ck, int e
                 const uint32_t win = __builtin_amdgcn_alignbit(hi, lo, acc);
                 acc += t.step[win >> t.kshift];
             }
-            if (lo16(acc) >= kBias - 2048u) break;
+            if (no_escape(acc)) break;
             acc += 0x1000u;
             uint32_t sym;
             const uint32_t win = __builtin_amdgcn_alignbit(hi, lo, acc);
@@ -339,7 +345,7 @@ __device__ __forceinline__ void write_codes_padded(const Chunk<C> &ck, int end, 
                 or_4_bytes(q0 + (acc >> 16), e.x);
                 acc += e.y;
             }
-            if (lo16(acc) >= kBias - 2048u) break;
+            if (no_escape(acc)) break;
             acc += 0x1000u;
             uint32_t sym;
             const uint32_t win = __builtin_amdgcn_alignbit(hi, lo, acc);

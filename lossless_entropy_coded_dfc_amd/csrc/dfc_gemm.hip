@@ -254,7 +254,7 @@ __device__ __forceinline__ bool gemm_items(const GemmArgs &g, uint32_t q0, uint3
         // products, so that their cache round trips overlap.
         const uint32_t extent = lead + total;
         // (equal to `rounds` here; kept opaque so that the compiler does not
-        // hold the prefetch's eight conditions in registers across the write
+        // hold the prefetch's conditions in registers across the write
         // pass to reuse them)
         uint32_t nfull = extent >> 9;
         asm volatile("" : "+s"(nfull));
