@@ -117,6 +117,17 @@ def test_constant_and_special_values():
     check(x, 8, label="specials")
 
 
+@pytest.mark.parametrize("C", [16, 32])
+def test_one_bit_codes(C):
+    """Two equally likely exponents (126, 127): one-bit codes, the most
+    values a block can hold (512 C), so the largest staging areas, store
+    runs and raw-byte rounds past the prefetched ones."""
+    u = synth.uniform_bits((64, 16384), (41, C))
+    x = (u & np.uint16(0x807F)) | ((np.uint16(126) + ((u >> np.uint16(7)) & np.uint16(1))) << np.uint16(7))
+    blob = check(x, C, k=11, label=f"one-bit codes C={C}")
+    assert dfc.blob_info(blob).max_block_elems == 512 * C
+
+
 def test_long_codes_everywhere():
     """Uniform data under a codebook trained on Gaussian weights: most codes
     are longer than the first-level table (slow path on every lane)."""

@@ -166,6 +166,26 @@ def test_stress_distributions(kind):
     assert np.array_equal(y, w_as_f32(w)[:, :64].T)
 
 
+@pytest.mark.parametrize("C", [16, 32])
+def test_one_bit_codes_fill_whole_blocks(C):
+    """Two equally likely exponents (126 and 127): every code is one bit, so
+    a block of 64 chunks holds 512 C values and completes up to C sub-tiles,
+    more than the kernel prefetches (7 at C = 16, 10 at C = 32): the rest
+    load when used.  At C = 32 the staging areas are large enough that fewer
+    than 8 wavefronts fit a workgroup."""
+    M, K = 64, 4096
+    u = synth.uniform_bits((M, K), (98, C))
+    w = (u & np.uint16(0x807F)) | ((np.uint16(126) + ((u >> np.uint16(7)) & np.uint16(1))) << np.uint16(7))
+    dev, info, _ = upload(w, C=C)
+    assert info.max_block_elems > 512 * (7 if C == 16 else 10)
+    say("case one-bit codes C", C)
+    for c0 in (0, K - 64):
+        cols = list(range(c0, c0 + 64))
+        assert np.array_equal(run(dev, info, unit_vectors(K, cols)), w_as_f32(w)[:, cols].T)
+    x = synth.gaussian((16, K), 1.0, (99, C))
+    check_product(w, x, run(dev, info, x))
+
+
 def test_oracle_written_container():
     w = synth.gaussian((64, 256), 0.02, (87,))
     blob = pn.write_panel_blob(pn.encode_panel(w, panel_k=128, chunk_bytes=16), 11)
