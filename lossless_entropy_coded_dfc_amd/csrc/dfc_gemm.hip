@@ -112,12 +112,17 @@ __device__ __forceinline__ uint32_t load_count(const __amdgpu_buffer_rsrc_t &cr,
 // rows past B read as zeros), that is 32 pieces of 32 bytes, one per vector;
 // from the packed copy (pack_x_kernel), one run of 1 KB.
 template <int NT, bool XPACK>
+__device__ __forceinline__ uint32_t x_offset(uint32_t xcol, uint32_t cols, uint32_t k, int nt, uint32_t lane) {
+    if constexpr (XPACK)
+        return (((k >> 4) * NT + uint32_t(nt)) * 64u + lane) * 16u;
+    else
+        return xcol + 2u * (32u * uint32_t(nt) * cols + k);
+}
+
+template <int NT, bool XPACK>
 __device__ __forceinline__ u32x4 load_x(const __amdgpu_buffer_rsrc_t &xr, uint32_t xcol, uint32_t cols, uint32_t k,
                                         int nt, uint32_t lane) {
-    if constexpr (XPACK)
-        return __builtin_amdgcn_raw_buffer_load_b128(xr, (((k >> 4) * NT + uint32_t(nt)) * 64u + lane) * 16u, 0, 0);
-    else
-        return __builtin_amdgcn_raw_buffer_load_b128(xr, xcol + 2u * (32u * uint32_t(nt) * cols + k), 0, 0);
+    return __builtin_amdgcn_raw_buffer_load_b128(xr, x_offset<NT, XPACK>(xcol, cols, k, nt, lane), 0, 0);
 }
 
 // X copied in the order load_x reads it: 16-byte unit ((k / 16) NT + nt)
@@ -187,8 +192,11 @@ __device__ __forceinline__ bool gemm_items(const GemmArgs &g, uint32_t q0, uint3
             asm volatile("" : "+v"(at));
             R[j] = __builtin_amdgcn_raw_buffer_load_b64(raw, at + 512u * j, 0, kLoadNT);
         }
-        // With one column tile, the X fragments of those sub-tiles too: their
-        // cache round trips then overlap the decoding instead of each product.
+        // The X fragments of those sub-tiles too, so that their cache round
+        // trips overlap the decoding instead of each product: all of them
+        // with one column tile, those of the first XQ sub-tiles (every
+        // column tile) with more, up to 16-byte chunks (the registers allow
+        // no more).
         const uint32_t xbase = xcol + 2u * kcol;
         u32x4 XP[NT == 1 ? PF : 1];
 #pragma unroll
@@ -197,6 +205,14 @@ __device__ __forceinline__ bool gemm_items(const GemmArgs &g, uint32_t q0, uint3
             asm volatile("" : "+v"(at));
             XP[j] = __builtin_amdgcn_raw_buffer_load_b128(xr, at + 32u * j, 0, 0);
         }
+        constexpr int XQ = NT > 1 && C <= 16 ? 2 : 0;
+        u32x4 XQP[XQ > 0 ? XQ : 1][NT];
+#pragma unroll
+        for (int j = 0; j < XQ; ++j)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                XQP[j][nt] = __builtin_amdgcn_raw_buffer_load_b128(
+                    xr, uint32_t(j) < rounds ? x_offset<NT, XPACK>(xcol, g.cols, kcol + 16u * j, nt, lane) : kFar, 0, 0);
         // the next block: this item's next, or the first of the next item
         const bool same = b + 1u < cur.b1;
         const bool more = same || cur.q + qstep < qend;
@@ -268,6 +284,8 @@ __device__ __forceinline__ bool gemm_items(const GemmArgs &g, uint32_t q0, uint3
                 for (int nt = 0; nt < NT; ++nt) {
                     if constexpr (NT == 1)
                         X[nt] = XP[j];
+                    else if (j < XQ)
+                        X[nt] = XQP[j < XQ ? j : 0][nt];
                     else
                         X[nt] = load_x<NT, XPACK>(xr, xcol, g.cols, kcol + 16u * j, nt, lane);
                 }
