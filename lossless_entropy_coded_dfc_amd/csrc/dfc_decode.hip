@@ -86,11 +86,12 @@ struct Prefetch {
 };
 
 // Wavefronts per SIMD the register budget is sized for (512 VGPRs per lane
-// shared by the resident wavefronts): 64 VGPRs give 8, the 32-byte chunk
-// path needs more registers and settles for 5.
+// shared by the resident wavefronts): 4, 128 VGPRs.  The decoder runs as
+// fast with 4 as with 8 (it is held by the memory path, not by latency), and
+// the registers hold the assembled rounds whose stores are deferred (below).
 template <int C>
 struct Occupancy {
-    static constexpr int kWavesPerSimd = C >= 32 ? 5 : 8;
+    static constexpr int kWavesPerSimd = 4;
 };
 
 // Output rounds.  A wavefront decodes a contiguous run of blocks and writes
@@ -98,7 +99,8 @@ struct Occupancy {
 // lane) aligned to multiples of 512 in the output: a block's exponents are
 // staged in LDS behind the values still pending from the blocks before it
 // (fewer than 512, kept in registers in between), every complete round is
-// merged with its raw bytes and stored, and the rest is carried on.  Only
+// merged with its raw bytes and stored (the first few during the next
+// block's write pass), and the rest is carried on.  Only
 // the first and last round of a run can be partial; values outside the
 // run's [lo, hi) are not written (an octet cut by lo or hi goes out with
 // 16-bit stores).
@@ -189,6 +191,15 @@ __global__ __launch_bounds__(1024, Occupancy<C>::kWavesPerSimd) void dfc_decode_
     // belong to another run; the carry holds [base, s_out)
     uint32_t base = s_out & ~(kRound - 1u), lo = s_out;
     u32x2 carry = {0u, 0u};
+    // Deferred stores: the first DEF complete rounds of a block are assembled
+    // into registers and stored during the next block's write pass, one per
+    // stream word, so that the wavefront's stores are spread over its decode
+    // instead of leaving in one burst (O[j] is round pbase + 512 j; npend
+    // of them are pending, the first only if it was not an edge round).
+    constexpr int DEF = C >= 32 ? 2 : (C / 4 + 1 < Prefetch<C>::N ? C / 4 + 1 : Prefetch<C>::N);
+    u32x4 O[DEF];
+    uint32_t pbase = 0, npend = 0;
+    bool pfirst_edge = false;
     for (;;) {
         // the block index is the same in every lane
         b = __builtin_amdgcn_readfirstlane(b);
@@ -243,16 +254,29 @@ __global__ __launch_bounds__(1024, Occupancy<C>::kWavesPerSimd) void dfc_decode_
         // A chunk of 8C bits holds at most 8C code starts; anything else (or
         // a total that disagrees with the block offsets) means a corrupt stream.
         const bool bad = (total != want) | (__builtin_amdgcn_ballot_w64(cnt > 8u * C) != 0);
-        if (!bad && cnt) {
-            if constexpr (Padded)
-                write_codes_padded<C>(cur, end, cnt, stage_addr + lead + (incl - cnt), t);
-            else
-                write_codes<C>(cur, start, end, stage_addr + lead + (incl - cnt), t);
-        }
         // Everything prefetched must be in registers before the first store,
         // on every path to the next block.
         wait_for(R);
         wait_for(nxt);
+        // The previous block's deferred rounds go out during this block's
+        // write pass, after its loads have arrived (a store issued before
+        // them would make their wait include the store).  Every lane runs
+        // the write pass (a lane without codes does no lookup), since every
+        // lane stores its octet of each round.
+        auto hook = [&](int w) {
+            if (uint32_t(w) < npend && (w > 0 || !pfirst_edge))
+                __builtin_amdgcn_raw_buffer_store_b128(O[w < DEF ? w : 0], bf.dst,
+                                                       2u * (pbase + kRound * uint32_t(w) + 8u * lane), 0, 0);
+        };
+        if (!bad) {
+            if constexpr (Padded)
+                write_codes_padded<C>(cur, end, cnt, stage_addr + lead + (incl - cnt), t, hook);
+            else
+                write_codes<C>(cur, start, end, stage_addr + lead + (incl - cnt), t, hook);
+        } else {
+            for (int w = 0; w <= C / 4; ++w) hook(w);
+        }
+        npend = 0;
         __builtin_amdgcn_s_setprio(0);
         if (bad) {
             // the block stays unwritten: store what is pending before it and
@@ -266,14 +290,23 @@ __global__ __launch_bounds__(1024, Occupancy<C>::kWavesPerSimd) void dfc_decode_
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            // complete rounds; only the first round of a run can start below lo
+            // complete rounds, kept for the next block's write pass to store
+            // (the first round of a run, which can start below lo, goes out now)
+            pfirst_edge = base < lo;
 #pragma unroll
             for (int j = 0; j < PF; ++j) {
                 if (uint32_t(j) < rounds) {
                     const u32x2 E = *reinterpret_cast<const u32x2 *>(stage + kRound * j + 8u * lane);
-                    store_round(bf, base + kRound * j, lane, E, R[j], base + kRound * j < lo, lo, e_out);
+                    if (j == 0 && pfirst_edge)
+                        store_round(bf, base, lane, E, R[0], true, lo, e_out);
+                    else if (j < DEF)
+                        O[j < DEF ? j : 0] = assemble8(E, R[j]);
+                    else
+                        store_round(bf, base + kRound * j, lane, E, R[j], false, lo, e_out);
                 }
             }
+            pbase = base;
+            npend = min(rounds, uint32_t(DEF));
             for (uint32_t j = PF; j < rounds; ++j) {
                 const u32x2 Rj = load_raw_octet(bf, base + kRound * j, lane, lo, e_out);
                 const u32x2 E = *reinterpret_cast<const u32x2 *>(stage + kRound * j + 8u * lane);
@@ -290,6 +323,8 @@ __global__ __launch_bounds__(1024, Occupancy<C>::kWavesPerSimd) void dfc_decode_
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         if (!more) {
+#pragma unroll
+            for (int w = 0; w < DEF; ++w) hook(w);
             flush_round(bf, base, lane, carry, lo, e_out);
             break;
         }

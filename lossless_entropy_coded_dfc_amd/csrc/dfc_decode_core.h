@@ -239,9 +239,13 @@ __device__ __forceinline__ void or_4_bytes(uint32_t q, uint32_t v) {
 // exponent to three codes.  Returns the number of codes that start in
 // [start, end), as count_codes does (callers that take their positions
 // from stored counts check them with it; for the others it is dead code).
-template <int C>
+struct NoHook {
+    __device__ __forceinline__ void operator()(int) const {}
+};
+
+template <int C, typename Hook = NoHook>
 __device__ __forceinline__ uint32_t write_codes(const Chunk<C> &ck, int start, int end, uint32_t q0,
-                                                const Tables &t) {
+                                                const Tables &t, const Hook &hook = Hook()) {
     constexpr int NW = C / 4;
     // the boundary mask at `end`, looked up first so that the stream words
     // need not outlive the loop
@@ -270,6 +274,7 @@ __device__ __forceinline__ uint32_t write_codes(const Chunk<C> &ck, int start, i
             acc += 0x10000u - l;
         }
         acc += 32u;
+        hook(k + 1);
     }
     uint32_t cnt = acc >> 16;
     const int pos = 32 * (NW + 1) - int(lo16(acc)) + int(kBias);
@@ -326,9 +331,9 @@ __device__ __forceinline__ uint32_t count_codes_padded(const Chunk<C> &ck, int e
 // no cut (their codes end by `end`); a long code is written only if it is
 // one of the cnt; the last few codes go out with their entry cut to the
 // codes still owed.
-template <int C>
+template <int C, typename Hook = NoHook>
 __device__ __forceinline__ void write_codes_padded(const Chunk<C> &ck, int end, uint32_t cnt, uint32_t q0,
-                                                   const Tables &t) {
+                                                   const Tables &t, const Hook &hook = Hook()) {
     constexpr int NW = C / 4;
     const int stop = end - int(t.kb) + 1;
     uint32_t acc = kBias;
@@ -354,6 +359,7 @@ __device__ __forceinline__ void write_codes_padded(const Chunk<C> &ck, int end, 
             acc += 0x10000u - l;
         }
         acc += 32u;
+        hook(k + 1);
     }
     // (done << 16) + kBias - pos, advanced by the symbol entries' steps.  The
     // codes owed end within k - 1 <= 11 bits, so three entries hold them.
