@@ -21,6 +21,7 @@ __all__ = [
     "DfcError", "DfcLibraryMissing", "Params", "Codebook", "Info", "BatchItem",
     "library", "library_path", "default_params", "histogram", "build_codebook",
     "encode_bound", "encode", "blob_info", "decode", "decode_batch", "set_launch",
+    "STORES_AUTO", "STORES_DEFERRED", "STORES_IMMEDIATE",
     "status_str", "MAX_BATCH", "derived_tables_bytes", "derive_tables",
 ]
 
@@ -147,7 +148,7 @@ def library():
     lib.dfc_derive_tables.argtypes = [ctypes.c_void_p, ctypes.POINTER(Info), ctypes.c_uint32, ctypes.c_void_p,
                                       ctypes.c_uint64, ctypes.c_void_p]
     lib.dfc_derive_tables.restype = st
-    lib.dfc_set_launch.argtypes = [ctypes.c_uint32, ctypes.c_uint32]
+    lib.dfc_set_launch.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32]
     lib.dfc_set_launch.restype = st
     lib.dfc_status_str.argtypes = [ctypes.c_int]
     lib.dfc_status_str.restype = ctypes.c_char_p
@@ -427,5 +428,8 @@ def derive_tables(blob_dev, info: Info, threads: int = 0, stream=None):
     return out
 
 
-def set_launch(waves_per_group: int = 0, blocks_per_wave: int = 0):
-    _check(library().dfc_set_launch(waves_per_group, blocks_per_wave), "dfc_set_launch")
+STORES_AUTO, STORES_DEFERRED, STORES_IMMEDIATE = 0, 1, 2
+
+
+def set_launch(waves_per_group: int = 0, blocks_per_wave: int = 0, stores: int = STORES_AUTO):
+    _check(library().dfc_set_launch(waves_per_group, blocks_per_wave, stores), "dfc_set_launch")

@@ -86,12 +86,15 @@ struct Prefetch {
 };
 
 // Wavefronts per SIMD the register budget is sized for (512 VGPRs per lane
-// shared by the resident wavefronts): 4, 128 VGPRs.  The decoder runs as
-// fast with 4 as with 8 (it is held by the memory path, not by latency), and
-// the registers hold the assembled rounds whose stores are deferred (below).
-template <int C>
+// shared by the resident wavefronts).  With deferred stores (below) the
+// assembled rounds held in registers take it to 128 VGPRs and 4 wavefronts,
+// which decode a large job as fast as 8 do (the decoder is held by the memory
+// path, not by latency); without them 64 VGPRs give 8 (the 32-byte chunk path
+// needs more and settles for 5), which finish a job of about one block per
+// wavefront sooner, since each wavefront then has less to do in sequence.
+template <int C, bool Defer>
 struct Occupancy {
-    static constexpr int kWavesPerSimd = 4;
+    static constexpr int kWavesPerSimd = Defer ? 4 : (C >= 32 ? 5 : 8);
 };
 
 // Output rounds.  A wavefront decodes a contiguous run of blocks and writes
@@ -146,8 +149,8 @@ __device__ __forceinline__ void flush_round(const Buffers &bf, uint32_t base, ui
     store_round(bf, base, lane, carry, R, true, lo, hi);
 }
 
-template <int C, bool Padded>
-__global__ __launch_bounds__(1024, Occupancy<C>::kWavesPerSimd) void dfc_decode_kernel(const BatchArgs args) {
+template <int C, bool Padded, bool Defer>
+__global__ __launch_bounds__(1024, (Occupancy<C, Defer>::kWavesPerSimd)) void dfc_decode_kernel(const BatchArgs args) {
     extern __shared__ __align__(16) uint8_t lds[];
     constexpr int PF = Prefetch<C>::N;
     const uint32_t wg = blockIdx.x;
@@ -196,8 +199,9 @@ __global__ __launch_bounds__(1024, Occupancy<C>::kWavesPerSimd) void dfc_decode_
     // stream word, so that the wavefront's stores are spread over its decode
     // instead of leaving in one burst (O[j] is round pbase + 512 j; npend
     // of them are pending, the first only if it was not an edge round).
-    constexpr int DEF = C >= 32 ? 2 : (C / 4 + 1 < Prefetch<C>::N ? C / 4 + 1 : Prefetch<C>::N);
-    u32x4 O[DEF];
+    // Without Defer, DEF is 0 and every round is stored when assembled.
+    constexpr int DEF = !Defer ? 0 : C >= 32 ? 2 : (C / 4 + 1 < Prefetch<C>::N ? C / 4 + 1 : Prefetch<C>::N);
+    u32x4 O[DEF > 0 ? DEF : 1];
     uint32_t pbase = 0, npend = 0;
     bool pfirst_edge = false;
     for (;;) {
@@ -254,10 +258,6 @@ __global__ __launch_bounds__(1024, Occupancy<C>::kWavesPerSimd) void dfc_decode_
         // A chunk of 8C bits holds at most 8C code starts; anything else (or
         // a total that disagrees with the block offsets) means a corrupt stream.
         const bool bad = (total != want) | (__builtin_amdgcn_ballot_w64(cnt > 8u * C) != 0);
-        // Everything prefetched must be in registers before the first store,
-        // on every path to the next block.
-        wait_for(R);
-        wait_for(nxt);
         // The previous block's deferred rounds go out during this block's
         // write pass, after its loads have arrived (a store issued before
         // them would make their wait include the store).  Every lane runs
@@ -268,13 +268,29 @@ __global__ __launch_bounds__(1024, Occupancy<C>::kWavesPerSimd) void dfc_decode_
                 __builtin_amdgcn_raw_buffer_store_b128(O[w < DEF ? w : 0], bf.dst,
                                                        2u * (pbase + kRound * uint32_t(w) + 8u * lane), 0, 0);
         };
-        if (!bad) {
-            if constexpr (Padded)
-                write_codes_padded<C>(cur, end, cnt, stage_addr + lead + (incl - cnt), t, hook);
-            else
-                write_codes<C>(cur, start, end, stage_addr + lead + (incl - cnt), t, hook);
+        if constexpr (Defer) {
+            // Everything prefetched must be in registers before the first
+            // store, on every path to the next block.
+            wait_for(R);
+            wait_for(nxt);
+            if (!bad) {
+                if constexpr (Padded)
+                    write_codes_padded<C>(cur, end, cnt, stage_addr + lead + (incl - cnt), t, hook);
+                else
+                    write_codes<C>(cur, start, end, stage_addr + lead + (incl - cnt), t, hook);
+            } else {
+                for (int w = 0; w <= C / 4; ++w) hook(w);
+            }
         } else {
-            for (int w = 0; w <= C / 4; ++w) hook(w);
+            // no stores in the write pass: the loads stay in flight during it
+            if (!bad && cnt) {
+                if constexpr (Padded)
+                    write_codes_padded<C>(cur, end, cnt, stage_addr + lead + (incl - cnt), t);
+                else
+                    write_codes<C>(cur, start, end, stage_addr + lead + (incl - cnt), t);
+            }
+            wait_for(R);
+            wait_for(nxt);
         }
         npend = 0;
         __builtin_amdgcn_s_setprio(0);
@@ -349,7 +365,7 @@ __global__ __launch_bounds__(1024) void derive_tables_kernel(const uint8_t *leng
 
 // Set by dfc_set_launch, read by every launch (possibly on other threads).
 struct LaunchCfg {
-    std::atomic<uint32_t> waves{0}, blocks_per_wave{0};
+    std::atomic<uint32_t> waves{0}, blocks_per_wave{0}, stores{0};
 } g_launch;
 
 // Split `slots` workgroups across items so that the largest per-workgroup
@@ -370,40 +386,51 @@ std::vector<uint32_t> share_workgroups(const std::vector<uint64_t> &blocks, uint
     return g;
 }
 
-template <int C, bool Padded>
-dfc_status launch_group(const dfc_batch_item *items, const uint32_t *idx, uint32_t count, uint32_t *status,
-                        hipStream_t stream) {
-    BatchArgs args;
-    std::memset(&args, 0, sizeof(args));
+// The launch geometry of one build of the decoder for a group of items: the
+// workgroup shape and LDS, each item's workgroups, and the most blocks any
+// wavefront decodes in sequence (the launch's critical path).
+struct Plan {
+    uint32_t waves = 0, lds = 0, stage = 0;
+    std::vector<uint32_t> live, g;
+    uint64_t crit = 0;
+};
+
+template <int C, bool Padded, bool Defer>
+dfc_status plan_group(const dfc_batch_item *items, const uint32_t *idx, uint32_t count, Plan &pl) {
     uint32_t max_tables = 0, max_block = 0, max_scratch = 0;
     std::vector<uint64_t> blocks;
-    std::vector<uint32_t> live;
     for (uint32_t k = 0; k < count; ++k) {
         const dfc_info &in = *items[idx[k]].info;
         if (in.n_blocks == 0) continue;
-        live.push_back(idx[k]);
+        pl.live.push_back(idx[k]);
         blocks.push_back(in.n_blocks);
         max_tables = std::max<uint32_t>(max_tables, uint32_t(dfc::tables_bytes(in.lut_bits)));
         if (!items[idx[k]].tables_dev) max_scratch = std::max<uint32_t>(max_scratch, derive_scratch_bytes(in.lut_bits));
         max_block = std::max(max_block, in.max_block_elems);
     }
-    if (live.empty()) return DFC_OK;
+    if (pl.live.empty()) return DFC_OK;
+    const void *kernel = reinterpret_cast<const void *>(&dfc_decode_kernel<C, Padded, Defer>);
     // staging: pending values of the round in progress (< 512) + the block's
     // values + the spill of its last lookup, rounded to 16
     const uint32_t stage = (511u + max_block + 32u + 15u) & ~15u;
-    if (!allow_full_lds(reinterpret_cast<const void *>(&dfc_decode_kernel<C, Padded>))) return DFC_EHIP;
+    if (!allow_full_lds(kernel)) return DFC_EHIP;
     // LDS of a workgroup of w wavefronts: the tables, then the staging
     // areas, which hold the derivation's scratch before the first block.
     auto lds_for = [&](uint32_t w) { return max_tables + std::max(w * stage, max_scratch); };
     // Resident workgroups per CU for w wavefronts each, under both the LDS
     // and the register budget.
+    // The answer for the last LDS size asked is kept per workgroup shape
+    // ((LDS << 32) | (count + 1), 0 = none), since every launch asks again.
+    static std::atomic<uint64_t> memo[kMaxWaves + 1];
     auto resident = [&](uint32_t w) -> int {
         const uint32_t lds = lds_for(w);
         if (lds > kLdsBytes) return 0;
+        const uint64_t m = memo[w].load(std::memory_order_relaxed);
+        if (m && uint32_t(m >> 32) == lds) return int(uint32_t(m)) - 1;
         int per_cu = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(&dfc_decode_kernel<C, Padded>),
-                                                         int(w * kWave), size_t(lds)) != hipSuccess)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, int(w * kWave), size_t(lds)) != hipSuccess)
             per_cu = int(kLdsBytes / lds);
+        memo[w].store((uint64_t(lds) << 32) | uint32_t(per_cu + 1), std::memory_order_relaxed);
         return per_cu;
     };
     // waves per workgroup: the most resident wavefronts per CU, then the
@@ -422,8 +449,7 @@ dfc_status launch_group(const dfc_batch_item *items, const uint32_t *idx, uint32
     }
     if (!waves) waves = 1;
     while (waves > 1 && lds_for(waves) > kLdsBytes) --waves;
-    const uint32_t lds = lds_for(waves);
-    if (lds > kLdsBytes) return DFC_EUNSUPPORTED;
+    if (lds_for(waves) > kLdsBytes) return DFC_EUNSUPPORTED;
     int per_cu = resident(waves);
     if (per_cu <= 0) per_cu = 1;
     uint64_t slots = uint64_t(per_cu) * uint64_t(device_cu_count());
@@ -433,11 +459,30 @@ dfc_status launch_group(const dfc_batch_item *items, const uint32_t *idx, uint32
         for (uint64_t nb : blocks) total += dfc::ceil_div(nb, uint64_t(waves) * blocks_per_wave);
         slots = total;
     }
-    const std::vector<uint32_t> g =
-        share_workgroups(blocks, std::max<uint64_t>(slots, live.size()), waves);
+    pl.g = share_workgroups(blocks, std::max<uint64_t>(slots, pl.live.size()), waves);
+    pl.waves = waves;
+    pl.lds = lds_for(waves);
+    pl.stage = stage;
+    // Workgroups beyond what the machine holds at once run after others
+    // finish: count them as further blocks in sequence.
+    uint64_t wgs = 0;
+    for (size_t k = 0; k < blocks.size(); ++k) {
+        const uint64_t per_wg = dfc::ceil_div(blocks[k], uint64_t(pl.g[k]));
+        pl.crit = std::max(pl.crit, dfc::ceil_div(per_wg, uint64_t(waves)));
+        wgs += dfc::ceil_div(blocks[k], per_wg);
+    }
+    pl.crit *= dfc::ceil_div(wgs, uint64_t(per_cu) * uint64_t(device_cu_count()));
+    return DFC_OK;
+}
+
+template <int C, bool Padded, bool Defer>
+dfc_status launch_planned(const dfc_batch_item *items, const Plan &pl, uint32_t *status, hipStream_t stream) {
+    if (pl.live.empty()) return DFC_OK;
+    BatchArgs args;
+    std::memset(&args, 0, sizeof(args));
     uint32_t wg = 0;
-    for (size_t k = 0; k < live.size(); ++k) {
-        const dfc_batch_item &bi = items[live[k]];
+    for (size_t k = 0; k < pl.live.size(); ++k) {
+        const dfc_batch_item &bi = items[pl.live[k]];
         const dfc_info &in = *bi.info;
         const uint8_t *base = static_cast<const uint8_t *>(bi.blob_dev);
         ItemArgs &a = args.item[k];
@@ -454,17 +499,44 @@ dfc_status launch_group(const dfc_batch_item *items, const uint32_t *idx, uint32
         a.dst_bytes = uint32_t(2 * in.n);
         a.total_bits = in.total_bits;
         a.n_blocks = uint32_t(in.n_blocks);
-        a.blocks_per_wg = uint32_t(dfc::ceil_div(in.n_blocks, g[k]));
+        a.blocks_per_wg = uint32_t(dfc::ceil_div(in.n_blocks, pl.g[k]));
         a.wg_begin = wg;
         a.tables_bytes = uint32_t(dfc::tables_bytes(in.lut_bits));
         a.lut_bits = in.lut_bits;
         wg += uint32_t(dfc::ceil_div(in.n_blocks, a.blocks_per_wg));
     }
-    args.count = uint32_t(live.size());
-    args.stage_bytes = stage;
+    args.count = uint32_t(pl.live.size());
+    args.stage_bytes = pl.stage;
     args.status = status;
-    dfc_decode_kernel<C, Padded><<<dim3(wg), dim3(waves * kWave), lds, stream>>>(args);
+    dfc_decode_kernel<C, Padded, Defer><<<dim3(wg), dim3(pl.waves * kWave), pl.lds, stream>>>(args);
     return hipGetLastError() == hipSuccess ? DFC_OK : DFC_EHIP;
+}
+
+// One launch for a group of items of one chunk size and layout.  Deferred
+// stores hold a wavefront to 4 per SIMD, the immediate build runs up to 8, so
+// on a job of a block or two per wavefront the deferred build can leave a
+// wavefront twice the blocks in sequence; it is used unless that happens
+// (with the flat layout a longer path that is not twice as long still
+// finishes sooner) or, with the padded layout, unless the immediate build's
+// wavefronts have fewer than 6 blocks each in sequence (padded decoding of
+// short jobs runs faster with more wavefronts).
+template <int C, bool Padded>
+dfc_status launch_group(const dfc_batch_item *items, const uint32_t *idx, uint32_t count, uint32_t *status,
+                        hipStream_t stream) {
+    const uint32_t mode = g_launch.stores.load(std::memory_order_relaxed);
+    Plan pd;
+    if (mode != DFC_STORES_IMMEDIATE) {
+        const dfc_status s = plan_group<C, Padded, true>(items, idx, count, pd);
+        if (s != DFC_OK) return s;
+        if (mode == DFC_STORES_DEFERRED) return launch_planned<C, Padded, true>(items, pd, status, stream);
+    }
+    Plan pi;
+    const dfc_status s = plan_group<C, Padded, false>(items, idx, count, pi);
+    if (s != DFC_OK) return s;
+    constexpr uint64_t kMinCrit = Padded ? 6 : 0;
+    if (mode == DFC_STORES_AUTO && pd.crit < 2 * pi.crit && pi.crit >= kMinCrit)
+        return launch_planned<C, Padded, true>(items, pd, status, stream);
+    return launch_planned<C, Padded, false>(items, pi, status, stream);
 }
 
 dfc_status check_item(const dfc_batch_item &it) {
@@ -494,11 +566,13 @@ dfc_status check_item(const dfc_batch_item &it) {
 
 extern "C" {
 
-dfc_status dfc_set_launch(uint32_t waves_per_group, uint32_t blocks_per_wave) {
+dfc_status dfc_set_launch(uint32_t waves_per_group, uint32_t blocks_per_wave, uint32_t stores) {
     if (waves_per_group > kMaxWaves) return DFC_EINVAL;
     if (blocks_per_wave > 64) return DFC_EINVAL;
+    if (stores > DFC_STORES_IMMEDIATE) return DFC_EINVAL;
     g_launch.waves.store(waves_per_group, std::memory_order_relaxed);
     g_launch.blocks_per_wave.store(blocks_per_wave, std::memory_order_relaxed);
+    g_launch.stores.store(stores, std::memory_order_relaxed);
     return DFC_OK;
 }
 

@@ -25,12 +25,22 @@ def say(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-@pytest.fixture(scope="module", autouse=True)
-def _device():
+# Every test runs twice: with each block's first complete rounds stored
+# during the next block's decode, and with every round stored at once (the
+# decoder picks one by job size; these inputs are small enough that it would
+# always pick the second).
+MODE = {"stores": dfc.STORES_AUTO}
+
+
+@pytest.fixture(scope="module", autouse=True, params=[dfc.STORES_DEFERRED, dfc.STORES_IMMEDIATE],
+                ids=["deferred", "immediate"])
+def _device(request):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-    dfc.set_launch(0, 0)
+    MODE["stores"] = request.param
+    dfc.set_launch(0, 0, MODE["stores"])
     yield
+    MODE["stores"] = dfc.STORES_AUTO
     dfc.set_launch(0, 0)
 
 
@@ -153,12 +163,12 @@ def test_oracle_written_container_decodes():
 
 @pytest.mark.parametrize("waves,bpw", [(4, 1), (8, 1), (8, 3), (16, 2), (4, 16)])
 def test_launch_shapes(waves, bpw):
-    dfc.set_launch(waves, bpw)
+    dfc.set_launch(waves, bpw, MODE["stores"])
     try:
         x = synth.gaussian((700, 1024), 0.02, (51,))
         check(x, 16, oracle=False, label=f"launch {waves}x{bpw}")
     finally:
-        dfc.set_launch(0, 0)
+        dfc.set_launch(0, 0, MODE["stores"])
 
 
 def test_status_flags_count_mismatch():
@@ -462,7 +472,7 @@ def test_corrupt_block_leaves_the_rest_exact(layout, waves, bpw):
     ob = struct.unpack_from("<III", bytes(blob[o - 4: o + 8]))
     bad[o: o + 4] = np.frombuffer(struct.pack("<I", ob[1] + 1), dtype=np.uint8)
     binfo = dfc.blob_info(bad)
-    dfc.set_launch(waves, bpw)
+    dfc.set_launch(waves, bpw, MODE["stores"])
     try:
         dev = torch.from_numpy(bad).cuda()
         out = torch.full((int(info.n),), 0x7E7E, dtype=torch.int16, device="cuda")
@@ -470,7 +480,7 @@ def test_corrupt_block_leaves_the_rest_exact(layout, waves, bpw):
         dfc.decode(dev, binfo, out, status)
         torch.cuda.synchronize()
     finally:
-        dfc.set_launch(0, 0)
+        dfc.set_launch(0, 0, MODE["stores"])
     got = out.cpu().numpy().view(np.uint16)
     assert int(status.item()) == dfc.ECORRUPT
     lo, hi = ob[0], ob[2]   # blocks b - 1 and b

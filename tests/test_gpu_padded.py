@@ -28,12 +28,22 @@ def say(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-@pytest.fixture(scope="module", autouse=True)
-def _device():
+# Every test runs twice: with each block's first complete rounds stored
+# during the next block's decode, and with every round stored at once (the
+# decoder picks one by job size; these inputs are small enough that it would
+# always pick the second).
+MODE = {"stores": dfc.STORES_AUTO}
+
+
+@pytest.fixture(scope="module", autouse=True, params=[dfc.STORES_DEFERRED, dfc.STORES_IMMEDIATE],
+                ids=["deferred", "immediate"])
+def _device(request):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-    dfc.set_launch(0, 0)
+    MODE["stores"] = request.param
+    dfc.set_launch(0, 0, MODE["stores"])
     yield
+    MODE["stores"] = dfc.STORES_AUTO
     dfc.set_launch(0, 0)
 
 
@@ -130,11 +140,11 @@ def test_mixed_layouts_and_chunk_sizes_in_one_batch():
 
 @pytest.mark.parametrize("waves,bpw", [(4, 1), (8, 3), (16, 2)])
 def test_launch_shapes(waves, bpw):
-    dfc.set_launch(waves, bpw)
+    dfc.set_launch(waves, bpw, MODE["stores"])
     try:
         check(synth.gaussian((512, 1024), 0.02, (79,)), 8, oracle=False, label=f"launch {waves}x{bpw}")
     finally:
-        dfc.set_launch(0, 0)
+        dfc.set_launch(0, 0, MODE["stores"])
 
 
 def test_status_flag_on_count_mismatch():

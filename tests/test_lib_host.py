@@ -77,6 +77,17 @@ def test_encoder_refuses_blocks_wider_than_a_wavefront(T, layout):
         dfc.encode_bound(x.size, dfc.default_params(lanes_per_block=T, layout=layout))
 
 
+def test_launch_knob_rejects_out_of_range_values():
+    """dfc_set_launch validates every field before it changes anything; no
+    GPU call is made."""
+    for bad in ((17, 0, 0), (0, 65, 0), (0, 0, 3)):
+        with pytest.raises(dfc.DfcError) as e:
+            dfc.set_launch(*bad)
+        assert e.value.status == dfc.EINVAL, bad
+    for mode in (dfc.STORES_DEFERRED, dfc.STORES_IMMEDIATE, dfc.STORES_AUTO):
+        dfc.set_launch(0, 0, mode)
+
+
 def test_edge_sizes_match_oracle():
     for n in (0, 1, 2, 15, 16, 17, 63, 64, 65, 1000):
         x = synth.uniform_bits((n,), (27, n))
