@@ -148,7 +148,7 @@ def library():
     lib.dfc_derive_tables.argtypes = [ctypes.c_void_p, ctypes.POINTER(Info), ctypes.c_uint32, ctypes.c_void_p,
                                       ctypes.c_uint64, ctypes.c_void_p]
     lib.dfc_derive_tables.restype = st
-    lib.dfc_set_launch.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32]
+    lib.dfc_set_launch.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32]
     lib.dfc_set_launch.restype = st
     lib.dfc_status_str.argtypes = [ctypes.c_int]
     lib.dfc_status_str.restype = ctypes.c_char_p
@@ -431,5 +431,5 @@ def derive_tables(blob_dev, info: Info, threads: int = 0, stream=None):
 STORES_AUTO, STORES_DEFERRED, STORES_IMMEDIATE = 0, 1, 2
 
 
-def set_launch(waves_per_group: int = 0, blocks_per_wave: int = 0, stores: int = STORES_AUTO):
-    _check(library().dfc_set_launch(waves_per_group, blocks_per_wave, stores), "dfc_set_launch")
+def set_launch(waves_per_group: int = 0, blocks_per_wave: int = 0, stores: int = STORES_AUTO, run_blocks: int = 0):
+    _check(library().dfc_set_launch(waves_per_group, blocks_per_wave, stores, run_blocks), "dfc_set_launch")

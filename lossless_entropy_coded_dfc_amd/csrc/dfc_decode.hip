@@ -19,11 +19,14 @@
 //
 // Work decomposition: one lane per chunk (C bytes of code stream), one
 // wavefront (64 lanes) per block of 64 chunks.  Workgroups are persistent:
-// the grid is sized to the resident capacity of the GPU, each workgroup owns
-// a contiguous run of blocks of one matrix, and each of its wavefronts a
-// contiguous share of that run, decoded block after block while the next
-// block's stream words, offsets and output range are in flight.  All
-// decoding is integer work on bit patterns.
+// the grid is sized to the resident capacity of the GPU and each matrix gets
+// a share of it.  A matrix's blocks are cut into runs of a few consecutive
+// blocks, dealt out to its V wavefronts in turn (wavefront v takes runs v,
+// v + V, v + 2V, ...), so that the wavefronts resident at one time read and
+// write neighbouring parts of the streams: memory serves that faster than as
+// many streams far apart.  A wavefront decodes block after block, within a
+// run and across runs, while the next block's stream words, offsets and
+// output range are in flight.  All decoding is integer work on bit patterns.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -51,10 +54,10 @@ struct ItemArgs {
     uint32_t words_bytes, offw_bytes, raw_bytes, dst_bytes;  // buffer ranges
     uint32_t n_blocks;
     uint32_t wg_begin;         // first workgroup of this item in the grid
-    uint32_t blocks_per_wg;
+    uint32_t wgs;              // workgroups of this item
     uint32_t tables_bytes;     // LDS image of the derived tables, a multiple of 16
     uint32_t lut_bits;
-    uint32_t pad;
+    uint32_t run;              // blocks per run (see the kernel)
 };
 
 struct Buffers {
@@ -167,12 +170,15 @@ __global__ __launch_bounds__(1024, (Occupancy<C, Defer>::kWavesPerSimd)) void df
     const uint32_t stage_off = a.tables_bytes + wave * args.stage_bytes;
     uint8_t *stage = lds + stage_off;
     const uint32_t stage_addr = lds_address(stage);  // its LDS address
-    // this wavefront's run: a contiguous share of the workgroup's blocks
-    const uint32_t lo_wg = (wg - a.wg_begin) * a.blocks_per_wg;
-    const uint32_t hi_wg = min(lo_wg + a.blocks_per_wg, a.n_blocks);
-    const uint32_t per = (hi_wg - min(lo_wg, hi_wg) + waves - 1u) / waves;
-    const uint32_t b_end = min(lo_wg + (wave + 1u) * per, hi_wg);
-    uint32_t b = lo_wg + wave * per;
+    // this wavefront's first run, [b, b_end), and the matrix's run count;
+    // runs go to the first wavefront of every workgroup, then to the
+    // second, ..., so that every workgroup gets an even share
+    const uint32_t run = a.run;
+    const uint32_t V = a.wgs * waves;
+    const uint32_t nruns = (a.n_blocks + run - 1u) / run;
+    uint32_t r = wave * a.wgs + (wg - a.wg_begin);
+    uint32_t b = min(r, nruns) * run;
+    uint32_t b_end = min(b + run, a.n_blocks);
 
     // The first block's stream words and output range are requested before
     // the tables are derived (the derivation's barriers wait for LDS only),
@@ -191,7 +197,8 @@ __global__ __launch_bounds__(1024, (Occupancy<C, Defer>::kWavesPerSimd)) void df
     wait_for(cur);
 
     // run state: rounds start at base (a multiple of 512); values below lo
-    // belong to another run; the carry holds [base, s_out)
+    // belong to another run; the carry holds [base, s_out).  Every run
+    // starts this way.
     uint32_t base = s_out & ~(kRound - 1u), lo = s_out;
     u32x2 carry = {0u, 0u};
     // Deferred stores: the first DEF complete rounds of a block are assembled
@@ -210,15 +217,24 @@ __global__ __launch_bounds__(1024, (Occupancy<C, Defer>::kWavesPerSimd)) void df
         const uint32_t lead = s_out - base;  // pending values, < 512
         const uint32_t want = e_out - s_out;
         const uint32_t rounds = (lead + want) / kRound;  // rounds this block completes
-        // raw bytes of those rounds (the first PF of them) per lane
-        // (rounds past them load nothing: their lanes' octets all lie
-        // outside [lo, 0), so no branch is needed around the loads)
+        // the next block: this run's next, or the first of the wavefront's next run
+        const bool in_run = b + 1u < b_end;
+        const uint32_t rn = in_run ? r : r + V;
+        const uint32_t bn = in_run ? b + 1u : min(rn, nruns) * run;
+        const bool more = in_run || rn < nruns;
+        // raw bytes of those rounds (the first PF of them) per lane, and at
+        // the end of a run those of its last, partial round; the loads of
+        // rounds past them are branched around (a load whose lanes all lie
+        // out of range would still take a slot in the address queue)
+        const uint32_t rounds_raw = rounds + (in_run ? 0u : 1u);
         u32x2 R[PF];
+        const uint32_t nraw = __builtin_amdgcn_readfirstlane(rounds_raw);
 #pragma unroll
-        for (int j = 0; j < PF; ++j) R[j] = load_raw_octet(bf, base + kRound * j, lane, lo, uint32_t(j) < rounds ? e_out : 0u);
+        for (int j = 0; j < PF; ++j) {
+            R[j] = u32x2{0u, 0u};
+            if (uint32_t(j) < nraw) R[j] = load_raw_octet(bf, base + kRound * j, lane, lo, e_out);
+        }
         // next block's stream words, offsets and output range
-        const uint32_t bn = b + 1u;
-        const bool more = bn < b_end;
         Chunk<C> nxt{};
         uint32_t s_nxt = 0, e_nxt = 0;
         if (more) {
@@ -333,6 +349,16 @@ __global__ __launch_bounds__(1024, (Occupancy<C, Defer>::kWavesPerSimd)) void df
             carry = 8u * lane < tail ? *reinterpret_cast<const u32x2 *>(stage + kRound * rounds + 8u * lane)
                                      : u32x2{0u, 0u};
             base += kRound * rounds;
+            if (!in_run && base < e_out) {
+                // the run ends inside this round: it goes out now, with the
+                // raw bytes loaded at the block's start
+                u32x2 Rt = {0u, 0u};
+#pragma unroll
+                for (int j = 0; j < PF; ++j)
+                    if (uint32_t(j) == rounds) Rt = R[j];
+                if (rounds >= uint32_t(PF)) Rt = load_raw_octet(bf, base, lane, lo, e_out);
+                store_round(bf, base, lane, carry, Rt, true, lo, e_out);
+            }
         }
         // The next block reuses this wavefront's staging area.
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -341,8 +367,17 @@ __global__ __launch_bounds__(1024, (Occupancy<C, Defer>::kWavesPerSimd)) void df
         if (!more) {
 #pragma unroll
             for (int w = 0; w < DEF; ++w) hook(w);
-            flush_round(bf, base, lane, carry, lo, e_out);
             break;
+        }
+        if (!in_run) {
+            // a new run: nothing pending in front of its first block (the
+            // deferred rounds of this block are complete and go out during
+            // the next block's write pass as usual)
+            r = rn;
+            b_end = min(bn + run, a.n_blocks);
+            base = s_nxt & ~(kRound - 1u);
+            lo = s_nxt;
+            carry = u32x2{0u, 0u};
         }
         cur = nxt;
         b = bn;
@@ -365,8 +400,16 @@ __global__ __launch_bounds__(1024) void derive_tables_kernel(const uint8_t *leng
 
 // Set by dfc_set_launch, read by every launch (possibly on other threads).
 struct LaunchCfg {
-    std::atomic<uint32_t> waves{0}, blocks_per_wave{0}, stores{0};
+    std::atomic<uint32_t> waves{0}, blocks_per_wave{0}, stores{0}, run{0};
 } g_launch;
+
+// Blocks per run when none is set: two once a matrix gives its wavefronts
+// at least 4 blocks each (the resident wavefronts then cover a stretch of
+// about 2V blocks of the streams at a time), else one, so that a small
+// matrix keeps every wavefront busy.
+uint32_t auto_run(uint64_t blocks, uint64_t wavefronts) {
+    return blocks >= 4u * wavefronts ? 2u : 1u;
+}
 
 // Split `slots` workgroups across items so that the largest per-workgroup
 // block count is as small as possible (each item gets at least one).
@@ -391,7 +434,7 @@ std::vector<uint32_t> share_workgroups(const std::vector<uint64_t> &blocks, uint
 // wavefront decodes in sequence (the launch's critical path).
 struct Plan {
     uint32_t waves = 0, lds = 0, stage = 0;
-    std::vector<uint32_t> live, g;
+    std::vector<uint32_t> live, g, run;
     uint64_t crit = 0;
 };
 
@@ -466,10 +509,15 @@ dfc_status plan_group(const dfc_batch_item *items, const uint32_t *idx, uint32_t
     // Workgroups beyond what the machine holds at once run after others
     // finish: count them as further blocks in sequence.
     uint64_t wgs = 0;
+    const uint32_t run_set = g_launch.run.load(std::memory_order_relaxed);
     for (size_t k = 0; k < blocks.size(); ++k) {
         const uint64_t per_wg = dfc::ceil_div(blocks[k], uint64_t(pl.g[k]));
-        pl.crit = std::max(pl.crit, dfc::ceil_div(per_wg, uint64_t(waves)));
-        wgs += dfc::ceil_div(blocks[k], per_wg);
+        const uint64_t wgs_k = dfc::ceil_div(blocks[k], per_wg);
+        const uint64_t wavefronts = wgs_k * waves;
+        const uint32_t run = run_set ? run_set : auto_run(blocks[k], wavefronts);
+        pl.run.push_back(run);
+        pl.crit = std::max(pl.crit, dfc::ceil_div(dfc::ceil_div(blocks[k], uint64_t(run)), wavefronts) * run);
+        wgs += wgs_k;
     }
     pl.crit *= dfc::ceil_div(wgs, uint64_t(per_cu) * uint64_t(device_cu_count()));
     return DFC_OK;
@@ -499,11 +547,13 @@ dfc_status launch_planned(const dfc_batch_item *items, const Plan &pl, uint32_t 
         a.dst_bytes = uint32_t(2 * in.n);
         a.total_bits = in.total_bits;
         a.n_blocks = uint32_t(in.n_blocks);
-        a.blocks_per_wg = uint32_t(dfc::ceil_div(in.n_blocks, pl.g[k]));
+        const uint64_t per_wg = dfc::ceil_div(in.n_blocks, pl.g[k]);
+        a.wgs = uint32_t(dfc::ceil_div(in.n_blocks, per_wg));
         a.wg_begin = wg;
         a.tables_bytes = uint32_t(dfc::tables_bytes(in.lut_bits));
         a.lut_bits = in.lut_bits;
-        wg += uint32_t(dfc::ceil_div(in.n_blocks, a.blocks_per_wg));
+        a.run = pl.run[k];
+        wg += a.wgs;
     }
     args.count = uint32_t(pl.live.size());
     args.stage_bytes = pl.stage;
@@ -566,13 +616,15 @@ dfc_status check_item(const dfc_batch_item &it) {
 
 extern "C" {
 
-dfc_status dfc_set_launch(uint32_t waves_per_group, uint32_t blocks_per_wave, uint32_t stores) {
+dfc_status dfc_set_launch(uint32_t waves_per_group, uint32_t blocks_per_wave, uint32_t stores, uint32_t run_blocks) {
     if (waves_per_group > kMaxWaves) return DFC_EINVAL;
     if (blocks_per_wave > 64) return DFC_EINVAL;
     if (stores > DFC_STORES_IMMEDIATE) return DFC_EINVAL;
+    if (run_blocks > 64) return DFC_EINVAL;
     g_launch.waves.store(waves_per_group, std::memory_order_relaxed);
     g_launch.blocks_per_wave.store(blocks_per_wave, std::memory_order_relaxed);
     g_launch.stores.store(stores, std::memory_order_relaxed);
+    g_launch.run.store(run_blocks, std::memory_order_relaxed);
     return DFC_OK;
 }
 

@@ -161,12 +161,16 @@ def test_oracle_written_container_decodes():
         assert status == 0 and np.array_equal(got, x.ravel())
 
 
-@pytest.mark.parametrize("waves,bpw", [(4, 1), (8, 1), (8, 3), (16, 2), (4, 16)])
-def test_launch_shapes(waves, bpw):
-    dfc.set_launch(waves, bpw, MODE["stores"])
+# (waves per workgroup, blocks per wavefront, blocks per run): with fixed
+# work per workgroup (bpw > 0) and runs of several blocks, each wavefront
+# decodes several runs, and its carry and prefetch cross from one to the next.
+@pytest.mark.parametrize("waves,bpw,run", [(4, 1, 0), (8, 1, 0), (8, 3, 0), (16, 2, 0), (4, 16, 0), (4, 16, 3),
+                                           (8, 3, 2), (4, 16, 16), (1, 8, 5), (2, 64, 64)])
+def test_launch_shapes(waves, bpw, run):
+    dfc.set_launch(waves, bpw, MODE["stores"], run)
     try:
         x = synth.gaussian((700, 1024), 0.02, (51,))
-        check(x, 16, oracle=False, label=f"launch {waves}x{bpw}")
+        check(x, 16, oracle=False, label=f"launch {waves}x{bpw} run {run}")
     finally:
         dfc.set_launch(0, 0, MODE["stores"])
 
@@ -455,8 +459,8 @@ def test_hip_graph_capture_and_replay():
 
 
 @pytest.mark.parametrize("layout", [dfc.LAYOUT_FLAT, dfc.LAYOUT_PADDED])
-@pytest.mark.parametrize("waves,bpw", [(0, 0), (1, 8), (4, 2)])
-def test_corrupt_block_leaves_the_rest_exact(layout, waves, bpw):
+@pytest.mark.parametrize("waves,bpw,run", [(0, 0, 0), (1, 8, 0), (4, 2, 0), (4, 4, 2), (2, 8, 3)])
+def test_corrupt_block_leaves_the_rest_exact(layout, waves, bpw, run):
     """A block offset moved by one makes the two blocks around it fail their
     count check: those two blocks stay unwritten, the status word is set,
     and every other block -- before them in the same run of blocks, and
@@ -472,7 +476,7 @@ def test_corrupt_block_leaves_the_rest_exact(layout, waves, bpw):
     ob = struct.unpack_from("<III", bytes(blob[o - 4: o + 8]))
     bad[o: o + 4] = np.frombuffer(struct.pack("<I", ob[1] + 1), dtype=np.uint8)
     binfo = dfc.blob_info(bad)
-    dfc.set_launch(waves, bpw, MODE["stores"])
+    dfc.set_launch(waves, bpw, MODE["stores"], run)
     try:
         dev = torch.from_numpy(bad).cuda()
         out = torch.full((int(info.n),), 0x7E7E, dtype=torch.int16, device="cuda")

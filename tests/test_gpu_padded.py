@@ -138,11 +138,11 @@ def test_mixed_layouts_and_chunk_sizes_in_one_batch():
         assert np.array_equal(out.cpu().numpy().view(np.uint16), x.ravel()), c
 
 
-@pytest.mark.parametrize("waves,bpw", [(4, 1), (8, 3), (16, 2)])
-def test_launch_shapes(waves, bpw):
-    dfc.set_launch(waves, bpw, MODE["stores"])
+@pytest.mark.parametrize("waves,bpw,run", [(4, 1, 0), (8, 3, 0), (16, 2, 0), (4, 16, 3), (2, 32, 2)])
+def test_launch_shapes(waves, bpw, run):
+    dfc.set_launch(waves, bpw, MODE["stores"], run)
     try:
-        check(synth.gaussian((512, 1024), 0.02, (79,)), 8, oracle=False, label=f"launch {waves}x{bpw}")
+        check(synth.gaussian((512, 1024), 0.02, (79,)), 8, oracle=False, label=f"launch {waves}x{bpw} run {run}")
     finally:
         dfc.set_launch(0, 0, MODE["stores"])
 

@@ -80,7 +80,7 @@ def test_encoder_refuses_blocks_wider_than_a_wavefront(T, layout):
 def test_launch_knob_rejects_out_of_range_values():
     """dfc_set_launch validates every field before it changes anything; no
     GPU call is made."""
-    for bad in ((17, 0, 0), (0, 65, 0), (0, 0, 3)):
+    for bad in ((17, 0, 0, 0), (0, 65, 0, 0), (0, 0, 3, 0), (0, 0, 0, 65)):
         with pytest.raises(dfc.DfcError) as e:
             dfc.set_launch(*bad)
         assert e.value.status == dfc.EINVAL, bad
