@@ -338,12 +338,14 @@ dfc_status dfc_encode_device_noalloc(const uint16_t *src_dev, uint64_t n, const 
  * stores them at once, 8 per SIMD, 5 for 32-byte chunks), and the blocks
  * per run (1..64): a matrix's blocks are cut into runs of that many
  * consecutive blocks, dealt out to its wavefronts in turn.  0 = automatic
- * for each (deferred once a launch has at least 4 blocks per wavefront the
- * machine holds at 8 per SIMD; runs of 2 blocks once a matrix gives each of
- * its wavefronts at least 4, else 1).  Returns DFC_EINVAL for other values.  The
- * library's only process-wide state: each value is read atomically by every
- * later decode launch, on any thread, so a caller that changes it while
- * other threads decode changes their launch shape (never their results). */
+ * for each (the most resident wavefronts, in the smallest workgroup that
+ * holds that many; deferred once the immediate build would give each of its
+ * wavefronts at least 24 blocks in sequence; runs of 2 blocks once a matrix
+ * gives each of its wavefronts at least 4, else 1).  Returns DFC_EINVAL for
+ * other values.  The library's only process-wide state: each value is read
+ * atomically by every later decode launch, on any thread, so a caller that
+ * changes it while other threads decode changes their launch shape (never
+ * their results). */
 enum { DFC_STORES_AUTO = 0, DFC_STORES_DEFERRED = 1, DFC_STORES_IMMEDIATE = 2 };
 dfc_status dfc_set_launch(uint32_t waves_per_group, uint32_t blocks_per_wave, uint32_t stores,
                           uint32_t run_blocks);
