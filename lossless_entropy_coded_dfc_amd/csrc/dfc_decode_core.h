@@ -405,8 +405,23 @@ __device__ __forceinline__ u32x4 assemble8(const u32x2 &E, const u32x2 &R) {
 __device__ __forceinline__ void load_or_derive_tables(uint8_t *lds, const uint8_t *tables, uint32_t tables_bytes,
                                                       const uint8_t *lengths, uint32_t lut_bits) {
     if (tables) {
-        for (uint32_t o = threadIdx.x * 16u; o < tables_bytes; o += blockDim.x * 16u)
-            *reinterpret_cast<uint4 *>(lds + o) = *reinterpret_cast<const uint4 *>(tables + o);
+        // every load of a thread is issued before its LDS writes, so the
+        // copy waits for one round trip to the cache, not one per 16 bytes
+        // (four per thread cover the largest tables, 57,984 bytes at k = 12,
+        // from 1,024 threads; smaller workgroups loop)
+        const __amdgpu_buffer_rsrc_t tr =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(tables), 0, int(tables_bytes), kBufferConfig);
+        const uint32_t step = blockDim.x * 16u;
+        for (uint32_t o = threadIdx.x * 16u; o < tables_bytes; o += 4u * step) {
+            const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(tr, o, 0, 0);
+            const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(tr, o + step, 0, 0);
+            const u32x4 c = __builtin_amdgcn_raw_buffer_load_b128(tr, o + 2u * step, 0, 0);
+            const u32x4 d = __builtin_amdgcn_raw_buffer_load_b128(tr, o + 3u * step, 0, 0);
+            *reinterpret_cast<u32x4 *>(lds + o) = a;
+            if (o + step < tables_bytes) *reinterpret_cast<u32x4 *>(lds + o + step) = b;
+            if (o + 2u * step < tables_bytes) *reinterpret_cast<u32x4 *>(lds + o + 2u * step) = c;
+            if (o + 3u * step < tables_bytes) *reinterpret_cast<u32x4 *>(lds + o + 3u * step) = d;
+        }
         __syncthreads();
     } else {
         derive_tables(lds, lds + tables_bytes, lengths, lut_bits);
