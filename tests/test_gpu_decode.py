@@ -92,6 +92,39 @@ def test_mixed_chunk_sizes_in_one_batch():
         assert np.array_equal(got, bl.decode_blob(bytes(b)))
 
 
+@pytest.mark.parametrize("run", [0, 3])
+def test_items_of_very_different_sizes_share_a_launch(run):
+    """32 matrices of one chunk size in one launch, from 1 weight to 33.5 M:
+    each gets its share of the resident wavefronts, and with automatic runs
+    the large ones are dealt out in runs of 2 blocks while the small ones
+    (fewer blocks than 4 per wavefront) go one block per run; run = 3 forces
+    runs longer than the small matrices' whole block count."""
+    shapes = [(1,), (2,), (7,), (8,), (9,), (63,), (64,), (65,), (511,), (512,), (513,), (1000,), (4097,),
+              (6300,), (3, 3151), (64, 1024), (100, 1037), (257, 1031), (512, 4096), (1024, 4096), (333, 7777),
+              (1024, 4096), (2048, 4096), (4096, 1024), (4096, 4096), (8192, 4096), (1, 65537), (17, 64),
+              (4096, 14336 // 4), (5, 200003), (128, 128), (4095, 4097)]
+    assert len(shapes) == 32
+    xs = [synth.gaussian_with_outliers(sh, 0.02, (58, j)) for j, sh in enumerate(shapes)]
+    blobs = [dfc.encode(x, chunk_bytes=16, lut_bits=11) for x in xs]
+    infos = [dfc.blob_info(b) for b in blobs]
+    devs = [torch.from_numpy(b).cuda() for b in blobs]
+    outs = [torch.full((int(i.n),), 0x7E7E, dtype=torch.int16, device="cuda") for i in infos]
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    say("case 32 sizes in one launch, run", run, "blocks", [int(i.n_blocks) for i in infos])
+    dfc.set_launch(0, 0, MODE["stores"], run)
+    try:
+        dfc.decode_batch(list(zip(devs, infos, outs)), status)
+        torch.cuda.synchronize()
+    finally:
+        dfc.set_launch(0, 0, MODE["stores"])
+    assert int(status.item()) == 0
+    for x, o, b, info in zip(xs, outs, blobs, infos):
+        got = o.cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, x.ravel()), x.shape
+        if info.n <= 300_000:
+            assert np.array_equal(got, bl.decode_blob(bytes(b))), x.shape
+
+
 @pytest.mark.parametrize("kind", ["outliers", "uniform", "ladder", "bimodal", "t"])
 def test_distributions_small(kind):
     shape = (257, 1031)
