@@ -432,4 +432,7 @@ STORES_AUTO, STORES_DEFERRED, STORES_IMMEDIATE = 0, 1, 2
 
 
 def set_launch(waves_per_group: int = 0, blocks_per_wave: int = 0, stores: int = STORES_AUTO, run_blocks: int = 0):
+    """dfc_set_launch: the Huffman decoder's process-wide launch shape
+    (wavefronts per workgroup, blocks per wavefront, store build, blocks per
+    run; 0 = automatic for each).  Changes launch shapes, never results."""
     _check(library().dfc_set_launch(waves_per_group, blocks_per_wave, stores, run_blocks), "dfc_set_launch")
