@@ -339,8 +339,10 @@ dfc_status dfc_encode_device_noalloc(const uint16_t *src_dev, uint64_t n, const 
  * per run (1..64): a matrix's blocks are cut into runs of that many
  * consecutive blocks, dealt out to its wavefronts in turn.  0 = automatic
  * for each (the most resident wavefronts, in the smallest workgroup that
- * holds that many; deferred once the immediate build would give each of its
- * wavefronts at least 24 blocks in sequence; runs of 2 blocks once a matrix
+ * holds that many; immediate for 4- and 8-byte chunks; for 16-byte chunks
+ * deferred once the immediate build would give each of its wavefronts at
+ * least 24 blocks in sequence; for 32-byte chunks deferred unless that
+ * doubles the blocks a wavefront decodes in sequence; runs of 2 blocks once a matrix
  * gives each of its wavefronts at least 4, else 1).  Returns DFC_EINVAL for
  * other values.  The library's only process-wide state: each value is read
  * atomically by every later decode launch, on any thread, so a caller that

@@ -564,14 +564,19 @@ dfc_status launch_planned(const dfc_batch_item *items, const Plan &pl, uint32_t 
     return hipGetLastError() == hipSuccess ? DFC_OK : DFC_EHIP;
 }
 
-// One launch for a group of items of one chunk size and layout.  Deferred
-// stores hold a wavefront to 4 per SIMD, the immediate build runs up to 8.
-// The deferred build is used once the immediate build's wavefronts would
-// each have at least kMinCrit blocks in sequence (a long job, where the
-// spread-out stores pay: the whole model of 226 matrices, about 40 blocks
-// per wavefront, decodes 5% faster deferred) and its own path is less than
-// twice as long; shorter jobs finish sooner with more wavefronts (one
-// Llama-3-8B block, about 10 blocks per wavefront, 4% faster immediate).
+// One launch for a group of items of one chunk size and layout.  The
+// deferred build's registers cost residency: at C = 4 and 8 it holds 7 and
+// 5 wavefronts per SIMD against the immediate build's 8, and decodes the
+// 8192 x 28672 stress tensors 24-47% slower, so small chunks always store
+// at once.  At C = 16 (4 against 8 per SIMD) the deferred build is used once
+// the immediate build's wavefronts would each have at least 24 blocks in
+// sequence (a long job, where the spread-out stores pay: the whole model of
+// 226 matrices, about 40 blocks per wavefront, decodes 5% faster deferred)
+// and its own path is less than twice as long; shorter jobs finish sooner
+// with more wavefronts (one Llama-3-8B block, about 10 blocks per
+// wavefront, 4% faster immediate).  At C = 32 the immediate build is held
+// to 5 per SIMD as well, and the deferred one (4) is 12-27% faster on the
+// stress tensors whenever its path is less than twice as long.
 template <int C, bool Padded>
 dfc_status launch_group(const dfc_batch_item *items, const uint32_t *idx, uint32_t count, uint32_t *status,
                         hipStream_t stream) {
@@ -585,8 +590,8 @@ dfc_status launch_group(const dfc_batch_item *items, const uint32_t *idx, uint32
     Plan pi;
     const dfc_status s = plan_group<C, Padded, false>(items, idx, count, pi);
     if (s != DFC_OK) return s;
-    constexpr uint64_t kMinCrit = 24;
-    if (mode == DFC_STORES_AUTO && pd.crit < 2 * pi.crit && pi.crit >= kMinCrit)
+    constexpr uint64_t kMinCrit = C >= 32 ? 0 : 24;
+    if (mode == DFC_STORES_AUTO && C >= 16 && pd.crit < 2 * pi.crit && pi.crit >= kMinCrit)
         return launch_planned<C, Padded, true>(items, pd, status, stream);
     return launch_planned<C, Padded, false>(items, pi, status, stream);
 }
