@@ -342,8 +342,10 @@ dfc_status dfc_encode_device_noalloc(const uint16_t *src_dev, uint64_t n, const 
  * holds that many; immediate for 4- and 8-byte chunks; for 16-byte chunks
  * deferred once the immediate build would give each of its wavefronts at
  * least 24 blocks in sequence; for 32-byte chunks deferred unless that
- * doubles the blocks a wavefront decodes in sequence; runs of 2 blocks once a matrix
- * gives each of its wavefronts at least 4, else 1).  Returns DFC_EINVAL for
+ * doubles the blocks a wavefront decodes in sequence; runs of about 6,144
+ * output values, 2 to 16 blocks, at most a quarter of a wavefront's share,
+ * so 1 for a matrix that gives its wavefronts fewer than 4 blocks each).
+ * Returns DFC_EINVAL for
  * other values.  The library's only process-wide state: each value is read
  * atomically by every later decode launch, on any thread, so a caller that
  * changes it while other threads decode changes their launch shape (never
