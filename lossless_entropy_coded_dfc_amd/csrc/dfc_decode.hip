@@ -90,19 +90,19 @@ struct Prefetch {
 
 // Wavefronts per SIMD the register budget is sized for (512 VGPRs per lane
 // shared by the resident wavefronts).  With deferred stores (below) the
-// assembled rounds held in registers take it to 128 VGPRs and 4 wavefronts,
-// which decode a large job as fast as 8 do (the decoder is held by the memory
-// path, not by latency); without them 64 VGPRs give 8 (the 32-byte chunk path
-// needs more and settles for 5), which finish a job of about one block per
-// wavefront sooner, since each wavefront then has less to do in sequence.
+// assembled rounds held in registers allow at most 128 VGPRs and 4
+// wavefronts (C = 16 uses all of them; C = 4 and 8 fit 7 and 5); without
+// them 64 VGPRs give 8 (the 32-byte chunk path needs more and settles for
+// 5).  The launcher picks the build per chunk size and job (launch_group).
 template <int C, bool Defer>
 struct Occupancy {
     static constexpr int kWavesPerSimd = Defer ? 4 : (C >= 32 ? 5 : 8);
 };
 
-// Output rounds.  A wavefront decodes a contiguous run of blocks and writes
-// its output in rounds of 512 values (1 KB of bf16, one 16-byte store per
-// lane) aligned to multiples of 512 in the output: a block's exponents are
+// Output rounds.  A wavefront decodes its runs of consecutive blocks one
+// after another and writes each run's output in rounds of 512 values (1 KB
+// of bf16, one 16-byte store per lane) aligned to multiples of 512 in the
+// output: a block's exponents are
 // staged in LDS behind the values still pending from the blocks before it
 // (fewer than 512, kept in registers in between), every complete round is
 // merged with its raw bytes and stored (the first few during the next
